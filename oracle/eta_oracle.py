@@ -1,0 +1,306 @@
+"""fp64 CPU oracle of the Elastic Threshold Attention (ETA) decode step.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the product path. It shares no code with
+the HIP library.
+
+Source: "Elastic Threshold Attention: Learned Contextual Sparsity for
+Long-Context Decoding" (paperpeel.com/paper/2609.20888). Section numbers below
+refer to that page. The page lost its display equations (the dual bound,
+Eq. 7) and the body of the decode algorithm (Algorithm 4); where a step is not
+fixed by the surviving text, the reading taken is stated at that step.
+
+What one decode step computes, for sequence n of length T and query head h
+served by KV head g = floor(h / G), G = H_Q / H_KV:
+
+  1. threshold      tau~ = w_h . q + b_h - a   (learned)   or   c_h - a
+                    (calibrated)  -- Sections 1, 4.7, D.1, G.1.
+  2. block record   for each complete 64-token block: centroid mu^ = fp16(mean k)
+                    (round to nearest even) and radius R = max_s ||k_s - mu^||_2
+                    -- Section 3.2 and F.1 (per-KV-head record of an fp16 centroid
+                    and an fp32 scalar norm). Reading: the scalar is the radius of
+                    the block's keys about the stored centroid, so that
+                    q.k <= q.mu^ + ||q|| R holds for every key (Cauchy-Schwarz).
+  3. screen         UB = s (q . mu^ + ||q|| R), s = 1/sqrt(d); a complete block is
+                    admitted unless UB < tau~ -- Section 3, 3.1, F.1. The partial
+                    last block is always loaded (Section 4.8, F.4) and so are the
+                    `lwb` most recent complete blocks (Section 4.8).
+  4. rescue         if nothing is admitted, the block with the largest UB (lowest
+                    index on ties) is admitted -- Section 3.2, F.4 (read globally,
+                    not per chunk).
+  5. attention      over every token t < T of the admitted blocks:
+                    S = s q . k_t,  S~ = S * sigmoid(beta (S - tau~)),
+                    o = sum_t exp(S~_t) v_t / sum_t exp(S~_t)  -- Sections 1, 2.2,
+                    E.3, G.1. The sign of the sigmoid argument is the one that
+                    reproduces sigma'(8) = 3.35e-4 and sigma'(40) ~ 4.3e-18 of B.1.
+
+All arithmetic is float64 on the stored values (bfloat16 or float32 K/V/q,
+upcast exactly); only mu^ is rounded, to float16, because that rounding is
+part of the stored record.
+
+Pins (tests, CPU): brute-force per-key enumeration on tiny inputs (sets, counts
+and outputs), exact bound soundness, no-false-negative and nesting properties,
+dense mode against torch's scaled_dot_product_attention, closed forms for the
+all-suppressed, equal-logit and single-key cases, the fp16 rounding mode of
+mu^, page-permutation invariance, and the sigmoid convention values of B.1.
+Parity unpinned: the pages' own dual bound (Eq. 7) and their chunk-local
+rescue rule are not reproducible from the text and are not implemented here.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Iterable, Optional
+
+import numpy as np
+
+BLOCK = 64
+_CHUNK_BLOCKS = 256
+
+
+# --------------------------------------------------------------------------- values
+def upcast(x: np.ndarray, kv_dtype: str) -> np.ndarray:
+    """Stored K/V/q values -> float64, exactly."""
+    if kv_dtype == "bf16":
+        bits = np.asarray(x, dtype=np.uint16).astype(np.uint32) << 16
+        return bits.view(np.float32).astype(np.float64)
+    if kv_dtype == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    raise ValueError(f"unknown kv dtype {kv_dtype!r}")
+
+
+def sigmoid(x):
+    """Logistic function 1/(1+e^-x), evaluated without overflow."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    pos = x >= 0
+    with np.errstate(over="ignore", invalid="ignore"):
+        out[pos] = 1.0 / (1.0 + np.exp(-x[pos]))
+        ex = np.exp(x[~pos])
+        out[~pos] = ex / (1.0 + ex)
+    return out
+
+
+def gate(S, tau: float, beta: float):
+    """Centered-SiLU filter of a logit: S * sigmoid(beta (S - tau)).
+
+    Sections 1 and E.3 (multiplicative masking S~ = S . sigma) and G.1 (the
+    tempered logit with the effective threshold). Logits well above tau pass
+    unchanged; logits well below shrink to 0, i.e. weight exp(0) = 1: the
+    uniform floor of Section 1."""
+    S = np.asarray(S, dtype=np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        return S * sigmoid(beta * (S - tau))
+
+
+# --------------------------------------------------------------------------- block records
+def block_summary(kb: np.ndarray):
+    """Record of complete blocks: kb is float64 [nb, 64, d] (or [64, d]).
+
+    Returns (mu^, R): mu^ float64 [nb, d] holding float16 values, R float64 [nb].
+    mu^ is the fp64 mean rounded to float16 (nearest even); if any coordinate is
+    not finite in float16 the centroid is the zero vector. R is the largest
+    Euclidean distance of a key to mu^, +inf when it is not finite.
+    Section 3.2 and F.1 (fp16 centroid, scalar fp32 norm per block per KV head)."""
+    single = kb.ndim == 2
+    if single:
+        kb = kb[None]
+    mean = kb.mean(axis=1)
+    with np.errstate(over="ignore", invalid="ignore"):
+        mu16 = mean.astype(np.float16).astype(np.float64)
+    ok = np.isfinite(mu16).all(axis=1)
+    mu = np.where(ok[:, None], mu16, 0.0)
+    with np.errstate(over="ignore", invalid="ignore"):
+        diff = kb - mu[:, None, :]
+        r = np.sqrt((diff * diff).sum(axis=2)).max(axis=1)
+    r = np.where(np.isnan(r) | np.isinf(r), np.inf, r)
+    if single:
+        return mu[0], float(r[0])
+    return mu, r
+
+
+def build_summaries(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray,
+                    seq_lens: np.ndarray, segments: Optional[Iterable] = None):
+    """Records for every complete block of every (sequence, KV head).
+
+    Returns mu float64 [num_pages][H_KV][d] and R float64 [num_pages][H_KV];
+    entries of pages that hold no complete block are NaN."""
+    P, HKV, B, D = k_pages.shape
+    assert B == BLOCK
+    mu = np.full((P, HKV, D), np.nan)
+    R = np.full((P, HKV), np.nan)
+    N = len(seq_lens)
+    segs = [(n, g) for n in range(N) for g in range(HKV)] if segments is None else list(segments)
+    for (n, g) in segs:
+        nfull = int(seq_lens[n]) // BLOCK
+        pages = np.asarray(block_table[n, :nfull], dtype=np.int64)
+        for j0 in range(0, nfull, _CHUNK_BLOCKS):
+            pg = pages[j0:j0 + _CHUNK_BLOCKS]
+            kb = upcast(k_pages[pg, g], kv_dtype)
+            m, r = block_summary(kb)
+            mu[pg, g] = m
+            R[pg, g] = r
+    return mu, R
+
+
+# --------------------------------------------------------------------------- screen
+def threshold(mode: str, q_h: np.ndarray, w_h, b_h: float, a: float) -> float:
+    """Effective threshold tau~ = tau - a.
+
+    learned:    tau = w_h . q + b_h   (Section 1; D.1: per-head linear predictor)
+    calibrated: tau = c_h             (Section 4.7: frozen per-head constant)
+    a: threshold adjustment (B.1 tables; G.1 writes tau~ = tau - a)."""
+    if mode == "learned":
+        return float(np.dot(np.asarray(w_h, dtype=np.float64), np.asarray(q_h, dtype=np.float64))) \
+            + float(b_h) - float(a)
+    if mode == "calibrated":
+        return float(b_h) - float(a)
+    raise ValueError(f"unknown threshold mode {mode!r}")
+
+
+def block_bound(q: np.ndarray, mu: np.ndarray, R: np.ndarray, scale: float) -> np.ndarray:
+    """Upper bound on the scaled logit s q.k of every key of each block:
+    s (q . mu^ + ||q||_2 R). Reading of the geometric block bound of Section 3
+    and F.1 (the display equation did not survive)."""
+    q = np.asarray(q, dtype=np.float64)
+    nq = math.sqrt(float(np.dot(q, q)))
+    with np.errstate(invalid="ignore", over="ignore"):
+        return scale * (mu @ q + nq * R)
+
+
+def admitted_blocks(ub: np.ndarray, tau: float, seq_len: int, lwb: int):
+    """Blocks loaded for one (sequence, query head).
+
+    ub: bounds of the complete blocks (length floor(T/64)). A complete block is
+    admitted unless its bound is below tau~ (Section 3.1: a block matters when
+    one of its keys reaches the threshold; a NaN bound cannot exclude it). The
+    partial last block and the lwb most recent complete blocks are always
+    admitted (Section 4.8, F.4). If nothing is admitted, the block with the
+    largest bound is (Top-1 rescue, Section 3.2 and F.4, taken over the whole
+    sequence; ties go to the lowest index).
+    Returns (bool mask over ceil(T/64) blocks, rescued flag)."""
+    nfull = seq_len // BLOCK
+    nblk = -(-seq_len // BLOCK)
+    adm = np.zeros(nblk, dtype=bool)
+    ub = np.asarray(ub, dtype=np.float64)[:nfull]
+    adm[:nfull] = ~(ub < tau)
+    if seq_len % BLOCK:
+        adm[nfull] = True
+    if lwb > 0 and nfull > 0:
+        adm[max(0, nfull - lwb):nfull] = True
+    rescued = False
+    if not adm.any():
+        adm[int(np.argmax(ub))] = True
+        rescued = True
+    return adm, rescued
+
+
+# --------------------------------------------------------------------------- attention
+def filtered_attention(q: np.ndarray, keys: np.ndarray, values: np.ndarray,
+                       tau: float, beta: float, scale: float) -> np.ndarray:
+    """o = sum_t exp(S~_t) v_t / sum_t exp(S~_t) over the retained tokens, with
+    S_t = s q.k_t and S~ = gate(S) (Section 2.2: weights w_s = exp(S~) on every
+    retained token, normalised over the retained set; G.1)."""
+    S = scale * (keys @ np.asarray(q, dtype=np.float64))
+    St = gate(S, tau, beta)
+    m = St.max()
+    w = np.exp(St - m)
+    return (w @ values) / w.sum()
+
+
+@dataclasses.dataclass
+class DecodeResult:
+    o: np.ndarray            # float64 [N][H_Q][d]  (NaN for heads not evaluated)
+    admitted: np.ndarray     # bool [N][H_Q][max_blocks]
+    rescued: np.ndarray      # bool [N][H_Q]
+    tau: np.ndarray          # float64 [N][H_Q]
+    ub: np.ndarray           # float64 [N][H_Q][max_blocks] (NaN where no record)
+    per_head: np.ndarray     # int64 [N][H_Q]   admitted blocks
+    union: np.ndarray        # int64 [N][H_KV]  blocks loaded for the group
+    tokens: np.ndarray       # int64 [N][H_Q]   attended tokens
+
+
+def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str,
+           w, b_or_c, a: float, beta: float, lwb: int, summaries=None,
+           heads: Optional[Iterable] = None, with_output: bool = True) -> DecodeResult:
+    """One ETA decode step for every sequence and query head.
+
+    q: [N][H_Q][d] stored values; w: [H_Q][d] (learned mode); b_or_c: [H_Q].
+    summaries: (mu, R) from build_summaries, built here if omitted.
+    heads: iterable of (n, h) whose output is evaluated (default: all)."""
+    N, HQ, D = q.shape
+    P, HKV, B, D2 = k_pages.shape
+    assert D2 == D and B == BLOCK and HQ % HKV == 0
+    G = HQ // HKV
+    MB = block_table.shape[1]
+    scale = 1.0 / math.sqrt(D)
+    if summaries is None:
+        summaries = build_summaries(k_pages, kv_dtype, block_table, seq_lens)
+    mu_all, R_all = summaries
+    qf = upcast(q, kv_dtype)
+    want = None if heads is None else set((int(n), int(h)) for n, h in heads)
+
+    o = np.full((N, HQ, D), np.nan)
+    admitted = np.zeros((N, HQ, MB), dtype=bool)
+    rescued = np.zeros((N, HQ), dtype=bool)
+    taus = np.zeros((N, HQ))
+    ubs = np.full((N, HQ, MB), np.nan)
+    for n in range(N):
+        T = int(seq_lens[n])
+        nfull = T // BLOCK
+        pages = np.asarray(block_table[n], dtype=np.int64)
+        for h in range(HQ):
+            g = h // G
+            tau = threshold(tau_mode, qf[n, h], None if w is None else w[h], b_or_c[h], a)
+            taus[n, h] = tau
+            ub = block_bound(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g], scale)
+            ubs[n, h, :nfull] = ub
+            adm, resc = admitted_blocks(ub, tau, T, lwb)
+            admitted[n, h, :len(adm)] = adm
+            rescued[n, h] = resc
+            if not with_output or (want is not None and (n, h) not in want):
+                continue
+            o[n, h] = _attend(qf[n, h], k_pages, v_pages, kv_dtype, pages, g, np.nonzero(adm)[0],
+                              T, tau, beta, scale)
+
+    per_head = admitted.sum(axis=2).astype(np.int64)
+    union = np.zeros((N, HKV), dtype=np.int64)
+    tokens = np.zeros((N, HQ), dtype=np.int64)
+    for n in range(N):
+        T = int(seq_lens[n])
+        nblk = -(-T // BLOCK)
+        width = np.minimum(BLOCK, T - BLOCK * np.arange(nblk))
+        for g in range(HKV):
+            union[n, g] = admitted[n, g * G:(g + 1) * G, :nblk].any(axis=0).sum()
+        tokens[n] = admitted[n, :, :nblk] @ width
+    return DecodeResult(o=o, admitted=admitted, rescued=rescued, tau=taus, ub=ubs,
+                        per_head=per_head, union=union, tokens=tokens)
+
+
+def _attend(qh, k_pages, v_pages, kv_dtype, pages, g, blocks, T, tau, beta, scale):
+    """filtered_attention over the tokens t < T of the given blocks, gathering
+    the cache in slices of blocks so that long contexts fit in memory. The max
+    is taken over all retained tokens first, then the weighted sums."""
+    St_parts = []
+    for b0 in range(0, len(blocks), _CHUNK_BLOCKS):
+        bl = blocks[b0:b0 + _CHUNK_BLOCKS]
+        kb = upcast(k_pages[pages[bl], g], kv_dtype).reshape(-1, qh.shape[0])
+        tok = (bl[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)
+        keep = tok < T
+        S = scale * (kb[keep] @ qh)
+        St_parts.append(gate(S, tau, beta))
+    St = np.concatenate(St_parts)
+    m = St.max()
+    num = np.zeros(qh.shape[0])
+    den = 0.0
+    pos = 0
+    for b0 in range(0, len(blocks), _CHUNK_BLOCKS):
+        bl = blocks[b0:b0 + _CHUNK_BLOCKS]
+        vb = upcast(v_pages[pages[bl], g], kv_dtype).reshape(-1, qh.shape[0])
+        tok = (bl[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)
+        keep = tok < T
+        wts = np.exp(St[pos:pos + int(keep.sum())] - m)
+        pos += int(keep.sum())
+        num += wts @ vb[keep]
+        den += wts.sum()
+    return num / den

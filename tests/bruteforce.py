@@ -1,0 +1,137 @@
+"""Per-key brute force of the ETA decode step, for tiny inputs only.
+
+An independent second implementation used to pin the oracle: pure-Python loops
+over every key with the `math` module (fsum, exact float16 rounding through
+`struct`), no NumPy vector arithmetic and no code shared with `oracle/`.
+It follows "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888),
+Sections 2.2, 3.1, 3.2, 4.8, F.1, F.4 and G.1, with the same readings as the
+oracle (geometric bound about the fp16 centroid, global top-1 rescue).
+"""
+from __future__ import annotations
+
+import math
+import struct
+
+BLOCK = 64
+
+
+def _f16(x: float) -> float:
+    try:
+        return struct.unpack("<e", struct.pack("<e", x))[0]
+    except OverflowError:
+        return math.inf
+
+
+def _sig(x: float) -> float:
+    if math.isnan(x):
+        return math.nan
+    if x >= 0:
+        return 1.0 / (1.0 + math.exp(-x))
+    try:
+        e = math.exp(x)
+    except OverflowError:  # pragma: no cover - x < 0 cannot overflow
+        return 0.0
+    return e / (1.0 + e)
+
+
+def value(stored, kv_dtype: str) -> float:
+    if kv_dtype == "bf16":
+        return struct.unpack("<f", struct.pack("<I", int(stored) << 16))[0]
+    return float(stored)
+
+
+def record(rows):
+    """(centroid, radius) of one complete block given its 64 key rows."""
+    d = len(rows[0])
+    mean = [math.fsum(r[c] for r in rows) / len(rows) for c in range(d)]
+    mu = [_f16(x) for x in mean]
+    if not all(math.isfinite(x) for x in mu):
+        mu = [0.0] * d
+    best = 0.0
+    for r in rows:
+        try:
+            dist = math.sqrt(math.fsum((r[c] - mu[c]) ** 2 for c in range(d)))
+        except (OverflowError, ValueError):
+            dist = math.inf
+        if math.isnan(dist) or math.isinf(dist):
+            return mu, math.inf
+        best = max(best, dist)
+    return mu, best
+
+
+def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, a, beta, lwb):
+    """Returns dict with per (n, h): admitted block list, rescued flag, output
+    list, plus union counts per (n, g). Inputs are NumPy arrays of stored values
+    but are read element by element."""
+    N, HQ, D = q.shape
+    HKV = wl_k.shape[1]
+    G = HQ // HKV
+    s = 1.0 / math.sqrt(D)
+    out = {}
+    union = {}
+    for n in range(N):
+        T = int(seq_lens[n])
+        nfull = T // BLOCK
+        nblk = -(-T // BLOCK)
+
+        def key(g, t):
+            page = int(block_table[n][t // BLOCK])
+            return [value(x, kv_dtype) for x in wl_k[page][g][t % BLOCK]]
+
+        def val(g, t):
+            page = int(block_table[n][t // BLOCK])
+            return [value(x, kv_dtype) for x in wl_v[page][g][t % BLOCK]]
+
+        for g in range(HKV):
+            recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
+            loaded = set()
+            for hh in range(G):
+                h = g * G + hh
+                qh = [value(x, kv_dtype) for x in q[n][h]]
+                if tau_mode == "learned":
+                    tau = math.fsum(float(w[h][c]) * qh[c] for c in range(D)) + float(b_or_c[h]) - a
+                else:
+                    tau = float(b_or_c[h]) - a
+                qn = math.sqrt(math.fsum(x * x for x in qh))
+                adm = []
+                ubs = []
+                for j in range(nfull):
+                    mu, R = recs[j]
+                    dot = math.fsum(qh[c] * mu[c] for c in range(D))
+                    ub = s * (dot + qn * R)
+                    ubs.append(ub)
+                    forced = j >= nfull - lwb
+                    if forced or not (ub < tau):
+                        adm.append(j)
+                if T % BLOCK:
+                    adm.append(nfull)
+                rescued = False
+                if not adm:
+                    best = 0
+                    for j in range(1, nfull):
+                        if ubs[j] > ubs[best]:
+                            best = j
+                    adm = [best]
+                    rescued = True
+                loaded.update(adm)
+                # attention over every retained token
+                logits = []
+                vals = []
+                for j in adm:
+                    for r in range(BLOCK):
+                        t = j * BLOCK + r
+                        if t >= T:
+                            break
+                        S = s * math.fsum(qh[c] * x for c, x in enumerate(key(g, t)))
+                        z = beta * (S - tau)
+                        logits.append(S * _sig(z))
+                        vals.append(val(g, t))
+                m = max(logits)
+                wts = [math.exp(x - m) for x in logits]
+                den = math.fsum(wts)
+                o = [math.fsum(wts[i] * vals[i][c] for i in range(len(wts))) / den for c in range(D)]
+                tokens = sum(min(BLOCK, T - j * BLOCK) for j in adm)
+                out[(n, h)] = dict(admitted=sorted(adm), rescued=rescued, o=o, tau=tau, ub=ubs,
+                                   tokens=tokens)
+            union[(n, g)] = len(loaded)
+    return out, union

@@ -1,0 +1,374 @@
+"""Checks that pin the fp64 oracle to facts outside itself.
+
+Each `pin_*` takes the oracle module (so that the mutation tests can hand in a
+deliberately broken copy) and raises AssertionError when the oracle disagrees
+with: values printed on the pages, closed forms, a library routine, or the
+per-key brute force. Source: "Elastic Threshold Attention: Learned Contextual
+Sparsity for Long-Context Decoding" (paperpeel.com/paper/2609.20888).
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import bruteforce
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _decode(E, wl, bias=None, a=None, beta=None, lwb=None, tau_mode=None, **kw):
+    return E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
+                    tau_mode or wl.tau_mode, wl.w, wl.bias if bias is None else bias,
+                    wl.a if a is None else a, wl.beta if beta is None else beta,
+                    wl.lwb if lwb is None else lwb, **kw)
+
+
+def tiny(seed, n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned", lwb=0,
+         a=0.0, beta=5.0, density=0.4, bias=None):
+    """A tiny random workload with its threshold constant placed so that about
+    `density` of the complete blocks pass (placement uses the module's own
+    bound only to choose a number; the checks do not depend on it)."""
+    wl = W.make_workload("cfg1", seed=seed, n_seqs=n, seq_lens=list(lens), h_q=h_q, h_kv=h_kv,
+                         d=d, kv_dtype=dtype, mode=mode, needles=0, lwb=lwb, a=a, beta=beta,
+                         threads=1)
+    if bias is None:
+        bias = np.zeros(h_q, dtype=np.float32)
+        rng = np.random.default_rng(seed + 99)
+        bias[:] = rng.uniform(1.0, 4.0, size=h_q).astype(np.float32)
+    wl.bias = np.asarray(bias, dtype=np.float32)
+    return wl
+
+
+# --------------------------------------------------------------------------- B.1 convention
+def pin_sigmoid_convention(E):
+    """Section 4.1 / B.1: at start-dense init (tau = -8, logits ~ 0) the gate's
+    sigmoid derivative is 3.35e-4 at beta = 1 and ~4.3e-18 at beta = 5, and
+    every key passes (Section 2.1)."""
+    with open(os.path.join(GOLDEN, "sigmoid_convention.json")) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        eps = 1e-3
+        ratio = float(E.gate(np.array([eps]), c["tau"], c["beta"])[0]) / eps
+        # the gate multiplies the logit by sigmoid(beta (S - tau)): recover the
+        # sigmoid's argument from the ratio and check the printed derivative
+        sig = float(E.sigmoid(np.array([c["sigmoid_arg"]]))[0])
+        assert abs(ratio - sig) < 1e-6, (ratio, sig)
+        assert ratio > 0.99, "start-dense init must let every key pass"
+        deriv = sig * float(E.sigmoid(np.array([-c["sigmoid_arg"]]))[0])
+        assert abs(deriv / c["sigmoid_prime"] - 1.0) < c["rel_tol"], (deriv, c)
+
+
+def pin_gate_closed_forms(E):
+    """sigmoid(0) = 1/2 at the threshold; far above it the logit passes; far
+    below it shrinks to 0 (the uniform floor of Section 1)."""
+    S = np.array([2.5, 30.0, -30.0, -2.0])
+    g = E.gate(S, 2.5, 5.0)
+    assert abs(g[0] - 1.25) < 1e-15
+    assert abs(g[1] - 30.0) < 1e-12
+    assert abs(g[2]) < 1e-60
+    assert abs(g[3] - (-2.0) / (1.0 + math.exp(22.5))) < 1e-20
+    gd = E.gate(S, -math.inf, 5.0)
+    assert np.array_equal(gd, S), "tau = -inf must leave logits unchanged"
+
+
+# --------------------------------------------------------------------------- block records
+def pin_fp16_rne(E):
+    """Centroids are stored as float16 with round-to-nearest-even (F.1)."""
+    d = 4
+    cases = [
+        (1.0 + 2.0 ** -11, 1.0),                       # tie -> even (down)
+        (1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),       # tie -> even (up)
+        (1.0 + 2.0 ** -11 + 2.0 ** -20, 1.0 + 2.0 ** -10),
+        (-(2.0 + 2.0 ** -10), -2.0),                   # tie at 2 -> even
+        (1000.3, 1000.5),                              # spacing 0.5 near 1000
+    ]
+    for x, want in cases:
+        kb = np.full((64, d), x, dtype=np.float64)
+        mu, R = E.block_summary(kb)
+        assert np.all(mu == want), (x, mu, want)
+        assert abs(R - math.sqrt(d) * abs(x - want)) <= 1e-12 * max(1.0, abs(x)), (R, x, want)
+    # the mean of distinct rows, not of a single row
+    kb = np.zeros((64, d))
+    kb[:32] = 1.0
+    mu, R = E.block_summary(kb)
+    assert np.all(mu == 0.5) and abs(R - 1.0) < 1e-15
+    # overflowing centroid falls back to the origin; non-finite keys give R = inf
+    kb = np.full((64, d), 70000.0)
+    mu, R = E.block_summary(kb)
+    assert np.all(mu == 0.0) and abs(R - 140000.0) < 1e-6
+    kb = np.zeros((64, d))
+    kb[5, 1] = np.inf
+    mu, R = E.block_summary(kb)
+    assert R == math.inf
+    kb[5, 1] = np.nan
+    mu, R = E.block_summary(kb)
+    assert R == math.inf
+
+
+def pin_bound_sound_and_tight(E, seed=0, trials=200):
+    """For every block and query, s q.k <= UB (Cauchy-Schwarz about the stored
+    centroid), with equality for a query pointing from the centroid to the
+    farthest key."""
+    rng = np.random.default_rng(seed)
+    for it in range(trials):
+        d = int(rng.choice([4, 8, 64, 128]))
+        kind = it % 5
+        if kind == 0:
+            kb = rng.standard_normal((1, d)) + 0.3 * rng.standard_normal((64, d))
+        elif kind == 1:  # coarse float16 spacing: centroid rounding is large
+            kb = 1000.0 + rng.uniform(0, 0.49, size=(1, d)) + 1e-3 * rng.standard_normal((64, d))
+        elif kind == 2:  # one outlier key
+            kb = rng.standard_normal((64, d))
+            kb[rng.integers(64)] *= 25.0
+        elif kind == 3:  # all keys equal, off the float16 grid
+            kb = np.repeat(rng.uniform(-3000, 3000, size=(1, d)), 64, axis=0)
+        else:
+            kb = rng.standard_normal((64, d)) * rng.uniform(0.01, 10.0)
+        s = 1.0 / math.sqrt(d)
+        mu, R = E.block_summary(kb)
+        qs = [rng.standard_normal(d) * rng.uniform(0.1, 5.0), -(kb[0] - mu) * 3.7]
+        far = int(np.argmax(np.linalg.norm(kb - mu, axis=1)))
+        tight_q = (kb[far] - mu) * 2.3
+        qs.append(tight_q)
+        for q in qs:
+            if not np.any(q):
+                continue
+            ub = float(E.block_bound(q, mu[None, :], np.array([R]), s)[0])
+            smax = float((s * (kb @ q)).max())
+            assert ub >= smax - 1e-9 * (1 + abs(smax)), (it, kind, ub, smax)
+        ub = float(E.block_bound(tight_q, mu[None, :], np.array([R]), s)[0])
+        smax = float((s * (kb @ tight_q)).max())
+        if np.any(tight_q):
+            assert abs(ub - smax) <= 1e-9 * (1 + abs(smax)), ("not tight", it, kind, ub, smax)
+
+
+# --------------------------------------------------------------------------- thresholds
+def pin_threshold_closed_form(E):
+    """tau~ = w.q + b - a (learned), c - a (calibrated): Sections 1, 4.7, D.1, G.1."""
+    q = np.array([2.0, -1.0, 0.5, 0.0])
+    w = np.array([3.0, 1.0, 4.0, 7.0])
+    assert abs(E.threshold("learned", q, w, 0.25, 0.4) - (6.0 - 1.0 + 2.0 + 0.25 - 0.4)) < 1e-15
+    assert abs(E.threshold("calibrated", q, w, 1.5, 0.4) - 1.1) < 1e-15
+    assert E.threshold("learned", q, np.zeros(4), -8.0, 0.0) == -8.0
+
+
+# --------------------------------------------------------------------------- whole step
+def pin_bruteforce(E, seeds=range(6)):
+    """Sets, counts, rescue flags and outputs equal the per-key brute force."""
+    variants = [
+        dict(n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+        dict(n=1, lens=(300,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated", lwb=2),
+        dict(n=3, lens=(64, 65, 191), h_q=4, h_kv=1, d=8, dtype="bf16", mode="learned", a=0.4),
+        dict(n=1, lens=(256,), h_q=1, h_kv=1, d=64, dtype="f32", mode="calibrated"),
+        dict(n=2, lens=(128, 70), h_q=2, h_kv=2, d=8, dtype="f32", mode="learned", beta=1.0, lwb=1),
+        dict(n=1, lens=(192,), h_q=4, h_kv=2, d=4, dtype="bf16", mode="calibrated",
+             bias=[1e4, 1e4, 1e4, 1e4]),  # forces the rescue path
+    ]
+    for seed in seeds:
+        v = dict(variants[seed % len(variants)])
+        wl = tiny(seed, **v)
+        res = _decode(E, wl)
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb)
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, n, h, got, r["admitted"])
+            assert bool(res.rescued[n, h]) == r["rescued"], (seed, n, h)
+            assert int(res.tokens[n, h]) == r["tokens"]
+            assert int(res.per_head[n, h]) == len(r["admitted"])
+            assert abs(res.tau[n, h] - r["tau"]) <= 1e-12 * (1 + abs(r["tau"]))
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+
+
+def pin_no_false_negatives(E, seeds=range(4)):
+    """Section 3.1: a block holding a key with S >= tau~ is significant; the
+    screen must admit every significant block."""
+    for seed in seeds:
+        wl = tiny(100 + seed, n=2, lens=(640, 300), h_q=4, h_kv=2, d=8, density=0.3)
+        # raise a few keys above their head's threshold
+        res0 = _decode(E, wl, with_output=False)
+        rng = np.random.default_rng(seed)
+        for _ in range(6):
+            n = int(rng.integers(2))
+            h = int(rng.integers(4))
+            t = int(rng.integers(int(wl.seq_lens[n])))
+            W.plant_needle(wl, n, h, t, logit=float(res0.tau[n, h]) + 0.5)
+        res = _decode(E, wl, with_output=False)
+        s = 1.0 / math.sqrt(wl.d)
+        for n in range(wl.n_seqs):
+            T = int(wl.seq_lens[n])
+            for h in range(wl.h_q):
+                g = h // wl.group
+                qh = W.storage_to_f32(wl.q[n, h], wl.kv_dtype).astype(np.float64)
+                for t in range(T):
+                    page = wl.block_table[n, t // 64]
+                    k = W.storage_to_f32(wl.k_pages[page, g, t % 64], wl.kv_dtype).astype(np.float64)
+                    if s * float(k @ qh) >= res.tau[n, h]:
+                        assert res.admitted[n, h, t // 64], (seed, n, h, t)
+
+
+def pin_nesting(E, seed=7):
+    """Raising the threshold can only remove blocks (no rescue involved)."""
+    wl = tiny(seed, n=1, lens=(64 * 12 + 5,), h_q=2, h_kv=1, d=8, mode="calibrated")
+    prev = None
+    for c in np.linspace(-1.0, 8.0, 19):
+        res = _decode(E, wl, bias=np.full(2, c, dtype=np.float32), with_output=False)
+        if prev is not None:
+            assert np.all(res.admitted <= prev), c
+        prev = res.admitted
+
+
+def pin_dense_sdpa(E):
+    """tau~ = -inf: the gate is the identity and the step is textbook softmax
+    attention, checked against torch's scaled_dot_product_attention (fp64,
+    grouped-query heads)."""
+    import torch
+    for seed, (lens, h_q, h_kv, d, dtype) in enumerate([((300, 64, 129), 4, 2, 8, "bf16"),
+                                                        ((1000,), 8, 2, 64, "f32")]):
+        wl = tiny(seed, n=len(lens), lens=lens, h_q=h_q, h_kv=h_kv, d=d, dtype=dtype,
+                  mode="calibrated", bias=np.full(h_q, -np.inf, dtype=np.float32))
+        res = _decode(E, wl)
+        for n in range(wl.n_seqs):
+            T = int(wl.seq_lens[n])
+            nb = -(-T // 64)
+            pages = wl.block_table[n, :nb]
+            f64 = lambda x: W.storage_to_f32(x, dtype).astype(np.float64)  # noqa: E731
+            K = f64(wl.k_pages[pages]).transpose(1, 0, 2, 3).reshape(h_kv, nb * 64, d)[:, :T]
+            V = f64(wl.v_pages[pages]).transpose(1, 0, 2, 3).reshape(h_kv, nb * 64, d)[:, :T]
+            q = f64(wl.q[n])[:, None, :]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                torch.from_numpy(q)[None], torch.from_numpy(np.ascontiguousarray(K))[None],
+                torch.from_numpy(np.ascontiguousarray(V))[None], enable_gqa=True)[0, :, 0].numpy()
+            np.testing.assert_allclose(res.o[n], ref, rtol=1e-10, atol=1e-12)
+            assert res.admitted[n, :, :nb].all()
+
+
+def pin_suppressed_mean(E):
+    """tau~ far above every logit: each logit is filtered to 0, every weight is
+    exp(0) = 1 and o is the plain mean of the retained values (Section 1's
+    uniform floor). With every block forced in, that is the mean over all T
+    tokens; with nothing admitted and no tail, the rescue keeps one block."""
+    wl = tiny(3, n=2, lens=(320, 200), h_q=2, h_kv=1, d=8, dtype="f32", mode="calibrated",
+              bias=np.full(2, 1e4, dtype=np.float32), lwb=100)
+    res = _decode(E, wl)
+    for n in range(2):
+        T = int(wl.seq_lens[n])
+        nb = -(-T // 64)
+        V = wl.v_pages[wl.block_table[n, :nb], 0].astype(np.float64).reshape(-1, 8)[:T]
+        for h in range(2):
+            np.testing.assert_allclose(res.o[n, h], V.mean(axis=0), rtol=1e-12, atol=1e-14)
+    wl = tiny(4, n=1, lens=(320,), h_q=2, h_kv=1, d=8, dtype="f32", mode="calibrated",
+              bias=np.full(2, 1e4, dtype=np.float32), lwb=0)
+    res = _decode(E, wl)
+    for h in range(2):
+        assert res.rescued[0, h] and res.per_head[0, h] == 1
+        j = int(np.nonzero(res.admitted[0, h])[0][0])
+        assert j == int(np.argmax(res.ub[0, h, :5]))
+        V = wl.v_pages[wl.block_table[0, j], 0].astype(np.float64)
+        np.testing.assert_allclose(res.o[0, h], V.mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def pin_equal_logits(E):
+    """All keys equal: every logit is equal, o is the mean of the retained
+    values whatever tau and beta are; all bounds tie, so with nothing admitted
+    the rescue takes block 0 (lowest index)."""
+    d = 8
+    wl = tiny(5, n=1, lens=(64 * 6,), h_q=1, h_kv=1, d=d, dtype="f32", mode="calibrated")
+    key = np.linspace(-1, 1, d).astype(np.float32)
+    wl.k_pages[:] = key
+    for c, expect_all in ((-50.0, True), (50.0, False)):
+        res = _decode(E, wl, bias=np.array([c], dtype=np.float32))
+        if expect_all:
+            assert res.per_head[0, 0] == 6
+            V = wl.v_pages[wl.block_table[0, :6], 0].astype(np.float64).reshape(-1, d)
+        else:
+            assert res.rescued[0, 0] and res.admitted[0, 0, 0] and res.per_head[0, 0] == 1
+            V = wl.v_pages[wl.block_table[0, 0], 0].astype(np.float64)
+        np.testing.assert_allclose(res.o[0, 0], V.mean(axis=0), rtol=1e-12, atol=1e-14)
+
+
+def pin_two_keys_closed_form(E):
+    """A hand-built block: one key exactly at the threshold (S = tau, gate 1/2),
+    63 keys at logit 0 (weight 1). o = (e^{tau/2} v0 + sum v_t) / (e^{tau/2} + 63)."""
+    d = 4
+    tau = 3.0
+    wl = tiny(6, n=1, lens=(64,), h_q=1, h_kv=1, d=d, dtype="f32", mode="calibrated",
+              bias=np.array([tau], dtype=np.float32), lwb=1)
+    wl.q[0, 0] = np.array([2.0, 0.0, 0.0, 0.0], dtype=np.float32)  # s = 1/2: S = k[0]
+    page = wl.block_table[0, 0]
+    wl.k_pages[page, 0] = 0.0
+    wl.k_pages[page, 0, 17, 0] = tau
+    wl.k_pages[page, 0, :, 1:] = 5.0  # orthogonal to q: logits unaffected
+    res = _decode(E, wl)
+    V = wl.v_pages[page, 0].astype(np.float64)
+    e = math.exp(tau / 2)
+    want = (e * V[17] + V.sum(axis=0) - V[17]) / (e + 63.0)
+    np.testing.assert_allclose(res.o[0, 0], want, rtol=1e-13, atol=1e-15)
+
+
+def pin_tail_masking(E):
+    """Rows of the last page past the sequence end are not tokens (F.4): junk
+    there (NaN) changes nothing."""
+    wl = tiny(8, n=2, lens=(130, 77), h_q=2, h_kv=1, d=8, dtype="f32", mode="calibrated")
+    res_nan = _decode(E, wl)
+    for n in range(2):
+        T = int(wl.seq_lens[n])
+        page = wl.block_table[n, T // 64]
+        wl.k_pages[page, :, T % 64:] = 0.0
+        wl.v_pages[page, :, T % 64:] = 0.0
+    res0 = _decode(E, wl)
+    assert np.all(np.isfinite(res_nan.o))
+    assert np.array_equal(res_nan.o, res0.o)
+
+
+def pin_page_permutation(E):
+    """The physical page order is invisible: same sets, same outputs."""
+    wl = tiny(9, n=2, lens=(400, 333), h_q=4, h_kv=2, d=8)
+    wl2 = W.permute_pages(wl, seed=3)
+    r1 = _decode(E, wl)
+    r2 = _decode(E, wl2)
+    assert np.array_equal(r1.admitted, r2.admitted)
+    assert np.array_equal(r1.o, r2.o)
+
+
+def pin_nonfinite_keys(E):
+    """A block with a non-finite key has R = inf and is admitted for any
+    finite threshold, also for a zero query (bound NaN)."""
+    wl = tiny(10, n=1, lens=(256,), h_q=1, h_kv=1, d=8, dtype="f32", mode="calibrated",
+              bias=np.array([1e3], dtype=np.float32))
+    wl.k_pages[wl.block_table[0, 2], 0, 5, 3] = np.inf
+    res = _decode(E, wl, with_output=False)
+    assert res.admitted[0, 0, 2] and res.per_head[0, 0] == 1 and not res.rescued[0, 0]
+    wl.q[:] = 0.0
+    res = _decode(E, wl, with_output=False)
+    assert res.admitted[0, 0, 2]
+
+
+def pin_threshold_tie_admitted(E):
+    """Section 3.1 counts a key with S >= tau as significant, so a block whose
+    bound equals tau~ exactly is admitted. Exact construction: keys equal to a
+    float16-representable vector (centroid exact, R = 0), s = 1/2."""
+    wl = tiny(11, n=1, lens=(128,), h_q=1, h_kv=1, d=4, dtype="f32", mode="calibrated",
+              bias=np.array([1.5], dtype=np.float32))
+    wl.q[0, 0] = np.array([2.0, 0.0, 0.0, 0.0], dtype=np.float32)
+    wl.k_pages[:] = 0.0
+    wl.k_pages[wl.block_table[0, 1], 0, :, 0] = 1.5   # UB = 0.5 * 2 * 1.5 = 1.5 = tau
+    wl.k_pages[wl.block_table[0, 0], 0, :, 0] = 1.0   # UB = 1.0 < tau
+    res = _decode(E, wl, with_output=False)
+    assert res.ub[0, 0, 1] == 1.5 and res.tau[0, 0] == 1.5
+    assert res.admitted[0, 0, 1] and not res.admitted[0, 0, 0] and not res.rescued[0, 0]
+
+
+ALL_PINS = [
+    pin_sigmoid_convention, pin_gate_closed_forms, pin_fp16_rne, pin_bound_sound_and_tight,
+    pin_threshold_closed_form, pin_bruteforce, pin_no_false_negatives, pin_nesting,
+    pin_dense_sdpa, pin_suppressed_mean, pin_equal_logits, pin_two_keys_closed_form,
+    pin_tail_masking, pin_page_permutation, pin_nonfinite_keys, pin_threshold_tie_admitted,
+]

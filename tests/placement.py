@@ -1,0 +1,85 @@
+"""Threshold placement for the test workloads (uses the oracle; test side only).
+
+Chooses each head's bias b_h (learned mode) or constant c_h (calibrated mode)
+so that about the target fraction of complete blocks passes the oracle's
+screen, then re-draws the noise of any block whose bound lies within `margin`
+of a threshold of its group, until none does. With that margin, the admitted
+sets are decided identically by any implementation whose bound and threshold
+agree with the oracle's to better than `margin`.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import oracle.eta_oracle as E
+import workloads as W
+
+BLOCK = 64
+
+
+def _bounds(wl, mu, R):
+    """ub[n][h][j] for complete blocks (NaN elsewhere), tau offsets per (n, h)."""
+    N, HQ, D = wl.q.shape
+    G = wl.group
+    s = 1.0 / math.sqrt(D)
+    qf = E.upcast(wl.q, wl.kv_dtype)
+    ub = np.full((N, HQ, wl.max_blocks), np.nan)
+    for n in range(N):
+        nfull = int(wl.seq_lens[n]) // BLOCK
+        pages = wl.block_table[n, :nfull]
+        for h in range(HQ):
+            g = h // G
+            ub[n, h, :nfull] = E.block_bound(qf[n, h], mu[pages, g], R[pages, g], s)
+    if wl.tau_mode == "learned":
+        off = np.einsum("nhd,hd->nh", qf, wl.w.astype(np.float64)) - wl.a
+    else:
+        off = np.full((N, HQ), -wl.a)
+    return ub, off
+
+
+def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None):
+    """Set wl.bias in place; returns the oracle summaries of the final cache."""
+    mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
+        if summaries is None else summaries
+    ub, off = _bounds(wl, mu, R)
+    HQ = wl.h_q
+    bias = np.zeros(HQ, dtype=np.float32)
+    for h in range(HQ):
+        t = float(wl.target_density[h])
+        x = (ub[:, h, :] - off[:, h, None]).ravel()  # admitted iff x >= bias
+        x = np.sort(x[~np.isnan(x)])[::-1]
+        if t >= 1.0:
+            bias[h] = -np.inf
+            continue
+        k = int(round(t * len(x)))
+        k = min(max(k, 1), len(x) - 1)
+        bias[h] = np.float32(0.5 * (x[k - 1] + x[k]))
+    wl.bias = bias
+    for _ in range(max_rounds):
+        tau = off + bias.astype(np.float64)[None, :]
+        close = np.abs(ub - tau[:, :, None]) < margin
+        bad = set()
+        G = wl.group
+        for n, h, j in zip(*np.nonzero(close)):
+            bad.add((int(n), int(h) // G, int(j)))
+        if not bad:
+            return mu, R
+        W.redraw_blocks(wl, bad)
+        for (n, g, j) in bad:
+            page = int(wl.block_table[n, j])
+            kb = E.upcast(wl.k_pages[page, g], wl.kv_dtype)
+            m, r = E.block_summary(kb)
+            mu[page, g] = m
+            R[page, g] = r
+        ub, off = _bounds(wl, mu, R)
+    raise RuntimeError("margin enforcement did not converge")
+
+
+def densities(res, wl):
+    """Per-head admitted fraction of blocks, and per-(n,g) union fraction."""
+    nblk = np.array([wl.nblk(n) for n in range(wl.n_seqs)], dtype=np.float64)
+    per_head = res.per_head / nblk[:, None]
+    union = res.union / nblk[:, None]
+    return per_head, union

@@ -1,0 +1,68 @@
+"""Planted mistakes in a copy of the oracle must each break at least one pin.
+
+Every mutant is a plausible slip (a dropped term, a flipped sign, a wrong
+index or rounding mode). The copy is built from the oracle's source text on
+the CPU; the real oracle module is never modified.
+"""
+import importlib.util
+import itertools
+import os
+
+import pytest
+
+import pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "eta_oracle.py")
+_count = itertools.count()
+
+MUTANTS = {
+    "bound_drops_radius_term": ("return scale * (mu @ q + nq * R)", "return scale * (mu @ q)"),
+    "bound_uses_squared_norm": ("return scale * (mu @ q + nq * R)", "return scale * (mu @ q + nq * nq * R)"),
+    "radius_about_unrounded_mean": ("diff = kb - mu[:, None, :]", "diff = kb - mean[:, None, :]"),
+    "centroid_rounded_to_fp32": ("mu16 = mean.astype(np.float16).astype(np.float64)",
+                                 "mu16 = mean.astype(np.float32).astype(np.float64)"),
+    "gate_sign_flipped": ("return S * sigmoid(beta * (S - tau))", "return S * sigmoid(beta * (tau - S))"),
+    "gate_additive": ("return S * sigmoid(beta * (S - tau))", "return S + sigmoid(beta * (S - tau)) - 1.0"),
+    "threshold_adds_a": ("+ float(b_h) - float(a)", "+ float(b_h) + float(a)"),
+    "group_index_modulo": ("g = h // G", "g = h % HKV"),
+    "tail_block_dropped": ("    if seq_len % BLOCK:\n        adm[nfull] = True\n", ""),
+    "lwb_counts_from_start": ("adm[max(0, nfull - lwb):nfull] = True", "adm[:min(lwb, nfull)] = True"),
+    "rescue_takes_last_max": ("adm[int(np.argmax(ub))] = True",
+                              "adm[len(ub) - 1 - int(np.argmax(ub[::-1]))] = True"),
+    "rescue_missing": ("    if not adm.any():\n        adm[int(np.argmax(ub))] = True\n        rescued = True\n", ""),
+    "no_logit_scale": ("scale = 1.0 / math.sqrt(D)", "scale = 1.0"),
+    "output_not_normalised": ("    return num / den\n", "    return num\n"),
+    "tail_mask_off_by_one": ("        keep = tok < T\n        S = scale", "        keep = tok <= T\n        S = scale"),
+    "union_counts_heads": ("union[n, g] = admitted[n, g * G:(g + 1) * G, :nblk].any(axis=0).sum()",
+                           "union[n, g] = admitted[n, g * G:(g + 1) * G, :nblk].sum()"),
+    "token_count_ignores_tail": ("width = np.minimum(BLOCK, T - BLOCK * np.arange(nblk))",
+                                 "width = np.full(nblk, BLOCK)"),
+    "strict_bound_comparison": ("adm[:nfull] = ~(ub < tau)", "adm[:nfull] = ub > tau + 1e-3"),
+}
+
+
+def load_mutant(name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) >= 1, f"mutation target for {name} not found"
+    src = src.replace(old, new)
+    mod_name = f"_oracle_mutant_{next(_count)}"
+    spec = importlib.util.spec_from_loader(mod_name, loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    exec(compile(src, f"<{name}>", "exec"), mod.__dict__)
+    return mod
+
+
+def caught(mod):
+    for pin in pins.ALL_PINS:
+        try:
+            pin(mod)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            return pin.__name__, repr(e)[:200]
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    res = caught(load_mutant(name))
+    assert res is not None, f"mutant {name} passed every pin"
