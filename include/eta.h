@@ -1,0 +1,175 @@
+/*
+ * eta.h - C ABI of the ETA (Elastic Threshold Attention) decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Method: "Elastic Threshold Attention: Learned Contextual Sparsity for
+ * Long-Context Decoding" (paperpeel.com/paper/2609.20888). One decode step,
+ * for every sequence n and query head h (KV head g = h / G, G = H_Q / H_KV):
+ *   threshold  tau~ = w_h . q + b_h - a   (learned, Sections 1 and D.1)
+ *              tau~ = c_h - a             (calibrated, Section 4.7)
+ *   screen     every complete 64-token block whose bound
+ *              s (q . mu^ + ||q|| R^) is not below tau~ is admitted
+ *              (Sections 3, 3.1, F.1); the partial last block and the `lwb`
+ *              most recent complete blocks always are (Section 4.8, F.4); if
+ *              nothing is admitted, the block with the largest bound is
+ *              (top-1 rescue, Section 3.2 and F.4);
+ *   attention  over the tokens t < T of admitted blocks:
+ *              S = s q.k,  S~ = S * sigmoid(beta (S - tau~)),
+ *              o = sum exp(S~) v / sum exp(S~)   (Sections 2.2, E.3, G.1),
+ *   with s = 1/sqrt(d). A KV block is read once for all G heads that admit
+ *   it; each head accumulates only the blocks it admitted (Section 4.3, F.1).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless the comment says "host".
+ *   - The caller owns all memory. The library allocates nothing and keeps no
+ *     state between calls apart from a per-device launch-geometry cache.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
+ *     stream) except eta_stats, which synchronises the stream.
+ *   - Host-checkable arguments are validated before any device work; a
+ *     failing call returns a negative eta_status and launches nothing.
+ *     Device-resident values (sequence lengths, block-table entries) are
+ *     checked by the kernels: offending blocks are skipped, and eta_stats
+ *     reports ETA_ERR_DEVICE_DATA for the decode step that met them.
+ *   - Nothing aborts and no C++ exception crosses this interface.
+ *   - Calls that share a workspace or a cache region must be ordered on one
+ *     stream (or by the caller's events); the library is re-entrant otherwise.
+ */
+#ifndef ETA_H_
+#define ETA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* eta_stream_t; /* same type as hipStream_t */
+
+typedef enum {
+  ETA_OK = 0,
+  ETA_ERR_INVALID_ARGUMENT = -1,   /* bad pointer, size, alignment or value */
+  ETA_ERR_UNSUPPORTED = -2,        /* valid but not implemented (block size, head dim, group size) */
+  ETA_ERR_WORKSPACE_TOO_SMALL = -3,
+  ETA_ERR_HIP = -4,                /* a HIP runtime call failed */
+  ETA_ERR_DEVICE_DATA = -5         /* a kernel met an out-of-range length or page id */
+} eta_status;
+
+enum { ETA_F32 = 0, ETA_BF16 = 1 };                 /* K/V/q element type */
+enum { ETA_TAU_LEARNED = 0, ETA_TAU_CALIBRATED = 1 }; /* threshold mode */
+enum { ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
+
+/* Paged KV cache plus its per-block records (caller-owned device buffers).
+ *   k_pages, v_pages : [num_pages][num_kv_heads][block_size][head_dim] of
+ *                      kv_dtype (bf16 as raw 16-bit patterns), 16-byte aligned.
+ *   mu               : [num_pages][num_kv_heads][head_dim] float16 bit patterns,
+ *                      the block centroid rounded to nearest even (Section 3.2,
+ *                      F.1), 16-byte aligned.
+ *   radius           : [num_pages][num_kv_heads] float32, an upper bound on the
+ *                      distance of every key of the block to mu (rounded up;
+ *                      +inf for blocks holding non-finite keys), 4-byte aligned.
+ * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
+typedef struct {
+  int kv_dtype;
+  int head_dim;
+  int num_kv_heads;
+  int block_size;
+  int num_pages;
+  void* k_pages;
+  void* v_pages;
+  uint16_t* mu;
+  float* radius;
+} eta_cache;
+
+/* Sequences of a batch.
+ *   seq_lens    : [num_seqs] int32 token counts, 1 <= T <= block_size*max_blocks_per_seq.
+ *   block_table : [num_seqs][max_blocks_per_seq] int32; entry j of row n is the
+ *                 page holding tokens [64j, 64j+64) of sequence n; entries past
+ *                 the last block are never read.                            */
+typedef struct {
+  int num_seqs;
+  int max_blocks_per_seq;
+  const int32_t* seq_lens;
+  const int32_t* block_table;
+} eta_seqs;
+
+/* Build the record (mu, radius) of every complete block of every sequence and
+ * KV head, reading the keys in k_pages. Idempotent; records of partial blocks
+ * are left untouched. (Section 3.2 and F.1: metadata per KV head, built from the
+ * cache; Section 4.8: built during prefill.) Rows of blocks with an
+ * out-of-range page id are skipped. */
+eta_status eta_build_block_summaries(const eta_cache* cache, const eta_seqs* seqs,
+                                     eta_stream_t stream);
+
+/* Append one token per sequence: k_new, v_new are [num_seqs][num_kv_heads][head_dim]
+ * of kv_dtype (16-byte aligned). seqs->seq_lens holds the lengths BEFORE the
+ * append; the token goes to row T%64 of page block_table[n][T/64], which the
+ * caller has assigned. When that fills the block (T%64 == 63) its record is
+ * built in the same launch, bit-identical to eta_build_block_summaries. The
+ * caller increments seq_lens afterwards. Sequences with T >= 64*max_blocks or
+ * an out-of-range page id are skipped. */
+eta_status eta_append_kv(const eta_cache* cache, const eta_seqs* seqs, const void* k_new,
+                         const void* v_new, eta_stream_t stream);
+
+/* Bytes of device workspace eta_decode needs for these sizes (0 if they are
+ * invalid or unsupported). The workspace carries the screen's compacted block
+ * lists and counts, the split partial results and the statistics; it must be
+ * 256-byte aligned and may be reused by later calls of the same or smaller
+ * size. */
+size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_blocks_per_seq,
+                                 int num_q_heads);
+
+/* One decode step: out[n][h][:] (float32, [num_seqs][num_q_heads][head_dim])
+ * for every sequence and query head.
+ *   q          [num_seqs][num_q_heads][head_dim] of kv_dtype, 16-byte aligned.
+ *   tau_mode   ETA_TAU_LEARNED: w [num_q_heads][head_dim] float32 and
+ *              b_or_c [num_q_heads] float32 (bias b_h) are required;
+ *              ETA_TAU_CALIBRATED: w is ignored, b_or_c holds c_h. c_h = -inf
+ *              admits every block and leaves logits unfiltered (plain softmax
+ *              attention: the dense comparator).
+ *   a          threshold adjustment (tau~ = tau - a), finite.
+ *   beta       gate sharpness, finite and > 0 (5 at inference, B.1).
+ *   lwb        number of most recent complete blocks always admitted, >= 0.
+ *   block_size must equal cache->block_size (64).
+ * num_q_heads must be a multiple of num_kv_heads with G = num_q_heads /
+ * num_kv_heads in {1, 2, 4, 8}. Equivalent to the three phases below in order. */
+eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* q,
+                      int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
+                      float a, float beta, int lwb, int block_size, float* out,
+                      void* workspace, size_t ws_bytes, eta_stream_t stream);
+
+/* One phase of eta_decode with the same arguments, for callers that overlap or
+ * time the phases: ETA_PHASE_SCREEN (thresholds, bound screen, compaction of
+ * admitted block ids, rescue, counts), ETA_PHASE_ATTEND (split flash-decode over
+ * the compacted lists; Section 3.2 and F.3 chunked decoding), ETA_PHASE_MERGE
+ * (associative merge of the split partials into out). Phases must run in this
+ * order on one workspace; ATTEND and MERGE read what the previous phase wrote. */
+eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* seqs,
+                            const void* q, int num_q_heads, int tau_mode, const float* w,
+                            const float* b_or_c, float a, float beta, int lwb, int block_size,
+                            float* out, void* workspace, size_t ws_bytes, eta_stream_t stream);
+
+/* Synchronise `stream`, then copy the counts of the last eta_decode on this
+ * workspace to host memory (Section F.4 validates exactly these integers):
+ *   admitted_per_head [num_seqs][num_q_heads] int32  blocks admitted per head
+ *   union_per_kv      [num_seqs][num_kv_heads] int32 blocks loaded per KV head
+ *   tokens_per_head   [num_seqs][num_q_heads] int64  attended tokens (nullable)
+ *   rescued           [num_seqs][num_q_heads] uint8  1 if top-1 rescue fired (nullable)
+ *   admitted_bitmap   [num_seqs][num_q_heads][ceil(max_blocks_per_seq/32)]
+ *                     uint32, bit j%32 of word j/32 = block j admitted (nullable)
+ * All output pointers are host pointers. Returns ETA_ERR_DEVICE_DATA (after
+ * filling the outputs) if that decode met invalid lengths or page ids, and
+ * ETA_ERR_INVALID_ARGUMENT if the sizes do not match that decode. */
+eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,
+                     int num_kv_heads, int32_t* admitted_per_head, int32_t* union_per_kv,
+                     int64_t* tokens_per_head, uint8_t* rescued, uint32_t* admitted_bitmap,
+                     eta_stream_t stream);
+
+/* Static text for a status code. */
+const char* eta_status_string(eta_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETA_H_ */

@@ -1,0 +1,210 @@
+"""ETA (Elastic Threshold Attention) long-context decode for AMD MI355X.
+
+Thin Python binding over libeta.so (C ABI in include/eta.h). PyTorch tensors
+provide device memory and the HIP stream; every step of the decode runs in the
+library's HIP kernels. Functions here only check tensor placement/dtypes and
+pass pointers.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import (  # noqa: F401
+    ETA_BF16, ETA_F32, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN, ETA_TAU_CALIBRATED,
+    ETA_TAU_LEARNED, EtaError, status_string,
+)
+
+BLOCK = 64
+_KV_DTYPES = {torch.bfloat16: ETA_BF16, torch.float32: ETA_F32}
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != _lib.ETA_OK:
+        raise EtaError(status, what)
+
+
+def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclasses.dataclass
+class Cache:
+    """Paged KV cache [num_pages][H_KV][64][d] plus per-block records."""
+    k_pages: torch.Tensor
+    v_pages: torch.Tensor
+    mu: torch.Tensor       # float16 [num_pages][H_KV][d]
+    radius: torch.Tensor   # float32 [num_pages][H_KV]
+
+    def __post_init__(self):
+        _need(self.k_pages, "k_pages")
+        dev = self.k_pages.device
+        if self.k_pages.dtype not in _KV_DTYPES:
+            raise TypeError("k_pages must be bfloat16 or float32")
+        _need(self.v_pages, "v_pages", self.k_pages.dtype, dev)
+        _need(self.mu, "mu", torch.float16, dev)
+        _need(self.radius, "radius", torch.float32, dev)
+        if self.k_pages.dim() != 4 or self.k_pages.shape != self.v_pages.shape:
+            raise ValueError("k_pages/v_pages must be [num_pages][H_KV][64][d]")
+        P, H, B, D = self.k_pages.shape
+        if tuple(self.mu.shape) != (P, H, D) or tuple(self.radius.shape) != (P, H):
+            raise ValueError("mu must be [num_pages][H_KV][d] and radius [num_pages][H_KV]")
+
+    @classmethod
+    def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda"):
+        k = torch.zeros(num_pages, num_kv_heads, BLOCK, head_dim, dtype=dtype, device=device)
+        v = torch.zeros_like(k)
+        mu = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.float16, device=device)
+        r = torch.zeros(num_pages, num_kv_heads, dtype=torch.float32, device=device)
+        return cls(k, v, mu, r)
+
+    @property
+    def kv_dtype(self) -> int:
+        return _KV_DTYPES[self.k_pages.dtype]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k_pages.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k_pages.shape[3]
+
+    def c_struct(self) -> _lib.EtaCacheC:
+        P, H, B, D = self.k_pages.shape
+        return _lib.EtaCacheC(self.kv_dtype, D, H, B, P, _ptr(self.k_pages), _ptr(self.v_pages),
+                              _ptr(self.mu), _ptr(self.radius))
+
+
+def _seqs(seq_lens: torch.Tensor, block_table: torch.Tensor, device) -> _lib.EtaSeqsC:
+    _need(seq_lens, "seq_lens", torch.int32, device)
+    _need(block_table, "block_table", torch.int32, device)
+    if block_table.dim() != 2 or block_table.shape[0] != seq_lens.shape[0]:
+        raise ValueError("block_table must be [num_seqs][max_blocks_per_seq]")
+    return _lib.EtaSeqsC(block_table.shape[0], block_table.shape[1], _ptr(seq_lens), _ptr(block_table))
+
+
+def build_block_summaries(cache: Cache, seq_lens, block_table, stream=None) -> None:
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, cache.k_pages.device)
+    _check(_lib.lib().eta_build_block_summaries(ctypes.byref(c), ctypes.byref(s), _stream(stream)),
+           "eta_build_block_summaries")
+
+
+def append_kv(cache: Cache, seq_lens, block_table, k_new, v_new, stream=None) -> None:
+    dev = cache.k_pages.device
+    _need(k_new, "k_new", cache.k_pages.dtype, dev)
+    _need(v_new, "v_new", cache.k_pages.dtype, dev)
+    N = seq_lens.shape[0]
+    if tuple(k_new.shape) != (N, cache.num_kv_heads, cache.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [num_seqs][H_KV][d]")
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    _check(_lib.lib().eta_append_kv(ctypes.byref(c), ctypes.byref(s), _ptr(k_new), _ptr(v_new),
+                                    _stream(stream)), "eta_append_kv")
+
+
+def decode_workspace_size(cache: Cache, num_seqs: int, max_blocks_per_seq: int, num_q_heads: int) -> int:
+    c = cache.c_struct()
+    return int(_lib.lib().eta_decode_workspace_size(ctypes.byref(c), num_seqs, max_blocks_per_seq,
+                                                    num_q_heads))
+
+
+def alloc_workspace(cache: Cache, num_seqs: int, max_blocks_per_seq: int, num_q_heads: int) -> torch.Tensor:
+    n = decode_workspace_size(cache, num_seqs, max_blocks_per_seq, num_q_heads)
+    if n == 0:
+        raise EtaError(_lib.ETA_ERR_UNSUPPORTED, "eta_decode_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=cache.k_pages.device)  # 256-byte aligned
+
+
+def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None, a: float = 0.0,
+           beta: float = 5.0, lwb: int = 0, out=None, workspace=None, phase: Optional[int] = None,
+           stream=None) -> torch.Tensor:
+    """One ETA decode step; returns out [num_seqs][H_Q][d] float32.
+    With `phase` set, runs only that phase (screen, attend or merge)."""
+    dev = cache.k_pages.device
+    _need(q, "q", cache.k_pages.dtype, dev)
+    N, HQ, D = q.shape
+    _need(b_or_c, "b_or_c", torch.float32, dev)
+    if w is not None:
+        _need(w, "w", torch.float32, dev)
+    if out is None:
+        out = torch.empty(N, HQ, D, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    if workspace is None:
+        workspace = alloc_workspace(cache, N, block_table.shape[1], HQ)
+    _need(workspace, "workspace", torch.uint8, dev)
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    args = (ctypes.byref(c), ctypes.byref(s), _ptr(q), HQ, int(tau_mode), _ptr(w), _ptr(b_or_c),
+            float(a), float(beta), int(lwb), BLOCK, _ptr(out), _ptr(workspace), workspace.numel(),
+            _stream(stream))
+    if phase is None:
+        _check(_lib.lib().eta_decode(*args), "eta_decode")
+    else:
+        _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
+    return out
+
+
+@dataclasses.dataclass
+class Stats:
+    admitted_per_head: np.ndarray   # int32 [N][H_Q]
+    union_per_kv: np.ndarray        # int32 [N][H_KV]
+    tokens_per_head: np.ndarray     # int64 [N][H_Q]
+    rescued: np.ndarray             # uint8 [N][H_Q]
+    bitmap: Optional[np.ndarray]    # uint32 [N][H_Q][ceil(MB/32)]
+    status: int
+
+    def admitted(self, max_blocks: int) -> np.ndarray:
+        """bool [N][H_Q][max_blocks] from the bitmap."""
+        b = np.unpackbits(self.bitmap.view(np.uint8), axis=-1, bitorder="little")
+        return b[..., :max_blocks].astype(bool)
+
+
+def stats(workspace: torch.Tensor, num_seqs: int, max_blocks_per_seq: int, num_q_heads: int,
+          num_kv_heads: int, bitmap: bool = True, stream=None, check: bool = True) -> Stats:
+    a = np.zeros((num_seqs, num_q_heads), np.int32)
+    u = np.zeros((num_seqs, num_kv_heads), np.int32)
+    t = np.zeros((num_seqs, num_q_heads), np.int64)
+    r = np.zeros((num_seqs, num_q_heads), np.uint8)
+    bm = np.zeros((num_seqs, num_q_heads, (max_blocks_per_seq + 31) // 32), np.uint32) if bitmap else None
+    st = _lib.lib().eta_stats(_ptr(workspace), num_seqs, max_blocks_per_seq, num_q_heads, num_kv_heads,
+                              a.ctypes.data, u.ctypes.data, t.ctypes.data, r.ctypes.data,
+                              None if bm is None else bm.ctypes.data, _stream(stream))
+    if check and st not in (_lib.ETA_OK,):
+        raise EtaError(st, "eta_stats")
+    return Stats(a, u, t, r, bm, st)
+
+
+# ----------------------------------------------------------------------------- uploads
+def bf16_tensor_from_bits(bits: np.ndarray, device) -> torch.Tensor:
+    """Upload an array of bfloat16 bit patterns (uint16) as a torch.bfloat16 tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def upload(arr: np.ndarray, kv_dtype: str, device) -> torch.Tensor:
+    if kv_dtype == "bf16":
+        return bf16_tensor_from_bits(arr, device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)

@@ -1,0 +1,433 @@
+// Attend and merge phases of one decode step: split flash-decode over the
+// compacted lists of admitted blocks, then the associative merge of the splits.
+//
+// "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888):
+//   S = s q.k, S~ = S * sigmoid(beta (S - tau~)), o = sum e^{S~} v / sum e^{S~}
+//   over the tokens of the admitted blocks (Sections 1, 2.2, E.3, G.1); a block
+//   is read from HBM once for the G heads of its group and each head updates
+//   only with the blocks it admitted (Section 4.3, F.1); partial last block
+//   masked past the sequence end (F.4); the sequence split into parts merged by
+//   an associative online-softmax reduction (Section 3.2, F.2, F.3).
+//
+// Work split: the screen produced, per (sequence, KV head), a contiguous list
+// of admitted blocks. Their concatenation (Utot entries) is cut into W' equal
+// ranges, one per attend workgroup (W' = min(grid, Utot), grid sized to fill
+// every CU once), so every workgroup streams the same number of 32 KB tiles
+// whatever the density or the length mix. A range that spans several
+// (sequence, KV head) segments emits one partial per segment.
+//
+// Inside a workgroup the four wavefronts take every fourth entry. A wavefront
+// owns a whole tile: 16-byte loads of one 64 x d tile (lane (r, cb) holds rows
+// RPI*i + r, 8 bf16 columns), keys consumed by v_dot2 bf16 products into
+// per-lane partial logits, finished by a transposing DPP reduction that leaves
+// one token's logit per lane. The gate and the online softmax run per lane in
+// float32 (running max per row of lanes); the weights go through 1 KB of LDS
+// to the lanes holding the matching value rows. V of tile i streams while the
+// logits of tile i are computed, K of tile i+1 while the values of tile i are
+// accumulated. No float atomics: results are bitwise reproducible.
+#include "eta_device.h"
+
+namespace eta {
+namespace {
+
+struct AttendArgs {
+  CacheView c;
+  SeqView s;
+  DecodeParams p;
+  Dims d;
+  Ws ws;
+};
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1))) void k_attend(AttendArgs A) {
+  using L = TileLayout<T::kBytes, D>;
+  constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
+  constexpr bool kBf16 = T::kBytes == 2;
+  using St = typename T::Stored;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane / LPR, cb = lane % LPR;
+  const int k = blockIdx.x;
+  const int Wp = A.ws.glob[kGlobWeff];
+  if (k >= Wp) return;
+  const int64_t Utot = A.ws.glob[kGlobUtot];
+  int64_t lo = (int64_t)k * Utot / Wp;
+  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  int s = A.ws.wg_seg[k];
+  const int HKV = A.d.HKV, HQ = A.d.HQ, MB = A.d.MB;
+  const float scale = A.p.scale, beta = A.p.beta;
+
+  __shared__ __attribute__((aligned(16))) float p_lds[4][G][64];
+  __shared__ float ml_lds[4][G][2];
+  __shared__ float acc_lds[4][G][D];
+
+  // lane offset (elements) of load (i=0, c) inside a tile
+  int loff[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
+
+  while (lo < hi) {
+    int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
+    while (lo >= (int64_t)P + Us) {
+      ++s;
+      P = A.ws.seg_P[s];
+      Us = A.ws.seg_U[s];
+    }
+    const int e0 = (int)(lo - P);
+    const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
+    const int n = s / HKV, g = s % HKV;
+    const int seq_len = A.s.lens[n];
+    const int nfull = seq_len / kBlock;
+    const int rem = seq_len - nfull * kBlock;
+
+    // queries of the group at this lane's columns, and thresholds
+    uint32_t qb[G][CPL * 4];  // packed bf16 pairs (bf16 path)
+    float qf[G][EPL];         // float32 path
+    float tau[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const St* qrow = (const St*)A.p.q + ((int64_t)n * HQ + g * G + h) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+        if constexpr (kBf16) {
+          qb[h][c * 4 + 0] = v.x; qb[h][c * 4 + 1] = v.y; qb[h][c * 4 + 2] = v.z; qb[h][c * 4 + 3] = v.w;
+        } else {
+          qf[h][c * 4 + 0] = __uint_as_float(v.x); qf[h][c * 4 + 1] = __uint_as_float(v.y);
+          qf[h][c * 4 + 2] = __uint_as_float(v.z); qf[h][c * 4 + 3] = __uint_as_float(v.w);
+        }
+      }
+      tau[h] = A.ws.tau[(int64_t)n * HQ + g * G + h];
+    }
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -__builtin_inff();
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+
+    const int span = e1 - e0;
+    const int cnt = span > wave ? (span - wave + 3) / 4 : 0;
+    const int2* list = A.ws.seg_list + (int64_t)s * MB + e0 + wave;
+    const St* kbase = (const St*)A.c.k;
+    const St* vbase = (const St*)A.c.v;
+
+    for (int b0 = 0; b0 < cnt; b0 += 64) {
+      const int bc = cnt - b0 < 64 ? cnt - b0 : 64;
+      int2 ev = make_int2(0, 0);
+      if (lane < bc) ev = list[4 * (b0 + lane)];
+      int page = __builtin_amdgcn_readlane(ev.x, 0);
+      int jm = __builtin_amdgcn_readlane(ev.y, 0);
+
+      uint4 kr[NI][CPL], vr[NI][CPL];
+      {
+        const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
+      }
+      for (int it = 0; it < bc; ++it) {
+        const int cur_page = page, cur_jm = jm;
+        {
+          const St* vt = vbase + ((int64_t)cur_page * HKV + g) * (kBlock * D);
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) vr[i][c] = *(const uint4*)(vt + loff[c] + i * RPI * D);
+        }
+        if (it + 1 < bc) {
+          page = __builtin_amdgcn_readlane(ev.x, it + 1);
+          jm = __builtin_amdgcn_readlane(ev.y, it + 1);
+        }
+        const uint32_t hmask = (uint32_t)cur_jm & 0xffu;
+        const int j = cur_jm >> 8;
+        const bool tail = (j == nfull);  // only the partial last block has j == nfull
+        const int tok = RPI * cb + r;     // token whose logit this lane finishes
+
+        // ---- logits, gate, online softmax per admitted head
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          if (!(hmask & (1u << h))) continue;
+          float pd[NI];
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+            float a = 0.f;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const uint32_t kw[4] = {kr[i][c].x, kr[i][c].y, kr[i][c].z, kr[i][c].w};
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                if constexpr (kBf16) {
+                  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qb[h][c * 4 + w]),
+                                                      __builtin_bit_cast(bf16x2_t, kw[w]), a, false);
+                } else {
+                  a = fmaf(qf[h][c * 4 + w], __uint_as_float(kw[w]), a);
+                }
+              }
+            }
+            pd[i] = a;
+          }
+          transpose_reduce<LPR>(pd, lane);
+          const float S = pd[0] * scale;
+          const float x = beta * (S - tau[h]);
+          const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
+          float st = S * sg;
+          if (tail && tok >= rem) st = -__builtin_inff();
+          const float mt = group_max<LPR>(st);
+          const float mnew = fmaxf(m[h], mt);
+          const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
+          const float alpha = fast_exp(m[h] - muse);
+          const float p = fast_exp(st - muse);
+          l[h] = fmaf(l[h], alpha, p);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          m[h] = mnew;
+          p_lds[wave][h][lane] = p;
+        }
+
+        // ---- K of the next tile streams while the values are accumulated
+        if (it + 1 < bc) {
+          const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
+        }
+        if (tail) {  // junk rows past the end must not reach the sums (0 * NaN)
+#pragma unroll
+          for (int i = 0; i < NI; ++i)
+            if (RPI * i + r >= rem)
+#pragma unroll
+              for (int c = 0; c < CPL; ++c) vr[i][c] = make_uint4(0, 0, 0, 0);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+
+        // ---- acc[h] += p_h(token) * v(token)
+#pragma unroll
+        for (int i4 = 0; i4 < NI / 4; ++i4) {
+          float4 pw[G];
+#pragma unroll
+          for (int h = 0; h < G; ++h)
+            if (hmask & (1u << h)) pw[h] = *(const float4*)&p_lds[wave][h][r * LPR + 4 * i4];
+#pragma unroll
+          for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * i4 + ii;
+            float vf[EPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const uint32_t vw[4] = {vr[i][c].x, vr[i][c].y, vr[i][c].z, vr[i][c].w};
+              if constexpr (kBf16) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                  vf[c * 8 + 2 * w] = bf16_lo(vw[w]);
+                  vf[c * 8 + 2 * w + 1] = bf16_hi(vw[w]);
+                }
+              } else {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) vf[c * 4 + w] = __uint_as_float(vw[w]);
+              }
+            }
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+              if (!(hmask & (1u << h))) continue;
+              const float pv = ii == 0 ? pw[h].x : ii == 1 ? pw[h].y : ii == 2 ? pw[h].z : pw[h].w;
+#pragma unroll
+              for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
+            }
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+
+    // ---- merge the rows of lanes, then the four wavefronts, write one partial
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float lr = group_sum<LPR>(l[h]);
+      float M = m[h];
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, shfl_xor_f(M, o));
+      const float sc = m[h] == -__builtin_inff() ? 0.f : fast_exp(m[h] - M);
+      float lw = sc * lr;
+#pragma unroll
+      for (int o = LPR; o < 64; o <<= 1) lw += shfl_xor_f(lw, o);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float a = sc * acc[h][e];
+#pragma unroll
+        for (int o = LPR; o < 64; o <<= 1) a += shfl_xor_f(a, o);
+        acc[h][e] = a;
+      }
+      if (r == 0) {
+#pragma unroll
+        for (int c = 0; c < CPL; ++c)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc_lds[wave][h][L::col(c, cb) + e] = acc[h][c * EPC + e];
+      }
+      if (lane == 0) {
+        ml_lds[wave][h][0] = M;
+        ml_lds[wave][h][1] = lw;
+      }
+    }
+    __syncthreads();
+    const int64_t piece = (int64_t)k + s;
+    for (int h = wave; h < G; h += 4) {
+      float Mw[4], M = -__builtin_inff();
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        Mw[w] = ml_lds[w][h][0];
+        M = fmaxf(M, Mw[w]);
+      }
+      float sc[4], Lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        sc[w] = Mw[w] == -__builtin_inff() ? 0.f : fast_exp(Mw[w] - M);
+        Lsum = fmaf(sc[w], ml_lds[w][h][1], Lsum);
+      }
+      float* pa = A.ws.part_acc + (piece * G + h) * D;
+      for (int dd = lane; dd < D; dd += 64) {
+        float a = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) a = fmaf(sc[w], acc_lds[w][h][dd], a);
+        pa[dd] = a;
+      }
+      if (lane == 0) {
+        A.ws.part_ml[(piece * G + h) * 2] = M;
+        A.ws.part_ml[(piece * G + h) * 2 + 1] = Lsum;
+      }
+    }
+    __syncthreads();
+    lo = (int64_t)P + e1;
+    ++s;
+  }
+}
+
+// ---------------------------------------------------------------- merge
+struct MergeArgs {
+  Dims d;
+  Ws ws;
+  float* out;
+};
+
+template <int D, int G>
+__global__ __launch_bounds__(64) void k_merge(MergeArgs A) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x;
+  const int nh = blockIdx.x;
+  const int HQ = A.d.HQ;
+  const int n = nh / HQ, h = nh % HQ;
+  const int g = h / G, hl = h % G;
+  const int s = n * A.d.HKV + g;
+  const int plo = A.ws.seg_plo[s], phi = A.ws.seg_phi[s];
+  float M = -__builtin_inff();
+  for (int p = plo + lane; p <= phi; p += 64) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
+  float lsum = 0.f, acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int p0 = plo; p0 <= phi; p0 += 64) {
+    const int p = p0 + lane;
+    float wgt = 0.f;
+    if (p <= phi) {
+      const float mp = A.ws.part_ml[((int64_t)p * G + hl) * 2];
+      const float lp = A.ws.part_ml[((int64_t)p * G + hl) * 2 + 1];
+      wgt = mp == -__builtin_inff() ? 0.f : fast_exp(mp - M);
+      lsum = fmaf(wgt, lp, lsum);
+    }
+    const int nb = phi - p0 + 1 < 64 ? phi - p0 + 1 : 64;
+    const float* pa = A.ws.part_acc + ((int64_t)p0 * G + hl) * D + lane * CPL;
+#pragma unroll 8
+    for (int q = 0; q < nb; ++q) {
+      const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), q));
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wq, pa[(int64_t)q * G * D + c], acc[c]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) lsum += shfl_xor_f(lsum, o);
+  float* o_ = A.out + ((int64_t)n * HQ + h) * D + lane * CPL;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o_[c] = lsum > 0.f ? acc[c] / lsum : __builtin_nanf("");
+}
+
+template <typename T, int D, int G>
+hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                       const Ws& ws, int W, hipStream_t st) {
+  AttendArgs a{c, s, p, d, ws};
+  hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(kAttendThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t attend_g(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                    const Ws& ws, int W, hipStream_t st) {
+  switch (d.G) {
+    case 1: return attend_impl<T, D, 1>(c, s, p, d, ws, W, st);
+    case 2: return attend_impl<T, D, 2>(c, s, p, d, ws, W, st);
+    case 4: return attend_impl<T, D, 4>(c, s, p, d, ws, W, st);
+    case 8: return attend_impl<T, D, 8>(c, s, p, d, ws, W, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D, int G>
+int occupancy_impl() {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G>),
+                                                   kAttendThreads, 0) != hipSuccess)
+    return 1;
+  return nb > 0 ? nb : 1;
+}
+
+template <typename T, int D>
+int occupancy_g(int G) {
+  switch (G) {
+    case 1: return occupancy_impl<T, D, 1>();
+    case 2: return occupancy_impl<T, D, 2>();
+    case 4: return occupancy_impl<T, D, 4>();
+    case 8: return occupancy_impl<T, D, 8>();
+  }
+  return 1;
+}
+
+template <int D, int G>
+hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
+  MergeArgs a{d, ws, p.out};
+  hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t merge_g(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
+  switch (d.G) {
+    case 1: return merge_impl<D, 1>(d, p, ws, st);
+    case 2: return merge_impl<D, 2>(d, p, ws, st);
+    case 4: return merge_impl<D, 4>(d, p, ws, st);
+    case 8: return merge_impl<D, 8>(d, p, ws, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                         const Ws& ws, int W, hipStream_t st) {
+  if (c.kv_dtype == 1) return d.D == 128 ? attend_g<Bf16, 128>(c, s, p, d, ws, W, st) : attend_g<Bf16, 64>(c, s, p, d, ws, W, st);
+  return d.D == 128 ? attend_g<F32, 128>(c, s, p, d, ws, W, st) : attend_g<F32, 64>(c, s, p, d, ws, W, st);
+}
+
+hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
+  return d.D == 128 ? merge_g<128>(d, p, ws, st) : merge_g<64>(d, p, ws, st);
+}
+
+int attend_wgs_per_cu(int kv_dtype, int D, int G) {
+  if (kv_dtype == 1) return D == 128 ? occupancy_g<Bf16, 128>(G) : occupancy_g<Bf16, 64>(G);
+  return D == 128 ? occupancy_g<F32, 128>(G) : occupancy_g<F32, 64>(G);
+}
+
+}  // namespace eta

@@ -1,0 +1,154 @@
+// Device-side helpers for the gfx950 kernels: lane layouts, DPP butterflies,
+// bf16 unpacking and exact float64 -> float16 rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "eta_internal.h"
+
+namespace eta {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---------------------------------------------------------------- element types
+struct Bf16 {
+  using Stored = uint16_t;
+  static constexpr int kBytes = 2;
+};
+struct F32 {
+  using Stored = float;
+  static constexpr int kBytes = 4;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Lane layout of a 64-row tile of D-element rows loaded with 16-byte accesses.
+// Lane (r, cb), r = lane / LPR, cb = lane % LPR, holds for load i the row
+// RPI*i + r, columns chunk(c) = c*(D/CPL) + cb*EPC .. +EPC for c < CPL. One load
+// instruction covers RPI whole rows (contiguous when CPL == 1).
+template <int EBYTES, int D>
+struct TileLayout {
+  static constexpr int EPC = 16 / EBYTES;            // elements per 16-byte chunk
+  static constexpr int ROWB = D * EBYTES;            // bytes per row
+  static constexpr int CPL = ROWB > 256 ? 2 : 1;     // chunks per lane per row
+  static constexpr int LPR = ROWB / 16 / CPL;        // lanes per row (8 or 16)
+  static constexpr int RPI = 64 / LPR;               // rows per load instruction
+  static constexpr int NI = 64 / RPI;                // load instructions per tile (== LPR)
+  static constexpr int EPL = EPC * CPL;              // elements per lane per row
+  static constexpr int DPL = EPL * EBYTES / 4;       // dwords per lane per row
+  static_assert(LPR == 8 || LPR == 16, "unsupported row width");
+  static_assert(NI == LPR, "transpose reduction needs one value per lane of a row");
+  __device__ static __forceinline__ int col(int c, int cb) { return c * (D / CPL) + cb * EPC; }
+};
+
+// ---------------------------------------------------------------- DPP
+// quad_perm [1,0,3,2] and [2,3,0,1]; row_half_mirror; row_mirror.
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Partner for the butterfly step that splits lanes on bit log2(H) inside a
+// group of 2H lanes: mirror (16), half mirror (8), quad xor 2 / xor 1.
+template <int H>
+__device__ __forceinline__ float bfly(float v) {
+  if constexpr (H == 8) return dpp_f<kDppMirror>(v);
+  else if constexpr (H == 4) return dpp_f<kDppHalfMirror>(v);
+  else if constexpr (H == 2) return dpp_f<kDppXor2>(v);
+  else return dpp_f<kDppXor1>(v);
+}
+
+// Transposing reduction inside groups of N lanes: lane j of a group starts with
+// N values v[0..N) and ends with v[0] = sum over the group's lanes of v[j].
+template <int N>
+__device__ __forceinline__ void transpose_reduce(float* v, int lane) {
+  if constexpr (N > 1) {
+    constexpr int H = N / 2;
+    const bool up = (lane & H) != 0;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const float keep = up ? v[k + H] : v[k];
+      const float send = up ? v[k] : v[k + H];
+      v[k] = keep + bfly<H>(send);
+    }
+    transpose_reduce<H>(v, lane);
+  }
+}
+
+// All-reduce inside groups of N (8 or 16) lanes.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (N >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (N >= 8) v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppXor2>(v);
+  v += dpp_f<kDppXor1>(v);
+  return v;
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+// exp(x) for the softmax weights: 2^(x log2 e) on the transcendental unit.
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// ---------------------------------------------------------------- rounding
+// float64 -> float16 bits, round to nearest even, in one rounding step
+// (IEEE 754 binary16: 1 sign, 5 exponent, 10 fraction bits). Infinity and NaN
+// map to infinity and a quiet NaN; overflow rounds to infinity.
+__device__ __forceinline__ uint16_t f64_to_f16_rne(double x) {
+  const uint64_t b = (uint64_t)__double_as_longlong(x);
+  const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
+  const int bexp = (int)((b >> 52) & 0x7ff);
+  const uint64_t frac = b & ((1ull << 52) - 1);
+  if (bexp == 0x7ff) return sign | (frac ? 0x7e00 : 0x7c00);
+  if (bexp == 0) return sign;  // float64 zero or subnormal: far below the float16 range
+  const int e = bexp - 1023;
+  if (e > 15) return sign | 0x7c00;
+  const uint64_t m = (1ull << 52) | frac;   // 53 significant bits
+  const int eu = e < -14 ? -14 : e;          // exponent of the result's leading place
+  const int shift = 42 + (eu - e);           // bits of m below the result's last place
+  if (shift >= 64) return sign;
+  uint64_t q = m >> shift;
+  const uint64_t rem = m & ((1ull << shift) - 1);
+  const uint64_t half = 1ull << (shift - 1);
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  uint32_t bits = ((uint32_t)(eu + 14) << 10) + (uint32_t)q;
+  if (bits >= 0x7c00u) bits = 0x7c00u;
+  return sign | (uint16_t)bits;
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Smallest float32 >= x (x >= 0), +inf for non-finite input.
+__device__ __forceinline__ float f64_to_f32_up(double x) {
+  if (!(x < 1e300)) return __builtin_inff();
+  float f = (float)x;
+  if ((double)f < x) f = __uint_as_float(__float_as_uint(f) + 1u);
+  return f;
+}
+
+}  // namespace eta

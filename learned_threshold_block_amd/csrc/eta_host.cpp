@@ -1,0 +1,349 @@
+// Host side of the C ABI declared in include/eta.h: argument validation,
+// workspace layout, launch geometry and statistics read-back.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/eta.h"
+#include "eta_internal.h"
+
+namespace eta {
+
+static size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
+  size_t off = 0;
+  char* b = static_cast<char*>(base);
+  auto take = [&](size_t bytes) -> void* {
+    off = align_up(off, 256);
+    void* p = b ? b + off : nullptr;
+    off += bytes;
+    return p;
+  };
+  const size_t S = (size_t)d.S, NT = (size_t)d.NT, G = (size_t)d.G;
+  const size_t nq = (size_t)d.N * d.HQ;
+  const size_t pieces = (size_t)kMaxAttendWgs + S;
+  Ws w;
+  w.glob = (int32_t*)take(sizeof(int32_t) * kGlobCount);
+  w.tau = (float*)take(sizeof(float) * nq);
+  w.tile_cnt = (int32_t*)take(sizeof(int32_t) * S * NT);
+  w.tile_ent = (int32_t*)take(sizeof(int32_t) * S * NT * kTile);
+  w.tile_hcnt = (int32_t*)take(sizeof(int32_t) * S * NT * G);
+  w.tile_bits = (uint64_t*)take(sizeof(uint64_t) * S * G * NT);
+  w.tile_umax = (float*)take(sizeof(float) * S * NT * G);
+  w.tile_uarg = (int32_t*)take(sizeof(int32_t) * S * NT * G);
+  w.tile_err = (int32_t*)take(sizeof(int32_t) * S * NT);
+  w.seg_list = (int2*)take(sizeof(int2) * S * (size_t)d.MB);
+  w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_P = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_plo = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_phi = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
+  w.wg_seg = (int32_t*)take(sizeof(int32_t) * kMaxAttendWgs);
+  w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
+  w.st_tokens = (int64_t*)take(sizeof(int64_t) * nq);
+  w.st_rescued = (int32_t*)take(sizeof(int32_t) * nq);
+  w.part_ml = (float*)take(sizeof(float) * pieces * G * 2);
+  w.part_acc = (float*)take(sizeof(float) * pieces * G * (size_t)d.D);
+  if (ws) *ws = w;
+  return align_up(off, 256);
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+eta_status check_cache(const eta_cache* c) {
+  if (!c) return ETA_ERR_INVALID_ARGUMENT;
+  if (c->kv_dtype != ETA_F32 && c->kv_dtype != ETA_BF16) return ETA_ERR_INVALID_ARGUMENT;
+  if (c->num_kv_heads < 1 || c->num_pages < 1 || c->head_dim < 1 || c->block_size < 1)
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (!c->k_pages || !c->v_pages || !c->mu || !c->radius) return ETA_ERR_INVALID_ARGUMENT;
+  if (!aligned(c->k_pages, 16) || !aligned(c->v_pages, 16) || !aligned(c->mu, 16) ||
+      !aligned(c->radius, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
+  if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
+  if ((int64_t)c->num_pages * c->num_kv_heads > (int64_t)1 << 31) return ETA_ERR_UNSUPPORTED;
+  return ETA_OK;
+}
+
+eta_status check_seqs(const eta_seqs* s) {
+  if (!s || s->num_seqs < 1 || s->max_blocks_per_seq < 1) return ETA_ERR_INVALID_ARGUMENT;
+  if (!s->seq_lens || !s->block_table) return ETA_ERR_INVALID_ARGUMENT;
+  if (!aligned(s->seq_lens, 4) || !aligned(s->block_table, 4)) return ETA_ERR_INVALID_ARGUMENT;
+  if (s->max_blocks_per_seq > kMaxBlocksPerSeq) return ETA_ERR_UNSUPPORTED;
+  return ETA_OK;
+}
+
+CacheView view_of(const eta_cache* c) {
+  CacheView v;
+  v.kv_dtype = c->kv_dtype;
+  v.D = c->head_dim;
+  v.HKV = c->num_kv_heads;
+  v.num_pages = c->num_pages;
+  v.k = c->k_pages;
+  v.v = c->v_pages;
+  v.kw = c->k_pages;
+  v.vw = c->v_pages;
+  v.mu = c->mu;
+  v.radius = c->radius;
+  return v;
+}
+
+SeqView view_of(const eta_seqs* s) {
+  SeqView v;
+  v.N = s->num_seqs;
+  v.MB = s->max_blocks_per_seq;
+  v.lens = s->seq_lens;
+  v.bt = s->block_table;
+  return v;
+}
+
+eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d) {
+  if (N < 1 || MB < 1 || HQ < 1) return ETA_ERR_INVALID_ARGUMENT;
+  if (HQ % c->num_kv_heads) return ETA_ERR_INVALID_ARGUMENT;
+  const int G = HQ / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ETA_ERR_UNSUPPORTED;
+  if (MB > kMaxBlocksPerSeq) return ETA_ERR_UNSUPPORTED;
+  const int64_t S = (int64_t)N * c->num_kv_heads;
+  if (S > (1 << 24) || S * MB >= ((int64_t)1 << 31) / 64) return ETA_ERR_UNSUPPORTED;
+  d->N = N;
+  d->MB = MB;
+  d->HQ = HQ;
+  d->HKV = c->num_kv_heads;
+  d->D = c->head_dim;
+  d->G = G;
+  d->S = (int)S;
+  d->NT = (MB + kTile - 1) / kTile;
+  return ETA_OK;
+}
+
+// attend grid: one resident wave of workgroups over the whole device
+std::mutex g_geom_mu;
+struct Geom {
+  int device = -1;
+  int key = -1;
+  int wgs = 0;
+};
+std::vector<Geom> g_geom;
+
+int attend_grid(int kv_dtype, int D, int G) {
+  if (const char* env = getenv("ETA_ATTEND_WGS")) {
+    const int v = atoi(env);
+    if (v >= 1) return v < kMaxAttendWgs ? v : kMaxAttendWgs;
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  const int key = kv_dtype * 1000 + D * 10 + G;
+  std::lock_guard<std::mutex> lk(g_geom_mu);
+  for (const Geom& g : g_geom)
+    if (g.device == dev && g.key == key) return g.wgs;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  int per_cu = attend_wgs_per_cu(kv_dtype, D, G);
+  int wgs = cus * per_cu;
+  if (wgs > kMaxAttendWgs) wgs = kMaxAttendWgs;
+  g_geom.push_back(Geom{dev, key, wgs});
+  return wgs;
+}
+
+eta_status hip_status(hipError_t e) { return e == hipSuccess ? ETA_OK : ETA_ERR_HIP; }
+
+struct Prepared {
+  CacheView c;
+  SeqView s;
+  DecodeParams p;
+  Dims d;
+  Ws ws;
+};
+
+eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                   int tau_mode, const float* w, const float* b_or_c, float a, float beta, int lwb,
+                   int block_size, float* out, void* workspace, size_t ws_bytes, Prepared* P) {
+  eta_status st = check_cache(cache);
+  if (st != ETA_OK) return st;
+  st = check_seqs(seqs);
+  if (st != ETA_OK) return st;
+  if (block_size != cache->block_size) return ETA_ERR_INVALID_ARGUMENT;
+  if (!q || !aligned(q, 16) || !out || !aligned(out, 4) || !b_or_c || !aligned(b_or_c, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (tau_mode != ETA_TAU_LEARNED && tau_mode != ETA_TAU_CALIBRATED) return ETA_ERR_INVALID_ARGUMENT;
+  if (tau_mode == ETA_TAU_LEARNED && (!w || !aligned(w, 16))) return ETA_ERR_INVALID_ARGUMENT;
+  if (!(beta > 0.f) || !isfinite(beta) || !isfinite(a) || lwb < 0) return ETA_ERR_INVALID_ARGUMENT;
+  st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &P->d);
+  if (st != ETA_OK) return st;
+  if (!workspace || !aligned(workspace, 256)) return ETA_ERR_INVALID_ARGUMENT;
+  if (ws_bytes < workspace_layout(P->d, nullptr, nullptr)) return ETA_ERR_WORKSPACE_TOO_SMALL;
+  workspace_layout(P->d, workspace, &P->ws);
+  P->c = view_of(cache);
+  P->s = view_of(seqs);
+  P->p.q = q;
+  P->p.HQ = num_q_heads;
+  P->p.G = P->d.G;
+  P->p.tau_mode = tau_mode;
+  P->p.w = w;
+  P->p.b = b_or_c;
+  P->p.a = a;
+  P->p.beta = beta;
+  P->p.scale = (float)(1.0 / sqrt((double)cache->head_dim));
+  P->p.lwb = lwb;
+  P->p.out = out;
+  return ETA_OK;
+}
+
+eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
+  const int W = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
+  hipError_t e = hipSuccess;
+  switch (phase) {
+    case ETA_PHASE_SCREEN:
+      e = launch_screen(P.c, P.s, P.p, P.d, P.ws, st);
+      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, W, st);
+      break;
+    case ETA_PHASE_ATTEND:
+      e = launch_attend(P.c, P.s, P.p, P.d, P.ws, W, st);
+      break;
+    case ETA_PHASE_MERGE:
+      e = launch_merge(P.d, P.p, P.ws, st);
+      break;
+    default:
+      return ETA_ERR_INVALID_ARGUMENT;
+  }
+  return hip_status(e);
+}
+
+}  // namespace
+}  // namespace eta
+
+using namespace eta;
+
+extern "C" {
+
+const char* eta_status_string(eta_status s) {
+  switch (s) {
+    case ETA_OK: return "ok";
+    case ETA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case ETA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ETA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ETA_ERR_HIP: return "HIP runtime error";
+    case ETA_ERR_DEVICE_DATA: return "invalid sequence length or page id in device data";
+  }
+  return "unknown status";
+}
+
+eta_status eta_build_block_summaries(const eta_cache* cache, const eta_seqs* seqs, eta_stream_t stream) {
+  eta_status st = check_cache(cache);
+  if (st != ETA_OK) return st;
+  st = check_seqs(seqs);
+  if (st != ETA_OK) return st;
+  return hip_status(launch_build_summaries(view_of(cache), view_of(seqs), (hipStream_t)stream));
+}
+
+eta_status eta_append_kv(const eta_cache* cache, const eta_seqs* seqs, const void* k_new,
+                         const void* v_new, eta_stream_t stream) {
+  eta_status st = check_cache(cache);
+  if (st != ETA_OK) return st;
+  st = check_seqs(seqs);
+  if (st != ETA_OK) return st;
+  if (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16)) return ETA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)seqs->num_seqs * cache->num_kv_heads > 0x7fffffff) return ETA_ERR_UNSUPPORTED;
+  return hip_status(launch_append(view_of(cache), view_of(seqs), k_new, v_new, (hipStream_t)stream));
+}
+
+size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_blocks_per_seq,
+                                 int num_q_heads) {
+  if (check_cache(cache) != ETA_OK) return 0;
+  Dims d;
+  if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d) != ETA_OK) return 0;
+  return workspace_layout(d, nullptr, nullptr);
+}
+
+eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* seqs, const void* q,
+                            int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
+                            float a, float beta, int lwb, int block_size, float* out,
+                            void* workspace, size_t ws_bytes, eta_stream_t stream) {
+  if (phase < ETA_PHASE_SCREEN || phase > ETA_PHASE_MERGE) return ETA_ERR_INVALID_ARGUMENT;
+  Prepared P;
+  eta_status st = prepare(cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb, block_size,
+                          out, workspace, ws_bytes, &P);
+  if (st != ETA_OK) return st;
+  return run_phase(phase, P, (hipStream_t)stream);
+}
+
+eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                      int tau_mode, const float* w, const float* b_or_c, float a, float beta, int lwb,
+                      int block_size, float* out, void* workspace, size_t ws_bytes,
+                      eta_stream_t stream) {
+  Prepared P;
+  eta_status st = prepare(cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb, block_size,
+                          out, workspace, ws_bytes, &P);
+  if (st != ETA_OK) return st;
+  for (int ph = ETA_PHASE_SCREEN; ph <= ETA_PHASE_MERGE; ++ph) {
+    st = run_phase(ph, P, (hipStream_t)stream);
+    if (st != ETA_OK) return st;
+  }
+  return ETA_OK;
+}
+
+eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,
+                     int num_kv_heads, int32_t* admitted_per_head, int32_t* union_per_kv,
+                     int64_t* tokens_per_head, uint8_t* rescued, uint32_t* admitted_bitmap,
+                     eta_stream_t stream) {
+  if (!workspace || !aligned(workspace, 256) || !admitted_per_head || !union_per_kv)
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 1 || max_blocks_per_seq < 1 || num_kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % num_kv_heads)
+    return ETA_ERR_INVALID_ARGUMENT;
+  Dims d;
+  d.N = num_seqs;
+  d.MB = max_blocks_per_seq;
+  d.HQ = num_q_heads;
+  d.HKV = num_kv_heads;
+  d.G = num_q_heads / num_kv_heads;
+  d.S = num_seqs * num_kv_heads;
+  d.NT = (max_blocks_per_seq + kTile - 1) / kTile;
+  d.D = 128;  // only the part_* sizes depend on D; they lie after everything read here
+  Ws ws;
+  workspace_layout(d, const_cast<void*>(workspace), &ws);
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return ETA_ERR_HIP;
+  int32_t glob[kGlobCount];
+  if (hipMemcpy(glob, ws.glob, sizeof(glob), hipMemcpyDeviceToHost) != hipSuccess) return ETA_ERR_HIP;
+  if (glob[kGlobN] != num_seqs || glob[kGlobMB] != max_blocks_per_seq || glob[kGlobHQ] != num_q_heads ||
+      glob[kGlobHKV] != num_kv_heads)
+    return ETA_ERR_INVALID_ARGUMENT;
+  const size_t nq = (size_t)num_seqs * num_q_heads;
+  std::vector<int32_t> tmp(nq);
+  if (hipMemcpy(admitted_per_head, ws.st_head, sizeof(int32_t) * nq, hipMemcpyDeviceToHost) != hipSuccess)
+    return ETA_ERR_HIP;
+  if (hipMemcpy(union_per_kv, ws.seg_U, sizeof(int32_t) * d.S, hipMemcpyDeviceToHost) != hipSuccess)
+    return ETA_ERR_HIP;
+  if (tokens_per_head &&
+      hipMemcpy(tokens_per_head, ws.st_tokens, sizeof(int64_t) * nq, hipMemcpyDeviceToHost) != hipSuccess)
+    return ETA_ERR_HIP;
+  if (rescued) {
+    if (hipMemcpy(tmp.data(), ws.st_rescued, sizeof(int32_t) * nq, hipMemcpyDeviceToHost) != hipSuccess)
+      return ETA_ERR_HIP;
+    for (size_t i = 0; i < nq; ++i) rescued[i] = tmp[i] ? 1 : 0;
+  }
+  if (admitted_bitmap) {
+    // tile_bits is [S][G][NT] == [N][HQ][NT] uint64 words, little-endian: the
+    // same bit order as [N][HQ][2*NT] uint32 words
+    const size_t words32 = (size_t)(max_blocks_per_seq + 31) / 32;
+    std::vector<uint64_t> bits(nq * d.NT);
+    if (hipMemcpy(bits.data(), ws.tile_bits, sizeof(uint64_t) * bits.size(), hipMemcpyDeviceToHost) != hipSuccess)
+      return ETA_ERR_HIP;
+    for (size_t i = 0; i < nq; ++i) {
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(bits.data() + i * d.NT);
+      memcpy(admitted_bitmap + i * words32, src, sizeof(uint32_t) * words32);
+    }
+  }
+  return glob[kGlobErr] ? ETA_ERR_DEVICE_DATA : ETA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Internal declarations shared by the host library and the kernel files:
+// workspace layout and kernel launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eta {
+
+constexpr int kBlock = 64;          // tokens per KV block (one page)
+constexpr int kTile = 64;           // blocks screened per wavefront
+constexpr int kAttendThreads = 256; // four wavefronts per attend workgroup
+constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace sizing)
+constexpr int kMaxBlocksPerSeq = 1 << 16;
+constexpr int kMaxGroup = 8;
+
+// global scalars in the workspace
+enum Glob : int {
+  kGlobCounter = 0,  // finalize arrival counter (zeroed by the screen kernel)
+  kGlobUtot = 1,     // total admitted (sequence, kv head, block) entries
+  kGlobWeff = 2,     // attend workgroups that have work: min(grid, Utot)
+  kGlobErr = 3,      // nonzero if a kernel met invalid device data
+  kGlobN = 4,        // header: sizes the workspace was laid out for
+  kGlobMB = 5,
+  kGlobHQ = 6,
+  kGlobHKV = 7,
+  kGlobD = 8,
+  kGlobCount = 16
+};
+
+struct Dims {
+  int N, MB, HQ, HKV, D, G, S, NT;  // S = N*HKV segments, NT = tiles of 64 blocks per segment
+};
+
+// Device pointers into one caller-provided workspace.
+struct Ws {
+  int32_t* glob;        // [kGlobCount]
+  float* tau;           // [N*HQ]       effective thresholds
+  int32_t* tile_cnt;    // [S][NT]      admitted union blocks per tile
+  int32_t* tile_ent;    // [S][NT][64]  (j << 8) | head mask, ascending j
+  int32_t* tile_hcnt;   // [S][NT][G]   admitted blocks per head per tile
+  uint64_t* tile_bits;  // [S][G][NT]   per-head admission bitmap words
+  float* tile_umax;     // [S][NT][G]   largest bound among complete blocks
+  int32_t* tile_uarg;   // [S][NT][G]   its block index (lowest on ties)
+  int32_t* tile_err;    // [S][NT]
+  int2* seg_list;       // [S][MB]      (page, (j << 8) | mask) compacted per segment
+  int32_t* seg_U;       // [S]          union blocks per segment
+  int32_t* seg_P;       // [S]          exclusive prefix of seg_U
+  int32_t* seg_plo;     // [S]          first partial slot of the segment
+  int32_t* seg_phi;     // [S]          last partial slot of the segment
+  int32_t* seg_err;     // [S]
+  int32_t* wg_seg;      // [kMaxAttendWgs] segment holding each attend workgroup's first entry
+  int32_t* st_head;     // [N*HQ]       admitted blocks per head
+  int64_t* st_tokens;   // [N*HQ]
+  int32_t* st_rescued;  // [N*HQ]
+  float* part_ml;       // [(kMaxAttendWgs + S)][G][2]  split running max and sum
+  float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs
+};
+
+size_t workspace_layout(const Dims& d, void* base, Ws* ws);  // base may be null (size only)
+
+struct CacheView {
+  int kv_dtype, D, HKV, num_pages;
+  const void* k;
+  const void* v;
+  void* kw;   // writable views for append
+  void* vw;
+  uint16_t* mu;
+  float* radius;
+};
+
+struct SeqView {
+  int N, MB;
+  const int32_t* lens;
+  const int32_t* bt;
+};
+
+struct DecodeParams {
+  const void* q;
+  int HQ, G, tau_mode;
+  const float* w;
+  const float* b;
+  float a, beta, scale;
+  int lwb;
+  float* out;
+};
+
+// launchers (return hipError_t of the launch)
+hipError_t launch_build_summaries(const CacheView& c, const SeqView& s, hipStream_t st);
+hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new, const void* v_new,
+                         hipStream_t st);
+hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                         const Ws& ws, hipStream_t st);
+hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws,
+                           int attend_wgs, hipStream_t st);
+hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                         const Ws& ws, int attend_wgs, hipStream_t st);
+hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st);
+int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
+
+}  // namespace eta

@@ -1,0 +1,123 @@
+"""The C ABI library loads, exports what include/eta.h declares, and rejects
+bad host-side arguments before any device work (runs without a GPU)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from learned_threshold_block_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eta.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(eta_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (eta_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    L = _lib.lib()
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.eta_status_string(code).decode() not in ("", "unknown status")
+    assert L.eta_status_string(7).decode() == "unknown status"
+
+
+FAKE = 1 << 20  # aligned fake device addresses: validation never dereferences them
+
+
+def cache(**kw):
+    c = dict(kv_dtype=_lib.ETA_BF16, head_dim=128, num_kv_heads=8, block_size=64, num_pages=16,
+             k_pages=FAKE, v_pages=FAKE * 2, mu=FAKE * 3, radius=FAKE * 4)
+    c.update(kw)
+    return _lib.EtaCacheC(**c)
+
+
+def seqs(**kw):
+    s = dict(num_seqs=2, max_blocks_per_seq=8, seq_lens=FAKE * 5, block_table=FAKE * 6)
+    s.update(kw)
+    return _lib.EtaSeqsC(**s)
+
+
+def ws_size(c, n=2, mb=8, hq=32):
+    return _lib.lib().eta_decode_workspace_size(ctypes.byref(c), n, mb, hq)
+
+
+def test_workspace_size():
+    c = cache()
+    n1 = ws_size(c)
+    assert n1 > 0 and n1 % 256 == 0
+    assert ws_size(c, n=4, mb=2048) > n1
+    assert ws_size(cache(head_dim=96)) == 0
+    assert ws_size(c, hq=31) == 0          # not a multiple of H_KV
+    assert ws_size(c, hq=24) == 0          # G = 3 unsupported
+    assert ws_size(c, mb=(1 << 16) + 1) == 0
+    assert ws_size(cache(k_pages=FAKE + 2)) == 0
+
+
+def decode(c=None, s=None, **kw):
+    c = c or cache()
+    s = s or seqs()
+    a = dict(q=FAKE * 7, hq=32, mode=_lib.ETA_TAU_LEARNED, w=FAKE * 8, b=FAKE * 9, a=0.0, beta=5.0,
+             lwb=0, bs=64, out=FAKE * 10, ws=FAKE * 11, nbytes=None)
+    a.update(kw)
+    nbytes = ws_size(c) if a["nbytes"] is None else a["nbytes"]
+    return _lib.lib().eta_decode(ctypes.byref(c), ctypes.byref(s), a["q"], a["hq"], a["mode"], a["w"],
+                                 a["b"], a["a"], a["beta"], a["lwb"], a["bs"], a["out"], a["ws"],
+                                 nbytes, None)
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(q=None), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(q=FAKE + 4), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(w=None), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(b=None), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(mode=5), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(beta=0.0), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(beta=float("inf")), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(a=float("nan")), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(lwb=-1), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(bs=32), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(hq=30), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(hq=48), _lib.ETA_ERR_UNSUPPORTED),
+    (dict(ws=None), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(ws=FAKE + 16), _lib.ETA_ERR_INVALID_ARGUMENT),
+    (dict(nbytes=1024), _lib.ETA_ERR_WORKSPACE_TOO_SMALL),
+])
+def test_decode_rejects(kw, expect):
+    assert decode(**kw) == expect
+
+
+def test_decode_rejects_cache_and_seqs():
+    assert decode(c=cache(block_size=32)) == _lib.ETA_ERR_UNSUPPORTED
+    assert decode(c=cache(head_dim=80)) == _lib.ETA_ERR_UNSUPPORTED
+    assert decode(c=cache(kv_dtype=3)) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode(c=cache(mu=0)) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode(s=seqs(num_seqs=0)) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode(s=seqs(seq_lens=0)) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode(s=seqs(block_table=FAKE + 2)) == _lib.ETA_ERR_INVALID_ARGUMENT
+    L = _lib.lib()
+    c, s = cache(), seqs()
+    assert L.eta_build_block_summaries(ctypes.byref(c), None, None) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert L.eta_build_block_summaries(None, ctypes.byref(s), None) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert L.eta_append_kv(ctypes.byref(c), ctypes.byref(s), None, FAKE, None) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert L.eta_decode_phase(9, ctypes.byref(c), ctypes.byref(s), FAKE, 32, 0, FAKE, FAKE, 0.0, 5.0, 0, 64,
+                              FAKE, FAKE, 1 << 30, None) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert L.eta_stats(None, 1, 1, 1, 1, None, None, None, None, None, None) == _lib.ETA_ERR_INVALID_ARGUMENT
