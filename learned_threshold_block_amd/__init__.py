@@ -16,8 +16,9 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    ETA_BF16, ETA_F32, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN, ETA_TAU_CALIBRATED,
-    ETA_TAU_LEARNED, EtaError, status_string,
+    ETA_BF16, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
+    ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
+    ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
 
 BLOCK = 64
