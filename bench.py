@@ -1,0 +1,295 @@
+#!/usr/bin/env python3
+"""ETA decode-step benchmark on one MI355X.
+
+Workload (default): one sequence of 524,288 tokens, GQA 32 query / 8 KV heads,
+d = 128, bfloat16 paged KV cache (64-token pages), learned thresholds placed
+for ~38% per-head block density, 16 planted needle keys. A step is one full
+ETA decode (threshold + bound screen + compaction, split flash-decode over the
+admitted blocks, merge) for every query head, with the cache resident in HBM.
+
+Prints one JSON line: decode latency (us/step), achieved HBM bandwidth on the
+bytes the step must read, the roofline of the dominant (attend) kernel from HIP
+events, a dense comparator (every block admitted, unfiltered softmax) on the
+same cache, and the fp64 CPU oracle timed on a bounded sample.
+
+Thresholds are calibrated on the GPU through the library itself (bisection
+on each head's bias until its admitted-block count hits the target), so the
+timed path never touches the oracle.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
+    p.add_argument("--density", type=float, default=None, help="per-head target density override")
+    p.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
+    p.add_argument("--sweep", action="store_true", help="also time cfg2 at 10/38/70/100%% density")
+    return p.parse_args()
+
+
+class Setup:
+    """One workload resident on the GPU."""
+
+    def __init__(self, name, density=None):
+        import torch
+
+        import learned_threshold_block_amd as eta
+        import workloads as W
+
+        t0 = time.time()
+        kw = {} if density is None else dict(density=density)
+        self.wl = wl = W.make_workload(name, **kw)
+        log(f"{name}: generated {wl.kv_bytes() / 1e9:.2f} GB of K/V in {time.time() - t0:.1f}s")
+        self.eta, self.torch = eta, torch
+        dev = torch.device("cuda")
+        self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
+                               torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev))
+        self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
+        self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
+        self.q = eta.upload(wl.q, wl.kv_dtype, dev)
+        self.w = torch.from_numpy(wl.w).to(dev)
+        self.ws = eta.alloc_workspace(self.cache, wl.n_seqs, wl.max_blocks, wl.h_q)
+        self.out = torch.empty(wl.n_seqs, wl.h_q, wl.d, dtype=torch.float32, device=dev)
+        self.mode = eta.ETA_TAU_LEARNED if wl.tau_mode == "learned" else eta.ETA_TAU_CALIBRATED
+        eta.build_block_summaries(self.cache, self.seq_lens, self.bt)
+        torch.cuda.synchronize()
+        self.nblk = np.array([wl.nblk(n) for n in range(wl.n_seqs)], dtype=np.float64)
+        self.bias = torch.zeros(wl.h_q, dtype=torch.float32, device=dev)
+
+    def run(self, phase=None, bias=None, mode=None):
+        self.eta.decode(self.cache, self.seq_lens, self.bt, self.q, self.mode if mode is None else mode,
+                        self.bias if bias is None else bias, w=self.w, a=self.wl.a, beta=self.wl.beta,
+                        lwb=self.wl.lwb, out=self.out, workspace=self.ws, phase=phase)
+
+    def stats(self):
+        wl = self.wl
+        return self.eta.stats(self.ws, wl.n_seqs, wl.max_blocks, wl.h_q, wl.h_kv, bitmap=False)
+
+    def calibrate(self, iters=40):
+        """Bisect each head's bias/constant so that its admitted fraction of
+        blocks (averaged over sequences) reaches the workload's target."""
+        wl, torch = self.wl, self.torch
+        target = wl.target_density
+        if np.all(target >= 1.0):
+            self.bias.fill_(-math.inf)
+            return
+        lo = np.full(wl.h_q, -64.0)
+        hi = np.full(wl.h_q, 64.0)
+        for _ in range(iters):
+            mid = 0.5 * (lo + hi)
+            self.bias.copy_(torch.from_numpy(mid.astype(np.float32)))
+            self.run(phase=self.eta.ETA_PHASE_SCREEN)
+            dens = (self.stats().admitted_per_head / self.nblk[:, None]).mean(axis=0)
+            lo = np.where(dens > target, mid, lo)
+            hi = np.where(dens > target, hi, mid)
+        self.bias.copy_(torch.from_numpy((0.5 * (lo + hi)).astype(np.float32)))
+        self.bias[target >= 1.0] = -math.inf
+
+    def densities(self):
+        st = self.stats()
+        per_head = float((st.admitted_per_head / self.nblk[:, None]).mean())
+        union = float((st.union_per_kv / self.nblk[:, None]).mean())
+        return st, per_head, union
+
+    def step_bytes(self, st):
+        """Bytes one step must move: admitted K/V tiles once per union block,
+        the records (centroid + radius) of every complete block, the block
+        table, the queries/thresholds and the output."""
+        wl = self.wl
+        esz = 2 if wl.kv_dtype == "bf16" else 4
+        union = int(st.union_per_kv.sum())
+        kv = union * 2 * 64 * wl.d * esz
+        nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
+        meta = nfull * wl.h_kv * (2 * wl.d + 4) + int(self.nblk.sum()) * 4
+        small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
+        return kv, kv + meta + small
+
+
+def time_steps(S, steps, warmup, phases=True):
+    """Wall-clock time of `steps` decode steps (after `warmup`), plus per-phase
+    HIP-event durations on the launch stream."""
+    eta, torch = S.eta, S.torch
+    for _ in range(warmup):
+        S.run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        if phases:
+            ev[i][0].record()
+            S.run(phase=eta.ETA_PHASE_SCREEN)
+            ev[i][1].record()
+            S.run(phase=eta.ETA_PHASE_ATTEND)
+            ev[i][2].record()
+            S.run(phase=eta.ETA_PHASE_MERGE)
+            ev[i][3].record()
+        else:
+            S.run()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    ph = None
+    if phases:
+        ph = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(steps)])
+        ph = ph.mean(axis=0) * 1e3  # us
+    return wall * 1e6, ph
+
+
+def cpu_baseline(S, budget_s):
+    """The fp64 oracle's decode step on one (sequence, KV head) segment at a
+    time, single-threaded, for about `budget_s` seconds; scaled to a full step."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle.eta_oracle as E
+
+    wl = S.wl
+    G = wl.group
+    bias = S.bias.cpu().numpy()
+    segs = [(n, g) for n in range(wl.n_seqs) for g in range(wl.h_kv)]
+    done, elapsed, blocks_done = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for (n, g) in segs:
+            sub = dict(k_pages=wl.k_pages[:, g:g + 1], v_pages=wl.v_pages[:, g:g + 1])
+            bt = wl.block_table[n:n + 1]
+            lens = wl.seq_lens[n:n + 1]
+            summ = E.build_summaries(sub["k_pages"], wl.kv_dtype, bt, lens)  # records: built once, not timed
+            q = wl.q[n:n + 1, g * G:(g + 1) * G]
+            t0 = time.perf_counter()
+            E.decode(sub["k_pages"], sub["v_pages"], wl.kv_dtype, bt, lens, q, wl.tau_mode,
+                     wl.w[g * G:(g + 1) * G], bias[g * G:(g + 1) * G], wl.a, wl.beta, wl.lwb, summaries=summ)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            blocks_done += wl.nblk(n)
+            if elapsed >= budget_s:
+                break
+    total_blocks = sum(wl.nblk(n) for (n, g) in segs)
+    per_step_s = elapsed * total_blocks / blocks_done
+    return {"value": per_step_s * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {len(segs)} (sequence, KV head) segments ({G} query heads each), "
+                      f"{elapsed:.1f}s of single-threaded fp64 NumPy, scaled by blocks to the full step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "needs a GPU"
+    torch.cuda.set_device(0)
+
+    S = Setup(args.workload, args.density)
+    S.calibrate()
+    st, dens_head, dens_union = S.densities()
+    kv_bytes, all_bytes = S.step_bytes(st)
+    log(f"density per-head {dens_head:.3f} union {dens_union:.3f}; union K/V {kv_bytes / 1e9:.3f} GB")
+
+    us, ph = time_steps(S, args.steps, args.warmup)
+    log(f"step {us:.1f} us; phases screen/attend/merge {ph[0]:.1f} / {ph[1]:.1f} / {ph[2]:.1f} us")
+    wl = S.wl
+    esz = 2 if wl.kv_dtype == "bf16" else 4
+    U = int(st.union_per_kv.sum())
+    G, D = wl.group, wl.d
+    attend_bytes = U * 2 * 64 * D * esz + U * 8 + wl.n_seqs * wl.h_q * D * esz
+    attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
+    result = {
+        "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",
+        "value": round(us, 2),
+        "unit": "us/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us / 1e3, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": {"cfg1": "1 seq x 32768 ctx", "cfg2": "4 seq x 131072 ctx",
+                         "cfg3": "1 seq x 524288 ctx", "cfg4": "16 ragged seqs 4K-256K"}[args.workload]
+                        + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
+                        + f"{wl.tau_mode} thresholds, target per-head density "
+                        + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys",
+            "kv_dtype": wl.kv_dtype,
+            "seq_lens_total": int(wl.seq_lens.sum()),
+            "density_per_head": round(dens_head, 4),
+            "density_union": round(dens_union, 4),
+        },
+        "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+        "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),
+        "phase_us": {"screen": round(float(ph[0]), 2), "attend": round(float(ph[1]), 2),
+                     "merge": round(float(ph[2]), 2)},
+        "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_attend", "bytes_per_launch": attend_bytes},
+    }
+    if not args.no_dense:
+        dense_bias = torch.full((wl.h_q,), -math.inf, device="cuda")
+        saved = S.bias.clone()
+        S.bias.copy_(dense_bias)
+        mode_saved = S.mode
+        S.mode = S.eta.ETA_TAU_CALIBRATED
+        S.run()
+        dst, _, dunion = S.densities()
+        dkv, dall = S.step_bytes(dst)
+        dus, dph = time_steps(S, max(10, args.steps // 2), 3)
+        result["dense_comparator"] = {"us_per_step": round(dus, 2), "density_union": round(dunion, 4),
+                                      "achieved_gbs_kv": round(dkv / (dus * 1e-6) / 1e9, 1),
+                                      "attend_us": round(float(dph[1]), 2),
+                                      "speedup_eta_vs_dense": round(dus / us, 3)}
+        S.bias.copy_(saved)
+        S.mode = mode_saved
+        log(f"dense comparator {dus:.1f} us")
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(S, args.cpu_budget)
+        log(f"cpu baseline {result['cpu_baseline']['value'] / 1e3:.1f} ms/step")
+    if args.sweep:
+        del S
+        torch.cuda.empty_cache()
+        sw = {}
+        for dens in (0.10, 0.38, 0.70, 1.0):
+            S2 = Setup("cfg2", dens)
+            S2.calibrate()
+            st2, dh, du = S2.densities()
+            k2, a2 = S2.step_bytes(st2)
+            us2, ph2 = time_steps(S2, max(10, args.steps // 2), 3)
+            sw[f"{int(dens * 100)}%"] = {"us_per_step": round(us2, 2), "density_per_head": round(dh, 4),
+                                        "density_union": round(du, 4),
+                                        "achieved_gbs_kv": round(k2 / (us2 * 1e-6) / 1e9, 1),
+                                        "attend_us": round(float(ph2[1]), 2)}
+            log(f"cfg2 {dens}: {us2:.1f} us, union {du:.3f}")
+            del S2
+            torch.cuda.empty_cache()
+        result["cfg2_density_sweep"] = sw
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
