@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
   constexpr bool kBf16 = T::kBytes == 2;
   using St = typename T::Stored;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
   const int k = blockIdx.x;
   const int Wp = A.ws.glob[kGlobWeff];
@@ -59,6 +59,8 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
   __shared__ __attribute__((aligned(16))) float p_lds[4][G][64];
   __shared__ float ml_lds[4][G][2];
   __shared__ float acc_lds[4][G][D];
+  __shared__ int toff_lds[kMaxBlocksPerSeq / kTile + 2];
+  const int NT = A.d.NT;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -107,16 +109,34 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
 
+    // the segment's tile prefix, for locating entries in the per-tile lists
+    const int ntn = A.ws.seg_ntn[s];
+    {
+      const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
+      for (int v = threadIdx.x; v <= ntn + 1; v += kAttendThreads) toff_lds[v] = toff[v];
+    }
+    __syncthreads();
+    const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
+
     const int span = e1 - e0;
     const int cnt = span > wave ? (span - wave + 3) / 4 : 0;
-    const int2* list = A.ws.seg_list + (int64_t)s * MB + e0 + wave;
     const St* kbase = (const St*)A.c.k;
     const St* vbase = (const St*)A.c.v;
 
     for (int b0 = 0; b0 < cnt; b0 += 64) {
       const int bc = cnt - b0 < 64 ? cnt - b0 : 64;
       int2 ev = make_int2(0, 0);
-      if (lane < bc) ev = list[4 * (b0 + lane)];
+      if (lane < bc) {
+        const int x = e0 + wave + 4 * (b0 + lane);
+        int lo_v = 0, hi_v = ntn;  // largest tile v <= ntn with toff[v] <= x (ntn: rescue tile)
+        while (lo_v < hi_v) {
+          const int mid = (lo_v + hi_v + 1) >> 1;
+          if (toff_lds[mid] <= x) lo_v = mid;
+          else hi_v = mid - 1;
+        }
+        const int phys = lo_v < ntn ? lo_v : NT;
+        ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
+      }
       int page = __builtin_amdgcn_readlane(ev.x, 0);
       int jm = __builtin_amdgcn_readlane(ev.y, 0);
 
@@ -313,46 +333,70 @@ struct MergeArgs {
   float* out;
 };
 
+// One workgroup per (sequence, query head): o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
+// over the partials p of the head's segment. Threads: D/4 column groups of
+// float4 x (256 / (D/4)) piece groups.
 template <int D, int G>
-__global__ __launch_bounds__(64) void k_merge(MergeArgs A) {
-  constexpr int CPL = D / 64;
-  const int lane = threadIdx.x;
+__global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
+  constexpr int CG = D / 4;          // float4 column groups
+  constexpr int PGN = 256 / CG;      // piece groups
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nh = blockIdx.x;
   const int HQ = A.d.HQ;
   const int n = nh / HQ, h = nh % HQ;
   const int g = h / G, hl = h % G;
   const int s = n * A.d.HKV + g;
   const int plo = A.ws.seg_plo[s], phi = A.ws.seg_phi[s];
+  __shared__ float s_red[4];
+  __shared__ float4 s_acc[PGN][CG];
+  __shared__ float s_l[PGN];
+
   float M = -__builtin_inff();
-  for (int p = plo + lane; p <= phi; p += 64) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
+  for (int p = plo + tid; p <= phi; p += 256) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-  float lsum = 0.f, acc[CPL];
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
-  for (int p0 = plo; p0 <= phi; p0 += 64) {
-    const int p = p0 + lane;
-    float wgt = 0.f;
-    if (p <= phi) {
-      const float mp = A.ws.part_ml[((int64_t)p * G + hl) * 2];
-      const float lp = A.ws.part_ml[((int64_t)p * G + hl) * 2 + 1];
-      wgt = mp == -__builtin_inff() ? 0.f : fast_exp(mp - M);
-      lsum = fmaf(wgt, lp, lsum);
-    }
-    const int nb = phi - p0 + 1 < 64 ? phi - p0 + 1 : 64;
-    const float* pa = A.ws.part_acc + ((int64_t)p0 * G + hl) * D + lane * CPL;
-#pragma unroll 8
-    for (int q = 0; q < nb; ++q) {
-      const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wgt), q));
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(wq, pa[(int64_t)q * G * D + c], acc[c]);
-    }
+  if (lane == 0) s_red[wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+
+  const int cg = tid % CG, pg = tid / CG;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lsum = 0.f;
+#pragma unroll 4
+  for (int p = plo + pg; p <= phi; p += PGN) {
+    const float2 ml = *(const float2*)&A.ws.part_ml[((int64_t)p * G + hl) * 2];
+    const float4 a = *(const float4*)&A.ws.part_acc[((int64_t)p * G + hl) * D + cg * 4];
+    const float wgt = ml.x == -__builtin_inff() ? 0.f : fast_exp(ml.x - M);
+    lsum = fmaf(wgt, ml.y, lsum);
+    acc.x = fmaf(wgt, a.x, acc.x);
+    acc.y = fmaf(wgt, a.y, acc.y);
+    acc.z = fmaf(wgt, a.z, acc.z);
+    acc.w = fmaf(wgt, a.w, acc.w);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) lsum += shfl_xor_f(lsum, o);
-  float* o_ = A.out + ((int64_t)n * HQ + h) * D + lane * CPL;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) o_[c] = lsum > 0.f ? acc[c] / lsum : __builtin_nanf("");
+  s_acc[pg][cg] = acc;
+  if (cg == 0) s_l[pg] = lsum;
+  __syncthreads();
+  if (tid < CG) {
+    float4 t = s_acc[0][tid];
+    float l = s_l[0];
+    for (int q = 1; q < PGN; ++q) {
+      const float4 u = s_acc[q][tid];
+      t.x += u.x;
+      t.y += u.y;
+      t.z += u.z;
+      t.w += u.w;
+      l += s_l[q];
+    }
+    float4 o;
+    if (l > 0.f) {
+      o = make_float4(t.x / l, t.y / l, t.z / l, t.w / l);
+    } else {
+      const float nan = __builtin_nanf("");
+      o = make_float4(nan, nan, nan, nan);
+    }
+    *(float4*)&A.out[((int64_t)n * HQ + h) * D + tid * 4] = o;
+  }
 }
 
 template <typename T, int D, int G>
@@ -398,7 +442,7 @@ int occupancy_g(int G) {
 template <int D, int G>
 hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
   MergeArgs a{d, ws, p.out};
-  hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -110,6 +110,13 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;
 }
 
+// Raw buffer resource over [base, base + bytes): loads at offsets past the end
+// return zeros instead of faulting (used for records of invalid pages).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // exp(x) for the softmax weights: 2^(x log2 e) on the transcendental unit.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 

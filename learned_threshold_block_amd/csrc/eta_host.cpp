@@ -31,15 +31,16 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   Ws w;
   w.glob = (int32_t*)take(sizeof(int32_t) * kGlobCount);
   w.tau = (float*)take(sizeof(float) * nq);
-  w.tile_cnt = (int32_t*)take(sizeof(int32_t) * S * NT);
-  w.tile_ent = (int32_t*)take(sizeof(int32_t) * S * NT * kTile);
+  w.tile_cnt = (int32_t*)take(sizeof(int32_t) * S * (NT + 1));
+  w.tile_ent = (int2*)take(sizeof(int2) * S * (NT + 1) * kTile);
+  w.tile_off = (int32_t*)take(sizeof(int32_t) * S * (NT + 2));
   w.tile_hcnt = (int32_t*)take(sizeof(int32_t) * S * NT * G);
   w.tile_bits = (uint64_t*)take(sizeof(uint64_t) * S * G * NT);
   w.tile_umax = (float*)take(sizeof(float) * S * NT * G);
   w.tile_uarg = (int32_t*)take(sizeof(int32_t) * S * NT * G);
   w.tile_err = (int32_t*)take(sizeof(int32_t) * S * NT);
-  w.seg_list = (int2*)take(sizeof(int2) * S * (size_t)d.MB);
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_P = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_plo = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_phi = (int32_t*)take(sizeof(int32_t) * S);

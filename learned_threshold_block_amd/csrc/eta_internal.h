@@ -37,15 +37,17 @@ struct Dims {
 struct Ws {
   int32_t* glob;        // [kGlobCount]
   float* tau;           // [N*HQ]       effective thresholds
-  int32_t* tile_cnt;    // [S][NT]      admitted union blocks per tile
-  int32_t* tile_ent;    // [S][NT][64]  (j << 8) | head mask, ascending j
+  int32_t* tile_cnt;    // [S][NT+1]    admitted union blocks per tile (tile NT: rescue entries)
+  int2* tile_ent;       // [S][NT+1][64] (page, (j << 8) | head mask), ascending j within a tile
+  int32_t* tile_off;    // [S][NT+2]    exclusive prefix of tile_cnt over the segment's used tiles,
+                        //              the rescue tile last (index ntn), total at ntn+1
   int32_t* tile_hcnt;   // [S][NT][G]   admitted blocks per head per tile
   uint64_t* tile_bits;  // [S][G][NT]   per-head admission bitmap words
   float* tile_umax;     // [S][NT][G]   largest bound among complete blocks
   int32_t* tile_uarg;   // [S][NT][G]   its block index (lowest on ties)
   int32_t* tile_err;    // [S][NT]
-  int2* seg_list;       // [S][MB]      (page, (j << 8) | mask) compacted per segment
   int32_t* seg_U;       // [S]          union blocks per segment
+  int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
   int32_t* seg_P;       // [S]          exclusive prefix of seg_U
   int32_t* seg_plo;     // [S]          first partial slot of the segment
   int32_t* seg_phi;     // [S]          last partial slot of the segment

@@ -16,9 +16,10 @@
 //   a transposing DPP reduction, so each lane ends up owning one block. Admitted
 //   blocks are compacted in ascending order with a wavefront ballot + prefix.
 // k_finalize: one workgroup per (sequence, KV head): per-head totals, rescue,
-//   prefix over the tiles and copy into one contiguous list of (page, j|mask);
-//   the last workgroup to finish (arrival counter) lays out the split of the
-//   total work over the attend grid.
+//   exclusive prefix over the tiles' compacted lists (the attend kernel reads
+//   entries in place through it); the last workgroup to finish (arrival
+//   counter, zeroed by k_screen) lays out the split of the total work over the
+//   attend grid.
 #include <limits.h>
 
 #include "eta_device.h"
@@ -59,7 +60,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
   const int s = blockIdx.y;
   const int HKV = A.d.HKV, MB = A.d.MB, NT = A.d.NT, HQ = A.d.HQ;
@@ -80,44 +81,72 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   const int nfull = badT ? 0 : seq_len / kBlock;
   const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
   const int64_t tix = (int64_t)s * NT + t;
+  const int64_t tcx = (int64_t)s * (NT + 1) + t;  // index into tile_cnt / tile_ent
   const int j0 = t * kTile;
-
-  if (j0 >= nblk) {
-    if (lane == 0) {
-      A.ws.tile_cnt[tix] = 0;
-      A.ws.tile_err[tix] = 0;
-    }
-    if (lane < G) {
-      A.ws.tile_hcnt[tix * G + lane] = 0;
-      A.ws.tile_umax[tix * G + lane] = -__builtin_inff();
-      A.ws.tile_uarg[tix * G + lane] = INT_MAX;
-      A.ws.tile_bits[((int64_t)s * G + lane) * NT + t] = 0;
-    }
+  if (j0 >= nblk) {  // past the sequence: only the bitmap words are read (by eta_stats)
+    if (lane < G) A.ws.tile_bits[((int64_t)s * G + lane) * NT + t] = 0;
     return;
   }
 
-  // thresholds and query norms of the G heads (every row of lanes holds all D columns)
+  // ---- every load of the wavefront is issued before the first use: block-table
+  //      entries, queries and predictor weights, then centroids and radii
+  const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  const int jmax = nblk - 1;
+  int pg[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) pg[i] = bt[min(j0 + RPI * i + r, jmax)];
+  const int jl = j0 + RPI * cb + r;  // block this lane owns after the reduction
+  const int page_l = bt[min(jl, jmax)];
+
   float qf[G][8];
-  float tau[G], qn[G];
   const auto* qbase = (const typename T::Stored*)A.p.q;
 #pragma unroll
+  for (int h = 0; h < G; ++h) load8<T>(qbase + ((int64_t)n * HQ + g * G + h) * D + cb * 8, qf[h]);
+  // predictor weights through a buffer of size 0 in calibrated mode (reads zeros)
+  const auto w_rsrc = make_rsrc(A.p.w, A.p.tau_mode == 0 ? (uint32_t)(HQ * D * 4) : 0u);
+  uint32_t wraw[G][8];
+#pragma unroll
   for (int h = 0; h < G; ++h) {
-    const int hq = g * G + h;
-    load8<T>(qbase + ((int64_t)n * HQ + hq) * D + cb * 8, qf[h]);
-    float ssq = 0.f, dot = 0.f;
-    if (A.p.tau_mode == 0) {
-      const float* wr = A.p.w + (int64_t)hq * D + cb * 8;
-      const float4 w0 = *(const float4*)wr;
-      const float4 w1 = *(const float4*)(wr + 4);
-      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+    const uint32_t off = (uint32_t)(((g * G + h) * D + cb * 8) * 4);
+    const auto w0 = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, off, 0, 0);
+    const auto w1 = __builtin_amdgcn_raw_buffer_load_b128(w_rsrc, off + 16, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dot = fmaf(wv[e], qf[h][e], dot);
+    for (int e = 0; e < 4; ++e) {
+      wraw[h][e] = w0[e];
+      wraw[h][4 + e] = w1[e];
     }
+  }
+
+  const bool lvalid = jl < nblk && page_l >= 0 && page_l < A.c.num_pages;
+  const bool complete = jl < nfull && lvalid;
+  // records through buffer loads: an invalid block reads zeros, without a branch
+  const auto mu_rsrc = make_rsrc(A.c.mu, (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
+  const auto r_rsrc = make_rsrc(A.c.radius, (uint32_t)((int64_t)A.c.num_pages * HKV * 4));
+  uint4 raw[NI];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ssq = fmaf(qf[h][e], qf[h][e], ssq);
-    dot = group_sum<LPR>(dot);
+  for (int i = 0; i < NI; ++i) {
+    const int j = j0 + RPI * i + r;
+    const bool ok = j < nfull && pg[i] >= 0 && pg[i] < A.c.num_pages;
+    const uint32_t off = ok ? (uint32_t)((((int64_t)pg[i] * HKV + g) * D + cb * 8) * 2) : kOutOfRange;
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(mu_rsrc, off, 0, 0);
+    raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+  }
+  const uint32_t roff = complete ? (uint32_t)(((int64_t)page_l * HKV + g) * 4) : kOutOfRange;
+  const float R = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rsrc, roff, 0, 0));
+
+  // ---- thresholds and query norms (every row of lanes holds all D columns)
+  float tau[G], qn[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    float ssq = 0.f, dotw = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ssq = fmaf(qf[h][e], qf[h][e], ssq);
+      dotw = fmaf(__uint_as_float(wraw[h][e]), qf[h][e], dotw);
+    }
+    const float dot = group_sum<LPR>(dotw);
     ssq = group_sum<LPR>(ssq);
-    const float bh = A.p.b[hq];
+    const float bh = A.p.b[g * G + h];
     tau[h] = (A.p.tau_mode == 0) ? (dot + bh) - A.p.a : bh - A.p.a;
     qn[h] = sqrtf(ssq);
   }
@@ -126,24 +155,16 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     for (int h = 0; h < G; ++h) A.ws.tau[(int64_t)n * HQ + g * G + h] = tau[h];
   }
 
-  // partial dot products q . mu^ for the NI blocks this lane reads
-  const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  // ---- q . mu^: partial products per lane, transposing reduction over each row
   float pd[G][NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int j = j0 + RPI * i + r;
-    float mv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    if (j < nfull) {
-      const int page = bt[j];
-      if (page >= 0 && page < A.c.num_pages) {
-        const uint4 raw = *(const uint4*)(A.c.mu + ((int64_t)page * HKV + g) * D + cb * 8);
-        const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+    float mv[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          mv[2 * e] = f16_bits_to_f32((uint16_t)(w4[e] & 0xffffu));
-          mv[2 * e + 1] = f16_bits_to_f32((uint16_t)(w4[e] >> 16));
-        }
-      }
+    for (int e = 0; e < 4; ++e) {
+      mv[2 * e] = f16_bits_to_f32((uint16_t)(w4[e] & 0xffffu));
+      mv[2 * e + 1] = f16_bits_to_f32((uint16_t)(w4[e] >> 16));
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -156,16 +177,6 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
 #pragma unroll
   for (int h = 0; h < G; ++h) transpose_reduce<LPR>(pd[h], lane);
 
-  // this lane now owns block jl
-  const int jl = j0 + RPI * cb + r;
-  int page = -1;
-  bool pvalid = false;
-  if (jl < nblk) {
-    page = bt[jl];
-    pvalid = page >= 0 && page < A.c.num_pages;
-  }
-  const bool complete = jl < nfull && pvalid;
-  const float R = complete ? A.c.radius[(int64_t)page * HKV + g] : 0.f;
   const uint32_t full = (1u << G) - 1u;
   uint32_t mask = 0;
   float ub[G];
@@ -175,7 +186,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     if (complete && !(ub[h] < tau[h])) mask |= 1u << h;
   }
   if (complete && jl >= nfull - A.p.lwb) mask = full;
-  if (jl == nfull && jl < nblk && pvalid) mask = full;  // partial last block
+  if (jl == nfull && lvalid) mask = full;  // partial last block (exists iff nfull < nblk)
 
   // largest bound per head among complete blocks (lowest index on ties)
 #pragma unroll
@@ -197,19 +208,22 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     }
   }
 
-  // back to block order, then ballot compaction (ascending block index)
+  // ---- back to block order, then ballot compaction (ascending block index)
   __shared__ uint32_t smask[4][64];
+  __shared__ int spage[4][64];
   smask[wave][jl - j0] = mask;
+  spage[wave][jl - j0] = page_l;
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
   const uint32_t mb = smask[wave][lane];
+  const int pb = spage[wave][lane];
   const uint64_t ball = __ballot(mb != 0);
   const int pos = __popcll(ball & ((1ull << lane) - 1ull));
-  if (mb) A.ws.tile_ent[tix * kTile + pos] = ((j0 + lane) << 8) | (int)mb;
-  const bool bad_page = jl < nblk && !pvalid;
+  if (mb) A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, ((j0 + lane) << 8) | (int)mb);
+  const bool bad_page = jl < nblk && !lvalid;
   const bool any_bad = __any(bad_page);
   if (lane == 0) {
-    A.ws.tile_cnt[tix] = __popcll(ball);
+    A.ws.tile_cnt[tcx] = __popcll(ball);
     A.ws.tile_err[tix] = any_bad ? 1 : 0;
   }
 #pragma unroll
@@ -232,7 +246,7 @@ struct FinArgs {
 };
 
 // exclusive scan of one int per thread over a 256-thread workgroup
-__device__ int block_excl_scan(int v, int* total, int* lds /*[8]*/) {
+__device__ int block_excl_scan(int v, int* total, int* lds /*[4]*/) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int x = v;
 #pragma unroll
@@ -254,9 +268,12 @@ __device__ int block_excl_scan(int v, int* total, int* lds /*[8]*/) {
   return base + x - v;
 }
 
+// One workgroup per (sequence, KV head): totals, rescue, tile prefix, counts.
+// The last workgroup to finish lays out the attend work split.
 template <int G>
 __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
-  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HKV = A.d.HKV, MB = A.d.MB, NT = A.d.NT, HQ = A.d.HQ;
   const int n = s / HKV, g = s % HKV;
   const int seq_len = A.s.lens[n];
@@ -265,23 +282,21 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
   const int ntn = (nblk + kTile - 1) / kTile;
   const int64_t tix0 = (int64_t)s * NT;
+  const int64_t tcx0 = (int64_t)s * (NT + 1);
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
 
-  __shared__ int s_scan[8];
-  __shared__ int s_toff[kMaxBlocksPerSeq / kTile + 1];
+  __shared__ int s_scan[4];
   __shared__ int s_hcnt[4][G];
   __shared__ float s_umax[4][G];
   __shared__ int s_uarg[4][G];
   __shared__ int s_err[4];
   __shared__ int s_nres;
   __shared__ int s_res_j[G];
-  __shared__ uint32_t s_res_bits[G];
-  __shared__ int s_or_tile[G], s_or_pos[G];
-  __shared__ uint32_t s_or_bits[G];
-  __shared__ int s_nor;
+  __shared__ int s_resc[G];
   __shared__ int s_last;
 
-  // 1. per-head totals, largest bound, errors; tile prefix
+  // 1. per-head totals, largest bound, errors; exclusive prefix over tiles
   int hc[G];
   float um[G];
   int ua[G];
@@ -291,20 +306,18 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     um[h] = -__builtin_inff();
     ua[h] = INT_MAX;
   }
-  int err = 0;
-  int carry = 0;
+  int err = 0, carry = 0;
   for (int t0 = 0; t0 < ntn; t0 += 256) {
     const int t = t0 + tid;
     int c = 0;
     if (t < ntn) {
-      const int64_t tix = tix0 + t;
-      c = A.ws.tile_cnt[tix];
-      err |= A.ws.tile_err[tix];
+      c = A.ws.tile_cnt[tcx0 + t];
+      err |= A.ws.tile_err[tix0 + t];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        hc[h] += A.ws.tile_hcnt[tix * G + h];
-        const float v = A.ws.tile_umax[tix * G + h];
-        const int j = A.ws.tile_uarg[tix * G + h];
+        hc[h] += A.ws.tile_hcnt[(tix0 + t) * G + h];
+        const float v = A.ws.tile_umax[(tix0 + t) * G + h];
+        const int j = A.ws.tile_uarg[(tix0 + t) * G + h];
         if (v > um[h] || (v == um[h] && j < ua[h])) {
           um[h] = v;
           ua[h] = j;
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     }
     int tot;
     const int ex = block_excl_scan(c, &tot, s_scan);
-    if (t < ntn) s_toff[t] = carry + ex;
+    if (t < ntn) toff[t] = carry + ex;
     carry += tot;
   }
   const int ucnt = carry;
@@ -343,9 +356,11 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   }
   __syncthreads();
 
-  // 2. rescue (thread 0): a head with nothing admitted gets its best-bound block
+  // 2. rescue (thread 0): a head with nothing admitted gets its best-bound
+  //    block; if another head of the group loads it already, only the head's
+  //    bit is added to that entry, otherwise it becomes a rescue-tile entry.
   if (tid == 0) {
-    int nres = 0, nor = 0;
+    int nres = 0;
     for (int h = 0; h < G; ++h) {
       int tot = 0;
       float v = -__builtin_inff();
@@ -357,75 +372,43 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
           jb = s_uarg[w][h];
         }
       }
-      s_hcnt[0][h] = tot;
-      s_uarg[0][h] = -1;
+      s_resc[h] = -1;
       if (tot == 0 && jb >= 0 && jb < nfull) {
-        s_uarg[0][h] = jb;
-        s_hcnt[0][h] = 1;
+        s_resc[h] = jb;
+        tot = 1;
         const int tt = jb / kTile;
-        const int64_t tix = tix0 + tt;
-        // already loaded for another head of the group?
-        const int c = A.ws.tile_cnt[tix];
+        int2* ent = A.ws.tile_ent + (tcx0 + tt) * kTile;
+        const int c = A.ws.tile_cnt[tcx0 + tt];
         int found = -1;
         for (int k = 0; k < c; ++k)
-          if ((A.ws.tile_ent[tix * kTile + k] >> 8) == jb) found = k;
+          if ((ent[k].y >> 8) == jb) found = k;
         if (found >= 0) {
-          int q = 0;
-          for (; q < nor; ++q)
-            if (s_or_tile[q] == tt && s_or_pos[q] == found) break;
-          if (q == nor) {
-            s_or_tile[q] = tt;
-            s_or_pos[q] = found;
-            s_or_bits[q] = 0;
-            ++nor;
-          }
-          s_or_bits[q] |= 1u << h;
+          ent[found].y |= 1 << h;
         } else {
           int q = 0;
           for (; q < nres; ++q)
             if (s_res_j[q] == jb) break;
+          int2* rent = A.ws.tile_ent + (tcx0 + NT) * kTile;
           if (q == nres) {
             s_res_j[q] = jb;
-            s_res_bits[q] = 0;
+            rent[q] = make_int2(bt[jb], jb << 8);
             ++nres;
           }
-          s_res_bits[q] |= 1u << h;
+          rent[q].y |= 1 << h;
         }
         A.ws.tile_bits[((int64_t)s * G + h) * NT + tt] |= 1ull << (jb % kTile);
       }
+      s_hcnt[0][h] = tot;
     }
     s_nres = nres;
-    s_nor = nor;
+    A.ws.tile_cnt[tcx0 + NT] = nres;
+    toff[ntn] = ucnt;
+    toff[ntn + 1] = ucnt + nres;
   }
   __syncthreads();
+  const int U = badT ? 0 : ucnt + s_nres;
 
-  // 3. contiguous list of (page, (j << 8) | mask)
-  const int nres = s_nres, nor = s_nor;
-  int2* list = A.ws.seg_list + (int64_t)s * MB;
-  int perr = 0;
-  for (int t = wave; t < ntn; t += 4) {
-    const int64_t tix = tix0 + t;
-    const int c = A.ws.tile_cnt[tix];
-    if (lane < c) {
-      int e = A.ws.tile_ent[tix * kTile + lane];
-      for (int q = 0; q < nor; ++q)
-        if (s_or_tile[q] == t && s_or_pos[q] == lane) e |= (int)s_or_bits[q];
-      int page = bt[e >> 8];
-      if (page < 0 || page >= A.c.num_pages) {
-        page = 0;
-        e &= ~0xff;
-        perr = 1;
-      }
-      list[s_toff[t] + lane] = make_int2(page, e);
-    }
-  }
-  if (tid < nres) {
-    const int j = s_res_j[tid];
-    list[ucnt + tid] = make_int2(bt[j], (j << 8) | (int)s_res_bits[tid]);
-  }
-  const int U = badT ? 0 : ucnt + nres;
-
-  // 4. statistics
+  // 3. statistics
   if (tid < G) {
     const int h = tid;
     const int64_t o = (int64_t)n * HQ + g * G + h;
@@ -433,12 +416,12 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     const int tail_missing = (!badT && (seq_len % kBlock)) ? kBlock - seq_len % kBlock : 0;
     A.ws.st_head[o] = cnt;
     A.ws.st_tokens[o] = cnt > 0 ? (int64_t)cnt * kBlock - tail_missing : 0;
-    A.ws.st_rescued[o] = s_uarg[0][h] >= 0 ? 1 : 0;
+    A.ws.st_rescued[o] = s_resc[h] >= 0 ? 1 : 0;
   }
-  const int any_perr = __syncthreads_or(perr);
   if (tid == 0) {
     A.ws.seg_U[s] = U;
-    A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3] || any_perr) ? 1 : 0;
+    A.ws.seg_ntn[s] = ntn;
+    A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
     __threadfence();
     const int old = atomicAdd(&A.ws.glob[kGlobCounter], 1);
     s_last = (old == A.d.S - 1) ? 1 : 0;
@@ -446,7 +429,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   __syncthreads();
   if (!s_last) return;
 
-  // 5. last workgroup: prefix over segments and the attend work split
+  // 4. last workgroup: prefix over segments and the attend work split
   __threadfence();
   const int S = A.d.S;
   int carry2 = 0, errs = 0;
@@ -470,9 +453,8 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   }
   if (Wp == 0) return;
   for (int si = tid; si < S; si += 256) {
-    // recompute the prefix for this segment from the values written above
     const int u = __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED);
-    const int P = A.ws.seg_P[si];
+    const int P = A.ws.seg_P[si];  // written by this thread above
     if (u == 0) {
       A.ws.seg_plo[si] = 0;
       A.ws.seg_phi[si] = -1;
@@ -480,11 +462,11 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     }
     const int64_t UU = Utot, WW = Wp;
     // attend workgroup k covers entries [floor(k U / W'), floor((k+1) U / W'))
-    const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;                 // first k starting in segment
-    const int64_t k_hi = ((int64_t)(P + u) * WW + UU - 1) / UU - 1;       // last k starting in segment
+    const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;            // first k starting in the segment
+    const int64_t k_hi = ((int64_t)(P + u) * WW + UU - 1) / UU - 1;  // last k starting in the segment
     for (int64_t k = k_lo; k <= k_hi && k < WW; ++k) A.ws.wg_seg[k] = si;
-    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;                  // workgroup holding entry P
-    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;                  // workgroup holding entry P+u-1
+    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;             // workgroup holding entry P
+    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;             // workgroup holding entry P+u-1
     A.ws.seg_plo[si] = (int)(kf + si);
     A.ws.seg_phi[si] = (int)(kl + si);
   }
