@@ -130,34 +130,39 @@ class Setup:
         return kv, kv + meta + small
 
 
-def time_steps(S, steps, warmup, phases=True):
-    """Wall-clock time of `steps` decode steps (after `warmup`), plus per-phase
-    HIP-event durations on the launch stream."""
-    eta, torch = S.eta, S.torch
+def time_steps(S, steps, warmup):
+    """Wall-clock time per decode step over `steps` back-to-back eta_decode
+    calls (after `warmup`), bracketed by device synchronisation."""
+    torch = S.torch
     for _ in range(warmup):
         S.run()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        if phases:
-            ev[i][0].record()
-            S.run(phase=eta.ETA_PHASE_SCREEN)
-            ev[i][1].record()
-            S.run(phase=eta.ETA_PHASE_ATTEND)
-            ev[i][2].record()
-            S.run(phase=eta.ETA_PHASE_MERGE)
-            ev[i][3].record()
-        else:
-            S.run()
+    for _ in range(steps):
+        S.run()
     torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    ph = None
-    if phases:
-        ph = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(steps)])
-        ph = ph.mean(axis=0) * 1e3  # us
-    return wall * 1e6, ph
+    return (time.perf_counter() - t0) / steps * 1e6
+
+
+def time_phases(S, steps):
+    """Per-phase durations (us) from HIP events recorded on the launch stream
+    between the three phases of each step (the events add small gaps, so this
+    loop is kept apart from the step timing)."""
+    eta, torch = S.eta, S.torch
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    S.run()
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        S.run(phase=eta.ETA_PHASE_SCREEN)
+        ev[i][1].record()
+        S.run(phase=eta.ETA_PHASE_ATTEND)
+        ev[i][2].record()
+        S.run(phase=eta.ETA_PHASE_MERGE)
+        ev[i][3].record()
+    torch.cuda.synchronize()
+    ph = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(steps)])
+    return ph.mean(axis=0) * 1e3
 
 
 def cpu_baseline(S, budget_s):
@@ -210,7 +215,8 @@ def main():
     kv_bytes, all_bytes = S.step_bytes(st)
     log(f"density per-head {dens_head:.3f} union {dens_union:.3f}; union K/V {kv_bytes / 1e9:.3f} GB")
 
-    us, ph = time_steps(S, args.steps, args.warmup)
+    us = time_steps(S, args.steps, args.warmup)
+    ph = time_phases(S, args.steps)
     log(f"step {us:.1f} us; phases screen/attend/merge {ph[0]:.1f} / {ph[1]:.1f} / {ph[2]:.1f} us")
     wl = S.wl
     esz = 2 if wl.kv_dtype == "bf16" else 4
@@ -259,7 +265,8 @@ def main():
         S.run()
         dst, _, dunion = S.densities()
         dkv, dall = S.step_bytes(dst)
-        dus, dph = time_steps(S, max(10, args.steps // 2), 3)
+        dus = time_steps(S, max(10, args.steps // 2), 3)
+        dph = time_phases(S, max(10, args.steps // 2))
         result["dense_comparator"] = {"us_per_step": round(dus, 2), "density_union": round(dunion, 4),
                                       "achieved_gbs_kv": round(dkv / (dus * 1e-6) / 1e9, 1),
                                       "attend_us": round(float(dph[1]), 2),
@@ -279,7 +286,8 @@ def main():
             S2.calibrate()
             st2, dh, du = S2.densities()
             k2, a2 = S2.step_bytes(st2)
-            us2, ph2 = time_steps(S2, max(10, args.steps // 2), 3)
+            us2 = time_steps(S2, max(10, args.steps // 2), 3)
+            ph2 = time_phases(S2, max(10, args.steps // 2))
             sw[f"{int(dens * 100)}%"] = {"us_per_step": round(us2, 2), "density_per_head": round(dh, 4),
                                         "density_union": round(du, 4),
                                         "achieved_gbs_kv": round(k2 / (us2 * 1e-6) / 1e9, 1),
