@@ -9,6 +9,7 @@ import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libeta.so")
 SOURCES = ["eta_summary.hip", "eta_screen.hip", "eta_attend.hip", "eta_host.cpp"]
 ARCH = os.environ.get("ETA_OFFLOAD_ARCH", "gfx950")
@@ -37,7 +38,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *HIP_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

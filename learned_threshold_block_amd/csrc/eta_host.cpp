@@ -9,7 +9,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/eta.h"
+#include "eta.h"
 #include "eta_internal.h"
 
 namespace eta {
