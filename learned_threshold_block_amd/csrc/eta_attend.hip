@@ -38,152 +38,118 @@ struct AttendArgs {
   Ws ws;
 };
 
-// Per-wavefront decode state of one run (one (sequence, KV head) segment):
-// the group's queries in this lane's columns, thresholds, and the online
-// softmax state (running max per row of lanes, per-lane sums and outputs).
 template <typename T, int D, int G>
-struct RunState {
-  using L = TileLayout<T::kBytes, D>;
-  uint32_t qb[G][L::CPL * 4];  // packed bf16 pairs (bf16 path)
-  float qf[G][L::EPL];         // float32 path
-  float tau[G];
-  float m[G], l[G], acc[G][L::EPL];
-};
-
-template <typename T, int D, int G>
-__device__ __forceinline__ void run_begin(RunState<T, D, G>& st, const AttendArgs& A, int n, int g, int cb) {
-  using L = TileLayout<T::kBytes, D>;
-  using St = typename T::Stored;
-  const int HQ = A.d.HQ;
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const St* qrow = (const St*)A.p.q + ((int64_t)n * HQ + g * G + h) * D;
-#pragma unroll
-    for (int c = 0; c < L::CPL; ++c) {
-      const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
-      if constexpr (T::kBytes == 2) {
-        st.qb[h][c * 4 + 0] = v.x; st.qb[h][c * 4 + 1] = v.y; st.qb[h][c * 4 + 2] = v.z; st.qb[h][c * 4 + 3] = v.w;
-      } else {
-        st.qf[h][c * 4 + 0] = __uint_as_float(v.x); st.qf[h][c * 4 + 1] = __uint_as_float(v.y);
-        st.qf[h][c * 4 + 2] = __uint_as_float(v.z); st.qf[h][c * 4 + 3] = __uint_as_float(v.w);
-      }
-    }
-    st.tau[h] = A.ws.tau[(int64_t)n * HQ + g * G + h];
-    st.m[h] = -__builtin_inff();
-    st.l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < L::EPL; ++e) st.acc[h][e] = 0.f;
-  }
-}
-
-// Entries [c, c + cnt) of the segment's compacted lists, one per lane
-// (lane < cnt): the tile whose prefix covers the index is found by binary
-// search over the prefix in LDS (index ntn is the rescue tile).
-__device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2* tents, int ntn, int NT,
-                                                int c, int cnt, int lane) {
-  int2 ev = make_int2(0, 0);
-  if (lane < cnt) {
-    const int x = c + lane;
-    int lo_v = 0, hi_v = ntn;
-    while (lo_v < hi_v) {
-      const int mid = (lo_v + hi_v + 1) >> 1;
-      if (toff_lds[mid] <= x) lo_v = mid;
-      else hi_v = mid - 1;
-    }
-    const int phys = lo_v < ntn ? lo_v : NT;
-    ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
-  }
-  return ev;
-}
-
-// Claim size for a wavefront: about half of the remaining entries' fair share,
-// between 1 and 16, so that claims shrink towards the end of the segment.
-__device__ __forceinline__ int claim_size(int remaining, int nwaves) {
-  int sz = remaining / (2 * nwaves);
-  return sz < 1 ? 1 : (sz > 16 ? 16 : sz);
-}
-
-template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu((T::kBytes == 2 || D == 64) && G <= 4 ? 2 : 1)))
-void k_attend(AttendArgs A) {
+__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1))) void k_attend(AttendArgs A) {
   using L = TileLayout<T::kBytes, D>;
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
   constexpr bool kBf16 = T::kBytes == 2;
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int tid = threadIdx.x;
   const int r = lane / LPR, cb = lane % LPR;
   const int k = blockIdx.x;
-  const int Utot = A.ws.glob[kGlobUtot];
-  if (Utot <= 0) return;
-  const int HKV = A.d.HKV, S = A.d.S, NT = A.d.NT;
+  const int Wp = A.ws.glob[kGlobWeff];
+  if (k >= Wp) return;
+  const int64_t Utot = A.ws.glob[kGlobUtot];
+  int64_t lo = (int64_t)k * Utot / Wp;
+  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  int s = A.ws.wg_seg[k];
+  const int HKV = A.d.HKV, HQ = A.d.HQ, MB = A.d.MB;
   const float scale = A.p.scale, beta = A.p.beta;
 
   __shared__ __attribute__((aligned(16))) float p_lds[4][G][64];
   __shared__ float ml_lds[4][G][2];
   __shared__ float acc_lds[4][G][D];
   __shared__ int toff_lds[kMaxBlocksPerSeq / kTile + 2];
-  __shared__ int s_red_v[4], s_red_s[4];
-  __shared__ int s_pick, s_slot;
+  const int NT = A.d.NT;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
-  const St* kbase = (const St*)A.c.k;
-  const St* vbase = (const St*)A.c.v;
 
-  int s = A.ws.wg_seg[k];  // home segment
-  int64_t slot = k;        // home run writes partial slot k
-  RunState<T, D, G> st;
-
-  for (;;) {
-    // ------------------------------------------------------------ one run on segment s
+  while (lo < hi) {
+    int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
+    while (lo >= (int64_t)P + Us) {
+      ++s;
+      P = A.ws.seg_P[s];
+      Us = A.ws.seg_U[s];
+    }
+    const int e0 = (int)(lo - P);
+    const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
     const int n = s / HKV, g = s % HKV;
     const int seq_len = A.s.lens[n];
     const int nfull = seq_len / kBlock;
     const int rem = seq_len - nfull * kBlock;
-    const int Us = A.ws.seg_U[s];
+
+    // queries of the group at this lane's columns, and thresholds
+    uint32_t qb[G][CPL * 4];  // packed bf16 pairs (bf16 path)
+    float qf[G][EPL];         // float32 path
+    float tau[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const St* qrow = (const St*)A.p.q + ((int64_t)n * HQ + g * G + h) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+        if constexpr (kBf16) {
+          qb[h][c * 4 + 0] = v.x; qb[h][c * 4 + 1] = v.y; qb[h][c * 4 + 2] = v.z; qb[h][c * 4 + 3] = v.w;
+        } else {
+          qf[h][c * 4 + 0] = __uint_as_float(v.x); qf[h][c * 4 + 1] = __uint_as_float(v.y);
+          qf[h][c * 4 + 2] = __uint_as_float(v.z); qf[h][c * 4 + 3] = __uint_as_float(v.w);
+        }
+      }
+      tau[h] = A.ws.tau[(int64_t)n * HQ + g * G + h];
+    }
+    float m[G], l[G], acc[G][EPL];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      m[h] = -__builtin_inff();
+      l[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+    }
+
+    // the segment's tile prefix, for locating entries in the per-tile lists
     const int ntn = A.ws.seg_ntn[s];
-    const int homes = A.ws.seg_khi[s] - A.ws.seg_klo[s] + 1;
-    const int nwaves = 4 * (homes > 0 ? homes : 1);
-    int32_t* next_ctr = A.ws.seg_next + s;
     {
       const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
-      for (int v = tid; v <= ntn + 1; v += kAttendThreads) toff_lds[v] = toff[v];
+      for (int v = threadIdx.x; v <= ntn + 1; v += kAttendThreads) toff_lds[v] = toff[v];
     }
     __syncthreads();
     const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
-    run_begin<T, D, G>(st, A, n, g, cb);
 
-    // wavefront claims, two deep: the current batch of entries, the next batch
-    // (resolved while the current one streams) and the claim after it (in flight)
-    int sz = claim_size(Us, nwaves);
-    const int c0 = __builtin_amdgcn_readfirstlane(lane == 0 ? atomicAdd(next_ctr, sz) : 0);
-    int bc = c0 < Us ? min(sz, Us - c0) : 0;
-    if (bc > 0) {
-      int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane);
-      int szn = claim_size(Us - (c0 + sz), nwaves);
-      const int c1 = __builtin_amdgcn_readfirstlane(lane == 0 ? atomicAdd(next_ctr, szn) : 0);
-      int bcn = c1 < Us ? min(szn, Us - c1) : 0;
-      int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane);
-      int c_last = c1, sz_last = szn;
-      int sz2 = claim_size(Us - (c_last + sz_last), nwaves);
-      int c2_raw = (bcn > 0 && lane == 0) ? atomicAdd(next_ctr, sz2) : Us;
-      int it = 0;
-      int page_nx = __builtin_amdgcn_readlane(ev.x, 0);
-      int jm_nx = __builtin_amdgcn_readlane(ev.y, 0);
+    const int span = e1 - e0;
+    const int cnt = span > wave ? (span - wave + 3) / 4 : 0;
+    const St* kbase = (const St*)A.c.k;
+    const St* vbase = (const St*)A.c.v;
+
+    for (int b0 = 0; b0 < cnt; b0 += 64) {
+      const int bc = cnt - b0 < 64 ? cnt - b0 : 64;
+      int2 ev = make_int2(0, 0);
+      if (lane < bc) {
+        const int x = e0 + wave + 4 * (b0 + lane);
+        int lo_v = 0, hi_v = ntn;  // largest tile v <= ntn with toff[v] <= x (ntn: rescue tile)
+        while (lo_v < hi_v) {
+          const int mid = (lo_v + hi_v + 1) >> 1;
+          if (toff_lds[mid] <= x) lo_v = mid;
+          else hi_v = mid - 1;
+        }
+        const int phys = lo_v < ntn ? lo_v : NT;
+        ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
+      }
+      int page = __builtin_amdgcn_readlane(ev.x, 0);
+      int jm = __builtin_amdgcn_readlane(ev.y, 0);
 
       uint4 kr[NI][CPL], vr[NI][CPL];
       {
-        const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
+        const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
       }
-      for (;;) {
-        const int cur_page = page_nx, cur_jm = jm_nx;
+      for (int it = 0; it < bc; ++it) {
+        const int cur_page = page, cur_jm = jm;
         {
           const St* vt = vbase + ((int64_t)cur_page * HKV + g) * (kBlock * D);
 #pragma unroll
@@ -191,29 +157,9 @@ void k_attend(AttendArgs A) {
 #pragma unroll
             for (int c = 0; c < CPL; ++c) vr[i][c] = *(const uint4*)(vt + loff[c] + i * RPI * D);
         }
-        // next entry: from this batch, or the first of the next one
-        bool has_next = true;
-        if (++it >= bc) {
-          ev = evn;
-          bc = bcn;
-          it = 0;
-          if (bc > 0) {
-            const int c2 = __builtin_amdgcn_readfirstlane(c2_raw);
-            bcn = c2 < Us ? min(sz2, Us - c2) : 0;
-            evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane);
-            if (bcn > 0) {
-              c_last = c2;
-              sz_last = sz2;
-              sz2 = claim_size(Us - (c_last + sz_last), nwaves);
-              c2_raw = lane == 0 ? atomicAdd(next_ctr, sz2) : 0;
-            }
-          } else {
-            has_next = false;
-          }
-        }
-        if (has_next) {
-          page_nx = __builtin_amdgcn_readlane(ev.x, it);
-          jm_nx = __builtin_amdgcn_readlane(ev.y, it);
+        if (it + 1 < bc) {
+          page = __builtin_amdgcn_readlane(ev.x, it + 1);
+          jm = __builtin_amdgcn_readlane(ev.y, it + 1);
         }
         const uint32_t hmask = (uint32_t)cur_jm & 0xffu;
         const int j = cur_jm >> 8;
@@ -234,36 +180,36 @@ void k_attend(AttendArgs A) {
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
                 if constexpr (kBf16) {
-                  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, st.qb[h][c * 4 + w]),
+                  a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qb[h][c * 4 + w]),
                                                       __builtin_bit_cast(bf16x2_t, kw[w]), a, false);
                 } else {
-                  a = fmaf(st.qf[h][c * 4 + w], __uint_as_float(kw[w]), a);
+                  a = fmaf(qf[h][c * 4 + w], __uint_as_float(kw[w]), a);
                 }
               }
             }
             pd[i] = a;
           }
           transpose_reduce<LPR>(pd, lane);
-          const float S_ = pd[0] * scale;
-          const float x = beta * (S_ - st.tau[h]);
+          const float S = pd[0] * scale;
+          const float x = beta * (S - tau[h]);
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-          float sv = S_ * sg;
-          if (tail && tok >= rem) sv = -__builtin_inff();
-          const float mt = group_max<LPR>(sv);
-          const float mnew = fmaxf(st.m[h], mt);
+          float st = S * sg;
+          if (tail && tok >= rem) st = -__builtin_inff();
+          const float mt = group_max<LPR>(st);
+          const float mnew = fmaxf(m[h], mt);
           const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
-          const float alpha = fast_exp(st.m[h] - muse);
-          const float p = fast_exp(sv - muse);
-          st.l[h] = fmaf(st.l[h], alpha, p);
+          const float alpha = fast_exp(m[h] - muse);
+          const float p = fast_exp(st - muse);
+          l[h] = fmaf(l[h], alpha, p);
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) st.acc[h][e] *= alpha;
-          st.m[h] = mnew;
+          for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+          m[h] = mnew;
           p_lds[wave][h][lane] = p;
         }
 
         // ---- K of the next tile streams while the values are accumulated
-        if (has_next) {
-          const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
+        if (it + 1 < bc) {
+          const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
 #pragma unroll
           for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -309,39 +255,38 @@ void k_attend(AttendArgs A) {
               if (!(hmask & (1u << h))) continue;
               const float pv = ii == 0 ? pw[h].x : ii == 1 ? pw[h].y : ii == 2 ? pw[h].z : pw[h].w;
 #pragma unroll
-              for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pv, vf[e], st.acc[h][e]);
+              for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);
             }
           }
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        if (!has_next) break;
       }
     }
 
-    // ---- end of run: merge rows of lanes, then the four wavefronts, write the partial
+    // ---- merge the rows of lanes, then the four wavefronts, write one partial
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      const float lr = group_sum<LPR>(st.l[h]);
-      float M = st.m[h];
+      const float lr = group_sum<LPR>(l[h]);
+      float M = m[h];
 #pragma unroll
       for (int o = LPR; o < 64; o <<= 1) M = fmaxf(M, shfl_xor_f(M, o));
-      const float sc = st.m[h] == -__builtin_inff() ? 0.f : fast_exp(st.m[h] - M);
+      const float sc = m[h] == -__builtin_inff() ? 0.f : fast_exp(m[h] - M);
       float lw = sc * lr;
 #pragma unroll
       for (int o = LPR; o < 64; o <<= 1) lw += shfl_xor_f(lw, o);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
-        float a = sc * st.acc[h][e];
+        float a = sc * acc[h][e];
 #pragma unroll
         for (int o = LPR; o < 64; o <<= 1) a += shfl_xor_f(a, o);
-        st.acc[h][e] = a;
+        acc[h][e] = a;
       }
       if (r == 0) {
 #pragma unroll
         for (int c = 0; c < CPL; ++c)
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) acc_lds[wave][h][L::col(c, cb) + e] = st.acc[h][c * EPC + e];
+          for (int e = 0; e < EPC; ++e) acc_lds[wave][h][L::col(c, cb) + e] = acc[h][c * EPC + e];
       }
       if (lane == 0) {
         ml_lds[wave][h][0] = M;
@@ -349,6 +294,7 @@ void k_attend(AttendArgs A) {
       }
     }
     __syncthreads();
+    const int64_t piece = (int64_t)k + s;
     for (int h = wave; h < G; h += 4) {
       float Mw[4], M = -__builtin_inff();
 #pragma unroll
@@ -362,7 +308,7 @@ void k_attend(AttendArgs A) {
         sc[w] = Mw[w] == -__builtin_inff() ? 0.f : fast_exp(Mw[w] - M);
         Lsum = fmaf(sc[w], ml_lds[w][h][1], Lsum);
       }
-      float* pa = A.ws.part_acc + (slot * G + h) * D;
+      float* pa = A.ws.part_acc + (piece * G + h) * D;
       for (int dd = lane; dd < D; dd += 64) {
         float a = 0.f;
 #pragma unroll
@@ -370,64 +316,13 @@ void k_attend(AttendArgs A) {
         pa[dd] = a;
       }
       if (lane == 0) {
-        A.ws.part_ml[(slot * G + h) * 2] = M;
-        A.ws.part_ml[(slot * G + h) * 2 + 1] = Lsum;
+        A.ws.part_ml[(piece * G + h) * 2] = M;
+        A.ws.part_ml[(piece * G + h) * 2 + 1] = Lsum;
       }
     }
-
-    // ------------------------------------------------------------ steal: the segment with
-    // the most unclaimed entries among those with a free stealing slot
-    for (;;) {
-      int best_v = 0, best_s = -1;
-      for (int si = tid; si < S; si += kAttendThreads) {
-        const int left = __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED) -
-                         __atomic_load_n(&A.ws.seg_next[si], __ATOMIC_RELAXED);
-        const int stl = __atomic_load_n(&A.ws.seg_steals[si], __ATOMIC_RELAXED);
-        if (stl < kMaxSteals && left > best_v) {
-          best_v = left;
-          best_s = si;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const int ov = __shfl_xor(best_v, o, 64);
-        const int os = __shfl_xor(best_s, o, 64);
-        if (ov > best_v || (ov == best_v && os >= 0 && (best_s < 0 || os < best_s))) {
-          best_v = ov;
-          best_s = os;
-        }
-      }
-      __syncthreads();  // also: every wavefront is done with the LDS of the last run
-      if (lane == 0) {
-        s_red_v[wave] = best_v;
-        s_red_s[wave] = best_s;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int bv = 0, bs = -1;
-        for (int w = 0; w < 4; ++w)
-          if (s_red_v[w] > bv || (s_red_v[w] == bv && s_red_s[w] >= 0 && (bs < 0 || s_red_s[w] < bs))) {
-            bv = s_red_v[w];
-            bs = s_red_s[w];
-          }
-        int sl = -1;
-        if (bs >= 0) {
-          const int idx = atomicAdd(&A.ws.seg_steals[bs], 1);
-          if (idx < kMaxSteals) sl = idx;
-        }
-        s_pick = bv > 0 ? bs : -1;
-        s_slot = sl;
-      }
-      __syncthreads();
-      const int pick = s_pick, sl = s_slot;
-      if (pick < 0) return;  // nothing left anywhere
-      if (sl >= 0) {
-        s = pick;
-        slot = (int64_t)kMaxAttendWgs + (int64_t)pick * kMaxSteals + sl;
-        break;
-      }
-      // lost the race for the last stealing slot of that segment: choose again
-    }
+    __syncthreads();
+    lo = (int64_t)P + e1;
+    ++s;
   }
 }
 
@@ -439,9 +334,8 @@ struct MergeArgs {
 };
 
 // One workgroup per (sequence, query head): o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
-// over the partials p of the head's segment: the home runs of workgroups
-// klo..khi, then the stealing runs. Threads: D/4 column groups of float4 x
-// (256 / (D/4)) piece groups.
+// over the partials p of the head's segment. Threads: D/4 column groups of
+// float4 x (256 / (D/4)) piece groups.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   constexpr int CG = D / 4;          // float4 column groups
@@ -453,19 +347,13 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   const int n = nh / HQ, h = nh % HQ;
   const int g = h / G, hl = h % G;
   const int s = n * A.d.HKV + g;
-  const int klo = A.ws.seg_klo[s], khi = A.ws.seg_khi[s];
-  const int nhome = khi >= klo ? khi - klo + 1 : 0;
-  const int nst = min(A.ws.seg_steals[s], kMaxSteals);
-  const int np = nhome + nst;
-  auto slot_of = [&](int p) -> int64_t {
-    return p < nhome ? (int64_t)(klo + p) : (int64_t)kMaxAttendWgs + (int64_t)s * kMaxSteals + (p - nhome);
-  };
+  const int plo = A.ws.seg_plo[s], phi = A.ws.seg_phi[s];
   __shared__ float s_red[4];
   __shared__ float4 s_acc[PGN][CG];
   __shared__ float s_l[PGN];
 
   float M = -__builtin_inff();
-  for (int p = tid; p < np; p += 256) M = fmaxf(M, A.ws.part_ml[(slot_of(p) * G + hl) * 2]);
+  for (int p = plo + tid; p <= phi; p += 256) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
   if (lane == 0) s_red[wave] = M;
@@ -476,10 +364,9 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
 #pragma unroll 4
-  for (int p = pg; p < np; p += PGN) {
-    const int64_t sl = slot_of(p);
-    const float2 ml = *(const float2*)&A.ws.part_ml[(sl * G + hl) * 2];
-    const float4 a = *(const float4*)&A.ws.part_acc[(sl * G + hl) * D + cg * 4];
+  for (int p = plo + pg; p <= phi; p += PGN) {
+    const float2 ml = *(const float2*)&A.ws.part_ml[((int64_t)p * G + hl) * 2];
+    const float4 a = *(const float4*)&A.ws.part_acc[((int64_t)p * G + hl) * D + cg * 4];
     const float wgt = ml.x == -__builtin_inff() ? 0.f : fast_exp(ml.x - M);
     lsum = fmaf(wgt, ml.y, lsum);
     acc.x = fmaf(wgt, a.x, acc.x);

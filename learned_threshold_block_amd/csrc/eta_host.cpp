@@ -27,7 +27,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   };
   const size_t S = (size_t)d.S, NT = (size_t)d.NT, G = (size_t)d.G;
   const size_t nq = (size_t)d.N * d.HQ;
-  const size_t pieces = (size_t)kMaxAttendWgs + S * kMaxSteals;
+  const size_t pieces = (size_t)kMaxAttendWgs + S;
   Ws w;
   w.glob = (int32_t*)take(sizeof(int32_t) * kGlobCount);
   w.tau = (float*)take(sizeof(float) * nq);
@@ -42,10 +42,8 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_P = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_klo = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_khi = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_next = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_steals = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_plo = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_phi = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
   w.wg_seg = (int32_t*)take(sizeof(int32_t) * kMaxAttendWgs);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);

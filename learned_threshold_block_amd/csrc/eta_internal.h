@@ -14,9 +14,6 @@ constexpr int kAttendThreads = 256; // four wavefronts per attend workgroup
 constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace sizing)
 constexpr int kMaxBlocksPerSeq = 1 << 16;
 constexpr int kMaxGroup = 8;
-constexpr int kMaxSteals = 8;       // stealing runs allowed per (sequence, KV head) segment
-constexpr int kMinClaim = 4;        // smallest claim of entries (one per wavefront)
-constexpr int kMaxClaim = 64;       // largest claim of entries
 
 // global scalars in the workspace
 enum Glob : int {
@@ -52,19 +49,15 @@ struct Ws {
   int32_t* seg_U;       // [S]          union blocks per segment
   int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
   int32_t* seg_P;       // [S]          exclusive prefix of seg_U
-  int32_t* seg_klo;     // [S]          first attend workgroup whose home is the segment
-  int32_t* seg_khi;     // [S]          last one (khi < klo: none)
-  int32_t* seg_next;    // [S]          entries claimed so far (attend work counter, zeroed by finalize)
-  int32_t* seg_steals;  // [S]          stealing runs started on the segment (zeroed by finalize)
+  int32_t* seg_plo;     // [S]          first partial slot of the segment
+  int32_t* seg_phi;     // [S]          last partial slot of the segment
   int32_t* seg_err;     // [S]
-  int32_t* wg_seg;      // [kMaxAttendWgs] home segment of each attend workgroup (-1: none)
+  int32_t* wg_seg;      // [kMaxAttendWgs] segment holding each attend workgroup's first entry
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
   int64_t* st_tokens;   // [N*HQ]
   int32_t* st_rescued;  // [N*HQ]
-  float* part_ml;       // [kMaxAttendWgs + S*kMaxSteals][G][2]  running max and sum of each run
-  float* part_acc;      // [kMaxAttendWgs + S*kMaxSteals][G][D]  unnormalised outputs of each run
-                        // slot k: home run of workgroup k; slot kMaxAttendWgs + s*kMaxSteals + i:
-                        // i-th stealing run on segment s
+  float* part_ml;       // [(kMaxAttendWgs + S)][G][2]  split running max and sum
+  float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs
 };
 
 size_t workspace_layout(const Dims& d, void* base, Ws* ws);  // base may be null (size only)

@@ -421,8 +421,6 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   if (tid == 0) {
     A.ws.seg_U[s] = U;
     A.ws.seg_ntn[s] = ntn;
-    A.ws.seg_next[s] = 0;
-    A.ws.seg_steals[s] = 0;
     A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
     __threadfence();
     const int old = atomicAdd(&A.ws.glob[kGlobCounter], 1);
@@ -431,11 +429,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   __syncthreads();
   if (!s_last) return;
 
-  // 4. last workgroup: prefix over segments and the attend workgroups' home
-  //    segments: workgroup k starts in the segment holding entry floor(k Utot / W)
+  // 4. last workgroup: prefix over segments and the attend work split
   __threadfence();
   const int S = A.d.S;
-  const int W = A.W;
   int carry2 = 0, errs = 0;
   for (int s0 = 0; s0 < S; s0 += 256) {
     const int si = s0 + tid;
@@ -447,30 +443,32 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     carry2 += tot;
   }
   const int Utot = carry2;
+  const int Wp = Utot < A.W ? Utot : A.W;
   errs = __syncthreads_or(errs);
   if (tid == 0) {
     A.ws.glob[kGlobUtot] = Utot;
+    A.ws.glob[kGlobWeff] = Wp;
     A.ws.glob[kGlobErr] = errs;
     A.ws.glob[kGlobCounter] = 0;
   }
-  if (Utot == 0) {
-    for (int k = tid; k < W; k += 256) A.ws.wg_seg[k] = -1;
-    for (int si = tid; si < S; si += 256) {
-      A.ws.seg_klo[si] = 0;
-      A.ws.seg_khi[si] = -1;
-    }
-    return;
-  }
+  if (Wp == 0) return;
   for (int si = tid; si < S; si += 256) {
     const int u = __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED);
     const int P = A.ws.seg_P[si];  // written by this thread above
-    const int64_t UU = Utot, WW = W;
-    // workgroups k with floor(k U / W) in [P, P + u)
-    const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;
-    const int64_t k_hi = u > 0 ? ((int64_t)(P + u) * WW + UU - 1) / UU - 1 : k_lo - 1;
+    if (u == 0) {
+      A.ws.seg_plo[si] = 0;
+      A.ws.seg_phi[si] = -1;
+      continue;
+    }
+    const int64_t UU = Utot, WW = Wp;
+    // attend workgroup k covers entries [floor(k U / W'), floor((k+1) U / W'))
+    const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;            // first k starting in the segment
+    const int64_t k_hi = ((int64_t)(P + u) * WW + UU - 1) / UU - 1;  // last k starting in the segment
     for (int64_t k = k_lo; k <= k_hi && k < WW; ++k) A.ws.wg_seg[k] = si;
-    A.ws.seg_klo[si] = (int)k_lo;
-    A.ws.seg_khi[si] = (int)(k_hi < WW ? k_hi : WW - 1);
+    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;             // workgroup holding entry P
+    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;             // workgroup holding entry P+u-1
+    A.ws.seg_plo[si] = (int)(kf + si);
+    A.ws.seg_phi[si] = (int)(kl + si);
   }
 }
 
