@@ -39,20 +39,15 @@ struct AttendArgs {
 };
 
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(G <= 4 ? 2 : 1))) void k_attend(AttendArgs A) {
+__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu((T::kBytes == 2 || D == 64) && G <= 4 ? 2 : 1))) void k_attend(AttendArgs A) {
   using L = TileLayout<T::kBytes, D>;
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
   constexpr bool kBf16 = T::kBytes == 2;
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
-  const int k = blockIdx.x;
-  const int Wp = A.ws.glob[kGlobWeff];
-  if (k >= Wp) return;
+  const int Wp = A.ws.glob[kGlobWeff];  // ranges with work: min(R * grid, Utot)
   const int64_t Utot = A.ws.glob[kGlobUtot];
-  int64_t lo = (int64_t)k * Utot / Wp;
-  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
-  int s = A.ws.wg_seg[k];
   const int HKV = A.d.HKV, HQ = A.d.HQ, MB = A.d.MB;
   const float scale = A.p.scale, beta = A.p.beta;
 
@@ -67,6 +62,12 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
 
+  // workgroup b takes ranges b, b + grid, b + 2 grid, ...: far-apart parts of the
+  // entry list, so every workgroup sees the same mix of (sequence, KV head) segments
+  for (int k = blockIdx.x; k < Wp; k += gridDim.x) {
+  int64_t lo = (int64_t)k * Utot / Wp;
+  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  int s = A.ws.wg_seg[k];
   while (lo < hi) {
     int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
     while (lo >= (int64_t)P + Us) {
@@ -323,6 +324,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     __syncthreads();
     lo = (int64_t)P + e1;
     ++s;
+  }
   }
 }
 

@@ -198,8 +198,21 @@ eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, 
   return ETA_OK;
 }
 
+// ranges per attend workgroup: far-apart parts of the work list average out
+// memory-channel and XCD speed differences between workgroups
+int attend_rounds(int grid) {
+  int R = 4;
+  if (const char* env = getenv("ETA_ATTEND_ROUNDS")) {
+    const int v = atoi(env);
+    if (v >= 1) R = v;
+  }
+  while (R > 1 && (int64_t)R * grid > kMaxAttendWgs) --R;
+  return R;
+}
+
 eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
-  const int W = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
+  const int grid = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
+  const int W = grid * attend_rounds(grid);
   hipError_t e = hipSuccess;
   switch (phase) {
     case ETA_PHASE_SCREEN:
@@ -207,7 +220,7 @@ eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
       if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, W, st);
       break;
     case ETA_PHASE_ATTEND:
-      e = launch_attend(P.c, P.s, P.p, P.d, P.ws, W, st);
+      e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);
       break;
     case ETA_PHASE_MERGE:
       e = launch_merge(P.d, P.p, P.ws, st);

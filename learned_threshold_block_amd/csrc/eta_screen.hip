@@ -242,7 +242,7 @@ struct FinArgs {
   SeqView s;
   Dims d;
   Ws ws;
-  int W;  // attend grid size
+  int W;  // attend ranges: rounds x attend grid
 };
 
 // exclusive scan of one int per thread over a 256-thread workgroup
