@@ -38,32 +38,73 @@ struct AttendArgs {
   Ws ws;
 };
 
+// Entries [c, c + cnt) of the segment's compacted lists, one per lane
+// (lane < cnt): the tile whose prefix covers the index is found by binary
+// search over the prefix in LDS (index ntn is the rescue tile).
+__device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2* tents, int ntn, int NT,
+                                                int c, int cnt, int lane) {
+  int2 ev = make_int2(0, 0);
+  if (lane < cnt) {
+    const int x = c + lane;
+    int lo_v = 0, hi_v = ntn;
+    while (lo_v < hi_v) {
+      const int mid = (lo_v + hi_v + 1) >> 1;
+      if (toff_lds[mid] <= x) lo_v = mid;
+      else hi_v = mid - 1;
+    }
+    const int phys = lo_v < ntn ? lo_v : NT;
+    ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
+  }
+  return ev;
+}
+
+// Claim of kClaim consecutive entries of the workgroup's current part through
+// an LDS counter (the fastest wavefronts take the most entries).
+__device__ __forceinline__ int claim_lds(int* ctr, int lane) {
+  int v = 0;
+  if (lane == 0) v = atomicAdd(ctr, kClaim);
+  return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Wavefronts per attend workgroup: eight (two per SIMD, one workgroup per CU)
+// when a wavefront fits in 256 VGPRs, else four with the full register file.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu((T::kBytes == 2 || D == 64) && G <= 4 ? 2 : 1))) void k_attend(AttendArgs A) {
+constexpr int attend_waves() {
+  return ((T::kBytes == 2 || D == 64) && G <= 4) ? 8 : 4;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__((64 * attend_waves<T, D, G>()))
+__attribute__((amdgpu_waves_per_eu((attend_waves<T, D, G>() / 4), (attend_waves<T, D, G>() / 4))))
+void k_attend(AttendArgs A) {
   using L = TileLayout<T::kBytes, D>;
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
+  constexpr int NW = attend_waves<T, D, G>();  // wavefronts per workgroup
+  constexpr int NTH = 64 * NW;
   constexpr bool kBf16 = T::kBytes == 2;
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
-  const int Wp = A.ws.glob[kGlobWeff];  // ranges with work: min(R * grid, Utot)
+  const int Wp = A.ws.glob[kGlobWeff];  // ranges with work: min(ranges, Utot)
   const int64_t Utot = A.ws.glob[kGlobUtot];
-  const int HKV = A.d.HKV, HQ = A.d.HQ, MB = A.d.MB;
+  const int HKV = A.d.HKV, HQ = A.d.HQ;
   const float scale = A.p.scale, beta = A.p.beta;
 
-  __shared__ __attribute__((aligned(16))) float p_lds[4][G][64];
-  __shared__ float ml_lds[4][G][2];
-  __shared__ float acc_lds[4][G][D];
+  __shared__ __attribute__((aligned(16))) float p_lds[NW][G][64];
+  __shared__ float ml_lds[NW][G][2];
+  __shared__ float acc_lds[NW][G][D];
   __shared__ int toff_lds[kMaxBlocksPerSeq / kTile + 2];
+  __shared__ int ctr_lds;
   const int NT = A.d.NT;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
+  const St* kbase = (const St*)A.c.k;
+  const St* vbase = (const St*)A.c.v;
 
-  // workgroup b takes ranges b, b + grid, b + 2 grid, ...: far-apart parts of the
-  // entry list, so every workgroup sees the same mix of (sequence, KV head) segments
+  // workgroup b takes ranges b, b + grid, ... of the entry list (one range by default)
   for (int k = blockIdx.x; k < Wp; k += gridDim.x) {
   int64_t lo = (int64_t)k * Utot / Wp;
   const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
@@ -110,47 +151,40 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
     }
 
-    // the segment's tile prefix, for locating entries in the per-tile lists
+    // the segment's tile prefix (to locate entries in the per-tile lists), and
+    // the part's claim counter
     const int ntn = A.ws.seg_ntn[s];
     {
       const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
-      for (int v = threadIdx.x; v <= ntn + 1; v += kAttendThreads) toff_lds[v] = toff[v];
+      for (int v = threadIdx.x; v <= ntn + 1; v += NTH) toff_lds[v] = toff[v];
     }
+    if (threadIdx.x == 0) ctr_lds = e0;
     __syncthreads();
     const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
 
-    const int span = e1 - e0;
-    const int cnt = span > wave ? (span - wave + 3) / 4 : 0;
-    const St* kbase = (const St*)A.c.k;
-    const St* vbase = (const St*)A.c.v;
-
-    for (int b0 = 0; b0 < cnt; b0 += 64) {
-      const int bc = cnt - b0 < 64 ? cnt - b0 : 64;
-      int2 ev = make_int2(0, 0);
-      if (lane < bc) {
-        const int x = e0 + wave + 4 * (b0 + lane);
-        int lo_v = 0, hi_v = ntn;  // largest tile v <= ntn with toff[v] <= x (ntn: rescue tile)
-        while (lo_v < hi_v) {
-          const int mid = (lo_v + hi_v + 1) >> 1;
-          if (toff_lds[mid] <= x) lo_v = mid;
-          else hi_v = mid - 1;
-        }
-        const int phys = lo_v < ntn ? lo_v : NT;
-        ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
-      }
-      int page = __builtin_amdgcn_readlane(ev.x, 0);
-      int jm = __builtin_amdgcn_readlane(ev.y, 0);
+    // claims, two deep: the batch being streamed, the next one (resolved while
+    // the current one streams) and the claim after it
+    const int c0 = claim_lds(&ctr_lds, lane);
+    int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
+    if (bc > 0) {
+      int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane);
+      const int c1 = claim_lds(&ctr_lds, lane);
+      int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
+      int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane);
+      int it = 0;
+      int page_nx = __builtin_amdgcn_readlane(ev.x, 0);
+      int jm_nx = __builtin_amdgcn_readlane(ev.y, 0);
 
       uint4 kr[NI][CPL], vr[NI][CPL];
       {
-        const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
+        const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
       }
-      for (int it = 0; it < bc; ++it) {
-        const int cur_page = page, cur_jm = jm;
+      for (;;) {
+        const int cur_page = page_nx, cur_jm = jm_nx;
         {
           const St* vt = vbase + ((int64_t)cur_page * HKV + g) * (kBlock * D);
 #pragma unroll
@@ -158,9 +192,23 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int c = 0; c < CPL; ++c) vr[i][c] = *(const uint4*)(vt + loff[c] + i * RPI * D);
         }
-        if (it + 1 < bc) {
-          page = __builtin_amdgcn_readlane(ev.x, it + 1);
-          jm = __builtin_amdgcn_readlane(ev.y, it + 1);
+        // next entry: from this batch, or the first of the next one
+        bool has_next = true;
+        if (++it >= bc) {
+          ev = evn;
+          bc = bcn;
+          it = 0;
+          if (bc > 0) {
+            const int c2 = claim_lds(&ctr_lds, lane);
+            bcn = c2 < e1 ? min(kClaim, e1 - c2) : 0;
+            evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane);
+          } else {
+            has_next = false;
+          }
+        }
+        if (has_next) {
+          page_nx = __builtin_amdgcn_readlane(ev.x, it);
+          jm_nx = __builtin_amdgcn_readlane(ev.y, it);
         }
         const uint32_t hmask = (uint32_t)cur_jm & 0xffu;
         const int j = cur_jm >> 8;
@@ -191,16 +239,16 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
             pd[i] = a;
           }
           transpose_reduce<LPR>(pd, lane);
-          const float S = pd[0] * scale;
-          const float x = beta * (S - tau[h]);
+          const float S_ = pd[0] * scale;
+          const float x = beta * (S_ - tau[h]);
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
-          float st = S * sg;
-          if (tail && tok >= rem) st = -__builtin_inff();
-          const float mt = group_max<LPR>(st);
+          float sv = S_ * sg;
+          if (tail && tok >= rem) sv = -__builtin_inff();
+          const float mt = group_max<LPR>(sv);
           const float mnew = fmaxf(m[h], mt);
           const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
           const float alpha = fast_exp(m[h] - muse);
-          const float p = fast_exp(st - muse);
+          const float p = fast_exp(sv - muse);
           l[h] = fmaf(l[h], alpha, p);
 #pragma unroll
           for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
@@ -209,8 +257,8 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
         }
 
         // ---- K of the next tile streams while the values are accumulated
-        if (it + 1 < bc) {
-          const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
+        if (has_next) {
+          const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
 #pragma unroll
           for (int i = 0; i < NI; ++i)
 #pragma unroll
@@ -262,10 +310,11 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
         }
         __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         __builtin_amdgcn_wave_barrier();
+        if (!has_next) break;
       }
     }
 
-    // ---- merge the rows of lanes, then the four wavefronts, write one partial
+    // ---- merge the rows of lanes, then the wavefronts, write one partial
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float lr = group_sum<LPR>(l[h]);
@@ -296,16 +345,16 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
     }
     __syncthreads();
     const int64_t piece = (int64_t)k + s;
-    for (int h = wave; h < G; h += 4) {
-      float Mw[4], M = -__builtin_inff();
+    for (int h = wave; h < G; h += NW) {
+      float Mw[NW], M = -__builtin_inff();
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         Mw[w] = ml_lds[w][h][0];
         M = fmaxf(M, Mw[w]);
       }
-      float sc[4], Lsum = 0.f;
+      float sc[NW], Lsum = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         sc[w] = Mw[w] == -__builtin_inff() ? 0.f : fast_exp(Mw[w] - M);
         Lsum = fmaf(sc[w], ml_lds[w][h][1], Lsum);
       }
@@ -313,7 +362,7 @@ __global__ __launch_bounds__(kAttendThreads) __attribute__((amdgpu_waves_per_eu(
       for (int dd = lane; dd < D; dd += 64) {
         float a = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) a = fmaf(sc[w], acc_lds[w][h][dd], a);
+        for (int w = 0; w < NW; ++w) a = fmaf(sc[w], acc_lds[w][h][dd], a);
         pa[dd] = a;
       }
       if (lane == 0) {
@@ -405,7 +454,7 @@ template <typename T, int D, int G>
 hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, int W, hipStream_t st) {
   AttendArgs a{c, s, p, d, ws};
-  hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(kAttendThreads), 0, st, a);
+  hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
   return hipGetLastError();
 }
 
@@ -425,7 +474,7 @@ template <typename T, int D, int G>
 int occupancy_impl() {
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G>),
-                                                   kAttendThreads, 0) != hipSuccess)
+                                                   64 * attend_waves<T, D, G>(), 0) != hipSuccess)
     return 1;
   return nb > 0 ? nb : 1;
 }

@@ -201,7 +201,7 @@ eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, 
 // ranges per attend workgroup: far-apart parts of the work list average out
 // memory-channel and XCD speed differences between workgroups
 int attend_rounds(int grid) {
-  int R = 4;
+  int R = 1;
   if (const char* env = getenv("ETA_ATTEND_ROUNDS")) {
     const int v = atoi(env);
     if (v >= 1) R = v;

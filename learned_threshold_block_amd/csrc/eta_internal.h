@@ -10,7 +10,7 @@ namespace eta {
 
 constexpr int kBlock = 64;          // tokens per KV block (one page)
 constexpr int kTile = 64;           // blocks screened per wavefront
-constexpr int kAttendThreads = 256; // four wavefronts per attend workgroup
+constexpr int kClaim = 2;           // entries per wavefront claim inside a workgroup
 constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace sizing)
 constexpr int kMaxBlocksPerSeq = 1 << 16;
 constexpr int kMaxGroup = 8;
