@@ -199,7 +199,14 @@ def test_rescue_path():
     check_output(wl, res, o)
 
 
-def test_page_permutation_invariance():
+def _same_up_to_rounding(o1, o2):
+    """Work is claimed dynamically, so the float32 summation order may differ
+    between calls: equal to a few float32 ulps of the output scale."""
+    scale = float(np.max(np.abs(o1)))
+    assert float(np.max(np.abs(o1 - o2))) <= 1e-6 * scale
+
+
+def test_page_permutation_invariance(monkeypatch):
     wl, summ = prepared("cfg1", seq_lens=[64 * 90 + 7, 3333], h_q=8, h_kv=2)
     dev = Dev(wl)
     dev.build()
@@ -208,7 +215,10 @@ def test_page_permutation_invariance():
     dev2 = Dev(wl2)
     dev2.build()
     o2 = dev2.decode()
-    assert np.array_equal(o1, o2)
+    _same_up_to_rounding(o1, o2)
+    # with the static assignment the physical page order is invisible bit for bit
+    monkeypatch.setenv("ETA_DETERMINISTIC", "1")
+    assert np.array_equal(dev.decode(), dev2.decode())
 
 
 def test_split_count_invariance(monkeypatch):
@@ -224,13 +234,22 @@ def test_split_count_invariance(monkeypatch):
     monkeypatch.delenv("ETA_ATTEND_WGS")
 
 
-def test_deterministic():
-    wl, summ = prepared("cfg1", seq_lens=[64 * 150 + 1], h_q=8, h_kv=2)
+def test_repeatable(monkeypatch):
+    """Default mode: repeated calls agree to float32 rounding; ETA_DETERMINISTIC=1:
+    bitwise, and within rounding of the default mode."""
+    wl, summ = prepared("cfg1", seq_lens=[64 * 150 + 1, 64 * 40], h_q=8, h_kv=2)
+    res = oracle_decode(wl, summaries=summ)
     dev = Dev(wl)
     dev.build()
     o1 = dev.decode()
     o2 = dev.decode()
-    assert np.array_equal(o1, o2)
+    _same_up_to_rounding(o1, o2)
+    monkeypatch.setenv("ETA_DETERMINISTIC", "1")
+    d1 = dev.decode()
+    d2 = dev.decode()
+    assert np.array_equal(d1, d2)
+    _same_up_to_rounding(o1, d1)
+    check_output(wl, res, d1)
 
 
 def test_junk_tail_rows_do_not_leak():
