@@ -11,22 +11,24 @@
 //
 // Work split: the screen produced, per (sequence, KV head), a contiguous list
 // of admitted blocks. Their concatenation (Utot entries) is cut into W' equal
-// ranges, one per attend workgroup (W' = min(grid, Utot), grid sized to fill
-// every CU once), so every workgroup streams the same number of 32 KB tiles
+// ranges, one per attend workgroup (W' = min(grid, Utot), grid = one
+// workgroup per CU), so every workgroup streams the same number of tiles
 // whatever the density or the length mix. A range that spans several
 // (sequence, KV head) segments emits one partial per segment.
 //
-// Inside a workgroup the four wavefronts take every fourth entry. A wavefront
-// owns a whole tile: 16-byte loads of one 64 x d tile (lane (r, cb) holds rows
-// RPI*i + r, 8 bf16 columns), keys consumed by v_dot2 bf16 products into
-// per-lane partial logits, finished by a transposing DPP reduction that leaves
-// one token's logit per lane. The gate and the online softmax run per lane in
-// float32 (running max per row of lanes); the weights go through 1 KB of LDS
-// to the lanes holding the matching value rows. V of tile i streams while the
-// logits of tile i are computed, K of tile i+1 while the values of tile i are
-// accumulated. No float atomics: results are bitwise reproducible.
-#include <stdlib.h>
-
+// Inside a workgroup the wavefronts claim kClaim entries at a time from an LDS
+// counter, so the wavefronts that run faster (older waves get issue priority on
+// a SIMD) take more tiles. With ETA_DETERMINISTIC=1 in the environment the
+// claims are static instead (wavefront w takes claims w, w + NW, ...) and the
+// result is bitwise reproducible; by default repeated calls agree to float32
+// rounding. A wavefront owns a whole tile: 16-byte loads of one 64 x d tile
+// (lane (r, cb) holds rows RPI*i + r, 8 bf16 columns), keys consumed by v_dot2
+// bf16 products into per-lane partial logits, finished by a transposing DPP
+// reduction that leaves one token's logit per lane. The gate and the online
+// softmax run per lane in float32 (running max per row of lanes); the weights
+// go through LDS to the lanes holding the matching value rows. V of tile i
+// streams while the logits of tile i are computed, K of tile i+1 while the
+// values of tile i are accumulated. No float atomics anywhere.
 #include "eta_device.h"
 
 namespace eta {
@@ -38,7 +40,7 @@ struct AttendArgs {
   DecodeParams p;
   Dims d;
   Ws ws;
-  int deterministic;  // 1: static entry assignment and no helpers (bitwise reproducible)
+  int deterministic;  // fixed claims instead of the LDS counter
 };
 
 // Entries [c, c + cnt) of the segment's compacted lists, one per lane
@@ -61,12 +63,13 @@ __device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2*
   return ev;
 }
 
-// Claim of kClaim consecutive entries of a part through its counter (the
-// fastest wavefronts, of any workgroup working on the part, take the most).
-// In deterministic mode the n-th claim of wavefront w is fixed instead:
-// entries (n * NW + w) * kClaim onwards.
-__device__ __forceinline__ int claim(int* ctr, int lane, bool fixed, int& nclaim, int wave, int nw) {
-  if (fixed) return (nclaim++ * nw + wave) * kClaim;
+// Claim of kClaim consecutive entries of the workgroup's current part: through
+// an LDS counter (the fastest wavefronts take the most entries), or, with
+// `fixed`, the wavefront's static share (claims wave, wave + NW, ... counted
+// from e0), which makes the result independent of timing.
+__device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nclaim, int wave, int nw,
+                                         int e0) {
+  if (fixed) return e0 + (nclaim++ * nw + wave) * kClaim;
   int v = 0;
   if (lane == 0) v = atomicAdd(ctr, kClaim);
   return __builtin_amdgcn_readfirstlane(v);
@@ -100,6 +103,7 @@ void k_attend(AttendArgs A) {
   __shared__ float ml_lds[NW][G][2];
   __shared__ float acc_lds[NW][G][D];
   __shared__ int toff_lds[kMaxBlocksPerSeq / kTile + 2];
+  __shared__ int ctr_lds;
   const int NT = A.d.NT;
 
   // lane offset (elements) of load (i=0, c) inside a tile
@@ -109,96 +113,20 @@ void k_attend(AttendArgs A) {
   const St* kbase = (const St*)A.c.k;
   const St* vbase = (const St*)A.c.v;
 
-  __shared__ int s_pick, s_slot;
-  __shared__ int s_best_v[NW], s_best_p[NW];
-  const int nparts = Wp + A.d.S;
-  const int64_t nhome = (int64_t)kMaxAttendWgs + A.d.S;
-
-  // jobs: the parts of the workgroup's own range(s) in order, then help on the
-  // parts with the most unclaimed entries
-  int k = blockIdx.x;
-  int64_t lo = 0, hi = 0;
-  int s = 0;
-  if (k < Wp) {
-    lo = (int64_t)k * Utot / Wp;
-    hi = (int64_t)(k + 1) * Utot / Wp;
-    s = A.ws.wg_seg[k];
-  }
-  for (;;) {
-    int jp, je0, jlen;
-    int64_t jslot;
-    if (k < Wp) {
-      if (lo >= hi) {
-        k += gridDim.x;
-        if (k < Wp) {
-          lo = (int64_t)k * Utot / Wp;
-          hi = (int64_t)(k + 1) * Utot / Wp;
-          s = A.ws.wg_seg[k];
-        }
-        continue;
-      }
-      int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
-      while (lo >= (int64_t)P + Us) {
-        ++s;
-        P = A.ws.seg_P[s];
-        Us = A.ws.seg_U[s];
-      }
-      const int e0 = (int)(lo - P);
-      const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
-      jp = k + s;
-      je0 = e0;
-      jlen = e1 - e0;
-      jslot = jp;
-      lo = (int64_t)P + e1;
-    } else {
-      if (A.deterministic) return;
-      int bv = 4 * kClaim, bp = -1;  // help only where at least a few claims remain
-      for (int pp = threadIdx.x; pp < nparts; pp += NTH) {
-        const int len = A.ws.part_info[pp].w;
-        if (len <= 0) continue;
-        const int left = len - __atomic_load_n(&A.ws.part_ctr[pp], __ATOMIC_RELAXED);
-        if (left > bv && __atomic_load_n(&A.ws.part_steals[pp], __ATOMIC_RELAXED) < kSteal) {
-          bv = left;
-          bp = pp;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const int ov = __shfl_xor(bv, o, 64), op = __shfl_xor(bp, o, 64);
-        if (ov > bv || (ov == bv && op >= 0 && (bp < 0 || op < bp))) {
-          bv = ov;
-          bp = op;
-        }
-      }
-      if (lane == 0) {
-        s_best_v[wave] = bv;
-        s_best_p[wave] = bp;
-      }
-      __syncthreads();
-      if (threadIdx.x == 0) {
-        int v = 0, pb = -1;
-        for (int w = 0; w < NW; ++w)
-          if (s_best_p[w] >= 0 && (s_best_v[w] > v || (s_best_v[w] == v && s_best_p[w] < pb))) {
-            v = s_best_v[w];
-            pb = s_best_p[w];
-          }
-        int sl = -1;
-        if (pb >= 0) sl = atomicAdd(&A.ws.part_steals[pb], 1);
-        s_pick = pb;
-        s_slot = sl;
-      }
-      __syncthreads();
-      const int pb = s_pick, sl = s_slot;
-      if (pb < 0) return;
-      if (sl >= kSteal) continue;  // another workgroup took the last helper slot
-      const int4 info = A.ws.part_info[pb];
-      s = info.y;
-      jp = pb;
-      je0 = info.z;
-      jlen = info.w;
-      jslot = nhome + (int64_t)pb * kSteal + sl;
+  // workgroup b takes ranges b, b + grid, ... of the entry list (one range by default)
+  for (int k = blockIdx.x; k < Wp; k += gridDim.x) {
+  int64_t lo = (int64_t)k * Utot / Wp;
+  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  int s = A.ws.wg_seg[k];
+  while (lo < hi) {
+    int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
+    while (lo >= (int64_t)P + Us) {
+      ++s;
+      P = A.ws.seg_P[s];
+      Us = A.ws.seg_U[s];
     }
-    const int e1 = je0 + jlen;
+    const int e0 = (int)(lo - P);
+    const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
     const int n = s / HKV, g = s % HKV;
     const int seq_len = A.s.lens[n];
     const int nfull = seq_len / kBlock;
@@ -239,19 +167,19 @@ void k_attend(AttendArgs A) {
       const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
       for (int v = threadIdx.x; v <= ntn + 1; v += NTH) toff_lds[v] = toff[v];
     }
+    if (threadIdx.x == 0) ctr_lds = e0;
     __syncthreads();
-    int* ctr = A.ws.part_ctr + jp;
     const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
 
     // claims, two deep: the batch being streamed, the next one (resolved while
     // the current one streams) and the claim after it
     const bool fixed = A.deterministic != 0;
     int nclaim = 0;
-    const int c0 = je0 + claim(ctr, lane, fixed, nclaim, wave, NW);
+    const int c0 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
     int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
     if (bc > 0) {
       int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane);
-      const int c1 = je0 + claim(ctr, lane, fixed, nclaim, wave, NW);
+      const int c1 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
       int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
       int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane);
       int it = 0;
@@ -282,7 +210,7 @@ void k_attend(AttendArgs A) {
           bc = bcn;
           it = 0;
           if (bc > 0) {
-            const int c2 = je0 + claim(ctr, lane, fixed, nclaim, wave, NW);
+            const int c2 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
             bcn = c2 < e1 ? min(kClaim, e1 - c2) : 0;
             evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane);
           } else {
@@ -427,7 +355,7 @@ void k_attend(AttendArgs A) {
       }
     }
     __syncthreads();
-    const int64_t piece = jslot;
+    const int64_t piece = (int64_t)k + s;
     for (int h = wave; h < G; h += NW) {
       float Mw[NW], M = -__builtin_inff();
 #pragma unroll
@@ -454,7 +382,9 @@ void k_attend(AttendArgs A) {
       }
     }
     __syncthreads();
-    if (k < Wp) ++s;
+    lo = (int64_t)P + e1;
+    ++s;
+  }
   }
 }
 
@@ -480,26 +410,12 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   const int g = h / G, hl = h % G;
   const int s = n * A.d.HKV + g;
   const int plo = A.ws.seg_plo[s], phi = A.ws.seg_phi[s];
-  // partials of the segment: the owner run of each part plo..phi, then the
-  // helper runs (slot nhome + p*kSteal + i for i < helpers of part p)
-  const int nown = phi >= plo ? phi - plo + 1 : 0;
-  const int nvirt = nown * (1 + kSteal);
-  const int64_t nhome = (int64_t)kMaxAttendWgs + A.d.S;
-  auto slot_of = [&](int q) -> int64_t {
-    if (q < nown) return plo + q;
-    const int j = q - nown, pp = plo + j / kSteal, i = j % kSteal;
-    if (i >= min(A.ws.part_steals[pp], kSteal)) return -1;
-    return nhome + (int64_t)pp * kSteal + i;
-  };
   __shared__ float s_red[4];
   __shared__ float4 s_acc[PGN][CG];
   __shared__ float s_l[PGN];
 
   float M = -__builtin_inff();
-  for (int q = tid; q < nvirt; q += 256) {
-    const int64_t sl = slot_of(q);
-    if (sl >= 0) M = fmaxf(M, A.ws.part_ml[(sl * G + hl) * 2]);
-  }
+  for (int p = plo + tid; p <= phi; p += 256) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
   if (lane == 0) s_red[wave] = M;
@@ -510,11 +426,9 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float lsum = 0.f;
 #pragma unroll 4
-  for (int q = pg; q < nvirt; q += PGN) {
-    const int64_t sl = slot_of(q);
-    if (sl < 0) continue;
-    const float2 ml = *(const float2*)&A.ws.part_ml[(sl * G + hl) * 2];
-    const float4 a = *(const float4*)&A.ws.part_acc[(sl * G + hl) * D + cg * 4];
+  for (int p = plo + pg; p <= phi; p += PGN) {
+    const float2 ml = *(const float2*)&A.ws.part_ml[((int64_t)p * G + hl) * 2];
+    const float4 a = *(const float4*)&A.ws.part_acc[((int64_t)p * G + hl) * D + cg * 4];
     const float wgt = ml.x == -__builtin_inff() ? 0.f : fast_exp(ml.x - M);
     lsum = fmaf(wgt, ml.y, lsum);
     acc.x = fmaf(wgt, a.x, acc.x);
@@ -550,8 +464,8 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
 template <typename T, int D, int G>
 hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, int W, hipStream_t st) {
-  const char* env = getenv("ETA_DETERMINISTIC");
-  AttendArgs a{c, s, p, d, ws, (env && env[0] == '1') ? 1 : 0};
+  const char* det = getenv("ETA_DETERMINISTIC");
+  AttendArgs a{c, s, p, d, ws, det != nullptr && det[0] == '1'};
   hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
   return hipGetLastError();
 }

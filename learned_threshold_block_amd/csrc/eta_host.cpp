@@ -27,8 +27,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   };
   const size_t S = (size_t)d.S, NT = (size_t)d.NT, G = (size_t)d.G;
   const size_t nq = (size_t)d.N * d.HQ;
-  const size_t parts = (size_t)kMaxAttendWgs + S;
-  const size_t pieces = parts * (1 + kSteal);
+  const size_t pieces = (size_t)kMaxAttendWgs + S;
   Ws w;
   w.glob = (int32_t*)take(sizeof(int32_t) * kGlobCount);
   w.tau = (float*)take(sizeof(float) * nq);
@@ -47,9 +46,6 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.seg_phi = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
   w.wg_seg = (int32_t*)take(sizeof(int32_t) * kMaxAttendWgs);
-  w.part_info = (int4*)take(sizeof(int4) * parts);
-  w.part_ctr = (int32_t*)take(sizeof(int32_t) * parts);
-  w.part_steals = (int32_t*)take(sizeof(int32_t) * parts);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
   w.st_tokens = (int64_t*)take(sizeof(int64_t) * nq);
   w.st_rescued = (int32_t*)take(sizeof(int32_t) * nq);

@@ -10,8 +10,7 @@ namespace eta {
 
 constexpr int kBlock = 64;          // tokens per KV block (one page)
 constexpr int kTile = 64;           // blocks screened per wavefront
-constexpr int kClaim = 2;           // entries per wavefront claim
-constexpr int kSteal = 2;           // workgroups that may help finish one part
+constexpr int kClaim = 2;           // entries per wavefront claim inside a workgroup
 constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace sizing)
 constexpr int kMaxBlocksPerSeq = 1 << 16;
 constexpr int kMaxGroup = 8;
@@ -54,16 +53,11 @@ struct Ws {
   int32_t* seg_phi;     // [S]          last partial slot of the segment
   int32_t* seg_err;     // [S]
   int32_t* wg_seg;      // [kMaxAttendWgs] segment holding each attend workgroup's first entry
-  int4* part_info;      // [kMaxAttendWgs + S] part p = k + s: (k, s, first entry in s, entries; 0 = unused)
-  int32_t* part_ctr;    // [kMaxAttendWgs + S] entries of the part claimed so far
-  int32_t* part_steals; // [kMaxAttendWgs + S] helper runs started on the part
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
   int64_t* st_tokens;   // [N*HQ]
   int32_t* st_rescued;  // [N*HQ]
-  float* part_ml;       // [(kMaxAttendWgs + S) * (1 + kSteal)][G][2]  running max and sum
-  float* part_acc;      // [(kMaxAttendWgs + S) * (1 + kSteal)][G][D]  unnormalised outputs
-                        // slot p: the owner's run on part p; slot (kMaxAttendWgs + S) + p*kSteal + i:
-                        // the i-th helper run on part p
+  float* part_ml;       // [(kMaxAttendWgs + S)][G][2]  split running max and sum
+  float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs
 };
 
 size_t workspace_layout(const Dims& d, void* base, Ws* ws);  // base may be null (size only)

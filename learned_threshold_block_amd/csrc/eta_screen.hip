@@ -452,15 +452,6 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     A.ws.glob[kGlobCounter] = 0;
   }
   if (Wp == 0) return;
-  // parts: the intersections of attend ranges and segments, id k + s (ids of
-  // consecutive parts differ by 1 or 2: a range and a segment may end together)
-  const int nparts = Wp + S;
-  for (int pp = tid; pp < nparts; pp += 256) {
-    A.ws.part_info[pp] = make_int4(0, 0, 0, 0);
-    A.ws.part_ctr[pp] = 0;
-    A.ws.part_steals[pp] = 0;
-  }
-  __syncthreads();
   for (int si = tid; si < S; si += 256) {
     const int u = __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED);
     const int P = A.ws.seg_P[si];  // written by this thread above
@@ -470,19 +461,14 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
       continue;
     }
     const int64_t UU = Utot, WW = Wp;
-    // attend range k covers entries [floor(k U / W'), floor((k+1) U / W'))
+    // attend workgroup k covers entries [floor(k U / W'), floor((k+1) U / W'))
     const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;            // first k starting in the segment
     const int64_t k_hi = ((int64_t)(P + u) * WW + UU - 1) / UU - 1;  // last k starting in the segment
     for (int64_t k = k_lo; k <= k_hi && k < WW; ++k) A.ws.wg_seg[k] = si;
-    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;             // range holding entry P
-    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;             // range holding entry P+u-1
+    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;             // workgroup holding entry P
+    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;             // workgroup holding entry P+u-1
     A.ws.seg_plo[si] = (int)(kf + si);
     A.ws.seg_phi[si] = (int)(kl + si);
-    for (int64_t k = kf; k <= kl; ++k) {
-      const int64_t rlo = k * UU / WW, rhi = (k + 1) * UU / WW;
-      const int64_t a = rlo > P ? rlo : P, b = rhi < (int64_t)P + u ? rhi : (int64_t)P + u;
-      A.ws.part_info[k + si] = make_int4((int)k, si, (int)(a - P), (int)(b - a));
-    }
   }
 }
 
