@@ -31,6 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+# sources whose change invalidates a stored counter measurement of the attend kernel
+ATTEND_SOURCES = ("learned_threshold_block_amd/csrc/eta_attend.hip", "learned_threshold_block_amd/csrc/eta_device.h",
+                  "learned_threshold_block_amd/csrc/eta_internal.h")
 
 
 def log(msg):
@@ -42,13 +46,63 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="cfg3", choices=["cfg1", "cfg2", "cfg3", "cfg4"])
+    p.add_argument("--workload", default="seq_512k", choices=["seq_32k", "batch_4x128k", "seq_512k", "ragged_16"])
     p.add_argument("--density", type=float, default=None, help="per-head target density override")
     p.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
-    p.add_argument("--sweep", action="store_true", help="also time cfg2 at 10/38/70/100%% density")
+    p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB `steps` times (calibrates the "
+                        "HBM byte counters) and exit")
     return p.parse_args()
+
+
+def attend_sources_sha256():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in ATTEND_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload_key):
+    """HBM bytes per attend launch from the committed counter summary (FETCH_SIZE
+    + WRITE_SIZE, scaled by the copy-kernel calibration), or None when there is
+    none for this workload or the attend kernel's sources changed since."""
+    import glob
+    import re
+
+    for path in sorted(glob.glob(os.path.join(PROFILES, "*traffic*.md"))):
+        with open(path) as f:
+            text = f.read()
+        fields = dict(re.findall(r"^- (\w+): `([^`]*)`", text, flags=re.M))
+        if fields.get("workload_key") != workload_key:
+            continue
+        if fields.get("attend_sources_sha256") != attend_sources_sha256():
+            return None
+        return int(fields["traffic_bytes_per_launch"])
+    return None
+
+
+def copy_probe(mib, steps):
+    """A plain copy of a known size, for the counter calibration."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    us = (time.perf_counter() - t0) / steps * 1e6
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "steps": steps,
+                      "us_per_copy": round(us, 2), "gbs_read_plus_write": round(2 * n * 4 / (us * 1e-6) / 1e9, 1)}),
+          flush=True)
 
 
 class Setup:
@@ -145,24 +199,25 @@ def time_steps(S, steps, warmup):
 
 
 def time_phases(S, steps):
-    """Per-phase durations (us) from HIP events recorded on the launch stream
-    between the three phases of each step (the events add small gaps, so this
-    loop is kept apart from the step timing)."""
+    """Average duration (us) of each phase's launches: HIP events on the launch
+    stream around `steps` back-to-back launches of that phase alone (screen +
+    finalize, attend, merge). Each phase is idempotent given the previous
+    phase's workspace contents, so repeating it measures the kernel itself
+    without the gaps that events between phases would add to a step."""
     eta, torch = S.eta, S.torch
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     S.run()
     torch.cuda.synchronize()
-    for i in range(steps):
-        ev[i][0].record()
-        S.run(phase=eta.ETA_PHASE_SCREEN)
-        ev[i][1].record()
-        S.run(phase=eta.ETA_PHASE_ATTEND)
-        ev[i][2].record()
-        S.run(phase=eta.ETA_PHASE_MERGE)
-        ev[i][3].record()
-    torch.cuda.synchronize()
-    ph = np.array([[ev[i][k].elapsed_time(ev[i][k + 1]) for k in range(3)] for i in range(steps)])
-    return ph.mean(axis=0) * 1e3
+    out = []
+    for phase in (eta.ETA_PHASE_SCREEN, eta.ETA_PHASE_ATTEND, eta.ETA_PHASE_MERGE):
+        S.run(phase=phase)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            S.run(phase=phase)
+        e1.record()
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) / steps * 1e3)
+    return np.array(out)
 
 
 def cpu_baseline(S, budget_s):
@@ -208,6 +263,9 @@ def main():
     import torch
     assert torch.cuda.is_available(), "needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        copy_probe(args.copy_probe, args.steps)
+        return
 
     S = Setup(args.workload, args.density)
     S.calibrate()
@@ -224,6 +282,8 @@ def main():
     G, D = wl.group, wl.d
     attend_bytes = U * 2 * 64 * D * esz + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
+    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}"
+    traffic = stored_traffic(workload_key)
     result = {
         "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",
         "value": round(us, 2),
@@ -238,8 +298,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": {"cfg1": "1 seq x 32768 ctx", "cfg2": "4 seq x 131072 ctx",
-                         "cfg3": "1 seq x 524288 ctx", "cfg4": "16 ragged seqs 4K-256K"}[args.workload]
+            "workload": {"seq_32k": "1 seq x 32768 ctx", "batch_4x128k": "4 seq x 131072 ctx",
+                         "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[args.workload]
                         + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
                         + f"{wl.tau_mode} thresholds, target per-head density "
                         + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys",
@@ -253,7 +313,7 @@ def main():
         "phase_us": {"screen": round(float(ph[0]), 2), "attend": round(float(ph[1]), 2),
                      "merge": round(float(ph[2]), 2)},
         "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_attend", "bytes_per_launch": attend_bytes},
     }
     if not args.no_dense:
@@ -282,7 +342,7 @@ def main():
         torch.cuda.empty_cache()
         sw = {}
         for dens in (0.10, 0.38, 0.70, 1.0):
-            S2 = Setup("cfg2", dens)
+            S2 = Setup("batch_4x128k", dens)
             S2.calibrate()
             st2, dh, du = S2.densities()
             k2, a2 = S2.step_bytes(st2)
@@ -292,10 +352,10 @@ def main():
                                         "density_union": round(du, 4),
                                         "achieved_gbs_kv": round(k2 / (us2 * 1e-6) / 1e9, 1),
                                         "attend_us": round(float(ph2[1]), 2)}
-            log(f"cfg2 {dens}: {us2:.1f} us, union {du:.3f}")
+            log(f"batch_4x128k {dens}: {us2:.1f} us, union {du:.3f}")
             del S2
             torch.cuda.empty_cache()
-        result["cfg2_density_sweep"] = sw
+        result["batch_4x128k_density_sweep"] = sw
     print(json.dumps(result), flush=True)
 
 

@@ -32,7 +32,7 @@ def tiny(seed, n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="lea
     """A tiny random workload with its threshold constant placed so that about
     `density` of the complete blocks pass (placement uses the module's own
     bound only to choose a number; the checks do not depend on it)."""
-    wl = W.make_workload("cfg1", seed=seed, n_seqs=n, seq_lens=list(lens), h_q=h_q, h_kv=h_kv,
+    wl = W.make_workload("seq_32k", seed=seed, n_seqs=n, seq_lens=list(lens), h_q=h_q, h_kv=h_kv,
                          d=d, kv_dtype=dtype, mode=mode, needles=0, lwb=lwb, a=a, beta=beta,
                          threads=1)
     if bias is None:

@@ -39,10 +39,10 @@ def run_case(name, **kw):
 
 # ----------------------------------------------------------------------------- records
 @pytest.mark.parametrize("name,kw", [
-    ("cfg0", {}),
-    ("cfg1", dict(seq_lens=[4096 + 17, 64 * 40], n_seqs=2)),
-    ("cfg1", dict(seq_lens=[1000, 3000], d=64)),
-    ("cfg0", dict(d=128, seq_lens=[2048 + 5, 640], h_q=4, h_kv=2)),
+    ("tiny_4k_f32", {}),
+    ("seq_32k", dict(seq_lens=[4096 + 17, 64 * 40], n_seqs=2)),
+    ("seq_32k", dict(seq_lens=[1000, 3000], d=64)),
+    ("tiny_4k_f32", dict(d=128, seq_lens=[2048 + 5, 640], h_q=4, h_kv=2)),
 ])
 def test_records_match_oracle_and_are_sound(name, kw):
     log(f"[records] {name} {kw}")
@@ -76,7 +76,7 @@ def test_record_rounding_edges():
     vals = [1 + 2 ** -11, 1 + 3 * 2 ** -11, -(2 + 2 ** -10), 2 ** -25, 3 * 2 ** -26, 2 ** -24 * 1.5,
             65504.0, 65519.0, 65520.0, 1e-8, 0.0, -0.0, 1000.3, 6.1e-5]
     n_pages = len(vals) + 4
-    wl = W.make_workload("cfg0", seq_len=64 * n_pages, needles=0)
+    wl = W.make_workload("tiny_4k_f32", seq_len=64 * n_pages, needles=0)
     for i, v in enumerate(vals):
         wl.k_pages[i, 0] = np.float32(v) + np.zeros((64, d), np.float32)
     # random values exactly representable, mean on a rounding boundary in random coordinates
@@ -103,7 +103,7 @@ def test_append_equals_bulk_build():
     """Appending tokens one at a time (records built when a block fills) gives
     the same bytes as building all records at once."""
     import learned_threshold_block_amd as eta
-    wl = W.make_workload("cfg1", seq_lens=[64 * 3 + 10, 64 * 2], h_q=8, h_kv=2, d=128, needles=0)
+    wl = W.make_workload("seq_32k", seq_lens=[64 * 3 + 10, 64 * 2], h_q=8, h_kv=2, d=128, needles=0)
     dev = Dev(wl)
     dev.build()
     torch.cuda.synchronize()
@@ -147,12 +147,12 @@ def test_append_equals_bulk_build():
 
 
 # ----------------------------------------------------------------------------- decode
-def test_cfg0_parity():
-    run_case("cfg0")
+def test_tiny_4k_f32_parity():
+    run_case("tiny_4k_f32")
 
 
-def test_cfg1_parity():
-    run_case("cfg1")
+def test_seq_32k_parity():
+    run_case("seq_32k")
 
 
 @pytest.mark.parametrize("kw", [
@@ -167,12 +167,12 @@ def test_cfg1_parity():
          seq_lens=[9000, 300, 64 * 12, 4097, 20000]),                                 # paged, spread
 ])
 def test_decode_variants(kw):
-    run_case("cfg1", **kw)
+    run_case("seq_32k", **kw)
 
 
 def test_dense_mode_is_plain_attention():
     """c = -inf admits every block and leaves logits unfiltered."""
-    wl, summ = prepared("cfg1", seq_lens=[64 * 40 + 9, 2000], h_q=8, h_kv=2, mode="calibrated")
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 40 + 9, 2000], h_q=8, h_kv=2, mode="calibrated")
     bias = np.full(wl.h_q, -np.inf, dtype=np.float32)
     dev = Dev(wl)
     dev.build()
@@ -187,7 +187,7 @@ def test_dense_mode_is_plain_attention():
 def test_rescue_path():
     """Nothing passes and there is no partial block: each head keeps its
     best-bound block only; o is the mean of that block's values."""
-    wl, summ = prepared("cfg1", seq_lens=[64 * 37, 64 * 8], h_q=8, h_kv=2, mode="calibrated")
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 37, 64 * 8], h_q=8, h_kv=2, mode="calibrated")
     bias = np.full(wl.h_q, 1e4, dtype=np.float32)
     dev = Dev(wl)
     dev.build()
@@ -207,7 +207,7 @@ def _same_up_to_rounding(o1, o2):
 
 
 def test_page_permutation_invariance(monkeypatch):
-    wl, summ = prepared("cfg1", seq_lens=[64 * 90 + 7, 3333], h_q=8, h_kv=2)
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 90 + 7, 3333], h_q=8, h_kv=2)
     dev = Dev(wl)
     dev.build()
     o1 = dev.decode()
@@ -222,7 +222,7 @@ def test_page_permutation_invariance(monkeypatch):
 
 
 def test_split_count_invariance(monkeypatch):
-    wl, summ = prepared("cfg1", seq_lens=[64 * 200 + 30, 64 * 77], h_q=8, h_kv=2)
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 200 + 30, 64 * 77], h_q=8, h_kv=2)
     res = oracle_decode(wl, summaries=summ)
     dev = Dev(wl)
     dev.build()
@@ -237,7 +237,7 @@ def test_split_count_invariance(monkeypatch):
 def test_repeatable(monkeypatch):
     """Default mode: repeated calls agree to float32 rounding; ETA_DETERMINISTIC=1:
     bitwise, and within rounding of the default mode."""
-    wl, summ = prepared("cfg1", seq_lens=[64 * 150 + 1, 64 * 40], h_q=8, h_kv=2)
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 150 + 1, 64 * 40], h_q=8, h_kv=2)
     res = oracle_decode(wl, summaries=summ)
     dev = Dev(wl)
     dev.build()
@@ -255,7 +255,7 @@ def test_repeatable(monkeypatch):
 def test_junk_tail_rows_do_not_leak():
     """Rows past the end hold NaN (the generator's fill); results stay finite and
     equal those with zeroed junk."""
-    wl, summ = prepared("cfg1", seq_lens=[64 * 20 + 3, 64 * 9 + 60], h_q=8, h_kv=2)
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 20 + 3, 64 * 9 + 60], h_q=8, h_kv=2)
     dev = Dev(wl)
     dev.build()
     o_nan = dev.decode()
@@ -273,7 +273,7 @@ def test_invalid_device_data_is_reported():
     """An out-of-range page id and an out-of-range length are caught on the
     device: no fault, ETA_ERR_DEVICE_DATA from eta_stats, other sequences fine."""
     import learned_threshold_block_amd as eta
-    wl, summ = prepared("cfg1", seq_lens=[64 * 10 + 5, 64 * 6, 64 * 3], h_q=8, h_kv=2)
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 10 + 5, 64 * 6, 64 * 3], h_q=8, h_kv=2)
     dev = Dev(wl)
     dev.build()
     bt_bad = dev.bt.clone()

@@ -1,0 +1,68 @@
+"""HIP path vs the fp64 oracle at the benchmark workloads' full sizes, in the
+launch configuration the benchmark times (default attend grid, dynamic claims).
+
+Admitted-block bitmaps and every count are compared bit-exactly for all heads;
+outputs are compared on a sample of heads that the oracle evaluates one by one
+(it screens every head but attends only the sampled ones)."""
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import Dev, check_output, check_sets_and_counts, log, oracle_decode, prepared
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _sample_heads(wl, per_seq, seed):
+    rng = np.random.default_rng(seed)
+    heads = []
+    for n in range(wl.n_seqs):
+        for h in rng.choice(wl.h_q, size=min(per_seq, wl.h_q), replace=False):
+            heads.append((n, int(h)))
+    return heads
+
+
+def _run_full(name, per_seq, seed=7):
+    log(f"[full-size] {name}: generating and placing thresholds")
+    wl, summ = prepared(name)
+    log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
+        f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
+    heads = _sample_heads(wl, per_seq, seed)
+    dev = Dev(wl)
+    dev.build()
+    o = dev.decode()
+    st = dev.stats()
+    log(f"[full-size] {name}: oracle on {len(heads)} heads")
+    res = oracle_decode(wl, summaries=summ, heads=heads)
+    check_sets_and_counts(wl, res, st)
+    check_output(wl, res, o, heads=heads)
+    dens = st.admitted_per_head.sum() / (wl.h_q * sum(wl.nblk(n) for n in range(wl.n_seqs)))
+    log(f"[full-size] {name}: per-head density {dens:.3f}, rescued {int(st.rescued.sum())}")
+    del dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_full():
+    """One sequence of 524,288 tokens, GQA 32/8, d = 128, bf16, learned
+    thresholds at ~38% per-head density, 16 planted needles: all 32 heads."""
+    _run_full("seq_512k", per_seq=32)
+
+
+@pytest.mark.timeout(600)
+def test_batch_4x128k_full():
+    """Four sequences of 131,072 tokens, calibrated thresholds: 8 heads each."""
+    _run_full("batch_4x128k", per_seq=8)
+
+
+@pytest.mark.timeout(600)
+def test_ragged_16_full():
+    """Sixteen log-uniform lengths in [4K, 256K], pages in random order,
+    per-head densities spread over [5%, 90%]: 3 heads per sequence."""
+    _run_full("ragged_16", per_seq=3)

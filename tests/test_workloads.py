@@ -20,8 +20,8 @@ def test_bf16_rounding_matches_torch():
 
 
 def test_deterministic_and_layout():
-    a = W.make_workload("cfg4", n_seqs=3, seq_lens=[300, 4097, 64], h_q=4, h_kv=2, d=64)
-    b = W.make_workload("cfg4", n_seqs=3, seq_lens=[300, 4097, 64], h_q=4, h_kv=2, d=64)
+    a = W.make_workload("ragged_16", n_seqs=3, seq_lens=[300, 4097, 64], h_q=4, h_kv=2, d=64)
+    b = W.make_workload("ragged_16", n_seqs=3, seq_lens=[300, 4097, 64], h_q=4, h_kv=2, d=64)
     for f in ("k_pages", "v_pages", "q", "w", "block_table"):
         assert np.array_equal(getattr(a, f), getattr(b, f), equal_nan=True), f
     used = a.block_table[a.block_table >= 0]
@@ -36,7 +36,7 @@ def test_deterministic_and_layout():
 
 
 def test_redraw_keeps_rest():
-    wl = W.make_workload("cfg1", seq_len=64 * 5 + 3, needles=0)
+    wl = W.make_workload("seq_32k", seq_len=64 * 5 + 3, needles=0)
     before = wl.k_pages.copy()
     W.redraw_blocks(wl, [(0, 1, 2)])
     page = wl.block_table[0, 2]
@@ -45,7 +45,7 @@ def test_redraw_keeps_rest():
 
 
 def test_placement_hits_density_with_margin():
-    wl = W.make_workload("cfg1")
+    wl = W.make_workload("seq_32k")
     mu, R = placement.place(wl)
     res = E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
                    wl.tau_mode, wl.w, wl.bias, wl.a, wl.beta, wl.lwb, summaries=(mu, R),

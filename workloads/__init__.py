@@ -110,13 +110,18 @@ class Workload:
 
 # --------------------------------------------------------------------------- generators
 _CONFIGS = {
-    # name: (N, H_Q, H_KV, d, T or None, dtype, mode)
-    "cfg0": dict(n=1, h_q=1, h_kv=1, d=64, T=4096, dtype="f32", mode="learned", density=0.40, needles=3),
-    "cfg1": dict(n=1, h_q=32, h_kv=8, d=128, T=32768, dtype="bf16", mode="learned", density=0.38, needles=0),
-    "cfg2": dict(n=4, h_q=32, h_kv=8, d=128, T=131072, dtype="bf16", mode="calibrated", density=0.38, needles=0),
-    "cfg3": dict(n=1, h_q=32, h_kv=8, d=128, T=524288, dtype="bf16", mode="learned", density=0.38, needles=16),
-    "cfg4": dict(n=16, h_q=32, h_kv=8, d=128, T=None, dtype="bf16", mode="learned", density=None, needles=0,
-                 t_lo=4096, t_hi=262144, paged=True),
+    # name: sizes, storage dtype, threshold mode, target per-head density, planted needles, default seed
+    "tiny_4k_f32": dict(seed=1000, n=1, h_q=1, h_kv=1, d=64, T=4096, dtype="f32", mode="learned",
+                        density=0.40, needles=3),
+    "seq_32k": dict(seed=1001, n=1, h_q=32, h_kv=8, d=128, T=32768, dtype="bf16", mode="learned",
+                    density=0.38, needles=0),
+    "batch_4x128k": dict(seed=1002, n=4, h_q=32, h_kv=8, d=128, T=131072, dtype="bf16", mode="calibrated",
+                         density=0.38, needles=0),
+    "seq_512k": dict(seed=1003, n=1, h_q=32, h_kv=8, d=128, T=524288, dtype="bf16", mode="learned",
+                     density=0.38, needles=16),
+    # lengths log-uniform in [t_lo, t_hi], pages in a seeded random physical order, per-head density U[0.05, 0.90]
+    "ragged_16": dict(seed=1004, n=16, h_q=32, h_kv=8, d=128, T=None, dtype="bf16", mode="learned",
+                      density=None, needles=0, t_lo=4096, t_hi=262144, paged=True),
 }
 
 CONFIG_NAMES = tuple(_CONFIGS)
@@ -136,11 +141,10 @@ def make_workload(name: str, seed: Optional[int] = None, *, n_seqs: Optional[int
                   mode: Optional[str] = None, density=None, needles: Optional[int] = None,
                   paged: Optional[bool] = None, lwb: int = 0, a: float = 0.0, beta: float = 5.0,
                   tail_fill: float = float("nan"), threads: int = 8) -> Workload:
-    """Draw one seeded workload. `name` picks the base recipe (cfg0..cfg4);
+    """Draw one seeded workload. `name` picks the base recipe (one of CONFIG_NAMES);
     keyword overrides shrink or reshape it for parity-size cases."""
     spec = config_spec(name)
-    cfg_index = int(name[3:]) if name.startswith("cfg") and name[3:].isdigit() else 0
-    seed = 1000 + cfg_index if seed is None else int(seed)
+    seed = spec["seed"] if seed is None else int(seed)
     N = spec["n"] if n_seqs is None else int(n_seqs)
     HQ = spec["h_q"] if h_q is None else int(h_q)
     HKV = spec["h_kv"] if h_kv is None else int(h_kv)
