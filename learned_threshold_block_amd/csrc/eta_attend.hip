@@ -113,7 +113,7 @@ void k_attend(AttendArgs A) {
   const St* kbase = (const St*)A.c.k;
   const St* vbase = (const St*)A.c.v;
 
-  // workgroup b takes ranges b, b + grid, ... of the entry list (one range by default)
+  // workgroup b takes range b of the entry list (only W' = min(grid, Utot) ranges exist)
   for (int k = blockIdx.x; k < Wp; k += gridDim.x) {
   int64_t lo = (int64_t)k * Utot / Wp;
   const int64_t hi = (int64_t)(k + 1) * Utot / Wp;

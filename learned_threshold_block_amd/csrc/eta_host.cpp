@@ -198,26 +198,13 @@ eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, 
   return ETA_OK;
 }
 
-// ranges per attend workgroup: far-apart parts of the work list average out
-// memory-channel and XCD speed differences between workgroups
-int attend_rounds(int grid) {
-  int R = 1;
-  if (const char* env = getenv("ETA_ATTEND_ROUNDS")) {
-    const int v = atoi(env);
-    if (v >= 1) R = v;
-  }
-  while (R > 1 && (int64_t)R * grid > kMaxAttendWgs) --R;
-  return R;
-}
-
 eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
   const int grid = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
-  const int W = grid * attend_rounds(grid);
   hipError_t e = hipSuccess;
   switch (phase) {
     case ETA_PHASE_SCREEN:
       e = launch_screen(P.c, P.s, P.p, P.d, P.ws, st);
-      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, W, st);
+      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, grid, st);
       break;
     case ETA_PHASE_ATTEND:
       e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);
