@@ -84,8 +84,9 @@ typedef struct {
 /* Sequences of a batch.
  *   seq_lens    : [num_seqs] int32 token counts, 1 <= T <= block_size*max_blocks_per_seq.
  *   block_table : [num_seqs][max_blocks_per_seq] int32; entry j of row n is the
- *                 page holding tokens [64j, 64j+64) of sequence n; entries past
- *                 the last block are never read.                            */
+ *                 page holding tokens [64j, 64j+64) of sequence n. Entries past
+ *                 the last block may hold anything: they are read but never
+ *                 used, so the whole row must be addressable.               */
 typedef struct {
   int num_seqs;
   int max_blocks_per_seq;

@@ -94,9 +94,7 @@ void k_attend(AttendArgs A) {
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
-  const int Wp = A.ws.glob[kGlobWeff];  // ranges with work: min(ranges, Utot)
-  const int64_t Utot = A.ws.glob[kGlobUtot];
-  const int HKV = A.d.HKV, HQ = A.d.HQ;
+  const int HKV = A.d.HKV, HQ = A.d.HQ, S = A.d.S;
   const float scale = A.p.scale, beta = A.p.beta;
 
   __shared__ __attribute__((aligned(16))) float p_lds[NW][G][64];
@@ -104,7 +102,53 @@ void k_attend(AttendArgs A) {
   __shared__ float acc_lds[NW][G][D];
   __shared__ int toff_lds[kMaxBlocksPerSeq / kTile + 2];
   __shared__ int ctr_lds;
+  __shared__ int scan_lds[NW];
+  __shared__ int pick_lds[3];
   const int NT = A.d.NT;
+
+  // ---- the work split, from the segments' union counts: Utot entries in
+  //      W' = min(grid, Utot) equal ranges; this workgroup takes range k
+  //      (one load round trip when there are at most NTH segments)
+  const int v0 = (int)threadIdx.x < S ? A.ws.seg_U[threadIdx.x] : 0;
+  int tot0;
+  const int incl0 = block_incl_scan<NW>(v0, &tot0, scan_lds);
+  int Utot = tot0;
+  if (S > NTH) {
+    int rest = 0;
+    for (int i = NTH + threadIdx.x; i < S; i += NTH) rest += A.ws.seg_U[i];
+    int totr;
+    block_incl_scan<NW>(rest, &totr, scan_lds);
+    Utot += totr;
+  }
+  const int Wp = Utot < (int)gridDim.x ? Utot : (int)gridDim.x;
+  const int k = blockIdx.x;
+  if (k >= Wp) return;
+  int64_t lo = (int64_t)k * Utot / Wp;
+  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  // the segment holding entry lo, its first entry and its count
+  if (v0 > 0 && incl0 - v0 <= lo && lo < incl0) {
+    pick_lds[0] = threadIdx.x;
+    pick_lds[1] = incl0 - v0;
+    pick_lds[2] = v0;
+  }
+  if (lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
+    int carry = tot0;
+    for (int c0 = NTH; c0 < S && carry <= lo; c0 += NTH) {
+      const int i = c0 + threadIdx.x;
+      const int v = i < S ? A.ws.seg_U[i] : 0;
+      int tot;
+      const int incl = carry + block_incl_scan<NW>(v, &tot, scan_lds);
+      if (v > 0 && incl - v <= lo && lo < incl) {
+        pick_lds[0] = i;
+        pick_lds[1] = incl - v;
+        pick_lds[2] = v;
+      }
+      carry += tot;
+    }
+  }
+  __syncthreads();
+  int s = pick_lds[0];
+  int P = pick_lds[1], Us = pick_lds[2];
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -113,16 +157,10 @@ void k_attend(AttendArgs A) {
   const St* kbase = (const St*)A.c.k;
   const St* vbase = (const St*)A.c.v;
 
-  // workgroup b takes range b of the entry list (only W' = min(grid, Utot) ranges exist)
-  for (int k = blockIdx.x; k < Wp; k += gridDim.x) {
-  int64_t lo = (int64_t)k * Utot / Wp;
-  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
-  int s = A.ws.wg_seg[k];
   while (lo < hi) {
-    int P = A.ws.seg_P[s], Us = A.ws.seg_U[s];
-    while (lo >= (int64_t)P + Us) {
+    while (lo >= (int64_t)P + Us) {  // next segment with entries
+      P += Us;
       ++s;
-      P = A.ws.seg_P[s];
       Us = A.ws.seg_U[s];
     }
     const int e0 = (int)(lo - P);
@@ -163,9 +201,9 @@ void k_attend(AttendArgs A) {
     // the segment's tile prefix (to locate entries in the per-tile lists), and
     // the part's claim counter
     const int ntn = A.ws.seg_ntn[s];
-    {
+    {  // the whole row, so that the loads do not wait for ntn
       const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
-      for (int v = threadIdx.x; v <= ntn + 1; v += NTH) toff_lds[v] = toff[v];
+      for (int v = threadIdx.x; v < NT + 2; v += NTH) toff_lds[v] = toff[v];
     }
     if (threadIdx.x == 0) ctr_lds = e0;
     __syncthreads();
@@ -383,8 +421,6 @@ void k_attend(AttendArgs A) {
     }
     __syncthreads();
     lo = (int64_t)P + e1;
-    ++s;
-  }
   }
 }
 
@@ -393,11 +429,14 @@ struct MergeArgs {
   Dims d;
   Ws ws;
   float* out;
+  int W;  // attend grid
 };
 
 // One workgroup per (sequence, query head): o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
-// over the partials p of the head's segment. Threads: D/4 column groups of
-// float4 x (256 / (D/4)) piece groups.
+// over the partials p of the head's segment. The segment's partials are the
+// slots k + s of the attend ranges k that overlap it, found from the union
+// counts the same way the attend kernel split the work. Threads: D/4 column
+// groups of float4 x (256 / (D/4)) piece groups.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   constexpr int CG = D / 4;          // float4 column groups
@@ -408,11 +447,29 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   const int HQ = A.d.HQ;
   const int n = nh / HQ, h = nh % HQ;
   const int g = h / G, hl = h % G;
-  const int s = n * A.d.HKV + g;
-  const int plo = A.ws.seg_plo[s], phi = A.ws.seg_phi[s];
+  const int s = n * A.d.HKV + g, S = A.d.S;
   __shared__ float s_red[4];
   __shared__ float4 s_acc[PGN][CG];
   __shared__ float s_l[PGN];
+  __shared__ int s_scan[4];
+
+  // first entry P of the segment, its count u and the total
+  int below = 0, all = 0;
+  for (int i = tid; i < S; i += 256) {
+    const int v = A.ws.seg_U[i];
+    all += v;
+    if (i < s) below += v;
+  }
+  const int u = A.ws.seg_U[s];
+  int P, Utot;
+  block_incl_scan<4>(below, &P, s_scan);
+  block_incl_scan<4>(all, &Utot, s_scan);
+  int plo = 0, phi = -1;
+  if (u > 0) {
+    const int64_t Wp = Utot < A.W ? Utot : A.W;
+    plo = (int)((((int64_t)P + 1) * Wp - 1) / Utot) + s;  // range holding entry P
+    phi = (int)((((int64_t)P + u) * Wp - 1) / Utot) + s;  // range holding entry P + u - 1
+  }
 
   float M = -__builtin_inff();
   for (int p = plo + tid; p <= phi; p += 256) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
@@ -503,19 +560,19 @@ int occupancy_g(int G) {
 }
 
 template <int D, int G>
-hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
-  MergeArgs a{d, ws, p.out};
+hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, int W, hipStream_t st) {
+  MergeArgs a{d, ws, p.out, W};
   hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t merge_g(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
+hipError_t merge_g(const Dims& d, const DecodeParams& p, const Ws& ws, int W, hipStream_t st) {
   switch (d.G) {
-    case 1: return merge_impl<D, 1>(d, p, ws, st);
-    case 2: return merge_impl<D, 2>(d, p, ws, st);
-    case 4: return merge_impl<D, 4>(d, p, ws, st);
-    case 8: return merge_impl<D, 8>(d, p, ws, st);
+    case 1: return merge_impl<D, 1>(d, p, ws, W, st);
+    case 2: return merge_impl<D, 2>(d, p, ws, W, st);
+    case 4: return merge_impl<D, 4>(d, p, ws, W, st);
+    case 8: return merge_impl<D, 8>(d, p, ws, W, st);
   }
   return hipErrorInvalidValue;
 }
@@ -528,8 +585,8 @@ hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParam
   return d.D == 128 ? attend_g<F32, 128>(c, s, p, d, ws, W, st) : attend_g<F32, 64>(c, s, p, d, ws, W, st);
 }
 
-hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st) {
-  return d.D == 128 ? merge_g<128>(d, p, ws, st) : merge_g<64>(d, p, ws, st);
+hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, int attend_wgs, hipStream_t st) {
+  return d.D == 128 ? merge_g<128>(d, p, ws, attend_wgs, st) : merge_g<64>(d, p, ws, attend_wgs, st);
 }
 
 int attend_wgs_per_cu(int kv_dtype, int D, int G) {

@@ -103,11 +103,60 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+// Whole-wavefront maximum and integer sum without LDS traffic: DPP all-reduce
+// inside each row of 16 lanes, then the four row results through readlane.
+__device__ __forceinline__ float wave_max_f(float v) {
+  v = group_max<16>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kDppMirror>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppXor2>(v);
+  v += dpp_i<kDppXor1>(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+         __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 
 __device__ __forceinline__ double wave_sum_f64(double v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
+}
+
+// Inclusive scan of one int per thread over a workgroup of NW wavefronts;
+// *total receives the workgroup's sum. lds: NW ints of scratch. Contains two
+// workgroup barriers, so every thread of the workgroup must call it.
+template <int NW>
+__device__ __forceinline__ int block_incl_scan(int v, int* total, int* lds) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) lds[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int ws = lds[w];
+    if (w < wave) base += ws;
+    tot += ws;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + x;
 }
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end

@@ -41,11 +41,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.tile_err = (int32_t*)take(sizeof(int32_t) * S * NT);
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_P = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_plo = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_phi = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
-  w.wg_seg = (int32_t*)take(sizeof(int32_t) * kMaxAttendWgs);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
   w.st_tokens = (int64_t*)take(sizeof(int64_t) * nq);
   w.st_rescued = (int32_t*)take(sizeof(int32_t) * nq);
@@ -204,13 +200,13 @@ eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
   switch (phase) {
     case ETA_PHASE_SCREEN:
       e = launch_screen(P.c, P.s, P.p, P.d, P.ws, st);
-      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, grid, st);
+      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, st);
       break;
     case ETA_PHASE_ATTEND:
       e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);
       break;
     case ETA_PHASE_MERGE:
-      e = launch_merge(P.d, P.p, P.ws, st);
+      e = launch_merge(P.d, P.p, P.ws, grid, st);
       break;
     default:
       return ETA_ERR_INVALID_ARGUMENT;
@@ -344,7 +340,12 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
       memcpy(admitted_bitmap + i * words32, src, sizeof(uint32_t) * words32);
     }
   }
-  return glob[kGlobErr] ? ETA_ERR_DEVICE_DATA : ETA_OK;
+  std::vector<int32_t> serr(d.S);
+  if (hipMemcpy(serr.data(), ws.seg_err, sizeof(int32_t) * d.S, hipMemcpyDeviceToHost) != hipSuccess)
+    return ETA_ERR_HIP;
+  for (int32_t e : serr)
+    if (e) return ETA_ERR_DEVICE_DATA;
+  return ETA_OK;
 }
 
 }  // extern "C"

@@ -15,17 +15,13 @@ constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace
 constexpr int kMaxBlocksPerSeq = 1 << 16;
 constexpr int kMaxGroup = 8;
 
-// global scalars in the workspace
+// header of the workspace: the sizes the last decode laid it out for
 enum Glob : int {
-  kGlobCounter = 0,  // finalize arrival counter (zeroed by the screen kernel)
-  kGlobUtot = 1,     // total admitted (sequence, kv head, block) entries
-  kGlobWeff = 2,     // attend workgroups that have work: min(grid, Utot)
-  kGlobErr = 3,      // nonzero if a kernel met invalid device data
-  kGlobN = 4,        // header: sizes the workspace was laid out for
-  kGlobMB = 5,
-  kGlobHQ = 6,
-  kGlobHKV = 7,
-  kGlobD = 8,
+  kGlobN = 0,
+  kGlobMB = 1,
+  kGlobHQ = 2,
+  kGlobHKV = 3,
+  kGlobD = 4,
   kGlobCount = 16
 };
 
@@ -48,16 +44,13 @@ struct Ws {
   int32_t* tile_err;    // [S][NT]
   int32_t* seg_U;       // [S]          union blocks per segment
   int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
-  int32_t* seg_P;       // [S]          exclusive prefix of seg_U
-  int32_t* seg_plo;     // [S]          first partial slot of the segment
-  int32_t* seg_phi;     // [S]          last partial slot of the segment
   int32_t* seg_err;     // [S]
-  int32_t* wg_seg;      // [kMaxAttendWgs] segment holding each attend workgroup's first entry
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
   int64_t* st_tokens;   // [N*HQ]
   int32_t* st_rescued;  // [N*HQ]
   float* part_ml;       // [(kMaxAttendWgs + S)][G][2]  split running max and sum
-  float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs
+  float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs; the partial of
+                        //              attend range k in segment s is slot k + s
 };
 
 size_t workspace_layout(const Dims& d, void* base, Ws* ws);  // base may be null (size only)
@@ -94,11 +87,10 @@ hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new
                          hipStream_t st);
 hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, hipStream_t st);
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws,
-                           int attend_wgs, hipStream_t st);
+hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st);
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
-hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, hipStream_t st);
+hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, int attend_wgs, hipStream_t st);
 int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
 
 }  // namespace eta

@@ -17,9 +17,10 @@
 //   blocks are compacted in ascending order with a wavefront ballot + prefix.
 // k_finalize: one workgroup per (sequence, KV head): per-head totals, rescue,
 //   exclusive prefix over the tiles' compacted lists (the attend kernel reads
-//   entries in place through it); the last workgroup to finish (arrival
-//   counter, zeroed by k_screen) lays out the split of the total work over the
-//   attend grid.
+//   entries in place through it), the segment's union count and statistics.
+//   The split of the total work over the attend grid needs only the union
+//   counts; each attend and merge workgroup derives it from them itself, so no
+//   workgroup has to wait for all the others here.
 #include <limits.h>
 
 #include "eta_device.h"
@@ -68,7 +69,6 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   const int t = blockIdx.x * 4 + wave;
 
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    A.ws.glob[kGlobCounter] = 0;
     A.ws.glob[kGlobN] = A.d.N;
     A.ws.glob[kGlobMB] = MB;
     A.ws.glob[kGlobHQ] = HQ;
@@ -76,27 +76,20 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     A.ws.glob[kGlobD] = D;
   }
   if (t >= NT) return;
-  const int seq_len = A.s.lens[n];
-  const bool badT = seq_len < 1 || seq_len > kBlock * MB;
-  const int nfull = badT ? 0 : seq_len / kBlock;
-  const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
   const int64_t tix = (int64_t)s * NT + t;
   const int64_t tcx = (int64_t)s * (NT + 1) + t;  // index into tile_cnt / tile_ent
   const int j0 = t * kTile;
-  if (j0 >= nblk) {  // past the sequence: only the bitmap words are read (by eta_stats)
-    if (lane < G) A.ws.tile_bits[((int64_t)s * G + lane) * NT + t] = 0;
-    return;
-  }
 
-  // ---- every load of the wavefront is issued before the first use: block-table
-  //      entries, queries and predictor weights, then centroids and radii
+  // ---- every load that does not need another load's value is issued first:
+  //      length, block-table entries (clamped to the row, whatever the length),
+  //      queries and predictor weights; then centroids and radii
+  const int seq_len = A.s.lens[n];
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
-  const int jmax = nblk - 1;
   int pg[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) pg[i] = bt[min(j0 + RPI * i + r, jmax)];
+  for (int i = 0; i < NI; ++i) pg[i] = bt[min(j0 + RPI * i + r, MB - 1)];
   const int jl = j0 + RPI * cb + r;  // block this lane owns after the reduction
-  const int page_l = bt[min(jl, jmax)];
+  const int page_l = bt[min(jl, MB - 1)];
 
   float qf[G][8];
   const auto* qbase = (const typename T::Stored*)A.p.q;
@@ -117,6 +110,11 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     }
   }
 
+  // tiles past the sequence run through with every block invalid: no entries,
+  // zero bitmap words
+  const bool badT = seq_len < 1 || seq_len > kBlock * MB;
+  const int nfull = badT ? 0 : seq_len / kBlock;
+  const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
   const bool lvalid = jl < nblk && page_l >= 0 && page_l < A.c.num_pages;
   const bool complete = jl < nfull && lvalid;
   // records through buffer loads: an invalid block reads zeros, without a branch
@@ -188,35 +186,32 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   if (complete && jl >= nfull - A.p.lwb) mask = full;
   if (jl == nfull && lvalid) mask = full;  // partial last block (exists iff nfull < nblk)
 
-  // largest bound per head among complete blocks (lowest index on ties)
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    float v = complete ? ub[h] : -__builtin_inff();
-    int jj = complete ? jl : INT_MAX;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(v, m, 64);
-      const int oj = __shfl_xor(jj, m, 64);
-      if (ov > v || (ov == v && oj < jj)) {
-        v = ov;
-        jj = oj;
-      }
-    }
-    if (lane == 0) {
-      A.ws.tile_umax[tix * G + h] = v;
-      A.ws.tile_uarg[tix * G + h] = jj;
-    }
-  }
-
-  // ---- back to block order, then ballot compaction (ascending block index)
+  // ---- back to block order (lane l then holds block j0 + l), the largest
+  //      bound per head among complete blocks (lowest index on ties), and
+  //      ballot compaction in ascending block order
   __shared__ uint32_t smask[4][64];
   __shared__ int spage[4][64];
-  smask[wave][jl - j0] = mask;
+  __shared__ float sub[4][G][64];
+  smask[wave][jl - j0] = mask | (complete ? 0x10000u : 0u);
   spage[wave][jl - j0] = page_l;
+#pragma unroll
+  for (int h = 0; h < G; ++h) sub[wave][h][jl - j0] = ub[h];
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const uint32_t mb = smask[wave][lane];
+  const uint32_t mfull = smask[wave][lane];
+  const uint32_t mb = mfull & 0xffffu;
+  const bool cpl = (mfull >> 16) != 0;
   const int pb = spage[wave][lane];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float u = cpl ? sub[wave][h][lane] : -__builtin_inff();
+    const float mx = wave_max_f(u);
+    const uint64_t at = __ballot(cpl && u == mx);
+    if (lane == 0) {
+      A.ws.tile_umax[tix * G + h] = at ? mx : -__builtin_inff();
+      A.ws.tile_uarg[tix * G + h] = at ? j0 + (int)__builtin_ctzll(at) : INT_MAX;
+    }
+  }
   const uint64_t ball = __ballot(mb != 0);
   const int pos = __popcll(ball & ((1ull << lane) - 1ull));
   if (mb) A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, ((j0 + lane) << 8) | (int)mb);
@@ -242,34 +237,9 @@ struct FinArgs {
   SeqView s;
   Dims d;
   Ws ws;
-  int W;  // attend ranges: rounds x attend grid
 };
 
-// exclusive scan of one int per thread over a 256-thread workgroup
-__device__ int block_excl_scan(int v, int* total, int* lds /*[4]*/) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) lds[wave] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const int ws = lds[w];
-    if (w < wave) base += ws;
-    tot += ws;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
 // One workgroup per (sequence, KV head): totals, rescue, tile prefix, counts.
-// The last workgroup to finish lays out the attend work split.
 template <int G>
 __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
@@ -294,7 +264,6 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   __shared__ int s_nres;
   __shared__ int s_res_j[G];
   __shared__ int s_resc[G];
-  __shared__ int s_last;
 
   // 1. per-head totals, largest bound, errors; exclusive prefix over tiles
   int hc[G];
@@ -306,55 +275,82 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     um[h] = -__builtin_inff();
     ua[h] = INT_MAX;
   }
+  // the tile loads do not wait for the length: every tile of the segment's
+  // row is read (the screen wrote all of them) and those past the sequence
+  // are masked afterwards
   int err = 0, carry = 0;
-  for (int t0 = 0; t0 < ntn; t0 += 256) {
+  for (int t0 = 0; t0 < NT; t0 += 256) {
     const int t = t0 + tid;
-    int c = 0;
-    if (t < ntn) {
+    int c = 0, e = 0, hcl[G], ual[G];
+    float uml[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      hcl[h] = 0;
+      uml[h] = -__builtin_inff();
+      ual[h] = INT_MAX;
+    }
+    if (t < NT) {
       c = A.ws.tile_cnt[tcx0 + t];
-      err |= A.ws.tile_err[tix0 + t];
+      e = A.ws.tile_err[tix0 + t];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        hc[h] += A.ws.tile_hcnt[(tix0 + t) * G + h];
-        const float v = A.ws.tile_umax[(tix0 + t) * G + h];
-        const int j = A.ws.tile_uarg[(tix0 + t) * G + h];
-        if (v > um[h] || (v == um[h] && j < ua[h])) {
-          um[h] = v;
-          ua[h] = j;
-        }
+        hcl[h] = A.ws.tile_hcnt[(tix0 + t) * G + h];
+        uml[h] = A.ws.tile_umax[(tix0 + t) * G + h];
+        ual[h] = A.ws.tile_uarg[(tix0 + t) * G + h];
       }
     }
+    const bool use = t < ntn;
+    if (use) {
+      err |= e;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        hc[h] += hcl[h];
+        if (uml[h] > um[h] || (uml[h] == um[h] && ual[h] < ua[h])) {
+          um[h] = uml[h];
+          ua[h] = ual[h];
+        }
+      }
+    } else {
+      c = 0;
+    }
     int tot;
-    const int ex = block_excl_scan(c, &tot, s_scan);
-    if (t < ntn) toff[t] = carry + ex;
+    const int ex = block_incl_scan<4>(c, &tot, s_scan) - c;
+    if (use) toff[t] = carry + ex;
     carry += tot;
   }
   const int ucnt = carry;
+  const bool err_w = __any(err != 0);
+  if (lane == 0) s_err[wave] = err_w ? 1 : 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      hc[h] += __shfl_xor(hc[h], m, 64);
-      const float ov = __shfl_xor(um[h], m, 64);
-      const int oj = __shfl_xor(ua[h], m, 64);
-      if (ov > um[h] || (ov == um[h] && oj < ua[h])) {
-        um[h] = ov;
-        ua[h] = oj;
-      }
-    }
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) err |= __shfl_xor(err, m, 64);
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      s_hcnt[wave][h] = hc[h];
-      s_umax[wave][h] = um[h];
-      s_uarg[wave][h] = ua[h];
-    }
-    s_err[wave] = err;
+    const int t_h = wave_sum_i(hc[h]);
+    if (lane == 0) s_hcnt[wave][h] = t_h;
   }
   __syncthreads();
+  // the block with the largest bound matters only to a head that admitted
+  // nothing (the same decision in every thread)
+  bool need_rescue = false;
+#pragma unroll
+  for (int h = 0; h < G; ++h) need_rescue |= (s_hcnt[0][h] + s_hcnt[1][h] + s_hcnt[2][h] + s_hcnt[3][h]) == 0;
+  if (need_rescue) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) {
+        const float ov = __shfl_xor(um[h], m, 64);
+        const int oj = __shfl_xor(ua[h], m, 64);
+        if (ov > um[h] || (ov == um[h] && oj < ua[h])) {
+          um[h] = ov;
+          ua[h] = oj;
+        }
+      }
+      if (lane == 0) {
+        s_umax[wave][h] = um[h];
+        s_uarg[wave][h] = ua[h];
+      }
+    }
+    __syncthreads();
+  }
 
   // 2. rescue (thread 0): a head with nothing admitted gets its best-bound
   //    block; if another head of the group loads it already, only the head's
@@ -363,13 +359,15 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     int nres = 0;
     for (int h = 0; h < G; ++h) {
       int tot = 0;
+      for (int w = 0; w < 4; ++w) tot += s_hcnt[w][h];
       float v = -__builtin_inff();
       int jb = INT_MAX;
-      for (int w = 0; w < 4; ++w) {
-        tot += s_hcnt[w][h];
-        if (s_umax[w][h] > v || (s_umax[w][h] == v && s_uarg[w][h] < jb)) {
-          v = s_umax[w][h];
-          jb = s_uarg[w][h];
+      if (tot == 0) {  // the per-wave maxima exist only in this case
+        for (int w = 0; w < 4; ++w) {
+          if (s_umax[w][h] > v || (s_umax[w][h] == v && s_uarg[w][h] < jb)) {
+            v = s_umax[w][h];
+            jb = s_uarg[w][h];
+          }
         }
       }
       s_resc[h] = -1;
@@ -422,53 +420,6 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     A.ws.seg_U[s] = U;
     A.ws.seg_ntn[s] = ntn;
     A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
-    __threadfence();
-    const int old = atomicAdd(&A.ws.glob[kGlobCounter], 1);
-    s_last = (old == A.d.S - 1) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-
-  // 4. last workgroup: prefix over segments and the attend work split
-  __threadfence();
-  const int S = A.d.S;
-  int carry2 = 0, errs = 0;
-  for (int s0 = 0; s0 < S; s0 += 256) {
-    const int si = s0 + tid;
-    const int u = si < S ? __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED) : 0;
-    if (si < S) errs |= __atomic_load_n(&A.ws.seg_err[si], __ATOMIC_RELAXED);
-    int tot;
-    const int ex = block_excl_scan(u, &tot, s_scan);
-    if (si < S) A.ws.seg_P[si] = carry2 + ex;
-    carry2 += tot;
-  }
-  const int Utot = carry2;
-  const int Wp = Utot < A.W ? Utot : A.W;
-  errs = __syncthreads_or(errs);
-  if (tid == 0) {
-    A.ws.glob[kGlobUtot] = Utot;
-    A.ws.glob[kGlobWeff] = Wp;
-    A.ws.glob[kGlobErr] = errs;
-    A.ws.glob[kGlobCounter] = 0;
-  }
-  if (Wp == 0) return;
-  for (int si = tid; si < S; si += 256) {
-    const int u = __atomic_load_n(&A.ws.seg_U[si], __ATOMIC_RELAXED);
-    const int P = A.ws.seg_P[si];  // written by this thread above
-    if (u == 0) {
-      A.ws.seg_plo[si] = 0;
-      A.ws.seg_phi[si] = -1;
-      continue;
-    }
-    const int64_t UU = Utot, WW = Wp;
-    // attend workgroup k covers entries [floor(k U / W'), floor((k+1) U / W'))
-    const int64_t k_lo = ((int64_t)P * WW + UU - 1) / UU;            // first k starting in the segment
-    const int64_t k_hi = ((int64_t)(P + u) * WW + UU - 1) / UU - 1;  // last k starting in the segment
-    for (int64_t k = k_lo; k <= k_hi && k < WW; ++k) A.ws.wg_seg[k] = si;
-    const int64_t kf = (((int64_t)P + 1) * WW - 1) / UU;             // workgroup holding entry P
-    const int64_t kl = (((int64_t)P + u) * WW - 1) / UU;             // workgroup holding entry P+u-1
-    A.ws.seg_plo[si] = (int)(kf + si);
-    A.ws.seg_phi[si] = (int)(kl + si);
   }
 }
 
@@ -494,9 +445,8 @@ hipError_t screen_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
 }
 
 template <int G>
-hipError_t finalize_impl(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, int W,
-                         hipStream_t st) {
-  FinArgs a{c, s, d, ws, W};
+hipError_t finalize_impl(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st) {
+  FinArgs a{c, s, d, ws};
   hipLaunchKernelGGL((k_finalize<G>), dim3(d.S), dim3(256), 0, st, a);
   return hipGetLastError();
 }
@@ -509,13 +459,12 @@ hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParam
   return d.D == 128 ? screen_g<F32, 128>(c, s, p, d, ws, st) : screen_g<F32, 64>(c, s, p, d, ws, st);
 }
 
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, int W,
-                           hipStream_t st) {
+hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st) {
   switch (d.G) {
-    case 1: return finalize_impl<1>(c, s, d, ws, W, st);
-    case 2: return finalize_impl<2>(c, s, d, ws, W, st);
-    case 4: return finalize_impl<4>(c, s, d, ws, W, st);
-    case 8: return finalize_impl<8>(c, s, d, ws, W, st);
+    case 1: return finalize_impl<1>(c, s, d, ws, st);
+    case 2: return finalize_impl<2>(c, s, d, ws, st);
+    case 4: return finalize_impl<4>(c, s, d, ws, st);
+    case 8: return finalize_impl<8>(c, s, d, ws, st);
   }
   return hipErrorInvalidValue;
 }
