@@ -40,7 +40,6 @@ struct AttendArgs {
   DecodeParams p;
   Dims d;
   Ws ws;
-  int deterministic;  // fixed claims instead of the LDS counter
 };
 
 // Entries [c, c + cnt) of the segment's compacted lists, one per lane
@@ -94,6 +93,7 @@ void k_attend(AttendArgs A) {
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
   const int HKV = A.d.HKV, HQ = A.d.HQ, S = A.d.S;
   const float scale = A.p.scale, beta = A.p.beta;
 
@@ -107,8 +107,10 @@ void k_attend(AttendArgs A) {
   const int NT = A.d.NT;
 
   // ---- the work split, from the segments' union counts: Utot entries in
-  //      W' = min(grid, Utot) equal ranges; this workgroup takes range k
-  //      (one load round trip when there are at most NTH segments)
+  //      W' = min(grid, Utot) ranges weighted per die class; this workgroup
+  //      takes range k (one load round trip when there are at most NTH segments)
+  int wts[kXcdClasses];
+  load_weights(A.ws.xcd_w, A.p.deterministic, wts);
   const int v0 = (int)threadIdx.x < S ? A.ws.seg_U[threadIdx.x] : 0;
   int tot0;
   const int incl0 = block_incl_scan<NW>(v0, &tot0, scan_lds);
@@ -123,15 +125,21 @@ void k_attend(AttendArgs A) {
   const int Wp = Utot < (int)gridDim.x ? Utot : (int)gridDim.x;
   const int k = blockIdx.x;
   if (k >= Wp) return;
-  int64_t lo = (int64_t)k * Utot / Wp;
-  const int64_t hi = (int64_t)(k + 1) * Utot / Wp;
+  int64_t lo, hi;
+  {
+    RangeSplit sp;
+    sp.init(Utot, Wp, wts);
+    lo = sp.B(k);
+    hi = sp.B(k + 1);
+  }
+  const int n_entries = (int)(hi - lo);
   // the segment holding entry lo, its first entry and its count
   if (v0 > 0 && incl0 - v0 <= lo && lo < incl0) {
     pick_lds[0] = threadIdx.x;
     pick_lds[1] = incl0 - v0;
     pick_lds[2] = v0;
   }
-  if (lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
+  if (lo < hi && lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
     int carry = tot0;
     for (int c0 = NTH; c0 < S && carry <= lo; c0 += NTH) {
       const int i = c0 + threadIdx.x;
@@ -147,8 +155,8 @@ void k_attend(AttendArgs A) {
     }
   }
   __syncthreads();
-  int s = pick_lds[0];
-  int P = pick_lds[1], Us = pick_lds[2];
+  int s = lo < hi ? pick_lds[0] : 0;
+  int P = lo < hi ? pick_lds[1] : 0, Us = lo < hi ? pick_lds[2] : 0;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -211,7 +219,7 @@ void k_attend(AttendArgs A) {
 
     // claims, two deep: the batch being streamed, the next one (resolved while
     // the current one streams) and the claim after it
-    const bool fixed = A.deterministic != 0;
+    const bool fixed = A.p.deterministic != 0;
     int nclaim = 0;
     const int c0 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
     int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
@@ -422,6 +430,16 @@ void k_attend(AttendArgs A) {
     __syncthreads();
     lo = (int64_t)P + e1;
   }
+  // entries and duration of this range, read by the next decode's weighting
+  if (threadIdx.x == 0) {
+    const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
+    A.ws.rng_stat[2 * k] = n_entries;
+    A.ws.rng_stat[2 * k + 1] = (int)min<uint64_t>(t_end - t_start, 0x7fffffffu);
+    if (k == 0) {
+      A.ws.glob[kGlobStatMagic] = kStatMagic;
+      A.ws.glob[kGlobStatW] = Wp;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- merge
@@ -429,7 +447,8 @@ struct MergeArgs {
   Dims d;
   Ws ws;
   float* out;
-  int W;  // attend grid
+  int W;              // attend grid
+  int deterministic;
 };
 
 // One workgroup per (sequence, query head): o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
@@ -464,15 +483,21 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   int P, Utot;
   block_incl_scan<4>(below, &P, s_scan);
   block_incl_scan<4>(all, &Utot, s_scan);
+  int wts[kXcdClasses];
+  load_weights(A.ws.xcd_w, A.deterministic, wts);
+  RangeSplit sp;
   int plo = 0, phi = -1;
   if (u > 0) {
-    const int64_t Wp = Utot < A.W ? Utot : A.W;
-    plo = (int)((((int64_t)P + 1) * Wp - 1) / Utot) + s;  // range holding entry P
-    phi = (int)((((int64_t)P + u) * Wp - 1) / Utot) + s;  // range holding entry P + u - 1
+    sp.init(Utot, Utot < A.W ? Utot : A.W, wts);
+    plo = sp.holder(P) + s;          // range holding entry P
+    phi = sp.holder(P + u - 1) + s;  // range holding entry P + u - 1
   }
+  // ranges without entries wrote no partial
+  auto has = [&](int p) { return sp.B(p - s) < sp.B(p - s + 1); };
 
   float M = -__builtin_inff();
-  for (int p = plo + tid; p <= phi; p += 256) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
+  for (int p = plo + tid; p <= phi; p += 256)
+    if (has(p)) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
   if (lane == 0) s_red[wave] = M;
@@ -484,6 +509,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
   float lsum = 0.f;
 #pragma unroll 4
   for (int p = plo + pg; p <= phi; p += PGN) {
+    if (!has(p)) continue;
     const float2 ml = *(const float2*)&A.ws.part_ml[((int64_t)p * G + hl) * 2];
     const float4 a = *(const float4*)&A.ws.part_acc[((int64_t)p * G + hl) * D + cg * 4];
     const float wgt = ml.x == -__builtin_inff() ? 0.f : fast_exp(ml.x - M);
@@ -521,8 +547,7 @@ __global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
 template <typename T, int D, int G>
 hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, int W, hipStream_t st) {
-  const char* det = getenv("ETA_DETERMINISTIC");
-  AttendArgs a{c, s, p, d, ws, det != nullptr && det[0] == '1'};
+  AttendArgs a{c, s, p, d, ws};
   hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
   return hipGetLastError();
 }
@@ -561,7 +586,7 @@ int occupancy_g(int G) {
 
 template <int D, int G>
 hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, int W, hipStream_t st) {
-  MergeArgs a{d, ws, p.out, W};
+  MergeArgs a{d, ws, p.out, W, p.deterministic};
   hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(256), 0, st, a);
   return hipGetLastError();
 }

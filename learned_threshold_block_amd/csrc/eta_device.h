@@ -159,6 +159,56 @@ __device__ __forceinline__ int block_incl_scan(int v, int* total, int* lds) {
   return base + x;
 }
 
+// Split of the Utot compacted entries over W attend ranges in proportion to
+// per-die weights: range k has weight w[k % 8] (fixed point) and covers
+// entries [B(k), B(k+1)), B(k) = floor(Utot C(k) / C(W)), C(k) = sum_{i<k} w[i % 8].
+// Integer arithmetic, so every kernel that evaluates it gets the same ranges.
+struct RangeSplit {
+  int64_t utot, cw;
+  int W, wsum;
+  int w[kXcdClasses];
+  __device__ void init(int64_t utot_, int W_, const int* w_) {
+    utot = utot_;
+    W = W_;
+    wsum = 0;
+#pragma unroll
+    for (int x = 0; x < kXcdClasses; ++x) {
+      w[x] = w_[x];
+      wsum += w_[x];
+    }
+    cw = C(W);
+  }
+  // compile-time indices only, so the weights stay in registers
+  __device__ int64_t C(int k) const {
+    const int r = k % kXcdClasses;
+    int part = 0;
+#pragma unroll
+    for (int x = 0; x < kXcdClasses; ++x) part += x < r ? w[x] : 0;
+    return (int64_t)(k / kXcdClasses) * wsum + part;
+  }
+  __device__ int64_t B(int k) const { return utot * C(k) / cw; }
+  // the range holding entry x (the largest k < W with B(k) <= x)
+  __device__ int holder(int64_t x) const {
+    int lo = 0, hi = W - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (B(mid) <= x) lo = mid;
+      else hi = mid - 1;
+    }
+    return lo;
+  }
+};
+
+// Per-die weights as stored in the workspace, clamped to the range the
+// weighting step writes (anything else reads as equal weights).
+__device__ __forceinline__ void load_weights(const int32_t* xcd_w, int deterministic, int* w) {
+#pragma unroll
+  for (int x = 0; x < kXcdClasses; ++x) {
+    const int v = deterministic ? kWeightOne : xcd_w[x];
+    w[x] = (v >= kWeightOne / 2 && v <= 2 * kWeightOne) ? v : kWeightOne;
+  }
+}
+
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end
 // return zeros instead of faulting (used for records of invalid pages).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -42,6 +42,8 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
+  w.rng_stat = (int32_t*)take(sizeof(int32_t) * 2 * kMaxAttendWgs);
+  w.xcd_w = (int32_t*)take(sizeof(int32_t) * kXcdClasses);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
   w.st_tokens = (int64_t*)take(sizeof(int64_t) * nq);
   w.st_rescued = (int32_t*)take(sizeof(int32_t) * nq);
@@ -191,6 +193,25 @@ eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, 
   P->p.scale = (float)(1.0 / sqrt((double)cache->head_dim));
   P->p.lwb = lwb;
   P->p.out = out;
+  const char* det = getenv("ETA_DETERMINISTIC");
+  P->p.deterministic = (det != nullptr && det[0] == '1') ? 1 : 0;
+  // ETA_RANGE_WEIGHTS="w0,...,w7" (each in [512, 2048], 1024 = 1): per-die
+  // weights of the attend split instead of the measured ones (for testing)
+  P->p.fixed_w[0] = 0;
+  if (const char* env = getenv("ETA_RANGE_WEIGHTS")) {
+    int v[kXcdClasses];
+    int nread = 0;
+    const char* c = env;
+    while (nread < kXcdClasses && *c) {
+      char* end = nullptr;
+      const long x = strtol(c, &end, 10);
+      if (end == c || x < kWeightOne / 2 || x > 2 * kWeightOne) break;
+      v[nread++] = (int)x;
+      c = *end == ',' ? end + 1 : end;
+    }
+    if (nread == kXcdClasses)
+      for (int x = 0; x < kXcdClasses; ++x) P->p.fixed_w[x] = v[x];
+  }
   return ETA_OK;
 }
 
@@ -200,7 +221,7 @@ eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
   switch (phase) {
     case ETA_PHASE_SCREEN:
       e = launch_screen(P.c, P.s, P.p, P.d, P.ws, st);
-      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.d, P.ws, st);
+      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.p, P.d, P.ws, st);
       break;
     case ETA_PHASE_ATTEND:
       e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);

@@ -14,14 +14,20 @@ constexpr int kClaim = 2;           // entries per wavefront claim inside a work
 constexpr int kMaxAttendWgs = 4096; // upper bound of the attend grid (workspace sizing)
 constexpr int kMaxBlocksPerSeq = 1 << 16;
 constexpr int kMaxGroup = 8;
+constexpr int kXcdClasses = 8;       // attend workgroup k runs on accelerator complex die k % 8
+constexpr int kWeightOne = 1024;     // fixed-point unit of the per-die work weights
+constexpr int kStatMagic = 0x45544131;
 
-// header of the workspace: the sizes the last decode laid it out for
+// header of the workspace: the sizes the last decode laid it out for, and
+// whether the attend timings of the last decode are present
 enum Glob : int {
   kGlobN = 0,
   kGlobMB = 1,
   kGlobHQ = 2,
   kGlobHKV = 3,
   kGlobD = 4,
+  kGlobStatMagic = 5,  // kStatMagic once an attend kernel has written rng_stat
+  kGlobStatW = 6,      // ranges that attend kernel had
   kGlobCount = 16
 };
 
@@ -45,6 +51,8 @@ struct Ws {
   int32_t* seg_U;       // [S]          union blocks per segment
   int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
   int32_t* seg_err;     // [S]
+  int32_t* rng_stat;    // [kMaxAttendWgs][2] entries and duration (10 ns ticks) of each attend range
+  int32_t* xcd_w;       // [kXcdClasses]  work weight of each die class (kWeightOne = 1)
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
   int64_t* st_tokens;   // [N*HQ]
   int32_t* st_rescued;  // [N*HQ]
@@ -79,6 +87,8 @@ struct DecodeParams {
   float a, beta, scale;
   int lwb;
   float* out;
+  int deterministic;  // static work split and claims: bitwise-reproducible results
+  int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };
 
 // launchers (return hipError_t of the launch)
@@ -87,7 +97,8 @@ hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new
                          hipStream_t st);
 hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, hipStream_t st);
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st);
+hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                           const Ws& ws, hipStream_t st);
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
 hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, int attend_wgs, hipStream_t st);

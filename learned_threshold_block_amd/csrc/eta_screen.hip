@@ -237,11 +237,88 @@ struct FinArgs {
   SeqView s;
   Dims d;
   Ws ws;
+  int deterministic;
+  int fixed_w[kXcdClasses];
 };
+
+// Work weights of the attend ranges per die class (workgroup k of a launch runs
+// on die k % 8; dies differ in memory throughput by several percent). The
+// previous decode's attend kernel left entries and duration per range; a
+// class's measured rate (entries per tick) relative to the mean rate, averaged
+// with its previous weight, becomes its weight for this decode, clamped to
+// [1/2, 2]. Equal weights when there is no valid record or in the
+// deterministic mode. Runs as one extra workgroup of the finalize grid.
+__device__ void update_weights(const FinArgs& A) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (A.fixed_w[0] > 0 && !A.deterministic) {
+    if (tid < kXcdClasses) A.ws.xcd_w[tid] = A.fixed_w[tid];
+    return;
+  }
+  __shared__ int s_acc[4][2 * kXcdClasses];
+  const int magic = A.ws.glob[kGlobStatMagic];
+  const int Wprev = A.ws.glob[kGlobStatW];
+  const bool valid = !A.deterministic && magic == kStatMagic && Wprev >= 1 && Wprev <= kMaxAttendWgs;
+  int e[kXcdClasses], t[kXcdClasses];
+#pragma unroll
+  for (int x = 0; x < kXcdClasses; ++x) e[x] = t[x] = 0;
+  if (valid) {
+    for (int k = tid; k < Wprev; k += 256) {
+      const int ek = A.ws.rng_stat[2 * k], tk = min(A.ws.rng_stat[2 * k + 1], 1 << 22);
+      if (ek > 0 && tk > 0) {
+#pragma unroll
+        for (int x = 0; x < kXcdClasses; ++x)
+          if (k % kXcdClasses == x) {
+            e[x] += ek;
+            t[x] += tk;
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < kXcdClasses; ++x) {
+    const int es = wave_sum_i(e[x]), ts = wave_sum_i(t[x]);
+    if (lane == 0) {
+      s_acc[wave][x] = es;
+      s_acc[wave][kXcdClasses + x] = ts;
+    }
+  }
+  __syncthreads();
+  if (tid != 0) return;
+  float rate[kXcdClasses], mean = 0.f;
+  int nr = 0;
+#pragma unroll
+  for (int x = 0; x < kXcdClasses; ++x) {
+    const float es = (float)(s_acc[0][x] + s_acc[1][x] + s_acc[2][x] + s_acc[3][x]);
+    const float ts = (float)(s_acc[0][kXcdClasses + x] + s_acc[1][kXcdClasses + x] + s_acc[2][kXcdClasses + x] +
+                             s_acc[3][kXcdClasses + x]);
+    rate[x] = (es > 0.f && ts > 0.f) ? es / ts : 0.f;
+    if (rate[x] > 0.f) {
+      mean += rate[x];
+      ++nr;
+    }
+  }
+  mean = nr ? mean / nr : 0.f;
+#pragma unroll
+  for (int x = 0; x < kXcdClasses; ++x) {
+    int w = kWeightOne;
+    if (valid && rate[x] > 0.f && mean > 0.f) {
+      const int old = A.ws.xcd_w[x];
+      const float prev = (old >= kWeightOne / 2 && old <= 2 * kWeightOne) ? (float)old : (float)kWeightOne;
+      const float meas = kWeightOne * rate[x] / mean;
+      w = (int)(0.5f * (prev + meas) + 0.5f);
+      w = w < kWeightOne / 2 ? kWeightOne / 2 : (w > 2 * kWeightOne ? 2 * kWeightOne : w);
+    }
+    A.ws.xcd_w[x] = w;
+  }
+}
 
 // One workgroup per (sequence, KV head): totals, rescue, tile prefix, counts.
 template <int G>
 __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
+  if ((int)blockIdx.x == A.d.S) {
+    update_weights(A);
+    return;
+  }
   const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HKV = A.d.HKV, MB = A.d.MB, NT = A.d.NT, HQ = A.d.HQ;
@@ -445,9 +522,11 @@ hipError_t screen_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
 }
 
 template <int G>
-hipError_t finalize_impl(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st) {
-  FinArgs a{c, s, d, ws};
-  hipLaunchKernelGGL((k_finalize<G>), dim3(d.S), dim3(256), 0, st, a);
+hipError_t finalize_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                         const Ws& ws, hipStream_t st) {
+  FinArgs a{c, s, d, ws, p.deterministic, {}};
+  for (int x = 0; x < kXcdClasses; ++x) a.fixed_w[x] = p.fixed_w[x];
+  hipLaunchKernelGGL((k_finalize<G>), dim3(d.S + 1), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
@@ -459,12 +538,13 @@ hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParam
   return d.D == 128 ? screen_g<F32, 128>(c, s, p, d, ws, st) : screen_g<F32, 64>(c, s, p, d, ws, st);
 }
 
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const Dims& d, const Ws& ws, hipStream_t st) {
+hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                           const Ws& ws, hipStream_t st) {
   switch (d.G) {
-    case 1: return finalize_impl<1>(c, s, d, ws, st);
-    case 2: return finalize_impl<2>(c, s, d, ws, st);
-    case 4: return finalize_impl<4>(c, s, d, ws, st);
-    case 8: return finalize_impl<8>(c, s, d, ws, st);
+    case 1: return finalize_impl<1>(c, s, p, d, ws, st);
+    case 2: return finalize_impl<2>(c, s, p, d, ws, st);
+    case 4: return finalize_impl<4>(c, s, p, d, ws, st);
+    case 8: return finalize_impl<8>(c, s, p, d, ws, st);
   }
   return hipErrorInvalidValue;
 }

@@ -200,8 +200,9 @@ def test_rescue_path():
 
 
 def _same_up_to_rounding(o1, o2):
-    """Work is claimed dynamically, so the float32 summation order may differ
-    between calls: equal to a few float32 ulps of the output scale."""
+    """Work is claimed dynamically and split by measured per-die speed, so the
+    float32 summation order may differ between calls: equal to a few float32
+    ulps of the output scale."""
     scale = float(np.max(np.abs(o1)))
     assert float(np.max(np.abs(o1 - o2))) <= 1e-6 * scale
 
@@ -234,6 +235,24 @@ def test_split_count_invariance(monkeypatch):
     monkeypatch.delenv("ETA_ATTEND_WGS")
 
 
+@pytest.mark.parametrize("weights", ["512,2048,512,2048,512,2048,512,2048", "2048,512,1024,1024,700,1900,512,2048"])
+def test_weighted_split(monkeypatch, weights):
+    """Uneven per-die weights of the attend split (the measured ones are
+    replaced through ETA_RANGE_WEIGHTS), including grids with more ranges than
+    some weights can fill (empty ranges), keep the results."""
+    wl, summ = prepared("seq_32k", seq_lens=[64 * 120 + 30, 64 * 33, 500], h_q=8, h_kv=2)
+    res = oracle_decode(wl, summaries=summ)
+    dev = Dev(wl)
+    dev.build()
+    monkeypatch.setenv("ETA_RANGE_WEIGHTS", weights)
+    for wgs in ("3", "256", "4096"):
+        monkeypatch.setenv("ETA_ATTEND_WGS", wgs)
+        o = dev.decode()
+        log(f"  weights {weights}, attend workgroups {wgs}")
+        check_output(wl, res, o)
+        check_sets_and_counts(wl, res, dev.stats())
+
+
 def test_repeatable(monkeypatch):
     """Default mode: repeated calls agree to float32 rounding; ETA_DETERMINISTIC=1:
     bitwise, and within rounding of the default mode."""
@@ -252,9 +271,10 @@ def test_repeatable(monkeypatch):
     check_output(wl, res, d1)
 
 
-def test_junk_tail_rows_do_not_leak():
+def test_junk_tail_rows_do_not_leak(monkeypatch):
     """Rows past the end hold NaN (the generator's fill); results stay finite and
-    equal those with zeroed junk."""
+    equal, bit for bit under the static work split, those with zeroed junk."""
+    monkeypatch.setenv("ETA_DETERMINISTIC", "1")
     wl, summ = prepared("seq_32k", seq_lens=[64 * 20 + 3, 64 * 9 + 60], h_q=8, h_kv=2)
     dev = Dev(wl)
     dev.build()
