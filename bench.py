@@ -5,7 +5,8 @@ Workload (default): one sequence of 524,288 tokens, GQA 32 query / 8 KV heads,
 d = 128, bfloat16 paged KV cache (64-token pages), learned thresholds placed
 for ~38% per-head block density, 16 planted needle keys. A step is one full
 ETA decode (threshold + bound screen + compaction, split flash-decode over the
-admitted blocks, merge) for every query head, with the cache resident in HBM.
+admitted blocks with the merge of the splits) for every query head, with the
+cache resident in HBM.
 
 Prints one JSON line: decode latency (us/step), achieved HBM bandwidth on the
 bytes the step must read, the roofline of the dominant (attend) kernel from HIP
@@ -201,14 +202,15 @@ def time_steps(S, steps, warmup):
 def time_phases(S, steps):
     """Average duration (us) of each phase's launches: HIP events on the launch
     stream around `steps` back-to-back launches of that phase alone (screen +
-    finalize, attend, merge). Each phase is idempotent given the previous
-    phase's workspace contents, so repeating it measures the kernel itself
-    without the gaps that events between phases would add to a step."""
+    finalize; attend with the merge of the splits). Each phase is idempotent
+    given the previous phase's workspace contents, so repeating it measures
+    the kernels themselves without the gaps that events between phases would
+    add to a step."""
     eta, torch = S.eta, S.torch
     S.run()
     torch.cuda.synchronize()
     out = []
-    for phase in (eta.ETA_PHASE_SCREEN, eta.ETA_PHASE_ATTEND, eta.ETA_PHASE_MERGE):
+    for phase in (eta.ETA_PHASE_SCREEN, eta.ETA_PHASE_ATTEND):
         S.run(phase=phase)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -275,7 +277,7 @@ def main():
 
     us = time_steps(S, args.steps, args.warmup)
     ph = time_phases(S, args.steps)
-    log(f"step {us:.1f} us; phases screen/attend/merge {ph[0]:.1f} / {ph[1]:.1f} / {ph[2]:.1f} us")
+    log(f"step {us:.1f} us; phases screen / attend+merge {ph[0]:.1f} / {ph[1]:.1f} us")
     wl = S.wl
     esz = 2 if wl.kv_dtype == "bf16" else 4
     U = int(st.union_per_kv.sum())
@@ -310,8 +312,7 @@ def main():
         },
         "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
         "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),
-        "phase_us": {"screen": round(float(ph[0]), 2), "attend": round(float(ph[1]), 2),
-                     "merge": round(float(ph[2]), 2)},
+        "phase_us": {"screen": round(float(ph[0]), 2), "attend_and_merge": round(float(ph[1]), 2)},
         "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_attend", "bytes_per_launch": attend_bytes},

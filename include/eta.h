@@ -142,9 +142,11 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
 /* One phase of eta_decode with the same arguments, for callers that overlap or
  * time the phases: ETA_PHASE_SCREEN (thresholds, bound screen, compaction of
  * admitted block ids, rescue, counts), ETA_PHASE_ATTEND (split flash-decode over
- * the compacted lists; Section 3.2 and F.3 chunked decoding), ETA_PHASE_MERGE
- * (associative merge of the split partials into out). Phases must run in this
- * order on one workspace; ATTEND and MERGE read what the previous phase wrote. */
+ * the compacted lists, Section 3.2 and F.3 chunked decoding, followed by the
+ * associative merge of the splits into out, done by the workgroup that
+ * completes each (sequence, KV head)), ETA_PHASE_MERGE (accepted for
+ * compatibility; no work, the merge is part of ETA_PHASE_ATTEND). Phases must
+ * run in this order on one workspace; ATTEND reads what SCREEN wrote. */
 eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* seqs,
                             const void* q, int num_q_heads, int tau_mode, const float* w,
                             const float* b_or_c, float a, float beta, int lwb, int block_size,

@@ -1,5 +1,5 @@
-// Attend and merge phases of one decode step: split flash-decode over the
-// compacted lists of admitted blocks, then the associative merge of the splits.
+// Attend phase of one decode step: split flash-decode over the compacted lists
+// of admitted blocks, and the associative merge of the splits.
 //
 // "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888):
 //   S = s q.k, S~ = S * sigmoid(beta (S - tau~)), o = sum e^{S~} v / sum e^{S~}
@@ -9,26 +9,31 @@
 //   masked past the sequence end (F.4); the sequence split into parts merged by
 //   an associative online-softmax reduction (Section 3.2, F.2, F.3).
 //
-// Work split: the screen produced, per (sequence, KV head), a contiguous list
-// of admitted blocks. Their concatenation (Utot entries) is cut into W' equal
-// ranges, one per attend workgroup (W' = min(grid, Utot), grid = one
-// workgroup per CU), so every workgroup streams the same number of tiles
-// whatever the density or the length mix. A range that spans several
-// (sequence, KV head) segments emits one partial per segment.
+// Work split: the screen produced, per (sequence, KV head) segment, a list of
+// admitted blocks. Their concatenation (Utot entries) is cut into W' ranges,
+// one per workgroup (W' = min(grid, ceil(Utot / 8)), grid = one workgroup per
+// CU), so every workgroup streams about the same number of tiles whatever the
+// density or the length mix. Range sizes follow per-die weights measured on
+// the previous decode (dies differ in memory throughput). A range that spans
+// several segments emits one partial per segment; the workgroup that
+// completes a segment's entries (counted with one atomic per partial) merges
+// the segment's partials into the output, so no separate merge launch waits
+// for the slowest workgroup of all.
 //
 // Inside a workgroup the wavefronts claim kClaim entries at a time from an LDS
 // counter, so the wavefronts that run faster (older waves get issue priority on
 // a SIMD) take more tiles. With ETA_DETERMINISTIC=1 in the environment the
-// claims are static instead (wavefront w takes claims w, w + NW, ...) and the
-// result is bitwise reproducible; by default repeated calls agree to float32
-// rounding. A wavefront owns a whole tile: 16-byte loads of one 64 x d tile
-// (lane (r, cb) holds rows RPI*i + r, 8 bf16 columns), keys consumed by v_dot2
-// bf16 products into per-lane partial logits, finished by a transposing DPP
-// reduction that leaves one token's logit per lane. The gate and the online
-// softmax run per lane in float32 (running max per row of lanes); the weights
-// go through LDS to the lanes holding the matching value rows. V of tile i
-// streams while the logits of tile i are computed, K of tile i+1 while the
-// values of tile i are accumulated. No float atomics anywhere.
+// split uses equal weights and the claims are static (wavefront w takes claims
+// w, w + NW, ...), so the result is bitwise reproducible; by default repeated
+// calls agree to float32 rounding. A wavefront owns a whole tile: 16-byte
+// loads of one 64 x d tile (lane (r, cb) holds rows RPI*i + r, 8 bf16
+// columns), keys consumed by v_dot2 bf16 products into per-lane partial
+// logits, finished by a transposing DPP reduction that leaves one token's logit
+// per lane. The gate and the online softmax run per lane in float32 (running
+// max per row of lanes); the weights go through LDS to the lanes holding the
+// matching value rows. V of tile i streams while the logits of tile i are
+// computed, K of tile i+1 while the values of tile i are accumulated. No float
+// atomics anywhere.
 #include "eta_device.h"
 
 namespace eta {
@@ -74,6 +79,95 @@ __device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nc
   return __builtin_amdgcn_readfirstlane(v);
 }
 
+// Merge of one segment's partials into the output, by the workgroup that
+// completed the segment: for each of its G heads,
+// o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p over the partial slots
+// p = kf + s .. kl + s. Thread (group pg, head h, float4 column group cg)
+// loads the partials pg, pg + PG, ... (kMergeBatch of them in flight) and
+// folds them with an online maximum; the PG groups are then combined in a
+// fixed order, so the result does not depend on timing. NaN when nothing was
+// accumulated.
+constexpr int kMergeBatch = 16;
+
+template <int D, int G, int NTH>
+__device__ void merge_segment(const Ws& ws, float* out, int s, int n, int g, int HQ, int kf, int kl) {
+  constexpr int CG = D / 4;                       // float4 column groups
+  constexpr int OUTS = G * CG;                    // (head, column group) outputs
+  static_assert(OUTS <= NTH, "one thread per output at least");
+  constexpr int PG = NTH / OUTS;                  // thread groups splitting the partials
+  __shared__ float4 red_a[PG][OUTS];
+  __shared__ float2 red_ml[PG][OUTS];
+  const int tid = threadIdx.x;
+  const int o = tid % OUTS, pg = tid / OUTS;
+  const bool act = pg < PG;
+  const int h = o / CG, cg = o % CG;
+  const int np = kl - kf + 1;
+  const int64_t slot0 = (int64_t)kf + s;
+  float M = -__builtin_inff(), l = 0.f;
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (act) {
+    for (int p0 = pg; p0 < np; p0 += kMergeBatch * PG) {
+      float4 v[kMergeBatch];
+      float2 ml[kMergeBatch];
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int p = p0 + j * PG;
+        const int64_t sl = slot0 + (p < np ? p : 0);
+        v[j] = *(const float4*)&ws.part_acc[(sl * G + h) * D + 4 * cg];
+        ml[j] = *(const float2*)&ws.part_ml[(sl * G + h) * 2];
+        if (p >= np) ml[j].x = -__builtin_inff();
+      }
+      float Mb = M;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j].x);
+      if (Mb == -__builtin_inff()) continue;
+      const float sc = M == -__builtin_inff() ? 0.f : fast_exp(M - Mb);
+      l *= sc;
+      a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
+      M = Mb;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float wgt = ml[j].x == -__builtin_inff() ? 0.f : fast_exp(ml[j].x - M);
+        l = fmaf(wgt, ml[j].y, l);
+        a.x = fmaf(wgt, v[j].x, a.x);
+        a.y = fmaf(wgt, v[j].y, a.y);
+        a.z = fmaf(wgt, v[j].z, a.z);
+        a.w = fmaf(wgt, v[j].w, a.w);
+      }
+    }
+    red_a[pg][o] = a;
+    red_ml[pg][o] = make_float2(M, l);
+  }
+  __syncthreads();
+  if (pg == 0) {
+    float Mt = -__builtin_inff();
+#pragma unroll
+    for (int q = 0; q < PG; ++q) Mt = fmaxf(Mt, red_ml[q][o].x);
+    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+    float lt = 0.f;
+#pragma unroll
+    for (int q = 0; q < PG; ++q) {
+      const float2 mq = red_ml[q][o];
+      const float wq = mq.x == -__builtin_inff() ? 0.f : fast_exp(mq.x - Mt);
+      const float4 u = red_a[q][o];
+      lt = fmaf(wq, mq.y, lt);
+      t.x = fmaf(wq, u.x, t.x);
+      t.y = fmaf(wq, u.y, t.y);
+      t.z = fmaf(wq, u.z, t.z);
+      t.w = fmaf(wq, u.w, t.w);
+    }
+    float4 r;
+    if (lt > 0.f) {
+      r = make_float4(t.x / lt, t.y / lt, t.z / lt, t.w / lt);
+    } else {
+      const float nan = __builtin_nanf("");
+      r = make_float4(nan, nan, nan, nan);
+    }
+    *(float4*)&out[((int64_t)n * HQ + g * G + h) * D + 4 * cg] = r;
+  }
+  if (tid == 0) ws.seg_done[s] = 0;  // ready for the next decode
+}
+
 // Wavefronts per attend workgroup: eight (two per SIMD, one workgroup per CU)
 // when a wavefront fits in 256 VGPRs, else four with the full register file.
 template <typename T, int D, int G>
@@ -104,6 +198,7 @@ void k_attend(AttendArgs A) {
   __shared__ int ctr_lds;
   __shared__ int scan_lds[NW];
   __shared__ int pick_lds[3];
+  __shared__ int last_lds;
   const int NT = A.d.NT;
 
   // ---- the work split, from the segments' union counts: Utot entries in
@@ -122,7 +217,10 @@ void k_attend(AttendArgs A) {
     block_incl_scan<NW>(rest, &totr, scan_lds);
     Utot += totr;
   }
-  const int Wp = Utot < (int)gridDim.x ? Utot : (int)gridDim.x;
+  Utot = __builtin_amdgcn_readfirstlane(Utot);
+  // at least 8 entries per range on average, so that no range is empty at any
+  // weights in [1/2, 2]
+  const int Wp = Utot < 8 * (int)gridDim.x ? (Utot + 7) / 8 : (int)gridDim.x;
   const int k = blockIdx.x;
   if (k >= Wp) return;
   int64_t lo, hi;
@@ -155,8 +253,13 @@ void k_attend(AttendArgs A) {
     }
   }
   __syncthreads();
-  int s = lo < hi ? pick_lds[0] : 0;
-  int P = lo < hi ? pick_lds[1] : 0, Us = lo < hi ? pick_lds[2] : 0;
+  // (uniform values go through readfirstlane so that they live in scalar
+  // registers: the streaming loop needs every vector register)
+  int s = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[0] : 0);
+  int P = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[1] : 0);
+  int Us = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[2] : 0);
+  const int s_first = s, P_first = P, U_first = Us;
+  const int64_t lo_first = lo;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -430,6 +533,47 @@ void k_attend(AttendArgs A) {
     __syncthreads();
     lo = (int64_t)P + e1;
   }
+
+  // ---- arrivals: for every segment the range touched, add its entries to the
+  //      segment's count; the workgroup that completes a segment merges the
+  //      segment's partials (slots kf + s .. kl + s) into the output. The
+  //      workgroup barrier orders every wavefront's partial stores before
+  //      thread 0's device-scope release and counts; a merging workgroup
+  //      acquires at device scope after its count.
+  __syncthreads();
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  {
+    int s2 = s_first, P2 = P_first, U2 = U_first;
+    int64_t x = lo_first;
+    while (x < hi) {
+      while (x >= (int64_t)P2 + U2) {
+        P2 += U2;
+        ++s2;
+        U2 = A.ws.seg_U[s2];
+      }
+      const int c0 = (int)(x - P2);
+      const int c1 = (int)((hi < (int64_t)P2 + U2 ? hi : (int64_t)P2 + U2) - P2);
+      if (threadIdx.x == 0) {
+        // one 64-bit add carries the entry count and, from the ranges that
+        // hold the segment's first and last entries, their indices
+        const uint64_t add = (uint64_t)(c1 - c0) + (c0 == 0 ? (uint64_t)k << 32 : 0ull) +
+                             (c1 == U2 ? (uint64_t)k << 48 : 0ull);
+        const uint64_t tot =
+            __hip_atomic_fetch_add(&A.ws.seg_done[s2], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+        const bool last = (uint32_t)tot == (uint32_t)U2;
+        last_lds = last ? 1 : 0;
+        pick_lds[0] = (int)((tot >> 32) & 0xffffu);  // kf
+        pick_lds[1] = (int)(tot >> 48);              // kl
+      }
+      __syncthreads();
+      if (last_lds) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        merge_segment<D, G, NTH>(A.ws, A.p.out, s2, s2 / HKV, s2 % HKV, HQ, pick_lds[0], pick_lds[1]);
+      }
+      __syncthreads();
+      x = (int64_t)P2 + c1;
+    }
+  }
   // entries and duration of this range, read by the next decode's weighting
   if (threadIdx.x == 0) {
     const uint64_t t_end = __builtin_amdgcn_s_memrealtime();
@@ -439,108 +583,6 @@ void k_attend(AttendArgs A) {
       A.ws.glob[kGlobStatMagic] = kStatMagic;
       A.ws.glob[kGlobStatW] = Wp;
     }
-  }
-}
-
-// ---------------------------------------------------------------- merge
-struct MergeArgs {
-  Dims d;
-  Ws ws;
-  float* out;
-  int W;              // attend grid
-  int deterministic;
-};
-
-// One workgroup per (sequence, query head): o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p
-// over the partials p of the head's segment. The segment's partials are the
-// slots k + s of the attend ranges k that overlap it, found from the union
-// counts the same way the attend kernel split the work. Threads: D/4 column
-// groups of float4 x (256 / (D/4)) piece groups.
-template <int D, int G>
-__global__ __launch_bounds__(256) void k_merge(MergeArgs A) {
-  constexpr int CG = D / 4;          // float4 column groups
-  constexpr int PGN = 256 / CG;      // piece groups
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nh = blockIdx.x;
-  const int HQ = A.d.HQ;
-  const int n = nh / HQ, h = nh % HQ;
-  const int g = h / G, hl = h % G;
-  const int s = n * A.d.HKV + g, S = A.d.S;
-  __shared__ float s_red[4];
-  __shared__ float4 s_acc[PGN][CG];
-  __shared__ float s_l[PGN];
-  __shared__ int s_scan[4];
-
-  // first entry P of the segment, its count u and the total
-  int below = 0, all = 0;
-  for (int i = tid; i < S; i += 256) {
-    const int v = A.ws.seg_U[i];
-    all += v;
-    if (i < s) below += v;
-  }
-  const int u = A.ws.seg_U[s];
-  int P, Utot;
-  block_incl_scan<4>(below, &P, s_scan);
-  block_incl_scan<4>(all, &Utot, s_scan);
-  int wts[kXcdClasses];
-  load_weights(A.ws.xcd_w, A.deterministic, wts);
-  RangeSplit sp;
-  int plo = 0, phi = -1;
-  if (u > 0) {
-    sp.init(Utot, Utot < A.W ? Utot : A.W, wts);
-    plo = sp.holder(P) + s;          // range holding entry P
-    phi = sp.holder(P + u - 1) + s;  // range holding entry P + u - 1
-  }
-  // ranges without entries wrote no partial
-  auto has = [&](int p) { return sp.B(p - s) < sp.B(p - s + 1); };
-
-  float M = -__builtin_inff();
-  for (int p = plo + tid; p <= phi; p += 256)
-    if (has(p)) M = fmaxf(M, A.ws.part_ml[((int64_t)p * G + hl) * 2]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, shfl_xor_f(M, o));
-  if (lane == 0) s_red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-
-  const int cg = tid % CG, pg = tid / CG;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float lsum = 0.f;
-#pragma unroll 4
-  for (int p = plo + pg; p <= phi; p += PGN) {
-    if (!has(p)) continue;
-    const float2 ml = *(const float2*)&A.ws.part_ml[((int64_t)p * G + hl) * 2];
-    const float4 a = *(const float4*)&A.ws.part_acc[((int64_t)p * G + hl) * D + cg * 4];
-    const float wgt = ml.x == -__builtin_inff() ? 0.f : fast_exp(ml.x - M);
-    lsum = fmaf(wgt, ml.y, lsum);
-    acc.x = fmaf(wgt, a.x, acc.x);
-    acc.y = fmaf(wgt, a.y, acc.y);
-    acc.z = fmaf(wgt, a.z, acc.z);
-    acc.w = fmaf(wgt, a.w, acc.w);
-  }
-  s_acc[pg][cg] = acc;
-  if (cg == 0) s_l[pg] = lsum;
-  __syncthreads();
-  if (tid < CG) {
-    float4 t = s_acc[0][tid];
-    float l = s_l[0];
-    for (int q = 1; q < PGN; ++q) {
-      const float4 u = s_acc[q][tid];
-      t.x += u.x;
-      t.y += u.y;
-      t.z += u.z;
-      t.w += u.w;
-      l += s_l[q];
-    }
-    float4 o;
-    if (l > 0.f) {
-      o = make_float4(t.x / l, t.y / l, t.z / l, t.w / l);
-    } else {
-      const float nan = __builtin_nanf("");
-      o = make_float4(nan, nan, nan, nan);
-    }
-    *(float4*)&A.out[((int64_t)n * HQ + h) * D + tid * 4] = o;
   }
 }
 
@@ -584,34 +626,12 @@ int occupancy_g(int G) {
   return 1;
 }
 
-template <int D, int G>
-hipError_t merge_impl(const Dims& d, const DecodeParams& p, const Ws& ws, int W, hipStream_t st) {
-  MergeArgs a{d, ws, p.out, W, p.deterministic};
-  hipLaunchKernelGGL((k_merge<D, G>), dim3(d.N * d.HQ), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
-template <int D>
-hipError_t merge_g(const Dims& d, const DecodeParams& p, const Ws& ws, int W, hipStream_t st) {
-  switch (d.G) {
-    case 1: return merge_impl<D, 1>(d, p, ws, W, st);
-    case 2: return merge_impl<D, 2>(d, p, ws, W, st);
-    case 4: return merge_impl<D, 4>(d, p, ws, W, st);
-    case 8: return merge_impl<D, 8>(d, p, ws, W, st);
-  }
-  return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int W, hipStream_t st) {
   if (c.kv_dtype == 1) return d.D == 128 ? attend_g<Bf16, 128>(c, s, p, d, ws, W, st) : attend_g<Bf16, 64>(c, s, p, d, ws, W, st);
   return d.D == 128 ? attend_g<F32, 128>(c, s, p, d, ws, W, st) : attend_g<F32, 64>(c, s, p, d, ws, W, st);
-}
-
-hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, int attend_wgs, hipStream_t st) {
-  return d.D == 128 ? merge_g<128>(d, p, ws, attend_wgs, st) : merge_g<64>(d, p, ws, attend_wgs, st);
 }
 
 int attend_wgs_per_cu(int kv_dtype, int D, int G) {

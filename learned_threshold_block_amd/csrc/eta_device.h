@@ -187,16 +187,6 @@ struct RangeSplit {
     return (int64_t)(k / kXcdClasses) * wsum + part;
   }
   __device__ int64_t B(int k) const { return utot * C(k) / cw; }
-  // the range holding entry x (the largest k < W with B(k) <= x)
-  __device__ int holder(int64_t x) const {
-    int lo = 0, hi = W - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (B(mid) <= x) lo = mid;
-      else hi = mid - 1;
-    }
-    return lo;
-  }
 };
 
 // Per-die weights as stored in the workspace, clamped to the range the

@@ -42,6 +42,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_done = (uint64_t*)take(sizeof(uint64_t) * S);
   w.rng_stat = (int32_t*)take(sizeof(int32_t) * 2 * kMaxAttendWgs);
   w.xcd_w = (int32_t*)take(sizeof(int32_t) * kXcdClasses);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
@@ -226,8 +227,7 @@ eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
     case ETA_PHASE_ATTEND:
       e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);
       break;
-    case ETA_PHASE_MERGE:
-      e = launch_merge(P.d, P.p, P.ws, grid, st);
+    case ETA_PHASE_MERGE:  // merged at the end of the attend phase
       break;
     default:
       return ETA_ERR_INVALID_ARGUMENT;

@@ -51,6 +51,8 @@ struct Ws {
   int32_t* seg_U;       // [S]          union blocks per segment
   int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
   int32_t* seg_err;     // [S]
+  uint64_t* seg_done;   // [S]          arrivals (zeroed by finalize): bits 0-31 entries whose partial is
+                        //              written, 32-47 the range holding the first entry, 48-63 the last
   int32_t* rng_stat;    // [kMaxAttendWgs][2] entries and duration (10 ns ticks) of each attend range
   int32_t* xcd_w;       // [kXcdClasses]  work weight of each die class (kWeightOne = 1)
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
@@ -98,10 +100,9 @@ hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new
 hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, hipStream_t st);
 hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                           const Ws& ws, hipStream_t st);
+                           const Ws& ws, hipStream_t st);  // also writes NaN rows for segments with no entries
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
-hipError_t launch_merge(const Dims& d, const DecodeParams& p, const Ws& ws, int attend_wgs, hipStream_t st);
 int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
 
 }  // namespace eta

@@ -237,6 +237,7 @@ struct FinArgs {
   SeqView s;
   Dims d;
   Ws ws;
+  float* out;
   int deterministic;
   int fixed_w[kXcdClasses];
 };
@@ -497,6 +498,14 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     A.ws.seg_U[s] = U;
     A.ws.seg_ntn[s] = ntn;
     A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
+    A.ws.seg_done[s] = 0;
+  }
+  // a segment without entries (invalid length) gets no attend work: its
+  // heads' outputs are NaN, as for an empty softmax
+  if (U == 0) {
+    const int D = A.d.D;
+    for (int i = tid; i < G * D; i += 256)
+      A.out[((int64_t)n * HQ + g * G) * D + i] = __builtin_nanf("");
   }
 }
 
@@ -524,7 +533,7 @@ hipError_t screen_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
 template <int G>
 hipError_t finalize_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, hipStream_t st) {
-  FinArgs a{c, s, d, ws, p.deterministic, {}};
+  FinArgs a{c, s, d, ws, p.out, p.deterministic, {}};
   for (int x = 0; x < kXcdClasses; ++x) a.fixed_w[x] = p.fixed_w[x];
   hipLaunchKernelGGL((k_finalize<G>), dim3(d.S + 1), dim3(256), 0, st, a);
   return hipGetLastError();
