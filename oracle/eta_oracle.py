@@ -43,8 +43,16 @@ and outputs), exact bound soundness, no-false-negative and nesting properties,
 dense mode against torch's scaled_dot_product_attention, closed forms for the
 all-suppressed, equal-logit and single-key cases, the fp16 rounding mode of
 mu^, page-permutation invariance, and the sigmoid convention values of B.1.
-Parity unpinned: the pages' own dual bound (Eq. 7) and their chunk-local
-rescue rule are not reproducible from the text and are not implemented here.
+Optional dual screen (Sections 3.1 and F.1; Eq. 7 did not survive): each
+record also carries the coordinate standard deviation sigma^ (float16), and a
+block's score is the smaller of the geometric bound and the probabilistic
+estimate s (q . mu^ + z ||q * sigma^||), z = 2 by default (B.1 tables). This
+reading is not sound (it can miss a block whose best key lies more than z
+deviations out), so its sets are pinned against a per-key brute force and
+measured for recall, not checked for soundness.
+
+Parity unpinned: the pages' exact Eq. 7 and their chunk-local rescue rule are
+not reproducible from the text and are not implemented here.
 """
 from __future__ import annotations
 
@@ -144,6 +152,39 @@ def build_summaries(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray,
 
 
 # --------------------------------------------------------------------------- screen
+def block_sigma(kb: np.ndarray) -> np.ndarray:
+    """Coordinate standard deviation of complete blocks (kb float64 [nb, 64, d]):
+    population deviation (divide by 64) about the float64 mean, stored as
+    float16 with round to nearest even; +inf where it is not finite. Section
+    F.1: 64-dimensional coordinate standard deviation in float16 (the deviation
+    rather than the variance, which would underflow in half precision)."""
+    single = kb.ndim == 2
+    if single:
+        kb = kb[None]
+    with np.errstate(over="ignore", invalid="ignore"):
+        mean = kb.mean(axis=1)
+        dev = kb - mean[:, None, :]
+        sd = np.sqrt((dev * dev).mean(axis=1))
+        sd16 = sd.astype(np.float16).astype(np.float64)
+    sd16 = np.where(np.isfinite(sd16), sd16, np.inf)
+    return sd16[0] if single else sd16
+
+
+def build_sigmas(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, seq_lens: np.ndarray):
+    """sigma^ for every complete block of every (sequence, KV head): float64
+    [num_pages][H_KV][d] holding float16 values, NaN where there is none."""
+    P, HKV, B, D = k_pages.shape
+    sig = np.full((P, HKV, D), np.nan)
+    for n in range(len(seq_lens)):
+        nfull = int(seq_lens[n]) // BLOCK
+        pages = np.asarray(block_table[n, :nfull], dtype=np.int64)
+        for g in range(HKV):
+            for j0 in range(0, nfull, _CHUNK_BLOCKS):
+                pg = pages[j0:j0 + _CHUNK_BLOCKS]
+                sig[pg, g] = block_sigma(upcast(k_pages[pg, g], kv_dtype))
+    return sig
+
+
 def threshold(mode: str, q_h: np.ndarray, w_h, b_h: float, a: float) -> float:
     """Effective threshold tau~ = tau - a.
 
@@ -166,6 +207,20 @@ def block_bound(q: np.ndarray, mu: np.ndarray, R: np.ndarray, scale: float) -> n
     nq = math.sqrt(float(np.dot(q, q)))
     with np.errstate(invalid="ignore", over="ignore"):
         return scale * (mu @ q + nq * R)
+
+
+def dual_score(q: np.ndarray, mu: np.ndarray, R: np.ndarray, sigma: np.ndarray, scale: float,
+               z: float) -> np.ndarray:
+    """Dual screen score of each block: the smaller of the geometric bound
+    s (q . mu^ + ||q|| R) and the probabilistic estimate
+    s (q . mu^ + z ||q * sigma^||_2) (Sections 3.1 and F.1, reading of the lost
+    Eq. 7). A NaN on one side leaves the other (np.fmin)."""
+    q = np.asarray(q, dtype=np.float64)
+    geo = block_bound(q, mu, R, scale)
+    with np.errstate(invalid="ignore", over="ignore"):
+        spread = np.sqrt(((sigma * q[None, :]) ** 2).sum(axis=1))
+        prob = scale * (mu @ q + z * spread)
+    return np.fmin(geo, prob)
 
 
 def admitted_blocks(ub: np.ndarray, tau: float, seq_len: int, lwb: int):
@@ -222,12 +277,15 @@ class DecodeResult:
 
 def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str,
            w, b_or_c, a: float, beta: float, lwb: int, summaries=None,
-           heads: Optional[Iterable] = None, with_output: bool = True) -> DecodeResult:
+           heads: Optional[Iterable] = None, with_output: bool = True,
+           bound: str = "geometric", z: float = 2.0, sigmas=None) -> DecodeResult:
     """One ETA decode step for every sequence and query head.
 
     q: [N][H_Q][d] stored values; w: [H_Q][d] (learned mode); b_or_c: [H_Q].
     summaries: (mu, R) from build_summaries, built here if omitted.
-    heads: iterable of (n, h) whose output is evaluated (default: all)."""
+    heads: iterable of (n, h) whose output is evaluated (default: all).
+    bound: "geometric" (the sound bound) or "dual" (dual_score with z and the
+    sigma^ records from build_sigmas, built here if omitted)."""
     N, HQ, D = q.shape
     P, HKV, B, D2 = k_pages.shape
     assert D2 == D and B == BLOCK and HQ % HKV == 0
@@ -237,6 +295,10 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
     if summaries is None:
         summaries = build_summaries(k_pages, kv_dtype, block_table, seq_lens)
     mu_all, R_all = summaries
+    if bound not in ("geometric", "dual"):
+        raise ValueError(f"unknown bound {bound!r}")
+    if bound == "dual" and sigmas is None:
+        sigmas = build_sigmas(k_pages, kv_dtype, block_table, seq_lens)
     qf = upcast(q, kv_dtype)
     want = None if heads is None else set((int(n), int(h)) for n, h in heads)
 
@@ -253,7 +315,11 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
             g = h // G
             tau = threshold(tau_mode, qf[n, h], None if w is None else w[h], b_or_c[h], a)
             taus[n, h] = tau
-            ub = block_bound(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g], scale)
+            if bound == "dual":
+                ub = dual_score(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g],
+                                sigmas[pages[:nfull], g], scale, z)
+            else:
+                ub = block_bound(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g], scale)
             ubs[n, h, :nfull] = ub
             adm, resc = admitted_blocks(ub, tau, T, lwb)
             admitted[n, h, :len(adm)] = adm

@@ -5,7 +5,8 @@ over every key with the `math` module (fsum, exact float16 rounding through
 `struct`), no NumPy vector arithmetic and no code shared with `oracle/`.
 It follows "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888),
 Sections 2.2, 3.1, 3.2, 4.8, F.1, F.4 and G.1, with the same readings as the
-oracle (geometric bound about the fp16 centroid, global top-1 rescue).
+oracle (geometric bound about the fp16 centroid, global top-1 rescue; the
+optional dual score as the smaller of that bound and s (q . mu^ + z ||q * sigma^||)).
 """
 from __future__ import annotations
 
@@ -59,7 +60,33 @@ def record(rows):
     return mu, best
 
 
-def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, a, beta, lwb):
+def deviation(rows):
+    """Coordinate standard deviation (population) of one block about its exact
+    mean, rounded to float16; inf where not finite."""
+    d = len(rows[0])
+    out = []
+    for c in range(d):
+        col = [r[c] for r in rows]
+        try:
+            m = math.fsum(col) / len(col)
+            sd = math.sqrt(math.fsum((x - m) ** 2 for x in col) / len(col))
+        except (OverflowError, ValueError):
+            sd = math.inf
+        sd = _f16(sd) if math.isfinite(sd) else math.inf
+        out.append(sd)
+    return out
+
+
+def _smaller(a: float, b: float) -> float:
+    if math.isnan(a):
+        return b
+    if math.isnan(b):
+        return a
+    return min(a, b)
+
+
+def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, a, beta, lwb,
+           bound="geometric", z=2.0):
     """Returns dict with per (n, h): admitted block list, rescued flag, output
     list, plus union counts per (n, g). Inputs are NumPy arrays of stored values
     but are read element by element."""
@@ -84,6 +111,8 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
 
         for g in range(HKV):
             recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
+            devs = [deviation([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
+                if bound == "dual" else None
             loaded = set()
             for hh in range(G):
                 h = g * G + hh
@@ -99,6 +128,13 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                     mu, R = recs[j]
                     dot = math.fsum(qh[c] * mu[c] for c in range(D))
                     ub = s * (dot + qn * R)
+                    if bound == "dual":
+                        try:
+                            spread = math.sqrt(math.fsum((qh[c] * devs[j][c]) ** 2 for c in range(D)))
+                            est = s * (dot + z * spread)
+                        except (OverflowError, ValueError):
+                            est = math.inf
+                        ub = _smaller(ub, est)
                     ubs.append(ub)
                     forced = j >= nfull - lwb
                     if forced or not (ub < tau):
@@ -123,8 +159,8 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                         if t >= T:
                             break
                         S = s * math.fsum(qh[c] * x for c, x in enumerate(key(g, t)))
-                        z = beta * (S - tau)
-                        logits.append(S * _sig(z))
+                        arg = beta * (S - tau)
+                        logits.append(S * _sig(arg))
                         vals.append(val(g, t))
                 m = max(logits)
                 wts = [math.exp(x - m) for x in logits]

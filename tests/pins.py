@@ -146,6 +146,85 @@ def pin_bound_sound_and_tight(E, seed=0, trials=200):
             assert abs(ub - smax) <= 1e-9 * (1 + abs(smax)), ("not tight", it, kind, ub, smax)
 
 
+
+# --------------------------------------------------------------------------- dual screen
+def pin_sigma_rne(E):
+    """sigma^ is the population deviation about the exact mean, stored as
+    float16 with round to nearest even (F.1)."""
+    d = 4
+    for a, b, want in [(3.0, 1.0 + 2.0 ** -11, 1.0),               # tie -> even (down)
+                       (3.0, 1.0 + 3 * 2.0 ** -11, 1.0 + 2.0 ** -9),  # tie -> even (up)
+                       (-7.25, 0.125, 0.125),
+                       (100.0, 2.0 ** -20, 2.0 ** -20)]:              # float16 subnormal range
+        kb = np.full((64, d), a)
+        kb[::2] += b
+        kb[1::2] -= b
+        sig = E.block_sigma(kb)
+        assert np.all(sig == np.float64(np.float16(want))), (a, b, sig)
+    assert np.all(E.block_sigma(np.full((64, d), 5.5)) == 0.0)
+    kb = np.zeros((64, d))
+    kb[7, 2] = np.inf
+    assert np.isinf(E.block_sigma(kb)[2])
+
+
+def pin_dual_closed_form(E):
+    """Keys mu +/- b (every coordinate) around an fp16-exact mu: sigma^ = b,
+    R = b sqrt(d); the dual score is s (q.mu + z b ||q||) for z < sqrt(d) and
+    the geometric bound s (q.mu + b sqrt(d) ||q||) for z > sqrt(d)."""
+    rng = np.random.default_rng(3)
+    d = 8
+    mu = np.round(rng.standard_normal(d) * 64) / 64
+    b = 0.375
+    kb = np.repeat(mu[None], 64, axis=0)
+    kb[::2] += b
+    kb[1::2] -= b
+    m, R = E.block_summary(kb)
+    sig = E.block_sigma(kb)
+    assert np.array_equal(m, mu) and abs(R - b * math.sqrt(d)) < 1e-15 and np.all(sig == b)
+    q = rng.standard_normal(d)
+    s = 1 / math.sqrt(d)
+    qn = math.sqrt(float(q @ q))
+    for z, want in [(2.0, s * (q @ mu + 2.0 * b * qn)), (3.0, s * (q @ mu + b * math.sqrt(d) * qn))]:
+        got = float(E.dual_score(q, m[None], np.array([R]), sig[None], s, z)[0])
+        assert abs(got - want) <= 1e-12 * (1 + abs(want)), (z, got, want)
+
+
+def pin_dual_within_geometric(E, seeds=range(3)):
+    """The dual score never exceeds the geometric bound, so without rescue the
+    dual sets nest inside the geometric ones; a huge z gives the geometric sets."""
+    for seed in seeds:
+        wl = tiny(40 + seed, n=2, lens=(64 * 9 + 3, 64 * 5 + 7), h_q=4, h_kv=2, d=8, mode="calibrated",
+                  bias=np.full(4, 1.0, dtype=np.float32))
+        geo = _decode(E, wl, with_output=False)
+        dual = _decode(E, wl, with_output=False, bound="dual", z=2.0)
+        assert not geo.rescued.any() and not dual.rescued.any()
+        ok = ~np.isnan(geo.ub)
+        assert np.all(dual.ub[ok] <= geo.ub[ok])
+        assert np.all(dual.admitted <= geo.admitted)
+        huge = _decode(E, wl, with_output=False, bound="dual", z=1e6)
+        assert np.array_equal(huge.admitted, geo.admitted)
+
+
+def pin_dual_bruteforce(E, seeds=range(3)):
+    """Dual-screen sets, counts and outputs equal the per-key brute force."""
+    variants = [dict(n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(320,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated"),
+                dict(n=2, lens=(130, 256), h_q=2, h_kv=2, d=8, dtype="bf16", mode="calibrated", lwb=1)]
+    for seed in seeds:
+        wl = tiny(60 + seed, **variants[seed % len(variants)])
+        res = _decode(E, wl, bound="dual", z=2.0)
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb, bound="dual", z=2.0)
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, n, h, got, r["admitted"])
+            assert bool(res.rescued[n, h]) == r["rescued"]
+            np.testing.assert_allclose(res.ub[n, h, :len(r["ub"])], r["ub"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+
 # --------------------------------------------------------------------------- thresholds
 def pin_threshold_closed_form(E):
     """tau~ = w.q + b - a (learned), c - a (calibrated): Sections 1, 4.7, D.1, G.1."""
@@ -371,4 +450,5 @@ ALL_PINS = [
     pin_threshold_closed_form, pin_bruteforce, pin_no_false_negatives, pin_nesting,
     pin_dense_sdpa, pin_suppressed_mean, pin_equal_logits, pin_two_keys_closed_form,
     pin_tail_masking, pin_page_permutation, pin_nonfinite_keys, pin_threshold_tie_admitted,
+    pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
 ]

@@ -38,6 +38,13 @@ MUTANTS = {
     "token_count_ignores_tail": ("width = np.minimum(BLOCK, T - BLOCK * np.arange(nblk))",
                                  "width = np.full(nblk, BLOCK)"),
     "strict_bound_comparison": ("adm[:nfull] = ~(ub < tau)", "adm[:nfull] = ub > tau + 1e-3"),
+    "sigma_is_variance": ("sd = np.sqrt((dev * dev).mean(axis=1))", "sd = (dev * dev).mean(axis=1)"),
+    "sigma_sample_deviation": ("sd = np.sqrt((dev * dev).mean(axis=1))",
+                               "sd = np.sqrt((dev * dev).sum(axis=1) / (kb.shape[1] - 1))"),
+    "dual_takes_larger": ("return np.fmin(geo, prob)", "return np.fmax(geo, prob)"),
+    "dual_drops_z": ("prob = scale * (mu @ q + z * spread)", "prob = scale * (mu @ q + spread)"),
+    "dual_spread_unsquared": ("spread = np.sqrt(((sigma * q[None, :]) ** 2).sum(axis=1))",
+                              "spread = (sigma * np.abs(q[None, :])).sum(axis=1)"),
 }
 
 
