@@ -57,7 +57,8 @@ typedef enum {
 
 enum { ETA_F32 = 0, ETA_BF16 = 1 };                 /* K/V/q element type */
 enum { ETA_TAU_LEARNED = 0, ETA_TAU_CALIBRATED = 1 }; /* threshold mode */
-enum { ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
+enum { ETA_PHASE_ALL = -1, ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
+enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1 }; /* block screen, see eta_screen_opts */
 
 /* Paged KV cache plus its per-block records (caller-owned device buffers).
  *   k_pages, v_pages : [num_pages][num_kv_heads][block_size][head_dim] of
@@ -68,6 +69,12 @@ enum { ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
  *   radius           : [num_pages][num_kv_heads] float32, an upper bound on the
  *                      distance of every key of the block to mu (rounded up;
  *                      +inf for blocks holding non-finite keys), 4-byte aligned.
+ *   sigma            : NULL, or [num_pages][num_kv_heads][head_dim] float16 bit
+ *                      patterns, 16-byte aligned: the coordinate standard
+ *                      deviation of the block's keys (population, about their
+ *                      mean), rounded to nearest even; +inf where not finite
+ *                      (Section F.1; only the dual screen reads it). When not
+ *                      NULL, the record builders fill it too.
  * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
 typedef struct {
   int kv_dtype;
@@ -79,6 +86,7 @@ typedef struct {
   void* v_pages;
   uint16_t* mu;
   float* radius;
+  uint16_t* sigma;
 } eta_cache;
 
 /* Sequences of a batch.
@@ -138,6 +146,32 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
                       int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
                       float a, float beta, int lwb, int block_size, float* out,
                       void* workspace, size_t ws_bytes, eta_stream_t stream);
+
+/* Block screen of a decode step (Sections 3.1 and F.1).
+ *   ETA_BOUND_GEOMETRIC : score s (q . mu + ||q|| R), an upper bound on the
+ *                         scaled logit of every key of the block (the default).
+ *   ETA_BOUND_DUAL      : score min(geometric, s (q . mu + z ||q * sigma||)), the
+ *                         geometric bound tightened by a z-deviation estimate
+ *                         (the reading of the paper's dual bound, Eq. 7, whose
+ *                         display did not survive). Not a bound: a block whose
+ *                         best key lies more than z deviations out can be
+ *                         missed. Needs cache->sigma; z finite and >= 0
+ *                         (2.0 in the paper's B.1 tables).
+ * The score also ranks blocks for the top-1 rescue. */
+typedef struct {
+  int bound;
+  float z;
+} eta_screen_opts;
+
+/* eta_decode / eta_decode_phase with a screen choice: phase is ETA_PHASE_ALL
+ * for the whole step or one ETA_PHASE_*; screen NULL means the geometric bound.
+ * Returns ETA_ERR_INVALID_ARGUMENT for an unknown bound, a negative or
+ * non-finite z, or the dual bound without cache->sigma. */
+eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache,
+                         const eta_seqs* seqs, const void* q, int num_q_heads, int tau_mode,
+                         const float* w, const float* b_or_c, float a, float beta, int lwb,
+                         int block_size, float* out, void* workspace, size_t ws_bytes,
+                         eta_stream_t stream);
 
 /* One phase of eta_decode with the same arguments, for callers that overlap or
  * time the phases: ETA_PHASE_SCREEN (thresholds, bound screen, compaction of

@@ -16,8 +16,8 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    ETA_BF16, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
-    ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
+    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
+    ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ALL, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
     ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
 
@@ -60,6 +60,7 @@ class Cache:
     v_pages: torch.Tensor
     mu: torch.Tensor       # float16 [num_pages][H_KV][d]
     radius: torch.Tensor   # float32 [num_pages][H_KV]
+    sigma: Optional[torch.Tensor] = None  # float16 [num_pages][H_KV][d], for the dual screen
 
     def __post_init__(self):
         _need(self.k_pages, "k_pages")
@@ -74,14 +75,19 @@ class Cache:
         P, H, B, D = self.k_pages.shape
         if tuple(self.mu.shape) != (P, H, D) or tuple(self.radius.shape) != (P, H):
             raise ValueError("mu must be [num_pages][H_KV][d] and radius [num_pages][H_KV]")
+        if self.sigma is not None:
+            _need(self.sigma, "sigma", torch.float16, dev)
+            if tuple(self.sigma.shape) != (P, H, D):
+                raise ValueError("sigma must be [num_pages][H_KV][d]")
 
     @classmethod
-    def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda"):
+    def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False):
         k = torch.zeros(num_pages, num_kv_heads, BLOCK, head_dim, dtype=dtype, device=device)
         v = torch.zeros_like(k)
         mu = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.float16, device=device)
         r = torch.zeros(num_pages, num_kv_heads, dtype=torch.float32, device=device)
-        return cls(k, v, mu, r)
+        sig = torch.zeros_like(mu) if with_sigma else None
+        return cls(k, v, mu, r, sig)
 
     @property
     def kv_dtype(self) -> int:
@@ -98,7 +104,7 @@ class Cache:
     def c_struct(self) -> _lib.EtaCacheC:
         P, H, B, D = self.k_pages.shape
         return _lib.EtaCacheC(self.kv_dtype, D, H, B, P, _ptr(self.k_pages), _ptr(self.v_pages),
-                              _ptr(self.mu), _ptr(self.radius))
+                              _ptr(self.mu), _ptr(self.radius), _ptr(self.sigma))
 
 
 def _seqs(seq_lens: torch.Tensor, block_table: torch.Tensor, device) -> _lib.EtaSeqsC:
@@ -142,9 +148,10 @@ def alloc_workspace(cache: Cache, num_seqs: int, max_blocks_per_seq: int, num_q_
 
 def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None, a: float = 0.0,
            beta: float = 5.0, lwb: int = 0, out=None, workspace=None, phase: Optional[int] = None,
-           stream=None) -> torch.Tensor:
+           stream=None, bound: str = "geometric", z: float = 2.0) -> torch.Tensor:
     """One ETA decode step; returns out [num_seqs][H_Q][d] float32.
-    With `phase` set, runs only that phase (screen, attend or merge)."""
+    With `phase` set, runs only that phase (screen, attend or merge).
+    bound: "geometric" or "dual" (needs cache.sigma; z deviations)."""
     dev = cache.k_pages.device
     _need(q, "q", cache.k_pages.dtype, dev)
     N, HQ, D = q.shape
@@ -161,10 +168,17 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
     args = (ctypes.byref(c), ctypes.byref(s), _ptr(q), HQ, int(tau_mode), _ptr(w), _ptr(b_or_c),
             float(a), float(beta), int(lwb), BLOCK, _ptr(out), _ptr(workspace), workspace.numel(),
             _stream(stream))
-    if phase is None:
-        _check(_lib.lib().eta_decode(*args), "eta_decode")
+    if bound == "geometric":
+        if phase is None:
+            _check(_lib.lib().eta_decode(*args), "eta_decode")
+        else:
+            _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
+    elif bound == "dual":
+        opts = _lib.EtaScreenOptsC(_lib.ETA_BOUND_DUAL, float(z))
+        ph = _lib.ETA_PHASE_ALL if phase is None else int(phase)
+        _check(_lib.lib().eta_decode_ex(ph, ctypes.byref(opts), *args), "eta_decode_ex")
     else:
-        _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
+        raise ValueError(f"unknown bound {bound!r}")
     return out
 
 

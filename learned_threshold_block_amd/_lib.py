@@ -22,9 +22,12 @@ ETA_F32 = 0
 ETA_BF16 = 1
 ETA_TAU_LEARNED = 0
 ETA_TAU_CALIBRATED = 1
+ETA_PHASE_ALL = -1
 ETA_PHASE_SCREEN = 0
 ETA_PHASE_ATTEND = 1
 ETA_PHASE_MERGE = 2
+ETA_BOUND_GEOMETRIC = 0
+ETA_BOUND_DUAL = 1
 
 EXPORTS = (
     "eta_build_block_summaries",
@@ -32,6 +35,7 @@ EXPORTS = (
     "eta_decode_workspace_size",
     "eta_decode",
     "eta_decode_phase",
+    "eta_decode_ex",
     "eta_stats",
     "eta_status_string",
 )
@@ -48,6 +52,14 @@ class EtaCacheC(ctypes.Structure):
         ("v_pages", ctypes.c_void_p),
         ("mu", ctypes.c_void_p),
         ("radius", ctypes.c_void_p),
+        ("sigma", ctypes.c_void_p),
+    ]
+
+
+class EtaScreenOptsC(ctypes.Structure):
+    _fields_ = [
+        ("bound", ctypes.c_int),
+        ("z", ctypes.c_float),
     ]
 
 
@@ -90,6 +102,8 @@ def lib() -> ctypes.CDLL:
     L.eta_decode.restype = I
     L.eta_decode_phase.argtypes = [I] + dec
     L.eta_decode_phase.restype = I
+    L.eta_decode_ex.argtypes = [I, ctypes.POINTER(EtaScreenOptsC)] + dec
+    L.eta_decode_ex.restype = I
     L.eta_stats.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
     L.eta_stats.restype = I
     L.eta_status_string.argtypes = [I]

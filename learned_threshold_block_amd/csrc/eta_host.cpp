@@ -65,7 +65,7 @@ eta_status check_cache(const eta_cache* c) {
     return ETA_ERR_INVALID_ARGUMENT;
   if (!c->k_pages || !c->v_pages || !c->mu || !c->radius) return ETA_ERR_INVALID_ARGUMENT;
   if (!aligned(c->k_pages, 16) || !aligned(c->v_pages, 16) || !aligned(c->mu, 16) ||
-      !aligned(c->radius, 4))
+      !aligned(c->radius, 4) || !aligned(c->sigma, 16))
     return ETA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
   if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
@@ -93,6 +93,7 @@ CacheView view_of(const eta_cache* c) {
   v.vw = c->v_pages;
   v.mu = c->mu;
   v.radius = c->radius;
+  v.sigma = c->sigma;
   return v;
 }
 
@@ -163,11 +164,21 @@ struct Prepared {
   Ws ws;
 };
 
-eta_status prepare(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
-                   int tau_mode, const float* w, const float* b_or_c, float a, float beta, int lwb,
-                   int block_size, float* out, void* workspace, size_t ws_bytes, Prepared* P) {
+eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs, const void* q,
+                   int num_q_heads, int tau_mode, const float* w, const float* b_or_c, float a, float beta,
+                   int lwb, int block_size, float* out, void* workspace, size_t ws_bytes, Prepared* P) {
   eta_status st = check_cache(cache);
   if (st != ETA_OK) return st;
+  P->p.dual = 0;
+  P->p.z = 0.f;
+  if (screen) {
+    if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL) return ETA_ERR_INVALID_ARGUMENT;
+    if (screen->bound == ETA_BOUND_DUAL) {
+      if (!cache->sigma || !isfinite(screen->z) || !(screen->z >= 0.f)) return ETA_ERR_INVALID_ARGUMENT;
+      P->p.dual = 1;
+      P->p.z = screen->z;
+    }
+  }
   st = check_seqs(seqs);
   if (st != ETA_OK) return st;
   if (block_size != cache->block_size) return ETA_ERR_INVALID_ARGUMENT;
@@ -281,31 +292,38 @@ size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_b
   return workspace_layout(d, nullptr, nullptr);
 }
 
+eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs,
+                         const void* q, int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
+                         float a, float beta, int lwb, int block_size, float* out, void* workspace,
+                         size_t ws_bytes, eta_stream_t stream) {
+  if (phase < ETA_PHASE_ALL || phase > ETA_PHASE_MERGE) return ETA_ERR_INVALID_ARGUMENT;
+  Prepared P;
+  eta_status st = prepare(screen, cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb, block_size,
+                          out, workspace, ws_bytes, &P);
+  if (st != ETA_OK) return st;
+  if (phase != ETA_PHASE_ALL) return run_phase(phase, P, (hipStream_t)stream);
+  for (int ph = ETA_PHASE_SCREEN; ph <= ETA_PHASE_MERGE; ++ph) {
+    st = run_phase(ph, P, (hipStream_t)stream);
+    if (st != ETA_OK) return st;
+  }
+  return ETA_OK;
+}
+
 eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* seqs, const void* q,
                             int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
                             float a, float beta, int lwb, int block_size, float* out,
                             void* workspace, size_t ws_bytes, eta_stream_t stream) {
   if (phase < ETA_PHASE_SCREEN || phase > ETA_PHASE_MERGE) return ETA_ERR_INVALID_ARGUMENT;
-  Prepared P;
-  eta_status st = prepare(cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb, block_size,
-                          out, workspace, ws_bytes, &P);
-  if (st != ETA_OK) return st;
-  return run_phase(phase, P, (hipStream_t)stream);
+  return eta_decode_ex(phase, nullptr, cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb,
+                       block_size, out, workspace, ws_bytes, stream);
 }
 
 eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
                       int tau_mode, const float* w, const float* b_or_c, float a, float beta, int lwb,
                       int block_size, float* out, void* workspace, size_t ws_bytes,
                       eta_stream_t stream) {
-  Prepared P;
-  eta_status st = prepare(cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb, block_size,
-                          out, workspace, ws_bytes, &P);
-  if (st != ETA_OK) return st;
-  for (int ph = ETA_PHASE_SCREEN; ph <= ETA_PHASE_MERGE; ++ph) {
-    st = run_phase(ph, P, (hipStream_t)stream);
-    if (st != ETA_OK) return st;
-  }
-  return ETA_OK;
+  return eta_decode_ex(ETA_PHASE_ALL, nullptr, cache, seqs, q, num_q_heads, tau_mode, w, b_or_c, a, beta, lwb,
+                       block_size, out, workspace, ws_bytes, stream);
 }
 
 eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,

@@ -73,6 +73,7 @@ struct CacheView {
   void* vw;
   uint16_t* mu;
   float* radius;
+  uint16_t* sigma;  // may be null
 };
 
 struct SeqView {
@@ -90,6 +91,8 @@ struct DecodeParams {
   int lwb;
   float* out;
   int deterministic;  // static work split and claims: bitwise-reproducible results
+  int dual;           // dual screen (geometric bound tightened by z deviations)
+  float z;
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };
 

@@ -8,6 +8,8 @@
 //             group, a block is loaded if any head admits it (Section 4.3, F.1)
 //   forced    partial last block and the lwb most recent complete blocks (4.8)
 //   rescue    block with the largest bound when a head admits nothing (3.2, F.4)
+//   dual      optionally the bound is tightened to min(bound, s (q.mu^ + z ||q sigma^||))
+//             with the per-block coordinate deviation sigma^ (Section 3.1, F.1)
 //   counts    per-head blocks, union blocks, attended tokens (F.4)
 //
 // k_screen: one wavefront per 64 consecutive blocks of one (sequence, KV head).
@@ -56,7 +58,7 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-template <typename T, int D, int G>
+template <typename T, int D, int G, bool DUAL>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
@@ -131,6 +133,19 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   }
   const uint32_t roff = complete ? (uint32_t)(((int64_t)page_l * HKV + g) * 4) : kOutOfRange;
   const float R = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rsrc, roff, 0, 0));
+  // dual screen: coordinate deviations, laid out like the centroids
+  uint4 sraw[DUAL ? NI : 1];
+  if constexpr (DUAL) {
+    const auto s_rsrc = make_rsrc(A.c.sigma, (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int j = j0 + RPI * i + r;
+      const bool ok = j < nfull && pg[i] >= 0 && pg[i] < A.c.num_pages;
+      const uint32_t off = ok ? (uint32_t)((((int64_t)pg[i] * HKV + g) * D + cb * 8) * 2) : kOutOfRange;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(s_rsrc, off, 0, 0);
+      sraw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
+  }
 
   // ---- thresholds and query norms (every row of lanes holds all D columns)
   float tau[G], qn[G];
@@ -153,8 +168,10 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     for (int h = 0; h < G; ++h) A.ws.tau[(int64_t)n * HQ + g * G + h] = tau[h];
   }
 
-  // ---- q . mu^: partial products per lane, transposing reduction over each row
+  // ---- q . mu^ (and, dual, sum of (q sigma^)^2): partial products per lane,
+  //      transposing reduction over each row
   float pd[G][NI];
+  float ps[DUAL ? G : 1][NI];
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
@@ -171,9 +188,32 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       for (int e = 0; e < 8; ++e) a = fmaf(qf[h][e], mv[e], a);
       pd[h][i] = a;
     }
+    if constexpr (DUAL) {
+      const uint32_t s4[4] = {sraw[i].x, sraw[i].y, sraw[i].z, sraw[i].w};
+      float sv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sv[2 * e] = f16_bits_to_f32((uint16_t)(s4[e] & 0xffffu));
+        sv[2 * e + 1] = f16_bits_to_f32((uint16_t)(s4[e] >> 16));
+      }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = qf[h][e] * sv[e];
+          a = fmaf(t, t, a);
+        }
+        ps[h][i] = a;
+      }
+    }
   }
 #pragma unroll
   for (int h = 0; h < G; ++h) transpose_reduce<LPR>(pd[h], lane);
+  if constexpr (DUAL) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) transpose_reduce<LPR>(ps[h], lane);
+  }
 
   const uint32_t full = (1u << G) - 1u;
   uint32_t mask = 0;
@@ -181,6 +221,10 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     ub[h] = A.p.scale * (pd[h][0] + qn[h] * R);
+    if constexpr (DUAL) {  // the smaller of the bound and the z-deviation estimate (a NaN side yields)
+      const float est = A.p.scale * (pd[h][0] + A.p.z * sqrtf(ps[h][0]));
+      ub[h] = fminf(ub[h], est);
+    }
     if (complete && !(ub[h] < tau[h])) mask |= 1u << h;
   }
   if (complete && jl >= nfull - A.p.lwb) mask = full;
@@ -514,7 +558,8 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
                        const Ws& ws, hipStream_t st) {
   ScreenArgs a{c, s, p, d, ws};
   dim3 grid((d.NT + 3) / 4, d.S);
-  hipLaunchKernelGGL((k_screen<T, D, G>), grid, dim3(256), 0, st, a);
+  if (p.dual) hipLaunchKernelGGL((k_screen<T, D, G, true>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_screen<T, D, G, false>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

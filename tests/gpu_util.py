@@ -24,13 +24,14 @@ def log(msg: str) -> None:
 class Dev:
     """A workload's inputs on the GPU."""
 
-    def __init__(self, wl: W.Workload, device="cuda"):
+    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False):
         self.wl = wl
         self.device = torch.device(device)
+        sig = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device) if with_sigma else None
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, device),
                                eta.upload(wl.v_pages, wl.kv_dtype, device),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device),
-                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device))
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device), sig)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(device)
         self.q = eta.upload(wl.q, wl.kv_dtype, device)
@@ -41,14 +42,14 @@ class Dev:
     def build(self):
         eta.build_block_summaries(self.cache, self.seq_lens, self.bt)
 
-    def decode(self, bias=None, tau_mode=None, a=None, beta=None, lwb=None):
+    def decode(self, bias=None, tau_mode=None, a=None, beta=None, lwb=None, bound="geometric", z=2.0):
         wl = self.wl
         b = torch.from_numpy(np.asarray(wl.bias if bias is None else bias, dtype=np.float32)).to(self.device)
         mode = wl.tau_mode if tau_mode is None else tau_mode
         m = eta.ETA_TAU_LEARNED if mode == "learned" else eta.ETA_TAU_CALIBRATED
         eta.decode(self.cache, self.seq_lens, self.bt, self.q, m, b, w=self.w,
                    a=wl.a if a is None else a, beta=wl.beta if beta is None else beta,
-                   lwb=wl.lwb if lwb is None else lwb, out=self.out, workspace=self.ws)
+                   lwb=wl.lwb if lwb is None else lwb, out=self.out, workspace=self.ws, bound=bound, z=z)
         torch.cuda.synchronize()
         return self.out.cpu().numpy().astype(np.float64)
 
@@ -62,13 +63,22 @@ class Dev:
     def radius(self):
         return self.cache.radius.cpu().numpy()
 
+    def sigma_bits(self):
+        return self.cache.sigma.cpu().view(torch.int16).numpy().view(np.uint16)
 
-def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=None, beta=None, lwb=None):
+
+def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=None, beta=None, lwb=None,
+                  bound="geometric", z=2.0):
+    """summaries: (mu, R) or, for the dual screen, (mu, R, sigma)."""
+    sig = None
+    if summaries is not None and len(summaries) == 3:
+        sig = summaries[2]
+        summaries = summaries[:2]
     return E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
                     wl.tau_mode if tau_mode is None else tau_mode, wl.w,
                     wl.bias if bias is None else bias, wl.a if a is None else a,
                     wl.beta if beta is None else beta, wl.lwb if lwb is None else lwb,
-                    summaries=summaries, heads=heads)
+                    summaries=summaries, heads=heads, bound=bound, z=z, sigmas=sig)
 
 
 def check_sets_and_counts(wl, res, st):
@@ -101,10 +111,11 @@ def check_output(wl, res, o_gpu, heads=None, tol=None):
     return err
 
 
-def prepared(name, **kw):
-    """Workload with thresholds placed and margins enforced (oracle side)."""
+def prepared(name, bound="geometric", z=2.0, **kw):
+    """Workload with thresholds placed and margins enforced (oracle side) for
+    the given screen."""
     wl = W.make_workload(name, **kw)
-    summ = placement.place(wl)
+    summ = placement.place(wl, bound=bound, z=z)
     return wl, summ
 
 

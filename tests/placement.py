@@ -19,8 +19,9 @@ import workloads as W
 BLOCK = 64
 
 
-def _bounds(wl, mu, R):
-    """ub[n][h][j] for complete blocks (NaN elsewhere), tau offsets per (n, h)."""
+def _bounds(wl, mu, R, sigma=None, z=2.0):
+    """ub[n][h][j] for complete blocks (NaN elsewhere), tau offsets per (n, h).
+    With sigma, the dual screen score instead of the geometric bound."""
     N, HQ, D = wl.q.shape
     G = wl.group
     s = 1.0 / math.sqrt(D)
@@ -31,7 +32,10 @@ def _bounds(wl, mu, R):
         pages = wl.block_table[n, :nfull]
         for h in range(HQ):
             g = h // G
-            ub[n, h, :nfull] = E.block_bound(qf[n, h], mu[pages, g], R[pages, g], s)
+            if sigma is None:
+                ub[n, h, :nfull] = E.block_bound(qf[n, h], mu[pages, g], R[pages, g], s)
+            else:
+                ub[n, h, :nfull] = E.dual_score(qf[n, h], mu[pages, g], R[pages, g], sigma[pages, g], s, z)
     if wl.tau_mode == "learned":
         off = np.einsum("nhd,hd->nh", qf, wl.w.astype(np.float64)) - wl.a
     else:
@@ -39,11 +43,16 @@ def _bounds(wl, mu, R):
     return ub, off
 
 
-def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None):
-    """Set wl.bias in place; returns the oracle summaries of the final cache."""
+def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound: str = "geometric",
+          z: float = 2.0):
+    """Set wl.bias in place; returns the oracle summaries of the final cache
+    ((mu, R), or (mu, R, sigma) for the dual screen)."""
     mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
-        if summaries is None else summaries
-    ub, off = _bounds(wl, mu, R)
+        if summaries is None else summaries[:2]
+    sigma = None
+    if bound == "dual":
+        sigma = E.build_sigmas(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens)
+    ub, off = _bounds(wl, mu, R, sigma, z)
     HQ = wl.h_q
     bias = np.zeros(HQ, dtype=np.float32)
     for h in range(HQ):
@@ -65,7 +74,7 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None):
         for n, h, j in zip(*np.nonzero(close)):
             bad.add((int(n), int(h) // G, int(j)))
         if not bad:
-            return mu, R
+            return (mu, R) if sigma is None else (mu, R, sigma)
         W.redraw_blocks(wl, bad)
         for (n, g, j) in bad:
             page = int(wl.block_table[n, j])
@@ -73,7 +82,9 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None):
             m, r = E.block_summary(kb)
             mu[page, g] = m
             R[page, g] = r
-        ub, off = _bounds(wl, mu, R)
+            if sigma is not None:
+                sigma[page, g] = E.block_sigma(kb)
+        ub, off = _bounds(wl, mu, R, sigma, z)
     raise RuntimeError("margin enforcement did not converge")
 
 

@@ -32,6 +32,35 @@ def test_library_exports_every_declared_symbol():
     assert set(declared_functions()) <= exported
 
 
+def test_struct_layouts_match_header(tmp_path):
+    """The ctypes mirrors of eta_cache, eta_seqs and eta_screen_opts have the
+    header's fields, offsets and sizes (a C program compiled against eta.h
+    prints them): a field added on one side only is caught here."""
+    structs = {"eta_cache": _lib.EtaCacheC, "eta_seqs": _lib.EtaSeqsC, "eta_screen_opts": _lib.EtaScreenOptsC}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "eta.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in cls._fields_:
+            lines.append(f'  printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for fname, _ in cls._fields_:
+            assert got[(cname, fname)] == getattr(cls, fname).offset, (cname, fname)
+    # and the header has no field the mirror lacks
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for cname, cls in structs.items():
+        body = re.search(r"typedef struct \{([^}]*)\}\s*" + cname + ";", text).group(1)
+        names = re.findall(r"(\w+)\s*;", body)
+        assert names == [f for f, _ in cls._fields_], (cname, names)
+
+
 def test_status_strings():
     L = _lib.lib()
     for code in (0, -1, -2, -3, -4, -5):
@@ -44,7 +73,7 @@ FAKE = 1 << 20  # aligned fake device addresses: validation never dereferences t
 
 def cache(**kw):
     c = dict(kv_dtype=_lib.ETA_BF16, head_dim=128, num_kv_heads=8, block_size=64, num_pages=16,
-             k_pages=FAKE, v_pages=FAKE * 2, mu=FAKE * 3, radius=FAKE * 4)
+             k_pages=FAKE, v_pages=FAKE * 2, mu=FAKE * 3, radius=FAKE * 4, sigma=None)
     c.update(kw)
     return _lib.EtaCacheC(**c)
 
@@ -121,3 +150,29 @@ def test_decode_rejects_cache_and_seqs():
     assert L.eta_decode_phase(9, ctypes.byref(c), ctypes.byref(s), FAKE, 32, 0, FAKE, FAKE, 0.0, 5.0, 0, 64,
                               FAKE, FAKE, 1 << 30, None) == _lib.ETA_ERR_INVALID_ARGUMENT
     assert L.eta_stats(None, 1, 1, 1, 1, None, None, None, None, None, None) == _lib.ETA_ERR_INVALID_ARGUMENT
+
+
+def decode_ex(phase, bound, z, c=None, nbytes=None):
+    c = c or cache()
+    s = seqs()
+    opts = _lib.EtaScreenOptsC(bound, z)
+    return _lib.lib().eta_decode_ex(phase, ctypes.byref(opts), ctypes.byref(c), ctypes.byref(s), FAKE * 7, 32,
+                                    _lib.ETA_TAU_LEARNED, FAKE * 8, FAKE * 9, 0.0, 5.0, 0, 64, FAKE * 10,
+                                    FAKE * 11, 1024 if nbytes is None else nbytes, None)
+
+
+def test_decode_ex_rejects_bad_screens():
+    """Validation of the screen choice runs before anything else reaches the
+    device (a too-small workspace is the first error a valid screen meets)."""
+    with_sigma = cache(sigma=FAKE * 12)
+    too_small = _lib.ETA_ERR_WORKSPACE_TOO_SMALL
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0) == _lib.ETA_ERR_INVALID_ARGUMENT  # no sigma
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, -1.0, c=with_sigma) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, float("nan"), c=with_sigma) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, 7, 2.0, c=with_sigma) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(5, _lib.ETA_BOUND_GEOMETRIC, 0.0) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0, c=cache(sigma=FAKE + 2)) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT  # misaligned sigma
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0, c=with_sigma) == too_small
+    assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small

@@ -28,18 +28,18 @@ def _sample_heads(wl, per_seq, seed):
     return heads
 
 
-def _run_full(name, per_seq, seed=7):
-    log(f"[full-size] {name}: generating and placing thresholds")
-    wl, summ = prepared(name)
+def _run_full(name, per_seq, seed=7, bound="geometric"):
+    log(f"[full-size] {name} ({bound} screen): generating and placing thresholds")
+    wl, summ = prepared(name, bound=bound)
     log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
         f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
     heads = _sample_heads(wl, per_seq, seed)
-    dev = Dev(wl)
+    dev = Dev(wl, with_sigma=bound == "dual")
     dev.build()
-    o = dev.decode()
+    o = dev.decode(bound=bound)
     st = dev.stats()
     log(f"[full-size] {name}: oracle on {len(heads)} heads")
-    res = oracle_decode(wl, summaries=summ, heads=heads)
+    res = oracle_decode(wl, summaries=summ, heads=heads, bound=bound)
     check_sets_and_counts(wl, res, st)
     check_output(wl, res, o, heads=heads)
     dens = st.admitted_per_head.sum() / (wl.h_q * sum(wl.nblk(n) for n in range(wl.n_seqs)))
@@ -66,3 +66,9 @@ def test_ragged_16_full():
     """Sixteen log-uniform lengths in [4K, 256K], pages in random order,
     per-head densities spread over [5%, 90%]: 3 heads per sequence."""
     _run_full("ragged_16", per_seq=3)
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_dual_full():
+    """The 512K workload under the dual screen (z = 2): 8 heads."""
+    _run_full("seq_512k", per_seq=8, bound="dual")
