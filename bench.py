@@ -53,6 +53,9 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
+    p.add_argument("--bound", default="geometric", choices=["geometric", "dual"],
+                   help="block screen: the geometric bound, or the dual screen (z deviations)")
+    p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB `steps` times (calibrates the "
                         "HBM byte counters) and exit")
@@ -109,7 +112,7 @@ def copy_probe(mib, steps):
 class Setup:
     """One workload resident on the GPU."""
 
-    def __init__(self, name, density=None):
+    def __init__(self, name, density=None, bound="geometric", z=2.0):
         import torch
 
         import learned_threshold_block_amd as eta
@@ -121,9 +124,11 @@ class Setup:
         log(f"{name}: generated {wl.kv_bytes() / 1e9:.2f} GB of K/V in {time.time() - t0:.1f}s")
         self.eta, self.torch = eta, torch
         dev = torch.device("cuda")
+        self.bound, self.z = bound, z
+        sig = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev) if bound == "dual" else None
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
-                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev))
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
         self.q = eta.upload(wl.q, wl.kv_dtype, dev)
@@ -139,7 +144,7 @@ class Setup:
     def run(self, phase=None, bias=None, mode=None):
         self.eta.decode(self.cache, self.seq_lens, self.bt, self.q, self.mode if mode is None else mode,
                         self.bias if bias is None else bias, w=self.w, a=self.wl.a, beta=self.wl.beta,
-                        lwb=self.wl.lwb, out=self.out, workspace=self.ws, phase=phase)
+                        lwb=self.wl.lwb, out=self.out, workspace=self.ws, phase=phase, bound=self.bound, z=self.z)
 
     def stats(self):
         wl = self.wl
@@ -180,7 +185,8 @@ class Setup:
         union = int(st.union_per_kv.sum())
         kv = union * 2 * 64 * wl.d * esz
         nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
-        meta = nfull * wl.h_kv * (2 * wl.d + 4) + int(self.nblk.sum()) * 4
+        rec = 2 * wl.d + 4 + (2 * wl.d if self.bound == "dual" else 0)  # centroid, radius (, deviation)
+        meta = nfull * wl.h_kv * rec + int(self.nblk.sum()) * 4
         small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
         return kv, kv + meta + small
 
@@ -269,7 +275,7 @@ def main():
         copy_probe(args.copy_probe, args.steps)
         return
 
-    S = Setup(args.workload, args.density)
+    S = Setup(args.workload, args.density, args.bound, args.z)
     S.calibrate()
     st, dens_head, dens_union = S.densities()
     kv_bytes, all_bytes = S.step_bytes(st)
@@ -284,7 +290,7 @@ def main():
     G, D = wl.group, wl.d
     attend_bytes = U * 2 * 64 * D * esz + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
-    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}"
+    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + ("" if args.bound == "geometric" else "-dual")
     traffic = stored_traffic(workload_key)
     result = {
         "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",
@@ -304,8 +310,10 @@ def main():
                          "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[args.workload]
                         + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
                         + f"{wl.tau_mode} thresholds, target per-head density "
-                        + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys",
+                        + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
+                        + ("" if args.bound == "geometric" else f", dual screen z={args.z:g}"),
             "kv_dtype": wl.kv_dtype,
+            "screen": args.bound if args.bound == "geometric" else f"dual z={args.z:g}",
             "seq_lens_total": int(wl.seq_lens.sum()),
             "density_per_head": round(dens_head, 4),
             "density_union": round(dens_union, 4),

@@ -30,59 +30,36 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
   return *p;
 }
 
-// This lane's CPL columns of one key row, kept in registers as stored
-// (bfloat16 pairs share one dword).
-template <typename T, int CPL>
-struct RowCols {
-  static constexpr bool kPacked = T::kBytes == 2 && CPL == 2;
-  uint32_t w[kPacked ? 1 : CPL];
-  __device__ __forceinline__ void load(const typename T::Stored* p) {
-    if constexpr (kPacked) {
-      w[0] = *(const uint32_t*)p;
-    } else {
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) w[c] = __float_as_uint(load_elem<T>(p + c));
-    }
-  }
-  __device__ __forceinline__ float get(int c) const {
-    if constexpr (kPacked) return c == 0 ? bf16_lo(w[0]) : bf16_hi(w[0]);
-    else return __uint_as_float(w[c]);
-  }
-};
-
 // One wavefront. tile: [64][D] keys of one (page, kv head). If override_row is
-// non-null, row 63 is read from it instead of the tile. Lane l holds columns
-// l*CPL .. l*CPL+CPL-1 of every row in registers, so the tile is read once.
-// Writes the centroid and radius, and the coordinate deviation if sig_out is
-// not null.
+// non-null, row 63 is read from it instead of the tile. Lanes own columns;
+// the rows are read twice (sums, then distances and deviations), which keeps
+// the register footprint small enough for eight wavefronts per SIMD. Writes
+// the centroid and radius, and the coordinate deviation if sig_out is not null.
 template <typename T, int D>
 __device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
                              uint16_t* mu_out, float* r_out, uint16_t* sig_out, int lane) {
   constexpr int CPL = D / 64;  // columns per lane: 2 (D=128) or 1 (D=64)
-  RowCols<T, CPL> x[kBlock];
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r) {
-    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
-    x[r].load(row + lane * CPL);
-  }
   double sum[CPL];
   bool finite = true;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) sum[c] = 0.0;
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r)
+  for (int r = 0; r < kBlock; ++r) {
+    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const float v = x[r].get(c);
-      finite = finite && (fabsf(v) <= 3.4028234663852886e38f);
-      sum[c] += (double)v;
+      const float x = load_elem<T>(row + lane * CPL + c);
+      finite = finite && (fabsf(x) <= 3.4028234663852886e38f);
+      sum[c] += (double)x;
     }
+  }
   uint16_t h[CPL];
-  double mu[CPL];
+  double mu[CPL], mean[CPL], dev2[CPL];
   bool ok = finite;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    h[c] = f64_to_f16_rne(sum[c] * (1.0 / kBlock));
+    mean[c] = sum[c] * (1.0 / kBlock);
+    dev2[c] = 0.0;
+    h[c] = f64_to_f16_rne(mean[c]);
     ok = ok && ((h[c] & 0x7c00u) != 0x7c00u);
   }
   const bool all_ok = __all(ok);
@@ -92,43 +69,28 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     mu[c] = (double)f16_bits_to_f32(h[c]);
     mu_out[lane * CPL + c] = h[c];
   }
-  // each later pass converts the stored words again instead of keeping 64 x CPL
-  // doubles alive (an empty asm hides that the words are unchanged)
-#pragma unroll
-  for (int r = 0; r < kBlock; ++r)
-#pragma unroll
-    for (int i = 0; i < (int)(sizeof(x[r].w) / 4); ++i) asm volatile("" : "+v"(x[r].w[i]));
-  // coordinate deviation about the float64 mean (population), float16
-  if (sig_out) {
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-      const double m = sum[c] * (1.0 / kBlock);
-      double acc = 0.0;
-#pragma unroll
-      for (int r = 0; r < kBlock; ++r) {
-        const double dd = (double)x[r].get(c) - m;
-        acc += dd * dd;
-      }
-      const double sd = sqrt(acc * (1.0 / kBlock));
-      sig_out[lane * CPL + c] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
-    }
-#pragma unroll
-    for (int r = 0; r < kBlock; ++r)
-#pragma unroll
-      for (int i = 0; i < (int)(sizeof(x[r].w) / 4); ++i) asm volatile("" : "+v"(x[r].w[i]));
-  }
-  // largest squared distance of a row to the stored centroid
   double rmax = 0.0;
-#pragma unroll 8
   for (int r = 0; r < kBlock; ++r) {
+    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
     double part = 0.0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const double dlt = (double)x[r].get(c) - mu[c];
+      const double x = (double)load_elem<T>(row + lane * CPL + c);
+      const double dlt = x - mu[c];
       part += dlt * dlt;
+      const double dm = x - mean[c];  // deviation about the float64 mean
+      dev2[c] += dm * dm;
     }
     const double tot = wave_sum_f64(part);
     rmax = (tot > rmax || tot != tot) ? tot : rmax;  // NaN propagates
+  }
+  // coordinate deviation (population) as float16
+  if (sig_out) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const double sd = sqrt(dev2[c] * (1.0 / kBlock));
+      sig_out[lane * CPL + c] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
+    }
   }
   const bool any_bad = __any(!finite);
   if (lane == 0) {
