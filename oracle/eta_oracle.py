@@ -51,8 +51,12 @@ reading is not sound (it can miss a block whose best key lies more than z
 deviations out), so its sets are pinned against a per-key brute force and
 measured for recall, not checked for soundness.
 
-Parity unpinned: the pages' exact Eq. 7 and their chunk-local rescue rule are
-not reproducible from the text and are not implemented here.
+Offline calibration (Section 4.7, D.2, Algorithm 1): calibration_histogram,
+calibrated_bin and calibrate below; the reading taken is stated there.
+
+Parity unpinned: the pages' exact Eq. 7, the body of Algorithm 1 and their
+chunk-local rescue rule are not reproducible from the text; the first two are
+implemented as readings, the last is not implemented.
 """
 from __future__ import annotations
 
@@ -370,3 +374,102 @@ def _attend(qh, k_pages, v_pages, kv_dtype, pages, g, blocks, T, tau, beta, scal
         num += wts @ vb[keep]
         den += wts.sum()
     return num / den
+
+
+# --------------------------------------------------------------------------- offline calibration
+# Section 4.7 and Appendix D.2 (Algorithm 1, whose body did not survive): the
+# learned predictor of a head is replaced by a frozen constant c_h found from a
+# 1/t-weighted histogram of attention scores over calibration sequences and a
+# binary search for the head's training density. Reading taken here:
+#   * every position t (0-based) of a calibration sequence is a query row over
+#     the keys s <= t (causal), with scaled scores S = s_scale q_t . k_s;
+#   * each key of row t carries the integer weight floor(2^31 / (t + 1)), so
+#     every row weighs about the same whatever its length (the 1/t weighting);
+#   * the histogram has num_bins equal bins over [lo, hi); scores outside fall
+#     in the end bins;
+#   * the target is the head's training density: the weighted count of scores
+#     at or above the learned threshold w_h . q_t + b_h (or a given fraction
+#     rho_h of the total weight);
+#   * the binary search returns the lowest bin edge whose weighted tail (the
+#     weight of the bins at or above it) does not exceed the target; c_h is
+#     that edge.
+CALIB_WEIGHT_ONE = 1 << 31
+
+
+def row_weight(t: int) -> int:
+    """Integer weight of every key of query row t (0-based, t + 1 keys)."""
+    return CALIB_WEIGHT_ONE // (t + 1)
+
+
+def score_bins(S: np.ndarray, lo: float, hi: float, num_bins: int) -> np.ndarray:
+    """Bin index of each score: floor((S - lo) num_bins / (hi - lo)), clamped to the end bins."""
+    x = np.floor((np.asarray(S, dtype=np.float64) - lo) * (num_bins / (hi - lo)))
+    return np.clip(x, 0, num_bins - 1).astype(np.int64)
+
+
+def calibration_histogram(k_pages, kv_dtype: str, block_table, seq_lens, q_all, h: int, G: int,
+                          lo: float, hi: float, num_bins: int, w_h=None, b_h=None, chunk: int = 256):
+    """Weighted histogram of one query head's scores over the calibration
+    sequences. q_all: [N][positions][H_Q][d] stored values (a query at every
+    position). Returns (hist int64 [num_bins], above, total): above is the
+    weighted count of scores at or above the learned threshold w_h . q_t + b_h
+    (None without a predictor), total the weight of all scores."""
+    D = q_all.shape[-1]
+    scale = 1.0 / math.sqrt(D)
+    g = h // G
+    hist = np.zeros(num_bins, dtype=np.int64)
+    above = 0 if w_h is not None else None
+    total = 0
+    for n in range(len(seq_lens)):
+        T = int(seq_lens[n])
+        nb = -(-T // BLOCK)
+        pages = np.asarray(block_table[n, :nb], dtype=np.int64)
+        K = upcast(k_pages[pages, g], kv_dtype).reshape(nb * BLOCK, D)[:T]
+        Q = upcast(q_all[n, :T, h], kv_dtype)
+        for t0 in range(0, T, chunk):
+            t1 = min(T, t0 + chunk)
+            S = scale * (Q[t0:t1] @ K[:t1].T)               # rows t0..t1-1, keys 0..t1-1
+            bins = score_bins(S, lo, hi, num_bins)
+            if w_h is not None:
+                tau = Q[t0:t1] @ np.asarray(w_h, dtype=np.float64) + float(b_h)
+            for i in range(t1 - t0):
+                t = t0 + i
+                wt = row_weight(t)
+                hist += wt * np.bincount(bins[i, :t + 1], minlength=num_bins)
+                total += wt * (t + 1)
+                if w_h is not None:
+                    above += wt * int(np.count_nonzero(S[i, :t + 1] >= tau[i]))
+    return hist, above, total
+
+
+def calibrated_bin(hist: np.ndarray, target: int) -> int:
+    """Binary search for the lowest bin edge b (0..num_bins) whose weighted tail
+    sum(hist[b:]) does not exceed target."""
+    tail = np.concatenate([np.cumsum(hist[::-1])[::-1], [0]])  # tail[b] = sum(hist[b:])
+    lo_b, hi_b = 0, len(hist)
+    while lo_b < hi_b:
+        mid = (lo_b + hi_b) // 2
+        if tail[mid] <= target:
+            hi_b = mid
+        else:
+            lo_b = mid + 1
+    return lo_b
+
+
+def calibrate(k_pages, kv_dtype: str, block_table, seq_lens, q_all, num_kv_heads: int, lo: float, hi: float,
+              num_bins: int, w=None, b=None, rho=None, heads: Optional[Iterable] = None):
+    """Calibrated constants c_h for the given query heads (default: all).
+    Target from the learned predictor (w, b) or from densities rho [H_Q]
+    (target = floor(rho_h * total)). Returns {h: dict(hist, above, total, target, bin, c)}."""
+    HQ = q_all.shape[2]
+    G = HQ // num_kv_heads
+    out = {}
+    for h in (range(HQ) if heads is None else heads):
+        hist, above, total = calibration_histogram(k_pages, kv_dtype, block_table, seq_lens, q_all, h, G, lo, hi,
+                                                   num_bins, None if w is None else w[h],
+                                                   None if b is None else b[h])
+        target = above if rho is None else int(math.floor(float(rho[h]) * total))
+        bstar = calibrated_bin(hist, target)
+        out[h] = dict(hist=hist, above=above, total=total, target=target, bin=bstar,
+                      c=lo + bstar * (hi - lo) / num_bins)
+    return out

@@ -225,6 +225,85 @@ def pin_dual_bruteforce(E, seeds=range(3)):
         for (n, g), u in bf_union.items():
             assert int(res.union[n, g]) == u
 
+
+# --------------------------------------------------------------------------- offline calibration
+def _grid_trace(E, T=8, d=4):
+    """One sequence whose scaled scores are S_ts = s exactly: q_t = (sqrt(d), 0, ...)
+    and k_s = (s, 0, ...), float32 storage."""
+    wl = tiny(5, n=1, lens=(T,), h_q=1, h_kv=1, d=d, dtype="f32", mode="calibrated")
+    page = wl.block_table[0, 0]
+    wl.k_pages[page, 0] = 0.0
+    wl.k_pages[page, 0, :T, 0] = np.arange(T, dtype=np.float32)
+    q = np.zeros((1, 64, 1, d), dtype=np.float32)
+    q[0, :T, 0, 0] = math.sqrt(d)
+    return wl, q
+
+
+def pin_calibration_grid(E):
+    """Scores 0..t in row t, bins of width 1 over [0, T): bin b holds the weight
+    of every row t >= b; the tails and the binary search follow by hand."""
+    T = 8
+    wl, q = _grid_trace(E, T)
+    hist, above, total = E.calibration_histogram(wl.k_pages, "f32", wl.block_table, wl.seq_lens, q, 0, 1,
+                                                 0.0, float(T), T, w_h=np.zeros(4), b_h=3.5)
+    W = [(1 << 31) // (t + 1) for t in range(T)]
+    want = [sum(W[t] for t in range(b, T)) for b in range(T)]
+    assert hist.tolist() == want
+    assert total == sum(W[t] * (t + 1) for t in range(T))
+    # threshold 3.5: row t has max(0, t - 3) scores at or above it; so has 4.0
+    # (a score equal to the threshold counts)
+    assert above == sum(W[t] * max(0, t - 3) for t in range(T))
+    _, above4, _ = E.calibration_histogram(wl.k_pages, "f32", wl.block_table, wl.seq_lens, q, 0, 1,
+                                           0.0, float(T), T, w_h=np.zeros(4), b_h=4.0)
+    assert above4 == above
+    tails = [sum(want[b:]) for b in range(T + 1)]
+    for target in (0, tails[5], tails[5] + 1, tails[1] - 1, tails[0]):
+        b = E.calibrated_bin(hist, target)
+        assert tails[b] <= target and (b == 0 or tails[b - 1] > target), (target, b)
+    # the constant threshold 3.5 is recovered as the next bin edge, 4
+    res = E.calibrate(wl.k_pages, "f32", wl.block_table, wl.seq_lens, q, 1, 0.0, float(T), T,
+                      w=np.zeros((1, 4)), b=np.array([3.5]))
+    assert res[0]["c"] == 4.0
+
+
+def pin_calibration_row_weighting(E):
+    """Every row weighs about 2^31 whatever its length: two sequences whose rows
+    each have exactly half of their scores at or above 0 give a density of 1/2
+    at c = 0, though the long sequence has far more scores."""
+    d = 4
+    wl = tiny(6, n=2, lens=(4, 64), h_q=1, h_kv=1, d=d, dtype="f32", mode="calibrated")
+    q = np.zeros((2, 64, 1, d), dtype=np.float32)
+    for n, T in enumerate((4, 64)):
+        page = wl.block_table[n, 0]
+        wl.k_pages[page, 0] = 0.0
+        wl.k_pages[page, 0, :T, 0] = np.where(np.arange(T) % 2 == 0, 1.0, -1.0)
+        q[n, :T, 0, 0] = math.sqrt(d)
+    hist, _, total = E.calibration_histogram(wl.k_pages, "f32", wl.block_table, wl.seq_lens, q, 0, 1,
+                                             -2.0, 2.0, 4)
+    W = lambda t: (1 << 31) // (t + 1)  # noqa: E731
+    pos = sum(W(t) * (t // 2 + 1) for T in (4, 64) for t in range(T))
+    assert int(hist[2:].sum()) == pos and int(hist[:2].sum()) == total - pos
+    frac = pos / total
+    rows = sum((t // 2 + 1) / (t + 1) for T in (4, 64) for t in range(T)) / 68
+    assert abs(frac - rows) < 1e-6  # the row average, not the key count average
+
+
+def pin_calibration_target_property(E, seed=11):
+    """On a random trace the returned edge satisfies the search's definition,
+    and a larger density target gives a constant no larger."""
+    wl = tiny(seed, n=2, lens=(300, 170), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned")
+    q = W.trace_queries(wl, seed=3)
+    prev = None
+    for rho in (0.05, 0.2, 0.5, 0.9):
+        res = E.calibrate(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q, wl.h_kv, -8.0, 8.0, 256,
+                          rho=np.full(wl.h_q, rho))
+        for h, r in res.items():
+            tail = np.concatenate([np.cumsum(r["hist"][::-1])[::-1], [0]])
+            assert tail[r["bin"]] <= r["target"] and (r["bin"] == 0 or tail[r["bin"] - 1] > r["target"])
+            if prev is not None:
+                assert r["c"] <= prev[h]
+        prev = {h: r["c"] for h, r in res.items()}
+
 # --------------------------------------------------------------------------- thresholds
 def pin_threshold_closed_form(E):
     """tau~ = w.q + b - a (learned), c - a (calibrated): Sections 1, 4.7, D.1, G.1."""
@@ -451,4 +530,5 @@ ALL_PINS = [
     pin_dense_sdpa, pin_suppressed_mean, pin_equal_logits, pin_two_keys_closed_form,
     pin_tail_masking, pin_page_permutation, pin_nonfinite_keys, pin_threshold_tie_admitted,
     pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
+    pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
 ]

@@ -45,6 +45,11 @@ MUTANTS = {
     "dual_drops_z": ("prob = scale * (mu @ q + z * spread)", "prob = scale * (mu @ q + spread)"),
     "dual_spread_unsquared": ("spread = np.sqrt(((sigma * q[None, :]) ** 2).sum(axis=1))",
                               "spread = (sigma * np.abs(q[None, :])).sum(axis=1)"),
+    "calibration_unweighted_rows": ("    return CALIB_WEIGHT_ONE // (t + 1)\n", "    return CALIB_WEIGHT_ONE\n"),
+    "calibration_drops_diagonal": ("hist += wt * np.bincount(bins[i, :t + 1], minlength=num_bins)",
+                                   "hist += wt * np.bincount(bins[i, :t], minlength=num_bins)"),
+    "calibration_search_strict": ("        if tail[mid] <= target:\n", "        if tail[mid] < target:\n"),
+    "calibration_threshold_strict": ("np.count_nonzero(S[i, :t + 1] >= tau[i])", "np.count_nonzero(S[i, :t + 1] > tau[i])"),
 }
 
 

@@ -328,3 +328,16 @@ def permute_pages(wl: Workload, seed: int) -> Workload:
     bt[used] = perm[bt[used]]
     return dataclasses.replace(wl, k_pages=k_new, v_pages=v_new, block_table=bt,
                                needles=list(wl.needles))
+
+
+def trace_queries(wl: Workload, seed: int = 77) -> np.ndarray:
+    """A query for every position of every sequence (calibration traces):
+    [N][64 * max_blocks][H_Q][d] in the workload's storage type, N(0, 1)
+    entries; positions past a sequence's length hold zeros."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(1)[0])
+    L = BLOCK * wl.max_blocks
+    q = np.zeros((wl.n_seqs, L, wl.h_q, wl.d), dtype=np.float32)
+    for n in range(wl.n_seqs):
+        T = int(wl.seq_lens[n])
+        q[n, :T] = rng.standard_normal((T, wl.h_q, wl.d)).astype(np.float32)
+    return to_storage(q, wl.kv_dtype)
