@@ -202,6 +202,43 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
                      int64_t* tokens_per_head, uint8_t* rescued, uint32_t* admitted_bitmap,
                      eta_stream_t stream);
 
+/* Offline calibration of per-head constants c_h for the calibrated mode
+ * (Section 4.7 and Appendix D.2, Algorithm 1, whose body did not survive; the
+ * reading taken): over the sequences of `seqs` (keys from `cache`), every
+ * position t (0-based) is a query row over the keys s <= t with scaled scores
+ * S = q_t . k_s / sqrt(d); each key of row t weighs floor(2^31 / (t + 1)) (the
+ * 1/t row weighting, in integers). Scores fall in opts->num_bins equal bins
+ * over [opts->lo, opts->hi) (outside: the end bins; NaN: bin 0). The target is
+ * the weighted count of scores at or above the learned threshold
+ * w_h . q_t + b_h (the head's training density; w, b given, rho NULL) or
+ * floor(rho_h * total) (rho given, w and b NULL). c_h is the lowest bin edge
+ * whose weighted tail (the weight of the bins at or above it) does not exceed
+ * the target.
+ *   q        [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] kv_dtype,
+ *            a query for every position (positions >= seq_len unused), 16-byte aligned.
+ *   w, b     [num_q_heads][head_dim], [num_q_heads] float32 (device), or NULL.
+ *   rho      [num_q_heads] float32 (device) densities in [0, 1], or NULL.
+ *   hist     [num_q_heads][num_bins] uint64 out: weighted bin counts.
+ *   above    [num_q_heads] uint64 out: weighted count at or above the learned
+ *            threshold (zero without a predictor).
+ *   total    [num_q_heads] uint64 out: weight of all scores.
+ *   c_out    [num_q_heads] float32 out: the constants.
+ *   err_flag [1] int32 device out: 1 if an out-of-range page id was met.
+ * All outputs are device buffers the library overwrites (8-byte aligned for the
+ * uint64 ones). Requires 2 <= num_bins and G * num_bins <= 8192 (the
+ * per-workgroup histogram lives in 64 KB of LDS), lo < hi, both finite.
+ * Asynchronous on `stream`. */
+typedef struct {
+  int num_bins;
+  float lo;
+  float hi;
+} eta_calib_opts;
+
+eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                         const float* w, const float* b, const float* rho, const eta_calib_opts* opts,
+                         uint64_t* hist, uint64_t* above, uint64_t* total, float* c_out, int32_t* err_flag,
+                         eta_stream_t stream);
+
 /* Static text for a status code. */
 const char* eta_status_string(eta_status status);
 

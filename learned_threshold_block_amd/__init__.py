@@ -183,6 +183,41 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
 
 
 @dataclasses.dataclass
+class Calibration:
+    hist: torch.Tensor    # int64 view of uint64 [H_Q][num_bins]
+    above: torch.Tensor   # [H_Q]
+    total: torch.Tensor   # [H_Q]
+    c: torch.Tensor       # float32 [H_Q] calibrated constants
+    err: torch.Tensor     # int32 [1]
+
+
+def calibrate(cache: Cache, seq_lens, block_table, q_all, num_bins: int, lo: float, hi: float, w=None, b=None,
+              rho=None, stream=None) -> Calibration:
+    """Offline calibration of per-head constants (eta_calibrate): q_all is
+    [N][64*max_blocks][H_Q][d] (a query at every position); the target is the
+    training density of the learned predictor (w, b) or the densities rho."""
+    dev = cache.k_pages.device
+    _need(q_all, "q_all", cache.k_pages.dtype, dev)
+    N, L, HQ, D = q_all.shape
+    if L != BLOCK * block_table.shape[1] or N != block_table.shape[0] or D != cache.head_dim:
+        raise ValueError("q_all must be [num_seqs][64 * max_blocks_per_seq][H_Q][d]")
+    for t, name in ((w, "w"), (b, "b"), (rho, "rho")):
+        if t is not None:
+            _need(t, name, torch.float32, dev)
+    hist = torch.empty(HQ, num_bins, dtype=torch.int64, device=dev)
+    above = torch.empty(HQ, dtype=torch.int64, device=dev)
+    total = torch.empty(HQ, dtype=torch.int64, device=dev)
+    c = torch.empty(HQ, dtype=torch.float32, device=dev)
+    err = torch.empty(1, dtype=torch.int32, device=dev)
+    cs, ss = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    opts = _lib.EtaCalibOptsC(int(num_bins), float(lo), float(hi))
+    _check(_lib.lib().eta_calibrate(ctypes.byref(cs), ctypes.byref(ss), _ptr(q_all), HQ, _ptr(w), _ptr(b), _ptr(rho),
+                                    ctypes.byref(opts), _ptr(hist), _ptr(above), _ptr(total), _ptr(c), _ptr(err),
+                                    _stream(stream)), "eta_calibrate")
+    return Calibration(hist, above, total, c, err)
+
+
+@dataclasses.dataclass
 class Stats:
     admitted_per_head: np.ndarray   # int32 [N][H_Q]
     union_per_kv: np.ndarray        # int32 [N][H_KV]

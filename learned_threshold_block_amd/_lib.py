@@ -36,6 +36,7 @@ EXPORTS = (
     "eta_decode",
     "eta_decode_phase",
     "eta_decode_ex",
+    "eta_calibrate",
     "eta_stats",
     "eta_status_string",
 )
@@ -60,6 +61,14 @@ class EtaScreenOptsC(ctypes.Structure):
     _fields_ = [
         ("bound", ctypes.c_int),
         ("z", ctypes.c_float),
+    ]
+
+
+class EtaCalibOptsC(ctypes.Structure):
+    _fields_ = [
+        ("num_bins", ctypes.c_int),
+        ("lo", ctypes.c_float),
+        ("hi", ctypes.c_float),
     ]
 
 
@@ -104,6 +113,8 @@ def lib() -> ctypes.CDLL:
     L.eta_decode_phase.restype = I
     L.eta_decode_ex.argtypes = [I, ctypes.POINTER(EtaScreenOptsC)] + dec
     L.eta_decode_ex.restype = I
+    L.eta_calibrate.argtypes = [cp, sp, P, I, P, P, P, ctypes.POINTER(EtaCalibOptsC), P, P, P, P, P, P]
+    L.eta_calibrate.restype = I
     L.eta_stats.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
     L.eta_stats.restype = I
     L.eta_status_string.argtypes = [I]

@@ -1,0 +1,275 @@
+// Offline calibration of per-head constant thresholds: 1/t-weighted score
+// histograms over calibration sequences and a search for each head's training
+// density.
+//
+// "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Section 4.7
+// and Appendix D.2 (Algorithm 1; its body did not survive, the reading is):
+//   * every position t (0-based) of a sequence is a query row over the keys
+//     s <= t, scaled scores S = q_t . k_s / sqrt(d);
+//   * each key of row t weighs floor(2^31 / (t + 1)) (integer, so every row
+//     weighs about the same and the sums are exact and order-free);
+//   * equal-width bins over [lo, hi), outside scores in the end bins;
+//   * target: the weighted count of scores at or above the learned threshold
+//     w_h . q_t + b_h (the head's training density), or floor(rho_h * total);
+//   * c_h = the lowest bin edge whose weighted tail does not exceed the target.
+//
+// k_calib_hist: one workgroup per (sequence, KV head, tile of 64 query
+//   positions); the four wavefronts take 16 queries each and walk the key tiles
+//   up to the diagonal. Scores come from the same tile layout and transposing
+//   DPP reduction as the decode; each lane bins the score of one key into a
+//   per-workgroup LDS histogram with 64-bit integer atomics, which is added to
+//   the global one at the end (non-empty bins only).
+// k_calib_search: one wavefront per query head: suffix sums of the histogram
+//   and the count of edges whose tail exceeds the target.
+#include "eta_device.h"
+
+namespace eta {
+namespace {
+
+struct CalibArgs {
+  CacheView c;
+  SeqView s;
+  const void* q;       // [N][Lq][HQ][D]
+  int Lq, HQ, B;
+  const float* w;      // [HQ][D] or null
+  const float* b;      // [HQ] or null
+  const float* rho;    // [HQ] or null
+  float lo, hi, bscale;  // bscale = B / (hi - lo)
+  unsigned long long* hist;   // [HQ][B]
+  unsigned long long* above;  // [HQ]
+  unsigned long long* total;  // [HQ]
+  float* c_out;               // [HQ]
+  int* err;                   // [1] set on an out-of-range page id
+};
+
+__global__ void k_calib_zero(CalibArgs A) {
+  const int64_t n = (int64_t)A.HQ * A.B;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    A.hist[i] = 0ull;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < A.HQ) {
+    A.above[i] = 0ull;
+    A.total[i] = 0ull;
+  }
+  if (i == 0) A.err[0] = 0;
+}
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
+  using L = TileLayout<T::kBytes, D>;
+  constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL;
+  constexpr bool kBf16 = T::kBytes == 2;
+  using St = typename T::Stored;
+  extern __shared__ unsigned long long lhist[];  // [G][B]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int r = lane / LPR, cb = lane % LPR;
+  const int HKV = A.c.HKV, MB = A.s.MB, B = A.B;
+  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
+  const int qt = blockIdx.x;
+  const int len = A.s.lens[n];
+  if (len < 1 || len > kBlock * MB || qt * kBlock >= len) return;
+  for (int i = threadIdx.x; i < G * B; i += 256) lhist[i] = 0ull;
+  __syncthreads();
+
+  const float scale = 1.0f / sqrtf((float)D);
+  const bool learned = A.w != nullptr;
+  unsigned long long abv[G], tot[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) abv[h] = tot[h] = 0ull;
+  int loff[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
+  const St* kbase = (const St*)A.c.k;
+  const int tok = RPI * cb + r;  // key (within the tile) whose score this lane finishes
+
+  for (int j = 0; j <= qt; ++j) {
+    const int page = A.s.bt[(int64_t)n * MB + j];
+    if (page < 0 || page >= A.c.num_pages) {
+      if (threadIdx.x == 0) A.err[0] = 1;
+      continue;
+    }
+    uint4 kr[NI][CPL];
+    const St* kt = kbase + ((int64_t)page * HKV + g) * (kBlock * D);
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
+    const int s_key = j * kBlock + tok;
+    for (int i = 0; i < 16; ++i) {
+      const int t = qt * kBlock + wave * 16 + i;
+      if (t >= len) break;
+      const unsigned long long wt = (unsigned long long)((1u << 31) / (unsigned)(t + 1));
+      const bool valid = s_key <= t;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const St* qrow = (const St*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G + h) * D;
+        uint32_t qw[CPL * 4];
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+          qw[c * 4 + 0] = v.x; qw[c * 4 + 1] = v.y; qw[c * 4 + 2] = v.z; qw[c * 4 + 3] = v.w;
+        }
+        float pd[NI];
+#pragma unroll
+        for (int ii = 0; ii < NI; ++ii) {
+          float a = 0.f;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const uint32_t kw[4] = {kr[ii][c].x, kr[ii][c].y, kr[ii][c].z, kr[ii][c].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (kBf16) {
+                a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qw[c * 4 + e]),
+                                                    __builtin_bit_cast(bf16x2_t, kw[e]), a, false);
+              } else {
+                a = fmaf(__uint_as_float(qw[c * 4 + e]), __uint_as_float(kw[e]), a);
+              }
+            }
+          }
+          pd[ii] = a;
+        }
+        transpose_reduce<LPR>(pd, lane);
+        const float S = pd[0] * scale;
+        if (valid) {
+          const float x = floorf((S - A.lo) * A.bscale);
+          const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
+          atomicAdd(&lhist[h * B + bin], wt);
+        }
+        if (learned) {  // this row's learned threshold w_h . q_t + b_h
+          float pw = 0.f;
+          const float* wr = A.w + (int64_t)(g * G + h) * D;
+#pragma unroll
+          for (int c = 0; c < CPL; ++c) {
+            const float4 w0 = *(const float4*)(wr + L::col(c, cb));
+            const float4 w1 = EPL / CPL > 4 ? *(const float4*)(wr + L::col(c, cb) + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+            float qv[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if constexpr (kBf16) {
+                qv[2 * e] = bf16_lo(qw[c * 4 + e]);
+                qv[2 * e + 1] = bf16_hi(qw[c * 4 + e]);
+              } else {
+                qv[e] = __uint_as_float(qw[c * 4 + e]);
+                qv[4 + e] = 0.f;
+              }
+            }
+            pw = fmaf(w0.x, qv[0], pw); pw = fmaf(w0.y, qv[1], pw);
+            pw = fmaf(w0.z, qv[2], pw); pw = fmaf(w0.w, qv[3], pw);
+            if constexpr (kBf16) {
+              pw = fmaf(w1.x, qv[4], pw); pw = fmaf(w1.y, qv[5], pw);
+              pw = fmaf(w1.z, qv[6], pw); pw = fmaf(w1.w, qv[7], pw);
+            }
+          }
+          const float tau = group_sum<LPR>(pw) + A.b[g * G + h];
+          if (valid && S >= tau) abv[h] += wt;
+        }
+        if (j == qt && lane == 0) tot[h] += wt * (unsigned long long)(t + 1);
+      }
+    }
+  }
+  // per-head sums of the wavefront, then the workgroup's bins into the totals
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    unsigned long long a = abv[h];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+    if (lane == 0) {
+      if (learned && a) atomicAdd(&A.above[g * G + h], a);
+      if (tot[h]) atomicAdd(&A.total[g * G + h], tot[h]);
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * B; i += 256) {
+    const unsigned long long v = lhist[i];
+    if (v) atomicAdd(&A.hist[(int64_t)(g * G) * B + i], v);
+  }
+}
+
+// One wavefront per query head: tail(b) = sum of bins >= b is non-increasing,
+// so the lowest edge with tail(b) <= target is the number of edges b < B whose
+// tail exceeds it.
+__global__ __launch_bounds__(64) void k_calib_search(CalibArgs A) {
+  const int h = blockIdx.x, lane = threadIdx.x, B = A.B;
+  const unsigned long long* hb = A.hist + (int64_t)h * B;
+  unsigned long long target;
+  if (A.rho) {
+    target = (unsigned long long)floor((double)A.rho[h] * (double)A.total[h]);
+  } else {
+    target = A.above[h];
+  }
+  // lane l owns bins [l*per, (l+1)*per)
+  const int per = (B + 63) / 64;
+  const int b0 = lane * per, b1 = min(B, b0 + per);
+  unsigned long long own = 0ull;
+  for (int b = b0; b < b1; ++b) own += hb[b];
+  // sum of the bins owned by higher lanes (inclusive suffix, minus own)
+  unsigned long long suf = own;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const unsigned long long y = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += y;
+  }
+  unsigned long long tail = suf;  // tail(b0)
+  int cnt = 0;
+  for (int b = b0; b < b1; ++b) {
+    if (tail > target) ++cnt;
+    tail -= hb[b];
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) A.c_out[h] = (float)((double)A.lo + (double)cnt * ((double)A.hi - (double)A.lo) / (double)B);
+}
+
+template <typename T, int D, int G>
+hipError_t calib_impl(const CalibArgs& a, int N, int MB, hipStream_t st) {
+  hipLaunchKernelGGL((k_calib_hist<T, D, G>), dim3(MB, N * a.c.HKV), dim3(256),
+                     (size_t)G * a.B * sizeof(unsigned long long), st, a);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t calib_g(const CalibArgs& a, int G, int N, int MB, hipStream_t st) {
+  switch (G) {
+    case 1: return calib_impl<T, D, 1>(a, N, MB, st);
+    case 2: return calib_impl<T, D, 2>(a, N, MB, st);
+    case 4: return calib_impl<T, D, 4>(a, N, MB, st);
+    case 8: return calib_impl<T, D, 8>(a, N, MB, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_calibrate(const CacheView& c, const SeqView& s, const CalibParams& p, hipStream_t st) {
+  CalibArgs a;
+  a.c = c;
+  a.s = s;
+  a.q = p.q;
+  a.Lq = kBlock * s.MB;
+  a.HQ = p.HQ;
+  a.B = p.num_bins;
+  a.w = p.w;
+  a.b = p.b;
+  a.rho = p.rho;
+  a.lo = p.lo;
+  a.hi = p.hi;
+  a.bscale = (float)((double)p.num_bins / ((double)p.hi - (double)p.lo));
+  a.hist = (unsigned long long*)p.hist;
+  a.above = (unsigned long long*)p.above;
+  a.total = (unsigned long long*)p.total;
+  a.c_out = p.c_out;
+  a.err = p.err;
+  const int G = p.HQ / c.HKV;
+  const int64_t nz = (int64_t)p.HQ * p.num_bins;
+  const int zgrid = (int)((nz + 255) / 256 > 1024 ? 1024 : (nz + 255) / 256);
+  hipLaunchKernelGGL(k_calib_zero, dim3(zgrid > 0 ? zgrid : 1), dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (c.kv_dtype == 1) e = c.D == 128 ? calib_g<Bf16, 128>(a, G, s.N, s.MB, st) : calib_g<Bf16, 64>(a, G, s.N, s.MB, st);
+  else e = c.D == 128 ? calib_g<F32, 128>(a, G, s.N, s.MB, st) : calib_g<F32, 64>(a, G, s.N, s.MB, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_calib_search, dim3(p.HQ), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace eta

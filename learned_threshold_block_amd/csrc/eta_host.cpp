@@ -326,6 +326,45 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
                        block_size, out, workspace, ws_bytes, stream);
 }
 
+eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                         const float* w, const float* b, const float* rho, const eta_calib_opts* opts,
+                         uint64_t* hist, uint64_t* above, uint64_t* total, float* c_out, int32_t* err_flag,
+                         eta_stream_t stream) {
+  eta_status st = check_cache(cache);
+  if (st != ETA_OK) return st;
+  st = check_seqs(seqs);
+  if (st != ETA_OK) return st;
+  if (!opts || !q || !aligned(q, 16)) return ETA_ERR_INVALID_ARGUMENT;
+  if (!hist || !above || !total || !c_out || !err_flag || !aligned(hist, 8) || !aligned(above, 8) ||
+      !aligned(total, 8) || !aligned(c_out, 4) || !aligned(err_flag, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  const bool learned = w != nullptr || b != nullptr;
+  if (learned && (!w || !b || rho || !aligned(w, 16) || !aligned(b, 4))) return ETA_ERR_INVALID_ARGUMENT;
+  if (!learned && (!rho || !aligned(rho, 4))) return ETA_ERR_INVALID_ARGUMENT;
+  if (!(opts->lo < opts->hi) || !isfinite(opts->lo) || !isfinite(opts->hi) || opts->num_bins < 2)
+    return ETA_ERR_INVALID_ARGUMENT;
+  Dims d;
+  st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &d);
+  if (st != ETA_OK) return st;
+  if ((int64_t)d.G * opts->num_bins > 8192) return ETA_ERR_UNSUPPORTED;
+  if ((int64_t)seqs->num_seqs * d.HKV > 65535) return ETA_ERR_UNSUPPORTED;  // grid rows
+  CalibParams p;
+  p.q = q;
+  p.HQ = num_q_heads;
+  p.num_bins = opts->num_bins;
+  p.w = w;
+  p.b = b;
+  p.rho = rho;
+  p.lo = opts->lo;
+  p.hi = opts->hi;
+  p.hist = hist;
+  p.above = above;
+  p.total = total;
+  p.c_out = c_out;
+  p.err = err_flag;
+  return hip_status(launch_calibrate(view_of(cache), view_of(seqs), p, (hipStream_t)stream));
+}
+
 eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,
                      int num_kv_heads, int32_t* admitted_per_head, int32_t* union_per_kv,
                      int64_t* tokens_per_head, uint8_t* rescued, uint32_t* admitted_bitmap,

@@ -96,6 +96,20 @@ struct DecodeParams {
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };
 
+struct CalibParams {
+  const void* q;  // [N][64 * MB][HQ][D]
+  int HQ, num_bins;
+  const float* w;    // [HQ][D] learned predictor, or null
+  const float* b;    // [HQ]
+  const float* rho;  // [HQ] target densities, or null
+  float lo, hi;
+  uint64_t* hist;   // [HQ][num_bins]
+  uint64_t* above;  // [HQ]
+  uint64_t* total;  // [HQ]
+  float* c_out;     // [HQ]
+  int* err;         // [1] device flag: an out-of-range page id was met
+};
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_build_summaries(const CacheView& c, const SeqView& s, hipStream_t st);
 hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new, const void* v_new,
@@ -106,6 +120,7 @@ hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodePar
                            const Ws& ws, hipStream_t st);  // also writes NaN rows for segments with no entries
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
+hipError_t launch_calibrate(const CacheView& c, const SeqView& s, const CalibParams& p, hipStream_t st);
 int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
 
 }  // namespace eta

@@ -402,8 +402,11 @@ def row_weight(t: int) -> int:
 
 
 def score_bins(S: np.ndarray, lo: float, hi: float, num_bins: int) -> np.ndarray:
-    """Bin index of each score: floor((S - lo) num_bins / (hi - lo)), clamped to the end bins."""
-    x = np.floor((np.asarray(S, dtype=np.float64) - lo) * (num_bins / (hi - lo)))
+    """Bin index of each score: floor((S - lo) num_bins / (hi - lo)), clamped to the
+    end bins; a NaN score (non-finite key) falls in bin 0."""
+    with np.errstate(invalid="ignore"):
+        x = np.floor((np.asarray(S, dtype=np.float64) - lo) * (num_bins / (hi - lo)))
+    x = np.where(np.isnan(x), 0.0, x)
     return np.clip(x, 0, num_bins - 1).astype(np.int64)
 
 

@@ -36,7 +36,8 @@ def test_struct_layouts_match_header(tmp_path):
     """The ctypes mirrors of eta_cache, eta_seqs and eta_screen_opts have the
     header's fields, offsets and sizes (a C program compiled against eta.h
     prints them): a field added on one side only is caught here."""
-    structs = {"eta_cache": _lib.EtaCacheC, "eta_seqs": _lib.EtaSeqsC, "eta_screen_opts": _lib.EtaScreenOptsC}
+    structs = {"eta_cache": _lib.EtaCacheC, "eta_seqs": _lib.EtaSeqsC, "eta_screen_opts": _lib.EtaScreenOptsC,
+               "eta_calib_opts": _lib.EtaCalibOptsC}
     lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "eta.h"', "int main(void) {"]
     for cname, cls in structs.items():
         lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
@@ -176,3 +177,24 @@ def test_decode_ex_rejects_bad_screens():
         _lib.ETA_ERR_INVALID_ARGUMENT  # misaligned sigma
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0, c=with_sigma) == too_small
     assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small
+
+
+def test_calibrate_rejects():
+    L = _lib.lib()
+    c, s = cache(), seqs()
+
+    def call(w=FAKE * 8, b=FAKE * 9, rho=None, bins=512, lo=-8.0, hi=8.0, hq=32, q=FAKE * 7, hist=FAKE * 10):
+        o = _lib.EtaCalibOptsC(bins, lo, hi)
+        return L.eta_calibrate(ctypes.byref(c), ctypes.byref(s), q, hq, w, b, rho, ctypes.byref(o), hist,
+                               FAKE * 11, FAKE * 12, FAKE * 13, FAKE * 14, None)
+    bad = _lib.ETA_ERR_INVALID_ARGUMENT
+    assert call(w=None, b=None, rho=None) == bad          # no target
+    assert call(rho=FAKE * 15) == bad                     # both targets
+    assert call(b=None) == bad                            # half a predictor
+    assert call(bins=1) == bad
+    assert call(lo=1.0, hi=1.0) == bad
+    assert call(hi=float("inf")) == bad
+    assert call(q=FAKE + 2) == bad
+    assert call(hist=FAKE + 4) == bad
+    assert call(hq=30) == bad
+    assert call(bins=4096) == _lib.ETA_ERR_UNSUPPORTED    # G = 4: 16384 bins of LDS
