@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--bound", default="geometric", choices=["geometric", "dual"],
                    help="block screen: the geometric bound, or the dual screen (z deviations)")
     p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
+    p.add_argument("--calibration", action="store_true",
+                   help="only time the offline calibration (16 sequences x 4096 positions, GQA 32/8, d=128, bf16) "
+                        "and print its own JSON line")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB `steps` times (calibrates the "
                         "HBM byte counters) and exit")
@@ -89,6 +92,68 @@ def stored_traffic(workload_key):
             return None
         return int(fields["traffic_bytes_per_launch"])
     return None
+
+
+def calibration_bench(steps):
+    """Offline calibration (eta_calibrate): 1/t-weighted score histograms over
+    16 synthetic sequences of 4096 positions, a query at every position, and
+    the per-head search. Times the GPU call with HIP events; the fp64 oracle
+    on one (sequence, head) pair, scaled to the whole job."""
+    import torch
+
+    import learned_threshold_block_amd as eta
+    import workloads as W
+
+    wl = W.make_workload("seq_32k", n_seqs=16, seq_len=4096, needles=0)
+    q_all = W.trace_queries(wl, seed=5)
+    dev = torch.device("cuda")
+    cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
+                      torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
+                      torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev))
+    lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
+    bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
+    qd = eta.upload(q_all, wl.kv_dtype, dev)
+    w = torch.from_numpy(wl.w).to(dev)
+    b = torch.full((wl.h_q,), 1.0, dtype=torch.float32, device=dev)
+    B, lo, hi = 1024, -8.0, 8.0
+    cal = eta.calibrate(cache, lens, bt, qd, B, lo, hi, w=w, b=b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        eta.calibrate(cache, lens, bt, qd, B, lo, hi, w=w, b=b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    scores = sum(int(T) * (int(T) + 1) // 2 for T in wl.seq_lens) * wl.h_q
+    tflops = 2.0 * wl.d * scores / (ms * 1e-3) / 1e12
+    dens = (cal.above.double() / cal.total.double()).cpu().numpy()
+    # oracle on one (sequence, head): the same histogram in fp64
+    import oracle.eta_oracle as E
+    from threadpoolctl import threadpool_limits
+
+    one = dict(k_pages=wl.k_pages, kv_dtype=wl.kv_dtype, block_table=wl.block_table[:1], seq_lens=wl.seq_lens[:1],
+               q_all=q_all[:1])
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        E.calibration_histogram(one["k_pages"], one["kv_dtype"], one["block_table"], one["seq_lens"], one["q_all"],
+                                0, wl.group, lo, hi, B, w_h=wl.w[0], b_h=1.0)
+        cpu_s = (time.perf_counter() - t0) * wl.n_seqs * wl.h_q
+    print(json.dumps({
+        "metric": "ETA offline calibration (1/t-weighted score histograms + per-head search), ms per job",
+        "value": round(ms, 3), "unit": "ms", "higher_is_better": False, "steps": steps, "data": "synthetic",
+        "config": {"workload": "16 seqs x 4096 positions, a query at every position, GQA 32/8, d=128, bf16 keys, "
+                               "learned predictor w ~ N(0, 1/d), b = 1.0, 1024 bins over [-8, 8)",
+                   "scores": scores},
+        "dtype": "f32",
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3, "unit": "TFLOP/s",
+                     "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "note": "2*d flops per scored (query, key) pair; the dot products run as bf16 dot2 into fp32"},
+        "training_density_mean": round(float(dens.mean()), 4),
+        "calibrated_c_mean": round(float(cal.c.mean().item()), 4),
+        "cpu_baseline": {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
+                         "sample": "one (sequence, head) pair of fp64 NumPy histogramming, scaled by 16 x 32"},
+    }), flush=True)
 
 
 def copy_probe(mib, steps):
@@ -273,6 +338,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         copy_probe(args.copy_probe, args.steps)
+        return
+    if args.calibration:
+        calibration_bench(max(3, min(args.steps, 20)))
         return
 
     S = Setup(args.workload, args.density, args.bound, args.z)
