@@ -54,6 +54,10 @@ measured for recall, not checked for soundness.
 Offline calibration (Section 4.7, D.2, Algorithm 1): calibration_histogram,
 calibrated_bin and calibrate below; the reading taken is stated there.
 
+Causal prefill (prefill below): the same gated rule at every position of a
+prompt over the keys up to it, dense (no block pruning), thresholds per
+position.
+
 Parity unpinned: the pages' exact Eq. 7, the body of Algorithm 1 and their
 chunk-local rescue rule are not reproducible from the text; the first two are
 implemented as readings, the last is not implemented.
@@ -476,3 +480,48 @@ def calibrate(k_pages, kv_dtype: str, block_table, seq_lens, q_all, num_kv_heads
         out[h] = dict(hist=hist, above=above, total=total, target=target, bin=bstar,
                       c=lo + bstar * (hi - lo) / num_bins)
     return out
+
+
+# --------------------------------------------------------------------------- causal prefill
+def prefill(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q_all, tau_mode: str, w, b_or_c,
+            a: float, beta: float, heads: Optional[Iterable] = None, chunk: int = 512) -> np.ndarray:
+    """Causal ETA attention over a whole prompt (the training-time rule of
+    Sections 2.2, E.3 and G.1 applied at every position): for position t of
+    sequence n and query head h, over the keys s <= t,
+        S = s_scale q_t . k_s,  S~ = S sigmoid(beta (S - tau~_t)),
+        o_t = sum_s exp(S~) v_s / sum_s exp(S~),
+    with tau~_t the learned (w_h . q_t + b_h - a) or calibrated (c_h - a)
+    threshold of that position. No block is pruned: the prompt pass is dense
+    and the gate alone filters (the blocks' records are built alongside, by
+    build_summaries). q_all: [N][positions][H_Q][d]; returns float64
+    [N][positions][H_Q][d], NaN at positions >= seq_len and for heads not in
+    `heads`."""
+    N, Lq, HQ, D = q_all.shape
+    HKV = k_pages.shape[1]
+    G = HQ // HKV
+    scale = 1.0 / math.sqrt(D)
+    want = None if heads is None else set((int(n), int(h)) for n, h in heads)
+    o = np.full((N, Lq, HQ, D), np.nan)
+    for n in range(N):
+        T = int(seq_lens[n])
+        nb = -(-T // BLOCK)
+        pages = np.asarray(block_table[n, :nb], dtype=np.int64)
+        for h in range(HQ):
+            if want is not None and (n, h) not in want:
+                continue
+            g = h // G
+            K = upcast(k_pages[pages, g], kv_dtype).reshape(nb * BLOCK, D)[:T]
+            V = upcast(v_pages[pages, g], kv_dtype).reshape(nb * BLOCK, D)[:T]
+            Q = upcast(q_all[n, :T, h], kv_dtype)
+            for t0 in range(0, T, chunk):
+                t1 = min(T, t0 + chunk)
+                tau = np.array([threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a)
+                                for t in range(t0, t1)])
+                S = scale * (Q[t0:t1] @ K[:t1].T)
+                St = gate(S, tau[:, None], beta)
+                causal = np.arange(t1)[None, :] <= np.arange(t0, t1)[:, None]
+                St = np.where(causal, St, -np.inf)
+                m = St.max(axis=1, keepdims=True)
+                wts = np.exp(St - m)
+                o[n, t0:t1, h] = (wts @ V[:t1]) / wts.sum(axis=1, keepdims=True)
+    return o

@@ -304,6 +304,85 @@ def pin_calibration_target_property(E, seed=11):
                 assert r["c"] <= prev[h]
         prev = {h: r["c"] for h, r in res.items()}
 
+
+# --------------------------------------------------------------------------- causal prefill
+def _prefill(E, wl, q, bias=None, mode=None, **kw):
+    return E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q, mode or wl.tau_mode,
+                     wl.w, wl.bias if bias is None else bias, wl.a, wl.beta, **kw)
+
+
+def pin_prefill_causal_sdpa(E):
+    """tau~ = -inf: every position is textbook causal softmax attention (torch
+    SDPA with is_causal, fp64, grouped-query heads)."""
+    import torch
+    wl = tiny(21, n=2, lens=(150, 97), h_q=4, h_kv=2, d=8, dtype="bf16", mode="calibrated",
+              bias=np.full(4, -np.inf, dtype=np.float32))
+    q = W.trace_queries(wl, seed=2)
+    o = _prefill(E, wl, q)
+    for n in range(wl.n_seqs):
+        T = int(wl.seq_lens[n])
+        nb = -(-T // 64)
+        pages = wl.block_table[n, :nb]
+        f64 = lambda x: W.storage_to_f32(x, wl.kv_dtype).astype(np.float64)  # noqa: E731
+        K = f64(wl.k_pages[pages]).transpose(1, 0, 2, 3).reshape(wl.h_kv, nb * 64, wl.d)[:, :T]
+        V = f64(wl.v_pages[pages]).transpose(1, 0, 2, 3).reshape(wl.h_kv, nb * 64, wl.d)[:, :T]
+        Q = f64(q[n, :T]).transpose(1, 0, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(np.ascontiguousarray(Q))[None], torch.from_numpy(np.ascontiguousarray(K))[None],
+            torch.from_numpy(np.ascontiguousarray(V))[None], is_causal=True, enable_gqa=True)[0].numpy()
+        np.testing.assert_allclose(o[n, :T].transpose(1, 0, 2), ref, rtol=1e-10, atol=1e-12)
+
+
+def pin_prefill_prefix_means(E):
+    """tau~ far above every logit: every logit is filtered to 0 and position t
+    returns the plain mean of v_0 .. v_t (the uniform floor, prefix by prefix)."""
+    wl = tiny(22, n=1, lens=(130,), h_q=2, h_kv=1, d=8, dtype="f32", mode="calibrated",
+              bias=np.full(2, 1e4, dtype=np.float32))
+    q = W.trace_queries(wl, seed=4)
+    o = _prefill(E, wl, q)
+    V = wl.v_pages[wl.block_table[0, :3], 0].astype(np.float64).reshape(-1, wl.d)[:130]
+    want = np.cumsum(V, axis=0) / np.arange(1, 131)[:, None]
+    for h in range(2):
+        np.testing.assert_allclose(o[0, :130, h], want, rtol=1e-12, atol=1e-14)
+
+
+def pin_prefill_last_row_is_decode(E):
+    """The last position of a prompt is one decode step with every block
+    admitted: the prefill row equals the decode oracle with lwb >= blocks."""
+    wl = tiny(23, n=2, lens=(200, 64), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned")
+    q = W.trace_queries(wl, seed=6)
+    o = _prefill(E, wl, q)
+    for n in range(wl.n_seqs):
+        T = int(wl.seq_lens[n])
+        qd = q[:, T - 1].copy()
+        res = E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, qd, wl.tau_mode, wl.w,
+                       wl.bias, wl.a, wl.beta, lwb=10 ** 6)
+        np.testing.assert_allclose(o[n, T - 1], res.o[n], rtol=1e-10, atol=1e-12)
+
+
+def pin_prefill_bruteforce(E):
+    """Every position of a tiny prompt against a per-element pure-Python loop."""
+    wl = tiny(24, n=1, lens=(70,), h_q=2, h_kv=1, d=4, dtype="f32", mode="learned", beta=2.0, a=0.3)
+    q = W.trace_queries(wl, seed=8)
+    o = _prefill(E, wl, q)
+    s = 1.0 / math.sqrt(wl.d)
+    page = [int(x) for x in wl.block_table[0, :2]]
+    key = lambda t: [float(x) for x in wl.k_pages[page[t // 64], 0, t % 64]]  # noqa: E731
+    val = lambda t: [float(x) for x in wl.v_pages[page[t // 64], 0, t % 64]]  # noqa: E731
+    for h in range(2):
+        for t in (0, 1, 37, 63, 64, 69):
+            qt = [float(x) for x in q[0, t, h]]
+            tau = math.fsum(float(wl.w[h][c]) * qt[c] for c in range(wl.d)) + float(wl.bias[h]) - wl.a
+            logits = []
+            for u in range(t + 1):
+                S = s * math.fsum(qt[c] * key(u)[c] for c in range(wl.d))
+                logits.append(S / (1.0 + math.exp(-wl.beta * (S - tau))))
+            m = max(logits)
+            wts = [math.exp(x - m) for x in logits]
+            den = math.fsum(wts)
+            want = [math.fsum(wts[u] * val(u)[c] for u in range(t + 1)) / den for c in range(wl.d)]
+            np.testing.assert_allclose(o[0, t, h], want, rtol=1e-11, atol=1e-13)
+
 # --------------------------------------------------------------------------- thresholds
 def pin_threshold_closed_form(E):
     """tau~ = w.q + b - a (learned), c - a (calibrated): Sections 1, 4.7, D.1, G.1."""
@@ -531,4 +610,5 @@ ALL_PINS = [
     pin_tail_masking, pin_page_permutation, pin_nonfinite_keys, pin_threshold_tie_admitted,
     pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
     pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
+    pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
 ]
