@@ -239,6 +239,33 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
                          uint64_t* hist, uint64_t* above, uint64_t* total, float* c_out, int32_t* err_flag,
                          eta_stream_t stream);
 
+/* Causal prompt pass (Sections 2.2 and 2.3, the fused causal forward; E.1,
+ * E.3 and G.1, the gate inside the softmax; 4.8, records built while the
+ * prompt is processed). For every position t < seq_len of every sequence and
+ * every query head h, over the keys s <= t of the sequence's pages:
+ *   S = q_t . k_s / sqrt(d),  S~ = S sigmoid(beta (S - tau~_t)),
+ *   out_t = sum_s exp(S~) v_s / sum_s exp(S~),
+ * with tau~_t = w_h . q_t + b_h - a (ETA_TAU_LEARNED) or c_h - a
+ * (ETA_TAU_CALIBRATED; c_h = -inf gives plain causal attention). Dense: no
+ * block is skipped, the gate alone filters. In the same launch the records
+ * (centroid, radius, and the deviation if cache->sigma is set) of every
+ * complete block (64 j + 64 <= seq_len) are written, bit-identical to
+ * eta_build_block_summaries'; the cache must hold the prompt's keys and values.
+ *   q        [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] bfloat16
+ *            bits (device, 16-byte aligned); positions >= seq_len are not read.
+ *   w, b_or_c  as for eta_decode (device float32; w ignored when calibrated).
+ *   out      [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] float32
+ *            (device, 16-byte aligned); rows at positions >= seq_len are NaN.
+ *   err_flag [1] int32 device out: 1 if a length outside [0, 64*max_blocks]
+ *            (that sequence's rows are then NaN) or an out-of-range page id
+ *            (the block reads as zeros and its record is left alone) was met.
+ * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise: the products run
+ * on the bfloat16 matrix cores), beta > 0 finite, a finite, and
+ * num_seqs * num_kv_heads <= 65535. Asynchronous on `stream`. */
+eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                       int tau_mode, const float* w, const float* b_or_c, float a, float beta, float* out,
+                       int32_t* err_flag, eta_stream_t stream);
+
 /* Static text for a status code. */
 const char* eta_status_string(eta_status status);
 

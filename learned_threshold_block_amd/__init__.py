@@ -218,6 +218,36 @@ def calibrate(cache: Cache, seq_lens, block_table, q_all, num_bins: int, lo: flo
 
 
 @dataclasses.dataclass
+class Prefill:
+    out: torch.Tensor  # float32 [N][64*max_blocks][H_Q][d]; NaN rows at positions >= seq_len
+    err: torch.Tensor  # int32 [1]: 1 if an out-of-range length or page id was met
+
+
+def prefill(cache: Cache, seq_lens, block_table, q_all, tau_mode: int, b_or_c, w=None, a: float = 0.0,
+            beta: float = 5.0, out=None, stream=None) -> Prefill:
+    """Causal prompt pass (eta_prefill): gated attention at every position of
+    every sequence over the keys up to it, and the records of every complete
+    block. q_all is [N][64*max_blocks][H_Q][d] bfloat16."""
+    dev = cache.k_pages.device
+    _need(q_all, "q_all", cache.k_pages.dtype, dev)
+    N, L, HQ, D = q_all.shape
+    if L != BLOCK * block_table.shape[1] or N != block_table.shape[0] or D != cache.head_dim:
+        raise ValueError("q_all must be [num_seqs][64 * max_blocks_per_seq][H_Q][d]")
+    _need(b_or_c, "b_or_c", torch.float32, dev)
+    if w is not None:
+        _need(w, "w", torch.float32, dev)
+    if out is None:
+        out = torch.empty(N, L, HQ, D, dtype=torch.float32, device=dev)
+    _need(out, "out", torch.float32, dev)
+    err = torch.empty(1, dtype=torch.int32, device=dev)
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    _check(_lib.lib().eta_prefill(ctypes.byref(c), ctypes.byref(s), _ptr(q_all), HQ, int(tau_mode), _ptr(w),
+                                  _ptr(b_or_c), float(a), float(beta), _ptr(out), _ptr(err), _stream(stream)),
+           "eta_prefill")
+    return Prefill(out, err)
+
+
+@dataclasses.dataclass
 class Stats:
     admitted_per_head: np.ndarray   # int32 [N][H_Q]
     union_per_kv: np.ndarray        # int32 [N][H_KV]

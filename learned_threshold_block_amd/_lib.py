@@ -37,6 +37,7 @@ EXPORTS = (
     "eta_decode_phase",
     "eta_decode_ex",
     "eta_calibrate",
+    "eta_prefill",
     "eta_stats",
     "eta_status_string",
 )
@@ -115,6 +116,8 @@ def lib() -> ctypes.CDLL:
     L.eta_decode_ex.restype = I
     L.eta_calibrate.argtypes = [cp, sp, P, I, P, P, P, ctypes.POINTER(EtaCalibOptsC), P, P, P, P, P, P]
     L.eta_calibrate.restype = I
+    L.eta_prefill.argtypes = [cp, sp, P, I, I, P, P, F, F, P, P, P]
+    L.eta_prefill.restype = I
     L.eta_stats.argtypes = [P, I, I, I, I, P, P, P, P, P, P]
     L.eta_stats.restype = I
     L.eta_status_string.argtypes = [I]

@@ -365,6 +365,37 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
   return hip_status(launch_calibrate(view_of(cache), view_of(seqs), p, (hipStream_t)stream));
 }
 
+eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
+                       int tau_mode, const float* w, const float* b_or_c, float a, float beta, float* out,
+                       int32_t* err_flag, eta_stream_t stream) {
+  eta_status st = check_cache(cache);
+  if (st != ETA_OK) return st;
+  st = check_seqs(seqs);
+  if (st != ETA_OK) return st;
+  if (!q || !out || !b_or_c || !err_flag || !aligned(q, 16) || !aligned(out, 16) || !aligned(b_or_c, 4) ||
+      !aligned(err_flag, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (tau_mode != ETA_TAU_LEARNED && tau_mode != ETA_TAU_CALIBRATED) return ETA_ERR_INVALID_ARGUMENT;
+  if (tau_mode == ETA_TAU_LEARNED && (!w || !aligned(w, 16))) return ETA_ERR_INVALID_ARGUMENT;
+  if (!(beta > 0.f) || !isfinite(beta) || !isfinite(a)) return ETA_ERR_INVALID_ARGUMENT;
+  Dims d;
+  st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &d);
+  if (st != ETA_OK) return st;
+  if (cache->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;  // the matrix-core path is bfloat16
+  if ((int64_t)seqs->num_seqs * d.HKV > 65535) return ETA_ERR_UNSUPPORTED;  // grid rows
+  PrefillParams p;
+  p.q = q;
+  p.HQ = num_q_heads;
+  p.tau_mode = tau_mode == ETA_TAU_LEARNED ? 0 : 1;
+  p.w = w;
+  p.b = b_or_c;
+  p.a = a;
+  p.beta = beta;
+  p.out = out;
+  p.err = err_flag;
+  return hip_status(launch_prefill(view_of(cache), view_of(seqs), p, (hipStream_t)stream));
+}
+
 eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,
                      int num_kv_heads, int32_t* admitted_per_head, int32_t* union_per_kv,
                      int64_t* tokens_per_head, uint8_t* rescued, uint32_t* admitted_bitmap,

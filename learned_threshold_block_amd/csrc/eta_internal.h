@@ -110,6 +110,16 @@ struct CalibParams {
   int* err;         // [1] device flag: an out-of-range page id was met
 };
 
+struct PrefillParams {
+  const void* q;  // [N][64 * MB][HQ][D]
+  int HQ, tau_mode;
+  const float* w;  // [HQ][D] (learned)
+  const float* b;  // [HQ]
+  float a, beta;
+  float* out;  // [N][64 * MB][HQ][D]
+  int* err;    // [1] device flag: an out-of-range length or page id was met
+};
+
 // launchers (return hipError_t of the launch)
 hipError_t launch_build_summaries(const CacheView& c, const SeqView& s, hipStream_t st);
 hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new, const void* v_new,
@@ -121,6 +131,7 @@ hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodePar
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
 hipError_t launch_calibrate(const CacheView& c, const SeqView& s, const CalibParams& p, hipStream_t st);
+hipError_t launch_prefill(const CacheView& c, const SeqView& s, const PrefillParams& p, hipStream_t st);
 int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
 
 }  // namespace eta

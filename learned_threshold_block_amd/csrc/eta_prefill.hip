@@ -1,0 +1,384 @@
+// Causal prompt pass: the gated attention rule at every prompt position, with
+// the blocks' decode records built in the same launch.
+//
+// "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Sections 2.2
+// and 2.3 (the fused causal forward over query blocks and key blocks), E.1,
+// E.3 and G.1 (the gate S~ = S sigmoid(beta (S - tau~)) inside the softmax),
+// and 4.8 (records built while the prompt is processed). For position t of a
+// sequence and query head h, over the keys s <= t:
+//   S = q_t . k_s / sqrt(d),  S~ = S sigmoid(beta (S - tau~_t)),
+//   o_t = sum_s exp(S~) v_s / sum_s exp(S~),
+// tau~_t = w_h . q_t + b_h - a (learned) or c_h - a (calibrated). Nothing is
+// pruned in the prompt pass; the gate alone filters.
+//
+// One workgroup of eight wavefronts takes one (sequence, KV head) and QT
+// consecutive positions; wavefront w takes head w % G of the group and the 32
+// positions (w / G) * 32 .. + 31. The workgroup walks the key blocks of 64
+// tokens up to the diagonal; K (row-major) and V (transposed) of the next
+// block stream into the other half of a double-buffered LDS area while the
+// current one is used. Both products run on the matrix cores
+// (v_mfma_f32_32x32x16_bf16, float32 accumulation):
+//   S^T = K Q^T  (A = 32 keys x 16 dims from LDS, B = the wavefront's 32
+//                 queries, held in registers for the whole pass): each lane
+//                 ends with one query and 16 of the 32 keys, so the gate and
+//                 the softmax are per-lane, with one exchange between the two
+//                 half-waves for the row maximum and sum.
+//   O^T += V^T P^T (A = 32 dims x 16 keys of V^T from LDS, B = the weights
+//                 straight from the lane's registers): the keys of a step are
+//                 taken in the order the lanes hold them, and V^T is read in the
+//                 same order, so P needs no data movement.
+// P enters the matrix cores as two bfloat16 terms (its leading 8 mantissa bits
+// and the rounded remainder), so each weight is carried to about 2^-16
+// relative; one bfloat16 term would perturb outputs by a few 1e-3. The running
+// maximum is only moved when a weight would exceed 2^8 (float32 and the two
+// terms are exact well beyond that), which spares most rescales of the
+// accumulators.
+//
+// Records: the workgroup holding a complete block's last position builds the
+// block's centroid, radius (and deviation, if the cache has a deviation
+// buffer) with the same device function as the bulk builder, so the bits are
+// the same as eta_build_block_summaries'.
+#include "eta_records.h"
+
+namespace eta {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr float kRescaleLog2 = 8.0f;  // weights stay <= 2^8 between rescales
+
+struct PrefillArgs {
+  CacheView c;
+  SeqView s;
+  const uint16_t* q;  // [N][Lq][HQ][D] bfloat16 bits
+  int Lq, HQ, tau_mode;
+  const float* w;  // [HQ][D] (learned)
+  const float* b;  // [HQ] bias (learned) or constant (calibrated)
+  float a, beta;
+  float* out;  // [N][Lq][HQ][D]
+  int* err;    // [1]
+};
+
+__global__ void k_prefill_zero(int* err) { *err = 0; }
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+template <int D>
+struct PfLds {
+  static constexpr int KS = D + 8;     // K row stride (elements): rows start 4 banks apart
+  static constexpr int VS = 64 + 4;    // V^T row stride (elements): 8-byte reads of 32 rows hit 64 banks
+  static constexpr int KE = 64 * KS;   // elements of one K buffer
+  static constexpr int VE = D * VS;    // elements of one V^T buffer
+  static constexpr int BUF = KE + VE;
+};
+
+template <int D>
+struct PfTileRegs {
+  static constexpr int KC = 64 * D / 8 / kPfThreads;  // 16-byte K chunks per thread
+  uint4 k[KC];
+  uint4 v0, v1;  // rows 2 kp and 2 kp + 1 of V, 8 dims from 8 dc
+};
+
+// Loads key block kt of (n, g) into registers; rows at or past `rem` (the
+// sequence's end inside this block) read as zeros, as does a block whose page
+// id is out of range.
+template <int D>
+__device__ __forceinline__ void pf_load(PfTileRegs<D>& R, const PrefillArgs& A, int page, bool valid, int rem,
+                                        int g, int tid) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const uint16_t* kt = (const uint16_t*)A.c.k + ((int64_t)page * A.c.HKV + g) * (kBlock * D);
+  const uint16_t* vt = (const uint16_t*)A.c.v + ((int64_t)page * A.c.HKV + g) * (kBlock * D);
+#pragma unroll
+  for (int i = 0; i < PfTileRegs<D>::KC; ++i) {
+    const int cidx = tid + i * kPfThreads, row = cidx / CPR, col = (cidx % CPR) * 8;
+    R.k[i] = (valid && row < rem) ? *(const uint4*)(kt + row * D + col) : make_uint4(0, 0, 0, 0);
+  }
+  const int kp = tid / CPR, dc = tid % CPR;
+  const bool vown = tid < 32 * CPR;
+  R.v0 = (vown && valid && 2 * kp < rem) ? *(const uint4*)(vt + (2 * kp) * D + dc * 8) : make_uint4(0, 0, 0, 0);
+  R.v1 = (vown && valid && 2 * kp + 1 < rem) ? *(const uint4*)(vt + (2 * kp + 1) * D + dc * 8)
+                                              : make_uint4(0, 0, 0, 0);
+}
+
+template <int D>
+__device__ __forceinline__ void pf_store(const PfTileRegs<D>& R, uint16_t* buf, int tid) {
+  using L = PfLds<D>;
+  constexpr int CPR = D / 8;
+  uint16_t* kl = buf;
+  uint16_t* vl = buf + L::KE;
+#pragma unroll
+  for (int i = 0; i < PfTileRegs<D>::KC; ++i) {
+    const int cidx = tid + i * kPfThreads, row = cidx / CPR, col = (cidx % CPR) * 8;
+    *(uint4*)(kl + row * L::KS + col) = R.k[i];
+  }
+  if (tid < 32 * CPR) {
+    const int kp = tid / CPR, dc = tid % CPR;
+    const uint32_t a[4] = {R.v0.x, R.v0.y, R.v0.z, R.v0.w};
+    const uint32_t b[4] = {R.v1.x, R.v1.y, R.v1.z, R.v1.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      // dims 8 dc + 2u (low halves) and 8 dc + 2u + 1 (high halves): keys 2 kp, 2 kp + 1
+      const uint32_t even = (a[u] & 0xffffu) | (b[u] << 16);
+      const uint32_t odd = (a[u] >> 16) | (b[u] & 0xffff0000u);
+      *(uint32_t*)(vl + (8 * dc + 2 * u) * L::VS + 2 * kp) = even;
+      *(uint32_t*)(vl + (8 * dc + 2 * u + 1) * L::VS + 2 * kp) = odd;
+    }
+  }
+}
+
+template <int D, int G>
+__global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
+  using L = PfLds<D>;
+  constexpr int QT = 32 * kPfWaves / G;  // positions per workgroup
+  constexpr int KSTEPS = D / 16;         // k-steps of S^T = K Q^T
+  constexpr int DT = D / 32;             // 32-dim tiles of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::BUF];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int HKV = A.c.HKV, MB = A.s.MB, HQ = A.HQ, Lq = A.Lq;
+  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
+  const int nqt = gridDim.x;
+  const int P0 = (nqt - 1 - (int)blockIdx.x) * QT;  // longest rows first
+  const int hl = wave % G, hq = g * G + hl;
+  const int pw0 = P0 + (wave / G) * 32;  // first position of this wavefront
+  const int qi = lane & 31, hh = lane >> 5;
+  const int p = pw0 + qi;                // this lane's position
+  int T = A.s.lens[n];
+  if (T < 0 || T > kBlock * MB) {  // invalid length: flagged, every row NaN
+    if (tid == 0) A.err[0] = 1;
+    T = 0;
+  }
+  const int64_t orow = (((int64_t)n * Lq + p) * HQ + hq) * D;
+
+  if (P0 >= T) {  // no valid position in this tile
+    if (p < Lq) {
+      const float4 nan4 = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+#pragma unroll
+      for (int m = 0; m < DT; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(float4*)(A.out + orow + 32 * m + 8 * i + 4 * hh) = nan4;
+    }
+    return;
+  }
+
+  // ---- queries (B operand of S^T = K Q^T) and thresholds
+  uint4 qr[KSTEPS];
+  float dot = 0.f;
+  const bool learned = A.tau_mode == 0;
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const int d0 = 16 * ks + 8 * hh;
+    qr[ks] = p < T ? *(const uint4*)(A.q + orow + d0) : make_uint4(0, 0, 0, 0);
+    if (learned) {
+      const float4 w0 = *(const float4*)(A.w + (int64_t)hq * D + d0);
+      const float4 w1 = *(const float4*)(A.w + (int64_t)hq * D + d0 + 4);
+      const uint32_t qw[4] = {qr[ks].x, qr[ks].y, qr[ks].z, qr[ks].w};
+      dot = fmaf(w0.x, bf16_lo(qw[0]), dot);
+      dot = fmaf(w0.y, bf16_hi(qw[0]), dot);
+      dot = fmaf(w0.z, bf16_lo(qw[1]), dot);
+      dot = fmaf(w0.w, bf16_hi(qw[1]), dot);
+      dot = fmaf(w1.x, bf16_lo(qw[2]), dot);
+      dot = fmaf(w1.y, bf16_hi(qw[2]), dot);
+      dot = fmaf(w1.z, bf16_lo(qw[3]), dot);
+      dot = fmaf(w1.w, bf16_hi(qw[3]), dot);
+    }
+  }
+  dot += __shfl_xor(dot, 32, 64);
+  const float bh = A.b[hq];
+  const float tau = learned ? (dot + bh) - A.a : bh - A.a;
+  const float scale = 1.0f / sqrtf((float)D);
+  const float c2 = scale * kLog2e;                 // logits to log2 units
+  const float kb = -A.beta * kLog2e * scale;       // exp2 argument of the gate: kb * acc + tb
+  const float tb = A.beta * kLog2e * tau;
+  const float thr = kRescaleLog2 / c2;             // headroom of the running maximum
+
+  f32x16_t o[DT];
+#pragma unroll
+  for (int m = 0; m < DT; ++m)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[m][e] = 0.f;
+  float mrun = -__builtin_inff(), lsum = 0.f;
+
+  // ---- key blocks 0 .. last, double-buffered through LDS
+  const int last = (min(P0 + QT, T) - 1) / kBlock;
+  const int wlast = (min(pw0 + 31, T - 1)) / kBlock;  // last block this wavefront needs (pw0 < T or none)
+  const bool wactive = pw0 < T;
+  const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  PfTileRegs<D> R;
+  {
+    const int page = bt[0];
+    const bool valid = page >= 0 && page < A.c.num_pages;
+    if (!valid && tid == 0) A.err[0] = 1;
+    pf_load<D>(R, A, valid ? page : 0, valid, T, g, tid);
+    pf_store<D>(R, lds, tid);
+  }
+  __syncthreads();
+  for (int kt = 0; kt <= last; ++kt) {
+    const bool has_next = kt < last;
+    if (has_next) {
+      const int page = bt[kt + 1];
+      const bool valid = page >= 0 && page < A.c.num_pages;
+      if (!valid && tid == 0) A.err[0] = 1;
+      pf_load<D>(R, A, valid ? page : 0, valid, T - (kt + 1) * kBlock, g, tid);
+    }
+    const uint16_t* kl = lds + (kt & 1) * L::BUF;
+    const uint16_t* vl = kl + L::KE;
+    if (wactive && kt <= wlast) {
+      // ---- S^T for keys 32 t + 8 i + 4 hh + j (acc element 4 i + j), query qi
+      f32x16_t s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+          const bf16x8_t av = *(const bf16x8_t*)(kl + (32 * t + qi) * L::KS + 16 * ks + 8 * hh);
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, qr[ks]), s[t], 0, 0, 0);
+        }
+      }
+      // ---- gate, causal mask, running maximum
+      const bool diag = kt * kBlock + kBlock - 1 > pw0;  // some key may lie after some position
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float v = s[t][e];
+          const float ex = __builtin_amdgcn_exp2f(fmaf(kb, v, tb));
+          float y = v * __builtin_amdgcn_rcpf(1.0f + ex);
+          if (diag) {
+            const int key = kt * kBlock + 32 * t + 8 * (e >> 2) + 4 * hh + (e & 3);
+            if (key > p) y = -__builtin_inff();
+          }
+          s[t][e] = y;
+          mx = fmaxf(mx, y);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const bool need = mx > mrun + thr;
+      if (__any(need)) {
+        const float mnew = need ? mx : mrun;
+        const float alpha = need ? (mrun == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(c2 * (mrun - mnew))) : 1.f;
+        lsum *= alpha;
+#pragma unroll
+        for (int m = 0; m < DT; ++m)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o[m][e] *= alpha;
+        mrun = mnew;
+      }
+      const float moff = mrun == -__builtin_inff() ? 0.f : -c2 * mrun;
+      // ---- weights, split into two bfloat16 terms, and O^T += V^T P^T
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(c2, s[t][8 * ks + 2 * u], moff));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(c2, s[t][8 * ks + 2 * u + 1], moff));
+            lsum += p0 + p1;
+            const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
+            hb[u] = (h0 >> 16) | h1;
+            lb[u] = pack_bf16_rne(p0 - __uint_as_float(h0), p1 - __uint_as_float(h1));
+          }
+          const bf16x8_t bh8 = __builtin_bit_cast(bf16x8_t, make_uint4(hb[0], hb[1], hb[2], hb[3]));
+          const bf16x8_t bl8 = __builtin_bit_cast(bf16x8_t, make_uint4(lb[0], lb[1], lb[2], lb[3]));
+          const int k0 = 32 * t + 16 * ks + 4 * hh;  // keys k0 .. k0+3 and k0+8 .. k0+11
+#pragma unroll
+          for (int m = 0; m < DT; ++m) {
+            const uint16_t* vr = vl + (32 * m + qi) * L::VS;
+            const uint2 x0 = *(const uint2*)(vr + k0);
+            const uint2 x1 = *(const uint2*)(vr + k0 + 8);
+            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y));
+            o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, o[m], 0, 0, 0);
+            o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, o[m], 0, 0, 0);
+          }
+        }
+      }
+    }
+    if (has_next) pf_store<D>(R, lds + ((kt + 1) & 1) * L::BUF, tid);
+    __syncthreads();
+  }
+
+  // ---- outputs: O^T element 4 i + j of tile m is dim 32 m + 8 i + 4 hh + j of query qi
+  if (p < Lq) {
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const bool ok = p < T;
+    const float inv = 1.0f / ltot;
+#pragma unroll
+    for (int m = 0; m < DT; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 r;
+        r.x = ok ? o[m][4 * i + 0] * inv : __builtin_nanf("");
+        r.y = ok ? o[m][4 * i + 1] * inv : __builtin_nanf("");
+        r.z = ok ? o[m][4 * i + 2] * inv : __builtin_nanf("");
+        r.w = ok ? o[m][4 * i + 3] * inv : __builtin_nanf("");
+        *(float4*)(A.out + orow + 32 * m + 8 * i + 4 * hh) = r;
+      }
+  }
+
+  // ---- records of the complete blocks whose last position lies in this tile
+  const int jb = P0 / kBlock + wave;
+  if (jb * kBlock + kBlock - 1 < P0 + QT && jb * kBlock + kBlock <= T) {
+    const int page = bt[jb];
+    if (page >= 0 && page < A.c.num_pages) {
+      const int64_t rec = (int64_t)page * HKV + g;
+      const uint16_t* tile = (const uint16_t*)A.c.k + rec * kBlock * D;
+      build_record<Bf16, D>(tile, nullptr, A.c.mu + rec * D, A.c.radius + rec,
+                            A.c.sigma ? A.c.sigma + rec * D : nullptr, lane);
+    }
+  }
+}
+
+template <int D, int G>
+hipError_t pf_launch(const PrefillArgs& a, hipStream_t st) {
+  constexpr int QT = 32 * kPfWaves / G;
+  const int nqt = (a.Lq + QT - 1) / QT;
+  hipLaunchKernelGGL((k_prefill<D, G>), dim3(nqt, a.s.N * a.c.HKV), dim3(kPfThreads), 0, st, a);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t pf_g(const PrefillArgs& a, int G, hipStream_t st) {
+  switch (G) {
+    case 1: return pf_launch<D, 1>(a, st);
+    case 2: return pf_launch<D, 2>(a, st);
+    case 4: return pf_launch<D, 4>(a, st);
+    case 8: return pf_launch<D, 8>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const CacheView& c, const SeqView& s, const PrefillParams& p, hipStream_t st) {
+  PrefillArgs a;
+  a.c = c;
+  a.s = s;
+  a.q = (const uint16_t*)p.q;
+  a.Lq = kBlock * s.MB;
+  a.HQ = p.HQ;
+  a.tau_mode = p.tau_mode;
+  a.w = p.w;
+  a.b = p.b;
+  a.a = p.a;
+  a.beta = p.beta;
+  a.out = p.out;
+  a.err = p.err;
+  hipLaunchKernelGGL(k_prefill_zero, dim3(1), dim3(1), 0, st, p.err);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int G = p.HQ / c.HKV;
+  return c.D == 128 ? pf_g<128>(a, G, st) : pf_g<64>(a, G, st);
+}
+
+}  // namespace eta

@@ -1,0 +1,99 @@
+// Block record builder shared by the record kernels and the prompt pass:
+// centroid mu^ (float16, nearest even) and radius R^ (float32, rounded up) of
+// one complete 64-token key block, and optionally its coordinate deviation.
+//
+// "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Section 3.2
+// and Appendix F.1: the decode screen reads one compact record per block and
+// KV head instead of the keys. The radius is measured about the stored
+// (rounded) centroid, so that q.k <= q.mu^ + ||q|| R^ holds for every key of
+// the block.
+#pragma once
+
+#include "eta_device.h"
+
+namespace eta {
+
+template <typename T>
+__device__ __forceinline__ float load_elem(const typename T::Stored* p);
+template <>
+__device__ __forceinline__ float load_elem<Bf16>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)(*p) << 16);
+}
+template <>
+__device__ __forceinline__ float load_elem<F32>(const float* p) {
+  return *p;
+}
+
+// One wavefront. tile: [64][D] keys of one (page, kv head). If override_row is
+// non-null, row 63 is read from it instead of the tile. Lanes own columns;
+// the rows are read twice (sums, then distances and deviations), which keeps
+// the register footprint small enough for eight wavefronts per SIMD. Writes
+// the centroid and radius, and the coordinate deviation if sig_out is not null.
+template <typename T, int D>
+__device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
+                             uint16_t* mu_out, float* r_out, uint16_t* sig_out, int lane) {
+  constexpr int CPL = D / 64;  // columns per lane: 2 (D=128) or 1 (D=64)
+  double sum[CPL];
+  bool finite = true;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) sum[c] = 0.0;
+  for (int r = 0; r < kBlock; ++r) {
+    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const float x = load_elem<T>(row + lane * CPL + c);
+      finite = finite && (fabsf(x) <= 3.4028234663852886e38f);
+      sum[c] += (double)x;
+    }
+  }
+  uint16_t h[CPL];
+  double mu[CPL], mean[CPL], dev2[CPL];
+  bool ok = finite;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    mean[c] = sum[c] * (1.0 / kBlock);
+    dev2[c] = 0.0;
+    h[c] = f64_to_f16_rne(mean[c]);
+    ok = ok && ((h[c] & 0x7c00u) != 0x7c00u);
+  }
+  const bool all_ok = __all(ok);
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    if (!all_ok) h[c] = 0;
+    mu[c] = (double)f16_bits_to_f32(h[c]);
+    mu_out[lane * CPL + c] = h[c];
+  }
+  double rmax = 0.0;
+  for (int r = 0; r < kBlock; ++r) {
+    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
+    double part = 0.0;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const double x = (double)load_elem<T>(row + lane * CPL + c);
+      const double dlt = x - mu[c];
+      part += dlt * dlt;
+      const double dm = x - mean[c];  // deviation about the float64 mean
+      dev2[c] += dm * dm;
+    }
+    const double tot = wave_sum_f64(part);
+    rmax = (tot > rmax || tot != tot) ? tot : rmax;  // NaN propagates
+  }
+  // coordinate deviation (population) as float16
+  if (sig_out) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const double sd = sqrt(dev2[c] * (1.0 / kBlock));
+      sig_out[lane * CPL + c] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
+    }
+  }
+  const bool any_bad = __any(!finite);
+  if (lane == 0) {
+    float r;
+    if (any_bad || !(rmax < 1e300)) r = __builtin_inff();
+    else r = f64_to_f32_up(sqrt(rmax) * (1.0 + 0x1p-40));
+    *r_out = r;
+  }
+}
+
+
+}  // namespace eta

@@ -484,7 +484,8 @@ def calibrate(k_pages, kv_dtype: str, block_table, seq_lens, q_all, num_kv_heads
 
 # --------------------------------------------------------------------------- causal prefill
 def prefill(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q_all, tau_mode: str, w, b_or_c,
-            a: float, beta: float, heads: Optional[Iterable] = None, chunk: int = 512) -> np.ndarray:
+            a: float, beta: float, heads: Optional[Iterable] = None, chunk: int = 512,
+            positions: Optional[Iterable] = None) -> np.ndarray:
     """Causal ETA attention over a whole prompt (the training-time rule of
     Sections 2.2, E.3 and G.1 applied at every position): for position t of
     sequence n and query head h, over the keys s <= t,
@@ -494,16 +495,21 @@ def prefill(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q_all, tau_m
     threshold of that position. No block is pruned: the prompt pass is dense
     and the gate alone filters (the blocks' records are built alongside, by
     build_summaries). q_all: [N][positions][H_Q][d]; returns float64
-    [N][positions][H_Q][d], NaN at positions >= seq_len and for heads not in
-    `heads`."""
+    [N][positions][H_Q][d], NaN at positions >= seq_len, for heads not in
+    `heads` and, if `positions` is given, at positions not in it (each row
+    depends only on its own query and the keys up to it)."""
     N, Lq, HQ, D = q_all.shape
     HKV = k_pages.shape[1]
     G = HQ // HKV
     scale = 1.0 / math.sqrt(D)
     want = None if heads is None else set((int(n), int(h)) for n, h in heads)
+    pick = None if positions is None else np.unique(np.asarray(list(positions), dtype=np.int64))
     o = np.full((N, Lq, HQ, D), np.nan)
     for n in range(N):
         T = int(seq_lens[n])
+        rows = np.arange(T) if pick is None else pick[(pick >= 0) & (pick < T)]
+        if rows.size == 0:
+            continue
         nb = -(-T // BLOCK)
         pages = np.asarray(block_table[n, :nb], dtype=np.int64)
         for h in range(HQ):
@@ -513,15 +519,15 @@ def prefill(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q_all, tau_m
             K = upcast(k_pages[pages, g], kv_dtype).reshape(nb * BLOCK, D)[:T]
             V = upcast(v_pages[pages, g], kv_dtype).reshape(nb * BLOCK, D)[:T]
             Q = upcast(q_all[n, :T, h], kv_dtype)
-            for t0 in range(0, T, chunk):
-                t1 = min(T, t0 + chunk)
-                tau = np.array([threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a)
-                                for t in range(t0, t1)])
-                S = scale * (Q[t0:t1] @ K[:t1].T)
+            for c0 in range(0, rows.size, chunk):
+                r = rows[c0:c0 + chunk]
+                t1 = int(r[-1]) + 1
+                tau = np.array([threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a) for t in r])
+                S = scale * (Q[r] @ K[:t1].T)
                 St = gate(S, tau[:, None], beta)
-                causal = np.arange(t1)[None, :] <= np.arange(t0, t1)[:, None]
+                causal = np.arange(t1)[None, :] <= r[:, None]
                 St = np.where(causal, St, -np.inf)
                 m = St.max(axis=1, keepdims=True)
                 wts = np.exp(St - m)
-                o[n, t0:t1, h] = (wts @ V[:t1]) / wts.sum(axis=1, keepdims=True)
+                o[n, r, h] = (wts @ V[:t1]) / wts.sum(axis=1, keepdims=True)
     return o

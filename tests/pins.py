@@ -365,6 +365,10 @@ def pin_prefill_bruteforce(E):
     wl = tiny(24, n=1, lens=(70,), h_q=2, h_kv=1, d=4, dtype="f32", mode="learned", beta=2.0, a=0.3)
     q = W.trace_queries(wl, seed=8)
     o = _prefill(E, wl, q)
+    sel = (1, 37, 64)  # the row-selection path computes the chosen rows alone
+    o_sel = E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q, wl.tau_mode, wl.w,
+                      wl.bias, wl.a, wl.beta, positions=sel + (500,))
+    assert np.all(np.isnan(np.delete(o_sel[0], sel, axis=0)))
     s = 1.0 / math.sqrt(wl.d)
     page = [int(x) for x in wl.block_table[0, :2]]
     key = lambda t: [float(x) for x in wl.k_pages[page[t // 64], 0, t % 64]]  # noqa: E731
@@ -382,6 +386,8 @@ def pin_prefill_bruteforce(E):
             den = math.fsum(wts)
             want = [math.fsum(wts[u] * val(u)[c] for u in range(t + 1)) / den for c in range(wl.d)]
             np.testing.assert_allclose(o[0, t, h], want, rtol=1e-11, atol=1e-13)
+            if t in sel:
+                np.testing.assert_allclose(o_sel[0, t, h], want, rtol=1e-11, atol=1e-13)
 
 # --------------------------------------------------------------------------- thresholds
 def pin_threshold_closed_form(E):

@@ -198,3 +198,32 @@ def test_calibrate_rejects():
     assert call(hist=FAKE + 4) == bad
     assert call(hq=30) == bad
     assert call(bins=4096) == _lib.ETA_ERR_UNSUPPORTED    # G = 4: 16384 bins of LDS
+
+
+def test_prefill_rejects():
+    """Host-checkable arguments of eta_prefill fail before any device work."""
+    L = _lib.lib()
+    s = seqs()
+
+    def call(c=None, mode=_lib.ETA_TAU_LEARNED, w=FAKE * 8, b=FAKE * 9, a=0.0, beta=5.0, hq=32, q=FAKE * 7,
+             out=FAKE * 10, err=FAKE * 11, ss=None):
+        c = cache() if c is None else c
+        ss = s if ss is None else ss
+        return L.eta_prefill(ctypes.byref(c), ctypes.byref(ss), q, hq, mode, w, b, a, beta, out, err, None)
+    bad = _lib.ETA_ERR_INVALID_ARGUMENT
+    assert call(w=None) == bad                              # learned needs w
+    assert call(b=None, mode=_lib.ETA_TAU_CALIBRATED) == bad
+    assert call(mode=7) == bad
+    assert call(beta=0.0) == bad
+    assert call(beta=float("inf")) == bad
+    assert call(a=float("nan")) == bad
+    assert call(q=FAKE + 2) == bad
+    assert call(out=FAKE + 4) == bad
+    assert call(out=None) == bad
+    assert call(err=None) == bad
+    assert call(hq=30) == bad
+    assert call(ss=seqs(num_seqs=0)) == bad
+    assert call(c=cache(kv_dtype=_lib.ETA_F32)) == _lib.ETA_ERR_UNSUPPORTED    # bfloat16 matrix cores only
+    assert call(c=cache(head_dim=96)) == _lib.ETA_ERR_UNSUPPORTED
+    assert call(hq=8 * 16) == _lib.ETA_ERR_UNSUPPORTED                         # G = 16
+    assert call(ss=seqs(num_seqs=65536 // 8 + 1)) == _lib.ETA_ERR_UNSUPPORTED  # grid rows

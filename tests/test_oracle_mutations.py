@@ -50,10 +50,10 @@ MUTANTS = {
                                    "hist += wt * np.bincount(bins[i, :t], minlength=num_bins)"),
     "calibration_search_strict": ("        if tail[mid] <= target:\n", "        if tail[mid] < target:\n"),
     "calibration_threshold_strict": ("np.count_nonzero(S[i, :t + 1] >= tau[i])", "np.count_nonzero(S[i, :t + 1] > tau[i])"),
-    "prefill_excludes_diagonal": ("causal = np.arange(t1)[None, :] <= np.arange(t0, t1)[:, None]",
-                                  "causal = np.arange(t1)[None, :] < np.arange(t0, t1)[:, None]"),
-    "prefill_threshold_of_first_row": ("threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a)\n                                for t in range(t0, t1)",
-                                       "threshold(tau_mode, Q[t0], None if w is None else w[h], b_or_c[h], a)\n                                for t in range(t0, t1)"),
+    "prefill_excludes_diagonal": ("causal = np.arange(t1)[None, :] <= r[:, None]",
+                                  "causal = np.arange(t1)[None, :] < r[:, None]"),
+    "prefill_threshold_of_first_row": ("threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a) for t in r",
+                                       "threshold(tau_mode, Q[r[0]], None if w is None else w[h], b_or_c[h], a) for t in r"),
     "prefill_ungated": ("                St = gate(S, tau[:, None], beta)\n", "                St = S\n"),
 }
 
