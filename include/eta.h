@@ -261,7 +261,7 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
  *            (the block reads as zeros and its record is left alone) was met.
  * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise: the products run
  * on the bfloat16 matrix cores), beta > 0 finite, a finite, and
- * num_seqs * num_kv_heads <= 65535. Asynchronous on `stream`. */
+ * num_seqs * num_q_heads <= 65535. Asynchronous on `stream`. */
 eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
                        int tau_mode, const float* w, const float* b_or_c, float a, float beta, float* out,
                        int32_t* err_flag, eta_stream_t stream);

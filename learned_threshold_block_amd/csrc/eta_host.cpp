@@ -382,7 +382,7 @@ eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void*
   st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &d);
   if (st != ETA_OK) return st;
   if (cache->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;  // the matrix-core path is bfloat16
-  if ((int64_t)seqs->num_seqs * d.HKV > 65535) return ETA_ERR_UNSUPPORTED;  // grid rows
+  if ((int64_t)seqs->num_seqs * num_q_heads > 65535) return ETA_ERR_UNSUPPORTED;  // grid rows
   PrefillParams p;
   p.q = q;
   p.HQ = num_q_heads;

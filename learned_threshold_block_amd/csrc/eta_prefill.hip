@@ -47,8 +47,9 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Eight wavefronts per workgroup: with two per SIMD, K and V of a block are
+// read from memory once for 8 x 32 (query, head) rows.
 constexpr int kPfWaves = 8;
-constexpr int kPfThreads = 64 * kPfWaves;
 constexpr float kRescaleLog2 = 8.0f;  // weights stay <= 2^8 between rescales
 
 struct PrefillArgs {
@@ -79,64 +80,98 @@ struct PfLds {
   static constexpr int BUF = KE + VE;
 };
 
-template <int D>
+template <int D, int NTH>
 struct PfTileRegs {
-  static constexpr int KC = 64 * D / 8 / kPfThreads;  // 16-byte K chunks per thread
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int KC = 64 * CPR / NTH;      // K chunks per thread
+  static constexpr int VC = (32 * CPR + NTH - 1) / NTH;  // V (key pair, chunk) items per thread
   uint4 k[KC];
-  uint4 v0, v1;  // rows 2 kp and 2 kp + 1 of V, 8 dims from 8 dc
+  uint4 v0[VC], v1[VC];  // rows 2 kp and 2 kp + 1 of V, 8 dims from 8 dc
 };
 
 // Loads key block kt of (n, g) into registers; rows at or past `rem` (the
 // sequence's end inside this block) read as zeros, as does a block whose page
 // id is out of range.
-template <int D>
-__device__ __forceinline__ void pf_load(PfTileRegs<D>& R, const PrefillArgs& A, int page, bool valid, int rem,
+template <int D, int NTH>
+__device__ __forceinline__ void pf_load(PfTileRegs<D, NTH>& R, const PrefillArgs& A, int page, bool valid, int rem,
                                         int g, int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  using TR = PfTileRegs<D, NTH>;
+  constexpr int CPR = TR::CPR;
   const uint16_t* kt = (const uint16_t*)A.c.k + ((int64_t)page * A.c.HKV + g) * (kBlock * D);
   const uint16_t* vt = (const uint16_t*)A.c.v + ((int64_t)page * A.c.HKV + g) * (kBlock * D);
 #pragma unroll
-  for (int i = 0; i < PfTileRegs<D>::KC; ++i) {
-    const int cidx = tid + i * kPfThreads, row = cidx / CPR, col = (cidx % CPR) * 8;
+  for (int i = 0; i < TR::KC; ++i) {
+    const int cidx = tid + i * NTH, row = cidx / CPR, col = (cidx % CPR) * 8;
     R.k[i] = (valid && row < rem) ? *(const uint4*)(kt + row * D + col) : make_uint4(0, 0, 0, 0);
   }
-  const int kp = tid / CPR, dc = tid % CPR;
-  const bool vown = tid < 32 * CPR;
-  R.v0 = (vown && valid && 2 * kp < rem) ? *(const uint4*)(vt + (2 * kp) * D + dc * 8) : make_uint4(0, 0, 0, 0);
-  R.v1 = (vown && valid && 2 * kp + 1 < rem) ? *(const uint4*)(vt + (2 * kp + 1) * D + dc * 8)
-                                              : make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < TR::VC; ++i) {
+    const int it = tid + i * NTH, kp = it / CPR, dc = it % CPR;
+    const bool own = it < 32 * CPR;
+    R.v0[i] = (own && valid && 2 * kp < rem) ? *(const uint4*)(vt + (2 * kp) * D + dc * 8) : make_uint4(0, 0, 0, 0);
+    R.v1[i] = (own && valid && 2 * kp + 1 < rem) ? *(const uint4*)(vt + (2 * kp + 1) * D + dc * 8)
+                                                 : make_uint4(0, 0, 0, 0);
+  }
 }
 
-template <int D>
-__device__ __forceinline__ void pf_store(const PfTileRegs<D>& R, uint16_t* buf, int tid) {
+template <int D, int NTH>
+__device__ __forceinline__ void pf_store(const PfTileRegs<D, NTH>& R, uint16_t* buf, int tid) {
   using L = PfLds<D>;
-  constexpr int CPR = D / 8;
+  using TR = PfTileRegs<D, NTH>;
+  constexpr int CPR = TR::CPR;
   uint16_t* kl = buf;
   uint16_t* vl = buf + L::KE;
 #pragma unroll
-  for (int i = 0; i < PfTileRegs<D>::KC; ++i) {
-    const int cidx = tid + i * kPfThreads, row = cidx / CPR, col = (cidx % CPR) * 8;
+  for (int i = 0; i < TR::KC; ++i) {
+    const int cidx = tid + i * NTH, row = cidx / CPR, col = (cidx % CPR) * 8;
     *(uint4*)(kl + row * L::KS + col) = R.k[i];
   }
-  if (tid < 32 * CPR) {
-    const int kp = tid / CPR, dc = tid % CPR;
-    const uint32_t a[4] = {R.v0.x, R.v0.y, R.v0.z, R.v0.w};
-    const uint32_t b[4] = {R.v1.x, R.v1.y, R.v1.z, R.v1.w};
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      // dims 8 dc + 2u (low halves) and 8 dc + 2u + 1 (high halves): keys 2 kp, 2 kp + 1
-      const uint32_t even = (a[u] & 0xffffu) | (b[u] << 16);
-      const uint32_t odd = (a[u] >> 16) | (b[u] & 0xffff0000u);
-      *(uint32_t*)(vl + (8 * dc + 2 * u) * L::VS + 2 * kp) = even;
-      *(uint32_t*)(vl + (8 * dc + 2 * u + 1) * L::VS + 2 * kp) = odd;
+  for (int i = 0; i < TR::VC; ++i) {
+    const int it = tid + i * NTH, kp = it / CPR, dc = it % CPR;
+    if (it < 32 * CPR) {
+      const uint32_t a[4] = {R.v0[i].x, R.v0[i].y, R.v0[i].z, R.v0[i].w};
+      const uint32_t b[4] = {R.v1[i].x, R.v1[i].y, R.v1[i].z, R.v1[i].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        // dims 8 dc + 2u (low halves) and 8 dc + 2u + 1 (high halves): keys 2 kp, 2 kp + 1
+        const uint32_t even = (a[u] & 0xffffu) | (b[u] << 16);
+        const uint32_t odd = (a[u] >> 16) | (b[u] & 0xffff0000u);
+        *(uint32_t*)(vl + (8 * dc + 2 * u) * L::VS + 2 * kp) = even;
+        *(uint32_t*)(vl + (8 * dc + 2 * u + 1) * L::VS + 2 * kp) = odd;
+      }
     }
   }
 }
 
-template <int D, int G>
-__global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
+// Gate of one block's logits in place, S -> S sigmoid(beta (S - tau~)) in the
+// units of the accumulators, with keys past the lane's position set to -inf
+// when MASK (lim: the largest key offset 32 t + 8 i + j the lane may see);
+// returns the lane's maximum.
+template <bool MASK>
+__device__ __forceinline__ float pf_gate(f32x16_t* s, float kb, float tb, int lim) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const float v = s[t][e];
+      const float ex = __builtin_amdgcn_exp2f(fmaf(kb, v, tb));
+      float y = v * __builtin_amdgcn_rcpf(1.0f + ex);
+      if (MASK && 32 * t + 8 * (e >> 2) + (e & 3) > lim) y = -__builtin_inff();
+      s[t][e] = y;
+      mx = fmaxf(mx, y);
+    }
+  return mx;
+}
+
+template <int D, int G, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_prefill(PrefillArgs A) {
   using L = PfLds<D>;
-  constexpr int QT = 32 * kPfWaves / G;  // positions per workgroup
+  constexpr int NTH = 64 * NW;
+  constexpr int HW = G < NW ? G : NW;    // heads per workgroup
+  constexpr int HC = G / HW;             // workgroups per (sequence, KV head, tile)
+  constexpr int QT = 32 * (NW / HW);     // positions per workgroup
   constexpr int KSTEPS = D / 16;         // k-steps of S^T = K Q^T
   constexpr int DT = D / 32;             // 32-dim tiles of O^T
   __shared__ __attribute__((aligned(16))) uint16_t lds[2 * L::BUF];
@@ -144,11 +179,12 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HKV = A.c.HKV, MB = A.s.MB, HQ = A.HQ, Lq = A.Lq;
-  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
+  const int hc = blockIdx.y % HC, ng = blockIdx.y / HC;
+  const int n = ng / HKV, g = ng % HKV;
   const int nqt = gridDim.x;
   const int P0 = (nqt - 1 - (int)blockIdx.x) * QT;  // longest rows first
-  const int hl = wave % G, hq = g * G + hl;
-  const int pw0 = P0 + (wave / G) * 32;  // first position of this wavefront
+  const int hl = hc * HW + wave % HW, hq = g * G + hl;
+  const int pw0 = P0 + (wave / HW) * 32;  // first position of this wavefront
   const int qi = lane & 31, hh = lane >> 5;
   const int p = pw0 + qi;                // this lane's position
   int T = A.s.lens[n];
@@ -207,18 +243,20 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
     for (int e = 0; e < 16; ++e) o[m][e] = 0.f;
   float mrun = -__builtin_inff(), lsum = 0.f;
 
-  // ---- key blocks 0 .. last, double-buffered through LDS
+  // ---- key blocks 0 .. last
   const int last = (min(P0 + QT, T) - 1) / kBlock;
   const int wlast = (min(pw0 + 31, T - 1)) / kBlock;  // last block this wavefront needs (pw0 < T or none)
   const bool wactive = pw0 < T;
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
-  PfTileRegs<D> R;
+  // Two LDS slots: block kt + 1 is written into the other one while block kt
+  // is used.
+  PfTileRegs<D, NTH> R;
   {
     const int page = bt[0];
     const bool valid = page >= 0 && page < A.c.num_pages;
     if (!valid && tid == 0) A.err[0] = 1;
-    pf_load<D>(R, A, valid ? page : 0, valid, T, g, tid);
-    pf_store<D>(R, lds, tid);
+    pf_load<D, NTH>(R, A, valid ? page : 0, valid, T, g, tid);
+    pf_store<D, NTH>(R, lds, tid);
   }
   __syncthreads();
   for (int kt = 0; kt <= last; ++kt) {
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
       const int page = bt[kt + 1];
       const bool valid = page >= 0 && page < A.c.num_pages;
       if (!valid && tid == 0) A.err[0] = 1;
-      pf_load<D>(R, A, valid ? page : 0, valid, T - (kt + 1) * kBlock, g, tid);
+      pf_load<D, NTH>(R, A, valid ? page : 0, valid, T - (kt + 1) * kBlock, g, tid);
     }
     const uint16_t* kl = lds + (kt & 1) * L::BUF;
     const uint16_t* vl = kl + L::KE;
@@ -245,22 +283,11 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
         }
       }
       // ---- gate, causal mask, running maximum
-      const bool diag = kt * kBlock + kBlock - 1 > pw0;  // some key may lie after some position
-      float mx = -__builtin_inff();
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float v = s[t][e];
-          const float ex = __builtin_amdgcn_exp2f(fmaf(kb, v, tb));
-          float y = v * __builtin_amdgcn_rcpf(1.0f + ex);
-          if (diag) {
-            const int key = kt * kBlock + 32 * t + 8 * (e >> 2) + 4 * hh + (e & 3);
-            if (key > p) y = -__builtin_inff();
-          }
-          s[t][e] = y;
-          mx = fmaxf(mx, y);
-        }
+      float mx;
+      if (kt * kBlock + kBlock - 1 > pw0)  // the diagonal block: some key may lie after some position
+        mx = pf_gate<true>(s, kb, tb, p - kt * kBlock - 4 * hh);
+      else
+        mx = pf_gate<false>(s, kb, tb, 0);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const bool need = mx > mrun + thr;
       if (__any(need)) {
@@ -304,7 +331,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
         }
       }
     }
-    if (has_next) pf_store<D>(R, lds + ((kt + 1) & 1) * L::BUF, tid);
+    if (has_next) pf_store<D, NTH>(R, lds + ((kt + 1) & 1) * L::BUF, tid);
     __syncthreads();
   }
 
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
 
   // ---- records of the complete blocks whose last position lies in this tile
   const int jb = P0 / kBlock + wave;
-  if (jb * kBlock + kBlock - 1 < P0 + QT && jb * kBlock + kBlock <= T) {
+  if (hc == 0 && jb * kBlock + kBlock - 1 < P0 + QT && jb * kBlock + kBlock <= T) {
     const int page = bt[jb];
     if (page >= 0 && page < A.c.num_pages) {
       const int64_t rec = (int64_t)page * HKV + g;
@@ -341,9 +368,11 @@ __global__ __launch_bounds__(kPfThreads) void k_prefill(PrefillArgs A) {
 
 template <int D, int G>
 hipError_t pf_launch(const PrefillArgs& a, hipStream_t st) {
-  constexpr int QT = 32 * kPfWaves / G;
+  constexpr int NW = kPfWaves;
+  constexpr int HW = G < NW ? G : NW;
+  constexpr int QT = 32 * (NW / HW);
   const int nqt = (a.Lq + QT - 1) / QT;
-  hipLaunchKernelGGL((k_prefill<D, G>), dim3(nqt, a.s.N * a.c.HKV), dim3(kPfThreads), 0, st, a);
+  hipLaunchKernelGGL((k_prefill<D, G, NW>), dim3(nqt, a.s.N * a.c.HKV * (G / HW)), dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
