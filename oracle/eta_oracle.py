@@ -58,6 +58,11 @@ Causal prefill (prefill below): the same gated rule at every position of a
 prompt over the keys up to it, dense (no block pruning), thresholds per
 position.
 
+Comparator screen (Section 4.3, "Comparison with Quest"): per block and KV
+head the coordinate-wise minimum and maximum of the keys, rounded outward to
+float16, and the box bound s sum_i max(q_i kmax_i, q_i kmin_i) in place of the
+geometric one (block_box, quest_bound, decode(bound="quest")).
+
 Parity unpinned: the pages' exact Eq. 7, the body of Algorithm 1 and their
 chunk-local rescue rule are not reproducible from the text; the first two are
 implemented as readings, the last is not implemented.
@@ -193,6 +198,72 @@ def build_sigmas(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, se
     return sig
 
 
+def f16_round_down(x):
+    """Largest float16 value <= x (float64 in, float64 out; -inf below the
+    range, NaN stays NaN)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = x.astype(np.float16)
+        fix = y.astype(np.float64) > x
+        y = np.where(fix, np.nextafter(y, np.float16(-np.inf)), y)
+    return y.astype(np.float64)
+
+
+def f16_round_up(x):
+    """Smallest float16 value >= x (float64 in, float64 out; +inf above the
+    range, NaN stays NaN)."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        y = x.astype(np.float16)
+        fix = y.astype(np.float64) < x
+        y = np.where(fix, np.nextafter(y, np.float16(np.inf)), y)
+    return y.astype(np.float64)
+
+
+def block_box(kb: np.ndarray):
+    """Coordinate-wise bounding box of complete blocks (kb float64 [nb, 64, d]
+    or [64, d]): kmin rounded down and kmax rounded up to float16, so that every
+    key lies inside the stored box (Section 4.3: the per-block minimum and
+    maximum of each coordinate that the Quest comparator keeps). A block with a
+    non-finite key gets NaN in both, which no threshold excludes."""
+    single = kb.ndim == 2
+    if single:
+        kb = kb[None]
+    lo = f16_round_down(kb.min(axis=1))
+    hi = f16_round_up(kb.max(axis=1))
+    bad = ~np.isfinite(kb).all(axis=(1, 2))
+    lo[bad] = np.nan
+    hi[bad] = np.nan
+    return (lo[0], hi[0]) if single else (lo, hi)
+
+
+def build_boxes(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, seq_lens: np.ndarray):
+    """(kmin, kmax) for every complete block of every (sequence, KV head): float64
+    [num_pages][H_KV][d] each, holding float16 values; NaN where there is none."""
+    P, HKV, B, D = k_pages.shape
+    lo = np.full((P, HKV, D), np.nan)
+    hi = np.full((P, HKV, D), np.nan)
+    for n in range(len(seq_lens)):
+        nfull = int(seq_lens[n]) // BLOCK
+        pages = np.asarray(block_table[n, :nfull], dtype=np.int64)
+        for g in range(HKV):
+            for j0 in range(0, nfull, _CHUNK_BLOCKS):
+                pg = pages[j0:j0 + _CHUNK_BLOCKS]
+                lo[pg, g], hi[pg, g] = block_box(upcast(k_pages[pg, g], kv_dtype))
+    return lo, hi
+
+
+def quest_bound(q: np.ndarray, kmin: np.ndarray, kmax: np.ndarray, scale: float) -> np.ndarray:
+    """Box bound of each block: s sum_i max(q_i kmax_i, q_i kmin_i), the largest
+    q.k over the box's corners (Section 4.3). Each term takes the IEEE maximum
+    in which a NaN product (0 times an infinite edge) yields to the other; a
+    NaN record gives a NaN bound."""
+    q = np.asarray(q, dtype=np.float64)
+    with np.errstate(invalid="ignore", over="ignore"):
+        terms = np.fmax(kmax * q[None, :], kmin * q[None, :])
+        return scale * terms.sum(axis=1)
+
+
 def threshold(mode: str, q_h: np.ndarray, w_h, b_h: float, a: float) -> float:
     """Effective threshold tau~ = tau - a.
 
@@ -286,14 +357,15 @@ class DecodeResult:
 def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str,
            w, b_or_c, a: float, beta: float, lwb: int, summaries=None,
            heads: Optional[Iterable] = None, with_output: bool = True,
-           bound: str = "geometric", z: float = 2.0, sigmas=None) -> DecodeResult:
+           bound: str = "geometric", z: float = 2.0, sigmas=None, boxes=None) -> DecodeResult:
     """One ETA decode step for every sequence and query head.
 
     q: [N][H_Q][d] stored values; w: [H_Q][d] (learned mode); b_or_c: [H_Q].
     summaries: (mu, R) from build_summaries, built here if omitted.
     heads: iterable of (n, h) whose output is evaluated (default: all).
-    bound: "geometric" (the sound bound) or "dual" (dual_score with z and the
-    sigma^ records from build_sigmas, built here if omitted)."""
+    bound: "geometric" (the sound bound), "dual" (dual_score with z and the
+    sigma^ records from build_sigmas, built here if omitted) or "quest" (the
+    comparator's box bound with the (kmin, kmax) records from build_boxes)."""
     N, HQ, D = q.shape
     P, HKV, B, D2 = k_pages.shape
     assert D2 == D and B == BLOCK and HQ % HKV == 0
@@ -303,10 +375,12 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
     if summaries is None:
         summaries = build_summaries(k_pages, kv_dtype, block_table, seq_lens)
     mu_all, R_all = summaries
-    if bound not in ("geometric", "dual"):
+    if bound not in ("geometric", "dual", "quest"):
         raise ValueError(f"unknown bound {bound!r}")
     if bound == "dual" and sigmas is None:
         sigmas = build_sigmas(k_pages, kv_dtype, block_table, seq_lens)
+    if bound == "quest" and boxes is None:
+        boxes = build_boxes(k_pages, kv_dtype, block_table, seq_lens)
     qf = upcast(q, kv_dtype)
     want = None if heads is None else set((int(n), int(h)) for n, h in heads)
 
@@ -326,6 +400,8 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
             if bound == "dual":
                 ub = dual_score(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g],
                                 sigmas[pages[:nfull], g], scale, z)
+            elif bound == "quest":
+                ub = quest_bound(qf[n, h], boxes[0][pages[:nfull], g], boxes[1][pages[:nfull], g], scale)
             else:
                 ub = block_bound(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g], scale)
             ubs[n, h, :nfull] = ub

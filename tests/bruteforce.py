@@ -6,7 +6,9 @@ over every key with the `math` module (fsum, exact float16 rounding through
 It follows "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888),
 Sections 2.2, 3.1, 3.2, 4.8, F.1, F.4 and G.1, with the same readings as the
 oracle (geometric bound about the fp16 centroid, global top-1 rescue; the
-optional dual score as the smaller of that bound and s (q . mu^ + z ||q * sigma^||)).
+optional dual score as the smaller of that bound and s (q . mu^ + z ||q * sigma^||);
+the Quest comparator's box bound of Section 4.3 over outward-rounded float16
+coordinate extrema).
 """
 from __future__ import annotations
 
@@ -77,6 +79,47 @@ def deviation(rows):
     return out
 
 
+def _f16_directed(x: float, up: bool) -> float:
+    """float16 value nearest to x on the requested side, through the bit
+    pattern: struct rounds to nearest, then one step of the pattern fixes the
+    side (patterns of one sign order like their magnitudes)."""
+    if math.isnan(x):
+        return math.nan
+    try:
+        bits = struct.unpack("<H", struct.pack("<e", x))[0]
+    except OverflowError:
+        bits = 0x7C00 if x > 0 else 0xFC00
+    y = struct.unpack("<e", struct.pack("<H", bits))[0]
+    if (up and y < x) or (not up and y > x):
+        if bits & 0x7FFF == 0:
+            bits = 0x0001 if up else 0x8001
+        elif (bits & 0x8000 != 0) == up:
+            bits -= 1
+        else:
+            bits += 1
+        y = struct.unpack("<e", struct.pack("<H", bits))[0]
+    return y
+
+
+def box(rows):
+    """(kmin, kmax) of one block: per coordinate the least and greatest key
+    value, rounded outward to float16; NaN for a block with a non-finite key."""
+    d = len(rows[0])
+    if not all(math.isfinite(x) for r in rows for x in r):
+        return [math.nan] * d, [math.nan] * d
+    lo = [_f16_directed(min(r[c] for r in rows), up=False) for c in range(d)]
+    hi = [_f16_directed(max(r[c] for r in rows), up=True) for c in range(d)]
+    return lo, hi
+
+
+def _greater(a: float, b: float) -> float:
+    if math.isnan(a):
+        return b
+    if math.isnan(b):
+        return a
+    return max(a, b)
+
+
 def _smaller(a: float, b: float) -> float:
     if math.isnan(a):
         return b
@@ -113,6 +156,8 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
             recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
             devs = [deviation([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
                 if bound == "dual" else None
+            boxes = [box([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
+                if bound == "quest" else None
             loaded = set()
             for hh in range(G):
                 h = g * G + hh
@@ -128,6 +173,17 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                     mu, R = recs[j]
                     dot = math.fsum(qh[c] * mu[c] for c in range(D))
                     ub = s * (dot + qn * R)
+                    if bound == "quest":
+                        lo, hi = boxes[j]
+                        terms = []
+                        for c in range(D):
+                            with_nan = [qh[c] * hi[c] if not (qh[c] == 0 and math.isinf(hi[c])) else math.nan,
+                                        qh[c] * lo[c] if not (qh[c] == 0 and math.isinf(lo[c])) else math.nan]
+                            terms.append(_greater(*with_nan))
+                        try:
+                            ub = math.nan if any(math.isnan(x) for x in terms) else s * math.fsum(terms)
+                        except ValueError:  # +inf and -inf terms
+                            ub = math.nan
                     if bound == "dual":
                         try:
                             spread = math.sqrt(math.fsum((qh[c] * devs[j][c]) ** 2 for c in range(D)))

@@ -226,6 +226,76 @@ def pin_dual_bruteforce(E, seeds=range(3)):
             assert int(res.union[n, g]) == u
 
 
+# --------------------------------------------------------------------------- Quest comparator
+def pin_quest_directed_rounding(E):
+    """float16 rounding toward -inf / +inf, by hand: spacing 2^-10 at 1, the
+    largest finite 65504, the smallest subnormal 2^-24."""
+    x = np.array([1.0001, -1.0001, 1.0, 0.5, -3.25, 65504.0, 70000.0, -70000.0, 2.0 ** -30, -2.0 ** -30, 0.0])
+    down = [1.0, -1.0 - 2.0 ** -10, 1.0, 0.5, -3.25, 65504.0, 65504.0, -np.inf, 0.0, -2.0 ** -24, 0.0]
+    up = [1.0 + 2.0 ** -10, -1.0, 1.0, 0.5, -3.25, 65504.0, np.inf, -65504.0, 2.0 ** -24, 0.0, 0.0]
+    assert np.array_equal(E.f16_round_down(x), np.array(down))
+    assert np.array_equal(E.f16_round_up(x), np.array(up))
+    assert np.isnan(E.f16_round_down(np.nan)) and np.isnan(E.f16_round_up(np.nan))
+
+
+def pin_quest_box_corners(E, seed=3, trials=50):
+    """The box bound is the best corner of the stored box (all 2^d corners
+    enumerated, d = 4), never below any key's logit, equal to it for a block
+    of one repeated float16-exact key; the stored box is the independent
+    brute force's outward rounding of the coordinate extrema."""
+    import itertools
+    rng = np.random.default_rng(seed)
+    d = 4
+    s = 1.0 / math.sqrt(d)
+    for _ in range(trials):
+        kb = W.bf16_bits_to_f32(W.f32_to_bf16_bits(rng.normal(0, 2, (64, d)).astype(np.float32))).astype(np.float64)
+        q = rng.normal(0, 1, d)
+        lo, hi = E.block_box(kb)
+        blo, bhi = bruteforce.box([list(map(float, r)) for r in kb])
+        assert np.array_equal(lo, blo) and np.array_equal(hi, bhi)
+        assert np.all(lo <= kb.min(axis=0)) and np.all(hi >= kb.max(axis=0))
+        ub = float(E.quest_bound(q, lo[None], hi[None], s)[0])
+        corners = max(s * sum(q[c] * (hi[c] if pick[c] else lo[c]) for c in range(d))
+                      for pick in itertools.product((0, 1), repeat=d))
+        assert abs(ub - corners) <= 1e-12 * max(1.0, abs(corners))
+        assert ub >= s * float((kb @ q).max()) - 1e-12
+    k = np.array([0.5, -1.25, 3.0, 0.0])
+    lo, hi = E.block_box(np.tile(k, (64, 1)))
+    assert np.array_equal(lo, k) and np.array_equal(hi, k)
+    assert float(E.quest_bound(np.array([1.0, 2.0, -1.0, 4.0]), lo[None], hi[None], 1.0)[0]) == 0.5 - 2.5 - 3.0
+    bad = np.zeros((64, d))
+    bad[5, 2] = np.inf
+    lo, hi = E.block_box(bad)
+    assert np.all(np.isnan(lo)) and np.all(np.isnan(hi))
+    assert np.isnan(E.quest_bound(np.ones(d), lo[None], hi[None], s)[0])
+
+
+def pin_quest_bruteforce(E, seeds=range(3)):
+    """Quest-screen sets, bounds and outputs equal the per-key brute force."""
+    variants = [dict(n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(320,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated"),
+                dict(n=2, lens=(130, 256), h_q=2, h_kv=2, d=8, dtype="bf16", mode="calibrated", lwb=1)]
+    for seed in seeds:
+        wl = tiny(80 + seed, **variants[seed % len(variants)])
+        # thresholds at the median box bound of each head (a number only)
+        zero = _decode(E, wl, bias=np.zeros(wl.h_q, np.float32), bound="quest", with_output=False)
+        wl.bias = np.array([np.nanmedian(zero.ub[:, h] - zero.tau[:, h, None]) for h in range(wl.h_q)],
+                           dtype=np.float32)
+        res = _decode(E, wl, bound="quest")
+        assert 0 < res.admitted.sum() < res.admitted.size
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb, bound="quest")
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, n, h, got, r["admitted"])
+            assert bool(res.rescued[n, h]) == r["rescued"]
+            np.testing.assert_allclose(res.ub[n, h, :len(r["ub"])], r["ub"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+
+
 # --------------------------------------------------------------------------- offline calibration
 def _grid_trace(E, T=8, d=4):
     """One sequence whose scaled scores are S_ts = s exactly: q_t = (sqrt(d), 0, ...)
@@ -617,4 +687,5 @@ ALL_PINS = [
     pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
     pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
+    pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,
 ]

@@ -54,6 +54,11 @@ MUTANTS = {
                                   "causal = np.arange(t1)[None, :] < r[:, None]"),
     "prefill_threshold_of_first_row": ("threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a) for t in r",
                                        "threshold(tau_mode, Q[r[0]], None if w is None else w[h], b_or_c[h], a) for t in r"),
+    "quest_round_down_to_nearest": ("        fix = y.astype(np.float64) > x\n",
+                                    "        fix = np.zeros(np.shape(x), dtype=bool)\n"),
+    "quest_box_min_rounded_up": ("lo = f16_round_down(kb.min(axis=1))", "lo = f16_round_up(kb.min(axis=1))"),
+    "quest_upper_corner_only": ("terms = np.fmax(kmax * q[None, :], kmin * q[None, :])", "terms = kmax * q[None, :]"),
+    "quest_nonfinite_block_kept": ("    lo[bad] = np.nan\n", "    lo[bad] = 0.0\n"),
     "prefill_ungated": ("                St = gate(S, tau[:, None], beta)\n", "                St = S\n"),
 }
 
