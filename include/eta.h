@@ -58,7 +58,7 @@ typedef enum {
 enum { ETA_F32 = 0, ETA_BF16 = 1 };                 /* K/V/q element type */
 enum { ETA_TAU_LEARNED = 0, ETA_TAU_CALIBRATED = 1 }; /* threshold mode */
 enum { ETA_PHASE_ALL = -1, ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
-enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1 }; /* block screen, see eta_screen_opts */
+enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2 }; /* block screen, see eta_screen_opts */
 
 /* Paged KV cache plus its per-block records (caller-owned device buffers).
  *   k_pages, v_pages : [num_pages][num_kv_heads][block_size][head_dim] of
@@ -75,6 +75,13 @@ enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1 }; /* block screen, see eta_s
  *                      mean), rounded to nearest even; +inf where not finite
  *                      (Section F.1; only the dual screen reads it). When not
  *                      NULL, the record builders fill it too.
+ *   kmin, kmax       : NULL (both), or [num_pages][num_kv_heads][head_dim]
+ *                      float16 bit patterns each, 16-byte aligned: per key
+ *                      coordinate the least value of the block rounded down
+ *                      and the greatest rounded up to float16, NaN in both for
+ *                      a block holding a non-finite key (the per-block extrema
+ *                      of the comparator of Section 4.3; only ETA_BOUND_QUEST
+ *                      reads them). When not NULL, the record builders fill them.
  * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
 typedef struct {
   int kv_dtype;
@@ -87,6 +94,8 @@ typedef struct {
   uint16_t* mu;
   float* radius;
   uint16_t* sigma;
+  uint16_t* kmin;
+  uint16_t* kmax;
 } eta_cache;
 
 /* Sequences of a batch.
@@ -157,6 +166,12 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
  *                         best key lies more than z deviations out can be
  *                         missed. Needs cache->sigma; z finite and >= 0
  *                         (2.0 in the paper's B.1 tables).
+ *   ETA_BOUND_QUEST     : score s sum_i max(q_i kmax_i, q_i kmin_i), the best
+ *                         corner of the block's stored key box: the comparator
+ *                         bound of Section 4.3 (sound, like the geometric one;
+ *                         each term takes the IEEE maximum, in which a NaN
+ *                         product yields to the other). Needs cache->kmin and
+ *                         cache->kmax.
  * The score also ranks blocks for the top-1 rescue. */
 typedef struct {
   int bound;
@@ -166,7 +181,8 @@ typedef struct {
 /* eta_decode / eta_decode_phase with a screen choice: phase is ETA_PHASE_ALL
  * for the whole step or one ETA_PHASE_*; screen NULL means the geometric bound.
  * Returns ETA_ERR_INVALID_ARGUMENT for an unknown bound, a negative or
- * non-finite z, or the dual bound without cache->sigma. */
+ * non-finite z, the dual bound without cache->sigma, or the comparator bound
+ * without cache->kmin and cache->kmax. */
 eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache,
                          const eta_seqs* seqs, const void* q, int num_q_heads, int tau_mode,
                          const float* w, const float* b_or_c, float a, float beta, int lwb,

@@ -16,7 +16,7 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
+    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
     ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ALL, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
     ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
@@ -61,6 +61,8 @@ class Cache:
     mu: torch.Tensor       # float16 [num_pages][H_KV][d]
     radius: torch.Tensor   # float32 [num_pages][H_KV]
     sigma: Optional[torch.Tensor] = None  # float16 [num_pages][H_KV][d], for the dual screen
+    kmin: Optional[torch.Tensor] = None   # float16 [num_pages][H_KV][d], key box (comparator screen)
+    kmax: Optional[torch.Tensor] = None
 
     def __post_init__(self):
         _need(self.k_pages, "k_pages")
@@ -75,19 +77,26 @@ class Cache:
         P, H, B, D = self.k_pages.shape
         if tuple(self.mu.shape) != (P, H, D) or tuple(self.radius.shape) != (P, H):
             raise ValueError("mu must be [num_pages][H_KV][d] and radius [num_pages][H_KV]")
-        if self.sigma is not None:
-            _need(self.sigma, "sigma", torch.float16, dev)
-            if tuple(self.sigma.shape) != (P, H, D):
-                raise ValueError("sigma must be [num_pages][H_KV][d]")
+        for name in ("sigma", "kmin", "kmax"):
+            t = getattr(self, name)
+            if t is not None:
+                _need(t, name, torch.float16, dev)
+                if tuple(t.shape) != (P, H, D):
+                    raise ValueError(f"{name} must be [num_pages][H_KV][d]")
+        if (self.kmin is None) != (self.kmax is None):
+            raise ValueError("kmin and kmax go together")
 
     @classmethod
-    def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False):
+    def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False,
+              with_box=False):
         k = torch.zeros(num_pages, num_kv_heads, BLOCK, head_dim, dtype=dtype, device=device)
         v = torch.zeros_like(k)
         mu = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.float16, device=device)
         r = torch.zeros(num_pages, num_kv_heads, dtype=torch.float32, device=device)
         sig = torch.zeros_like(mu) if with_sigma else None
-        return cls(k, v, mu, r, sig)
+        lo = torch.zeros_like(mu) if with_box else None
+        hi = torch.zeros_like(mu) if with_box else None
+        return cls(k, v, mu, r, sig, lo, hi)
 
     @property
     def kv_dtype(self) -> int:
@@ -104,7 +113,8 @@ class Cache:
     def c_struct(self) -> _lib.EtaCacheC:
         P, H, B, D = self.k_pages.shape
         return _lib.EtaCacheC(self.kv_dtype, D, H, B, P, _ptr(self.k_pages), _ptr(self.v_pages),
-                              _ptr(self.mu), _ptr(self.radius), _ptr(self.sigma))
+                              _ptr(self.mu), _ptr(self.radius), _ptr(self.sigma), _ptr(self.kmin),
+                              _ptr(self.kmax))
 
 
 def _seqs(seq_lens: torch.Tensor, block_table: torch.Tensor, device) -> _lib.EtaSeqsC:
@@ -151,7 +161,8 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
            stream=None, bound: str = "geometric", z: float = 2.0) -> torch.Tensor:
     """One ETA decode step; returns out [num_seqs][H_Q][d] float32.
     With `phase` set, runs only that phase (screen, attend or merge).
-    bound: "geometric" or "dual" (needs cache.sigma; z deviations)."""
+    bound: "geometric", "dual" (needs cache.sigma; z deviations) or "quest"
+    (the comparator's box bound; needs cache.kmin and cache.kmax)."""
     dev = cache.k_pages.device
     _need(q, "q", cache.k_pages.dtype, dev)
     N, HQ, D = q.shape
@@ -173,8 +184,8 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
             _check(_lib.lib().eta_decode(*args), "eta_decode")
         else:
             _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
-    elif bound == "dual":
-        opts = _lib.EtaScreenOptsC(_lib.ETA_BOUND_DUAL, float(z))
+    elif bound in ("dual", "quest"):
+        opts = _lib.EtaScreenOptsC(_lib.ETA_BOUND_DUAL if bound == "dual" else _lib.ETA_BOUND_QUEST, float(z))
         ph = _lib.ETA_PHASE_ALL if phase is None else int(phase)
         _check(_lib.lib().eta_decode_ex(ph, ctypes.byref(opts), *args), "eta_decode_ex")
     else:

@@ -28,6 +28,7 @@ ETA_PHASE_ATTEND = 1
 ETA_PHASE_MERGE = 2
 ETA_BOUND_GEOMETRIC = 0
 ETA_BOUND_DUAL = 1
+ETA_BOUND_QUEST = 2
 
 EXPORTS = (
     "eta_build_block_summaries",
@@ -55,6 +56,8 @@ class EtaCacheC(ctypes.Structure):
         ("mu", ctypes.c_void_p),
         ("radius", ctypes.c_void_p),
         ("sigma", ctypes.c_void_p),
+        ("kmin", ctypes.c_void_p),
+        ("kmax", ctypes.c_void_p),
     ]
 
 

@@ -239,6 +239,21 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
+// float16 bits of the nearest value at or below (up = false) or at or above
+// (up = true) a finite float32 x: round to nearest, then one step of the bit
+// pattern if that landed on the wrong side (patterns of one sign order like
+// their magnitudes; beyond the range: +-65504 or +-inf as the side requires).
+__device__ __forceinline__ uint16_t f32_to_f16_dir(float x, bool up) {
+  uint16_t h = f64_to_f16_rne((double)x);
+  const float back = f16_bits_to_f32(h);
+  if (up ? back < x : back > x) {
+    if ((h & 0x7fffu) == 0) h = up ? 0x0001u : 0x8001u;
+    else if (((h & 0x8000u) != 0) == up) h = (uint16_t)(h - 1u);
+    else h = (uint16_t)(h + 1u);
+  }
+  return h;
+}
+
 // Smallest float32 >= x (x >= 0), +inf for non-finite input.
 __device__ __forceinline__ float f64_to_f32_up(double x) {
   if (!(x < 1e300)) return __builtin_inff();

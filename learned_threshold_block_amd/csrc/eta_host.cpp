@@ -65,8 +65,9 @@ eta_status check_cache(const eta_cache* c) {
     return ETA_ERR_INVALID_ARGUMENT;
   if (!c->k_pages || !c->v_pages || !c->mu || !c->radius) return ETA_ERR_INVALID_ARGUMENT;
   if (!aligned(c->k_pages, 16) || !aligned(c->v_pages, 16) || !aligned(c->mu, 16) ||
-      !aligned(c->radius, 4) || !aligned(c->sigma, 16))
+      !aligned(c->radius, 4) || !aligned(c->sigma, 16) || !aligned(c->kmin, 16) || !aligned(c->kmax, 16))
     return ETA_ERR_INVALID_ARGUMENT;
+  if ((c->kmin == nullptr) != (c->kmax == nullptr)) return ETA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
   if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
   if ((int64_t)c->num_pages * c->num_kv_heads > (int64_t)1 << 31) return ETA_ERR_UNSUPPORTED;
@@ -94,6 +95,8 @@ CacheView view_of(const eta_cache* c) {
   v.mu = c->mu;
   v.radius = c->radius;
   v.sigma = c->sigma;
+  v.kmin = c->kmin;
+  v.kmax = c->kmax;
   return v;
 }
 
@@ -169,14 +172,19 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
                    int lwb, int block_size, float* out, void* workspace, size_t ws_bytes, Prepared* P) {
   eta_status st = check_cache(cache);
   if (st != ETA_OK) return st;
-  P->p.dual = 0;
+  P->p.bound = 0;
   P->p.z = 0.f;
   if (screen) {
-    if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL) return ETA_ERR_INVALID_ARGUMENT;
+    if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL && screen->bound != ETA_BOUND_QUEST)
+      return ETA_ERR_INVALID_ARGUMENT;
     if (screen->bound == ETA_BOUND_DUAL) {
       if (!cache->sigma || !isfinite(screen->z) || !(screen->z >= 0.f)) return ETA_ERR_INVALID_ARGUMENT;
-      P->p.dual = 1;
+      P->p.bound = 1;
       P->p.z = screen->z;
+    }
+    if (screen->bound == ETA_BOUND_QUEST) {
+      if (!cache->kmin || !cache->kmax) return ETA_ERR_INVALID_ARGUMENT;
+      P->p.bound = 2;
     }
   }
   st = check_seqs(seqs);

@@ -74,6 +74,8 @@ struct CacheView {
   uint16_t* mu;
   float* radius;
   uint16_t* sigma;  // may be null
+  uint16_t* kmin;   // may be null (both or neither)
+  uint16_t* kmax;
 };
 
 struct SeqView {
@@ -91,7 +93,7 @@ struct DecodeParams {
   int lwb;
   float* out;
   int deterministic;  // static work split and claims: bitwise-reproducible results
-  int dual;           // dual screen (geometric bound tightened by z deviations)
+  int bound;          // 0 geometric, 1 dual (tightened by z deviations), 2 comparator box bound
   float z;
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };

@@ -361,7 +361,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const int64_t rec = (int64_t)page * HKV + g;
       const uint16_t* tile = (const uint16_t*)A.c.k + rec * kBlock * D;
       build_record<Bf16, D>(tile, nullptr, A.c.mu + rec * D, A.c.radius + rec,
-                            A.c.sigma ? A.c.sigma + rec * D : nullptr, lane);
+                            A.c.sigma ? A.c.sigma + rec * D : nullptr, A.c.kmin ? A.c.kmin + rec * D : nullptr,
+                            A.c.kmax ? A.c.kmax + rec * D : nullptr, lane);
     }
   }
 }

@@ -1,6 +1,7 @@
 // Block record builder shared by the record kernels and the prompt pass:
 // centroid mu^ (float16, nearest even) and radius R^ (float32, rounded up) of
-// one complete 64-token key block, and optionally its coordinate deviation.
+// one complete 64-token key block, and optionally its coordinate deviation and
+// its coordinate-wise key box (the comparator's record).
 //
 // "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Section 3.2
 // and Appendix F.1: the decode screen reads one compact record per block and
@@ -28,15 +29,24 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
 // non-null, row 63 is read from it instead of the tile. Lanes own columns;
 // the rows are read twice (sums, then distances and deviations), which keeps
 // the register footprint small enough for eight wavefronts per SIMD. Writes
-// the centroid and radius, and the coordinate deviation if sig_out is not null.
+// the centroid and radius, the coordinate deviation if sig_out is not null,
+// and the key box if kmin_out is not null: per coordinate the least key value
+// rounded down and the greatest rounded up to float16 (Section 4.3, the
+// comparator's per-block extrema; NaN for a block with a non-finite key).
 template <typename T, int D>
 __device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
-                             uint16_t* mu_out, float* r_out, uint16_t* sig_out, int lane) {
+                             uint16_t* mu_out, float* r_out, uint16_t* sig_out, uint16_t* kmin_out,
+                             uint16_t* kmax_out, int lane) {
   constexpr int CPL = D / 64;  // columns per lane: 2 (D=128) or 1 (D=64)
   double sum[CPL];
+  float cmin[CPL], cmax[CPL];
   bool finite = true;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) sum[c] = 0.0;
+  for (int c = 0; c < CPL; ++c) {
+    sum[c] = 0.0;
+    cmin[c] = __builtin_inff();
+    cmax[c] = -__builtin_inff();
+  }
   for (int r = 0; r < kBlock; ++r) {
     const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
 #pragma unroll
@@ -44,6 +54,8 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
       const float x = load_elem<T>(row + lane * CPL + c);
       finite = finite && (fabsf(x) <= 3.4028234663852886e38f);
       sum[c] += (double)x;
+      cmin[c] = fminf(cmin[c], x);
+      cmax[c] = fmaxf(cmax[c], x);
     }
   }
   uint16_t h[CPL];
@@ -57,6 +69,14 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     ok = ok && ((h[c] & 0x7c00u) != 0x7c00u);
   }
   const bool all_ok = __all(ok);
+  if (kmin_out) {
+    const bool all_finite = __all(finite);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      kmin_out[lane * CPL + c] = all_finite ? f32_to_f16_dir(cmin[c], false) : (uint16_t)0x7e00u;
+      kmax_out[lane * CPL + c] = all_finite ? f32_to_f16_dir(cmax[c], true) : (uint16_t)0x7e00u;
+    }
+  }
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     if (!all_ok) h[c] = 0;

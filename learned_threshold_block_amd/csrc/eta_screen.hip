@@ -10,6 +10,8 @@
 //   rescue    block with the largest bound when a head admits nothing (3.2, F.4)
 //   dual      optionally the bound is tightened to min(bound, s (q.mu^ + z ||q sigma^||))
 //             with the per-block coordinate deviation sigma^ (Section 3.1, F.1)
+//   box       or, as the comparator of Section 4.3, replaced by the best corner
+//             s sum_i max(q_i kmax_i, q_i kmin_i) of the block's key box
 //   counts    per-head blocks, union blocks, attended tokens (F.4)
 //
 // k_screen: one wavefront per 64 consecutive blocks of one (sequence, KV head).
@@ -58,8 +60,10 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-template <typename T, int D, int G, bool DUAL>
+// MODE: 0 geometric bound, 1 dual score, 2 comparator box bound.
+template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
+  constexpr bool DUAL = MODE == 1, BOX = MODE == 2;
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
@@ -120,7 +124,9 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   const bool lvalid = jl < nblk && page_l >= 0 && page_l < A.c.num_pages;
   const bool complete = jl < nfull && lvalid;
   // records through buffer loads: an invalid block reads zeros, without a branch
-  const auto mu_rsrc = make_rsrc(A.c.mu, (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
+  // (the box bound reads the key box's lower corner here and its upper one below)
+  const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : (const void*)A.c.mu,
+                                 (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
   const auto r_rsrc = make_rsrc(A.c.radius, (uint32_t)((int64_t)A.c.num_pages * HKV * 4));
   uint4 raw[NI];
 #pragma unroll
@@ -132,11 +138,13 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
   }
   const uint32_t roff = complete ? (uint32_t)(((int64_t)page_l * HKV + g) * 4) : kOutOfRange;
-  const float R = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rsrc, roff, 0, 0));
-  // dual screen: coordinate deviations, laid out like the centroids
-  uint4 sraw[DUAL ? NI : 1];
-  if constexpr (DUAL) {
-    const auto s_rsrc = make_rsrc(A.c.sigma, (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
+  const float R = BOX ? 0.f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rsrc, roff, 0, 0));
+  // dual screen: coordinate deviations; box bound: upper corners (both laid
+  // out like the centroids)
+  uint4 sraw[DUAL || BOX ? NI : 1];
+  if constexpr (DUAL || BOX) {
+    const auto s_rsrc = make_rsrc(BOX ? (const void*)A.c.kmax : (const void*)A.c.sigma,
+                                  (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int j = j0 + RPI * i + r;
@@ -181,12 +189,29 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       mv[2 * e] = f16_bits_to_f32((uint16_t)(w4[e] & 0xffffu));
       mv[2 * e + 1] = f16_bits_to_f32((uint16_t)(w4[e] >> 16));
     }
+    if constexpr (BOX) {  // mv: lower corner; sum of max(q kmax, q kmin) per lane
+      const uint32_t u4[4] = {sraw[i].x, sraw[i].y, sraw[i].z, sraw[i].w};
+      float xv[8];
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float a = 0.f;
+      for (int e = 0; e < 4; ++e) {
+        xv[2 * e] = f16_bits_to_f32((uint16_t)(u4[e] & 0xffffu));
+        xv[2 * e + 1] = f16_bits_to_f32((uint16_t)(u4[e] >> 16));
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = fmaf(qf[h][e], mv[e], a);
-      pd[h][i] = a;
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a += fmaxf(qf[h][e] * xv[e], qf[h][e] * mv[e]);
+        pd[h][i] = a;
+      }
+    } else {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a = fmaf(qf[h][e], mv[e], a);
+        pd[h][i] = a;
+      }
     }
     if constexpr (DUAL) {
       const uint32_t s4[4] = {sraw[i].x, sraw[i].y, sraw[i].z, sraw[i].w};
@@ -220,7 +245,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   float ub[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
-    ub[h] = A.p.scale * (pd[h][0] + qn[h] * R);
+    ub[h] = BOX ? A.p.scale * pd[h][0] : A.p.scale * (pd[h][0] + qn[h] * R);
     if constexpr (DUAL) {  // the smaller of the bound and the z-deviation estimate (a NaN side yields)
       const float est = A.p.scale * (pd[h][0] + A.p.z * sqrtf(ps[h][0]));
       ub[h] = fminf(ub[h], est);
@@ -558,8 +583,9 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
                        const Ws& ws, hipStream_t st) {
   ScreenArgs a{c, s, p, d, ws};
   dim3 grid((d.NT + 3) / 4, d.S);
-  if (p.dual) hipLaunchKernelGGL((k_screen<T, D, G, true>), grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL((k_screen<T, D, G, false>), grid, dim3(256), 0, st, a);
+  if (p.bound == 1) hipLaunchKernelGGL((k_screen<T, D, G, 1>), grid, dim3(256), 0, st, a);
+  else if (p.bound == 2) hipLaunchKernelGGL((k_screen<T, D, G, 2>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_screen<T, D, G, 0>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

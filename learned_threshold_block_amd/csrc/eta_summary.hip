@@ -36,7 +36,8 @@ __global__ __launch_bounds__(256) void k_build(CacheView c, SeqView s) {
   if (page < 0 || page >= c.num_pages) return;
   const int64_t rec = (int64_t)page * c.HKV + g;
   const auto* tile = (const typename T::Stored*)c.k + rec * kBlock * D;
-  build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr, lane);
+  build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
+                     c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr, lane);
 }
 
 template <typename T, int D>
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(64) void k_append(CacheView c, SeqView s, const voi
   }
   if (row == kBlock - 1) {
     const St* tile = (const St*)c.kw + rec * kBlock * D;
-    build_record<T, D>(tile, kn, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr, lane);
+    build_record<T, D>(tile, kn, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
+                       c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr, lane);
   }
 }
 

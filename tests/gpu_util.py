@@ -24,14 +24,17 @@ def log(msg: str) -> None:
 class Dev:
     """A workload's inputs on the GPU."""
 
-    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False):
+    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False, with_box=False):
         self.wl = wl
         self.device = torch.device(device)
-        sig = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device) if with_sigma else None
+        z16 = lambda: torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device)  # noqa: E731
+        sig = z16() if with_sigma else None
+        lo, hi = (z16(), z16()) if with_box else (None, None)
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, device),
                                eta.upload(wl.v_pages, wl.kv_dtype, device),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device),
-                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device), sig)
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device), sig,
+                               lo, hi)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(device)
         self.q = eta.upload(wl.q, wl.kv_dtype, device)
@@ -66,19 +69,28 @@ class Dev:
     def sigma_bits(self):
         return self.cache.sigma.cpu().view(torch.int16).numpy().view(np.uint16)
 
+    def box_bits(self):
+        f = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
+        return f(self.cache.kmin), f(self.cache.kmax)
+
 
 def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=None, beta=None, lwb=None,
                   bound="geometric", z=2.0):
-    """summaries: (mu, R) or, for the dual screen, (mu, R, sigma)."""
+    """summaries: (mu, R); for the dual screen (mu, R, sigma); for the
+    comparator's box bound (mu, R, kmin, kmax)."""
     sig = None
+    boxes = None
     if summaries is not None and len(summaries) == 3:
         sig = summaries[2]
+        summaries = summaries[:2]
+    if summaries is not None and len(summaries) == 4:
+        boxes = summaries[2:]
         summaries = summaries[:2]
     return E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
                     wl.tau_mode if tau_mode is None else tau_mode, wl.w,
                     wl.bias if bias is None else bias, wl.a if a is None else a,
                     wl.beta if beta is None else beta, wl.lwb if lwb is None else lwb,
-                    summaries=summaries, heads=heads, bound=bound, z=z, sigmas=sig)
+                    summaries=summaries, heads=heads, bound=bound, z=z, sigmas=sig, boxes=boxes)
 
 
 def check_sets_and_counts(wl, res, st):

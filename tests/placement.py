@@ -19,9 +19,10 @@ import workloads as W
 BLOCK = 64
 
 
-def _bounds(wl, mu, R, sigma=None, z=2.0):
+def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None):
     """ub[n][h][j] for complete blocks (NaN elsewhere), tau offsets per (n, h).
-    With sigma, the dual screen score instead of the geometric bound."""
+    With sigma, the dual screen score instead of the geometric bound; with
+    boxes (kmin, kmax), the comparator's box bound."""
     N, HQ, D = wl.q.shape
     G = wl.group
     s = 1.0 / math.sqrt(D)
@@ -32,7 +33,9 @@ def _bounds(wl, mu, R, sigma=None, z=2.0):
         pages = wl.block_table[n, :nfull]
         for h in range(HQ):
             g = h // G
-            if sigma is None:
+            if boxes is not None:
+                ub[n, h, :nfull] = E.quest_bound(qf[n, h], boxes[0][pages, g], boxes[1][pages, g], s)
+            elif sigma is None:
                 ub[n, h, :nfull] = E.block_bound(qf[n, h], mu[pages, g], R[pages, g], s)
             else:
                 ub[n, h, :nfull] = E.dual_score(qf[n, h], mu[pages, g], R[pages, g], sigma[pages, g], s, z)
@@ -46,13 +49,17 @@ def _bounds(wl, mu, R, sigma=None, z=2.0):
 def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound: str = "geometric",
           z: float = 2.0):
     """Set wl.bias in place; returns the oracle summaries of the final cache
-    ((mu, R), or (mu, R, sigma) for the dual screen)."""
+    ((mu, R), (mu, R, sigma) for the dual screen, (mu, R, kmin, kmax) for the
+    comparator's box bound)."""
     mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
         if summaries is None else summaries[:2]
     sigma = None
+    boxes = None
     if bound == "dual":
         sigma = E.build_sigmas(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens)
-    ub, off = _bounds(wl, mu, R, sigma, z)
+    if bound == "quest":
+        boxes = E.build_boxes(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens)
+    ub, off = _bounds(wl, mu, R, sigma, z, boxes)
     HQ = wl.h_q
     bias = np.zeros(HQ, dtype=np.float32)
     for h in range(HQ):
@@ -74,6 +81,8 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         for n, h, j in zip(*np.nonzero(close)):
             bad.add((int(n), int(h) // G, int(j)))
         if not bad:
+            if boxes is not None:
+                return mu, R, boxes[0], boxes[1]
             return (mu, R) if sigma is None else (mu, R, sigma)
         W.redraw_blocks(wl, bad)
         for (n, g, j) in bad:
@@ -84,7 +93,9 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
             R[page, g] = r
             if sigma is not None:
                 sigma[page, g] = E.block_sigma(kb)
-        ub, off = _bounds(wl, mu, R, sigma, z)
+            if boxes is not None:
+                boxes[0][page, g], boxes[1][page, g] = E.block_box(kb)
+        ub, off = _bounds(wl, mu, R, sigma, z, boxes)
     raise RuntimeError("margin enforcement did not converge")
 
 

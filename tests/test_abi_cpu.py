@@ -176,6 +176,14 @@ def test_decode_ex_rejects_bad_screens():
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0, c=cache(sigma=FAKE + 2)) == \
         _lib.ETA_ERR_INVALID_ARGUMENT  # misaligned sigma
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_DUAL, 2.0, c=with_sigma) == too_small
+    # comparator box bound: needs both corners, aligned
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_QUEST, 0.0) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_QUEST, 0.0, c=cache(kmin=FAKE * 13)) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT  # one corner only
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_QUEST, 0.0, c=cache(kmin=FAKE * 13, kmax=FAKE + 8)) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT  # misaligned
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_QUEST, 0.0, c=cache(kmin=FAKE * 13, kmax=FAKE * 14)) == \
+        too_small
     assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small
 
 

@@ -34,7 +34,7 @@ def _run_full(name, per_seq, seed=7, bound="geometric"):
     log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
         f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
     heads = _sample_heads(wl, per_seq, seed)
-    dev = Dev(wl, with_sigma=bound == "dual")
+    dev = Dev(wl, with_sigma=bound == "dual", with_box=bound == "quest")
     dev.build()
     o = dev.decode(bound=bound)
     st = dev.stats()
@@ -72,3 +72,9 @@ def test_ragged_16_full():
 def test_seq_512k_dual_full():
     """The 512K workload under the dual screen (z = 2): 8 heads."""
     _run_full("seq_512k", per_seq=8, bound="dual")
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_quest_full():
+    """The 512K workload under the comparator's box bound: 8 heads."""
+    _run_full("seq_512k", per_seq=8, bound="quest")
