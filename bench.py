@@ -53,12 +53,14 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
-    p.add_argument("--bound", default="geometric", choices=["geometric", "dual"],
-                   help="block screen: the geometric bound, or the dual screen (z deviations)")
+    p.add_argument("--bound", default="geometric", choices=["geometric", "dual", "quest"],
+                   help="block screen: the geometric bound, the dual screen (z deviations) or the comparator box bound")
     p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
     p.add_argument("--calibration", action="store_true",
                    help="only time the offline calibration (16 sequences x 4096 positions, GQA 32/8, d=128, bf16) "
                         "and print its own JSON line")
+    p.add_argument("--compare-screens", action="store_true",
+                   help="geometric, dual and box-bound screens at the same thresholds")
     p.add_argument("--prefill", action="store_true",
                    help="time the causal prompt pass over the seq_32k prompt instead of the decode step")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -155,6 +157,36 @@ def calibration_bench(steps):
         "calibrated_c_mean": round(float(cal.c.mean().item()), 4),
         "cpu_baseline": {"value": round(cpu_s * 1e3, 1), "unit": "ms", "cores": 1, "kind": "oracle",
                          "sample": "one (sequence, head) pair of fp64 NumPy histogramming, scaled by 16 x 32"},
+    }), flush=True)
+
+
+def compare_screens(workload, density, steps, warmup, z):
+    """The three screens at the same thresholds (placed for the geometric
+    bound at the workload's target density): admitted fraction per head and
+    per KV head, and the decode step time, for the geometric bound, the dual
+    score and the comparator's box bound (Section 4.3)."""
+    S = Setup(workload, density, "all", z)
+    S.calibrate()
+    rows = {}
+    for b in ("geometric", "dual", "quest"):
+        S.bound = b
+        S.run()
+        S.torch.cuda.synchronize()
+        st, dh, du = S.densities()
+        us = time_steps(S, steps, warmup)
+        ph = time_phases(S, steps)
+        rows[b] = {"density_per_head": round(dh, 4), "density_union": round(du, 4), "us_per_step": round(us, 2),
+                   "screen_us": round(float(ph[0]), 2), "attend_and_merge_us": round(float(ph[1]), 2)}
+        log(f"{b}: per-head {dh:.4f} union {du:.4f} step {us:.1f} us")
+    wl = S.wl
+    print(json.dumps({
+        "metric": "block screens at equal thresholds: admitted density and decode step time",
+        "unit": "us/step", "higher_is_better": False, "steps": steps, "warmup": warmup, "data": "synthetic",
+        "dtype": wl.kv_dtype,
+        "config": {"workload": f"{workload}: {wl.n_seqs} x {int(wl.seq_lens.max())} tokens, GQA {wl.h_q}/{wl.h_kv}, "
+                               f"d={wl.d}; thresholds placed for the geometric bound at per-head density "
+                               f"{float(np.mean(wl.target_density)):.2f}; dual z={z:g}"},
+        "screens": rows,
     }), flush=True)
 
 
@@ -291,10 +323,14 @@ class Setup:
         self.eta, self.torch = eta, torch
         dev = torch.device("cuda")
         self.bound, self.z = bound, z
-        sig = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev) if bound == "dual" else None
+        z16 = lambda: torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev)  # noqa: E731
+        sig = z16() if bound in ("dual", "all") else None
+        lo, hi = (z16(), z16()) if bound in ("quest", "all") else (None, None)
+        if bound == "all":  # every record, for comparisons at equal thresholds
+            self.bound = "geometric"
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
-                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig)
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig, lo, hi)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
         self.q = eta.upload(wl.q, wl.kv_dtype, dev)
@@ -344,14 +380,15 @@ class Setup:
 
     def step_bytes(self, st):
         """Bytes one step must move: admitted K/V tiles once per union block,
-        the records (centroid + radius) of every complete block, the block
+        the records the screen reads for every complete block, the block
         table, the queries/thresholds and the output."""
         wl = self.wl
         esz = 2 if wl.kv_dtype == "bf16" else 4
         union = int(st.union_per_kv.sum())
         kv = union * 2 * 64 * wl.d * esz
         nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
-        rec = 2 * wl.d + 4 + (2 * wl.d if self.bound == "dual" else 0)  # centroid, radius (, deviation)
+        # records the screen reads: centroid and radius (and the deviation), or the key box
+        rec = {"geometric": 2 * wl.d + 4, "dual": 4 * wl.d + 4, "quest": 4 * wl.d}[self.bound]
         meta = nfull * wl.h_kv * rec + int(self.nblk.sum()) * 4
         small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
         return kv, kv + meta + small
@@ -443,6 +480,9 @@ def main():
     if args.calibration:
         calibration_bench(max(3, min(args.steps, 20)))
         return
+    if args.compare_screens:
+        compare_screens(args.workload, args.density, max(5, min(args.steps, 50)), min(args.warmup, 5), args.z)
+        return
     if args.prefill:
         prefill_bench(max(2, min(args.steps, 20)), min(args.warmup, 3), args.cpu_budget, args.no_cpu)
         return
@@ -462,7 +502,8 @@ def main():
     G, D = wl.group, wl.d
     attend_bytes = U * 2 * 64 * D * esz + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
-    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + ("" if args.bound == "geometric" else "-dual")
+    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + \
+        ("" if args.bound == "geometric" else "-" + args.bound)
     traffic = stored_traffic(workload_key)
     result = {
         "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",
@@ -483,9 +524,10 @@ def main():
                         + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
                         + f"{wl.tau_mode} thresholds, target per-head density "
                         + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
-                        + ("" if args.bound == "geometric" else f", dual screen z={args.z:g}"),
+                        + {"geometric": "", "dual": f", dual screen z={args.z:g}",
+                           "quest": ", comparator box-bound screen"}[args.bound],
             "kv_dtype": wl.kv_dtype,
-            "screen": args.bound if args.bound == "geometric" else f"dual z={args.z:g}",
+            "screen": f"dual z={args.z:g}" if args.bound == "dual" else args.bound,
             "seq_lens_total": int(wl.seq_lens.sum()),
             "density_per_head": round(dens_head, 4),
             "density_union": round(dens_union, 4),
