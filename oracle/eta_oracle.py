@@ -58,6 +58,13 @@ Causal prefill (prefill below): the same gated rule at every position of a
 prompt over the keys up to it, dense (no block pruning), thresholds per
 position.
 
+FP8 records (Section 5 lists FP8 metadata quantization as future work; the
+reading taken): the block centroid stored in an OCP FP8 format (E4M3, 3
+mantissa bits, largest 448; or E5M2, 2 mantissa bits, largest 57344), rounded
+to nearest even and saturated at the largest finite value, with the radius
+measured about that stored centroid, so the geometric bound stays an upper
+bound (fp8_round, block_summary_fp8, decode(bound="geometric_fp8")).
+
 Comparator screen (Section 4.3, "Comparison with Quest"): per block and KV
 head the coordinate-wise minimum and maximum of the keys, rounded outward to
 float16, and the box bound s sum_i max(q_i kmax_i, q_i kmin_i) in place of the
@@ -138,6 +145,63 @@ def block_summary(kb: np.ndarray):
     if single:
         return mu[0], float(r[0])
     return mu, r
+
+
+FP8_FORMATS = {
+    # mantissa bits, smallest normal exponent, largest finite value (OCP 8-bit formats)
+    "e4m3": (3, -6, 448.0),
+    "e5m2": (2, -14, 57344.0),
+}
+
+
+def fp8_round(x, fmt: str):
+    """Nearest value of the FP8 format (ties to even), saturating at the largest
+    finite magnitude; zeros keep their sign, NaN stays NaN. float64 in and out."""
+    mbits, emin, vmax = FP8_FORMATS[fmt]
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    with np.errstate(invalid="ignore", over="ignore"):
+        _, e2 = np.frexp(a)                       # a = f 2^e2, f in [0.5, 1): floor(log2 a) = e2 - 1
+        e = np.maximum(e2 - 1, emin)              # binade, the subnormal range sharing the smallest
+        quantum = np.ldexp(1.0, (e - mbits).astype(np.int64))
+        r = np.minimum(np.round(a / quantum) * quantum, vmax)
+        out = np.where(a == 0, x, np.copysign(r, x))
+    return out
+
+
+def block_summary_fp8(kb: np.ndarray, fmt: str):
+    """Geometric record with an FP8 centroid: mu8 = fp8_round(mean k) and R8 the
+    largest distance of a key to mu8 (+inf when not finite); a block holding a
+    non-finite key gets the zero centroid and R8 = +inf. kb float64 [nb, 64, d]
+    or [64, d]; returns (mu8 float64 holding FP8 values, R8 float64)."""
+    single = kb.ndim == 2
+    if single:
+        kb = kb[None]
+    ok = np.isfinite(kb).all(axis=(1, 2))
+    with np.errstate(over="ignore", invalid="ignore"):
+        mu8 = np.where(ok[:, None], fp8_round(kb.mean(axis=1), fmt), 0.0)
+        off8 = kb - mu8[:, None, :]
+        r = np.sqrt((off8 * off8).sum(axis=2)).max(axis=1)
+    r = np.where(ok & np.isfinite(r), r, np.inf)
+    mu = mu8
+    return (mu[0], r[0]) if single else (mu, r)
+
+
+def build_summaries_fp8(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, seq_lens: np.ndarray,
+                        fmt: str):
+    """(mu8, R8) for every complete block of every (sequence, KV head); NaN where
+    there is none."""
+    P, HKV, B, D = k_pages.shape
+    mu = np.full((P, HKV, D), np.nan)
+    R = np.full((P, HKV), np.nan)
+    for n in range(len(seq_lens)):
+        nfull = int(seq_lens[n]) // BLOCK
+        pages = np.asarray(block_table[n, :nfull], dtype=np.int64)
+        for g in range(HKV):
+            for j0 in range(0, nfull, _CHUNK_BLOCKS):
+                pg = pages[j0:j0 + _CHUNK_BLOCKS]
+                mu[pg, g], R[pg, g] = block_summary_fp8(upcast(k_pages[pg, g], kv_dtype), fmt)
+    return mu, R
 
 
 def build_summaries(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray,
@@ -357,15 +421,18 @@ class DecodeResult:
 def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str,
            w, b_or_c, a: float, beta: float, lwb: int, summaries=None,
            heads: Optional[Iterable] = None, with_output: bool = True,
-           bound: str = "geometric", z: float = 2.0, sigmas=None, boxes=None) -> DecodeResult:
+           bound: str = "geometric", z: float = 2.0, sigmas=None, boxes=None,
+           fp8: str = "e4m3", summaries8=None) -> DecodeResult:
     """One ETA decode step for every sequence and query head.
 
     q: [N][H_Q][d] stored values; w: [H_Q][d] (learned mode); b_or_c: [H_Q].
     summaries: (mu, R) from build_summaries, built here if omitted.
     heads: iterable of (n, h) whose output is evaluated (default: all).
     bound: "geometric" (the sound bound), "dual" (dual_score with z and the
-    sigma^ records from build_sigmas, built here if omitted) or "quest" (the
-    comparator's box bound with the (kmin, kmax) records from build_boxes)."""
+    sigma^ records from build_sigmas, built here if omitted), "quest" (the
+    comparator's box bound with the (kmin, kmax) records from build_boxes) or
+    "geometric_fp8" (the geometric bound over the FP8 records of format `fp8`,
+    summaries8 = (mu8, R8) from build_summaries_fp8, built here if omitted)."""
     N, HQ, D = q.shape
     P, HKV, B, D2 = k_pages.shape
     assert D2 == D and B == BLOCK and HQ % HKV == 0
@@ -375,8 +442,10 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
     if summaries is None:
         summaries = build_summaries(k_pages, kv_dtype, block_table, seq_lens)
     mu_all, R_all = summaries
-    if bound not in ("geometric", "dual", "quest"):
+    if bound not in ("geometric", "dual", "quest", "geometric_fp8"):
         raise ValueError(f"unknown bound {bound!r}")
+    if bound == "geometric_fp8" and summaries8 is None:
+        summaries8 = build_summaries_fp8(k_pages, kv_dtype, block_table, seq_lens, fp8)
     if bound == "dual" and sigmas is None:
         sigmas = build_sigmas(k_pages, kv_dtype, block_table, seq_lens)
     if bound == "quest" and boxes is None:
@@ -402,6 +471,8 @@ def decode(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: 
                                 sigmas[pages[:nfull], g], scale, z)
             elif bound == "quest":
                 ub = quest_bound(qf[n, h], boxes[0][pages[:nfull], g], boxes[1][pages[:nfull], g], scale)
+            elif bound == "geometric_fp8":
+                ub = block_bound(qf[n, h], summaries8[0][pages[:nfull], g], summaries8[1][pages[:nfull], g], scale)
             else:
                 ub = block_bound(qf[n, h], mu_all[pages[:nfull], g], R_all[pages[:nfull], g], scale)
             ubs[n, h, :nfull] = ub

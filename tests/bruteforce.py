@@ -112,6 +112,57 @@ def box(rows):
     return lo, hi
 
 
+def fp8_values(fmt: str):
+    """Every finite value of an OCP 8-bit format, by code (sign, exponent,
+    mantissa fields decoded from the definition): {code: value}."""
+    eb, mb = (4, 3) if fmt == "e4m3" else (5, 2)
+    bias = (1 << (eb - 1)) - 1
+    vals = {}
+    for code in range(256):
+        sgn = -1.0 if code & 0x80 else 1.0
+        e = (code >> mb) & ((1 << eb) - 1)
+        m = code & ((1 << mb) - 1)
+        if fmt == "e4m3" and e == 15 and m == 7:
+            continue  # NaN
+        if fmt == "e5m2" and e == 31:
+            continue  # infinities and NaN
+        v = m * 2.0 ** (1 - bias - mb) if e == 0 else (1.0 + m / 2.0 ** mb) * 2.0 ** (e - bias)
+        vals[code] = sgn * v
+    return vals
+
+
+def fp8_nearest(x: float, fmt: str) -> float:
+    """The format's value nearest to x by search over all codes; a tie goes to
+    the code with an even mantissa; beyond the largest finite magnitude, that
+    magnitude (saturation)."""
+    if math.isnan(x):
+        return math.nan
+    vals = fp8_values(fmt)
+    top = max(vals.values())
+    if abs(x) >= top:
+        return math.copysign(top, x)
+    best = None
+    for code, v in vals.items():
+        dist = abs(v - x)
+        if best is None or dist < best[0] or (dist == best[0] and code % 2 == 0 and best[1] % 2 == 1):
+            best = (dist, code, v)
+    return best[2] if best[2] != 0 else math.copysign(0.0, x)
+
+
+def record_fp8(rows, fmt: str):
+    """(FP8 centroid, radius about it) of one block; zero centroid and an
+    infinite radius for a block with a non-finite key."""
+    d = len(rows[0])
+    if not all(math.isfinite(x) for r in rows for x in r):
+        return [0.0] * d, math.inf
+    mean = [math.fsum(r[c] for r in rows) / len(rows) for c in range(d)]
+    mu = [fp8_nearest(x, fmt) for x in mean]
+    best = 0.0
+    for r in rows:
+        best = max(best, math.sqrt(math.fsum((r[c] - mu[c]) ** 2 for c in range(d))))
+    return mu, best
+
+
 def _greater(a: float, b: float) -> float:
     if math.isnan(a):
         return b
@@ -129,7 +180,7 @@ def _smaller(a: float, b: float) -> float:
 
 
 def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, a, beta, lwb,
-           bound="geometric", z=2.0):
+           bound="geometric", z=2.0, fp8="e4m3"):
     """Returns dict with per (n, h): admitted block list, rescued flag, output
     list, plus union counts per (n, g). Inputs are NumPy arrays of stored values
     but are read element by element."""
@@ -153,7 +204,10 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
             return [value(x, kv_dtype) for x in wl_v[page][g][t % BLOCK]]
 
         for g in range(HKV):
-            recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
+            if bound == "geometric_fp8":
+                recs = [record_fp8([key(g, j * BLOCK + r) for r in range(BLOCK)], fp8) for j in range(nfull)]
+            else:
+                recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
             devs = [deviation([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
                 if bound == "dual" else None
             boxes = [box([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \

@@ -296,6 +296,89 @@ def pin_quest_bruteforce(E, seeds=range(3)):
             assert int(res.union[n, g]) == u
 
 
+# --------------------------------------------------------------------------- FP8 records
+def pin_fp8_rounding_table(E):
+    """OCP FP8 rounding by hand: ties to even, the subnormal steps 2^-9 (E4M3)
+    and 2^-16 (E5M2), saturation at 448 and 57344."""
+    x = np.array([1.0, 1.0625, 1.1875, 460.0, 500.0, -1e6, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 0.3,
+                  2.0 ** -7 + 2.0 ** -10, -0.0])
+    e4m3 = [1.0, 1.0, 1.25, 448.0, 448.0, -448.0, 2.0 ** -9, 0.0, 2.0 ** -9, 0.3125, 2.0 ** -7, -0.0]
+    e5m2 = [1.0, 1.0, 1.25, 448.0, 512.0, -57344.0, 2.0 ** -9, 2.0 ** -10, 3 * 2.0 ** -11, 0.3125,
+            2.0 ** -7, -0.0]
+    assert np.array_equal(E.fp8_round(x, "e4m3"), np.array(e4m3))
+    assert np.array_equal(E.fp8_round(x, "e5m2"), np.array(e5m2))
+    assert np.signbit(E.fp8_round(np.array([-0.0]), "e4m3")[0])
+    assert np.isnan(E.fp8_round(np.array([np.nan]), "e5m2")[0])
+    assert E.fp8_round(np.array([2.0 ** -17]), "e5m2")[0] == 0.0          # half the smallest subnormal: even
+    assert E.fp8_round(np.array([3 * 2.0 ** -17]), "e5m2")[0] == 2.0 ** -15
+
+
+def pin_fp8_matches_code_search(E, seed=5):
+    """fp8_round agrees with a search over all 256 codes of each format, on
+    random magnitudes over the whole range, exact ties and the saturation edge."""
+    rng = np.random.default_rng(seed)
+    for fmt in ("e4m3", "e5m2"):
+        vals = sorted(set(bruteforce.fp8_values(fmt).values()))
+        mids = [(a + b) / 2 for a, b in zip(vals, vals[1:])]
+        x = np.concatenate([rng.normal(0, 1, 200) * 2.0 ** rng.integers(-18, 17, 200), np.array(mids[::7]),
+                            np.array(vals[::9]), np.array([1e9, -1e9])])
+        got = E.fp8_round(x, fmt)
+        want = np.array([bruteforce.fp8_nearest(float(v), fmt) for v in x])
+        assert np.array_equal(got, want), (fmt, x[got != want][:5], got[got != want][:5], want[got != want][:5])
+
+
+def pin_fp8_bound_sound(E, seed=9, trials=100):
+    """The geometric bound over FP8 records is never below a key's logit, its
+    radius is the farthest key's distance to the stored centroid (attained by
+    some key), and it is exact for a block of one repeated FP8-exact key."""
+    rng = np.random.default_rng(seed)
+    d = 16
+    s = 1.0 / math.sqrt(d)
+    for _ in range(trials):
+        kb = rng.normal(0, 1, (64, d)) + rng.normal(0, 2, d)
+        q = rng.normal(0, 1, d)
+        for fmt in ("e4m3", "e5m2"):
+            mu, R = E.block_summary_fp8(kb, fmt)
+            assert np.array_equal(mu, E.fp8_round(kb.mean(axis=0), fmt))
+            dist = [math.sqrt(math.fsum((float(kb[t, c]) - float(mu[c])) ** 2 for c in range(d))) for t in range(64)]
+            assert abs(R - max(dist)) <= 1e-12 * max(dist)
+            ub = float(E.block_bound(q, mu[None], np.array([R]), s)[0])
+            assert ub >= s * float((kb @ q).max()) - 1e-12
+    k = np.array([0.5, -1.25, 3.0, 0.0] * 4)
+    mu, R = E.block_summary_fp8(np.tile(k, (64, 1)), "e4m3")
+    assert np.array_equal(mu, k) and R == 0.0
+    bad = np.zeros((64, d))
+    bad[3, 3] = np.nan
+    mu, R = E.block_summary_fp8(bad, "e5m2")
+    assert np.all(mu == 0.0) and R == math.inf
+
+
+def pin_fp8_bruteforce(E, seeds=range(2)):
+    """Sets, bounds and outputs of the geometric screen over FP8 records equal
+    the per-key brute force (its own code-search rounding)."""
+    variants = [dict(n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(320,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated")]
+    for seed in seeds:
+        fmt = ("e4m3", "e5m2")[seed % 2]
+        wl = tiny(90 + seed, **variants[seed % len(variants)])
+        zero = _decode(E, wl, bias=np.zeros(wl.h_q, np.float32), bound="geometric_fp8", fp8=fmt,
+                       with_output=False)
+        wl.bias = np.array([np.nanmedian(zero.ub[:, h] - zero.tau[:, h, None]) for h in range(wl.h_q)],
+                           dtype=np.float32)
+        res = _decode(E, wl, bound="geometric_fp8", fp8=fmt)
+        assert 0 < res.admitted.sum() < res.admitted.size
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb, bound="geometric_fp8", fp8=fmt)
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, n, h, got, r["admitted"])
+            np.testing.assert_allclose(res.ub[n, h, :len(r["ub"])], r["ub"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+
+
 # --------------------------------------------------------------------------- offline calibration
 def _grid_trace(E, T=8, d=4):
     """One sequence whose scaled scores are S_ts = s exactly: q_t = (sqrt(d), 0, ...)
@@ -688,4 +771,5 @@ ALL_PINS = [
     pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
     pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,
+    pin_fp8_rounding_table, pin_fp8_matches_code_search, pin_fp8_bound_sound, pin_fp8_bruteforce,
 ]

@@ -59,6 +59,12 @@ MUTANTS = {
     "quest_box_min_rounded_up": ("lo = f16_round_down(kb.min(axis=1))", "lo = f16_round_up(kb.min(axis=1))"),
     "quest_upper_corner_only": ("terms = np.fmax(kmax * q[None, :], kmin * q[None, :])", "terms = kmax * q[None, :]"),
     "quest_nonfinite_block_kept": ("    lo[bad] = np.nan\n", "    lo[bad] = 0.0\n"),
+    "fp8_round_truncates": ("r = np.minimum(np.round(a / quantum) * quantum, vmax)",
+                            "r = np.minimum(np.floor(a / quantum) * quantum, vmax)"),
+    "fp8_no_subnormal_binade": ("e = np.maximum(e2 - 1, emin)", "e = e2 - 1"),
+    "fp8_no_saturation": ("r = np.minimum(np.round(a / quantum) * quantum, vmax)",
+                          "r = np.round(a / quantum) * quantum"),
+    "fp8_radius_about_mean": ("off8 = kb - mu8[:, None, :]", "off8 = kb - kb.mean(axis=1)[:, None, :]"),
     "prefill_ungated": ("                St = gate(S, tau[:, None], beta)\n", "                St = S\n"),
 }
 
