@@ -53,14 +53,14 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
-    p.add_argument("--bound", default="geometric", choices=["geometric", "dual", "quest"],
+    p.add_argument("--bound", default="geometric", choices=["geometric", "dual", "quest", "geometric_fp8"],
                    help="block screen: the geometric bound, the dual screen (z deviations) or the comparator box bound")
     p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
     p.add_argument("--calibration", action="store_true",
                    help="only time the offline calibration (16 sequences x 4096 positions, GQA 32/8, d=128, bf16) "
                         "and print its own JSON line")
     p.add_argument("--compare-screens", action="store_true",
-                   help="geometric, dual and box-bound screens at the same thresholds")
+                   help="geometric, dual, box-bound and FP8 screens at the same thresholds")
     p.add_argument("--prefill", action="store_true",
                    help="time the causal prompt pass over the seq_32k prompt instead of the decode step")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -161,14 +161,15 @@ def calibration_bench(steps):
 
 
 def compare_screens(workload, density, steps, warmup, z):
-    """The three screens at the same thresholds (placed for the geometric
-    bound at the workload's target density): admitted fraction per head and
-    per KV head, and the decode step time, for the geometric bound, the dual
-    score and the comparator's box bound (Section 4.3)."""
+    """The screens at the same thresholds (placed for the geometric bound at
+    the workload's target density): admitted fraction per head and per KV head,
+    and the decode step time, for the geometric bound, the dual score, the
+    comparator's box bound (Section 4.3) and the geometric bound over E4M3
+    records."""
     S = Setup(workload, density, "all", z)
     S.calibrate()
     rows = {}
-    for b in ("geometric", "dual", "quest"):
+    for b in ("geometric", "dual", "quest", "geometric_fp8"):
         S.bound = b
         S.run()
         S.torch.cuda.synchronize()
@@ -326,11 +327,15 @@ class Setup:
         z16 = lambda: torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev)  # noqa: E731
         sig = z16() if bound in ("dual", "all") else None
         lo, hi = (z16(), z16()) if bound in ("quest", "all") else (None, None)
+        fp8 = bound in ("geometric_fp8", "all")
+        mu8 = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.uint8, device=dev) if fp8 else None
+        r8 = torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev) if fp8 else None
         if bound == "all":  # every record, for comparisons at equal thresholds
             self.bound = "geometric"
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
-                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig, lo, hi)
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig, lo, hi,
+                               mu8, r8, "e4m3")
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
         self.q = eta.upload(wl.q, wl.kv_dtype, dev)
@@ -388,7 +393,8 @@ class Setup:
         kv = union * 2 * 64 * wl.d * esz
         nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
         # records the screen reads: centroid and radius (and the deviation), or the key box
-        rec = {"geometric": 2 * wl.d + 4, "dual": 4 * wl.d + 4, "quest": 4 * wl.d}[self.bound]
+        rec = {"geometric": 2 * wl.d + 4, "dual": 4 * wl.d + 4, "quest": 4 * wl.d,
+               "geometric_fp8": wl.d + 4}[self.bound]
         meta = nfull * wl.h_kv * rec + int(self.nblk.sum()) * 4
         small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
         return kv, kv + meta + small
@@ -525,7 +531,8 @@ def main():
                         + f"{wl.tau_mode} thresholds, target per-head density "
                         + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
                         + {"geometric": "", "dual": f", dual screen z={args.z:g}",
-                           "quest": ", comparator box-bound screen"}[args.bound],
+                           "quest": ", comparator box-bound screen",
+                           "geometric_fp8": ", geometric screen over E4M3 records"}[args.bound],
             "kv_dtype": wl.kv_dtype,
             "screen": f"dual z={args.z:g}" if args.bound == "dual" else args.bound,
             "seq_lens_total": int(wl.seq_lens.sum()),

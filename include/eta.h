@@ -58,7 +58,9 @@ typedef enum {
 enum { ETA_F32 = 0, ETA_BF16 = 1 };                 /* K/V/q element type */
 enum { ETA_TAU_LEARNED = 0, ETA_TAU_CALIBRATED = 1 }; /* threshold mode */
 enum { ETA_PHASE_ALL = -1, ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
-enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2 }; /* block screen, see eta_screen_opts */
+enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2, ETA_BOUND_GEOMETRIC_FP8 = 3 };
+                                                      /* block screen, see eta_screen_opts */
+enum { ETA_FP8_E4M3 = 0, ETA_FP8_E5M2 = 1 };          /* FP8 record formats (OCP 8-bit floats) */
 
 /* Paged KV cache plus its per-block records (caller-owned device buffers).
  *   k_pages, v_pages : [num_pages][num_kv_heads][block_size][head_dim] of
@@ -82,6 +84,19 @@ enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2 }; /* bl
  *                      a block holding a non-finite key (the per-block extrema
  *                      of the comparator of Section 4.3; only ETA_BOUND_QUEST
  *                      reads them). When not NULL, the record builders fill them.
+ *   mu8, radius8     : NULL (both), or an FP8 copy of the geometric record
+ *                      (Section 5 names FP8 metadata as future work; the reading
+ *                      taken): mu8 [num_pages][num_kv_heads][head_dim] bytes,
+ *                      16-byte aligned, the block mean rounded to nearest even
+ *                      in format mu8_format and saturated at its largest finite
+ *                      value; radius8 [num_pages][num_kv_heads] float32, the
+ *                      farthest key's distance to that stored centroid, rounded
+ *                      up (zero centroid, +inf radius for a block holding a
+ *                      non-finite key). Only ETA_BOUND_GEOMETRIC_FP8 reads them;
+ *                      when not NULL, the record builders fill them.
+ *   mu8_format       : ETA_FP8_E4M3 (3 mantissa bits, largest 448) or
+ *                      ETA_FP8_E5M2 (2 mantissa bits, largest 57344); read only
+ *                      when mu8 is not NULL.
  * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
 typedef struct {
   int kv_dtype;
@@ -96,6 +111,9 @@ typedef struct {
   uint16_t* sigma;
   uint16_t* kmin;
   uint16_t* kmax;
+  uint8_t* mu8;
+  float* radius8;
+  int mu8_format;
 } eta_cache;
 
 /* Sequences of a batch.
@@ -172,6 +190,10 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
  *                         each term takes the IEEE maximum, in which a NaN
  *                         product yields to the other). Needs cache->kmin and
  *                         cache->kmax.
+ *   ETA_BOUND_GEOMETRIC_FP8 : the geometric bound over the FP8 records,
+ *                         s (q . mu8 + ||q|| radius8): half the record bytes of
+ *                         the float16 centroid, a coarser centroid and so a
+ *                         larger radius. Needs cache->mu8 and cache->radius8.
  * The score also ranks blocks for the top-1 rescue. */
 typedef struct {
   int bound;
@@ -181,8 +203,9 @@ typedef struct {
 /* eta_decode / eta_decode_phase with a screen choice: phase is ETA_PHASE_ALL
  * for the whole step or one ETA_PHASE_*; screen NULL means the geometric bound.
  * Returns ETA_ERR_INVALID_ARGUMENT for an unknown bound, a negative or
- * non-finite z, the dual bound without cache->sigma, or the comparator bound
- * without cache->kmin and cache->kmax. */
+ * non-finite z, the dual bound without cache->sigma, the comparator bound
+ * without cache->kmin and cache->kmax, or the FP8 bound without cache->mu8
+ * and cache->radius8. */
 eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache,
                          const eta_seqs* seqs, const void* q, int num_q_heads, int tau_mode,
                          const float* w, const float* b_or_c, float a, float beta, int lwb,

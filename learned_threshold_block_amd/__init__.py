@@ -16,7 +16,8 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
+    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_GEOMETRIC_FP8, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA,
+    ETA_FP8_E4M3, ETA_FP8_E5M2, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
     ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ALL, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
     ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
@@ -63,6 +64,9 @@ class Cache:
     sigma: Optional[torch.Tensor] = None  # float16 [num_pages][H_KV][d], for the dual screen
     kmin: Optional[torch.Tensor] = None   # float16 [num_pages][H_KV][d], key box (comparator screen)
     kmax: Optional[torch.Tensor] = None
+    mu8: Optional[torch.Tensor] = None    # uint8 [num_pages][H_KV][d], FP8 centroid (FP8 screen)
+    radius8: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV], radius about it
+    mu8_format: str = "e4m3"              # "e4m3" or "e5m2"
 
     def __post_init__(self):
         _need(self.k_pages, "k_pages")
@@ -85,10 +89,19 @@ class Cache:
                     raise ValueError(f"{name} must be [num_pages][H_KV][d]")
         if (self.kmin is None) != (self.kmax is None):
             raise ValueError("kmin and kmax go together")
+        if (self.mu8 is None) != (self.radius8 is None):
+            raise ValueError("mu8 and radius8 go together")
+        if self.mu8 is not None:
+            _need(self.mu8, "mu8", torch.uint8, dev)
+            _need(self.radius8, "radius8", torch.float32, dev)
+            if tuple(self.mu8.shape) != (P, H, D) or tuple(self.radius8.shape) != (P, H):
+                raise ValueError("mu8 must be [num_pages][H_KV][d] and radius8 [num_pages][H_KV]")
+        if self.mu8_format not in ("e4m3", "e5m2"):
+            raise ValueError("mu8_format must be 'e4m3' or 'e5m2'")
 
     @classmethod
     def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False,
-              with_box=False):
+              with_box=False, fp8: Optional[str] = None):
         k = torch.zeros(num_pages, num_kv_heads, BLOCK, head_dim, dtype=dtype, device=device)
         v = torch.zeros_like(k)
         mu = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.float16, device=device)
@@ -96,7 +109,9 @@ class Cache:
         sig = torch.zeros_like(mu) if with_sigma else None
         lo = torch.zeros_like(mu) if with_box else None
         hi = torch.zeros_like(mu) if with_box else None
-        return cls(k, v, mu, r, sig, lo, hi)
+        mu8 = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.uint8, device=device) if fp8 else None
+        r8 = torch.zeros_like(r) if fp8 else None
+        return cls(k, v, mu, r, sig, lo, hi, mu8, r8, fp8 or "e4m3")
 
     @property
     def kv_dtype(self) -> int:
@@ -114,7 +129,8 @@ class Cache:
         P, H, B, D = self.k_pages.shape
         return _lib.EtaCacheC(self.kv_dtype, D, H, B, P, _ptr(self.k_pages), _ptr(self.v_pages),
                               _ptr(self.mu), _ptr(self.radius), _ptr(self.sigma), _ptr(self.kmin),
-                              _ptr(self.kmax))
+                              _ptr(self.kmax), _ptr(self.mu8), _ptr(self.radius8),
+                              _lib.ETA_FP8_E4M3 if self.mu8_format == "e4m3" else _lib.ETA_FP8_E5M2)
 
 
 def _seqs(seq_lens: torch.Tensor, block_table: torch.Tensor, device) -> _lib.EtaSeqsC:
@@ -161,8 +177,9 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
            stream=None, bound: str = "geometric", z: float = 2.0) -> torch.Tensor:
     """One ETA decode step; returns out [num_seqs][H_Q][d] float32.
     With `phase` set, runs only that phase (screen, attend or merge).
-    bound: "geometric", "dual" (needs cache.sigma; z deviations) or "quest"
-    (the comparator's box bound; needs cache.kmin and cache.kmax)."""
+    bound: "geometric", "dual" (needs cache.sigma; z deviations), "quest"
+    (the comparator's box bound; needs cache.kmin and cache.kmax) or
+    "geometric_fp8" (the geometric bound over cache.mu8 / cache.radius8)."""
     dev = cache.k_pages.device
     _need(q, "q", cache.k_pages.dtype, dev)
     N, HQ, D = q.shape
@@ -184,8 +201,10 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
             _check(_lib.lib().eta_decode(*args), "eta_decode")
         else:
             _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
-    elif bound in ("dual", "quest"):
-        opts = _lib.EtaScreenOptsC(_lib.ETA_BOUND_DUAL if bound == "dual" else _lib.ETA_BOUND_QUEST, float(z))
+    elif bound in ("dual", "quest", "geometric_fp8"):
+        code = {"dual": _lib.ETA_BOUND_DUAL, "quest": _lib.ETA_BOUND_QUEST,
+                "geometric_fp8": _lib.ETA_BOUND_GEOMETRIC_FP8}[bound]
+        opts = _lib.EtaScreenOptsC(code, float(z))
         ph = _lib.ETA_PHASE_ALL if phase is None else int(phase)
         _check(_lib.lib().eta_decode_ex(ph, ctypes.byref(opts), *args), "eta_decode_ex")
     else:

@@ -29,6 +29,9 @@ ETA_PHASE_MERGE = 2
 ETA_BOUND_GEOMETRIC = 0
 ETA_BOUND_DUAL = 1
 ETA_BOUND_QUEST = 2
+ETA_BOUND_GEOMETRIC_FP8 = 3
+ETA_FP8_E4M3 = 0
+ETA_FP8_E5M2 = 1
 
 EXPORTS = (
     "eta_build_block_summaries",
@@ -58,6 +61,9 @@ class EtaCacheC(ctypes.Structure):
         ("sigma", ctypes.c_void_p),
         ("kmin", ctypes.c_void_p),
         ("kmax", ctypes.c_void_p),
+        ("mu8", ctypes.c_void_p),
+        ("radius8", ctypes.c_void_p),
+        ("mu8_format", ctypes.c_int),
     ]
 
 

@@ -254,6 +254,43 @@ __device__ __forceinline__ uint16_t f32_to_f16_dir(float x, bool up) {
   return h;
 }
 
+// OCP 8-bit floats for the FP8 records: format 0 E4M3 (3 mantissa bits,
+// exponent bias 7, largest 448, no infinities), format 1 E5M2 (2 mantissa bits,
+// bias 15, largest 57344). Encoding rounds a finite float64 to nearest even
+// and saturates at the largest finite magnitude.
+template <int MBITS, int EMIN>
+__device__ __forceinline__ uint8_t f64_to_fp8_sat(double x, double vmax, uint8_t maxcode) {
+  const uint8_t sign = __double_as_longlong(x) < 0 ? 0x80u : 0u;
+  const double a = fabs(x);
+  if (a >= vmax) return sign | maxcode;
+  if (a == 0.0) return sign;
+  int e;
+  (void)frexp(a, &e);
+  e -= 1;  // floor(log2 a)
+  if (e < EMIN) e = EMIN;
+  const double r = rint(ldexp(a, MBITS - e));  // multiples of the binade's quantum
+  if (ldexp(r, e - MBITS) >= vmax) return sign | maxcode;
+  int m = (int)r;
+  if (m == 0) return sign;
+  if (m == (2 << MBITS)) {  // carried into the next binade
+    e += 1;
+    m = 1 << MBITS;
+  }
+  if (m < (1 << MBITS)) return sign | (uint8_t)m;  // subnormal: exponent field 0
+  return sign | (uint8_t)(((e + 1 - EMIN) << MBITS) | (m - (1 << MBITS)));
+}
+
+__device__ __forceinline__ uint8_t f64_to_fp8(double x, int fmt) {
+  return fmt == 0 ? f64_to_fp8_sat<3, -6>(x, 448.0, 0x7eu) : f64_to_fp8_sat<2, -14>(x, 57344.0, 0x7bu);
+}
+
+__device__ __forceinline__ float fp8_to_f32(uint32_t b, int fmt) {
+  if (fmt != 0) return f16_bits_to_f32((uint16_t)((b & 0xffu) << 8));  // E5M2 is binary16's high byte
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
+}
+
 // Smallest float32 >= x (x >= 0), +inf for non-finite input.
 __device__ __forceinline__ float f64_to_f32_up(double x) {
   if (!(x < 1e300)) return __builtin_inff();

@@ -68,6 +68,9 @@ eta_status check_cache(const eta_cache* c) {
       !aligned(c->radius, 4) || !aligned(c->sigma, 16) || !aligned(c->kmin, 16) || !aligned(c->kmax, 16))
     return ETA_ERR_INVALID_ARGUMENT;
   if ((c->kmin == nullptr) != (c->kmax == nullptr)) return ETA_ERR_INVALID_ARGUMENT;
+  if ((c->mu8 == nullptr) != (c->radius8 == nullptr) || !aligned(c->mu8, 16) || !aligned(c->radius8, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (c->mu8 && c->mu8_format != ETA_FP8_E4M3 && c->mu8_format != ETA_FP8_E5M2) return ETA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
   if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
   if ((int64_t)c->num_pages * c->num_kv_heads > (int64_t)1 << 31) return ETA_ERR_UNSUPPORTED;
@@ -97,6 +100,9 @@ CacheView view_of(const eta_cache* c) {
   v.sigma = c->sigma;
   v.kmin = c->kmin;
   v.kmax = c->kmax;
+  v.mu8 = c->mu8;
+  v.radius8 = c->radius8;
+  v.mu8_fmt = c->mu8_format == ETA_FP8_E5M2 ? 1 : 0;
   return v;
 }
 
@@ -175,7 +181,8 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
   P->p.bound = 0;
   P->p.z = 0.f;
   if (screen) {
-    if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL && screen->bound != ETA_BOUND_QUEST)
+    if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL && screen->bound != ETA_BOUND_QUEST &&
+        screen->bound != ETA_BOUND_GEOMETRIC_FP8)
       return ETA_ERR_INVALID_ARGUMENT;
     if (screen->bound == ETA_BOUND_DUAL) {
       if (!cache->sigma || !isfinite(screen->z) || !(screen->z >= 0.f)) return ETA_ERR_INVALID_ARGUMENT;
@@ -185,6 +192,10 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
     if (screen->bound == ETA_BOUND_QUEST) {
       if (!cache->kmin || !cache->kmax) return ETA_ERR_INVALID_ARGUMENT;
       P->p.bound = 2;
+    }
+    if (screen->bound == ETA_BOUND_GEOMETRIC_FP8) {
+      if (!cache->mu8 || !cache->radius8) return ETA_ERR_INVALID_ARGUMENT;
+      P->p.bound = 3;
     }
   }
   st = check_seqs(seqs);

@@ -76,6 +76,9 @@ struct CacheView {
   uint16_t* sigma;  // may be null
   uint16_t* kmin;   // may be null (both or neither)
   uint16_t* kmax;
+  uint8_t* mu8;     // may be null (with radius8): FP8 centroids
+  float* radius8;
+  int mu8_fmt;      // 0 E4M3, 1 E5M2
 };
 
 struct SeqView {
@@ -93,7 +96,8 @@ struct DecodeParams {
   int lwb;
   float* out;
   int deterministic;  // static work split and claims: bitwise-reproducible results
-  int bound;          // 0 geometric, 1 dual (tightened by z deviations), 2 comparator box bound
+  int bound;          // 0 geometric, 1 dual (tightened by z deviations), 2 comparator box bound,
+                      // 3 geometric over the FP8 records
   float z;
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };

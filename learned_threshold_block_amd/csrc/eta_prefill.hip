@@ -362,7 +362,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
       const uint16_t* tile = (const uint16_t*)A.c.k + rec * kBlock * D;
       build_record<Bf16, D>(tile, nullptr, A.c.mu + rec * D, A.c.radius + rec,
                             A.c.sigma ? A.c.sigma + rec * D : nullptr, A.c.kmin ? A.c.kmin + rec * D : nullptr,
-                            A.c.kmax ? A.c.kmax + rec * D : nullptr, lane);
+                            A.c.kmax ? A.c.kmax + rec * D : nullptr, A.c.mu8 ? A.c.mu8 + rec * D : nullptr,
+                            A.c.mu8 ? A.c.radius8 + rec : nullptr, A.c.mu8_fmt, lane);
     }
   }
 }

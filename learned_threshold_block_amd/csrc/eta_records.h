@@ -32,11 +32,14 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
 // the centroid and radius, the coordinate deviation if sig_out is not null,
 // and the key box if kmin_out is not null: per coordinate the least key value
 // rounded down and the greatest rounded up to float16 (Section 4.3, the
-// comparator's per-block extrema; NaN for a block with a non-finite key).
+// comparator's per-block extrema; NaN for a block with a non-finite key), and
+// the FP8 record if mu8_out is not null: the mean rounded to the FP8 format
+// fmt8 (nearest even, saturating) and the radius about it, rounded up like R^
+// (zero centroid and infinite radius for a block with a non-finite key).
 template <typename T, int D>
 __device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
                              uint16_t* mu_out, float* r_out, uint16_t* sig_out, uint16_t* kmin_out,
-                             uint16_t* kmax_out, int lane) {
+                             uint16_t* kmax_out, uint8_t* mu8_out, float* r8_out, int fmt8, int lane) {
   constexpr int CPL = D / 64;  // columns per lane: 2 (D=128) or 1 (D=64)
   double sum[CPL];
   float cmin[CPL], cmax[CPL];
@@ -59,7 +62,7 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     }
   }
   uint16_t h[CPL];
-  double mu[CPL], mean[CPL], dev2[CPL];
+  double mu[CPL], mean[CPL], dev2[CPL], mu8[CPL];
   bool ok = finite;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
@@ -69,8 +72,16 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     ok = ok && ((h[c] & 0x7c00u) != 0x7c00u);
   }
   const bool all_ok = __all(ok);
+  const bool all_finite = __all(finite);
+  if (mu8_out) {
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const uint8_t b = all_finite ? f64_to_fp8(mean[c], fmt8) : (uint8_t)0;
+      mu8[c] = (double)fp8_to_f32(b, fmt8);
+      mu8_out[lane * CPL + c] = b;
+    }
+  }
   if (kmin_out) {
-    const bool all_finite = __all(finite);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       kmin_out[lane * CPL + c] = all_finite ? f32_to_f16_dir(cmin[c], false) : (uint16_t)0x7e00u;
@@ -83,10 +94,10 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     mu[c] = (double)f16_bits_to_f32(h[c]);
     mu_out[lane * CPL + c] = h[c];
   }
-  double rmax = 0.0;
+  double rmax = 0.0, rmax8 = 0.0;
   for (int r = 0; r < kBlock; ++r) {
     const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
-    double part = 0.0;
+    double part = 0.0, part8 = 0.0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const double x = (double)load_elem<T>(row + lane * CPL + c);
@@ -94,9 +105,17 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
       part += dlt * dlt;
       const double dm = x - mean[c];  // deviation about the float64 mean
       dev2[c] += dm * dm;
+      if (mu8_out) {
+        const double d8 = x - mu8[c];
+        part8 += d8 * d8;
+      }
     }
     const double tot = wave_sum_f64(part);
     rmax = (tot > rmax || tot != tot) ? tot : rmax;  // NaN propagates
+    if (mu8_out) {
+      const double tot8 = wave_sum_f64(part8);
+      rmax8 = (tot8 > rmax8 || tot8 != tot8) ? tot8 : rmax8;
+    }
   }
   // coordinate deviation (population) as float16
   if (sig_out) {
@@ -106,12 +125,13 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
       sig_out[lane * CPL + c] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
     }
   }
-  const bool any_bad = __any(!finite);
+  const bool any_bad = !all_finite;
   if (lane == 0) {
     float r;
     if (any_bad || !(rmax < 1e300)) r = __builtin_inff();
     else r = f64_to_f32_up(sqrt(rmax) * (1.0 + 0x1p-40));
     *r_out = r;
+    if (mu8_out) *r8_out = (any_bad || !(rmax8 < 1e300)) ? __builtin_inff() : f64_to_f32_up(sqrt(rmax8) * (1.0 + 0x1p-40));
   }
 }
 

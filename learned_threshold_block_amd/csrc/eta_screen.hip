@@ -12,6 +12,8 @@
 //             with the per-block coordinate deviation sigma^ (Section 3.1, F.1)
 //   box       or, as the comparator of Section 4.3, replaced by the best corner
 //             s sum_i max(q_i kmax_i, q_i kmin_i) of the block's key box
+//   fp8       or the geometric bound over the FP8 records (centroid mu8 in an
+//             8-bit float, radius about it)
 //   counts    per-head blocks, union blocks, attended tokens (F.4)
 //
 // k_screen: one wavefront per 64 consecutive blocks of one (sequence, KV head).
@@ -60,10 +62,11 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
   out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
 }
 
-// MODE: 0 geometric bound, 1 dual score, 2 comparator box bound.
+// MODE: 0 geometric bound, 1 dual score, 2 comparator box bound, 3 geometric
+// bound over the FP8 records.
 template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
-  constexpr bool DUAL = MODE == 1, BOX = MODE == 2;
+  constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3;
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
@@ -128,17 +131,26 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : (const void*)A.c.mu,
                                  (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
   const auto r_rsrc = make_rsrc(A.c.radius, (uint32_t)((int64_t)A.c.num_pages * HKV * 4));
-  uint4 raw[NI];
+  const auto mu8_rsrc = make_rsrc(A.c.mu8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * D) : 0u);
+  const auto r8_rsrc = make_rsrc(A.c.radius8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * 4) : 0u);
+  uint4 raw[NI];  // FP8: the lane's 8 bytes in .x/.y
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int j = j0 + RPI * i + r;
     const bool ok = j < nfull && pg[i] >= 0 && pg[i] < A.c.num_pages;
-    const uint32_t off = ok ? (uint32_t)((((int64_t)pg[i] * HKV + g) * D + cb * 8) * 2) : kOutOfRange;
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(mu_rsrc, off, 0, 0);
-    raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    if constexpr (FP8) {
+      const uint32_t off = ok ? (uint32_t)(((int64_t)pg[i] * HKV + g) * D + cb * 8) : kOutOfRange;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b64(mu8_rsrc, off, 0, 0);
+      raw[i] = make_uint4(v[0], v[1], 0u, 0u);
+    } else {
+      const uint32_t off = ok ? (uint32_t)((((int64_t)pg[i] * HKV + g) * D + cb * 8) * 2) : kOutOfRange;
+      const auto v = __builtin_amdgcn_raw_buffer_load_b128(mu_rsrc, off, 0, 0);
+      raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
+    }
   }
   const uint32_t roff = complete ? (uint32_t)(((int64_t)page_l * HKV + g) * 4) : kOutOfRange;
-  const float R = BOX ? 0.f : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r_rsrc, roff, 0, 0));
+  const float R = BOX ? 0.f
+                      : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(FP8 ? r8_rsrc : r_rsrc, roff, 0, 0));
   // dual screen: coordinate deviations; box bound: upper corners (both laid
   // out like the centroids)
   uint4 sraw[DUAL || BOX ? NI : 1];
@@ -184,10 +196,15 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   for (int i = 0; i < NI; ++i) {
     const uint32_t w4[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
     float mv[8];
+    if constexpr (FP8) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      mv[2 * e] = f16_bits_to_f32((uint16_t)(w4[e] & 0xffffu));
-      mv[2 * e + 1] = f16_bits_to_f32((uint16_t)(w4[e] >> 16));
+      for (int e = 0; e < 8; ++e) mv[e] = fp8_to_f32(w4[e >> 2] >> (8 * (e & 3)), A.c.mu8_fmt);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        mv[2 * e] = f16_bits_to_f32((uint16_t)(w4[e] & 0xffffu));
+        mv[2 * e + 1] = f16_bits_to_f32((uint16_t)(w4[e] >> 16));
+      }
     }
     if constexpr (BOX) {  // mv: lower corner; sum of max(q kmax, q kmin) per lane
       const uint32_t u4[4] = {sraw[i].x, sraw[i].y, sraw[i].z, sraw[i].w};
@@ -585,6 +602,7 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
   dim3 grid((d.NT + 3) / 4, d.S);
   if (p.bound == 1) hipLaunchKernelGGL((k_screen<T, D, G, 1>), grid, dim3(256), 0, st, a);
   else if (p.bound == 2) hipLaunchKernelGGL((k_screen<T, D, G, 2>), grid, dim3(256), 0, st, a);
+  else if (p.bound == 3) hipLaunchKernelGGL((k_screen<T, D, G, 3>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_screen<T, D, G, 0>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

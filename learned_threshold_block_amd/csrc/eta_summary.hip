@@ -37,7 +37,8 @@ __global__ __launch_bounds__(256) void k_build(CacheView c, SeqView s) {
   const int64_t rec = (int64_t)page * c.HKV + g;
   const auto* tile = (const typename T::Stored*)c.k + rec * kBlock * D;
   build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
-                     c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr, lane);
+                     c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
+                     c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
 }
 
 template <typename T, int D>
@@ -63,7 +64,8 @@ __global__ __launch_bounds__(64) void k_append(CacheView c, SeqView s, const voi
   if (row == kBlock - 1) {
     const St* tile = (const St*)c.kw + rec * kBlock * D;
     build_record<T, D>(tile, kn, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
-                       c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr, lane);
+                       c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
+                     c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
   }
 }
 

@@ -24,7 +24,7 @@ def log(msg: str) -> None:
 class Dev:
     """A workload's inputs on the GPU."""
 
-    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False, with_box=False):
+    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False, with_box=False, fp8=None):
         self.wl = wl
         self.device = torch.device(device)
         z16 = lambda: torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device)  # noqa: E731
@@ -34,7 +34,11 @@ class Dev:
                                eta.upload(wl.v_pages, wl.kv_dtype, device),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device),
                                torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device), sig,
-                               lo, hi)
+                               lo, hi,
+                               torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.uint8, device=device)
+                               if fp8 else None,
+                               torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device)
+                               if fp8 else None, fp8 or "e4m3")
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(device)
         self.q = eta.upload(wl.q, wl.kv_dtype, device)
@@ -69,15 +73,25 @@ class Dev:
     def sigma_bits(self):
         return self.cache.sigma.cpu().view(torch.int16).numpy().view(np.uint16)
 
+    def fp8_codes(self):
+        return self.cache.mu8.cpu().numpy(), self.cache.radius8.cpu().numpy()
+
     def box_bits(self):
         f = lambda t: t.cpu().view(torch.int16).numpy().view(np.uint16)  # noqa: E731
         return f(self.cache.kmin), f(self.cache.kmax)
 
 
 def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=None, beta=None, lwb=None,
-                  bound="geometric", z=2.0):
+                  bound="geometric", z=2.0, fp8="e4m3"):
     """summaries: (mu, R); for the dual screen (mu, R, sigma); for the
-    comparator's box bound (mu, R, kmin, kmax)."""
+    comparator's box bound (mu, R, kmin, kmax); for "geometric_fp8" the FP8
+    records (mu8, R8)."""
+    if bound == "geometric_fp8":
+        return E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
+                        wl.tau_mode if tau_mode is None else tau_mode, wl.w,
+                        wl.bias if bias is None else bias, wl.a if a is None else a,
+                        wl.beta if beta is None else beta, wl.lwb if lwb is None else lwb,
+                        heads=heads, bound=bound, fp8=fp8, summaries8=summaries)
     sig = None
     boxes = None
     if summaries is not None and len(summaries) == 3:
@@ -123,11 +137,11 @@ def check_output(wl, res, o_gpu, heads=None, tol=None):
     return err
 
 
-def prepared(name, bound="geometric", z=2.0, **kw):
+def prepared(name, bound="geometric", z=2.0, fp8="e4m3", **kw):
     """Workload with thresholds placed and margins enforced (oracle side) for
     the given screen."""
     wl = W.make_workload(name, **kw)
-    summ = placement.place(wl, bound=bound, z=z)
+    summ = placement.place(wl, bound=bound, z=z, fp8=fp8)
     return wl, summ
 
 

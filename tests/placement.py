@@ -47,12 +47,15 @@ def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None):
 
 
 def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound: str = "geometric",
-          z: float = 2.0):
+          z: float = 2.0, fp8: str = "e4m3"):
     """Set wl.bias in place; returns the oracle summaries of the final cache
     ((mu, R), (mu, R, sigma) for the dual screen, (mu, R, kmin, kmax) for the
-    comparator's box bound)."""
-    mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
-        if summaries is None else summaries[:2]
+    comparator's box bound; the FP8 records (mu8, R8) for "geometric_fp8")."""
+    if bound == "geometric_fp8":
+        mu, R = E.build_summaries_fp8(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, fp8)
+    else:
+        mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
+            if summaries is None else summaries[:2]
     sigma = None
     boxes = None
     if bound == "dual":
@@ -88,7 +91,7 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         for (n, g, j) in bad:
             page = int(wl.block_table[n, j])
             kb = E.upcast(wl.k_pages[page, g], wl.kv_dtype)
-            m, r = E.block_summary(kb)
+            m, r = E.block_summary_fp8(kb, fp8) if bound == "geometric_fp8" else E.block_summary(kb)
             mu[page, g] = m
             R[page, g] = r
             if sigma is not None:

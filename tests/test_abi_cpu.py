@@ -184,6 +184,16 @@ def test_decode_ex_rejects_bad_screens():
         _lib.ETA_ERR_INVALID_ARGUMENT  # misaligned
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_QUEST, 0.0, c=cache(kmin=FAKE * 13, kmax=FAKE * 14)) == \
         too_small
+    # FP8 records: both buffers, aligned, a known format
+    fp8 = dict(mu8=FAKE * 15, radius8=FAKE * 16, mu8_format=_lib.ETA_FP8_E5M2)
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(mu8=FAKE * 15)) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(**dict(fp8, mu8_format=5))) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(**dict(fp8, mu8=FAKE + 4))) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(**fp8)) == too_small
     assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small
 
 

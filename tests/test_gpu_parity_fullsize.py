@@ -28,18 +28,19 @@ def _sample_heads(wl, per_seq, seed):
     return heads
 
 
-def _run_full(name, per_seq, seed=7, bound="geometric"):
+def _run_full(name, per_seq, seed=7, bound="geometric", fp8="e4m3"):
     log(f"[full-size] {name} ({bound} screen): generating and placing thresholds")
-    wl, summ = prepared(name, bound=bound)
+    wl, summ = prepared(name, bound=bound, fp8=fp8)
     log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
         f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
     heads = _sample_heads(wl, per_seq, seed)
-    dev = Dev(wl, with_sigma=bound == "dual", with_box=bound == "quest")
+    dev = Dev(wl, with_sigma=bound == "dual", with_box=bound == "quest",
+              fp8=fp8 if bound == "geometric_fp8" else None)
     dev.build()
     o = dev.decode(bound=bound)
     st = dev.stats()
     log(f"[full-size] {name}: oracle on {len(heads)} heads")
-    res = oracle_decode(wl, summaries=summ, heads=heads, bound=bound)
+    res = oracle_decode(wl, summaries=summ, heads=heads, bound=bound, fp8=fp8)
     check_sets_and_counts(wl, res, st)
     check_output(wl, res, o, heads=heads)
     dens = st.admitted_per_head.sum() / (wl.h_q * sum(wl.nblk(n) for n in range(wl.n_seqs)))
@@ -78,3 +79,9 @@ def test_seq_512k_dual_full():
 def test_seq_512k_quest_full():
     """The 512K workload under the comparator's box bound: 8 heads."""
     _run_full("seq_512k", per_seq=8, bound="quest")
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_fp8_full():
+    """The 512K workload under the geometric bound over E4M3 records: 8 heads."""
+    _run_full("seq_512k", per_seq=8, bound="geometric_fp8", fp8="e4m3")
