@@ -65,6 +65,12 @@ to nearest even and saturated at the largest finite value, with the radius
 measured about that stored centroid, so the geometric bound stays an upper
 bound (fp8_round, block_summary_fp8, decode(bound="geometric_fp8")).
 
+Smaller screen blocks (Appendix F.3, Table 10 ablates the block size; the
+reading taken): with b = 16 or 32 every 64-token page holds 64/b screen
+blocks, each with its own record (centroid and radius of its b keys); the
+screen, the forced and rescued blocks, the counts and the attention all work
+on b-token blocks (build_summaries_sub, decode_blocks).
+
 Comparator screen (Section 4.3, "Comparison with Quest"): per block and KV
 head the coordinate-wise minimum and maximum of the keys, rounded outward to
 float16, and the box bound s sum_i max(q_i kmax_i, q_i kmin_i) in place of the
@@ -366,8 +372,8 @@ def dual_score(q: np.ndarray, mu: np.ndarray, R: np.ndarray, sigma: np.ndarray, 
     return np.fmin(geo, prob)
 
 
-def admitted_blocks(ub: np.ndarray, tau: float, seq_len: int, lwb: int):
-    """Blocks loaded for one (sequence, query head).
+def admitted_blocks(ub: np.ndarray, tau: float, seq_len: int, lwb: int, block: int = BLOCK):
+    """Blocks loaded for one (sequence, query head) (blocks of `block` tokens).
 
     ub: bounds of the complete blocks (length floor(T/64)). A complete block is
     admitted unless its bound is below tau~ (Section 3.1: a block matters when
@@ -377,12 +383,12 @@ def admitted_blocks(ub: np.ndarray, tau: float, seq_len: int, lwb: int):
     largest bound is (Top-1 rescue, Section 3.2 and F.4, taken over the whole
     sequence; ties go to the lowest index).
     Returns (bool mask over ceil(T/64) blocks, rescued flag)."""
-    nfull = seq_len // BLOCK
-    nblk = -(-seq_len // BLOCK)
+    nfull = seq_len // block
+    nblk = -(-seq_len // block)
     adm = np.zeros(nblk, dtype=bool)
     ub = np.asarray(ub, dtype=np.float64)[:nfull]
     adm[:nfull] = ~(ub < tau)
-    if seq_len % BLOCK:
+    if seq_len % block:
         adm[nfull] = True
     if lwb > 0 and nfull > 0:
         adm[max(0, nfull - lwb):nfull] = True
@@ -525,6 +531,97 @@ def _attend(qh, k_pages, v_pages, kv_dtype, pages, g, blocks, T, tau, beta, scal
         num += wts @ vb[keep]
         den += wts.sum()
     return num / den
+
+
+# --------------------------------------------------------------------------- smaller screen blocks
+def build_summaries_sub(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, seq_lens: np.ndarray,
+                        block: int):
+    """Records of every complete block of `block` tokens (16 or 32; a page
+    holds 64/b consecutive blocks, its block q being rows q b .. q b + b - 1):
+    mu float64 [num_pages][H_KV][64/b][d] holding float16 values and R
+    float64 [num_pages][H_KV][64/b], NaN where there is none. Same record rule
+    as build_summaries (block_summary on b keys)."""
+    assert BLOCK % block == 0 and block < BLOCK
+    SB = BLOCK // block
+    P, HKV, B, D = k_pages.shape
+    mu = np.full((P, HKV, SB, D), np.nan)
+    R = np.full((P, HKV, SB), np.nan)
+    for n in range(len(seq_lens)):
+        nsub = int(seq_lens[n]) // block
+        if nsub == 0:
+            continue
+        j = np.arange(nsub)
+        pg = np.asarray(block_table[n], dtype=np.int64)[j // SB]
+        sub = j % SB
+        for g in range(HKV):
+            for j0 in range(0, nsub, _CHUNK_BLOCKS * SB):
+                sl = slice(j0, j0 + _CHUNK_BLOCKS * SB)
+                rows = upcast(k_pages[pg[sl], g], kv_dtype).reshape(-1, SB, block, D)[np.arange(len(pg[sl])), sub[sl]]
+                m, r = block_summary(rows)
+                mu[pg[sl], g, sub[sl]] = m
+                R[pg[sl], g, sub[sl]] = r
+    return mu, R
+
+
+def decode_blocks(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str, w, b_or_c, a: float,
+                  beta: float, lwb: int, block: int, summaries=None, heads: Optional[Iterable] = None,
+                  with_output: bool = True) -> DecodeResult:
+    """decode with the geometric screen on blocks of `block` tokens (16 or 32):
+    block j of sequence n is rows (j mod 64/b) b .. + b - 1 of page
+    block_table[n][j b / 64]. Admitted sets, bounds, forced blocks (the partial
+    last block, the lwb most recent complete blocks), the rescue and the counts
+    are per b-token block; admitted is [N][H_Q][max_blocks 64/b]; union counts
+    b-token blocks admitted by any head of the group; attention runs over the
+    tokens t < T of the admitted blocks."""
+    N, HQ, D = q.shape
+    P, HKV, B, D2 = k_pages.shape
+    assert D2 == D and B == BLOCK and HQ % HKV == 0 and BLOCK % block == 0
+    SB = BLOCK // block
+    G = HQ // HKV
+    MB = block_table.shape[1] * SB
+    scale = 1.0 / math.sqrt(D)
+    mu_all, R_all = build_summaries_sub(k_pages, kv_dtype, block_table, seq_lens, block) \
+        if summaries is None else summaries
+    qf = upcast(q, kv_dtype)
+    want = None if heads is None else set((int(n), int(h)) for n, h in heads)
+    o = np.full((N, HQ, D), np.nan)
+    admitted = np.zeros((N, HQ, MB), dtype=bool)
+    rescued = np.zeros((N, HQ), dtype=bool)
+    taus = np.zeros((N, HQ))
+    ubs = np.full((N, HQ, MB), np.nan)
+    for n in range(N):
+        T = int(seq_lens[n])
+        nfull = T // block
+        pages = np.asarray(block_table[n], dtype=np.int64)
+        j = np.arange(nfull)
+        for h in range(HQ):
+            g = h // G
+            tau = threshold(tau_mode, qf[n, h], None if w is None else w[h], b_or_c[h], a)
+            taus[n, h] = tau
+            ub = block_bound(qf[n, h], mu_all[pages[j // SB], g, j % SB], R_all[pages[j // SB], g, j % SB], scale)
+            ubs[n, h, :nfull] = ub
+            adm, resc = admitted_blocks(ub, tau, T, lwb, block)
+            admitted[n, h, :len(adm)] = adm
+            rescued[n, h] = resc
+            if not with_output or (want is not None and (n, h) not in want):
+                continue
+            tok = (np.nonzero(adm)[0][:, None] * block + np.arange(block)[None, :]).reshape(-1)
+            tok = tok[tok < T]
+            K = upcast(k_pages[pages[tok // BLOCK], g, tok % BLOCK], kv_dtype)
+            V = upcast(v_pages[pages[tok // BLOCK], g, tok % BLOCK], kv_dtype)
+            o[n, h] = filtered_attention(qf[n, h], K, V, tau, beta, scale)
+    per_head = admitted.sum(axis=2).astype(np.int64)
+    union = np.zeros((N, HKV), dtype=np.int64)
+    tokens = np.zeros((N, HQ), dtype=np.int64)
+    for n in range(N):
+        T = int(seq_lens[n])
+        nblk = -(-T // block)
+        width = np.minimum(block, T - block * np.arange(nblk))
+        for g in range(HKV):
+            union[n, g] = admitted[n, g * G:(g + 1) * G, :nblk].any(axis=0).sum()
+        tokens[n] = admitted[n, :, :nblk] @ width
+    return DecodeResult(o=o, admitted=admitted, rescued=rescued, tau=taus, ub=ubs,
+                        per_head=per_head, union=union, tokens=tokens)
 
 
 # --------------------------------------------------------------------------- offline calibration

@@ -3,6 +3,7 @@
 An independent second implementation used to pin the oracle: pure-Python loops
 over every key with the `math` module (fsum, exact float16 rounding through
 `struct`), no NumPy vector arithmetic and no code shared with `oracle/`.
+Screen blocks of 16 or 32 tokens are taken through the `block` argument.
 It follows "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888),
 Sections 2.2, 3.1, 3.2, 4.8, F.1, F.4 and G.1, with the same readings as the
 oracle (geometric bound about the fp16 centroid, global top-1 rescue; the
@@ -44,7 +45,7 @@ def value(stored, kv_dtype: str) -> float:
 
 
 def record(rows):
-    """(centroid, radius) of one complete block given its 64 key rows."""
+    """(centroid, radius) of one complete block given its key rows."""
     d = len(rows[0])
     mean = [math.fsum(r[c] for r in rows) / len(rows) for c in range(d)]
     mu = [_f16(x) for x in mean]
@@ -180,7 +181,7 @@ def _smaller(a: float, b: float) -> float:
 
 
 def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, a, beta, lwb,
-           bound="geometric", z=2.0, fp8="e4m3"):
+           bound="geometric", z=2.0, fp8="e4m3", block=BLOCK):
     """Returns dict with per (n, h): admitted block list, rescued flag, output
     list, plus union counts per (n, g). Inputs are NumPy arrays of stored values
     but are read element by element."""
@@ -192,8 +193,8 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
     union = {}
     for n in range(N):
         T = int(seq_lens[n])
-        nfull = T // BLOCK
-        nblk = -(-T // BLOCK)
+        nfull = T // block
+        nblk = -(-T // block)
 
         def key(g, t):
             page = int(block_table[n][t // BLOCK])
@@ -205,12 +206,12 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
 
         for g in range(HKV):
             if bound == "geometric_fp8":
-                recs = [record_fp8([key(g, j * BLOCK + r) for r in range(BLOCK)], fp8) for j in range(nfull)]
+                recs = [record_fp8([key(g, j * block + r) for r in range(block)], fp8) for j in range(nfull)]
             else:
-                recs = [record([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)]
-            devs = [deviation([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
+                recs = [record([key(g, j * block + r) for r in range(block)]) for j in range(nfull)]
+            devs = [deviation([key(g, j * block + r) for r in range(block)]) for j in range(nfull)] \
                 if bound == "dual" else None
-            boxes = [box([key(g, j * BLOCK + r) for r in range(BLOCK)]) for j in range(nfull)] \
+            boxes = [box([key(g, j * block + r) for r in range(block)]) for j in range(nfull)] \
                 if bound == "quest" else None
             loaded = set()
             for hh in range(G):
@@ -249,7 +250,7 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                     forced = j >= nfull - lwb
                     if forced or not (ub < tau):
                         adm.append(j)
-                if T % BLOCK:
+                if T % block:
                     adm.append(nfull)
                 rescued = False
                 if not adm:
@@ -264,8 +265,8 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                 logits = []
                 vals = []
                 for j in adm:
-                    for r in range(BLOCK):
-                        t = j * BLOCK + r
+                    for r in range(block):
+                        t = j * block + r
                         if t >= T:
                             break
                         S = s * math.fsum(qh[c] * x for c, x in enumerate(key(g, t)))
@@ -276,7 +277,7 @@ def decode(wl_k, wl_v, kv_dtype, block_table, seq_lens, q, tau_mode, w, b_or_c, 
                 wts = [math.exp(x - m) for x in logits]
                 den = math.fsum(wts)
                 o = [math.fsum(wts[i] * vals[i][c] for i in range(len(wts))) / den for c in range(D)]
-                tokens = sum(min(BLOCK, T - j * BLOCK) for j in adm)
+                tokens = sum(min(block, T - j * block) for j in adm)
                 out[(n, h)] = dict(admitted=sorted(adm), rescued=rescued, o=o, tau=tau, ub=ubs,
                                    tokens=tokens)
             union[(n, g)] = len(loaded)

@@ -379,6 +379,55 @@ def pin_fp8_bruteforce(E, seeds=range(2)):
             assert int(res.union[n, g]) == u
 
 
+# --------------------------------------------------------------------------- smaller screen blocks
+def pin_subblock_bruteforce(E, seeds=range(4)):
+    """Screens on 16- and 32-token blocks: sets, bounds, rescue, token counts,
+    outputs and union counts equal the per-key brute force at that block size."""
+    variants = [dict(n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(150,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated", lwb=2),
+                dict(n=2, lens=(77, 96), h_q=2, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(300,), h_q=4, h_kv=1, d=4, dtype="f32", mode="learned", lwb=1)]
+    for seed in seeds:
+        block = (16, 32)[seed % 2]
+        wl = tiny(110 + seed, **variants[seed % len(variants)])
+        zero = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                               wl.w, np.zeros(wl.h_q, np.float32), wl.a, wl.beta, wl.lwb, block, with_output=False)
+        wl.bias = np.array([np.nanmedian(zero.ub[:, h] - zero.tau[:, h, None]) for h in range(wl.h_q)],
+                           dtype=np.float32)
+        res = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                              wl.w, wl.bias, wl.a, wl.beta, wl.lwb, block)
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb, block=block)
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, block, n, h, got, r["admitted"])
+            assert bool(res.rescued[n, h]) == r["rescued"]
+            assert int(res.tokens[n, h]) == r["tokens"]
+            np.testing.assert_allclose(res.ub[n, h, :len(r["ub"])], r["ub"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+
+
+def pin_subblock_no_false_negatives(E, seeds=range(3)):
+    """Every key whose logit reaches its head's threshold lies in an admitted
+    16-token block (the bound is sound at any block size)."""
+    for seed in seeds:
+        wl = tiny(120 + seed, n=2, lens=(256, 190), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned")
+        res = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                              wl.w, wl.bias, wl.a, wl.beta, wl.lwb, 16, with_output=False)
+        for n in range(wl.n_seqs):
+            T = int(wl.seq_lens[n])
+            for h in range(wl.h_q):
+                g = h // wl.group
+                for t in range(T):
+                    k = E.upcast(wl.k_pages[wl.block_table[n, t // 64], g, t % 64], wl.kv_dtype)
+                    S = float(E.upcast(wl.q[n, h], wl.kv_dtype) @ k) / math.sqrt(wl.d)
+                    if S >= res.tau[n, h]:
+                        assert res.admitted[n, h, t // 16], (seed, n, h, t)
+
+
 # --------------------------------------------------------------------------- offline calibration
 def _grid_trace(E, T=8, d=4):
     """One sequence whose scaled scores are S_ts = s exactly: q_t = (sqrt(d), 0, ...)
@@ -772,4 +821,5 @@ ALL_PINS = [
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
     pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,
     pin_fp8_rounding_table, pin_fp8_matches_code_search, pin_fp8_bound_sound, pin_fp8_bruteforce,
+    pin_subblock_bruteforce, pin_subblock_no_false_negatives,
 ]

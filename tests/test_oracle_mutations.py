@@ -25,7 +25,7 @@ MUTANTS = {
     "gate_additive": ("return S * sigmoid(beta * (S - tau))", "return S + sigmoid(beta * (S - tau)) - 1.0"),
     "threshold_adds_a": ("+ float(b_h) - float(a)", "+ float(b_h) + float(a)"),
     "group_index_modulo": ("g = h // G", "g = h % HKV"),
-    "tail_block_dropped": ("    if seq_len % BLOCK:\n        adm[nfull] = True\n", ""),
+    "tail_block_dropped": ("    if seq_len % block:\n        adm[nfull] = True\n", ""),
     "lwb_counts_from_start": ("adm[max(0, nfull - lwb):nfull] = True", "adm[:min(lwb, nfull)] = True"),
     "rescue_takes_last_max": ("adm[int(np.argmax(ub))] = True",
                               "adm[len(ub) - 1 - int(np.argmax(ub[::-1]))] = True"),
@@ -65,6 +65,11 @@ MUTANTS = {
     "fp8_no_saturation": ("r = np.minimum(np.round(a / quantum) * quantum, vmax)",
                           "r = np.round(a / quantum) * quantum"),
     "fp8_radius_about_mean": ("off8 = kb - mu8[:, None, :]", "off8 = kb - kb.mean(axis=1)[:, None, :]"),
+    "subblock_record_slot": ("        sub = j % SB\n", "        sub = (j + 1) % SB\n"),
+    "subblock_token_width": ("        width = np.minimum(block, T - block * np.arange(nblk))",
+                             "        width = np.minimum(BLOCK, T - block * np.arange(nblk))"),
+    "subblock_key_page": ("            K = upcast(k_pages[pages[tok // BLOCK], g, tok % BLOCK], kv_dtype)",
+                          "            K = upcast(k_pages[pages[tok // BLOCK], g, (tok + 1) % BLOCK], kv_dtype)"),
     "prefill_ungated": ("                St = gate(S, tau[:, None], beta)\n", "                St = S\n"),
 }
 
