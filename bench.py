@@ -53,9 +53,12 @@ def parse():
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
-    p.add_argument("--bound", default="geometric", choices=["geometric", "dual", "quest", "geometric_fp8"],
+    p.add_argument("--bound", default="geometric",
+                   choices=["geometric", "dual", "quest", "geometric_fp8", "geometric_sub"],
                    help="block screen: the geometric bound, the dual screen (z deviations) or the comparator box bound")
     p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
+    p.add_argument("--sub-block", type=int, default=16, choices=[16, 32],
+                   help="tokens per screen block for --bound geometric_sub")
     p.add_argument("--calibration", action="store_true",
                    help="only time the offline calibration (16 sequences x 4096 positions, GQA 32/8, d=128, bf16) "
                         "and print its own JSON line")
@@ -164,21 +167,25 @@ def compare_screens(workload, density, steps, warmup, z):
     """The screens at the same thresholds (placed for the geometric bound at
     the workload's target density): admitted fraction per head and per KV head,
     and the decode step time, for the geometric bound, the dual score, the
-    comparator's box bound (Section 4.3) and the geometric bound over E4M3
-    records."""
+    comparator's box bound (Section 4.3), the geometric bound over E4M3
+    records, and the geometric bound on 16- and 32-token screen blocks
+    (Appendix F.3's block size; densities in those blocks)."""
     S = Setup(workload, density, "all", z)
     S.calibrate()
     rows = {}
-    for b in ("geometric", "dual", "quest", "geometric_fp8"):
-        S.bound = b
+    for b in ("geometric", "dual", "quest", "geometric_fp8", "geometric_sub", "geometric_sub32"):
+        if b == "geometric_sub32":
+            S.use_sub_block(32)
+        S.bound = "geometric_sub" if b == "geometric_sub32" else b
         S.run()
         S.torch.cuda.synchronize()
         st, dh, du = S.densities()
         us = time_steps(S, steps, warmup)
         ph = time_phases(S, steps)
-        rows[b] = {"density_per_head": round(dh, 4), "density_union": round(du, 4), "us_per_step": round(us, 2),
+        key = {"geometric_sub": "geometric_b16", "geometric_sub32": "geometric_b32"}.get(b, b)
+        rows[key] = {"density_per_head": round(dh, 4), "density_union": round(du, 4), "us_per_step": round(us, 2),
                    "screen_us": round(float(ph[0]), 2), "attend_and_merge_us": round(float(ph[1]), 2)}
-        log(f"{b}: per-head {dh:.4f} union {du:.4f} step {us:.1f} us")
+        log(f"{key}: per-head {dh:.4f} union {du:.4f} step {us:.1f} us")
     wl = S.wl
     print(json.dumps({
         "metric": "block screens at equal thresholds: admitted density and decode step time",
@@ -311,7 +318,7 @@ def copy_probe(mib, steps):
 class Setup:
     """One workload resident on the GPU."""
 
-    def __init__(self, name, density=None, bound="geometric", z=2.0):
+    def __init__(self, name, density=None, bound="geometric", z=2.0, sub_block=16):
         import torch
 
         import learned_threshold_block_amd as eta
@@ -330,12 +337,16 @@ class Setup:
         fp8 = bound in ("geometric_fp8", "all")
         mu8 = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.uint8, device=dev) if fp8 else None
         r8 = torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev) if fp8 else None
+        self.sub_block = sub_block if bound in ("geometric_sub", "all") else 0
+        sb = 64 // self.sub_block if self.sub_block else 0
+        mus = torch.zeros(wl.num_pages, wl.h_kv, sb, wl.d, dtype=torch.float16, device=dev) if sb else None
+        rs = torch.zeros(wl.num_pages, wl.h_kv, sb, dtype=torch.float32, device=dev) if sb else None
         if bound == "all":  # every record, for comparisons at equal thresholds
             self.bound = "geometric"
         self.cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
                                torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev), sig, lo, hi,
-                               mu8, r8, "e4m3")
+                               mu8, r8, "e4m3", self.sub_block, mus, rs)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(dev)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
         self.q = eta.upload(wl.q, wl.kv_dtype, dev)
@@ -371,17 +382,39 @@ class Setup:
             mid = 0.5 * (lo + hi)
             self.bias.copy_(torch.from_numpy(mid.astype(np.float32)))
             self.run(phase=self.eta.ETA_PHASE_SCREEN)
-            dens = (self.stats().admitted_per_head / self.nblk[:, None]).mean(axis=0)
+            b = self.block_tokens()
+            nb = np.array([-(-int(T) // b) for T in wl.seq_lens], dtype=np.float64)
+            dens = (self.stats().admitted_per_head / nb[:, None]).mean(axis=0)
             lo = np.where(dens > target, mid, lo)
             hi = np.where(dens > target, hi, mid)
         self.bias.copy_(torch.from_numpy((0.5 * (lo + hi)).astype(np.float32)))
         self.bias[target >= 1.0] = -math.inf
 
+    def block_tokens(self):
+        """Tokens per screen block of the current screen."""
+        return self.sub_block if self.bound == "geometric_sub" else 64
+
     def densities(self):
         st = self.stats()
-        per_head = float((st.admitted_per_head / self.nblk[:, None]).mean())
-        union = float((st.union_per_kv / self.nblk[:, None]).mean())
+        b = self.block_tokens()
+        nb = np.array([-(-int(T) // b) for T in self.wl.seq_lens], dtype=np.float64)
+        per_head = float((st.admitted_per_head / nb[:, None]).mean())
+        union = float((st.union_per_kv / nb[:, None]).mean())
         return st, per_head, union
+
+    def use_sub_block(self, sub_block):
+        """Records of another smaller screen block size (same K/V and thresholds)."""
+        eta, torch, wl = self.eta, self.torch, self.wl
+        sb = 64 // sub_block
+        c = self.cache
+        self.cache = eta.Cache(c.k_pages, c.v_pages, c.mu, c.radius, c.sigma, c.kmin, c.kmax, c.mu8, c.radius8,
+                               c.mu8_format, sub_block,
+                               torch.zeros(wl.num_pages, wl.h_kv, sb, wl.d, dtype=torch.float16, device=c.mu.device),
+                               torch.zeros(wl.num_pages, wl.h_kv, sb, dtype=torch.float32, device=c.mu.device))
+        self.sub_block = sub_block
+        self.ws = eta.alloc_workspace(self.cache, wl.n_seqs, wl.max_blocks, wl.h_q)
+        eta.build_block_summaries(self.cache, self.seq_lens, self.bt)
+        torch.cuda.synchronize()
 
     def step_bytes(self, st):
         """Bytes one step must move: admitted K/V tiles once per union block,
@@ -390,11 +423,11 @@ class Setup:
         wl = self.wl
         esz = 2 if wl.kv_dtype == "bf16" else 4
         union = int(st.union_per_kv.sum())
-        kv = union * 2 * 64 * wl.d * esz
+        kv = union * 2 * self.block_tokens() * wl.d * esz
         nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
         # records the screen reads: centroid and radius (and the deviation), or the key box
         rec = {"geometric": 2 * wl.d + 4, "dual": 4 * wl.d + 4, "quest": 4 * wl.d,
-               "geometric_fp8": wl.d + 4}[self.bound]
+               "geometric_fp8": wl.d + 4, "geometric_sub": (2 * wl.d + 4) * (64 // max(self.sub_block, 1))}[self.bound]
         meta = nfull * wl.h_kv * rec + int(self.nblk.sum()) * 4
         small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
         return kv, kv + meta + small
@@ -493,7 +526,7 @@ def main():
         prefill_bench(max(2, min(args.steps, 20)), min(args.warmup, 3), args.cpu_budget, args.no_cpu)
         return
 
-    S = Setup(args.workload, args.density, args.bound, args.z)
+    S = Setup(args.workload, args.density, args.bound, args.z, args.sub_block)
     S.calibrate()
     st, dens_head, dens_union = S.densities()
     kv_bytes, all_bytes = S.step_bytes(st)
@@ -532,7 +565,8 @@ def main():
                         + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
                         + {"geometric": "", "dual": f", dual screen z={args.z:g}",
                            "quest": ", comparator box-bound screen",
-                           "geometric_fp8": ", geometric screen over E4M3 records"}[args.bound],
+                           "geometric_fp8": ", geometric screen over E4M3 records",
+                           "geometric_sub": f", geometric screen on {args.sub_block}-token blocks"}[args.bound],
             "kv_dtype": wl.kv_dtype,
             "screen": f"dual z={args.z:g}" if args.bound == "dual" else args.bound,
             "seq_lens_total": int(wl.seq_lens.sum()),

@@ -58,7 +58,8 @@ typedef enum {
 enum { ETA_F32 = 0, ETA_BF16 = 1 };                 /* K/V/q element type */
 enum { ETA_TAU_LEARNED = 0, ETA_TAU_CALIBRATED = 1 }; /* threshold mode */
 enum { ETA_PHASE_ALL = -1, ETA_PHASE_SCREEN = 0, ETA_PHASE_ATTEND = 1, ETA_PHASE_MERGE = 2 };
-enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2, ETA_BOUND_GEOMETRIC_FP8 = 3 };
+enum { ETA_BOUND_GEOMETRIC = 0, ETA_BOUND_DUAL = 1, ETA_BOUND_QUEST = 2, ETA_BOUND_GEOMETRIC_FP8 = 3,
+       ETA_BOUND_GEOMETRIC_SUB = 4 };
                                                       /* block screen, see eta_screen_opts */
 enum { ETA_FP8_E4M3 = 0, ETA_FP8_E5M2 = 1 };          /* FP8 record formats (OCP 8-bit floats) */
 
@@ -97,6 +98,16 @@ enum { ETA_FP8_E4M3 = 0, ETA_FP8_E5M2 = 1 };          /* FP8 record formats (OCP
  *   mu8_format       : ETA_FP8_E4M3 (3 mantissa bits, largest 448) or
  *                      ETA_FP8_E5M2 (2 mantissa bits, largest 57344); read only
  *                      when mu8 is not NULL.
+ *   sub_block, mu_sub, radius_sub : screen blocks smaller than a page
+ *                      (Appendix F.3 ablates the block size; the reading taken):
+ *                      sub_block 16 or 32 tokens, so a page holds 64/sub_block
+ *                      consecutive blocks; mu_sub [num_pages][num_kv_heads]
+ *                      [64/sub_block][head_dim] float16 bits (16-byte aligned)
+ *                      and radius_sub [num_pages][num_kv_heads][64/sub_block]
+ *                      float32: the record of each such block, by the same
+ *                      rule as mu/radius. Both NULL, or both set; only
+ *                      ETA_BOUND_GEOMETRIC_SUB reads them; when set, the record
+ *                      builders fill them.
  * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
 typedef struct {
   int kv_dtype;
@@ -114,6 +125,9 @@ typedef struct {
   uint8_t* mu8;
   float* radius8;
   int mu8_format;
+  int sub_block;
+  uint16_t* mu_sub;
+  float* radius_sub;
 } eta_cache;
 
 /* Sequences of a batch.
@@ -194,6 +208,16 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
  *                         s (q . mu8 + ||q|| radius8): half the record bytes of
  *                         the float16 centroid, a coarser centroid and so a
  *                         larger radius. Needs cache->mu8 and cache->radius8.
+ *   ETA_BOUND_GEOMETRIC_SUB : the geometric bound on blocks of cache->sub_block
+ *                         tokens (records mu_sub/radius_sub). Screen, forced
+ *                         blocks (the partial last block, the lwb most recent
+ *                         complete ones), rescue and counts work on those
+ *                         blocks; the attention loads a page's rows only for
+ *                         the blocks some head of the group admitted and each
+ *                         head attends only to the tokens of its own blocks.
+ *                         eta_stats then reports per-head counts, union counts
+ *                         and the bitmap in these smaller blocks
+ *                         (max_blocks_per_seq * 64/sub_block bits per head).
  * The score also ranks blocks for the top-1 rescue. */
 typedef struct {
   int bound;
@@ -204,8 +228,8 @@ typedef struct {
  * for the whole step or one ETA_PHASE_*; screen NULL means the geometric bound.
  * Returns ETA_ERR_INVALID_ARGUMENT for an unknown bound, a negative or
  * non-finite z, the dual bound without cache->sigma, the comparator bound
- * without cache->kmin and cache->kmax, or the FP8 bound without cache->mu8
- * and cache->radius8. */
+ * without cache->kmin and cache->kmax, the FP8 bound without cache->mu8
+ * and cache->radius8, or the smaller-block bound without cache->mu_sub. */
 eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache,
                          const eta_seqs* seqs, const void* q, int num_q_heads, int tau_mode,
                          const float* w, const float* b_or_c, float a, float beta, int lwb,
@@ -233,7 +257,10 @@ eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* s
  *   rescued           [num_seqs][num_q_heads] uint8  1 if top-1 rescue fired (nullable)
  *   admitted_bitmap   [num_seqs][num_q_heads][ceil(max_blocks_per_seq/32)]
  *                     uint32, bit j%32 of word j/32 = block j admitted (nullable)
- * All output pointers are host pointers. Returns ETA_ERR_DEVICE_DATA (after
+ * Blocks are the screen's blocks: after a decode with ETA_BOUND_GEOMETRIC_SUB
+ * they are the cache's smaller blocks, and the bitmap has
+ * ceil(max_blocks_per_seq * 64/sub_block / 32) words per head (the sizes
+ * passed stay those of the decode call). All output pointers are host pointers. Returns ETA_ERR_DEVICE_DATA (after
  * filling the outputs) if that decode met invalid lengths or page ids, and
  * ETA_ERR_INVALID_ARGUMENT if the sizes do not match that decode. */
 eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,

@@ -16,13 +16,14 @@ import torch
 
 from . import _lib
 from ._lib import (  # noqa: F401
-    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_GEOMETRIC_FP8, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA,
+    ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_GEOMETRIC_FP8, ETA_BOUND_GEOMETRIC_SUB, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA,
     ETA_FP8_E4M3, ETA_FP8_E5M2, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
     ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ALL, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
     ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
 
 BLOCK = 64
+_WS_GLOB_SB = 7  # int32 slot of the workspace header holding the last decode's screen blocks per page
 _KV_DTYPES = {torch.bfloat16: ETA_BF16, torch.float32: ETA_F32}
 
 
@@ -67,6 +68,9 @@ class Cache:
     mu8: Optional[torch.Tensor] = None    # uint8 [num_pages][H_KV][d], FP8 centroid (FP8 screen)
     radius8: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV], radius about it
     mu8_format: str = "e4m3"              # "e4m3" or "e5m2"
+    sub_block: int = 0                    # 16 or 32: records of smaller screen blocks (0: none)
+    mu_sub: Optional[torch.Tensor] = None   # float16 [num_pages][H_KV][64/sub_block][d]
+    radius_sub: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV][64/sub_block]
 
     def __post_init__(self):
         _need(self.k_pages, "k_pages")
@@ -98,10 +102,20 @@ class Cache:
                 raise ValueError("mu8 must be [num_pages][H_KV][d] and radius8 [num_pages][H_KV]")
         if self.mu8_format not in ("e4m3", "e5m2"):
             raise ValueError("mu8_format must be 'e4m3' or 'e5m2'")
+        if (self.mu_sub is None) != (self.radius_sub is None) or (self.mu_sub is None) != (self.sub_block == 0):
+            raise ValueError("sub_block, mu_sub and radius_sub go together")
+        if self.mu_sub is not None:
+            if self.sub_block not in (16, 32):
+                raise ValueError("sub_block must be 16 or 32")
+            sb = BLOCK // self.sub_block
+            _need(self.mu_sub, "mu_sub", torch.float16, dev)
+            _need(self.radius_sub, "radius_sub", torch.float32, dev)
+            if tuple(self.mu_sub.shape) != (P, H, sb, D) or tuple(self.radius_sub.shape) != (P, H, sb):
+                raise ValueError("mu_sub must be [num_pages][H_KV][64/sub_block][d], radius_sub [num_pages][H_KV][64/sub_block]")
 
     @classmethod
     def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False,
-              with_box=False, fp8: Optional[str] = None):
+              with_box=False, fp8: Optional[str] = None, sub_block: int = 0):
         k = torch.zeros(num_pages, num_kv_heads, BLOCK, head_dim, dtype=dtype, device=device)
         v = torch.zeros_like(k)
         mu = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.float16, device=device)
@@ -111,7 +125,10 @@ class Cache:
         hi = torch.zeros_like(mu) if with_box else None
         mu8 = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.uint8, device=device) if fp8 else None
         r8 = torch.zeros_like(r) if fp8 else None
-        return cls(k, v, mu, r, sig, lo, hi, mu8, r8, fp8 or "e4m3")
+        sb = BLOCK // sub_block if sub_block else 0
+        mus = torch.zeros(num_pages, num_kv_heads, sb, head_dim, dtype=torch.float16, device=device) if sb else None
+        rs = torch.zeros(num_pages, num_kv_heads, sb, dtype=torch.float32, device=device) if sb else None
+        return cls(k, v, mu, r, sig, lo, hi, mu8, r8, fp8 or "e4m3", sub_block, mus, rs)
 
     @property
     def kv_dtype(self) -> int:
@@ -130,7 +147,8 @@ class Cache:
         return _lib.EtaCacheC(self.kv_dtype, D, H, B, P, _ptr(self.k_pages), _ptr(self.v_pages),
                               _ptr(self.mu), _ptr(self.radius), _ptr(self.sigma), _ptr(self.kmin),
                               _ptr(self.kmax), _ptr(self.mu8), _ptr(self.radius8),
-                              _lib.ETA_FP8_E4M3 if self.mu8_format == "e4m3" else _lib.ETA_FP8_E5M2)
+                              _lib.ETA_FP8_E4M3 if self.mu8_format == "e4m3" else _lib.ETA_FP8_E5M2,
+                              int(self.sub_block), _ptr(self.mu_sub), _ptr(self.radius_sub))
 
 
 def _seqs(seq_lens: torch.Tensor, block_table: torch.Tensor, device) -> _lib.EtaSeqsC:
@@ -178,8 +196,9 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
     """One ETA decode step; returns out [num_seqs][H_Q][d] float32.
     With `phase` set, runs only that phase (screen, attend or merge).
     bound: "geometric", "dual" (needs cache.sigma; z deviations), "quest"
-    (the comparator's box bound; needs cache.kmin and cache.kmax) or
-    "geometric_fp8" (the geometric bound over cache.mu8 / cache.radius8)."""
+    (the comparator's box bound; needs cache.kmin and cache.kmax),
+    "geometric_fp8" (the geometric bound over cache.mu8 / cache.radius8) or
+    "geometric_sub" (the geometric bound on cache.sub_block-token blocks)."""
     dev = cache.k_pages.device
     _need(q, "q", cache.k_pages.dtype, dev)
     N, HQ, D = q.shape
@@ -201,9 +220,9 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
             _check(_lib.lib().eta_decode(*args), "eta_decode")
         else:
             _check(_lib.lib().eta_decode_phase(int(phase), *args), "eta_decode_phase")
-    elif bound in ("dual", "quest", "geometric_fp8"):
+    elif bound in ("dual", "quest", "geometric_fp8", "geometric_sub"):
         code = {"dual": _lib.ETA_BOUND_DUAL, "quest": _lib.ETA_BOUND_QUEST,
-                "geometric_fp8": _lib.ETA_BOUND_GEOMETRIC_FP8}[bound]
+                "geometric_fp8": _lib.ETA_BOUND_GEOMETRIC_FP8, "geometric_sub": _lib.ETA_BOUND_GEOMETRIC_SUB}[bound]
         opts = _lib.EtaScreenOptsC(code, float(z))
         ph = _lib.ETA_PHASE_ALL if phase is None else int(phase)
         _check(_lib.lib().eta_decode_ex(ph, ctypes.byref(opts), *args), "eta_decode_ex")
@@ -293,12 +312,21 @@ class Stats:
 
 
 def stats(workspace: torch.Tensor, num_seqs: int, max_blocks_per_seq: int, num_q_heads: int,
-          num_kv_heads: int, bitmap: bool = True, stream=None, check: bool = True) -> Stats:
+          num_kv_heads: int, bitmap: bool = True, stream=None, check: bool = True,
+          blocks_per_page: Optional[int] = None) -> Stats:
+    """Counts of the last decode on this workspace. blocks_per_page: screen
+    blocks per 64-token page of that decode (64 / sub_block after a
+    "geometric_sub" decode, else 1), which sizes the bitmap; read from the
+    workspace's header when not given."""
+    if blocks_per_page is None:
+        blocks_per_page = int(workspace[:64].view(torch.int32)[_WS_GLOB_SB].item()) if bitmap else 1
+        blocks_per_page = blocks_per_page if blocks_per_page in (2, 4) else 1
     a = np.zeros((num_seqs, num_q_heads), np.int32)
     u = np.zeros((num_seqs, num_kv_heads), np.int32)
     t = np.zeros((num_seqs, num_q_heads), np.int64)
     r = np.zeros((num_seqs, num_q_heads), np.uint8)
-    bm = np.zeros((num_seqs, num_q_heads, (max_blocks_per_seq + 31) // 32), np.uint32) if bitmap else None
+    bm = np.zeros((num_seqs, num_q_heads, (max_blocks_per_seq * blocks_per_page + 31) // 32), np.uint32) \
+        if bitmap else None
     st = _lib.lib().eta_stats(_ptr(workspace), num_seqs, max_blocks_per_seq, num_q_heads, num_kv_heads,
                               a.ctypes.data, u.ctypes.data, t.ctypes.data, r.ctypes.data,
                               None if bm is None else bm.ctypes.data, _stream(stream))

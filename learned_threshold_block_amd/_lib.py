@@ -30,6 +30,7 @@ ETA_BOUND_GEOMETRIC = 0
 ETA_BOUND_DUAL = 1
 ETA_BOUND_QUEST = 2
 ETA_BOUND_GEOMETRIC_FP8 = 3
+ETA_BOUND_GEOMETRIC_SUB = 4
 ETA_FP8_E4M3 = 0
 ETA_FP8_E5M2 = 1
 
@@ -64,6 +65,9 @@ class EtaCacheC(ctypes.Structure):
         ("mu8", ctypes.c_void_p),
         ("radius8", ctypes.c_void_p),
         ("mu8_format", ctypes.c_int),
+        ("sub_block", ctypes.c_int),
+        ("mu_sub", ctypes.c_void_p),
+        ("radius_sub", ctypes.c_void_p),
     ]
 
 

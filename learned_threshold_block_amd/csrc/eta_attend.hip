@@ -50,8 +50,11 @@ struct AttendArgs {
 // Entries [c, c + cnt) of the segment's compacted lists, one per lane
 // (lane < cnt): the tile whose prefix covers the index is found by binary
 // search over the prefix in LDS (index ntn is the rescue tile).
+// With smaller screen blocks (tsub not null), *sw receives the entry's word of
+// per-head block bits from the same position of the parallel list.
 __device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2* tents, int ntn, int NT,
-                                                int c, int cnt, int lane) {
+                                                int c, int cnt, int lane, const uint32_t* tsub = nullptr,
+                                                uint32_t* sw = nullptr) {
   int2 ev = make_int2(0, 0);
   if (lane < cnt) {
     const int x = c + lane;
@@ -62,7 +65,9 @@ __device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2*
       else hi_v = mid - 1;
     }
     const int phys = lo_v < ntn ? lo_v : NT;
-    ev = tents[(int64_t)phys * kTile + (x - toff_lds[lo_v])];
+    const int64_t at = (int64_t)phys * kTile + (x - toff_lds[lo_v]);
+    ev = tents[at];
+    if (tsub) *sw = tsub[at];
   }
   return ev;
 }
@@ -175,7 +180,23 @@ constexpr int attend_waves() {
   return ((T::kBytes == 2 || D == 64) && G <= 4) ? 8 : 4;
 }
 
-template <typename T, int D, int G>
+// Bit q set when some head of the group admitted block q of the page (word
+// of per-head block bits, bit q G + h).
+template <int G>
+__device__ __forceinline__ uint32_t block_union(uint32_t sw, int sb) {
+  constexpr uint32_t full = (1u << G) - 1u;
+  uint32_t u = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (q < sb && ((sw >> (q * G)) & full)) u |= 1u << q;
+  return u;
+}
+
+// SUBB: screen blocks smaller than a page (2 or 4 per page, A.d.SB): each
+// entry carries a word of per-head block bits (bit q G + h); a head attends
+// only to the rows of its own blocks, and rows of blocks that no head of the
+// group admitted are not loaded.
+template <typename T, int D, int G, bool SUBB>
 __global__ __launch_bounds__((64 * attend_waves<T, D, G>()))
 __attribute__((amdgpu_waves_per_eu((attend_waves<T, D, G>() / 4), (attend_waves<T, D, G>() / 4))))
 void k_attend(AttendArgs A) {
@@ -267,6 +288,8 @@ void k_attend(AttendArgs A) {
   for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
   const St* kbase = (const St*)A.c.k;
   const St* vbase = (const St*)A.c.v;
+  // smaller screen blocks: log2 of their tokens, and the block of load i's rows
+  const int lbs = SUBB ? (A.d.SB == 4 ? 4 : 5) : 6;
 
   while (lo < hi) {
     while (lo >= (int64_t)P + Us) {  // next segment with entries
@@ -319,6 +342,7 @@ void k_attend(AttendArgs A) {
     if (threadIdx.x == 0) ctr_lds = e0;
     __syncthreads();
     const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
+    const uint32_t* tsubs = SUBB ? A.ws.tile_sub + (int64_t)s * (NT + 1) * kTile : nullptr;
 
     // claims, two deep: the batch being streamed, the next one (resolved while
     // the current one streams) and the claim after it
@@ -327,41 +351,51 @@ void k_attend(AttendArgs A) {
     const int c0 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
     int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
     if (bc > 0) {
-      int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane);
+      uint32_t ews = 0, ewsn = 0;
+      int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane, tsubs, &ews);
       const int c1 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
       int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
-      int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane);
+      int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane, tsubs, &ewsn);
       int it = 0;
       int page_nx = __builtin_amdgcn_readlane(ev.x, 0);
       int jm_nx = __builtin_amdgcn_readlane(ev.y, 0);
+      uint32_t sw_nx = SUBB ? (uint32_t)__builtin_amdgcn_readlane((int)ews, 0) : 0u;
 
       uint4 kr[NI][CPL], vr[NI][CPL];
       {
         const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
+        const uint32_t ub = SUBB ? block_union<G>(sw_nx, A.d.SB) : 0u;
 #pragma unroll
         for (int i = 0; i < NI; ++i)
 #pragma unroll
-          for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
+          for (int c = 0; c < CPL; ++c)
+            kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(kt + loff[c] + i * RPI * D)
+                                                                   : make_uint4(0, 0, 0, 0);
       }
       for (;;) {
         const int cur_page = page_nx, cur_jm = jm_nx;
+        const uint32_t cur_sw = sw_nx;
         {
           const St* vt = vbase + ((int64_t)cur_page * HKV + g) * (kBlock * D);
+          const uint32_t ub = SUBB ? block_union<G>(cur_sw, A.d.SB) : 0u;
 #pragma unroll
           for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) vr[i][c] = *(const uint4*)(vt + loff[c] + i * RPI * D);
+            for (int c = 0; c < CPL; ++c)
+              vr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(vt + loff[c] + i * RPI * D)
+                                                                     : make_uint4(0, 0, 0, 0);
         }
         // next entry: from this batch, or the first of the next one
         bool has_next = true;
         if (++it >= bc) {
           ev = evn;
+          ews = ewsn;
           bc = bcn;
           it = 0;
           if (bc > 0) {
             const int c2 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
             bcn = c2 < e1 ? min(kClaim, e1 - c2) : 0;
-            evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane);
+            evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane, tsubs, &ewsn);
           } else {
             has_next = false;
           }
@@ -369,6 +403,7 @@ void k_attend(AttendArgs A) {
         if (has_next) {
           page_nx = __builtin_amdgcn_readlane(ev.x, it);
           jm_nx = __builtin_amdgcn_readlane(ev.y, it);
+          if (SUBB) sw_nx = (uint32_t)__builtin_amdgcn_readlane((int)ews, it);
         }
         const uint32_t hmask = (uint32_t)cur_jm & 0xffu;
         const int j = cur_jm >> 8;
@@ -404,6 +439,7 @@ void k_attend(AttendArgs A) {
           const float sg = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-x * kLog2e));
           float sv = S_ * sg;
           if (tail && tok >= rem) sv = -__builtin_inff();
+          if (SUBB && !((cur_sw >> ((tok >> lbs) * G + h)) & 1u)) sv = -__builtin_inff();  // not this head's block
           const float mt = group_max<LPR>(sv);
           const float mnew = fmaxf(m[h], mt);
           const float muse = mnew == -__builtin_inff() ? 0.f : mnew;
@@ -419,10 +455,13 @@ void k_attend(AttendArgs A) {
         // ---- K of the next tile streams while the values are accumulated
         if (has_next) {
           const St* kt = kbase + ((int64_t)page_nx * HKV + g) * (kBlock * D);
+          const uint32_t ub = SUBB ? block_union<G>(sw_nx, A.d.SB) : 0u;
 #pragma unroll
           for (int i = 0; i < NI; ++i)
 #pragma unroll
-            for (int c = 0; c < CPL; ++c) kr[i][c] = *(const uint4*)(kt + loff[c] + i * RPI * D);
+            for (int c = 0; c < CPL; ++c)
+              kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(kt + loff[c] + i * RPI * D)
+                                                                     : make_uint4(0, 0, 0, 0);
         }
         if (tail) {  // junk rows past the end must not reach the sums (0 * NaN)
 #pragma unroll
@@ -590,7 +629,8 @@ template <typename T, int D, int G>
 hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, int W, hipStream_t st) {
   AttendArgs a{c, s, p, d, ws};
-  hipLaunchKernelGGL((k_attend<T, D, G>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
+  if (d.SB > 1) hipLaunchKernelGGL((k_attend<T, D, G, true>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
+  else hipLaunchKernelGGL((k_attend<T, D, G, false>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
   return hipGetLastError();
 }
 
@@ -609,7 +649,7 @@ hipError_t attend_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
 template <typename T, int D, int G>
 int occupancy_impl() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G, false>),
                                                    64 * attend_waves<T, D, G>(), 0) != hipSuccess)
     return 1;
   return nb > 0 ? nb : 1;

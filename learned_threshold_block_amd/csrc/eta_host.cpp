@@ -33,6 +33,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.tau = (float*)take(sizeof(float) * nq);
   w.tile_cnt = (int32_t*)take(sizeof(int32_t) * S * (NT + 1));
   w.tile_ent = (int2*)take(sizeof(int2) * S * (NT + 1) * kTile);
+  w.tile_sub = (uint32_t*)take(d.SB > 1 ? sizeof(uint32_t) * S * (NT + 1) * kTile : 0);
   w.tile_off = (int32_t*)take(sizeof(int32_t) * S * (NT + 2));
   w.tile_hcnt = (int32_t*)take(sizeof(int32_t) * S * NT * G);
   w.tile_bits = (uint64_t*)take(sizeof(uint64_t) * S * G * NT);
@@ -40,6 +41,7 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.tile_uarg = (int32_t*)take(sizeof(int32_t) * S * NT * G);
   w.tile_err = (int32_t*)take(sizeof(int32_t) * S * NT);
   w.seg_U = (int32_t*)take(sizeof(int32_t) * S);
+  w.seg_ub = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_done = (uint64_t*)take(sizeof(uint64_t) * S);
@@ -71,6 +73,9 @@ eta_status check_cache(const eta_cache* c) {
   if ((c->mu8 == nullptr) != (c->radius8 == nullptr) || !aligned(c->mu8, 16) || !aligned(c->radius8, 4))
     return ETA_ERR_INVALID_ARGUMENT;
   if (c->mu8 && c->mu8_format != ETA_FP8_E4M3 && c->mu8_format != ETA_FP8_E5M2) return ETA_ERR_INVALID_ARGUMENT;
+  if ((c->mu_sub == nullptr) != (c->radius_sub == nullptr) || !aligned(c->mu_sub, 16) || !aligned(c->radius_sub, 4))
+    return ETA_ERR_INVALID_ARGUMENT;
+  if (c->mu_sub && c->sub_block != 16 && c->sub_block != 32) return ETA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
   if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
   if ((int64_t)c->num_pages * c->num_kv_heads > (int64_t)1 << 31) return ETA_ERR_UNSUPPORTED;
@@ -103,6 +108,9 @@ CacheView view_of(const eta_cache* c) {
   v.mu8 = c->mu8;
   v.radius8 = c->radius8;
   v.mu8_fmt = c->mu8_format == ETA_FP8_E5M2 ? 1 : 0;
+  v.sub = c->mu_sub ? kBlock / c->sub_block : 0;
+  v.mu_sub = c->mu_sub;
+  v.radius_sub = c->radius_sub;
   return v;
 }
 
@@ -115,7 +123,7 @@ SeqView view_of(const eta_seqs* s) {
   return v;
 }
 
-eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d) {
+eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d, int SB = 1) {
   if (N < 1 || MB < 1 || HQ < 1) return ETA_ERR_INVALID_ARGUMENT;
   if (HQ % c->num_kv_heads) return ETA_ERR_INVALID_ARGUMENT;
   const int G = HQ / c->num_kv_heads;
@@ -130,9 +138,16 @@ eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d) {
   d->D = c->head_dim;
   d->G = G;
   d->S = (int)S;
-  d->NT = (MB + kTile - 1) / kTile;
+  // smaller screen blocks multiply the blocks per sequence (the attend kernel
+  // keeps a sequence's tile prefix in LDS, sized for kMaxBlocksPerSeq blocks)
+  if ((int64_t)MB * SB > kMaxBlocksPerSeq || S * MB * SB >= ((int64_t)1 << 31) / 64) return ETA_ERR_UNSUPPORTED;
+  d->SB = SB;
+  d->NT = (MB * SB + kTile - 1) / kTile;
   return ETA_OK;
 }
+
+// Screen blocks per page of the cache's smaller-block records (1 if none).
+int sub_blocks(const eta_cache* c) { return c->mu_sub ? kBlock / c->sub_block : 1; }
 
 // attend grid: one resident wave of workgroups over the whole device
 std::mutex g_geom_mu;
@@ -182,7 +197,7 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
   P->p.z = 0.f;
   if (screen) {
     if (screen->bound != ETA_BOUND_GEOMETRIC && screen->bound != ETA_BOUND_DUAL && screen->bound != ETA_BOUND_QUEST &&
-        screen->bound != ETA_BOUND_GEOMETRIC_FP8)
+        screen->bound != ETA_BOUND_GEOMETRIC_FP8 && screen->bound != ETA_BOUND_GEOMETRIC_SUB)
       return ETA_ERR_INVALID_ARGUMENT;
     if (screen->bound == ETA_BOUND_DUAL) {
       if (!cache->sigma || !isfinite(screen->z) || !(screen->z >= 0.f)) return ETA_ERR_INVALID_ARGUMENT;
@@ -197,6 +212,10 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
       if (!cache->mu8 || !cache->radius8) return ETA_ERR_INVALID_ARGUMENT;
       P->p.bound = 3;
     }
+    if (screen->bound == ETA_BOUND_GEOMETRIC_SUB) {
+      if (!cache->mu_sub) return ETA_ERR_INVALID_ARGUMENT;
+      P->p.bound = 4;
+    }
   }
   st = check_seqs(seqs);
   if (st != ETA_OK) return st;
@@ -206,7 +225,8 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
   if (tau_mode != ETA_TAU_LEARNED && tau_mode != ETA_TAU_CALIBRATED) return ETA_ERR_INVALID_ARGUMENT;
   if (tau_mode == ETA_TAU_LEARNED && (!w || !aligned(w, 16))) return ETA_ERR_INVALID_ARGUMENT;
   if (!(beta > 0.f) || !isfinite(beta) || !isfinite(a) || lwb < 0) return ETA_ERR_INVALID_ARGUMENT;
-  st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &P->d);
+  st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &P->d,
+               P->p.bound == 4 ? sub_blocks(cache) : 1);
   if (st != ETA_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return ETA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < workspace_layout(P->d, nullptr, nullptr)) return ETA_ERR_WORKSPACE_TOO_SMALL;
@@ -307,7 +327,8 @@ size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_b
                                  int num_q_heads) {
   if (check_cache(cache) != ETA_OK) return 0;
   Dims d;
-  if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d) != ETA_OK) return 0;
+  // large enough for a decode on the cache's smallest screen blocks as well
+  if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d, sub_blocks(cache)) != ETA_OK) return 0;
   return workspace_layout(d, nullptr, nullptr);
 }
 
@@ -424,6 +445,13 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
   if (num_seqs < 1 || max_blocks_per_seq < 1 || num_kv_heads < 1 || num_q_heads < 1 ||
       num_q_heads % num_kv_heads)
     return ETA_ERR_INVALID_ARGUMENT;
+  hipStream_t st = (hipStream_t)stream;
+  if (hipStreamSynchronize(st) != hipSuccess) return ETA_ERR_HIP;
+  int32_t glob[kGlobCount];  // the header region sits at the workspace's start whatever the sizes
+  if (hipMemcpy(glob, workspace, sizeof(glob), hipMemcpyDeviceToHost) != hipSuccess) return ETA_ERR_HIP;
+  if (glob[kGlobN] != num_seqs || glob[kGlobMB] != max_blocks_per_seq || glob[kGlobHQ] != num_q_heads ||
+      glob[kGlobHKV] != num_kv_heads)
+    return ETA_ERR_INVALID_ARGUMENT;
   Dims d;
   d.N = num_seqs;
   d.MB = max_blocks_per_seq;
@@ -431,22 +459,16 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
   d.HKV = num_kv_heads;
   d.G = num_q_heads / num_kv_heads;
   d.S = num_seqs * num_kv_heads;
-  d.NT = (max_blocks_per_seq + kTile - 1) / kTile;
+  d.SB = (glob[kGlobSB] == 2 || glob[kGlobSB] == 4) ? glob[kGlobSB] : 1;
+  d.NT = (max_blocks_per_seq * d.SB + kTile - 1) / kTile;
   d.D = 128;  // only the part_* sizes depend on D; they lie after everything read here
   Ws ws;
   workspace_layout(d, const_cast<void*>(workspace), &ws);
-  hipStream_t st = (hipStream_t)stream;
-  if (hipStreamSynchronize(st) != hipSuccess) return ETA_ERR_HIP;
-  int32_t glob[kGlobCount];
-  if (hipMemcpy(glob, ws.glob, sizeof(glob), hipMemcpyDeviceToHost) != hipSuccess) return ETA_ERR_HIP;
-  if (glob[kGlobN] != num_seqs || glob[kGlobMB] != max_blocks_per_seq || glob[kGlobHQ] != num_q_heads ||
-      glob[kGlobHKV] != num_kv_heads)
-    return ETA_ERR_INVALID_ARGUMENT;
   const size_t nq = (size_t)num_seqs * num_q_heads;
   std::vector<int32_t> tmp(nq);
   if (hipMemcpy(admitted_per_head, ws.st_head, sizeof(int32_t) * nq, hipMemcpyDeviceToHost) != hipSuccess)
     return ETA_ERR_HIP;
-  if (hipMemcpy(union_per_kv, ws.seg_U, sizeof(int32_t) * d.S, hipMemcpyDeviceToHost) != hipSuccess)
+  if (hipMemcpy(union_per_kv, ws.seg_ub, sizeof(int32_t) * d.S, hipMemcpyDeviceToHost) != hipSuccess)
     return ETA_ERR_HIP;
   if (tokens_per_head &&
       hipMemcpy(tokens_per_head, ws.st_tokens, sizeof(int64_t) * nq, hipMemcpyDeviceToHost) != hipSuccess)
@@ -459,7 +481,7 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
   if (admitted_bitmap) {
     // tile_bits is [S][G][NT] == [N][HQ][NT] uint64 words, little-endian: the
     // same bit order as [N][HQ][2*NT] uint32 words
-    const size_t words32 = (size_t)(max_blocks_per_seq + 31) / 32;
+    const size_t words32 = (size_t)(max_blocks_per_seq * d.SB + 31) / 32;
     std::vector<uint64_t> bits(nq * d.NT);
     if (hipMemcpy(bits.data(), ws.tile_bits, sizeof(uint64_t) * bits.size(), hipMemcpyDeviceToHost) != hipSuccess)
       return ETA_ERR_HIP;

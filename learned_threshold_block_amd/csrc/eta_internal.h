@@ -28,11 +28,13 @@ enum Glob : int {
   kGlobD = 4,
   kGlobStatMagic = 5,  // kStatMagic once an attend kernel has written rng_stat
   kGlobStatW = 6,      // ranges that attend kernel had
+  kGlobSB = 7,         // screen blocks per page of the last decode (1, 2 or 4)
   kGlobCount = 16
 };
 
 struct Dims {
-  int N, MB, HQ, HKV, D, G, S, NT;  // S = N*HKV segments, NT = tiles of 64 blocks per segment
+  int N, MB, HQ, HKV, D, G, S, NT;  // S = N*HKV segments, NT = tiles of 64 screen blocks per segment
+  int SB;                           // screen blocks per 64-token page: 1 (b = 64), 2 (b = 32) or 4 (b = 16)
 };
 
 // Device pointers into one caller-provided workspace.
@@ -40,7 +42,9 @@ struct Ws {
   int32_t* glob;        // [kGlobCount]
   float* tau;           // [N*HQ]       effective thresholds
   int32_t* tile_cnt;    // [S][NT+1]    admitted union blocks per tile (tile NT: rescue entries)
-  int2* tile_ent;       // [S][NT+1][64] (page, (j << 8) | head mask), ascending j within a tile
+  int2* tile_ent;       // [S][NT+1][64] (page, (j << 8) | head mask), ascending page index j within a tile
+  uint32_t* tile_sub;   // [S][NT+1][64] with screen blocks smaller than a page: bit q G + h = head h
+                        //              admitted block q of the entry's page
   int32_t* tile_off;    // [S][NT+2]    exclusive prefix of tile_cnt over the segment's used tiles,
                         //              the rescue tile last (index ntn), total at ntn+1
   int32_t* tile_hcnt;   // [S][NT][G]   admitted blocks per head per tile
@@ -48,7 +52,8 @@ struct Ws {
   float* tile_umax;     // [S][NT][G]   largest bound among complete blocks
   int32_t* tile_uarg;   // [S][NT][G]   its block index (lowest on ties)
   int32_t* tile_err;    // [S][NT]
-  int32_t* seg_U;       // [S]          union blocks per segment
+  int32_t* seg_U;       // [S]          union entries (pages) per segment
+  int32_t* seg_ub;      // [S]          screen blocks admitted by any head of the segment
   int32_t* seg_ntn;     // [S]          tiles of 64 blocks the segment uses
   int32_t* seg_err;     // [S]
   uint64_t* seg_done;   // [S]          arrivals (zeroed by finalize): bits 0-31 entries whose partial is
@@ -79,6 +84,9 @@ struct CacheView {
   uint8_t* mu8;     // may be null (with radius8): FP8 centroids
   float* radius8;
   int mu8_fmt;      // 0 E4M3, 1 E5M2
+  int sub;          // records of smaller screen blocks: blocks per page (2 or 4), 0 if none
+  uint16_t* mu_sub;  // [pages][HKV][sub][D]
+  float* radius_sub;  // [pages][HKV][sub]
 };
 
 struct SeqView {
@@ -97,7 +105,7 @@ struct DecodeParams {
   float* out;
   int deterministic;  // static work split and claims: bitwise-reproducible results
   int bound;          // 0 geometric, 1 dual (tightened by z deviations), 2 comparator box bound,
-                      // 3 geometric over the FP8 records
+                      // 3 geometric over the FP8 records, 4 geometric over smaller screen blocks
   float z;
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };

@@ -366,6 +366,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                             A.c.mu8 ? A.c.radius8 + rec : nullptr, A.c.mu8_fmt, lane);
     }
   }
+  // records of the smaller screen blocks (16 or 32 tokens) that end in this tile
+  if (hc == 0 && A.c.sub) {
+    const int sb = A.c.sub, rows = kBlock / sb;
+    for (int q = wave; q < QT / rows; q += kPfWaves) {
+      const int js = P0 / rows + q;
+      if (js * rows + rows > T) break;
+      const int page = bt[js / sb];
+      if (page < 0 || page >= A.c.num_pages) continue;
+      const int64_t srec = ((int64_t)page * HKV + g) * sb + js % sb;
+      const uint16_t* tile = (const uint16_t*)A.c.k + srec * rows * D;
+      if (rows == 16)
+        build_record<Bf16, D, 16>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, 0, lane);
+      else
+        build_record<Bf16, D, 32>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, 0, lane);
+    }
+  }
 }
 
 template <int D, int G>

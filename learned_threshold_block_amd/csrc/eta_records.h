@@ -25,8 +25,9 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
   return *p;
 }
 
-// One wavefront. tile: [64][D] keys of one (page, kv head). If override_row is
-// non-null, row 63 is read from it instead of the tile. Lanes own columns;
+// One wavefront. tile: [ROWS][D] keys of one block (a whole 64-token page, or
+// a 16- or 32-token block of it). If override_row is non-null, the last row is
+// read from it instead of the tile. Lanes own columns;
 // the rows are read twice (sums, then distances and deviations), which keeps
 // the register footprint small enough for eight wavefronts per SIMD. Writes
 // the centroid and radius, the coordinate deviation if sig_out is not null,
@@ -36,7 +37,7 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
 // the FP8 record if mu8_out is not null: the mean rounded to the FP8 format
 // fmt8 (nearest even, saturating) and the radius about it, rounded up like R^
 // (zero centroid and infinite radius for a block with a non-finite key).
-template <typename T, int D>
+template <typename T, int D, int ROWS = kBlock>
 __device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
                              uint16_t* mu_out, float* r_out, uint16_t* sig_out, uint16_t* kmin_out,
                              uint16_t* kmax_out, uint8_t* mu8_out, float* r8_out, int fmt8, int lane) {
@@ -50,8 +51,8 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     cmin[c] = __builtin_inff();
     cmax[c] = -__builtin_inff();
   }
-  for (int r = 0; r < kBlock; ++r) {
-    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
+  for (int r = 0; r < ROWS; ++r) {
+    const typename T::Stored* row = (r == ROWS - 1 && override_row) ? override_row : tile + r * D;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const float x = load_elem<T>(row + lane * CPL + c);
@@ -66,7 +67,7 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
   bool ok = finite;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    mean[c] = sum[c] * (1.0 / kBlock);
+    mean[c] = sum[c] * (1.0 / ROWS);
     dev2[c] = 0.0;
     h[c] = f64_to_f16_rne(mean[c]);
     ok = ok && ((h[c] & 0x7c00u) != 0x7c00u);
@@ -95,8 +96,8 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     mu_out[lane * CPL + c] = h[c];
   }
   double rmax = 0.0, rmax8 = 0.0;
-  for (int r = 0; r < kBlock; ++r) {
-    const typename T::Stored* row = (r == kBlock - 1 && override_row) ? override_row : tile + r * D;
+  for (int r = 0; r < ROWS; ++r) {
+    const typename T::Stored* row = (r == ROWS - 1 && override_row) ? override_row : tile + r * D;
     double part = 0.0, part8 = 0.0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
@@ -121,7 +122,7 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
   if (sig_out) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const double sd = sqrt(dev2[c] * (1.0 / kBlock));
+      const double sd = sqrt(dev2[c] * (1.0 / ROWS));
       sig_out[lane * CPL + c] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
     }
   }

@@ -14,6 +14,10 @@
 //             s sum_i max(q_i kmax_i, q_i kmin_i) of the block's key box
 //   fp8       or the geometric bound over the FP8 records (centroid mu8 in an
 //             8-bit float, radius about it)
+//   blocks    or the geometric bound on screen blocks of 16 or 32 tokens (2 or
+//             4 per page, each with its own record; Appendix F.3's block size):
+//             the block index j then counts those blocks, and the compacted
+//             entries stay one per page, with a word of per-head block bits
 //   counts    per-head blocks, union blocks, attended tokens (F.4)
 //
 // k_screen: one wavefront per 64 consecutive blocks of one (sequence, KV head).
@@ -63,10 +67,11 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
 }
 
 // MODE: 0 geometric bound, 1 dual score, 2 comparator box bound, 3 geometric
-// bound over the FP8 records.
+// bound over the FP8 records, 4 geometric bound on smaller screen blocks
+// (SB = A.d.SB of them per page).
 template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
-  constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3;
+  constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3, SUBB = MODE == 4;
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
@@ -83,6 +88,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     A.ws.glob[kGlobHQ] = HQ;
     A.ws.glob[kGlobHKV] = HKV;
     A.ws.glob[kGlobD] = D;
+    A.ws.glob[kGlobSB] = A.d.SB;
   }
   if (t >= NT) return;
   const int64_t tix = (int64_t)s * NT + t;
@@ -94,11 +100,13 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   //      queries and predictor weights; then centroids and radii
   const int seq_len = A.s.lens[n];
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  // screen blocks per page (1 unless SUBB) and its log2
+  const int SB = SUBB ? A.d.SB : 1, lsb = SUBB ? (A.d.SB == 4 ? 2 : 1) : 0;
   int pg[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) pg[i] = bt[min(j0 + RPI * i + r, MB - 1)];
+  for (int i = 0; i < NI; ++i) pg[i] = bt[min((j0 + RPI * i + r) >> lsb, MB - 1)];
   const int jl = j0 + RPI * cb + r;  // block this lane owns after the reduction
-  const int page_l = bt[min(jl, MB - 1)];
+  const int page_l = bt[min(jl >> lsb, MB - 1)];
 
   float qf[G][8];
   const auto* qbase = (const typename T::Stored*)A.p.q;
@@ -122,15 +130,18 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   // tiles past the sequence run through with every block invalid: no entries,
   // zero bitmap words
   const bool badT = seq_len < 1 || seq_len > kBlock * MB;
-  const int nfull = badT ? 0 : seq_len / kBlock;
-  const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
+  const int bsz = kBlock >> lsb;  // tokens per screen block
+  const int nfull = badT ? 0 : seq_len / bsz;
+  const int nblk = badT ? 0 : (seq_len + bsz - 1) / bsz;
   const bool lvalid = jl < nblk && page_l >= 0 && page_l < A.c.num_pages;
   const bool complete = jl < nfull && lvalid;
   // records through buffer loads: an invalid block reads zeros, without a branch
-  // (the box bound reads the key box's lower corner here and its upper one below)
-  const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : (const void*)A.c.mu,
-                                 (uint32_t)((int64_t)A.c.num_pages * HKV * D * 2));
-  const auto r_rsrc = make_rsrc(A.c.radius, (uint32_t)((int64_t)A.c.num_pages * HKV * 4));
+  // (the box bound reads the key box's lower corner here and its upper one below;
+  // a smaller screen block's record is block j mod SB of its page's records)
+  const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : SUBB ? (const void*)A.c.mu_sub : (const void*)A.c.mu,
+                                 (uint32_t)((int64_t)A.c.num_pages * HKV * SB * D * 2));
+  const auto r_rsrc = make_rsrc(SUBB ? (const void*)A.c.radius_sub : (const void*)A.c.radius,
+                                (uint32_t)((int64_t)A.c.num_pages * HKV * SB * 4));
   const auto mu8_rsrc = make_rsrc(A.c.mu8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * D) : 0u);
   const auto r8_rsrc = make_rsrc(A.c.radius8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * 4) : 0u);
   uint4 raw[NI];  // FP8: the lane's 8 bytes in .x/.y
@@ -143,12 +154,13 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(mu8_rsrc, off, 0, 0);
       raw[i] = make_uint4(v[0], v[1], 0u, 0u);
     } else {
-      const uint32_t off = ok ? (uint32_t)((((int64_t)pg[i] * HKV + g) * D + cb * 8) * 2) : kOutOfRange;
+      const int64_t rec = ((int64_t)pg[i] * HKV + g) * SB + (j & (SB - 1));
+      const uint32_t off = ok ? (uint32_t)((rec * D + cb * 8) * 2) : kOutOfRange;
       const auto v = __builtin_amdgcn_raw_buffer_load_b128(mu_rsrc, off, 0, 0);
       raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
-  const uint32_t roff = complete ? (uint32_t)(((int64_t)page_l * HKV + g) * 4) : kOutOfRange;
+  const uint32_t roff = complete ? (uint32_t)((((int64_t)page_l * HKV + g) * SB + (jl & (SB - 1))) * 4) : kOutOfRange;
   const float R = BOX ? 0.f
                       : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(FP8 ? r8_rsrc : r_rsrc, roff, 0, 0));
   // dual screen: coordinate deviations; box bound: upper corners (both laid
@@ -298,9 +310,30 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       A.ws.tile_uarg[tix * G + h] = at ? j0 + (int)__builtin_ctzll(at) : INT_MAX;
     }
   }
-  const uint64_t ball = __ballot(mb != 0);
-  const int pos = __popcll(ball & ((1ull << lane) - 1ull));
-  if (mb) A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, ((j0 + lane) << 8) | (int)mb);
+  uint64_t ball;
+  if constexpr (SUBB) {
+    // one entry per page: the SB lanes of a page gather their head masks into
+    // one word (bit q G + h: head h admitted block q of the page); the page's
+    // first lane writes the entry with the union of the heads
+    uint32_t sw = mb << ((lane & (SB - 1)) * G);
+    sw |= (uint32_t)__shfl_xor((int)sw, 1, 64);
+    if (SB == 4) sw |= (uint32_t)__shfl_xor((int)sw, 2, 64);
+    uint32_t um = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < SB) um |= (sw >> (q * G)) & full;
+    const bool lead = (lane & (SB - 1)) == 0 && um != 0;
+    ball = __ballot(lead);
+    const int pos = __popcll(ball & ((1ull << lane) - 1ull));
+    if (lead) {
+      A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, (((j0 + lane) >> lsb) << 8) | (int)um);
+      A.ws.tile_sub[tcx * kTile + pos] = sw;
+    }
+  } else {
+    ball = __ballot(mb != 0);
+    const int pos = __popcll(ball & ((1ull << lane) - 1ull));
+    if (mb) A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, ((j0 + lane) << 8) | (int)mb);
+  }
   const bool bad_page = jl < nblk && !lvalid;
   const bool any_bad = __any(bad_page);
   if (lane == 0) {
@@ -412,8 +445,10 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int n = s / HKV, g = s % HKV;
   const int seq_len = A.s.lens[n];
   const bool badT = seq_len < 1 || seq_len > kBlock * MB;
-  const int nfull = badT ? 0 : seq_len / kBlock;
-  const int nblk = badT ? 0 : (seq_len + kBlock - 1) / kBlock;
+  const int SB = A.d.SB, lsb = SB == 4 ? 2 : SB == 2 ? 1 : 0;  // screen blocks per page
+  const int bsz = kBlock >> lsb;                               // tokens per screen block
+  const int nfull = badT ? 0 : seq_len / bsz;
+  const int nblk = badT ? 0 : (seq_len + bsz - 1) / bsz;
   const int ntn = (nblk + kTile - 1) / kTile;
   const int64_t tix0 = (int64_t)s * NT;
   const int64_t tcx0 = (int64_t)s * (NT + 1);
@@ -428,6 +463,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   __shared__ int s_nres;
   __shared__ int s_res_j[G];
   __shared__ int s_resc[G];
+  __shared__ int s_ub[4];
 
   // 1. per-head totals, largest bound, errors; exclusive prefix over tiles
   int hc[G];
@@ -442,10 +478,11 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   // the tile loads do not wait for the length: every tile of the segment's
   // row is read (the screen wrote all of them) and those past the sequence
   // are masked afterwards
-  int err = 0, carry = 0;
+  int err = 0, carry = 0, ublk = 0;
   for (int t0 = 0; t0 < NT; t0 += 256) {
     const int t = t0 + tid;
     int c = 0, e = 0, hcl[G], ual[G];
+    uint64_t orb = 0;
     float uml[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -461,11 +498,13 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
         hcl[h] = A.ws.tile_hcnt[(tix0 + t) * G + h];
         uml[h] = A.ws.tile_umax[(tix0 + t) * G + h];
         ual[h] = A.ws.tile_uarg[(tix0 + t) * G + h];
+        if (SB > 1) orb |= A.ws.tile_bits[((int64_t)s * G + h) * NT + t];
       }
     }
     const bool use = t < ntn;
     if (use) {
       err |= e;
+      ublk += __popcll(orb);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         hc[h] += hcl[h];
@@ -485,6 +524,10 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int ucnt = carry;
   const bool err_w = __any(err != 0);
   if (lane == 0) s_err[wave] = err_w ? 1 : 0;
+  if (SB > 1) {
+    const int ub_w = wave_sum_i(ublk);
+    if (lane == 0) s_ub[wave] = ub_w;
+  }
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const int t_h = wave_sum_i(hc[h]);
@@ -521,6 +564,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   //    bit is added to that entry, otherwise it becomes a rescue-tile entry.
   if (tid == 0) {
     int nres = 0;
+    int ub = SB > 1 ? s_ub[0] + s_ub[1] + s_ub[2] + s_ub[3] : 0;  // screen blocks admitted by any head
     for (int h = 0; h < G; ++h) {
       int tot = 0;
       for (int w = 0; w < 4; ++w) tot += s_hcnt[w][h];
@@ -539,30 +583,41 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
         s_resc[h] = jb;
         tot = 1;
         const int tt = jb / kTile;
+        const int jp = jb >> lsb;                                     // its page's index
+        const uint32_t sbit = SB > 1 ? 1u << ((jb & (SB - 1)) * G + h) : 0u;
+        if (SB > 1) {  // a new block for the union unless another head admits it
+          uint64_t any = 0;
+          for (int h2 = 0; h2 < G; ++h2) any |= A.ws.tile_bits[((int64_t)s * G + h2) * NT + tt];
+          if (!((any >> (jb % kTile)) & 1ull)) ++ub;
+        }
         int2* ent = A.ws.tile_ent + (tcx0 + tt) * kTile;
         const int c = A.ws.tile_cnt[tcx0 + tt];
         int found = -1;
         for (int k = 0; k < c; ++k)
-          if ((ent[k].y >> 8) == jb) found = k;
+          if ((ent[k].y >> 8) == jp) found = k;
         if (found >= 0) {
           ent[found].y |= 1 << h;
+          if (SB > 1) A.ws.tile_sub[(tcx0 + tt) * kTile + found] |= sbit;
         } else {
           int q = 0;
           for (; q < nres; ++q)
-            if (s_res_j[q] == jb) break;
+            if (s_res_j[q] == jp) break;
           int2* rent = A.ws.tile_ent + (tcx0 + NT) * kTile;
           if (q == nres) {
-            s_res_j[q] = jb;
-            rent[q] = make_int2(bt[jb], jb << 8);
+            s_res_j[q] = jp;
+            rent[q] = make_int2(bt[jp], jp << 8);
+            if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] = 0u;
             ++nres;
           }
           rent[q].y |= 1 << h;
+          if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] |= sbit;
         }
         A.ws.tile_bits[((int64_t)s * G + h) * NT + tt] |= 1ull << (jb % kTile);
       }
       s_hcnt[0][h] = tot;
     }
     s_nres = nres;
+    s_ub[0] = ub;
     A.ws.tile_cnt[tcx0 + NT] = nres;
     toff[ntn] = ucnt;
     toff[ntn + 1] = ucnt + nres;
@@ -575,13 +630,14 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     const int h = tid;
     const int64_t o = (int64_t)n * HQ + g * G + h;
     const int cnt = badT ? 0 : s_hcnt[0][h];
-    const int tail_missing = (!badT && (seq_len % kBlock)) ? kBlock - seq_len % kBlock : 0;
+    const int tail_missing = (!badT && (seq_len % bsz)) ? bsz - seq_len % bsz : 0;
     A.ws.st_head[o] = cnt;
-    A.ws.st_tokens[o] = cnt > 0 ? (int64_t)cnt * kBlock - tail_missing : 0;
+    A.ws.st_tokens[o] = cnt > 0 ? (int64_t)cnt * bsz - tail_missing : 0;
     A.ws.st_rescued[o] = s_resc[h] >= 0 ? 1 : 0;
   }
   if (tid == 0) {
     A.ws.seg_U[s] = U;
+    A.ws.seg_ub[s] = SB > 1 ? (badT ? 0 : s_ub[0]) : U;
     A.ws.seg_ntn[s] = ntn;
     A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
     A.ws.seg_done[s] = 0;
@@ -603,6 +659,7 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
   if (p.bound == 1) hipLaunchKernelGGL((k_screen<T, D, G, 1>), grid, dim3(256), 0, st, a);
   else if (p.bound == 2) hipLaunchKernelGGL((k_screen<T, D, G, 2>), grid, dim3(256), 0, st, a);
   else if (p.bound == 3) hipLaunchKernelGGL((k_screen<T, D, G, 3>), grid, dim3(256), 0, st, a);
+  else if (p.bound == 4) hipLaunchKernelGGL((k_screen<T, D, G, 4>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_screen<T, D, G, 0>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -41,6 +41,31 @@ __global__ __launch_bounds__(256) void k_build(CacheView c, SeqView s) {
                      c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
 }
 
+// Records of the smaller screen blocks (16 or 32 tokens, ROWS): one wavefront
+// per (sequence, block, KV head), complete blocks only; block j of a sequence
+// is rows (j mod 64/ROWS) ROWS .. + ROWS - 1 of page block_table[n][j ROWS / 64].
+template <typename T, int D, int ROWS>
+__global__ __launch_bounds__(256) void k_build_sub(CacheView c, SeqView s) {
+  constexpr int SB = kBlock / ROWS;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over N * MB * SB * HKV
+  const int64_t total = (int64_t)s.N * s.MB * SB * c.HKV;
+  if (idx >= total) return;
+  const int g = (int)(idx % c.HKV);
+  const int64_t nj = idx / c.HKV;
+  const int j = (int)(nj % ((int64_t)s.MB * SB));
+  const int n = (int)(nj / ((int64_t)s.MB * SB));
+  const int len = s.lens[n];
+  if (len < 1 || len > kBlock * s.MB) return;
+  if (j >= len / ROWS) return;
+  const int page = s.bt[(int64_t)n * s.MB + j / SB];
+  if (page < 0 || page >= c.num_pages) return;
+  const int64_t rec = ((int64_t)page * c.HKV + g) * SB + j % SB;
+  const auto* tile = (const typename T::Stored*)c.k + rec * ROWS * D;
+  build_record<T, D, ROWS>(tile, nullptr, c.mu_sub + rec * D, c.radius_sub + rec, nullptr, nullptr, nullptr,
+                           nullptr, nullptr, 0, lane);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(64) void k_append(CacheView c, SeqView s, const void* k_new,
                                                const void* v_new) {
@@ -67,6 +92,16 @@ __global__ __launch_bounds__(64) void k_append(CacheView c, SeqView s, const voi
                        c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
                      c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
   }
+  // the smaller screen block this token completes
+  if (c.sub == 2 && row % 32 == 31) {
+    const int64_t srec = rec * 2 + row / 32;
+    build_record<T, D, 32>((const St*)c.kw + srec * 32 * D, kn, c.mu_sub + srec * D, c.radius_sub + srec, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, 0, lane);
+  } else if (c.sub == 4 && row % 16 == 15) {
+    const int64_t srec = rec * 4 + row / 16;
+    build_record<T, D, 16>((const St*)c.kw + srec * 16 * D, kn, c.mu_sub + srec * D, c.radius_sub + srec, nullptr,
+                           nullptr, nullptr, nullptr, nullptr, 0, lane);
+  }
 }
 
 template <typename T, int D>
@@ -75,6 +110,12 @@ hipError_t build_impl(const CacheView& c, const SeqView& s, hipStream_t st) {
   const int64_t grid = (waves + 3) / 4;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_build<T, D>), dim3((unsigned)grid), dim3(256), 0, st, c, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c.sub == 0) return e;
+  const int64_t sgrid = (waves * c.sub + 3) / 4;
+  if (sgrid > 0x7fffffff) return hipErrorInvalidValue;
+  if (c.sub == 2) hipLaunchKernelGGL((k_build_sub<T, D, 32>), dim3((unsigned)sgrid), dim3(256), 0, st, c, s);
+  else hipLaunchKernelGGL((k_build_sub<T, D, 16>), dim3((unsigned)sgrid), dim3(256), 0, st, c, s);
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def log(msg: str) -> None:
 class Dev:
     """A workload's inputs on the GPU."""
 
-    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False, with_box=False, fp8=None):
+    def __init__(self, wl: W.Workload, device="cuda", with_sigma=False, with_box=False, fp8=None, sub_block=0):
         self.wl = wl
         self.device = torch.device(device)
         z16 = lambda: torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=device)  # noqa: E731
@@ -38,7 +38,11 @@ class Dev:
                                torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.uint8, device=device)
                                if fp8 else None,
                                torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device)
-                               if fp8 else None, fp8 or "e4m3")
+                               if fp8 else None, fp8 or "e4m3", sub_block,
+                               torch.zeros(wl.num_pages, wl.h_kv, 64 // sub_block, wl.d, dtype=torch.float16,
+                                           device=device) if sub_block else None,
+                               torch.zeros(wl.num_pages, wl.h_kv, 64 // sub_block, dtype=torch.float32,
+                                           device=device) if sub_block else None)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(device)
         self.q = eta.upload(wl.q, wl.kv_dtype, device)
@@ -64,6 +68,10 @@ class Dev:
         wl = self.wl
         return eta.stats(self.ws, wl.n_seqs, wl.max_blocks, wl.h_q, wl.h_kv, check=check)
 
+    def sub_records(self):
+        return (self.cache.mu_sub.cpu().view(torch.int16).numpy().view(np.uint16),
+                self.cache.radius_sub.cpu().numpy())
+
     def mu_bits(self):
         return self.cache.mu.cpu().view(torch.int16).numpy().view(np.uint16)
 
@@ -82,10 +90,17 @@ class Dev:
 
 
 def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=None, beta=None, lwb=None,
-                  bound="geometric", z=2.0, fp8="e4m3"):
+                  bound="geometric", z=2.0, fp8="e4m3", block=64):
     """summaries: (mu, R); for the dual screen (mu, R, sigma); for the
     comparator's box bound (mu, R, kmin, kmax); for "geometric_fp8" the FP8
-    records (mu8, R8)."""
+    records (mu8, R8); for "geometric_sub" the records of `block`-token
+    blocks."""
+    if bound == "geometric_sub":
+        return E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
+                               wl.tau_mode if tau_mode is None else tau_mode, wl.w,
+                               wl.bias if bias is None else bias, wl.a if a is None else a,
+                               wl.beta if beta is None else beta, wl.lwb if lwb is None else lwb, block,
+                               summaries=summaries, heads=heads)
     if bound == "geometric_fp8":
         return E.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q,
                         wl.tau_mode if tau_mode is None else tau_mode, wl.w,
@@ -108,8 +123,8 @@ def oracle_decode(wl, summaries=None, heads=None, bias=None, tau_mode=None, a=No
 
 
 def check_sets_and_counts(wl, res, st):
-    """Admitted bitmaps bit-exact, counts exact."""
-    adm = st.admitted(wl.max_blocks)
+    """Admitted bitmaps bit-exact, counts exact (in the screen's blocks)."""
+    adm = st.admitted(res.admitted.shape[2])
     if not np.array_equal(adm, res.admitted):
         bad = np.argwhere(adm != res.admitted)
         n, h, j = bad[0]
@@ -137,11 +152,11 @@ def check_output(wl, res, o_gpu, heads=None, tol=None):
     return err
 
 
-def prepared(name, bound="geometric", z=2.0, fp8="e4m3", **kw):
+def prepared(name, bound="geometric", z=2.0, fp8="e4m3", block=64, **kw):
     """Workload with thresholds placed and margins enforced (oracle side) for
     the given screen."""
     wl = W.make_workload(name, **kw)
-    summ = placement.place(wl, bound=bound, z=z, fp8=fp8)
+    summ = placement.place(wl, bound=bound, z=z, fp8=fp8, block=block)
     return wl, summ
 
 

@@ -19,7 +19,7 @@ import workloads as W
 BLOCK = 64
 
 
-def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None):
+def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None, block=64):
     """ub[n][h][j] for complete blocks (NaN elsewhere), tau offsets per (n, h).
     With sigma, the dual screen score instead of the geometric bound; with
     boxes (kmin, kmax), the comparator's box bound."""
@@ -27,8 +27,16 @@ def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None):
     G = wl.group
     s = 1.0 / math.sqrt(D)
     qf = E.upcast(wl.q, wl.kv_dtype)
-    ub = np.full((N, HQ, wl.max_blocks), np.nan)
+    SB = BLOCK // block
+    ub = np.full((N, HQ, wl.max_blocks * SB), np.nan)
     for n in range(N):
+        if SB > 1:  # records of smaller screen blocks: mu [P][HKV][SB][d]
+            nsub = int(wl.seq_lens[n]) // block
+            j = np.arange(nsub)
+            pg = wl.block_table[n][j // SB]
+            for h in range(HQ):
+                ub[n, h, :nsub] = E.block_bound(qf[n, h], mu[pg, h // G, j % SB], R[pg, h // G, j % SB], s)
+            continue
         nfull = int(wl.seq_lens[n]) // BLOCK
         pages = wl.block_table[n, :nfull]
         for h in range(HQ):
@@ -47,11 +55,14 @@ def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None):
 
 
 def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound: str = "geometric",
-          z: float = 2.0, fp8: str = "e4m3"):
+          z: float = 2.0, fp8: str = "e4m3", block: int = 64):
     """Set wl.bias in place; returns the oracle summaries of the final cache
     ((mu, R), (mu, R, sigma) for the dual screen, (mu, R, kmin, kmax) for the
-    comparator's box bound; the FP8 records (mu8, R8) for "geometric_fp8")."""
-    if bound == "geometric_fp8":
+    comparator's box bound; the FP8 records (mu8, R8) for "geometric_fp8"; the
+    records of `block`-token blocks (mu_sub, R_sub) for "geometric_sub")."""
+    if bound == "geometric_sub":
+        mu, R = E.build_summaries_sub(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, block)
+    elif bound == "geometric_fp8":
         mu, R = E.build_summaries_fp8(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, fp8)
     else:
         mu, R = E.build_summaries(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens) \
@@ -62,7 +73,8 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         sigma = E.build_sigmas(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens)
     if bound == "quest":
         boxes = E.build_boxes(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens)
-    ub, off = _bounds(wl, mu, R, sigma, z, boxes)
+    blk = block if bound == "geometric_sub" else 64
+    ub, off = _bounds(wl, mu, R, sigma, z, boxes, blk)
     HQ = wl.h_q
     bias = np.zeros(HQ, dtype=np.float32)
     for h in range(HQ):
@@ -82,7 +94,7 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         bad = set()
         G = wl.group
         for n, h, j in zip(*np.nonzero(close)):
-            bad.add((int(n), int(h) // G, int(j)))
+            bad.add((int(n), int(h) // G, int(j) * blk // 64))  # the page holding the block
         if not bad:
             if boxes is not None:
                 return mu, R, boxes[0], boxes[1]
@@ -91,14 +103,17 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         for (n, g, j) in bad:
             page = int(wl.block_table[n, j])
             kb = E.upcast(wl.k_pages[page, g], wl.kv_dtype)
-            m, r = E.block_summary_fp8(kb, fp8) if bound == "geometric_fp8" else E.block_summary(kb)
+            if bound == "geometric_sub":
+                m, r = E.block_summary(kb.reshape(64 // blk, blk, -1))
+            else:
+                m, r = E.block_summary_fp8(kb, fp8) if bound == "geometric_fp8" else E.block_summary(kb)
             mu[page, g] = m
             R[page, g] = r
             if sigma is not None:
                 sigma[page, g] = E.block_sigma(kb)
             if boxes is not None:
                 boxes[0][page, g], boxes[1][page, g] = E.block_box(kb)
-        ub, off = _bounds(wl, mu, R, sigma, z, boxes)
+        ub, off = _bounds(wl, mu, R, sigma, z, boxes, blk)
     raise RuntimeError("margin enforcement did not converge")
 
 

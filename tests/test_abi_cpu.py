@@ -194,6 +194,16 @@ def test_decode_ex_rejects_bad_screens():
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(**dict(fp8, mu8=FAKE + 4))) == \
         _lib.ETA_ERR_INVALID_ARGUMENT
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_FP8, 0.0, c=cache(**fp8)) == too_small
+    # smaller screen blocks: 16 or 32 tokens, both buffers
+    sub = dict(sub_block=16, mu_sub=FAKE * 17, radius_sub=FAKE * 18)
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**dict(sub, sub_block=8))) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**dict(sub, radius_sub=None))) == \
+        _lib.ETA_ERR_INVALID_ARGUMENT
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**sub)) == too_small
+    # the workspace for a cache with smaller-block records covers their tiles
+    assert ws_size(cache(**sub)) > ws_size(cache())
     assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small
 
 

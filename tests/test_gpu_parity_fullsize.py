@@ -28,22 +28,22 @@ def _sample_heads(wl, per_seq, seed):
     return heads
 
 
-def _run_full(name, per_seq, seed=7, bound="geometric", fp8="e4m3"):
+def _run_full(name, per_seq, seed=7, bound="geometric", fp8="e4m3", block=64):
     log(f"[full-size] {name} ({bound} screen): generating and placing thresholds")
-    wl, summ = prepared(name, bound=bound, fp8=fp8)
+    wl, summ = prepared(name, bound=bound, fp8=fp8, block=block)
     log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
         f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
     heads = _sample_heads(wl, per_seq, seed)
     dev = Dev(wl, with_sigma=bound == "dual", with_box=bound == "quest",
-              fp8=fp8 if bound == "geometric_fp8" else None)
+              fp8=fp8 if bound == "geometric_fp8" else None, sub_block=block if bound == "geometric_sub" else 0)
     dev.build()
     o = dev.decode(bound=bound)
     st = dev.stats()
     log(f"[full-size] {name}: oracle on {len(heads)} heads")
-    res = oracle_decode(wl, summaries=summ, heads=heads, bound=bound, fp8=fp8)
+    res = oracle_decode(wl, summaries=summ, heads=heads, bound=bound, fp8=fp8, block=block)
     check_sets_and_counts(wl, res, st)
     check_output(wl, res, o, heads=heads)
-    dens = st.admitted_per_head.sum() / (wl.h_q * sum(wl.nblk(n) for n in range(wl.n_seqs)))
+    dens = st.admitted_per_head.sum() / (wl.h_q * sum(-(-int(T) // block) for T in wl.seq_lens))
     log(f"[full-size] {name}: per-head density {dens:.3f}, rescued {int(st.rescued.sum())}")
     del dev
     torch.cuda.empty_cache()
@@ -85,3 +85,9 @@ def test_seq_512k_quest_full():
 def test_seq_512k_fp8_full():
     """The 512K workload under the geometric bound over E4M3 records: 8 heads."""
     _run_full("seq_512k", per_seq=8, bound="geometric_fp8", fp8="e4m3")
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_subblock16_full():
+    """The 512K workload with 16-token screen blocks: 8 heads."""
+    _run_full("seq_512k", per_seq=8, bound="geometric_sub", block=16)
