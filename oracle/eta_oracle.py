@@ -65,11 +65,13 @@ to nearest even and saturated at the largest finite value, with the radius
 measured about that stored centroid, so the geometric bound stays an upper
 bound (fp8_round, block_summary_fp8, decode(bound="geometric_fp8")).
 
-Smaller screen blocks (Appendix F.3, Table 10 ablates the block size; the
+Other screen block sizes (Appendix F.3, Table 10 ablates the block size; the
 reading taken): with b = 16 or 32 every 64-token page holds 64/b screen
-blocks, each with its own record (centroid and radius of its b keys); the
-screen, the forced and rescued blocks, the counts and the attention all work
-on b-token blocks (build_summaries_sub, decode_blocks).
+blocks, each with its own record (centroid and radius of its b keys); with
+b = 128 a screen block spans two consecutive entries 2j and 2j + 1 of the
+block table and its record (over its 128 keys) is kept with the first of the
+two pages. The screen, the forced and rescued blocks, the counts and the
+attention all work on b-token blocks (build_summaries_sub, decode_blocks).
 
 Comparator screen (Section 4.3, "Comparison with Quest"): per block and KV
 head the coordinate-wise minimum and maximum of the keys, rounded outward to
@@ -536,27 +538,34 @@ def _attend(qh, k_pages, v_pages, kv_dtype, pages, g, blocks, T, tau, beta, scal
 # --------------------------------------------------------------------------- smaller screen blocks
 def build_summaries_sub(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndarray, seq_lens: np.ndarray,
                         block: int):
-    """Records of every complete block of `block` tokens (16 or 32; a page
-    holds 64/b consecutive blocks, its block q being rows q b .. q b + b - 1):
-    mu float64 [num_pages][H_KV][64/b][d] holding float16 values and R
-    float64 [num_pages][H_KV][64/b], NaN where there is none. Same record rule
-    as build_summaries (block_summary on b keys)."""
-    assert BLOCK % block == 0 and block < BLOCK
-    SB = BLOCK // block
+    """Records of every complete screen block of `block` tokens (16, 32 or
+    128). Block j of a sequence holds its tokens j b .. j b + b - 1; its record
+    lives with the page of its first token, in slot (j b mod 64) / b of that
+    page: a page holds 64/b blocks of 16 or 32 tokens, while a 128-token block
+    spans the pages 2j and 2j + 1 of the block table and its record sits in
+    the single slot of page 2j. mu float64 [num_pages][H_KV][slots][d] holding
+    float16 values and R float64 [num_pages][H_KV][slots] (slots = 64/b, or 1),
+    NaN where there is none. Same record rule as build_summaries (block_summary
+    on the block's b keys)."""
+    assert block in (16, 32, 128)
+    SB = max(1, BLOCK // block)
     P, HKV, B, D = k_pages.shape
     mu = np.full((P, HKV, SB, D), np.nan)
     R = np.full((P, HKV, SB), np.nan)
+    chunk = max(1, _CHUNK_BLOCKS * BLOCK // block)
     for n in range(len(seq_lens)):
         nsub = int(seq_lens[n]) // block
         if nsub == 0:
             continue
-        j = np.arange(nsub)
-        pg = np.asarray(block_table[n], dtype=np.int64)[j // SB]
-        sub = j % SB
+        bt = np.asarray(block_table[n], dtype=np.int64)
+        first = np.arange(nsub) * block
+        pg = bt[first // BLOCK]
+        sub = (first % BLOCK) // block
         for g in range(HKV):
-            for j0 in range(0, nsub, _CHUNK_BLOCKS * SB):
-                sl = slice(j0, j0 + _CHUNK_BLOCKS * SB)
-                rows = upcast(k_pages[pg[sl], g], kv_dtype).reshape(-1, SB, block, D)[np.arange(len(pg[sl])), sub[sl]]
+            for j0 in range(0, nsub, chunk):
+                sl = slice(j0, j0 + chunk)
+                tok = first[sl, None] + np.arange(block)[None, :]
+                rows = upcast(k_pages[bt[tok // BLOCK], g, tok % BLOCK], kv_dtype)
                 m, r = block_summary(rows)
                 mu[pg[sl], g, sub[sl]] = m
                 R[pg[sl], g, sub[sl]] = r
@@ -566,19 +575,20 @@ def build_summaries_sub(k_pages: np.ndarray, kv_dtype: str, block_table: np.ndar
 def decode_blocks(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau_mode: str, w, b_or_c, a: float,
                   beta: float, lwb: int, block: int, summaries=None, heads: Optional[Iterable] = None,
                   with_output: bool = True) -> DecodeResult:
-    """decode with the geometric screen on blocks of `block` tokens (16 or 32):
-    block j of sequence n is rows (j mod 64/b) b .. + b - 1 of page
-    block_table[n][j b / 64]. Admitted sets, bounds, forced blocks (the partial
-    last block, the lwb most recent complete blocks), the rescue and the counts
-    are per b-token block; admitted is [N][H_Q][max_blocks 64/b]; union counts
-    b-token blocks admitted by any head of the group; attention runs over the
-    tokens t < T of the admitted blocks."""
+    """decode with the geometric screen on blocks of `block` tokens (16, 32 or
+    128): block j of sequence n is its tokens j b .. j b + b - 1 (token t lies in
+    page block_table[n][t / 64], row t mod 64), with the record that
+    build_summaries_sub keeps for it. Admitted sets, bounds, forced blocks (the
+    partial last block, the lwb most recent complete blocks), the rescue and
+    the counts are per b-token block; admitted is
+    [N][H_Q][ceil(64 max_blocks / b)]; union counts b-token blocks admitted by
+    any head of the group; attention runs over the tokens t < T of the
+    admitted blocks."""
     N, HQ, D = q.shape
     P, HKV, B, D2 = k_pages.shape
-    assert D2 == D and B == BLOCK and HQ % HKV == 0 and BLOCK % block == 0
-    SB = BLOCK // block
+    assert D2 == D and B == BLOCK and HQ % HKV == 0 and block in (16, 32, 128)
     G = HQ // HKV
-    MB = block_table.shape[1] * SB
+    MB = -(-block_table.shape[1] * BLOCK // block)
     scale = 1.0 / math.sqrt(D)
     mu_all, R_all = build_summaries_sub(k_pages, kv_dtype, block_table, seq_lens, block) \
         if summaries is None else summaries
@@ -593,12 +603,13 @@ def decode_blocks(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q, tau
         T = int(seq_lens[n])
         nfull = T // block
         pages = np.asarray(block_table[n], dtype=np.int64)
-        j = np.arange(nfull)
+        first = np.arange(nfull) * block
+        rp, rs = pages[first // BLOCK], (first % BLOCK) // block  # where each block's record lives
         for h in range(HQ):
             g = h // G
             tau = threshold(tau_mode, qf[n, h], None if w is None else w[h], b_or_c[h], a)
             taus[n, h] = tau
-            ub = block_bound(qf[n, h], mu_all[pages[j // SB], g, j % SB], R_all[pages[j // SB], g, j % SB], scale)
+            ub = block_bound(qf[n, h], mu_all[rp, g, rs], R_all[rp, g, rs], scale)
             ubs[n, h, :nfull] = ub
             adm, resc = admitted_blocks(ub, tau, T, lwb, block)
             admitted[n, h, :len(adm)] = adm

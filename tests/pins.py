@@ -28,13 +28,13 @@ def _decode(E, wl, bias=None, a=None, beta=None, lwb=None, tau_mode=None, **kw):
 
 
 def tiny(seed, n=2, lens=(200, 128), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned", lwb=0,
-         a=0.0, beta=5.0, density=0.4, bias=None):
+         a=0.0, beta=5.0, density=0.4, bias=None, paged=None):
     """A tiny random workload with its threshold constant placed so that about
     `density` of the complete blocks pass (placement uses the module's own
     bound only to choose a number; the checks do not depend on it)."""
     wl = W.make_workload("seq_32k", seed=seed, n_seqs=n, seq_lens=list(lens), h_q=h_q, h_kv=h_kv,
                          d=d, kv_dtype=dtype, mode=mode, needles=0, lwb=lwb, a=a, beta=beta,
-                         threads=1)
+                         threads=1, paged=paged)
     if bias is None:
         bias = np.zeros(h_q, dtype=np.float32)
         rng = np.random.default_rng(seed + 99)
@@ -426,6 +426,64 @@ def pin_subblock_no_false_negatives(E, seeds=range(3)):
                     S = float(E.upcast(wl.q[n, h], wl.kv_dtype) @ k) / math.sqrt(wl.d)
                     if S >= res.tau[n, h]:
                         assert res.admitted[n, h, t // 16], (seed, n, h, t)
+
+
+def pin_pairblock_bruteforce(E, seeds=range(4)):
+    """Screens on 128-token blocks (two consecutive block-table entries each,
+    pages in a random physical order): sets, bounds, rescue, token counts,
+    outputs and union counts equal the per-key brute force at b = 128. One
+    head's threshold lies above every bound, so with no partial block its
+    rescue decides its set."""
+    variants = [dict(n=2, lens=(700, 384), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned"),
+                dict(n=1, lens=(1000,), h_q=2, h_kv=1, d=4, dtype="f32", mode="calibrated", lwb=2),
+                dict(n=3, lens=(129, 255, 64), h_q=2, h_kv=2, d=8, dtype="bf16", mode="learned", lwb=1),
+                dict(n=2, lens=(256, 640), h_q=4, h_kv=1, d=4, dtype="f32", mode="learned")]
+    for seed in seeds:
+        v = variants[seed % len(variants)]
+        wl = tiny(130 + seed, paged=True, **v)
+        zero = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                               wl.w, np.zeros(wl.h_q, np.float32), wl.a, wl.beta, wl.lwb, 128, with_output=False)
+        off = [zero.ub[:, h] - zero.tau[:, h, None] for h in range(wl.h_q)]
+        wl.bias = np.array([np.nanmedian(o) if np.isfinite(o).any() else 0.0 for o in off], dtype=np.float32)
+        if v["lens"] == (256, 640):
+            wl.bias[0] = np.float32(np.nanmax(off[0]) + 5.0)
+        res = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                              wl.w, wl.bias, wl.a, wl.beta, wl.lwb, 128)
+        bf, bf_union = bruteforce.decode(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table,
+                                         wl.seq_lens, wl.q, wl.tau_mode, wl.w, wl.bias, wl.a,
+                                         wl.beta, wl.lwb, block=128)
+        for (n, h), r in bf.items():
+            got = sorted(np.nonzero(res.admitted[n, h])[0].tolist())
+            assert got == r["admitted"], (seed, n, h, got, r["admitted"])
+            assert bool(res.rescued[n, h]) == r["rescued"]
+            assert int(res.tokens[n, h]) == r["tokens"]
+            np.testing.assert_allclose(res.ub[n, h, :len(r["ub"])], r["ub"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res.o[n, h], r["o"], rtol=1e-10, atol=1e-12)
+        for (n, g), u in bf_union.items():
+            assert int(res.union[n, g]) == u
+        if v["lens"] == (256, 640):
+            assert res.rescued[:, 0].all()
+
+
+def pin_pairblock_no_false_negatives(E, seeds=range(2)):
+    """Every key whose logit reaches its head's threshold lies in an admitted
+    128-token block."""
+    for seed in seeds:
+        wl = tiny(140 + seed, n=2, lens=(900, 450), h_q=4, h_kv=2, d=8, dtype="bf16", mode="learned", paged=True)
+        res = E.decode_blocks(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, wl.q, wl.tau_mode,
+                              wl.w, wl.bias, wl.a, wl.beta, wl.lwb, 128, with_output=False)
+        hits = 0
+        for n in range(wl.n_seqs):
+            T = int(wl.seq_lens[n])
+            for h in range(wl.h_q):
+                g = h // wl.group
+                for t in range(T):
+                    k = E.upcast(wl.k_pages[wl.block_table[n, t // 64], g, t % 64], wl.kv_dtype)
+                    S = float(E.upcast(wl.q[n, h], wl.kv_dtype) @ k) / math.sqrt(wl.d)
+                    if S >= res.tau[n, h]:
+                        hits += 1
+                        assert res.admitted[n, h, t // 128], (seed, n, h, t)
+        assert hits > 0
 
 
 # --------------------------------------------------------------------------- offline calibration
@@ -821,5 +879,6 @@ ALL_PINS = [
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
     pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,
     pin_fp8_rounding_table, pin_fp8_matches_code_search, pin_fp8_bound_sound, pin_fp8_bruteforce,
-    pin_subblock_bruteforce, pin_subblock_no_false_negatives,
+    pin_subblock_bruteforce, pin_subblock_no_false_negatives, pin_pairblock_bruteforce,
+    pin_pairblock_no_false_negatives,
 ]

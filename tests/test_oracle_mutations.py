@@ -65,7 +65,12 @@ MUTANTS = {
     "fp8_no_saturation": ("r = np.minimum(np.round(a / quantum) * quantum, vmax)",
                           "r = np.round(a / quantum) * quantum"),
     "fp8_radius_about_mean": ("off8 = kb - mu8[:, None, :]", "off8 = kb - kb.mean(axis=1)[:, None, :]"),
-    "subblock_record_slot": ("        sub = j % SB\n", "        sub = (j + 1) % SB\n"),
+    "subblock_record_slot": ("        sub = (first % BLOCK) // block\n", "        sub = ((first % BLOCK) // block + 1) % SB\n"),
+    "pairblock_record_first_page_only": (
+        "rows = upcast(k_pages[bt[tok // BLOCK], g, tok % BLOCK], kv_dtype)",
+        "rows = upcast(k_pages[bt[tok[:, :BLOCK] // BLOCK], g, tok[:, :BLOCK] % BLOCK], kv_dtype)"),
+    "pairblock_record_on_second_page": ("rp, rs = pages[first // BLOCK], (first % BLOCK) // block",
+                                        "rp, rs = pages[(first + block - 1) // BLOCK], (first % BLOCK) // block"),
     "subblock_token_width": ("        width = np.minimum(block, T - block * np.arange(nblk))",
                              "        width = np.minimum(BLOCK, T - block * np.arange(nblk))"),
     "subblock_key_page": ("            K = upcast(k_pages[pages[tok // BLOCK], g, tok % BLOCK], kv_dtype)",
