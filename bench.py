@@ -57,7 +57,7 @@ def parse():
                    choices=["geometric", "dual", "quest", "geometric_fp8", "geometric_sub"],
                    help="block screen: the geometric bound, the dual screen (z deviations) or the comparator box bound")
     p.add_argument("--z", type=float, default=2.0, help="deviations of the dual screen")
-    p.add_argument("--sub-block", type=int, default=16, choices=[16, 32],
+    p.add_argument("--sub-block", type=int, default=16, choices=[16, 32, 128],
                    help="tokens per screen block for --bound geometric_sub")
     p.add_argument("--calibration", action="store_true",
                    help="only time the offline calibration (16 sequences x 4096 positions, GQA 32/8, d=128, bf16) "
@@ -168,21 +168,22 @@ def compare_screens(workload, density, steps, warmup, z):
     the workload's target density): admitted fraction per head and per KV head,
     and the decode step time, for the geometric bound, the dual score, the
     comparator's box bound (Section 4.3), the geometric bound over E4M3
-    records, and the geometric bound on 16- and 32-token screen blocks
+    records, and the geometric bound on 16-, 32- and 128-token screen blocks
     (Appendix F.3's block size; densities in those blocks)."""
     S = Setup(workload, density, "all", z)
     S.calibrate()
     rows = {}
-    for b in ("geometric", "dual", "quest", "geometric_fp8", "geometric_sub", "geometric_sub32"):
-        if b == "geometric_sub32":
-            S.use_sub_block(32)
-        S.bound = "geometric_sub" if b == "geometric_sub32" else b
+    for b in ("geometric", "dual", "quest", "geometric_fp8", "geometric_sub", "geometric_sub32", "geometric_sub128"):
+        if b in ("geometric_sub32", "geometric_sub128"):
+            S.use_sub_block(int(b[len("geometric_sub"):]))
+        S.bound = "geometric_sub" if b.startswith("geometric_sub") else b
         S.run()
         S.torch.cuda.synchronize()
         st, dh, du = S.densities()
         us = time_steps(S, steps, warmup)
         ph = time_phases(S, steps)
-        key = {"geometric_sub": "geometric_b16", "geometric_sub32": "geometric_b32"}.get(b, b)
+        key = {"geometric_sub": "geometric_b16", "geometric_sub32": "geometric_b32",
+               "geometric_sub128": "geometric_b128"}.get(b, b)
         rows[key] = {"density_per_head": round(dh, 4), "density_union": round(du, 4), "us_per_step": round(us, 2),
                    "screen_us": round(float(ph[0]), 2), "attend_and_merge_us": round(float(ph[1]), 2)}
         log(f"{key}: per-head {dh:.4f} union {du:.4f} step {us:.1f} us")
@@ -338,7 +339,7 @@ class Setup:
         mu8 = torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.uint8, device=dev) if fp8 else None
         r8 = torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev) if fp8 else None
         self.sub_block = sub_block if bound in ("geometric_sub", "all") else 0
-        sb = 64 // self.sub_block if self.sub_block else 0
+        sb = eta.sub_slots(self.sub_block) if self.sub_block else 0
         mus = torch.zeros(wl.num_pages, wl.h_kv, sb, wl.d, dtype=torch.float16, device=dev) if sb else None
         rs = torch.zeros(wl.num_pages, wl.h_kv, sb, dtype=torch.float32, device=dev) if sb else None
         if bound == "all":  # every record, for comparisons at equal thresholds
@@ -403,9 +404,9 @@ class Setup:
         return st, per_head, union
 
     def use_sub_block(self, sub_block):
-        """Records of another smaller screen block size (same K/V and thresholds)."""
+        """Records of another screen block size (same K/V and thresholds)."""
         eta, torch, wl = self.eta, self.torch, self.wl
-        sb = 64 // sub_block
+        sb = eta.sub_slots(sub_block)
         c = self.cache
         self.cache = eta.Cache(c.k_pages, c.v_pages, c.mu, c.radius, c.sigma, c.kmin, c.kmax, c.mu8, c.radius8,
                                c.mu8_format, sub_block,
@@ -422,13 +423,19 @@ class Setup:
         table, the queries/thresholds and the output."""
         wl = self.wl
         esz = 2 if wl.kv_dtype == "bf16" else 4
+        b = self.block_tokens()
         union = int(st.union_per_kv.sum())
-        kv = union * 2 * self.block_tokens() * wl.d * esz
+        if b > 64:  # a block's pages: a partial last block (always loaded) may have only its first page
+            one_page = sum(1 for T in wl.seq_lens if 0 < int(T) % b <= 64)
+            kv = (union * (b // 64) - one_page * wl.h_kv) * 2 * 64 * wl.d * esz
+        else:
+            kv = union * 2 * b * wl.d * esz
         nfull = int(sum(int(wl.seq_lens[n]) // 64 for n in range(wl.n_seqs)))
-        # records the screen reads: centroid and radius (and the deviation), or the key box
+        # records the screen reads per complete page: centroid and radius (and
+        # the deviation), or the key box; 64/b records of b-token blocks
         rec = {"geometric": 2 * wl.d + 4, "dual": 4 * wl.d + 4, "quest": 4 * wl.d,
-               "geometric_fp8": wl.d + 4, "geometric_sub": (2 * wl.d + 4) * (64 // max(self.sub_block, 1))}[self.bound]
-        meta = nfull * wl.h_kv * rec + int(self.nblk.sum()) * 4
+               "geometric_fp8": wl.d + 4, "geometric_sub": (2 * wl.d + 4) * 64 / max(b, 1)}[self.bound]
+        meta = int(nfull * wl.h_kv * rec) + int(self.nblk.sum()) * 4
         small = wl.n_seqs * wl.h_q * wl.d * (esz + 4) + wl.h_q * wl.d * 4
         return kv, kv + meta + small
 

@@ -98,16 +98,23 @@ enum { ETA_FP8_E4M3 = 0, ETA_FP8_E5M2 = 1 };          /* FP8 record formats (OCP
  *   mu8_format       : ETA_FP8_E4M3 (3 mantissa bits, largest 448) or
  *                      ETA_FP8_E5M2 (2 mantissa bits, largest 57344); read only
  *                      when mu8 is not NULL.
- *   sub_block, mu_sub, radius_sub : screen blocks smaller than a page
- *                      (Appendix F.3 ablates the block size; the reading taken):
- *                      sub_block 16 or 32 tokens, so a page holds 64/sub_block
- *                      consecutive blocks; mu_sub [num_pages][num_kv_heads]
- *                      [64/sub_block][head_dim] float16 bits (16-byte aligned)
- *                      and radius_sub [num_pages][num_kv_heads][64/sub_block]
- *                      float32: the record of each such block, by the same
- *                      rule as mu/radius. Both NULL, or both set; only
- *                      ETA_BOUND_GEOMETRIC_SUB reads them; when set, the record
- *                      builders fill them.
+ *   sub_block, mu_sub, radius_sub : screen blocks of another size than the
+ *                      page (Appendix F.3 ablates the block size; the reading
+ *                      taken): sub_block 16 or 32 tokens, so a page holds
+ *                      64/sub_block consecutive blocks, or 128 tokens, so a
+ *                      block spans the entries 2j and 2j + 1 of a sequence's
+ *                      block table. mu_sub [num_pages][num_kv_heads][slots]
+ *                      [head_dim] float16 bits (16-byte aligned) and radius_sub
+ *                      [num_pages][num_kv_heads][slots] float32, slots =
+ *                      64/sub_block (16, 32) or 1 (128): the record of each such
+ *                      block, by the same rule as mu/radius over its keys. A
+ *                      128-token block's record lives with its first page
+ *                      (entry 2j); every table that holds that page at an even
+ *                      entry must hold the same second page after it. Both
+ *                      NULL, or both set; only ETA_BOUND_GEOMETRIC_SUB reads
+ *                      them; when set, the record builders fill them (the
+ *                      append path builds a 128-token block's record when the
+ *                      token completing its second page arrives).
  * Supported: head_dim 64 or 128, block_size 64 (Section 4.8 and F.3 use 64). */
 typedef struct {
   int kv_dtype;
@@ -212,12 +219,14 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
  *                         tokens (records mu_sub/radius_sub). Screen, forced
  *                         blocks (the partial last block, the lwb most recent
  *                         complete ones), rescue and counts work on those
- *                         blocks; the attention loads a page's rows only for
- *                         the blocks some head of the group admitted and each
- *                         head attends only to the tokens of its own blocks.
- *                         eta_stats then reports per-head counts, union counts
- *                         and the bitmap in these smaller blocks
- *                         (max_blocks_per_seq * 64/sub_block bits per head).
+ *                         blocks; with 16 or 32 tokens the attention loads a
+ *                         page's rows only for the blocks some head of the group
+ *                         admitted and each head attends only to the tokens of
+ *                         its own blocks; with 128 it loads both pages of every
+ *                         block some head admitted. eta_stats then reports
+ *                         per-head counts, union counts and the bitmap in these
+ *                         blocks (ceil(max_blocks_per_seq * 64 / sub_block) bits
+ *                         per head).
  * The score also ranks blocks for the top-1 rescue. */
 typedef struct {
   int bound;
@@ -229,7 +238,7 @@ typedef struct {
  * Returns ETA_ERR_INVALID_ARGUMENT for an unknown bound, a negative or
  * non-finite z, the dual bound without cache->sigma, the comparator bound
  * without cache->kmin and cache->kmax, the FP8 bound without cache->mu8
- * and cache->radius8, or the smaller-block bound without cache->mu_sub. */
+ * and cache->radius8, or the sub_block bound without cache->mu_sub. */
 eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache,
                          const eta_seqs* seqs, const void* q, int num_q_heads, int tau_mode,
                          const float* w, const float* b_or_c, float a, float beta, int lwb,
@@ -258,9 +267,9 @@ eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* s
  *   admitted_bitmap   [num_seqs][num_q_heads][ceil(max_blocks_per_seq/32)]
  *                     uint32, bit j%32 of word j/32 = block j admitted (nullable)
  * Blocks are the screen's blocks: after a decode with ETA_BOUND_GEOMETRIC_SUB
- * they are the cache's smaller blocks, and the bitmap has
- * ceil(max_blocks_per_seq * 64/sub_block / 32) words per head (the sizes
- * passed stay those of the decode call). All output pointers are host pointers. Returns ETA_ERR_DEVICE_DATA (after
+ * they are the cache's sub_block-token blocks, and the bitmap has
+ * ceil(ceil(max_blocks_per_seq * 64 / sub_block) / 32) words per head (the
+ * sizes passed stay those of the decode call). All output pointers are host pointers. Returns ETA_ERR_DEVICE_DATA (after
  * filling the outputs) if that decode met invalid lengths or page ids, and
  * ETA_ERR_INVALID_ARGUMENT if the sizes do not match that decode. */
 eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq, int num_q_heads,

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
 
 BLOCK = 64
 _WS_GLOB_SB = 7  # int32 slot of the workspace header holding the last decode's screen blocks per page
+_WS_GLOB_PB = 8  # and the one holding its pages per screen block
 _KV_DTYPES = {torch.bfloat16: ETA_BF16, torch.float32: ETA_F32}
 
 
@@ -55,6 +56,12 @@ def _need(t: torch.Tensor, name: str, dtype=None, device=None) -> None:
         raise ValueError(f"{name} must be contiguous")
 
 
+def sub_slots(sub_block: int) -> int:
+    """Record slots per page for screen blocks of sub_block tokens: 64/sub_block
+    for blocks inside a page, one (kept by the first page) for 128."""
+    return BLOCK // sub_block if sub_block < BLOCK else 1
+
+
 @dataclasses.dataclass
 class Cache:
     """Paged KV cache [num_pages][H_KV][64][d] plus per-block records."""
@@ -68,9 +75,10 @@ class Cache:
     mu8: Optional[torch.Tensor] = None    # uint8 [num_pages][H_KV][d], FP8 centroid (FP8 screen)
     radius8: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV], radius about it
     mu8_format: str = "e4m3"              # "e4m3" or "e5m2"
-    sub_block: int = 0                    # 16 or 32: records of smaller screen blocks (0: none)
-    mu_sub: Optional[torch.Tensor] = None   # float16 [num_pages][H_KV][64/sub_block][d]
-    radius_sub: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV][64/sub_block]
+    sub_block: int = 0                    # 16, 32 or 128: records of other screen blocks (0: none)
+    mu_sub: Optional[torch.Tensor] = None   # float16 [num_pages][H_KV][slots][d], slots = 64/sub_block or 1
+    radius_sub: Optional[torch.Tensor] = None  # float32 [num_pages][H_KV][slots]; a 128-token block's record
+    #                                            sits with its first page (block-table entry 2j)
 
     def __post_init__(self):
         _need(self.k_pages, "k_pages")
@@ -105,13 +113,14 @@ class Cache:
         if (self.mu_sub is None) != (self.radius_sub is None) or (self.mu_sub is None) != (self.sub_block == 0):
             raise ValueError("sub_block, mu_sub and radius_sub go together")
         if self.mu_sub is not None:
-            if self.sub_block not in (16, 32):
-                raise ValueError("sub_block must be 16 or 32")
-            sb = BLOCK // self.sub_block
+            if self.sub_block not in (16, 32, 128):
+                raise ValueError("sub_block must be 16, 32 or 128")
+            sb = sub_slots(self.sub_block)
             _need(self.mu_sub, "mu_sub", torch.float16, dev)
             _need(self.radius_sub, "radius_sub", torch.float32, dev)
             if tuple(self.mu_sub.shape) != (P, H, sb, D) or tuple(self.radius_sub.shape) != (P, H, sb):
-                raise ValueError("mu_sub must be [num_pages][H_KV][64/sub_block][d], radius_sub [num_pages][H_KV][64/sub_block]")
+                raise ValueError("mu_sub must be [num_pages][H_KV][slots][d], radius_sub [num_pages][H_KV][slots] "
+                                 "(slots = 64/sub_block, or 1 for 128)")
 
     @classmethod
     def empty(cls, num_pages, num_kv_heads, head_dim, dtype=torch.bfloat16, device="cuda", with_sigma=False,
@@ -125,7 +134,7 @@ class Cache:
         hi = torch.zeros_like(mu) if with_box else None
         mu8 = torch.zeros(num_pages, num_kv_heads, head_dim, dtype=torch.uint8, device=device) if fp8 else None
         r8 = torch.zeros_like(r) if fp8 else None
-        sb = BLOCK // sub_block if sub_block else 0
+        sb = sub_slots(sub_block) if sub_block else 0
         mus = torch.zeros(num_pages, num_kv_heads, sb, head_dim, dtype=torch.float16, device=device) if sb else None
         rs = torch.zeros(num_pages, num_kv_heads, sb, dtype=torch.float32, device=device) if sb else None
         return cls(k, v, mu, r, sig, lo, hi, mu8, r8, fp8 or "e4m3", sub_block, mus, rs)
@@ -313,20 +322,24 @@ class Stats:
 
 def stats(workspace: torch.Tensor, num_seqs: int, max_blocks_per_seq: int, num_q_heads: int,
           num_kv_heads: int, bitmap: bool = True, stream=None, check: bool = True,
-          blocks_per_page: Optional[int] = None) -> Stats:
-    """Counts of the last decode on this workspace. blocks_per_page: screen
-    blocks per 64-token page of that decode (64 / sub_block after a
-    "geometric_sub" decode, else 1), which sizes the bitmap; read from the
-    workspace's header when not given."""
-    if blocks_per_page is None:
-        blocks_per_page = int(workspace[:64].view(torch.int32)[_WS_GLOB_SB].item()) if bitmap else 1
-        blocks_per_page = blocks_per_page if blocks_per_page in (2, 4) else 1
+          block_tokens: Optional[int] = None) -> Stats:
+    """Counts of the last decode on this workspace. block_tokens: tokens per
+    screen block of that decode (cache.sub_block after a "geometric_sub"
+    decode, else 64), which sizes the bitmap (ceil(64 max_blocks_per_seq /
+    block_tokens) bits per head); read from the workspace's header when not
+    given."""
+    if block_tokens is None:
+        block_tokens = BLOCK
+        if bitmap:
+            hdr = workspace[:64].view(torch.int32)
+            sb, pb = int(hdr[_WS_GLOB_SB].item()), int(hdr[_WS_GLOB_PB].item())
+            block_tokens = BLOCK // sb if sb in (2, 4) else 2 * BLOCK if pb == 2 else BLOCK
+    nbits = -(-max_blocks_per_seq * BLOCK // block_tokens)
     a = np.zeros((num_seqs, num_q_heads), np.int32)
     u = np.zeros((num_seqs, num_kv_heads), np.int32)
     t = np.zeros((num_seqs, num_q_heads), np.int64)
     r = np.zeros((num_seqs, num_q_heads), np.uint8)
-    bm = np.zeros((num_seqs, num_q_heads, (max_blocks_per_seq * blocks_per_page + 31) // 32), np.uint32) \
-        if bitmap else None
+    bm = np.zeros((num_seqs, num_q_heads, (nbits + 31) // 32), np.uint32) if bitmap else None
     st = _lib.lib().eta_stats(_ptr(workspace), num_seqs, max_blocks_per_seq, num_q_heads, num_kv_heads,
                               a.ctypes.data, u.ctypes.data, t.ctypes.data, r.ctypes.data,
                               None if bm is None else bm.ctypes.data, _stream(stream))

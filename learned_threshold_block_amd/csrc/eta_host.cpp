@@ -75,7 +75,8 @@ eta_status check_cache(const eta_cache* c) {
   if (c->mu8 && c->mu8_format != ETA_FP8_E4M3 && c->mu8_format != ETA_FP8_E5M2) return ETA_ERR_INVALID_ARGUMENT;
   if ((c->mu_sub == nullptr) != (c->radius_sub == nullptr) || !aligned(c->mu_sub, 16) || !aligned(c->radius_sub, 4))
     return ETA_ERR_INVALID_ARGUMENT;
-  if (c->mu_sub && c->sub_block != 16 && c->sub_block != 32) return ETA_ERR_INVALID_ARGUMENT;
+  if (c->mu_sub && c->sub_block != 16 && c->sub_block != 32 && c->sub_block != 2 * kBlock)
+    return ETA_ERR_INVALID_ARGUMENT;
   if (c->head_dim != 64 && c->head_dim != 128) return ETA_ERR_UNSUPPORTED;
   if (c->block_size != kBlock) return ETA_ERR_UNSUPPORTED;
   if ((int64_t)c->num_pages * c->num_kv_heads > (int64_t)1 << 31) return ETA_ERR_UNSUPPORTED;
@@ -108,7 +109,7 @@ CacheView view_of(const eta_cache* c) {
   v.mu8 = c->mu8;
   v.radius8 = c->radius8;
   v.mu8_fmt = c->mu8_format == ETA_FP8_E5M2 ? 1 : 0;
-  v.sub = c->mu_sub ? kBlock / c->sub_block : 0;
+  v.sub_rows = c->mu_sub ? c->sub_block : 0;
   v.mu_sub = c->mu_sub;
   v.radius_sub = c->radius_sub;
   return v;
@@ -123,7 +124,7 @@ SeqView view_of(const eta_seqs* s) {
   return v;
 }
 
-eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d, int SB = 1) {
+eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d, int SB = 1, int PB = 1) {
   if (N < 1 || MB < 1 || HQ < 1) return ETA_ERR_INVALID_ARGUMENT;
   if (HQ % c->num_kv_heads) return ETA_ERR_INVALID_ARGUMENT;
   const int G = HQ / c->num_kv_heads;
@@ -142,12 +143,14 @@ eta_status dims_of(const eta_cache* c, int N, int MB, int HQ, Dims* d, int SB = 
   // keeps a sequence's tile prefix in LDS, sized for kMaxBlocksPerSeq blocks)
   if ((int64_t)MB * SB > kMaxBlocksPerSeq || S * MB * SB >= ((int64_t)1 << 31) / 64) return ETA_ERR_UNSUPPORTED;
   d->SB = SB;
+  d->PB = PB;
   d->NT = (MB * SB + kTile - 1) / kTile;
   return ETA_OK;
 }
 
-// Screen blocks per page of the cache's smaller-block records (1 if none).
-int sub_blocks(const eta_cache* c) { return c->mu_sub ? kBlock / c->sub_block : 1; }
+// Screen blocks per page of the cache's smaller-block records (1 if none or
+// if they are 128-token blocks).
+int sub_blocks(const eta_cache* c) { return c->mu_sub && c->sub_block < kBlock ? kBlock / c->sub_block : 1; }
 
 // attend grid: one resident wave of workgroups over the whole device
 std::mutex g_geom_mu;
@@ -214,7 +217,7 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
     }
     if (screen->bound == ETA_BOUND_GEOMETRIC_SUB) {
       if (!cache->mu_sub) return ETA_ERR_INVALID_ARGUMENT;
-      P->p.bound = 4;
+      P->p.bound = cache->sub_block > kBlock ? 5 : 4;
     }
   }
   st = check_seqs(seqs);
@@ -226,7 +229,7 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
   if (tau_mode == ETA_TAU_LEARNED && (!w || !aligned(w, 16))) return ETA_ERR_INVALID_ARGUMENT;
   if (!(beta > 0.f) || !isfinite(beta) || !isfinite(a) || lwb < 0) return ETA_ERR_INVALID_ARGUMENT;
   st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &P->d,
-               P->p.bound == 4 ? sub_blocks(cache) : 1);
+               P->p.bound == 4 ? sub_blocks(cache) : 1, P->p.bound == 5 ? 2 : 1);
   if (st != ETA_OK) return st;
   if (!workspace || !aligned(workspace, 256)) return ETA_ERR_INVALID_ARGUMENT;
   if (ws_bytes < workspace_layout(P->d, nullptr, nullptr)) return ETA_ERR_WORKSPACE_TOO_SMALL;
@@ -460,6 +463,7 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
   d.G = num_q_heads / num_kv_heads;
   d.S = num_seqs * num_kv_heads;
   d.SB = (glob[kGlobSB] == 2 || glob[kGlobSB] == 4) ? glob[kGlobSB] : 1;
+  d.PB = (d.SB == 1 && glob[kGlobPB] == 2) ? 2 : 1;
   d.NT = (max_blocks_per_seq * d.SB + kTile - 1) / kTile;
   d.D = 128;  // only the part_* sizes depend on D; they lie after everything read here
   Ws ws;
@@ -480,14 +484,23 @@ eta_status eta_stats(const void* workspace, int num_seqs, int max_blocks_per_seq
   }
   if (admitted_bitmap) {
     // tile_bits is [S][G][NT] == [N][HQ][NT] uint64 words, little-endian: the
-    // same bit order as [N][HQ][2*NT] uint32 words
-    const size_t words32 = (size_t)(max_blocks_per_seq * d.SB + 31) / 32;
+    // same bit order as [N][HQ][2*NT] uint32 words. With 128-token blocks a
+    // bit is a page and block m is bit 2m.
+    const size_t nbits = d.PB == 2 ? (size_t)(max_blocks_per_seq + 1) / 2 : (size_t)max_blocks_per_seq * d.SB;
+    const size_t words32 = (nbits + 31) / 32;
     std::vector<uint64_t> bits(nq * d.NT);
     if (hipMemcpy(bits.data(), ws.tile_bits, sizeof(uint64_t) * bits.size(), hipMemcpyDeviceToHost) != hipSuccess)
       return ETA_ERR_HIP;
     for (size_t i = 0; i < nq; ++i) {
-      const uint32_t* src = reinterpret_cast<const uint32_t*>(bits.data() + i * d.NT);
-      memcpy(admitted_bitmap + i * words32, src, sizeof(uint32_t) * words32);
+      const uint64_t* row = bits.data() + i * d.NT;
+      uint32_t* dst = admitted_bitmap + i * words32;
+      if (d.PB == 2) {
+        memset(dst, 0, sizeof(uint32_t) * words32);
+        for (size_t m = 0; m < nbits; ++m)
+          if ((row[(2 * m) / 64] >> ((2 * m) % 64)) & 1ull) dst[m / 32] |= 1u << (m % 32);
+      } else {
+        memcpy(dst, reinterpret_cast<const uint32_t*>(row), sizeof(uint32_t) * words32);
+      }
     }
   }
   std::vector<int32_t> serr(d.S);

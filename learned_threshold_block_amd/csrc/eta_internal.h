@@ -29,12 +29,14 @@ enum Glob : int {
   kGlobStatMagic = 5,  // kStatMagic once an attend kernel has written rng_stat
   kGlobStatW = 6,      // ranges that attend kernel had
   kGlobSB = 7,         // screen blocks per page of the last decode (1, 2 or 4)
+  kGlobPB = 8,         // pages per screen block of the last decode (1 or 2)
   kGlobCount = 16
 };
 
 struct Dims {
   int N, MB, HQ, HKV, D, G, S, NT;  // S = N*HKV segments, NT = tiles of 64 screen blocks per segment
-  int SB;                           // screen blocks per 64-token page: 1 (b = 64), 2 (b = 32) or 4 (b = 16)
+  int SB;                           // screen blocks per 64-token page: 1 (b = 64, 128), 2 (b = 32) or 4 (b = 16)
+  int PB;                           // pages per screen block: 1, or 2 (b = 128; the screen's lanes stay pages)
 };
 
 // Device pointers into one caller-provided workspace.
@@ -48,7 +50,9 @@ struct Ws {
   int32_t* tile_off;    // [S][NT+2]    exclusive prefix of tile_cnt over the segment's used tiles,
                         //              the rescue tile last (index ntn), total at ntn+1
   int32_t* tile_hcnt;   // [S][NT][G]   admitted blocks per head per tile
-  uint64_t* tile_bits;  // [S][G][NT]   per-head admission bitmap words
+  uint64_t* tile_bits;  // [S][G][NT]   per-head admission bitmap words, a bit per screen lane (a
+                        //              screen block; with 128-token blocks a page, both pages of a
+                        //              block carrying its bit)
   float* tile_umax;     // [S][NT][G]   largest bound among complete blocks
   int32_t* tile_uarg;   // [S][NT][G]   its block index (lowest on ties)
   int32_t* tile_err;    // [S][NT]
@@ -84,10 +88,14 @@ struct CacheView {
   uint8_t* mu8;     // may be null (with radius8): FP8 centroids
   float* radius8;
   int mu8_fmt;      // 0 E4M3, 1 E5M2
-  int sub;          // records of smaller screen blocks: blocks per page (2 or 4), 0 if none
-  uint16_t* mu_sub;  // [pages][HKV][sub][D]
-  float* radius_sub;  // [pages][HKV][sub]
+  int sub_rows;     // tokens per block of the other screen-block records (16, 32 or 128), 0 if none
+  uint16_t* mu_sub;  // [pages][HKV][sub_slots(sub_rows)][D]; a 128-token block's record with its first page
+  float* radius_sub;  // [pages][HKV][sub_slots(sub_rows)]
 };
+
+// Record slots per page for screen blocks of `rows` tokens: 64/rows for blocks
+// inside a page, one (kept by the first page) for a block of two pages.
+__host__ __device__ constexpr int sub_slots(int rows) { return rows < kBlock ? kBlock / rows : 1; }
 
 struct SeqView {
   int N, MB;
@@ -105,7 +113,8 @@ struct DecodeParams {
   float* out;
   int deterministic;  // static work split and claims: bitwise-reproducible results
   int bound;          // 0 geometric, 1 dual (tightened by z deviations), 2 comparator box bound,
-                      // 3 geometric over the FP8 records, 4 geometric over smaller screen blocks
+                      // 3 geometric over the FP8 records, 4 geometric over screen blocks of 16 or
+                      // 32 tokens, 5 geometric over screen blocks of 128 tokens
   float z;
   int fixed_w[kXcdClasses];  // if fixed_w[0] > 0: per-die weights to use instead of measured ones
 };

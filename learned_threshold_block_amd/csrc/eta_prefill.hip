@@ -366,22 +366,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                             A.c.mu8 ? A.c.radius8 + rec : nullptr, A.c.mu8_fmt, lane);
     }
   }
-  // records of the smaller screen blocks (16 or 32 tokens) that end in this tile
-  if (hc == 0 && A.c.sub) {
-    const int sb = A.c.sub, rows = kBlock / sb;
-    for (int q = wave; q < QT / rows; q += kPfWaves) {
-      const int js = P0 / rows + q;
+  // records of the other screen blocks (16, 32 or 128 tokens) that end in this
+  // tile: blocks js with P0 <= js rows + rows - 1 < P0 + QT
+  if (hc == 0 && A.c.sub_rows) {
+    const int rows = A.c.sub_rows, sb = sub_slots(rows);
+    const int js_end = (P0 + QT) / rows;  // one past the last block ending in the tile
+    for (int js = P0 / rows + wave; js < js_end; js += kPfWaves) {
       if (js * rows + rows > T) break;
-      const int page = bt[js / sb];
+      const int p0 = (int)((int64_t)js * rows / kBlock);  // table entry of the block's first page
+      const int page = bt[p0];
       if (page < 0 || page >= A.c.num_pages) continue;
       const int64_t srec = ((int64_t)page * HKV + g) * sb + js % sb;
-      const uint16_t* tile = (const uint16_t*)A.c.k + srec * rows * D;
-      if (rows == 16)
+      const uint16_t* tile = (const uint16_t*)A.c.k + (((int64_t)page * HKV + g) * kBlock + (js % sb) * (kBlock / sb)) * D;
+      if (rows == 16) {
         build_record<Bf16, D, 16>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, 0, lane);
-      else
+      } else if (rows == 32) {
         build_record<Bf16, D, 32>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
                                   nullptr, nullptr, nullptr, 0, lane);
+      } else {
+        const int page1 = bt[p0 + 1];  // p0 + 1 < ceil(T / 64): the block is complete
+        if (page1 < 0 || page1 >= A.c.num_pages) continue;
+        build_record<Bf16, D, 128>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                   nullptr, nullptr, nullptr, 0, lane,
+                                   (const uint16_t*)A.c.k + ((int64_t)page1 * HKV + g) * kBlock * D);
+      }
     }
   }
 }

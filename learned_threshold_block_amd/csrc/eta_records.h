@@ -1,7 +1,8 @@
 // Block record builder shared by the record kernels and the prompt pass:
 // centroid mu^ (float16, nearest even) and radius R^ (float32, rounded up) of
-// one complete 64-token key block, and optionally its coordinate deviation and
-// its coordinate-wise key box (the comparator's record).
+// one complete key block (a 64-token page, or a screen block of 16, 32 or 128
+// tokens), and optionally its coordinate deviation, its coordinate-wise key box
+// (the comparator's record) and its FP8 record.
 //
 // "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Section 3.2
 // and Appendix F.1: the decode screen reads one compact record per block and
@@ -26,8 +27,9 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
 }
 
 // One wavefront. tile: [ROWS][D] keys of one block (a whole 64-token page, or
-// a 16- or 32-token block of it). If override_row is non-null, the last row is
-// read from it instead of the tile. Lanes own columns;
+// a 16- or 32-token block of it); a 128-token block takes its first 64 rows
+// from tile and the other 64 from tile_hi (its second page). If override_row
+// is non-null, the last row is read from it instead. Lanes own columns;
 // the rows are read twice (sums, then distances and deviations), which keeps
 // the register footprint small enough for eight wavefronts per SIMD. Writes
 // the centroid and radius, the coordinate deviation if sig_out is not null,
@@ -40,8 +42,15 @@ __device__ __forceinline__ float load_elem<F32>(const float* p) {
 template <typename T, int D, int ROWS = kBlock>
 __device__ void build_record(const typename T::Stored* tile, const typename T::Stored* override_row,
                              uint16_t* mu_out, float* r_out, uint16_t* sig_out, uint16_t* kmin_out,
-                             uint16_t* kmax_out, uint8_t* mu8_out, float* r8_out, int fmt8, int lane) {
+                             uint16_t* kmax_out, uint8_t* mu8_out, float* r8_out, int fmt8, int lane,
+                             const typename T::Stored* tile_hi = nullptr) {
+  static_assert(ROWS == 16 || ROWS == 32 || ROWS == kBlock || ROWS == 2 * kBlock, "block of 16, 32, 64 or 128 keys");
   constexpr int CPL = D / 64;  // columns per lane: 2 (D=128) or 1 (D=64)
+  const auto row_at = [&](int r) -> const typename T::Stored* {
+    if (r == ROWS - 1 && override_row) return override_row;
+    if (ROWS > kBlock && r >= kBlock) return tile_hi + (r - kBlock) * D;
+    return tile + r * D;
+  };
   double sum[CPL];
   float cmin[CPL], cmax[CPL];
   bool finite = true;
@@ -52,7 +61,7 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
     cmax[c] = -__builtin_inff();
   }
   for (int r = 0; r < ROWS; ++r) {
-    const typename T::Stored* row = (r == ROWS - 1 && override_row) ? override_row : tile + r * D;
+    const typename T::Stored* row = row_at(r);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const float x = load_elem<T>(row + lane * CPL + c);
@@ -97,7 +106,7 @@ __device__ void build_record(const typename T::Stored* tile, const typename T::S
   }
   double rmax = 0.0, rmax8 = 0.0;
   for (int r = 0; r < ROWS; ++r) {
-    const typename T::Stored* row = (r == ROWS - 1 && override_row) ? override_row : tile + r * D;
+    const typename T::Stored* row = row_at(r);
     double part = 0.0, part8 = 0.0;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {

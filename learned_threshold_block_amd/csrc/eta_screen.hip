@@ -17,7 +17,11 @@
 //   blocks    or the geometric bound on screen blocks of 16 or 32 tokens (2 or
 //             4 per page, each with its own record; Appendix F.3's block size):
 //             the block index j then counts those blocks, and the compacted
-//             entries stay one per page, with a word of per-head block bits
+//             entries stay one per page, with a word of per-head block bits;
+//             or on blocks of 128 tokens (two consecutive block-table entries,
+//             the record kept with the first page): lanes stay pages, both
+//             pages of a block take its bound and its bits, and the counts
+//             count blocks
 //   counts    per-head blocks, union blocks, attended tokens (F.4)
 //
 // k_screen: one wavefront per 64 consecutive blocks of one (sequence, KV head).
@@ -68,10 +72,10 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
 
 // MODE: 0 geometric bound, 1 dual score, 2 comparator box bound, 3 geometric
 // bound over the FP8 records, 4 geometric bound on smaller screen blocks
-// (SB = A.d.SB of them per page).
+// (SB = A.d.SB of them per page), 5 geometric bound on 128-token blocks.
 template <typename T, int D, int G, int MODE>
 __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
-  constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3, SUBB = MODE == 4;
+  constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3, SUBB = MODE == 4, PAIR = MODE == 5;
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
@@ -89,6 +93,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     A.ws.glob[kGlobHKV] = HKV;
     A.ws.glob[kGlobD] = D;
     A.ws.glob[kGlobSB] = A.d.SB;
+    A.ws.glob[kGlobPB] = A.d.PB;
   }
   if (t >= NT) return;
   const int64_t tix = (int64_t)s * NT + t;
@@ -100,13 +105,19 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   //      queries and predictor weights; then centroids and radii
   const int seq_len = A.s.lens[n];
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
-  // screen blocks per page (1 unless SUBB) and its log2
+  // screen blocks per page (1 unless SUBB) and its log2. A lane's unit j is a
+  // screen block, or with 128-token blocks a page (block j / 2, whose record
+  // lives with page j & ~1).
   const int SB = SUBB ? A.d.SB : 1, lsb = SUBB ? (A.d.SB == 4 ? 2 : 1) : 0;
-  int pg[NI];
+  int pg[NI];  // pages holding the records
 #pragma unroll
-  for (int i = 0; i < NI; ++i) pg[i] = bt[min((j0 + RPI * i + r) >> lsb, MB - 1)];
-  const int jl = j0 + RPI * cb + r;  // block this lane owns after the reduction
+  for (int i = 0; i < NI; ++i) {
+    const int j = j0 + RPI * i + r;
+    pg[i] = bt[min(PAIR ? (j & ~1) : j >> lsb, MB - 1)];
+  }
+  const int jl = j0 + RPI * cb + r;  // unit this lane owns after the reduction
   const int page_l = bt[min(jl >> lsb, MB - 1)];
+  const int page_r = PAIR ? bt[min(jl & ~1, MB - 1)] : page_l;
 
   float qf[G][8];
   const auto* qbase = (const typename T::Stored*)A.p.q;
@@ -130,17 +141,20 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   // tiles past the sequence run through with every block invalid: no entries,
   // zero bitmap words
   const bool badT = seq_len < 1 || seq_len > kBlock * MB;
-  const int bsz = kBlock >> lsb;  // tokens per screen block
+  const int bsz = PAIR ? 2 * kBlock : kBlock >> lsb;  // tokens per screen block
   const int nfull = badT ? 0 : seq_len / bsz;
   const int nblk = badT ? 0 : (seq_len + bsz - 1) / bsz;
-  const bool lvalid = jl < nblk && page_l >= 0 && page_l < A.c.num_pages;
-  const bool complete = jl < nfull && lvalid;
+  const int nunit = PAIR ? (badT ? 0 : (seq_len + kBlock - 1) / kBlock) : nblk;  // lanes' units in the sequence
+  const int jbl = PAIR ? jl >> 1 : jl;                                            // the lane's screen block
+  const bool lvalid = jl < nunit && page_l >= 0 && page_l < A.c.num_pages;
+  const bool complete = jbl < nfull && lvalid && page_r >= 0 && page_r < A.c.num_pages;
   // records through buffer loads: an invalid block reads zeros, without a branch
   // (the box bound reads the key box's lower corner here and its upper one below;
   // a smaller screen block's record is block j mod SB of its page's records)
-  const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : SUBB ? (const void*)A.c.mu_sub : (const void*)A.c.mu,
+  const auto mu_rsrc = make_rsrc(BOX ? (const void*)A.c.kmin : (SUBB || PAIR) ? (const void*)A.c.mu_sub
+                                                                              : (const void*)A.c.mu,
                                  (uint32_t)((int64_t)A.c.num_pages * HKV * SB * D * 2));
-  const auto r_rsrc = make_rsrc(SUBB ? (const void*)A.c.radius_sub : (const void*)A.c.radius,
+  const auto r_rsrc = make_rsrc((SUBB || PAIR) ? (const void*)A.c.radius_sub : (const void*)A.c.radius,
                                 (uint32_t)((int64_t)A.c.num_pages * HKV * SB * 4));
   const auto mu8_rsrc = make_rsrc(A.c.mu8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * D) : 0u);
   const auto r8_rsrc = make_rsrc(A.c.radius8, FP8 ? (uint32_t)((int64_t)A.c.num_pages * HKV * 4) : 0u);
@@ -148,7 +162,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
     const int j = j0 + RPI * i + r;
-    const bool ok = j < nfull && pg[i] >= 0 && pg[i] < A.c.num_pages;
+    const bool ok = (PAIR ? j >> 1 : j) < nfull && pg[i] >= 0 && pg[i] < A.c.num_pages;
     if constexpr (FP8) {
       const uint32_t off = ok ? (uint32_t)(((int64_t)pg[i] * HKV + g) * D + cb * 8) : kOutOfRange;
       const auto v = __builtin_amdgcn_raw_buffer_load_b64(mu8_rsrc, off, 0, 0);
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       raw[i] = make_uint4(v[0], v[1], v[2], v[3]);
     }
   }
-  const uint32_t roff = complete ? (uint32_t)((((int64_t)page_l * HKV + g) * SB + (jl & (SB - 1))) * 4) : kOutOfRange;
+  const uint32_t roff = complete ? (uint32_t)((((int64_t)page_r * HKV + g) * SB + (jl & (SB - 1))) * 4) : kOutOfRange;
   const float R = BOX ? 0.f
                       : __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(FP8 ? r8_rsrc : r_rsrc, roff, 0, 0));
   // dual screen: coordinate deviations; box bound: upper corners (both laid
@@ -279,10 +293,13 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
       const float est = A.p.scale * (pd[h][0] + A.p.z * sqrtf(ps[h][0]));
       ub[h] = fminf(ub[h], est);
     }
+    // both pages of a 128-token block take the bound of its first page's lane
+    // (unit j ^ 1 sits LPR lanes away), so they are admitted and ranked as one
+    if constexpr (PAIR) ub[h] = __shfl(ub[h], lane & ~LPR, 64);
     if (complete && !(ub[h] < tau[h])) mask |= 1u << h;
   }
-  if (complete && jl >= nfull - A.p.lwb) mask = full;
-  if (jl == nfull && lvalid) mask = full;  // partial last block (exists iff nfull < nblk)
+  if (complete && jbl >= nfull - A.p.lwb) mask = full;
+  if (jbl == nfull && lvalid) mask = full;  // partial last block (exists iff nfull < nblk)
 
   // ---- back to block order (lane l then holds block j0 + l), the largest
   //      bound per head among complete blocks (lowest index on ties), and
@@ -334,18 +351,20 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
     const int pos = __popcll(ball & ((1ull << lane) - 1ull));
     if (mb) A.ws.tile_ent[tcx * kTile + pos] = make_int2(pb, ((j0 + lane) << 8) | (int)mb);
   }
-  const bool bad_page = jl < nblk && !lvalid;
+  const bool bad_page = jl < nunit && !lvalid;
   const bool any_bad = __any(bad_page);
   if (lane == 0) {
     A.ws.tile_cnt[tcx] = __popcll(ball);
     A.ws.tile_err[tix] = any_bad ? 1 : 0;
   }
+  // counts are in screen blocks: a 128-token block is counted on its first page
+  const uint64_t cnt_lanes = PAIR ? 0x5555555555555555ull : ~0ull;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const uint64_t hb = __ballot((mb >> h) & 1u);
     if (lane == h) {
       A.ws.tile_bits[((int64_t)s * G + h) * NT + t] = hb;
-      A.ws.tile_hcnt[tix * G + h] = __popcll(hb);
+      A.ws.tile_hcnt[tix * G + h] = __popcll(hb & cnt_lanes);
     }
   }
 }
@@ -446,10 +465,14 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int seq_len = A.s.lens[n];
   const bool badT = seq_len < 1 || seq_len > kBlock * MB;
   const int SB = A.d.SB, lsb = SB == 4 ? 2 : SB == 2 ? 1 : 0;  // screen blocks per page
-  const int bsz = kBlock >> lsb;                               // tokens per screen block
+  const bool pair = A.d.PB == 2;                               // 128-token blocks, screen lanes are pages
+  const bool blk_bits = SB > 1 || pair;                        // union counted from the bitmaps
+  const int bsz = pair ? 2 * kBlock : kBlock >> lsb;           // tokens per screen block
   const int nfull = badT ? 0 : seq_len / bsz;
   const int nblk = badT ? 0 : (seq_len + bsz - 1) / bsz;
-  const int ntn = (nblk + kTile - 1) / kTile;
+  const int nunit = pair ? (badT ? 0 : (seq_len + kBlock - 1) / kBlock) : nblk;  // screen lanes used
+  const int ntn = (nunit + kTile - 1) / kTile;
+  const uint64_t cnt_lanes = pair ? 0x5555555555555555ull : ~0ull;  // a block counts on its first lane
   const int64_t tix0 = (int64_t)s * NT;
   const int64_t tcx0 = (int64_t)s * (NT + 1);
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   __shared__ int s_uarg[4][G];
   __shared__ int s_err[4];
   __shared__ int s_nres;
-  __shared__ int s_res_j[G];
+  __shared__ int s_res_j[2 * G];
   __shared__ int s_resc[G];
   __shared__ int s_ub[4];
 
@@ -498,13 +521,13 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
         hcl[h] = A.ws.tile_hcnt[(tix0 + t) * G + h];
         uml[h] = A.ws.tile_umax[(tix0 + t) * G + h];
         ual[h] = A.ws.tile_uarg[(tix0 + t) * G + h];
-        if (SB > 1) orb |= A.ws.tile_bits[((int64_t)s * G + h) * NT + t];
+        if (blk_bits) orb |= A.ws.tile_bits[((int64_t)s * G + h) * NT + t];
       }
     }
     const bool use = t < ntn;
     if (use) {
       err |= e;
-      ublk += __popcll(orb);
+      ublk += __popcll(orb & cnt_lanes);
 #pragma unroll
       for (int h = 0; h < G; ++h) {
         hc[h] += hcl[h];
@@ -524,7 +547,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int ucnt = carry;
   const bool err_w = __any(err != 0);
   if (lane == 0) s_err[wave] = err_w ? 1 : 0;
-  if (SB > 1) {
+  if (blk_bits) {
     const int ub_w = wave_sum_i(ublk);
     if (lane == 0) s_ub[wave] = ub_w;
   }
@@ -562,9 +585,11 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   // 2. rescue (thread 0): a head with nothing admitted gets its best-bound
   //    block; if another head of the group loads it already, only the head's
   //    bit is added to that entry, otherwise it becomes a rescue-tile entry.
+  //    The arg index is a screen lane: a block, or the first page of a
+  //    128-token block (whose two pages both get the head's bit).
   if (tid == 0) {
     int nres = 0;
-    int ub = SB > 1 ? s_ub[0] + s_ub[1] + s_ub[2] + s_ub[3] : 0;  // screen blocks admitted by any head
+    int ub = blk_bits ? s_ub[0] + s_ub[1] + s_ub[2] + s_ub[3] : 0;  // screen blocks admitted by any head
     for (int h = 0; h < G; ++h) {
       int tot = 0;
       for (int w = 0; w < 4; ++w) tot += s_hcnt[w][h];
@@ -579,40 +604,42 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
         }
       }
       s_resc[h] = -1;
-      if (tot == 0 && jb >= 0 && jb < nfull) {
+      if (tot == 0 && jb >= 0 && (pair ? jb >> 1 : jb) < nfull) {
         s_resc[h] = jb;
         tot = 1;
-        const int tt = jb / kTile;
-        const int jp = jb >> lsb;                                     // its page's index
-        const uint32_t sbit = SB > 1 ? 1u << ((jb & (SB - 1)) * G + h) : 0u;
-        if (SB > 1) {  // a new block for the union unless another head admits it
+        const int tt = jb / kTile;  // both pages of a 128-token block lie in one tile
+        if (blk_bits) {             // a new block for the union unless another head admits it
           uint64_t any = 0;
           for (int h2 = 0; h2 < G; ++h2) any |= A.ws.tile_bits[((int64_t)s * G + h2) * NT + tt];
           if (!((any >> (jb % kTile)) & 1ull)) ++ub;
         }
         int2* ent = A.ws.tile_ent + (tcx0 + tt) * kTile;
         const int c = A.ws.tile_cnt[tcx0 + tt];
-        int found = -1;
-        for (int k = 0; k < c; ++k)
-          if ((ent[k].y >> 8) == jp) found = k;
-        if (found >= 0) {
-          ent[found].y |= 1 << h;
-          if (SB > 1) A.ws.tile_sub[(tcx0 + tt) * kTile + found] |= sbit;
-        } else {
-          int q = 0;
-          for (; q < nres; ++q)
-            if (s_res_j[q] == jp) break;
-          int2* rent = A.ws.tile_ent + (tcx0 + NT) * kTile;
-          if (q == nres) {
-            s_res_j[q] = jp;
-            rent[q] = make_int2(bt[jp], jp << 8);
-            if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] = 0u;
-            ++nres;
+        for (int u = jb; u <= (pair ? jb + 1 : jb); ++u) {
+          const int jp = u >> lsb;  // the unit's page
+          const uint32_t sbit = SB > 1 ? 1u << ((u & (SB - 1)) * G + h) : 0u;
+          int found = -1;
+          for (int k = 0; k < c; ++k)
+            if ((ent[k].y >> 8) == jp) found = k;
+          if (found >= 0) {
+            ent[found].y |= 1 << h;
+            if (SB > 1) A.ws.tile_sub[(tcx0 + tt) * kTile + found] |= sbit;
+          } else {
+            int q = 0;
+            for (; q < nres; ++q)
+              if (s_res_j[q] == jp) break;
+            int2* rent = A.ws.tile_ent + (tcx0 + NT) * kTile;
+            if (q == nres) {
+              s_res_j[q] = jp;
+              rent[q] = make_int2(bt[jp], jp << 8);
+              if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] = 0u;
+              ++nres;
+            }
+            rent[q].y |= 1 << h;
+            if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] |= sbit;
           }
-          rent[q].y |= 1 << h;
-          if (SB > 1) A.ws.tile_sub[(tcx0 + NT) * kTile + q] |= sbit;
+          A.ws.tile_bits[((int64_t)s * G + h) * NT + tt] |= 1ull << (u % kTile);
         }
-        A.ws.tile_bits[((int64_t)s * G + h) * NT + tt] |= 1ull << (jb % kTile);
       }
       s_hcnt[0][h] = tot;
     }
@@ -637,7 +664,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   }
   if (tid == 0) {
     A.ws.seg_U[s] = U;
-    A.ws.seg_ub[s] = SB > 1 ? (badT ? 0 : s_ub[0]) : U;
+    A.ws.seg_ub[s] = blk_bits ? (badT ? 0 : s_ub[0]) : U;
     A.ws.seg_ntn[s] = ntn;
     A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
     A.ws.seg_done[s] = 0;
@@ -660,6 +687,7 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
   else if (p.bound == 2) hipLaunchKernelGGL((k_screen<T, D, G, 2>), grid, dim3(256), 0, st, a);
   else if (p.bound == 3) hipLaunchKernelGGL((k_screen<T, D, G, 3>), grid, dim3(256), 0, st, a);
   else if (p.bound == 4) hipLaunchKernelGGL((k_screen<T, D, G, 4>), grid, dim3(256), 0, st, a);
+  else if (p.bound == 5) hipLaunchKernelGGL((k_screen<T, D, G, 5>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_screen<T, D, G, 0>), grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }

@@ -41,29 +41,42 @@ __global__ __launch_bounds__(256) void k_build(CacheView c, SeqView s) {
                      c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
 }
 
-// Records of the smaller screen blocks (16 or 32 tokens, ROWS): one wavefront
-// per (sequence, block, KV head), complete blocks only; block j of a sequence
-// is rows (j mod 64/ROWS) ROWS .. + ROWS - 1 of page block_table[n][j ROWS / 64].
+// Records of the other screen blocks (ROWS = 16, 32 or 128 tokens): one
+// wavefront per (sequence, block, KV head), complete blocks only. Block j of a
+// sequence holds its tokens j ROWS .. j ROWS + ROWS - 1: with 16 or 32 tokens
+// rows (j mod 64/ROWS) ROWS .. + ROWS - 1 of page block_table[n][j ROWS / 64],
+// with 128 the pages block_table[n][2j] and [2j + 1], its record kept with
+// the first of them.
 template <typename T, int D, int ROWS>
 __global__ __launch_bounds__(256) void k_build_sub(CacheView c, SeqView s) {
-  constexpr int SB = kBlock / ROWS;
+  constexpr int SB = sub_slots(ROWS);                      // record slots per page
+  constexpr int PB = ROWS > kBlock ? ROWS / kBlock : 1;    // pages per block
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over N * MB * SB * HKV
-  const int64_t total = (int64_t)s.N * s.MB * SB * c.HKV;
+  const int64_t nbs = ((int64_t)s.MB * SB + PB - 1) / PB;  // blocks per block-table row
+  const int64_t idx = (int64_t)blockIdx.x * 4 + wave;      // over N * nbs * HKV
+  const int64_t total = (int64_t)s.N * nbs * c.HKV;
   if (idx >= total) return;
   const int g = (int)(idx % c.HKV);
   const int64_t nj = idx / c.HKV;
-  const int j = (int)(nj % ((int64_t)s.MB * SB));
-  const int n = (int)(nj / ((int64_t)s.MB * SB));
+  const int j = (int)(nj % nbs);
+  const int n = (int)(nj / nbs);
   const int len = s.lens[n];
   if (len < 1 || len > kBlock * s.MB) return;
   if (j >= len / ROWS) return;
-  const int page = s.bt[(int64_t)n * s.MB + j / SB];
+  const int p0 = (int)((int64_t)j * ROWS / kBlock);  // table entry of the block's first page
+  const int page = s.bt[(int64_t)n * s.MB + p0];
   if (page < 0 || page >= c.num_pages) return;
+  using St = typename T::Stored;
   const int64_t rec = ((int64_t)page * c.HKV + g) * SB + j % SB;
-  const auto* tile = (const typename T::Stored*)c.k + rec * ROWS * D;
+  const St* tile = (const St*)c.k + (((int64_t)page * c.HKV + g) * kBlock + (j % SB) * (kBlock / SB)) * D;
+  const St* hi = nullptr;
+  if constexpr (PB > 1) {  // p0 + 1 < ceil(len / 64) <= MB: the block is complete
+    const int page1 = s.bt[(int64_t)n * s.MB + p0 + 1];
+    if (page1 < 0 || page1 >= c.num_pages) return;
+    hi = (const St*)c.k + ((int64_t)page1 * c.HKV + g) * kBlock * D;
+  }
   build_record<T, D, ROWS>(tile, nullptr, c.mu_sub + rec * D, c.radius_sub + rec, nullptr, nullptr, nullptr,
-                           nullptr, nullptr, 0, lane);
+                           nullptr, nullptr, 0, lane, hi);
 }
 
 template <typename T, int D>
@@ -92,15 +105,22 @@ __global__ __launch_bounds__(64) void k_append(CacheView c, SeqView s, const voi
                        c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
                      c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
   }
-  // the smaller screen block this token completes
-  if (c.sub == 2 && row % 32 == 31) {
+  // the other screen block this token completes
+  if (c.sub_rows == 32 && row % 32 == 31) {
     const int64_t srec = rec * 2 + row / 32;
     build_record<T, D, 32>((const St*)c.kw + srec * 32 * D, kn, c.mu_sub + srec * D, c.radius_sub + srec, nullptr,
                            nullptr, nullptr, nullptr, nullptr, 0, lane);
-  } else if (c.sub == 4 && row % 16 == 15) {
+  } else if (c.sub_rows == 16 && row % 16 == 15) {
     const int64_t srec = rec * 4 + row / 16;
     build_record<T, D, 16>((const St*)c.kw + srec * 16 * D, kn, c.mu_sub + srec * D, c.radius_sub + srec, nullptr,
                            nullptr, nullptr, nullptr, nullptr, 0, lane);
+  } else if (c.sub_rows == 128 && row == kBlock - 1 && (j & 1)) {
+    // a 128-token block ends with this page: its record goes with the first page
+    const int page0 = s.bt[(int64_t)n * s.MB + j - 1];
+    if (page0 < 0 || page0 >= c.num_pages) return;
+    const int64_t srec = (int64_t)page0 * c.HKV + g;
+    build_record<T, D, 128>((const St*)c.kw + srec * kBlock * D, kn, c.mu_sub + srec * D, c.radius_sub + srec,
+                            nullptr, nullptr, nullptr, nullptr, nullptr, 0, lane, (const St*)c.kw + rec * kBlock * D);
   }
 }
 
@@ -111,11 +131,14 @@ hipError_t build_impl(const CacheView& c, const SeqView& s, hipStream_t st) {
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((k_build<T, D>), dim3((unsigned)grid), dim3(256), 0, st, c, s);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || c.sub == 0) return e;
-  const int64_t sgrid = (waves * c.sub + 3) / 4;
+  if (e != hipSuccess || c.sub_rows == 0) return e;
+  const int64_t nbs = c.sub_rows > kBlock ? (s.MB + 1) / 2 : (int64_t)s.MB * (kBlock / c.sub_rows);
+  const int64_t sgrid = ((int64_t)s.N * nbs * c.HKV + 3) / 4;
   if (sgrid > 0x7fffffff) return hipErrorInvalidValue;
-  if (c.sub == 2) hipLaunchKernelGGL((k_build_sub<T, D, 32>), dim3((unsigned)sgrid), dim3(256), 0, st, c, s);
-  else hipLaunchKernelGGL((k_build_sub<T, D, 16>), dim3((unsigned)sgrid), dim3(256), 0, st, c, s);
+  const dim3 g3((unsigned)sgrid);
+  if (c.sub_rows == 32) hipLaunchKernelGGL((k_build_sub<T, D, 32>), g3, dim3(256), 0, st, c, s);
+  else if (c.sub_rows == 16) hipLaunchKernelGGL((k_build_sub<T, D, 16>), g3, dim3(256), 0, st, c, s);
+  else hipLaunchKernelGGL((k_build_sub<T, D, 128>), g3, dim3(256), 0, st, c, s);
   return hipGetLastError();
 }
 

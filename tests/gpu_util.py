@@ -39,9 +39,9 @@ class Dev:
                                if fp8 else None,
                                torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=device)
                                if fp8 else None, fp8 or "e4m3", sub_block,
-                               torch.zeros(wl.num_pages, wl.h_kv, 64 // sub_block, wl.d, dtype=torch.float16,
-                                           device=device) if sub_block else None,
-                               torch.zeros(wl.num_pages, wl.h_kv, 64 // sub_block, dtype=torch.float32,
+                               torch.zeros(wl.num_pages, wl.h_kv, max(1, 64 // sub_block), wl.d,
+                                           dtype=torch.float16, device=device) if sub_block else None,
+                               torch.zeros(wl.num_pages, wl.h_kv, max(1, 64 // sub_block), dtype=torch.float32,
                                            device=device) if sub_block else None)
         self.seq_lens = torch.from_numpy(wl.seq_lens.astype(np.int32)).to(device)
         self.bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(device)

@@ -27,15 +27,14 @@ def _bounds(wl, mu, R, sigma=None, z=2.0, boxes=None, block=64):
     G = wl.group
     s = 1.0 / math.sqrt(D)
     qf = E.upcast(wl.q, wl.kv_dtype)
-    SB = BLOCK // block
-    ub = np.full((N, HQ, wl.max_blocks * SB), np.nan)
+    ub = np.full((N, HQ, -(-wl.max_blocks * BLOCK // block)), np.nan)
     for n in range(N):
-        if SB > 1:  # records of smaller screen blocks: mu [P][HKV][SB][d]
+        if block != BLOCK:  # records of other screen blocks: mu [P][HKV][slots][d], kept with the first page
             nsub = int(wl.seq_lens[n]) // block
-            j = np.arange(nsub)
-            pg = wl.block_table[n][j // SB]
+            first = np.arange(nsub) * block
+            pg, sl = wl.block_table[n][first // BLOCK], (first % BLOCK) // block
             for h in range(HQ):
-                ub[n, h, :nsub] = E.block_bound(qf[n, h], mu[pg, h // G, j % SB], R[pg, h // G, j % SB], s)
+                ub[n, h, :nsub] = E.block_bound(qf[n, h], mu[pg, h // G, sl], R[pg, h // G, sl], s)
             continue
         nfull = int(wl.seq_lens[n]) // BLOCK
         pages = wl.block_table[n, :nfull]
@@ -103,7 +102,10 @@ def place(wl, margin: float = 1e-3, max_rounds: int = 50, summaries=None, bound:
         for (n, g, j) in bad:
             page = int(wl.block_table[n, j])
             kb = E.upcast(wl.k_pages[page, g], wl.kv_dtype)
-            if bound == "geometric_sub":
+            if bound == "geometric_sub" and blk > 64:  # a 128-token block: pages j and j + 1
+                kb2 = E.upcast(wl.k_pages[int(wl.block_table[n, j + 1]), g], wl.kv_dtype)
+                m, r = E.block_summary(np.concatenate([kb, kb2]))
+            elif bound == "geometric_sub":
                 m, r = E.block_summary(kb.reshape(64 // blk, blk, -1))
             else:
                 m, r = E.block_summary_fp8(kb, fp8) if bound == "geometric_fp8" else E.block_summary(kb)

@@ -202,8 +202,15 @@ def test_decode_ex_rejects_bad_screens():
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**dict(sub, radius_sub=None))) == \
         _lib.ETA_ERR_INVALID_ARGUMENT
     assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**sub)) == too_small
-    # the workspace for a cache with smaller-block records covers their tiles
+    for bad in (64, 48, 256, 0, -16):  # 16, 32 and 128 are the supported sizes
+        assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**dict(sub, sub_block=bad))) \
+            == _lib.ETA_ERR_INVALID_ARGUMENT, bad
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=cache(**dict(sub, sub_block=128))) == \
+        too_small
+    # the workspace for a cache with smaller-block records covers their tiles;
+    # 128-token blocks screen pages and need no more than the page screen
     assert ws_size(cache(**sub)) > ws_size(cache())
+    assert ws_size(cache(**dict(sub, sub_block=128))) == ws_size(cache())
     assert decode_ex(_lib.ETA_PHASE_SCREEN, _lib.ETA_BOUND_GEOMETRIC, 0.0) == too_small
 
 

@@ -91,3 +91,9 @@ def test_seq_512k_fp8_full():
 def test_seq_512k_subblock16_full():
     """The 512K workload with 16-token screen blocks: 8 heads."""
     _run_full("seq_512k", per_seq=8, bound="geometric_sub", block=16)
+
+
+@pytest.mark.timeout(600)
+def test_seq_512k_pairblock128_full():
+    """The 512K workload with 128-token screen blocks: 8 heads."""
+    _run_full("seq_512k", per_seq=8, bound="geometric_sub", block=128)

@@ -1,12 +1,13 @@
-"""Screens on 16- and 32-token blocks (the block-size ablation of Appendix
-F.3) on the HIP path vs the fp64 oracle, through the C ABI.
+"""Screens on 16-, 32- and 128-token blocks (the block-size ablation of
+Appendix F.3) on the HIP path vs the fp64 oracle, through the C ABI.
 
-Each smaller block has its own record (float16 centroid, float32 radius,
-same rule as the page records): centroid bits must match, radii must bound
-the oracle's from above within 1e-6. Thresholds are placed 1e-3 away from
-every block's bound, so the admitted sets (in the smaller blocks) compare
-bit-exactly, and so do the per-head counts, the union counts, the token
-counts and the rescue flags; outputs at the usual bar."""
+Each such block has its own record (float16 centroid, float32 radius, same
+rule as the page records; a 128-token block spans two block-table entries
+and its record sits with the first page): centroid bits must match, radii
+must bound the oracle's from above within 1e-6. Thresholds are placed 1e-3
+away from every block's bound, so the admitted sets (in the screen's blocks)
+compare bit-exactly, and so do the per-head counts, the union counts, the
+token counts and the rescue flags; outputs at the usual bar."""
 import numpy as np
 import pytest
 import torch
@@ -38,7 +39,7 @@ def _check_records(wl, dev, block):
     assert np.all(got[~inf] <= ref[~inf] * (1 + 1e-6))
 
 
-@pytest.mark.parametrize("block", [16, 32])
+@pytest.mark.parametrize("block", [16, 32, 128])
 @pytest.mark.parametrize("name,kw", [
     ("seq_32k", dict(seq_lens=[4096 + 17, 64 * 40 + 40], n_seqs=2)),
     ("seq_32k", dict(seq_lens=[3000, 2000], d=64, kv_dtype="f32")),
@@ -58,11 +59,18 @@ def test_subblock_records(name, kw, block):
     assert np.array_equal(dev.radius(), dev2.radius())
 
 
-@pytest.mark.parametrize("block", [16, 32])
+def _record_slots(wl, block):
+    """(page, slot) of every complete block's record, per sequence 0."""
+    T = int(wl.seq_lens[0])
+    first = np.arange(T // block) * block
+    return [(int(wl.block_table[0, f // 64]), (f % 64) // block) for f in first]
+
+
+@pytest.mark.parametrize("block", [16, 32, 128])
 def test_append_and_prefill_build_subblock_records(block):
     """Records built token by token through eta_append_kv, and by the prompt
     pass, equal the bulk build."""
-    wl = W.make_workload("seq_32k", seq_lens=[64 * 3 + 40], h_q=4, h_kv=2, d=128, needles=0)
+    wl = W.make_workload("seq_32k", seq_lens=[64 * 5 + 40], h_q=4, h_kv=2, d=128, needles=0, paged=True)
     dev = Dev(wl, sub_block=block)
     dev.build()
     torch.cuda.synchronize()
@@ -75,22 +83,31 @@ def test_append_and_prefill_build_subblock_records(block):
         vn = dev.cache.v_pages[page, :, t % 64][None].contiguous()
         eta.append_kv(cache2, lens, dev.bt, kn, vn)
     torch.cuda.synchronize()
-    sb = 64 // block
-    for j in range(T // block):
-        page = int(wl.block_table[0, j // sb])
-        assert torch.equal(cache2.mu_sub[page, :, j % sb], dev.cache.mu_sub[page, :, j % sb])
-        assert torch.equal(cache2.radius_sub[page, :, j % sb], dev.cache.radius_sub[page, :, j % sb])
-    dev3 = Dev(wl, sub_block=block)
-    q_all = W.trace_queries(wl, seed=3)
-    eta.prefill(dev3.cache, dev3.seq_lens, dev3.bt, eta.upload(q_all, wl.kv_dtype, "cuda"), eta.ETA_TAU_LEARNED,
-                torch.ones(wl.h_q, dtype=torch.float32, device="cuda"), w=dev3.w)
-    torch.cuda.synchronize()
+    slots = _record_slots(wl, block)
+    assert len(slots) >= 2
+    for page, q in slots:
+        assert torch.equal(cache2.mu_sub[page, :, q], dev.cache.mu_sub[page, :, q])
+        assert torch.equal(cache2.radius_sub[page, :, q], dev.cache.radius_sub[page, :, q])
     m1, r1 = dev.sub_records()
-    m3, r3 = dev3.sub_records()
     used = np.zeros(r1.shape, dtype=bool)
-    for j in range(T // block):
-        used[int(wl.block_table[0, j // sb]), :, j % sb] = True
-    assert np.array_equal(m3[used], m1[used]) and np.array_equal(r3[used], r1[used])
+    for page, q in slots:
+        used[page, :, q] = True
+    # the prompt pass at three group sizes (positions per workgroup 128, 32, 256)
+    for h_q, h_kv in ((4, 2), (8, 1), (2, 2)):
+        wl3 = W.make_workload("seq_32k", seq_lens=[64 * 5 + 40], h_q=h_q, h_kv=h_kv, d=128, needles=0, paged=True)
+        ref = Dev(wl3, sub_block=block)
+        ref.build()
+        dev3 = Dev(wl3, sub_block=block)
+        q_all = W.trace_queries(wl3, seed=3)
+        eta.prefill(dev3.cache, dev3.seq_lens, dev3.bt, eta.upload(q_all, wl3.kv_dtype, "cuda"),
+                    eta.ETA_TAU_LEARNED, torch.ones(wl3.h_q, dtype=torch.float32, device="cuda"), w=dev3.w)
+        torch.cuda.synchronize()
+        ma, ra = ref.sub_records()
+        m3, r3 = dev3.sub_records()
+        used3 = np.zeros(ra.shape, dtype=bool)
+        for page, q in _record_slots(wl3, block):
+            used3[page, :, q] = True
+        assert np.array_equal(m3[used3], ma[used3]) and np.array_equal(r3[used3], ra[used3]), (h_q, h_kv)
 
 
 @pytest.mark.parametrize("block,kw", [
@@ -100,6 +117,12 @@ def test_append_and_prefill_build_subblock_records(block):
     (32, dict(n_seqs=4, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
               seq_lens=[9000, 300, 64 * 12, 4097])),
     (16, dict(seq_lens=[64 * 40 + 17], h_q=32, h_kv=4, d=128, density=0.02)),
+    (128, dict(seq_lens=[64 * 70 + 3, 64 * 64, 129], h_q=8, h_kv=2, d=128, paged=True)),
+    (128, dict(seq_lens=[5000, 7000], h_q=4, h_kv=4, d=64, kv_dtype="f32", mode="calibrated")),
+    (128, dict(seq_lens=[64 * 131 + 63, 64 * 5 + 20], h_q=16, h_kv=2, d=128, lwb=2, a=0.4)),
+    (128, dict(n_seqs=4, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
+               seq_lens=[9000, 300, 64 * 12, 4097])),
+    (128, dict(seq_lens=[64 * 40 + 17, 64], h_q=32, h_kv=4, d=128, density=0.02)),
 ])
 def test_subblock_decode_parity(block, kw):
     log(f"[sub decode] b={block} {kw}")
@@ -122,11 +145,29 @@ def test_subblock_requires_records():
         dev.decode(bound="geometric_sub")
 
 
-def test_page_screen_after_subblock_decode():
-    """A page-granular decode on the same workspace after a smaller-block one
-    reads its own counts (the stats follow the last decode's block size)."""
+def test_pairblock_rescue():
+    """A head whose threshold lies above every 128-token block's bound gets the
+    block with the largest bound, both of its pages."""
+    wl, summ = prepared("seq_32k", bound="geometric_sub", block=128, seq_lens=[64 * 36, 64 * 10], h_q=8, h_kv=2,
+                        d=128, paged=True)
+    wl.bias = wl.bias.copy()
+    wl.bias[[0, 5]] = np.float32(1e3)
+    dev = Dev(wl, sub_block=128)
+    dev.build()
+    o = dev.decode(bound="geometric_sub")
+    st = dev.stats()
+    res = oracle_decode(wl, summaries=summ, bound="geometric_sub", block=128)
+    assert res.rescued[:, 0].all() and res.rescued[:, 5].all()
+    check_sets_and_counts(wl, res, st)
+    check_output(wl, res, o)
+
+
+@pytest.mark.parametrize("block", [16, 128])
+def test_page_screen_after_subblock_decode(block):
+    """A page-granular decode on the same workspace after one on other screen
+    blocks reads its own counts (the stats follow the last decode's block size)."""
     wl, summ = prepared("seq_32k", seq_lens=[64 * 30 + 5, 64 * 9], h_q=8, h_kv=2, d=128)
-    dev = Dev(wl, sub_block=16)
+    dev = Dev(wl, sub_block=block)
     dev.build()
     dev.decode(bound="geometric_sub")
     o = dev.decode()
