@@ -369,7 +369,7 @@ void k_attend(AttendArgs A) {
         for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int c = 0; c < CPL; ++c)
-            kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(kt + loff[c] + i * RPI * D)
+            kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? load_stream16(kt + loff[c] + i * RPI * D)
                                                                    : make_uint4(0, 0, 0, 0);
       }
       for (;;) {
@@ -382,7 +382,7 @@ void k_attend(AttendArgs A) {
           for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-              vr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(vt + loff[c] + i * RPI * D)
+              vr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? load_stream16(vt + loff[c] + i * RPI * D)
                                                                      : make_uint4(0, 0, 0, 0);
         }
         // next entry: from this batch, or the first of the next one
@@ -460,7 +460,7 @@ void k_attend(AttendArgs A) {
           for (int i = 0; i < NI; ++i)
 #pragma unroll
             for (int c = 0; c < CPL; ++c)
-              kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? *(const uint4*)(kt + loff[c] + i * RPI * D)
+              kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? load_stream16(kt + loff[c] + i * RPI * D)
                                                                      : make_uint4(0, 0, 0, 0);
         }
         if (tail) {  // junk rows past the end must not reach the sums (0 * NaN)

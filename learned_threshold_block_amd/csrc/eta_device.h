@@ -26,6 +26,15 @@ struct F32 {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// 16-byte load marked non-temporal (the data is read once per call, so it
+// should not displace other lines in the caches). On scattered 16 KB tiles
+// this streams measurably faster from HBM than an ordinary load.
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
 // Lane layout of a 64-row tile of D-element rows loaded with 16-byte accesses.
 // Lane (r, cb), r = lane / LPR, cb = lane % LPR, holds for load i the row
 // RPI*i + r, columns chunk(c) = c*(D/CPL) + cb*EPC .. +EPC for c < CPL. One load
