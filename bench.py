@@ -357,11 +357,28 @@ class Setup:
         self.mode = eta.ETA_TAU_LEARNED if wl.tau_mode == "learned" else eta.ETA_TAU_CALIBRATED
         eta.build_block_summaries(self.cache, self.seq_lens, self.bt)
         torch.cuda.synchronize()
+        self._rotation()
         self.nblk = np.array([wl.nblk(n) for n in range(wl.n_seqs)], dtype=np.float64)
         self.bias = torch.zeros(wl.h_q, dtype=torch.float32, device=dev)
 
+    def _rotation(self):
+        """A K/V cache small enough to stay in the 256 MB last-level cache
+        (MALL) between steps would be timed from there: keep identical copies
+        (same pages, same records) of at least 600 MB in all and let each call
+        use the next one, so every step reads cold data."""
+        import dataclasses
+        ncopy = max(1, -(-600_000_000 // self.wl.kv_bytes()))
+        c = self.cache
+        clone = lambda: dataclasses.replace(c, **{f.name: getattr(c, f.name).clone()  # noqa: E731
+                                                  for f in dataclasses.fields(c)
+                                                  if isinstance(getattr(c, f.name), self.torch.Tensor)})
+        self.caches = [c] + [clone() for _ in range(ncopy - 1)]
+        self.rot = 0
+
     def run(self, phase=None, bias=None, mode=None):
-        self.eta.decode(self.cache, self.seq_lens, self.bt, self.q, self.mode if mode is None else mode,
+        cache = self.caches[self.rot]
+        self.rot = (self.rot + 1) % len(self.caches)
+        self.eta.decode(cache, self.seq_lens, self.bt, self.q, self.mode if mode is None else mode,
                         self.bias if bias is None else bias, w=self.w, a=self.wl.a, beta=self.wl.beta,
                         lwb=self.wl.lwb, out=self.out, workspace=self.ws, phase=phase, bound=self.bound, z=self.z)
 
@@ -396,6 +413,9 @@ class Setup:
         return self.sub_block if self.bound == "geometric_sub" else 64
 
     def densities(self):
+        """Per-head and union admitted fractions of the current thresholds
+        (one decode first, so the counts are those of this setup)."""
+        self.run()
         st = self.stats()
         b = self.block_tokens()
         nb = np.array([-(-int(T) // b) for T in self.wl.seq_lens], dtype=np.float64)
@@ -416,6 +436,7 @@ class Setup:
         self.ws = eta.alloc_workspace(self.cache, wl.n_seqs, wl.max_blocks, wl.h_q)
         eta.build_block_summaries(self.cache, self.seq_lens, self.bt)
         torch.cuda.synchronize()
+        self._rotation()
 
     def step_bytes(self, st):
         """Bytes one step must move: admitted K/V tiles once per union block,
@@ -579,6 +600,7 @@ def main():
             "seq_lens_total": int(wl.seq_lens.sum()),
             "density_per_head": round(dens_head, 4),
             "density_union": round(dens_union, 4),
+            "kv_copies_rotated": len(S.caches),
         },
         "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
         "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),

@@ -20,7 +20,7 @@ namespace eta {
 namespace {
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_build(CacheView c, SeqView s) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_build(CacheView c, SeqView s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over N * MB * HKV
   const int64_t total = (int64_t)s.N * s.MB * c.HKV;
