@@ -36,6 +36,38 @@ __device__ __forceinline__ double group_sum_f64(double v) {
   return v;
 }
 
+// A lane's EPL record values (EPC contiguous columns per chunk) stored with
+// one access per chunk: 16 or 8 bytes of float16 bits, 8 or 4 bytes of FP8
+// codes (partial-line stores of single elements cost a full write each).
+template <int EPC, int CPL, int D>
+__device__ __forceinline__ void store_u16(uint16_t* out, const uint16_t* v, int cb) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    uint16_t* p = out + c * (D / CPL) + cb * EPC;
+    const uint16_t* w = v + c * EPC;
+    if constexpr (EPC == 8) {
+      *(uint4*)p = make_uint4(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16, w[4] | (uint32_t)w[5] << 16,
+                              w[6] | (uint32_t)w[7] << 16);
+    } else {
+      *(uint2*)p = make_uint2(w[0] | (uint32_t)w[1] << 16, w[2] | (uint32_t)w[3] << 16);
+    }
+  }
+}
+template <int EPC, int CPL, int D>
+__device__ __forceinline__ void store_u8(uint8_t* out, const uint8_t* v, int cb) {
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    uint8_t* p = out + c * (D / CPL) + cb * EPC;
+    const uint8_t* w = v + c * EPC;
+    const uint32_t lo = w[0] | (uint32_t)w[1] << 8 | (uint32_t)w[2] << 16 | (uint32_t)w[3] << 24;
+    if constexpr (EPC == 8) {
+      *(uint2*)p = make_uint2(lo, w[4] | (uint32_t)w[5] << 8 | (uint32_t)w[6] << 16 | (uint32_t)w[7] << 24);
+    } else {
+      *(uint32_t*)p = lo;
+    }
+  }
+}
+
 // Element e (0 .. EPL-1) of a lane's row in the 16-byte-load layout: chunk
 // e / EPC of the row, element e % EPC of that chunk.
 template <typename T, int EPC>
@@ -147,30 +179,33 @@ __device__ __forceinline__ void build_record(const typename T::Stored* tile, con
   const bool all_ok = __all(ok);
   const bool all_finite = __all(finite);
   const bool writer = r == 0;  // one lane per column group stores
-  const auto col_of = [&](int e) { return L::col(e / EPC, cb) + e % EPC; };
   float mu8[EPL];  // FP8 centroid values (exact in float32)
   if (mu8_out) {
+    uint8_t b8[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      const uint8_t b = all_finite ? f64_to_fp8(sum[e] * (1.0 / ROWS), fmt8) : (uint8_t)0;
-      mu8[e] = fp8_to_f32(b, fmt8);
-      if (writer) mu8_out[col_of(e)] = b;
+      b8[e] = all_finite ? f64_to_fp8(sum[e] * (1.0 / ROWS), fmt8) : (uint8_t)0;
+      mu8[e] = fp8_to_f32(b8[e], fmt8);
     }
+    if (writer) store_u8<EPC, CPL, D>(mu8_out, b8, cb);
   }
   if (kmin_out && writer) {
+    uint16_t lo[EPL], hi[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
-      kmin_out[col_of(e)] = all_finite ? f32_to_f16_dir(cmin[e], false) : (uint16_t)0x7e00u;
-      kmax_out[col_of(e)] = all_finite ? f32_to_f16_dir(cmax[e], true) : (uint16_t)0x7e00u;
+      lo[e] = all_finite ? f32_to_f16_dir(cmin[e], false) : (uint16_t)0x7e00u;
+      hi[e] = all_finite ? f32_to_f16_dir(cmax[e], true) : (uint16_t)0x7e00u;
     }
+    store_u16<EPC, CPL, D>(kmin_out, lo, cb);
+    store_u16<EPC, CPL, D>(kmax_out, hi, cb);
   }
   float mu[EPL];  // stored centroid values (exact in float32)
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     if (!all_ok) h[e] = 0;
     mu[e] = f16_bits_to_f32(h[e]);
-    if (writer) mu_out[col_of(e)] = h[e];
   }
+  if (writer) store_u16<EPC, CPL, D>(mu_out, h, cb);
 
   // ---- pass 2: squared distances per row and their maximum (the radius);
   // then, only if asked for, the same about the FP8 centroid and the
@@ -241,11 +276,13 @@ __device__ __forceinline__ void build_record(const typename T::Stored* tile, con
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dev2[e] += __shfl_xor(dev2[e], m, 64);
     if (writer) {
+      uint16_t sg[EPL];
 #pragma unroll
       for (int e = 0; e < EPL; ++e) {
         const double sd = sqrt(dev2[e] * (1.0 / ROWS));
-        sig_out[col_of(e)] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
+        sg[e] = (sd < 1e300) ? f64_to_f16_rne(sd) : (uint16_t)0x7c00u;
       }
+      store_u16<EPC, CPL, D>(sig_out, sg, cb);
     }
   }
   const bool any_bad = !all_finite;
