@@ -43,6 +43,7 @@ def _check_records(wl, dev, block):
 @pytest.mark.parametrize("name,kw", [
     ("seq_32k", dict(seq_lens=[4096 + 17, 64 * 40 + 40], n_seqs=2)),
     ("seq_32k", dict(seq_lens=[3000, 2000], d=64, kv_dtype="f32")),
+    ("seq_32k", dict(seq_lens=[2000, 700], d=128, kv_dtype="f32")),
     ("ragged_16", dict(n_seqs=3, seq_lens=[300, 4097, 640], h_q=8, h_kv=2, d=128)),
 ])
 def test_subblock_records(name, kw, block):
