@@ -19,8 +19,12 @@
 namespace eta {
 namespace {
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_build(CacheView c, SeqView s) {
+// One wavefront per (sequence, complete block, KV head). OPT: the cache
+// carries optional records (deviation, key box or FP8); without them the
+// record needs about half the registers, so that kernel runs four wavefronts
+// per SIMD instead of two.
+template <typename T, int D, bool OPT>
+__device__ __forceinline__ void build_one(const CacheView& c, const SeqView& s) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int64_t idx = (int64_t)blockIdx.x * 4 + wave;  // over N * MB * HKV
   const int64_t total = (int64_t)s.N * s.MB * c.HKV;
@@ -36,9 +40,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (page < 0 || page >= c.num_pages) return;
   const int64_t rec = (int64_t)page * c.HKV + g;
   const auto* tile = (const typename T::Stored*)c.k + rec * kBlock * D;
-  build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
-                     c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
-                     c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
+  if constexpr (OPT)
+    build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, c.sigma ? c.sigma + rec * D : nullptr,
+                       c.kmin ? c.kmin + rec * D : nullptr, c.kmax ? c.kmax + rec * D : nullptr,
+                       c.mu8 ? c.mu8 + rec * D : nullptr, c.mu8 ? c.radius8 + rec : nullptr, c.mu8_fmt, lane);
+  else
+    build_record<T, D>(tile, nullptr, c.mu + rec * D, c.radius + rec, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       0, lane);
+}
+
+// wavefronts per SIMD of the lean kernel: four unless a row is 512 bytes
+// (float32 at d = 128: the kept rows alone take 128 registers)
+template <typename T, int D>
+constexpr int build_waves() {
+  return T::kBytes * D <= 256 ? 4 : 2;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(build_waves<T, D>(), build_waves<T, D>())))
+void k_build(CacheView c, SeqView s) {
+  build_one<T, D, false>(c, s);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_build_all(CacheView c, SeqView s) {
+  build_one<T, D, true>(c, s);
 }
 
 // Records of the other screen blocks (ROWS = 16, 32 or 128 tokens): one
@@ -129,7 +155,8 @@ hipError_t build_impl(const CacheView& c, const SeqView& s, hipStream_t st) {
   const int64_t waves = (int64_t)s.N * s.MB * c.HKV;
   const int64_t grid = (waves + 3) / 4;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_build<T, D>), dim3((unsigned)grid), dim3(256), 0, st, c, s);
+  if (c.sigma || c.kmin || c.mu8) hipLaunchKernelGGL((k_build_all<T, D>), dim3((unsigned)grid), dim3(256), 0, st, c, s);
+  else hipLaunchKernelGGL((k_build<T, D>), dim3((unsigned)grid), dim3(256), 0, st, c, s);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || c.sub_rows == 0) return e;
   const int64_t nbs = c.sub_rows > kBlock ? (s.MB + 1) / 2 : (int64_t)s.MB * (kBlock / c.sub_rows);
