@@ -82,6 +82,50 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   const St* kbase = (const St*)A.c.k;
   const int tok = RPI * cb + r;  // key (within the tile) whose score this lane finishes
 
+  // the learned threshold w_h . q_t + b_h of each of the wavefront's rows, once
+  // (every row of lanes holds all D columns, so every lane has the same sum)
+  __shared__ float s_tau[4][16][kMaxGroup];
+  if (learned) {
+    for (int i = 0; i < 16; ++i) {
+      const int t = qt * kBlock + wave * 16 + i;
+      if (t >= len) break;
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const St* qrow = (const St*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G + h) * D;
+        const float* wr = A.w + (int64_t)(g * G + h) * D;
+        float pw = 0.f;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+          const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+          const uint32_t qw[4] = {v.x, v.y, v.z, v.w};
+          const float4 w0 = *(const float4*)(wr + L::col(c, cb));
+          const float4 w1 = EPL / CPL > 4 ? *(const float4*)(wr + L::col(c, cb) + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+          float qv[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if constexpr (kBf16) {
+              qv[2 * e] = bf16_lo(qw[e]);
+              qv[2 * e + 1] = bf16_hi(qw[e]);
+            } else {
+              qv[e] = __uint_as_float(qw[e]);
+              qv[4 + e] = 0.f;
+            }
+          }
+          pw = fmaf(w0.x, qv[0], pw); pw = fmaf(w0.y, qv[1], pw);
+          pw = fmaf(w0.z, qv[2], pw); pw = fmaf(w0.w, qv[3], pw);
+          if constexpr (kBf16) {
+            pw = fmaf(w1.x, qv[4], pw); pw = fmaf(w1.y, qv[5], pw);
+            pw = fmaf(w1.z, qv[6], pw); pw = fmaf(w1.w, qv[7], pw);
+          }
+        }
+        const float tau = group_sum<LPR>(pw) + A.b[g * G + h];
+        if (lane == 0) s_tau[wave][i][h] = tau;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  }
+
   for (int j = 0; j <= qt; ++j) {
     const int page = A.s.bt[(int64_t)n * MB + j];
     if (page < 0 || page >= A.c.num_pages) {
@@ -135,34 +179,7 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
           const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
           atomicAdd(&lhist[h * B + bin], wt);
         }
-        if (learned) {  // this row's learned threshold w_h . q_t + b_h
-          float pw = 0.f;
-          const float* wr = A.w + (int64_t)(g * G + h) * D;
-#pragma unroll
-          for (int c = 0; c < CPL; ++c) {
-            const float4 w0 = *(const float4*)(wr + L::col(c, cb));
-            const float4 w1 = EPL / CPL > 4 ? *(const float4*)(wr + L::col(c, cb) + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-            float qv[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              if constexpr (kBf16) {
-                qv[2 * e] = bf16_lo(qw[c * 4 + e]);
-                qv[2 * e + 1] = bf16_hi(qw[c * 4 + e]);
-              } else {
-                qv[e] = __uint_as_float(qw[c * 4 + e]);
-                qv[4 + e] = 0.f;
-              }
-            }
-            pw = fmaf(w0.x, qv[0], pw); pw = fmaf(w0.y, qv[1], pw);
-            pw = fmaf(w0.z, qv[2], pw); pw = fmaf(w0.w, qv[3], pw);
-            if constexpr (kBf16) {
-              pw = fmaf(w1.x, qv[4], pw); pw = fmaf(w1.y, qv[5], pw);
-              pw = fmaf(w1.z, qv[6], pw); pw = fmaf(w1.w, qv[7], pw);
-            }
-          }
-          const float tau = group_sum<LPR>(pw) + A.b[g * G + h];
-          if (valid && S >= tau) abv[h] += wt;
-        }
+        if (learned && valid && S >= s_tau[wave][i][h]) abv[h] += wt;
         if (j == qt && lane == 0) tot[h] += wt * (unsigned long long)(t + 1);
       }
     }
