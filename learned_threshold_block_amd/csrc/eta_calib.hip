@@ -13,12 +13,12 @@
 //     w_h . q_t + b_h (the head's training density), or floor(rho_h * total);
 //   * c_h = the lowest bin edge whose weighted tail does not exceed the target.
 //
-// k_calib_hist: one workgroup per (sequence, KV head, tile of 64 query
-//   positions); the four wavefronts take 16 queries each and walk the key tiles
-//   up to the diagonal. Scores come from the same tile layout and transposing
-//   DPP reduction as the decode; each lane bins the score of one key into a
-//   per-workgroup LDS histogram with 64-bit integer atomics, which is added to
-//   the global one at the end (non-empty bins only).
+// k_calib_mfma (bfloat16) and k_calib_hist (float32): one workgroup per
+//   (sequence, KV head, tile of 64 query positions) walking the key tiles up to
+//   the diagonal; scores on the matrix cores (bfloat16) or from the decode's
+//   tile layout and transposing DPP reduction (float32); each lane bins its
+//   scores into a per-workgroup LDS histogram with 64-bit integer atomics,
+//   which is added to the global one at the end (non-empty bins only).
 // k_calib_search: one wavefront per query head: suffix sums of the histogram
 //   and the count of edges whose tail exceeds the target.
 #include "eta_device.h"
@@ -54,6 +54,56 @@ __global__ void k_calib_zero(CalibArgs A) {
   if (i == 0) A.err[0] = 0;
 }
 
+// The learned threshold w_h . q_t + b_h of rows t0 + 16 wave .. + 15 (those
+// below len) for every head of the group, into s_tau[t - t0][h]. Lanes in the
+// tile layout: every row of lanes holds all D columns, so every lane has the
+// same sum and lane 0 stores it.
+template <typename T, int D, int G>
+__device__ __forceinline__ void row_thresholds(const CalibArgs& A, int n, int g, int t0, int len, int wave, int lane,
+                                               float (*s_tau)[kMaxGroup]) {
+  using L = TileLayout<T::kBytes, D>;
+  constexpr int LPR = L::LPR, CPL = L::CPL, EPL = L::EPL;
+  constexpr bool kBf16 = T::kBytes == 2;
+  using St = typename T::Stored;
+  const int cb = lane % LPR;
+  for (int i = 0; i < 16; ++i) {
+    const int t = t0 + wave * 16 + i;
+    if (t >= len) break;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const St* qrow = (const St*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G + h) * D;
+      const float* wr = A.w + (int64_t)(g * G + h) * D;
+      float pw = 0.f;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+        const uint32_t qw[4] = {v.x, v.y, v.z, v.w};
+        const float4 w0 = *(const float4*)(wr + L::col(c, cb));
+        const float4 w1 = EPL / CPL > 4 ? *(const float4*)(wr + L::col(c, cb) + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        float qv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if constexpr (kBf16) {
+            qv[2 * e] = bf16_lo(qw[e]);
+            qv[2 * e + 1] = bf16_hi(qw[e]);
+          } else {
+            qv[e] = __uint_as_float(qw[e]);
+            qv[4 + e] = 0.f;
+          }
+        }
+        pw = fmaf(w0.x, qv[0], pw); pw = fmaf(w0.y, qv[1], pw);
+        pw = fmaf(w0.z, qv[2], pw); pw = fmaf(w0.w, qv[3], pw);
+        if constexpr (kBf16) {
+          pw = fmaf(w1.x, qv[4], pw); pw = fmaf(w1.y, qv[5], pw);
+          pw = fmaf(w1.z, qv[6], pw); pw = fmaf(w1.w, qv[7], pw);
+        }
+      }
+      const float tau = group_sum<LPR>(pw) + A.b[g * G + h];
+      if (lane == 0) s_tau[wave * 16 + i][h] = tau;
+    }
+  }
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   using L = TileLayout<T::kBytes, D>;
@@ -83,45 +133,9 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   const int tok = RPI * cb + r;  // key (within the tile) whose score this lane finishes
 
   // the learned threshold w_h . q_t + b_h of each of the wavefront's rows, once
-  // (every row of lanes holds all D columns, so every lane has the same sum)
-  __shared__ float s_tau[4][16][kMaxGroup];
+  __shared__ float s_tau[kBlock][kMaxGroup];
   if (learned) {
-    for (int i = 0; i < 16; ++i) {
-      const int t = qt * kBlock + wave * 16 + i;
-      if (t >= len) break;
-#pragma unroll
-      for (int h = 0; h < G; ++h) {
-        const St* qrow = (const St*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G + h) * D;
-        const float* wr = A.w + (int64_t)(g * G + h) * D;
-        float pw = 0.f;
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-          const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
-          const uint32_t qw[4] = {v.x, v.y, v.z, v.w};
-          const float4 w0 = *(const float4*)(wr + L::col(c, cb));
-          const float4 w1 = EPL / CPL > 4 ? *(const float4*)(wr + L::col(c, cb) + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
-          float qv[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if constexpr (kBf16) {
-              qv[2 * e] = bf16_lo(qw[e]);
-              qv[2 * e + 1] = bf16_hi(qw[e]);
-            } else {
-              qv[e] = __uint_as_float(qw[e]);
-              qv[4 + e] = 0.f;
-            }
-          }
-          pw = fmaf(w0.x, qv[0], pw); pw = fmaf(w0.y, qv[1], pw);
-          pw = fmaf(w0.z, qv[2], pw); pw = fmaf(w0.w, qv[3], pw);
-          if constexpr (kBf16) {
-            pw = fmaf(w1.x, qv[4], pw); pw = fmaf(w1.y, qv[5], pw);
-            pw = fmaf(w1.z, qv[6], pw); pw = fmaf(w1.w, qv[7], pw);
-          }
-        }
-        const float tau = group_sum<LPR>(pw) + A.b[g * G + h];
-        if (lane == 0) s_tau[wave][i][h] = tau;
-      }
-    }
+    row_thresholds<T, D, G>(A, n, g, qt * kBlock, len, wave, lane, s_tau);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
@@ -179,7 +193,7 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
           const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
           atomicAdd(&lhist[h * B + bin], wt);
         }
-        if (learned && valid && S >= s_tau[wave][i][h]) abv[h] += wt;
+        if (learned && valid && S >= s_tau[wave * 16 + i][h]) abv[h] += wt;
         if (j == qt && lane == 0) tot[h] += wt * (unsigned long long)(t + 1);
       }
     }
@@ -194,6 +208,100 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
       if (learned && a) atomicAdd(&A.above[g * G + h], a);
       if (tot[h]) atomicAdd(&A.total[g * G + h], tot[h]);
     }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * B; i += 256) {
+    const unsigned long long v = lhist[i];
+    if (v) atomicAdd(&A.hist[(int64_t)(g * G) * B + i], v);
+  }
+}
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// bfloat16 caches: the same histogram with the scores of each 64-query x
+// 64-key tile pair on the matrix cores. Wavefront w takes the quadrant (query
+// half w >> 1, key half w & 1) for every head of the group: S^T = K Q^T on
+// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims, B = 32 queries x 16 dims,
+// both loaded straight from memory as 16-byte rows), so lane l holds query
+// l % 32 of its half and, in element 4 i + j, key 8 i + 4 (l / 32) + j of its
+// half. Rows past the sequence end and keys after the query are skipped.
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_calib_mfma(CalibArgs A) {
+  constexpr int KS = D / 16;  // 16-dim steps
+  extern __shared__ unsigned long long lhist[];  // [G][B]
+  __shared__ float s_tau[kBlock][kMaxGroup];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int HKV = A.c.HKV, MB = A.s.MB, B = A.B;
+  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
+  const int qt = blockIdx.x;
+  const int len = A.s.lens[n];
+  if (len < 1 || len > kBlock * MB || qt * kBlock >= len) return;
+  for (int i = threadIdx.x; i < G * B; i += 256) lhist[i] = 0ull;
+  const bool learned = A.w != nullptr;
+  if (learned) row_thresholds<Bf16, D, G>(A, n, g, qt * kBlock, len, wave, lane, s_tau);
+  // row totals: row t has t + 1 keys of weight floor(2^31 / (t + 1)), the same for every head
+  if (wave == 0) {
+    const int t = qt * kBlock + lane;
+    unsigned long long tw = t < len ? (unsigned long long)((1u << 31) / (unsigned)(t + 1)) * (unsigned)(t + 1) : 0ull;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) tw += __shfl_xor(tw, m, 64);
+    if (lane < G) atomicAdd(&A.total[g * G + lane], tw);
+  }
+  __syncthreads();
+
+  const int qh = wave >> 1, kh = wave & 1, nq = lane & 31, hi = lane >> 5;
+  const int t = qt * kBlock + 32 * qh + nq;  // this lane's query (below 64 MB = Lq)
+  const bool t_ok = t < len;
+  const unsigned long long wt = t_ok ? (unsigned long long)((1u << 31) / (unsigned)(t + 1)) : 0ull;
+  const float scale = 1.0f / sqrtf((float)D);
+  float tau[G];
+  unsigned long long abv[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    tau[h] = learned ? s_tau[32 * qh + nq][h] : 0.f;
+    abv[h] = 0ull;
+  }
+  const uint16_t* qrow0 = (const uint16_t*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G) * D + 8 * hi;
+  for (int j = 0; j <= qt; ++j) {
+    const int page = A.s.bt[(int64_t)n * MB + j];
+    if (page < 0 || page >= A.c.num_pages) {
+      if (threadIdx.x == 0) A.err[0] = 1;
+      continue;
+    }
+    const uint16_t* krow = (const uint16_t*)A.c.k + (((int64_t)page * HKV + g) * kBlock + 32 * kh + nq) * D + 8 * hi;
+    uint4 ka[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const uint4*)(krow + 16 * ks);
+    const int s0 = j * kBlock + 32 * kh + 4 * hi;  // key of element 0
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      f32x16_t acc = {};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 qb = *(const uint4*)(qrow0 + h * D + 16 * ks);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                      __builtin_bit_cast(bf16x8_t, qb), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int sk = s0 + 8 * (e >> 2) + (e & 3);
+        if (t_ok && sk <= t) {
+          const float S = acc[e] * scale;
+          const float x = floorf((S - A.lo) * A.bscale);
+          const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
+          atomicAdd(&lhist[h * B + bin], wt);
+          if (learned && S >= tau[h]) abv[h] += wt;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    unsigned long long a = abv[h];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+    if (lane == 0 && learned && a) atomicAdd(&A.above[g * G + h], a);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < G * B; i += 256) {
@@ -239,8 +347,9 @@ __global__ __launch_bounds__(64) void k_calib_search(CalibArgs A) {
 
 template <typename T, int D, int G>
 hipError_t calib_impl(const CalibArgs& a, int N, int MB, hipStream_t st) {
-  hipLaunchKernelGGL((k_calib_hist<T, D, G>), dim3(MB, N * a.c.HKV), dim3(256),
-                     (size_t)G * a.B * sizeof(unsigned long long), st, a);
+  const size_t lds = (size_t)G * a.B * sizeof(unsigned long long);
+  if constexpr (T::kBytes == 2) hipLaunchKernelGGL((k_calib_mfma<D, G>), dim3(MB, N * a.c.HKV), dim3(256), lds, st, a);
+  else hipLaunchKernelGGL((k_calib_hist<T, D, G>), dim3(MB, N * a.c.HKV), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
