@@ -76,6 +76,9 @@ def _check_head(got_hist, got_above, got_total, got_c, ref, amb_bin, amb_tau, lo
     (dict(seq_lens=[1000, 700], h_q=8, h_kv=2, d=128), True),
     (dict(seq_lens=[900, 64 * 5], h_q=4, h_kv=4, d=64, kv_dtype="f32"), False),
     (dict(seq_lens=[777], h_q=16, h_kv=2, d=128), True),
+    (dict(seq_lens=[900, 64 * 5], h_q=4, h_kv=4, d=64), False),
+    (dict(seq_lens=[500, 130], h_q=4, h_kv=2, d=64), True),
+    (dict(seq_lens=[1000, 64], h_q=2, h_kv=1, d=128, paged=True), False),
 ])
 def test_calibration_parity(kw, learned):
     wl = W.make_workload("seq_32k", needles=0, **kw)
