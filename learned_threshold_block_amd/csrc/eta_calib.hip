@@ -104,6 +104,18 @@ __device__ __forceinline__ void row_thresholds(const CalibArgs& A, int n, int g,
   }
 }
 
+// Row totals of the tile's rows t0 .. t0 + 63 below len (one wavefront): row t
+// has t + 1 keys of weight floor(2^31 / (t + 1)), the same for every head of
+// the group; independent of the keys, so a skipped key tile leaves them whole.
+template <int G>
+__device__ __forceinline__ void row_totals(const CalibArgs& A, int g, int t0, int len, int lane) {
+  const int t = t0 + lane;
+  unsigned long long tw = t < len ? (unsigned long long)((1u << 31) / (unsigned)(t + 1)) * (unsigned)(t + 1) : 0ull;
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) tw += __shfl_xor(tw, m, 64);
+  if (lane < G) atomicAdd(&A.total[g * G + lane], tw);
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   using L = TileLayout<T::kBytes, D>;
@@ -123,9 +135,9 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
 
   const float scale = 1.0f / sqrtf((float)D);
   const bool learned = A.w != nullptr;
-  unsigned long long abv[G], tot[G];
+  unsigned long long abv[G];
 #pragma unroll
-  for (int h = 0; h < G; ++h) abv[h] = tot[h] = 0ull;
+  for (int h = 0; h < G; ++h) abv[h] = 0ull;
   int loff[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) loff[c] = r * D + L::col(c, cb);
@@ -139,6 +151,7 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     __builtin_amdgcn_wave_barrier();
   }
+  if (wave == 0) row_totals<G>(A, g, qt * kBlock, len, lane);
 
   for (int j = 0; j <= qt; ++j) {
     const int page = A.s.bt[(int64_t)n * MB + j];
@@ -194,7 +207,6 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
           atomicAdd(&lhist[h * B + bin], wt);
         }
         if (learned && valid && S >= s_tau[wave * 16 + i][h]) abv[h] += wt;
-        if (j == qt && lane == 0) tot[h] += wt * (unsigned long long)(t + 1);
       }
     }
   }
@@ -204,10 +216,7 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
     unsigned long long a = abv[h];
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-    if (lane == 0) {
-      if (learned && a) atomicAdd(&A.above[g * G + h], a);
-      if (tot[h]) atomicAdd(&A.total[g * G + h], tot[h]);
-    }
+    if (lane == 0 && learned && a) atomicAdd(&A.above[g * G + h], a);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < G * B; i += 256) {
@@ -240,14 +249,7 @@ __global__ __launch_bounds__(256) void k_calib_mfma(CalibArgs A) {
   for (int i = threadIdx.x; i < G * B; i += 256) lhist[i] = 0ull;
   const bool learned = A.w != nullptr;
   if (learned) row_thresholds<Bf16, D, G>(A, n, g, qt * kBlock, len, wave, lane, s_tau);
-  // row totals: row t has t + 1 keys of weight floor(2^31 / (t + 1)), the same for every head
-  if (wave == 0) {
-    const int t = qt * kBlock + lane;
-    unsigned long long tw = t < len ? (unsigned long long)((1u << 31) / (unsigned)(t + 1)) * (unsigned)(t + 1) : 0ull;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) tw += __shfl_xor(tw, m, 64);
-    if (lane < G) atomicAdd(&A.total[g * G + lane], tw);
-  }
+  if (wave == 0) row_totals<G>(A, g, qt * kBlock, len, lane);
   __syncthreads();
 
   const int qh = wave >> 1, kh = wave & 1, nq = lane & 31, hi = lane >> 5;

@@ -130,3 +130,23 @@ def test_calibrated_constant_reproduces_density():
         dens = hist[h, b:].sum() / total[h]
         below = hist[h, b - 1:].sum() / total[h]
         assert dens <= rho[h] < below + 1e-12, (h, dens, rho[h], below)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_out_of_range_page_is_reported(kv_dtype):
+    """A block-table entry past the cache sets the error flag; that key tile is
+    skipped and nothing else is disturbed (the row totals do not depend on it)."""
+    wl = W.make_workload("seq_32k", seq_lens=[64 * 6 + 9], h_q=4, h_kv=2, d=128, needles=0, kv_dtype=kv_dtype)
+    q_all = W.trace_queries(wl, seed=4)
+    dev = Dev(wl)
+    bt = dev.bt.clone()
+    bt[0, 2] = wl.num_pages  # one past the last page
+    cal = eta.calibrate(dev.cache, dev.seq_lens, bt, eta.upload(q_all, wl.kv_dtype, "cuda"), 256, -8.0, 8.0,
+                        rho=torch.full((wl.h_q,), 0.3, device="cuda"))
+    torch.cuda.synchronize()
+    assert int(cal.err.item()) == 1
+    T = int(wl.seq_lens[0])
+    want = sum(E.row_weight(t) * (t + 1) for t in range(T))
+    assert all(int(x) == want for x in cal.total.cpu().numpy())
+    # the skipped tile's scores are missing from the histogram: less weight than the full triangle
+    assert all(int(x) < want for x in cal.hist.cpu().numpy().sum(axis=1))
