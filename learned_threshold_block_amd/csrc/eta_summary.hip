@@ -1,5 +1,5 @@
 // Block records: centroid mu^ (float16, nearest even) and radius R^ (float32,
-// rounded up) of every complete 64-token key block, per KV head.
+// rounded up) of every complete key block, per KV head.
 //
 // "Elastic Threshold Attention" (paperpeel.com/paper/2609.20888), Section 3.2
 // and Appendix F.1: the decode screen reads one compact record per block and KV
@@ -12,8 +12,11 @@
 // 2^-40 relative margin that covers the float64 summation error. With a
 // deviation buffer, the coordinate standard deviation (population, about the
 // float64 mean; Section F.1) is rounded once to float16. One wavefront builds
-// one record; lanes own columns. The same device function serves the bulk
-// builder and the append path, so both give identical bits.
+// one record from the block's keys read once in the 16-byte tile layout
+// (build_record). The same device function serves the bulk builders, the
+// append path and the prompt pass, so all give identical bits. Records of
+// 16-, 32- and 128-token screen blocks (Appendix F.3's block size) follow the
+// same rule over their keys.
 #include "eta_records.h"
 
 namespace eta {
