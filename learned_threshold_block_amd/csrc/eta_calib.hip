@@ -265,37 +265,87 @@ __global__ __launch_bounds__(256) void k_calib_mfma(CalibArgs A) {
     abv[h] = 0ull;
   }
   const uint16_t* qrow0 = (const uint16_t*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G) * D + 8 * hi;
-  for (int j = 0; j <= qt; ++j) {
-    const int page = A.s.bt[(int64_t)n * MB + j];
-    if (page < 0 || page >= A.c.num_pages) {
-      if (threadIdx.x == 0) A.err[0] = 1;
-      continue;
+  // the B operands (this lane's query, 16-byte rows of 8 dims) of up to four
+  // heads stay in registers for a whole pass over the key tiles; eight heads
+  // take two passes. The key tiles go through a double-buffered LDS area
+  // (rows padded by 16 bytes): the workgroup loads tile j + 1 with 16-byte
+  // loads of whole rows while tile j is scored.
+  constexpr int HB = G < 4 ? G : 4;
+  constexpr int KSTR = D + 8;            // LDS row stride (elements)
+  constexpr int CPT = kBlock * D / 8 / 256;  // 16-byte chunks per thread per tile
+  __shared__ __attribute__((aligned(16))) uint16_t klds[2][kBlock * KSTR];
+  const int tid = threadIdx.x;
+  const auto tile_ok = [&](int jj) {
+    const int page = A.s.bt[(int64_t)n * MB + jj];
+    return page >= 0 && page < A.c.num_pages ? page : -1;
+  };
+  const auto load_tile = [&](int page, uint4 (&rg)[CPT]) {
+    const uint16_t* kt = (const uint16_t*)A.c.k + ((int64_t)page * HKV + g) * (kBlock * D);
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + 256 * c, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      rg[c] = page >= 0 ? *(const uint4*)(kt + row * D + col) : make_uint4(0, 0, 0, 0);
     }
-    const uint16_t* krow = (const uint16_t*)A.c.k + (((int64_t)page * HKV + g) * kBlock + 32 * kh + nq) * D + 8 * hi;
-    uint4 ka[KS];
+  };
+  const auto store_tile = [&](const uint4 (&rg)[CPT], int buf) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const uint4*)(krow + 16 * ks);
-    const int s0 = j * kBlock + 32 * kh + 4 * hi;  // key of element 0
+    for (int c = 0; c < CPT; ++c) {
+      const int ch = tid + 256 * c, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
+      *(uint4*)(&klds[buf][row * KSTR + col]) = rg[c];
+    }
+  };
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      f32x16_t acc = {};
+  for (int hb = 0; hb < G; hb += HB) {
+    uint4 qr[HB][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 qb = *(const uint4*)(qrow0 + h * D + 16 * ks);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                      __builtin_bit_cast(bf16x8_t, qb), acc, 0, 0, 0);
+    for (int hh = 0; hh < HB; ++hh)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qr[hh][ks] = *(const uint4*)(qrow0 + (hb + hh) * D + 16 * ks);
+    int page = tile_ok(0);
+    {
+      uint4 rg[CPT];
+      load_tile(page, rg);
+      store_tile(rg, 0);
+    }
+    __syncthreads();
+    for (int j = 0; j <= qt; ++j) {
+      const bool cur_ok = page >= 0;
+      if (!cur_ok && tid == 0) A.err[0] = 1;
+      uint4 rg[CPT];
+      const bool has_next = j < qt;
+      if (has_next) {
+        page = tile_ok(j + 1);
+        load_tile(page, rg);
       }
+      if (cur_ok) {
+        const uint16_t* krow = &klds[j & 1][(32 * kh + nq) * KSTR + 8 * hi];
+        uint4 ka[KS];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int sk = s0 + 8 * (e >> 2) + (e & 3);
-        if (t_ok && sk <= t) {
-          const float S = acc[e] * scale;
-          const float x = floorf((S - A.lo) * A.bscale);
-          const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
-          atomicAdd(&lhist[h * B + bin], wt);
-          if (learned && S >= tau[h]) abv[h] += wt;
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const uint4*)(krow + 16 * ks);
+        const int s0 = j * kBlock + 32 * kh + 4 * hi;  // key of element 0
+#pragma unroll
+        for (int hh = 0; hh < HB; ++hh) {
+          const int h = hb + hh;
+          f32x16_t acc = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                          __builtin_bit_cast(bf16x8_t, qr[hh][ks]), acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int sk = s0 + 8 * (e >> 2) + (e & 3);
+            if (t_ok && sk <= t) {
+              const float S = acc[e] * scale;
+              const float x = floorf((S - A.lo) * A.bscale);
+              const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
+              atomicAdd(&lhist[h * B + bin], wt);
+              if (learned && S >= tau[h]) abv[h] += wt;
+            }
+          }
         }
       }
+      if (has_next) store_tile(rg, (j + 1) & 1);
+      __syncthreads();
     }
   }
 #pragma unroll
