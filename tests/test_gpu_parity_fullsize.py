@@ -28,9 +28,9 @@ def _sample_heads(wl, per_seq, seed):
     return heads
 
 
-def _run_full(name, per_seq, seed=7, bound="geometric", fp8="e4m3", block=64):
+def _run_full(name, per_seq, seed=7, bound="geometric", fp8="e4m3", block=64, **kw):
     log(f"[full-size] {name} ({bound} screen): generating and placing thresholds")
-    wl, summ = prepared(name, bound=bound, fp8=fp8, block=block)
+    wl, summ = prepared(name, bound=bound, fp8=fp8, block=block, **kw)
     log(f"[full-size] {name}: {wl.n_seqs} seqs, {int(wl.seq_lens.sum())} tokens, "
         f"{wl.kv_bytes() / 1e9:.2f} GB K/V")
     heads = _sample_heads(wl, per_seq, seed)
@@ -97,3 +97,12 @@ def test_seq_512k_subblock16_full():
 def test_seq_512k_pairblock128_full():
     """The 512K workload with 128-token screen blocks: 8 heads."""
     _run_full("seq_512k", per_seq=8, bound="geometric_sub", block=128)
+
+
+@pytest.mark.timeout(600)
+def test_longest_supported_sequence():
+    """One sequence at the largest block table the library accepts (65,536
+    pages: 4,194,304 tokens), one KV head of four query heads, d = 64: the
+    screen's 1,024 tiles, the attend kernel's full tile prefix in LDS. Sets and
+    counts bit-exact for all heads, outputs on two of them."""
+    _run_full("seq_32k", per_seq=2, seq_lens=[64 * 65536], h_q=4, h_kv=1, d=64, needles=0)
