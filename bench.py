@@ -530,7 +530,20 @@ def cpu_baseline(S, budget_s):
     per_step_s = elapsed * total_blocks / blocks_done
     return {"value": per_step_s * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {len(segs)} (sequence, KV head) segments ({G} query heads each), "
-                      f"{elapsed:.1f}s of single-threaded fp64 NumPy, scaled by blocks to the full step"}
+                      f"{elapsed:.1f}s of single-threaded fp64 NumPy, scaled by blocks to the full step",
+            "cpu": host_cpu_model()}
+
+
+def host_cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
