@@ -124,6 +124,9 @@ def test_append_and_prefill_build_subblock_records(block):
     (128, dict(n_seqs=4, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
                seq_lens=[9000, 300, 64 * 12, 4097])),
     (128, dict(seq_lens=[64 * 40 + 17, 64], h_q=32, h_kv=4, d=128, density=0.02)),
+    (32, dict(seq_lens=[3000, 1000], h_q=4, h_kv=2, d=128)),                      # two heads per group
+    (128, dict(seq_lens=[3000, 1000 + 64], h_q=4, h_kv=2, d=64, paged=True)),
+    (16, dict(seq_lens=[2000, 513], h_q=2, h_kv=1, d=64, kv_dtype="f32", lwb=3)),
 ])
 def test_subblock_decode_parity(block, kw):
     log(f"[sub decode] b={block} {kw}")
