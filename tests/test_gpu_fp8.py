@@ -122,6 +122,7 @@ def test_append_and_prefill_build_fp8():
 @pytest.mark.parametrize("fmt,kw", [
     ("e4m3", dict(seq_lens=[64 * 70 + 3, 64 * 64, 129], h_q=8, h_kv=2, d=128)),
     ("e5m2", dict(seq_lens=[5000, 7000], h_q=4, h_kv=4, d=64, kv_dtype="f32", mode="calibrated")),
+    ("e4m3", dict(seq_lens=[3000, 64 * 20 + 1], h_q=4, h_kv=2, d=64)),              # two heads per group
     ("e4m3", dict(seq_lens=[64 * 130 + 63, 64 * 5], h_q=16, h_kv=2, d=128, lwb=2, a=0.4)),
     ("e5m2", dict(n_seqs=4, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
                   seq_lens=[9000, 300, 64 * 12, 4097])),

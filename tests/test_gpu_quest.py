@@ -115,6 +115,7 @@ def test_append_and_prefill_build_box():
 @pytest.mark.parametrize("kw", [
     dict(seq_lens=[64 * 70 + 3, 64 * 64, 129], h_q=8, h_kv=2, d=128),
     dict(seq_lens=[5000, 7000], h_q=4, h_kv=4, d=64, kv_dtype="f32", mode="calibrated"),
+    dict(seq_lens=[3000, 64 * 20 + 1], h_q=4, h_kv=2, d=64),                        # two heads per group
     dict(seq_lens=[64 * 130 + 63, 64 * 5], h_q=16, h_kv=2, d=128, lwb=2, a=0.4),
     dict(n_seqs=4, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
          seq_lens=[9000, 300, 64 * 12, 4097]),
