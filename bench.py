@@ -549,7 +549,7 @@ def host_cpu_model():
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this build has no multi-GPU path.",
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the library has no multi-GPU path.",
               file=sys.stderr)
         sys.exit(2)
     import torch

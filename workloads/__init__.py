@@ -109,7 +109,7 @@ class Workload:
 
 
 # --------------------------------------------------------------------------- generators
-_CONFIGS = {
+_RECIPES = {
     # name: sizes, storage dtype, threshold mode, target per-head density, planted needles, default seed
     "tiny_4k_f32": dict(seed=1000, n=1, h_q=1, h_kv=1, d=64, T=4096, dtype="f32", mode="learned",
                         density=0.40, needles=3),
@@ -124,11 +124,11 @@ _CONFIGS = {
                       density=None, needles=0, t_lo=4096, t_hi=262144, paged=True),
 }
 
-CONFIG_NAMES = tuple(_CONFIGS)
+WORKLOAD_NAMES = tuple(_RECIPES)
 
 
-def config_spec(name: str) -> dict:
-    return dict(_CONFIGS[name])
+def recipe(name: str) -> dict:
+    return dict(_RECIPES[name])
 
 
 def _streams(seed: int, k: int):
@@ -141,9 +141,9 @@ def make_workload(name: str, seed: Optional[int] = None, *, n_seqs: Optional[int
                   mode: Optional[str] = None, density=None, needles: Optional[int] = None,
                   paged: Optional[bool] = None, lwb: int = 0, a: float = 0.0, beta: float = 5.0,
                   tail_fill: float = float("nan"), threads: int = 8) -> Workload:
-    """Draw one seeded workload. `name` picks the base recipe (one of CONFIG_NAMES);
+    """Draw one seeded workload. `name` picks the base recipe (one of WORKLOAD_NAMES);
     keyword overrides shrink or reshape it for parity-size cases."""
-    spec = config_spec(name)
+    spec = recipe(name)
     seed = spec["seed"] if seed is None else int(seed)
     N = spec["n"] if n_seqs is None else int(n_seqs)
     HQ = spec["h_q"] if h_q is None else int(h_q)
