@@ -291,9 +291,9 @@ def prefill_bench(steps, warmup, cpu_budget, no_cpu):
                    "causal_pairs_per_head": pairs},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": None,
-                     "note": "4*d flops per causal (query, key) pair and head; the kernel also issues the second "
-                             "bfloat16 term of P (1.5x the method's matrix-core flops) and about 3 transcendental "
-                             "and 10 vector operations per logit for the gate and the softmax"},
+                     "note": "4*d flops per causal (query, key) pair and head, P times V in float16 (V within "
+                             "float16's exact range); the gate and the softmax add about 3 transcendental and 10 "
+                             "vector operations per logit"},
         "torch_sdpa_causal_ungated_ms": sdpa_ms,
         "cpu_baseline": cpu,
     }), flush=True)

@@ -334,9 +334,14 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
  *   err_flag [1] int32 device out: 1 if a length outside [0, 64*max_blocks]
  *            (that sequence's rows are then NaN) or an out-of-range page id
  *            (the block reads as zeros and its record is left alone) was met.
- * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise: the products run
- * on the bfloat16 matrix cores), beta > 0 finite, a finite, and
- * num_seqs * num_q_heads <= 65535. Asynchronous on `stream`. */
+ * Products on the matrix cores: S with bfloat16 operands; the weights times V
+ * in float16 (one term, V converted exactly) when every value of V in the
+ * prompts lies within +-65280, else in two bfloat16 terms of each weight (a
+ * range check over V picks the path for the whole call). Values of V must be
+ * finite: a non-finite one reaches the rows of its (sequence, KV head) whose
+ * last key block holds it as well, as NaN.
+ * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise), beta > 0 finite,
+ * a finite, and num_seqs * num_q_heads <= 65535. Asynchronous on `stream`. */
 eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
                        int tau_mode, const float* w, const float* b_or_c, float a, float beta, float* out,
                        int32_t* err_flag, eta_stream_t stream);

@@ -27,12 +27,14 @@
 //                 straight from the lane's registers): the keys of a step are
 //                 taken in the order the lanes hold them, and V^T is read in the
 //                 same order, so P needs no data movement.
-// P enters the matrix cores as two bfloat16 terms (its leading 8 mantissa bits
-// and the rounded remainder), so each weight is carried to about 2^-16
-// relative; one bfloat16 term would perturb outputs by a few 1e-3. The running
-// maximum is only moved when a weight would exceed 2^8 (float32 and the two
-// terms are exact well beyond that), which spares most rescales of the
-// accumulators.
+// P enters the matrix cores as one float16 term (11 significant bits) against
+// V converted to float16, which is exact when every value of V in the prompts
+// lies within +-65280 (a range check over V before the pass decides, for the
+// whole call); otherwise as two bfloat16 terms (its leading 8 mantissa bits
+// and the rounded remainder, about 2^-16 relative) against V in bfloat16. One
+// bfloat16 term would perturb outputs by a few 1e-3. The running maximum is
+// only moved when a weight would exceed 2^8 (float32 and both forms are exact
+// well beyond that), which spares most rescales of the accumulators.
 //
 // Records: the workgroup holding a complete block's last position builds the
 // block's centroid, radius (and deviation, if the cache has a deviation
@@ -44,6 +46,7 @@ namespace eta {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
@@ -64,7 +67,51 @@ struct PrefillArgs {
   int* err;    // [1]
 };
 
+// err bit 0: invalid length or page id (reported); bit 1, internal: some V
+// element of a sequence's prompt lies outside float16's exact range, so the
+// two-term bfloat16 products run (cleared again by k_prefill_fin)
+constexpr int kErrData = 1, kErrWideV = 2;
+
 __global__ void k_prefill_zero(int* err) { *err = 0; }
+__global__ void k_prefill_fin(int* err) {
+  if (*err & kErrWideV) atomicAnd(err, kErrData);
+}
+
+// bfloat16 pair (two halves of w) -> float16 pair, toward zero: exact for
+// every bfloat16 value the range test below admits (magnitudes up to 65280;
+// below 2^-14 float16 keeps 2^-24 steps, far under the outputs' error bar)
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(bf16_lo(w), bf16_hi(w)));
+}
+// nonzero if either bfloat16 half of w is not finite or larger in magnitude
+// than 65280, the largest bfloat16 value below float16's largest finite one
+__device__ __forceinline__ uint32_t f16_unsafe(uint32_t w) {
+  return ((w & 0x7fffu) > 0x477fu) | (((w >> 16) & 0x7fffu) > 0x477fu);
+}
+
+// One workgroup per (sequence, KV head, key block below the length): sets
+// kErrWideV if a value of V in the prompt is not exact in float16.
+template <int D>
+__global__ __launch_bounds__(256) void k_prefill_vcheck(CacheView c, SeqView s, int* err) {
+  const int j = blockIdx.x, n = blockIdx.y / c.HKV, g = blockIdx.y % c.HKV;
+  const int T = s.lens[n];
+  if (T < 1 || T > kBlock * s.MB || j * kBlock >= T) return;
+  const int page = s.bt[(int64_t)n * s.MB + j];
+  if (page < 0 || page >= c.num_pages) return;  // reported by the prompt pass
+  const uint16_t* vt = (const uint16_t*)c.v + ((int64_t)page * c.HKV + g) * (kBlock * D);
+  const int rows = min(kBlock, T - j * kBlock);
+  uint32_t bad = 0;
+  for (int ch = threadIdx.x; ch < rows * D / 8; ch += 256) {
+    const uint4 v = *(const uint4*)(vt + ch * 8);
+    bad |= f16_unsafe(v.x) | f16_unsafe(v.y) | f16_unsafe(v.z) | f16_unsafe(v.w);
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(err, kErrWideV);
+}
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, _Float16 __attribute__((ext_vector_type(2)))));
+}
 
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   const f32x2_t v = {lo, hi};
@@ -114,7 +161,8 @@ __device__ __forceinline__ void pf_load(PfTileRegs<D, NTH>& R, const PrefillArgs
   }
 }
 
-template <int D, int NTH>
+// V^T goes to LDS as bfloat16 or, with F16, converted to float16.
+template <int D, int NTH, bool F16>
 __device__ __forceinline__ void pf_store(const PfTileRegs<D, NTH>& R, uint16_t* buf, int tid) {
   using L = PfLds<D>;
   using TR = PfTileRegs<D, NTH>;
@@ -137,8 +185,8 @@ __device__ __forceinline__ void pf_store(const PfTileRegs<D, NTH>& R, uint16_t* 
         // dims 8 dc + 2u (low halves) and 8 dc + 2u + 1 (high halves): keys 2 kp, 2 kp + 1
         const uint32_t even = (a[u] & 0xffffu) | (b[u] << 16);
         const uint32_t odd = (a[u] >> 16) | (b[u] & 0xffff0000u);
-        *(uint32_t*)(vl + (8 * dc + 2 * u) * L::VS + 2 * kp) = even;
-        *(uint32_t*)(vl + (8 * dc + 2 * u + 1) * L::VS + 2 * kp) = odd;
+        *(uint32_t*)(vl + (8 * dc + 2 * u) * L::VS + 2 * kp) = F16 ? bf16x2_to_f16x2(even) : even;
+        *(uint32_t*)(vl + (8 * dc + 2 * u + 1) * L::VS + 2 * kp) = F16 ? bf16x2_to_f16x2(odd) : odd;
       }
     }
   }
@@ -165,8 +213,13 @@ __device__ __forceinline__ float pf_gate(f32x16_t* s, float kb, float tb, int li
   return mx;
 }
 
-template <int D, int G, int NW>
+// F16: the products O^T += V^T P^T take one float16 term (V exact in
+// float16: the range check found no wider value); otherwise two bfloat16
+// terms. Both instantiations are launched; the one that does not match the
+// check's flag returns at once.
+template <int D, int G, int NW, bool F16>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_prefill(PrefillArgs A) {
+  if (F16 == ((*A.err & kErrWideV) != 0)) return;
   using L = PfLds<D>;
   constexpr int NTH = 64 * NW;
   constexpr int HW = G < NW ? G : NW;    // heads per workgroup
@@ -189,7 +242,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int p = pw0 + qi;                // this lane's position
   int T = A.s.lens[n];
   if (T < 0 || T > kBlock * MB) {  // invalid length: flagged, every row NaN
-    if (tid == 0) A.err[0] = 1;
+    if (tid == 0) atomicOr(A.err, kErrData);
     T = 0;
   }
   const int64_t orow = (((int64_t)n * Lq + p) * HQ + hq) * D;
@@ -254,9 +307,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   {
     const int page = bt[0];
     const bool valid = page >= 0 && page < A.c.num_pages;
-    if (!valid && tid == 0) A.err[0] = 1;
+    if (!valid && tid == 0) atomicOr(A.err, kErrData);
     pf_load<D, NTH>(R, A, valid ? page : 0, valid, T, g, tid);
-    pf_store<D, NTH>(R, lds, tid);
+    pf_store<D, NTH, F16>(R, lds, tid);
   }
   __syncthreads();
   for (int kt = 0; kt <= last; ++kt) {
@@ -264,7 +317,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (has_next) {
       const int page = bt[kt + 1];
       const bool valid = page >= 0 && page < A.c.num_pages;
-      if (!valid && tid == 0) A.err[0] = 1;
+      if (!valid && tid == 0) atomicOr(A.err, kErrData);
       pf_load<D, NTH>(R, A, valid ? page : 0, valid, T - (kt + 1) * kBlock, g, tid);
     }
     const uint16_t* kl = lds + (kt & 1) * L::BUF;
@@ -301,7 +354,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         mrun = mnew;
       }
       const float moff = mrun == -__builtin_inff() ? 0.f : -c2 * mrun;
-      // ---- weights, split into two bfloat16 terms, and O^T += V^T P^T
+      // ---- weights and O^T += V^T P^T: one float16 term (F16), or two
+      //      bfloat16 terms, the leading 8 bits and the rounded remainder
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
 #pragma unroll
@@ -312,26 +366,36 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const float p0 = __builtin_amdgcn_exp2f(fmaf(c2, s[t][8 * ks + 2 * u], moff));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(c2, s[t][8 * ks + 2 * u + 1], moff));
             lsum += p0 + p1;
-            const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
-            hb[u] = (h0 >> 16) | h1;
-            lb[u] = pack_bf16_rne(p0 - __uint_as_float(h0), p1 - __uint_as_float(h1));
+            if constexpr (F16) {
+              hb[u] = pack_f16_rne(p0, p1);
+            } else {
+              const uint32_t h0 = __float_as_uint(p0) & 0xffff0000u, h1 = __float_as_uint(p1) & 0xffff0000u;
+              hb[u] = (h0 >> 16) | h1;
+              lb[u] = pack_bf16_rne(p0 - __uint_as_float(h0), p1 - __uint_as_float(h1));
+            }
           }
-          const bf16x8_t bh8 = __builtin_bit_cast(bf16x8_t, make_uint4(hb[0], hb[1], hb[2], hb[3]));
-          const bf16x8_t bl8 = __builtin_bit_cast(bf16x8_t, make_uint4(lb[0], lb[1], lb[2], lb[3]));
+          const uint4 ph = make_uint4(hb[0], hb[1], hb[2], hb[3]);
           const int k0 = 32 * t + 16 * ks + 4 * hh;  // keys k0 .. k0+3 and k0+8 .. k0+11
 #pragma unroll
           for (int m = 0; m < DT; ++m) {
             const uint16_t* vr = vl + (32 * m + qi) * L::VS;
             const uint2 x0 = *(const uint2*)(vr + k0);
             const uint2 x1 = *(const uint2*)(vr + k0 + 8);
-            const bf16x8_t av = __builtin_bit_cast(bf16x8_t, make_uint4(x0.x, x0.y, x1.x, x1.y));
-            o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bh8, o[m], 0, 0, 0);
-            o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bl8, o[m], 0, 0, 0);
+            const uint4 va = make_uint4(x0.x, x0.y, x1.x, x1.y);
+            if constexpr (F16) {
+              o[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, va),
+                                                            __builtin_bit_cast(f16x8_t, ph), o[m], 0, 0, 0);
+            } else {
+              const bf16x8_t av = __builtin_bit_cast(bf16x8_t, va);
+              o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, ph), o[m], 0, 0, 0);
+              o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  av, __builtin_bit_cast(bf16x8_t, make_uint4(lb[0], lb[1], lb[2], lb[3])), o[m], 0, 0, 0);
+            }
           }
         }
       }
     }
-    if (has_next) pf_store<D, NTH>(R, lds + ((kt + 1) & 1) * L::BUF, tid);
+    if (has_next) pf_store<D, NTH, F16>(R, lds + ((kt + 1) & 1) * L::BUF, tid);
     __syncthreads();
   }
 
@@ -401,7 +465,9 @@ hipError_t pf_launch(const PrefillArgs& a, hipStream_t st) {
   constexpr int HW = G < NW ? G : NW;
   constexpr int QT = 32 * (NW / HW);
   const int nqt = (a.Lq + QT - 1) / QT;
-  hipLaunchKernelGGL((k_prefill<D, G, NW>), dim3(nqt, a.s.N * a.c.HKV * (G / HW)), dim3(64 * NW), 0, st, a);
+  const dim3 grid(nqt, a.s.N * a.c.HKV * (G / HW));
+  hipLaunchKernelGGL((k_prefill<D, G, NW, true>), grid, dim3(64 * NW), 0, st, a);
+  hipLaunchKernelGGL((k_prefill<D, G, NW, false>), grid, dim3(64 * NW), 0, st, a);
   return hipGetLastError();
 }
 
@@ -433,10 +499,16 @@ hipError_t launch_prefill(const CacheView& c, const SeqView& s, const PrefillPar
   a.out = p.out;
   a.err = p.err;
   hipLaunchKernelGGL(k_prefill_zero, dim3(1), dim3(1), 0, st, p.err);
+  const dim3 cgrid(s.MB, s.N * c.HKV);
+  if (c.D == 128) hipLaunchKernelGGL((k_prefill_vcheck<128>), cgrid, dim3(256), 0, st, c, s, p.err);
+  else hipLaunchKernelGGL((k_prefill_vcheck<64>), cgrid, dim3(256), 0, st, c, s, p.err);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int G = p.HQ / c.HKV;
-  return c.D == 128 ? pf_g<128>(a, G, st) : pf_g<64>(a, G, st);
+  e = c.D == 128 ? pf_g<128>(a, G, st) : pf_g<64>(a, G, st);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_prefill_fin, dim3(1), dim3(1), 0, st, p.err);
+  return hipGetLastError();
 }
 
 }  // namespace eta

@@ -172,3 +172,27 @@ def test_prefill_seq32k_sampled():
     torch.cuda.synchronize()
     assert np.array_equal(dev.mu_bits(), dev2.mu_bits())
     assert np.array_equal(dev.radius().view(np.uint32), dev2.radius().view(np.uint32))
+
+
+@pytest.mark.parametrize("wide", [70000.0, -1e30])
+def test_prefill_values_beyond_float16(wide):
+    """A V element past float16's exact range anywhere in the prompt switches
+    the pass to the two-term bfloat16 products: outputs at the bar relative to
+    their size, no error reported."""
+    wl = W.make_workload("seq_32k", seq_lens=[64 * 3 + 7, 64 * 2], h_q=4, h_kv=2, d=64, needles=0)
+    bits = np.float32(wide).view(np.uint32) >> 16
+    page = int(wl.block_table[1, 1])
+    wl.v_pages[page, 0, 5, 3] = np.uint16(bits)  # sequence 1, KV head 0, token 69, dim 3
+    q_all = W.trace_queries(wl, seed=13)
+    b = np.linspace(0.5, 1.5, wl.h_q).astype(np.float32)
+    _, got, _ = _run(wl, q_all, "learned", b, 5.0)
+    ref = E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q_all, "learned", wl.w, b,
+                    0.0, 5.0)
+    for n in range(wl.n_seqs):
+        T = int(wl.seq_lens[n])
+        g, r = got[n, :T], ref[n, :T]
+        fin = np.isfinite(r)
+        assert np.array_equal(fin, np.isfinite(g))
+        err = np.abs(g[fin] - r[fin]) / np.maximum(1.0, np.abs(r[fin]))
+        assert float(err.max()) <= TOL["bf16"], float(err.max())
+    assert np.all(np.isfinite(got[0, :int(wl.seq_lens[0])]))  # the other sequence is untouched
