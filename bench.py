@@ -579,9 +579,11 @@ def main():
     log(f"step {us:.1f} us; phases screen / attend+merge {ph[0]:.1f} / {ph[1]:.1f} us")
     wl = S.wl
     esz = 2 if wl.kv_dtype == "bf16" else 4
-    U = int(st.union_per_kv.sum())
+    U = int(st.union_per_kv.sum())  # union blocks in the screen's block size
     G, D = wl.group, wl.d
-    attend_bytes = U * 2 * 64 * D * esz + U * 8 + wl.n_seqs * wl.h_q * D * esz
+    # K/V rows of the union's blocks (kv_bytes follows the screen's block size),
+    # one 8-byte entry per block, the queries
+    attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
     workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + \
         ("" if args.bound == "geometric" else "-" + args.bound)
