@@ -66,6 +66,8 @@ def parse():
                    help="geometric, dual, box-bound and FP8 screens at the same thresholds")
     p.add_argument("--prefill", action="store_true",
                    help="time the causal prompt pass over the seq_32k prompt instead of the decode step")
+    p.add_argument("--append", action="store_true",
+                   help="only time eta_append_kv on the workload's last pages and print its own JSON line")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB `steps` times (calibrates the "
                         "HBM byte counters) and exit")
@@ -296,6 +298,87 @@ def prefill_bench(steps, warmup, cpu_budget, no_cpu):
                              "vector operations per logit"},
         "torch_sdpa_causal_ungated_ms": sdpa_ms,
         "cpu_baseline": cpu,
+    }), flush=True)
+
+
+def append_bench(workload, steps, warmup):
+    """eta_append_kv: one new token per (sequence, KV head) written into its
+    page slot, with the record of the page built when the token fills slot 63.
+    Times both kinds of call on the last page of every sequence of the
+    workload (the sequence lengths set just below that page's slot 5 and slot
+    63), with HIP events on the launch stream and the calls back to back on
+    the GPU (the host's enqueue time per call is reported beside). The bytes
+    counted are the new K and V rows, plus the filled page's K rows read and
+    its record written; a call moves kilobytes, so it is bound by launch
+    latency, not by HBM."""
+    import torch
+
+    import learned_threshold_block_amd as eta
+    import workloads as W
+
+    wl = W.make_workload(workload)
+    dev = torch.device("cuda")
+    cache = eta.Cache(eta.upload(wl.k_pages, wl.kv_dtype, dev), eta.upload(wl.v_pages, wl.kv_dtype, dev),
+                      torch.zeros(wl.num_pages, wl.h_kv, wl.d, dtype=torch.float16, device=dev),
+                      torch.zeros(wl.num_pages, wl.h_kv, dtype=torch.float32, device=dev))
+    bt = torch.from_numpy(wl.block_table.astype(np.int32)).to(dev)
+    rng = np.random.default_rng(11)
+    shape = (wl.n_seqs, wl.h_kv, wl.d)
+    kvt = torch.bfloat16 if wl.kv_dtype == "bf16" else torch.float32
+    k_new = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev).to(kvt)
+    v_new = torch.from_numpy(rng.standard_normal(shape).astype(np.float32)).to(dev).to(kvt)
+    last = (wl.seq_lens.astype(np.int64) - 1) // 64 * 64  # first token of each sequence's last page
+    esz = 2 if wl.kv_dtype == "bf16" else 4
+    rows = wl.n_seqs * wl.h_kv
+    host_us = {}
+    # A call costs the host more than the kernel takes, so the calls are
+    # enqueued behind copies of the V pages that keep the GPU busy until the
+    # last call is queued: the events then time the kernels back to back.
+    ahead = torch.empty_like(cache.v_pages)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    v_bytes = cache.v_pages.numel() * esz
+    n_ahead = max(2, math.ceil(steps * 120e-6 / (2 * v_bytes / 4e12)))  # ~120 us of GPU work per call queued
+    res = {}
+    for name, slot in (("row", 5), ("row_and_record", 63)):
+        lens = torch.from_numpy((last + slot).astype(np.int32)).to(dev)
+        for _ in range(warmup):
+            eta.append_kv(cache, lens, bt, k_new, v_new)
+        torch.cuda.synchronize()
+        c0, e0, e1 = ev(), ev(), ev()
+        c0.record()
+        for _ in range(n_ahead):
+            ahead.copy_(cache.v_pages)
+        e0.record()
+        h0 = time.perf_counter()
+        for _ in range(steps):
+            eta.append_kv(cache, lens, bt, k_new, v_new)
+        host_s = time.perf_counter() - h0
+        e1.record()
+        torch.cuda.synchronize()
+        if host_s * 1e3 >= c0.elapsed_time(e0):
+            raise RuntimeError("the copies ahead ran out before the last call was queued")
+        us = e0.elapsed_time(e1) / steps * 1e3
+        host_us[name] = host_s / steps * 1e6
+        nbytes = rows * 2 * wl.d * esz * 2  # new K and V rows: read, then written into the page
+        if slot == 63:
+            nbytes += rows * (64 * wl.d * esz + wl.d * 2 + 4)  # the page's K rows read, its record written
+        res[name] = (us, nbytes)
+    us, nbytes = res["row_and_record"]
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({
+        "metric": "ETA append latency (one token per sequence and KV head; the call that fills a page also "
+                  "builds its record)",
+        "value": round(us, 2), "unit": "us/call", "higher_is_better": False, "steps": steps, "warmup": warmup,
+        "data": "synthetic", "dtype": wl.kv_dtype,
+        "config": {"workload": f"{workload}: {wl.n_seqs} sequences x {wl.h_kv} KV heads, d={wl.d}, "
+                               f"{wl.kv_dtype} K/V, the last page of every sequence"},
+        "row_only_us": round(res["row"][0], 2),
+        "host_enqueue_us": round(host_us["row_and_record"], 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": 8000.0, "unit": "GB/s",
+                     "frac": round(gbs / 8000.0, 5), "traffic": None,
+                     "note": f"{nbytes} bytes per call (new K and V rows read and written, the filled page's K "
+                             "rows read, its record written): launch latency bound"},
+        "cpu_baseline": None,
     }), flush=True)
 
 
@@ -563,6 +646,9 @@ def main():
         return
     if args.compare_screens:
         compare_screens(args.workload, args.density, max(5, min(args.steps, 50)), min(args.warmup, 5), args.z)
+        return
+    if args.append:
+        append_bench(args.workload, max(20, min(args.steps * 2, 100)), max(3, args.warmup))
         return
     if args.prefill:
         prefill_bench(max(2, min(args.steps, 20)), min(args.warmup, 3), args.cpu_budget, args.no_cpu)
