@@ -294,8 +294,8 @@ def prefill_bench(steps, warmup, cpu_budget, no_cpu):
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": 2500.0, "unit": "TFLOP/s",
                      "frac": round(tflops / 2500.0, 4), "traffic": None,
                      "note": "4*d flops per causal (query, key) pair and head, P times V in float16 (V within "
-                             "float16's exact range); the gate and the softmax add about 3 transcendental and 10 "
-                             "vector operations per logit"},
+                             "float16's exact range); bound by vector issue, not the matrix cores: the gate and the "
+                             "softmax take about 11.6 vector instructions per logit, 3 of them transcendental"},
         "torch_sdpa_causal_ungated_ms": sdpa_ms,
         "cpu_baseline": cpu,
     }), flush=True)

@@ -192,24 +192,44 @@ __device__ __forceinline__ void pf_store(const PfTileRegs<D, NTH>& R, uint16_t* 
   }
 }
 
-// Gate of one block's logits in place, S -> S sigmoid(beta (S - tau~)) in the
-// units of the accumulators, with keys past the lane's position set to -inf
-// when MASK (lim: the largest key offset 32 t + 8 i + j the lane may see);
-// returns the lane's maximum.
-template <bool MASK>
-__device__ __forceinline__ float pf_gate(f32x16_t* s, float kb, float tb, int lim) {
-  float mx = -__builtin_inff();
+// S^T of both 32-key halves of a block (keys 32 t + 8 i + 4 hh + j in acc
+// element 4 i + j of s[t], query qi), then the gate in place,
+// S -> S sigmoid(beta (S - tau~)) in the units of the accumulators, with keys
+// past the lane's position set to -inf when MASK (lim: the largest key offset
+// 32 t + 8 i + j the lane may see). The gate of the first half is issued
+// between the products of the second half, so that vector work runs while the
+// matrix cores are busy. Returns the lane's maximum.
+template <bool MASK, int KSTEPS, int KSTR>
+__device__ __forceinline__ float pf_scores_gated(f32x16_t (&s)[2], const uint16_t* kl, const uint4 (&qr)[KSTEPS],
+                                                 int qi, int hh, float kb, float tb, int lim) {
+  constexpr int PER = 16 / KSTEPS;  // first-half elements gated per product of the second half
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const float v = s[t][e];
-      const float ex = __builtin_amdgcn_exp2f(fmaf(kb, v, tb));
-      float y = v * __builtin_amdgcn_rcpf(1.0f + ex);
-      if (MASK && 32 * t + 8 * (e >> 2) + (e & 3) > lim) y = -__builtin_inff();
-      s[t][e] = y;
-      mx = fmaxf(mx, y);
-    }
+    for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const bf16x8_t av = *(const bf16x8_t*)(kl + qi * KSTR + 16 * ks + 8 * hh);
+    s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, qr[ks]), s[0], 0, 0, 0);
+  }
+  float mx = -__builtin_inff();
+  const auto gate = [&](int t, int e) {
+    const float v = s[t][e];
+    const float ex = __builtin_amdgcn_exp2f(fmaf(kb, v, tb));
+    float y = v * __builtin_amdgcn_rcpf(1.0f + ex);
+    if (MASK && 32 * t + 8 * (e >> 2) + (e & 3) > lim) y = -__builtin_inff();
+    s[t][e] = y;
+    mx = fmaxf(mx, y);
+  };
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    const bf16x8_t av = *(const bf16x8_t*)(kl + (32 + qi) * KSTR + 16 * ks + 8 * hh);
+    s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, qr[ks]), s[1], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) gate(0, PER * ks + u);
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) gate(1, e);
   return mx;
 }
 
@@ -323,24 +343,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint16_t* kl = lds + (kt & 1) * L::BUF;
     const uint16_t* vl = kl + L::KE;
     if (wactive && kt <= wlast) {
-      // ---- S^T for keys 32 t + 8 i + 4 hh + j (acc element 4 i + j), query qi
+      // ---- S^T for keys 32 t + 8 i + 4 hh + j (acc element 4 i + j), query
+      //      qi; gate, causal mask and running maximum
       f32x16_t s[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[t][e] = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-          const bf16x8_t av = *(const bf16x8_t*)(kl + (32 * t + qi) * L::KS + 16 * ks + 8 * hh);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8_t, qr[ks]), s[t], 0, 0, 0);
-        }
-      }
-      // ---- gate, causal mask, running maximum
       float mx;
       if (kt * kBlock + kBlock - 1 > pw0)  // the diagonal block: some key may lie after some position
-        mx = pf_gate<true>(s, kb, tb, p - kt * kBlock - 4 * hh);
+        mx = pf_scores_gated<true, KSTEPS, L::KS>(s, kl, qr, qi, hh, kb, tb, p - kt * kBlock - 4 * hh);
       else
-        mx = pf_gate<false>(s, kb, tb, 0);
+        mx = pf_scores_gated<false, KSTEPS, L::KS>(s, kl, qr, qi, hh, kb, tb, 0);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const bool need = mx > mrun + thr;
       if (__any(need)) {
