@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="seq_512k", choices=["seq_32k", "batch_4x128k", "seq_512k", "ragged_16"])
     p.add_argument("--density", type=float, default=None, help="per-head target density override")
+    p.add_argument("--seq-len", type=int, default=None,
+                   help="override the length of every sequence of the workload (the line then names the length "
+                        "and carries no stored traffic)")
     p.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
@@ -403,7 +406,7 @@ def copy_probe(mib, steps):
 class Setup:
     """One workload resident on the GPU."""
 
-    def __init__(self, name, density=None, bound="geometric", z=2.0, sub_block=16):
+    def __init__(self, name, density=None, bound="geometric", z=2.0, sub_block=16, seq_len=None):
         import torch
 
         import learned_threshold_block_amd as eta
@@ -411,6 +414,8 @@ class Setup:
 
         t0 = time.time()
         kw = {} if density is None else dict(density=density)
+        if seq_len is not None:
+            kw["seq_len"] = seq_len
         self.wl = wl = W.make_workload(name, **kw)
         log(f"{name}: generated {wl.kv_bytes() / 1e9:.2f} GB of K/V in {time.time() - t0:.1f}s")
         self.eta, self.torch = eta, torch
@@ -654,7 +659,7 @@ def main():
         prefill_bench(max(2, min(args.steps, 20)), min(args.warmup, 3), args.cpu_budget, args.no_cpu)
         return
 
-    S = Setup(args.workload, args.density, args.bound, args.z, args.sub_block)
+    S = Setup(args.workload, args.density, args.bound, args.z, args.sub_block, args.seq_len)
     S.calibrate()
     st, dens_head, dens_union = S.densities()
     kv_bytes, all_bytes = S.step_bytes(st)
@@ -672,6 +677,7 @@ def main():
     attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
     workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + \
+        ("" if args.seq_len is None else f"-T{args.seq_len}") + \
         ("" if args.bound == "geometric" else "-" + args.bound)
     traffic = stored_traffic(workload_key)
     result = {
@@ -688,8 +694,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": {"seq_32k": "1 seq x 32768 ctx", "batch_4x128k": "4 seq x 131072 ctx",
-                         "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[args.workload]
+            "workload": ({"seq_32k": "1 seq x 32768 ctx", "batch_4x128k": "4 seq x 131072 ctx",
+                          "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[args.workload]
+                         if args.seq_len is None else f"{wl.n_seqs} seq x {args.seq_len} ctx")
                         + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
                         + f"{wl.tau_mode} thresholds, target per-head density "
                         + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
