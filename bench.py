@@ -87,6 +87,14 @@ def attend_sources_sha256():
     return h.hexdigest()
 
 
+def traffic_key(workload, density, bound="geometric", seq_len=None):
+    """Name of a decode workload in the committed counter summaries: the
+    recipe, the mean per-head target density, and any length or screen that
+    differs from the recipe's defaults."""
+    return f"{workload}@{density:.2f}" + ("" if seq_len is None else f"-T{seq_len}") + \
+        ("" if bound == "geometric" else "-" + bound)
+
+
 def stored_traffic(workload_key):
     """HBM bytes per attend launch from the committed counter summary (FETCH_SIZE
     + WRITE_SIZE, scaled by the copy-kernel calibration), or None when there is
@@ -676,9 +684,7 @@ def main():
     # one 8-byte entry per block, the queries
     attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * D * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
-    workload_key = f"{args.workload}@{float(np.mean(wl.target_density)):.2f}" + \
-        ("" if args.seq_len is None else f"-T{args.seq_len}") + \
-        ("" if args.bound == "geometric" else "-" + args.bound)
+    workload_key = traffic_key(args.workload, float(np.mean(wl.target_density)), args.bound, args.seq_len)
     traffic = stored_traffic(workload_key)
     result = {
         "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",

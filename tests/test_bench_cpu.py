@@ -1,5 +1,5 @@
 """Host-side logic of bench.py (no GPU): the single-GPU guard, the stored
-traffic lookup and its source-hash check."""
+traffic lookup, its source-hash check and the workload names it keys on."""
 import os
 import subprocess
 import sys
@@ -28,3 +28,19 @@ def test_stored_traffic_follows_the_attend_sources(tmp_path, monkeypatch):
                     "- attend_sources_sha256: `0000`\n")
     assert bench.stored_traffic("w@0.38") is None  # the kernel changed since the counters were taken
 
+
+
+def test_committed_traffic_summary_names_the_default_workload():
+    import re
+    import workloads as W
+
+    keys = []
+    for name in os.listdir(bench.PROFILES):
+        if "traffic" in name:
+            with open(os.path.join(bench.PROFILES, name)) as f:
+                keys += re.findall(r"^- workload_key: `([^`]*)`", f.read(), flags=re.M)
+    density = float(W.recipe("seq_512k")["density"])  # one target for every head
+    assert bench.traffic_key("seq_512k", density) in keys
+    # other lengths or screens never pick up the default workload's figure
+    assert bench.traffic_key("seq_512k", density, seq_len=4194304) not in keys
+    assert bench.traffic_key("seq_512k", density, bound="dual") != bench.traffic_key("seq_512k", density)
