@@ -40,7 +40,9 @@ def test_committed_traffic_summary_names_the_default_workload():
             with open(os.path.join(bench.PROFILES, name)) as f:
                 keys += re.findall(r"^- workload_key: `([^`]*)`", f.read(), flags=re.M)
     density = float(W.recipe("seq_512k")["density"])  # one target for every head
-    assert bench.traffic_key("seq_512k", density) in keys
+    default = bench.traffic_key("seq_512k", density)
+    assert default in keys
+    assert len(set(keys)) == len(keys)  # one summary per workload
     # other lengths or screens never pick up the default workload's figure
-    assert bench.traffic_key("seq_512k", density, seq_len=4194304) not in keys
-    assert bench.traffic_key("seq_512k", density, bound="dual") != bench.traffic_key("seq_512k", density)
+    assert bench.traffic_key("seq_512k", density, seq_len=4194304) != default
+    assert bench.traffic_key("seq_512k", density, bound="dual") != default
