@@ -23,6 +23,9 @@
  *   - Pointers are DEVICE pointers unless the comment says "host".
  *   - The caller owns all memory. The library allocates nothing and keeps no
  *     state between calls apart from a per-device launch-geometry cache.
+ *     A decode workspace carries the previous call's per-die work weights
+ *     and range timings to the next call on it; they steer only how the work
+ *     is split, never what is computed.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = default
  *     stream) except eta_stats, which synchronises the stream.
  *   - Host-checkable arguments are validated before any device work; a
@@ -158,7 +161,10 @@ typedef struct {
 eta_status eta_build_block_summaries(const eta_cache* cache, const eta_seqs* seqs,
                                      eta_stream_t stream);
 
-/* Append one token per sequence: k_new, v_new are [num_seqs][num_kv_heads][head_dim]
+/* Append one token per sequence (Section 3.2: the block records sit in a
+ * table beside the paged cache; Section 4.8: they are built as the cache
+ * grows, so a decode step reads the records of every block completed so far).
+ * k_new, v_new are [num_seqs][num_kv_heads][head_dim]
  * of kv_dtype (16-byte aligned). seqs->seq_lens holds the lengths BEFORE the
  * append; the token goes to row T%64 of page block_table[n][T/64], which the
  * caller has assigned. When that fills the block (T%64 == 63) its record is
@@ -189,7 +195,12 @@ size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_b
  *   lwb        number of most recent complete blocks always admitted, >= 0.
  *   block_size must equal cache->block_size (64).
  * num_q_heads must be a multiple of num_kv_heads with G = num_q_heads /
- * num_kv_heads in {1, 2, 4, 8}. Equivalent to the three phases below in order. */
+ * num_kv_heads in {1, 2, 4, 8}. Equivalent to the three phases below in order.
+ * Values of V: those of a block a head did not admit never reach that head's
+ * output (with ETA_BOUND_GEOMETRIC_SUB, per screen block, also between the
+ * blocks of one page); a non-finite element i of V at a token a head attends
+ * to makes element i of that head's output non-finite (inf or NaN, as the
+ * exact weighted sum is), and the other elements are unaffected. */
 eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* q,
                       int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
                       float a, float beta, int lwb, int block_size, float* out,
@@ -337,9 +348,13 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
  * Products on the matrix cores: S with bfloat16 operands; the weights times V
  * in float16 (one term, V converted exactly) when every value of V in the
  * prompts lies within +-65280, else in two bfloat16 terms of each weight (a
- * range check over V picks the path for the whole call). Values of V must be
- * finite: a non-finite one reaches the rows of its (sequence, KV head) whose
- * last key block holds it as well, as NaN.
+ * range check over V picks the path for the whole call). A non-finite element
+ * i of V at key s makes element i of the outputs of s's (sequence, KV head)
+ * non-finite at every position of s's 64-token key block and later: from s on
+ * as the exact rule gives, and at the block's positions before s as well,
+ * where the exact rule does not use key s (the block's masked keys enter the
+ * products with weight 0, and 0 times a non-finite value is NaN). Earlier
+ * positions and the other elements are unaffected.
  * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise), beta > 0 finite,
  * a finite, and num_seqs * num_q_heads <= 65535. Asynchronous on `stream`. */
 eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,

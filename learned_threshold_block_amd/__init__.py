@@ -199,6 +199,28 @@ def alloc_workspace(cache: Cache, num_seqs: int, max_blocks_per_seq: int, num_q_
     return torch.empty(n, dtype=torch.uint8, device=cache.k_pages.device)  # 256-byte aligned
 
 
+def _decode_shapes(head_dim: int, seq_lens, block_table, q, tau_mode: int, b_or_c, w):
+    """Shape checks of a decode call's tensors (the C ABI takes raw pointers, so
+    a mismatch here would become out-of-bounds device accesses). Returns
+    (N, H_Q, d)."""
+    if q.dim() != 3:
+        raise ValueError("q must be [num_seqs][H_Q][d]")
+    N, HQ, D = q.shape
+    if D != head_dim:
+        raise ValueError(f"q's head dim {D} differs from the cache's {head_dim}")
+    if seq_lens.dim() != 1 or seq_lens.shape[0] != N:
+        raise ValueError(f"seq_lens must be [num_seqs] = [{N}], got {tuple(seq_lens.shape)}")
+    if block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError(f"block_table must be [num_seqs][max_blocks_per_seq] with num_seqs = {N}")
+    if b_or_c.numel() != HQ:
+        raise ValueError(f"b_or_c must hold H_Q = {HQ} values, got {b_or_c.numel()}")
+    if int(tau_mode) == ETA_TAU_LEARNED and w is None:
+        raise ValueError("the learned threshold mode needs w")
+    if w is not None and tuple(w.shape) != (HQ, D):
+        raise ValueError(f"w must be [H_Q][d] = {(HQ, D)}, got {tuple(w.shape)}")
+    return N, HQ, D
+
+
 def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None, a: float = 0.0,
            beta: float = 5.0, lwb: int = 0, out=None, workspace=None, phase: Optional[int] = None,
            stream=None, bound: str = "geometric", z: float = 2.0) -> torch.Tensor:
@@ -210,13 +232,15 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
     "geometric_sub" (the geometric bound on cache.sub_block-token blocks)."""
     dev = cache.k_pages.device
     _need(q, "q", cache.k_pages.dtype, dev)
-    N, HQ, D = q.shape
     _need(b_or_c, "b_or_c", torch.float32, dev)
     if w is not None:
         _need(w, "w", torch.float32, dev)
+    N, HQ, D = _decode_shapes(cache.head_dim, seq_lens, block_table, q, tau_mode, b_or_c, w)
     if out is None:
         out = torch.empty(N, HQ, D, dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev)
+    if tuple(out.shape) != (N, HQ, D):
+        raise ValueError(f"out must be [num_seqs][H_Q][d] = {(N, HQ, D)}, got {tuple(out.shape)}")
     if workspace is None:
         workspace = alloc_workspace(cache, N, block_table.shape[1], HQ)
     _need(workspace, "workspace", torch.uint8, dev)

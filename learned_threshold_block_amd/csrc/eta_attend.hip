@@ -501,6 +501,11 @@ void k_attend(AttendArgs A) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
               if (!(hmask & (1u << h))) continue;
+              // smaller screen blocks: the RPI rows of load i lie in one block
+              // (RPI <= 8 < 16 tokens); a head skips the rows of blocks it did
+              // not admit, so their values never reach its sums (not even as
+              // 0 * v, which a non-finite v would turn into NaN)
+              if (SUBB && !((cur_sw >> (((RPI * i) >> lbs) * G + h)) & 1u)) continue;
               const float pv = ii == 0 ? pw[h].x : ii == 1 ? pw[h].y : ii == 2 ? pw[h].z : pw[h].w;
 #pragma unroll
               for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(pv, vf[e], acc[h][e]);

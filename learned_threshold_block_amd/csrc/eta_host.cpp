@@ -220,6 +220,14 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
       P->p.bound = cache->sub_block > kBlock ? 5 : 4;
     }
   }
+  // the screen reads the records through buffer resources, whose size and
+  // offsets are 32-bit: the largest record array it reads must stay below 4 GiB
+  {
+    const int slots = P->p.bound == 4 ? sub_blocks(cache) : 1;
+    const int64_t elem = P->p.bound == 3 ? 1 : 2;  // FP8 codes or float16 values per coordinate
+    const int64_t rec_bytes = (int64_t)cache->num_pages * cache->num_kv_heads * slots * cache->head_dim * elem;
+    if (rec_bytes >= ((int64_t)1 << 32)) return ETA_ERR_UNSUPPORTED;
+  }
   st = check_seqs(seqs);
   if (st != ETA_OK) return st;
   if (block_size != cache->block_size) return ETA_ERR_INVALID_ARGUMENT;

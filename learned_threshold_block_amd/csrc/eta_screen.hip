@@ -117,7 +117,10 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   }
   const int jl = j0 + RPI * cb + r;  // unit this lane owns after the reduction
   const int page_l = bt[min(jl >> lsb, MB - 1)];
-  const int page_r = PAIR ? bt[min(jl & ~1, MB - 1)] : page_l;
+  // 128-token blocks: the other page of the lane's block, and the page that
+  // keeps the block's record (the first one)
+  const int page_o = PAIR ? bt[min(jl ^ 1, MB - 1)] : page_l;
+  const int page_r = PAIR && (jl & 1) ? page_o : page_l;
 
   float qf[G][8];
   const auto* qbase = (const typename T::Stored*)A.p.q;
@@ -147,7 +150,9 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   const int nunit = PAIR ? (badT ? 0 : (seq_len + kBlock - 1) / kBlock) : nblk;  // lanes' units in the sequence
   const int jbl = PAIR ? jl >> 1 : jl;                                            // the lane's screen block
   const bool lvalid = jl < nunit && page_l >= 0 && page_l < A.c.num_pages;
-  const bool complete = jbl < nfull && lvalid && page_r >= 0 && page_r < A.c.num_pages;
+  // a 128-token block is complete only when both of its pages are valid, so
+  // that neither lane of it can be admitted, ranked or rescued otherwise
+  const bool complete = jbl < nfull && lvalid && page_o >= 0 && page_o < A.c.num_pages;
   // records through buffer loads: an invalid block reads zeros, without a branch
   // (the box bound reads the key box's lower corner here and its upper one below;
   // a smaller screen block's record is block j mod SB of its page's records)
@@ -617,6 +622,9 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
         const int c = A.ws.tile_cnt[tcx0 + tt];
         for (int u = jb; u <= (pair ? jb + 1 : jb); ++u) {
           const int jp = u >> lsb;  // the unit's page
+          // the screen ranks only blocks whose pages are all valid; a page id
+          // out of range is never handed to the attend kernel
+          if (bt[jp] < 0 || bt[jp] >= A.c.num_pages) continue;
           const uint32_t sbit = SB > 1 ? 1u << ((u & (SB - 1)) * G + h) : 0u;
           int found = -1;
           for (int k = 0; k < c; ++k)

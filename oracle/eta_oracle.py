@@ -784,5 +784,22 @@ def prefill(k_pages, v_pages, kv_dtype: str, block_table, seq_lens, q_all, tau_m
                 St = np.where(causal, St, -np.inf)
                 m = St.max(axis=1, keepdims=True)
                 wts = np.exp(St - m)
-                o[n, r, h] = (wts @ V[:t1]) / wts.sum(axis=1, keepdims=True)
+                o[n, r, h] = causal_weighted_sum(wts, V[:t1], causal) / wts.sum(axis=1, keepdims=True)
     return o
+
+
+def causal_weighted_sum(wts: np.ndarray, V: np.ndarray, causal: np.ndarray) -> np.ndarray:
+    """Row t of the result is the sum over the keys s <= t (causal[t, s]) of
+    wts[t, s] v_s. The keys after t take no part in row t's sum, not even as
+    0 * v_s, which a non-finite v_s would turn into NaN (the causal sum of
+    Section 2.2 and E.1 runs over the keys up to t only). Elements of V that
+    are not finite are therefore added one by one to the rows that see them."""
+    bad = ~np.isfinite(V)
+    if not bad.any():
+        return wts @ V
+    with np.errstate(invalid="ignore", over="ignore"):
+        num = wts @ np.where(bad, 0.0, V)
+        for s, i in zip(*np.nonzero(bad)):
+            rows = causal[:, s]
+            num[rows, i] += wts[rows, s] * V[s, i]
+    return num

@@ -649,6 +649,28 @@ def pin_prefill_bruteforce(E):
             if t in sel:
                 np.testing.assert_allclose(o_sel[0, t, h], want, rtol=1e-11, atol=1e-13)
 
+def pin_prefill_future_value_excluded(E):
+    """Causality with a non-finite value: row t depends only on the keys s <= t
+    (Section 2.2, E.1), so a non-finite element i of v_s leaves every row
+    t < s exactly as it is with a finite value there, and makes element i of
+    every row t >= s non-finite (its weight is positive) while the other
+    elements stay as they were."""
+    wl = tiny(25, n=1, lens=(150,), h_q=2, h_kv=1, d=8, dtype="f32", mode="learned")
+    q = W.trace_queries(wl, seed=10)
+    s_tok, i = 70, 5
+    page, row = int(wl.block_table[0, s_tok // 64]), s_tok % 64
+    wl.v_pages[page, 0, row, i] = 0.25
+    base = _prefill(E, wl, q)
+    for bad in (np.inf, -np.inf, np.nan):
+        wl.v_pages[page, 0, row, i] = bad
+        o = _prefill(E, wl, q)
+        assert np.array_equal(o[0, :s_tok], base[0, :s_tok])
+        assert not np.isfinite(o[0, s_tok:150, :, i]).any()
+        others = [c for c in range(wl.d) if c != i]
+        assert np.array_equal(o[0, s_tok:150][..., others], base[0, s_tok:150][..., others])
+    wl.v_pages[page, 0, row, i] = 0.25
+
+
 # --------------------------------------------------------------------------- thresholds
 def pin_threshold_closed_form(E):
     """tau~ = w.q + b - a (learned), c - a (calibrated): Sections 1, 4.7, D.1, G.1."""
@@ -877,6 +899,7 @@ ALL_PINS = [
     pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
     pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
+    pin_prefill_future_value_excluded,
     pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,
     pin_fp8_rounding_table, pin_fp8_matches_code_search, pin_fp8_bound_sound, pin_fp8_bruteforce,
     pin_subblock_bruteforce, pin_subblock_no_false_negatives, pin_pairblock_bruteforce,

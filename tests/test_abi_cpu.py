@@ -262,3 +262,55 @@ def test_prefill_rejects():
     assert call(c=cache(head_dim=96)) == _lib.ETA_ERR_UNSUPPORTED
     assert call(hq=8 * 16) == _lib.ETA_ERR_UNSUPPORTED                         # G = 16
     assert call(ss=seqs(num_seqs=65536 // 32 + 1)) == _lib.ETA_ERR_UNSUPPORTED  # grid rows
+
+
+def test_decode_rejects_records_of_4gib_or_more():
+    """The screen addresses the records it reads with 32-bit offsets: a record
+    array of 2^32 bytes or more is refused before any launch (it would wrap to
+    a small size and read zeros)."""
+    # 16-token blocks at d = 128: 524,288 pages x 8 KV heads x 4 slots x 256 B = 4 GiB
+    sub = dict(sub_block=16, mu_sub=FAKE * 17, radius_sub=FAKE * 18)
+    big = cache(num_pages=524288, **sub)
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=big, nbytes=1 << 40) == \
+        _lib.ETA_ERR_UNSUPPORTED
+    # one page fewer fits (the first error it meets is then the fake workspace size)
+    ok = cache(num_pages=524287, **sub)
+    assert decode_ex(_lib.ETA_PHASE_ALL, _lib.ETA_BOUND_GEOMETRIC_SUB, 0.0, c=ok, nbytes=16) == \
+        _lib.ETA_ERR_WORKSPACE_TOO_SMALL
+    # page records at d = 128: 2^24 (page, KV head) pairs are 4 GiB of centroids
+    assert decode(c=cache(num_pages=1 << 21), nbytes=1 << 40) == _lib.ETA_ERR_UNSUPPORTED
+    assert decode(c=cache(num_pages=(1 << 21) - 1), nbytes=16) == _lib.ETA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_binding_shape_checks():
+    """decode()'s shape checks (CPU tensors suffice: they run before any
+    pointer is taken)."""
+    import torch
+    from learned_threshold_block_amd import _decode_shapes
+    N, HQ, D = 2, 8, 128
+    lens = torch.zeros(N, dtype=torch.int32)
+    bt = torch.zeros(N, 4, dtype=torch.int32)
+    q = torch.zeros(N, HQ, D)
+    b = torch.zeros(HQ)
+    w = torch.zeros(HQ, D)
+    learned = _lib.ETA_TAU_LEARNED
+    assert _decode_shapes(D, lens, bt, q, learned, b, w) == (N, HQ, D)
+    assert _decode_shapes(D, lens, bt, q, _lib.ETA_TAU_CALIBRATED, b, None) == (N, HQ, D)
+    bad = [
+        dict(head_dim=64),                          # q's d differs from the cache's
+        dict(q=torch.zeros(N, HQ * D)),             # not 3-D
+        dict(lens=torch.zeros(N + 1, dtype=torch.int32)),
+        dict(lens=torch.zeros(N, 1, dtype=torch.int32)),
+        dict(bt=torch.zeros(N + 1, 4, dtype=torch.int32)),
+        dict(bt=torch.zeros(N * 4, dtype=torch.int32)),
+        dict(b=torch.zeros(HQ - 1)),
+        dict(b=torch.zeros(HQ + 1)),
+        dict(w=torch.zeros(HQ, D - 1)),
+        dict(w=torch.zeros(HQ - 1, D)),
+        dict(w=None),                               # learned mode without a predictor
+    ]
+    for kw in bad:
+        a = dict(head_dim=D, lens=lens, bt=bt, q=q, b=b, w=w)
+        a.update(kw)
+        with pytest.raises(ValueError):
+            _decode_shapes(a["head_dim"], a["lens"], a["bt"], a["q"], learned, a["b"], a["w"])

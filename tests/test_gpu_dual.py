@@ -138,4 +138,4 @@ def test_dual_requires_sigma():
     wl = W.make_workload("seq_32k", seq_lens=[640], h_q=4, h_kv=2, needles=0)
     dev = Dev(wl)
     with pytest.raises(eta.EtaError):
-        dev.decode(bound="dual")
+        dev.decode(bound="dual", bias=np.zeros(wl.h_q))

@@ -144,4 +144,4 @@ def test_fp8_requires_records():
     wl = W.make_workload("seq_32k", seq_lens=[640], h_q=4, h_kv=2, needles=0)
     dev = Dev(wl)
     with pytest.raises(eta.EtaError):
-        dev.decode(bound="geometric_fp8")
+        dev.decode(bound="geometric_fp8", bias=np.zeros(wl.h_q))

@@ -137,4 +137,4 @@ def test_quest_requires_box():
     wl = W.make_workload("seq_32k", seq_lens=[640], h_q=4, h_kv=2, needles=0)
     dev = Dev(wl)
     with pytest.raises(eta.EtaError):
-        dev.decode(bound="quest")
+        dev.decode(bound="quest", bias=np.zeros(wl.h_q))

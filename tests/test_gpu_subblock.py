@@ -146,7 +146,7 @@ def test_subblock_requires_records():
     wl = W.make_workload("seq_32k", seq_lens=[640], h_q=4, h_kv=2, needles=0)
     dev = Dev(wl)
     with pytest.raises(eta.EtaError):
-        dev.decode(bound="geometric_sub")
+        dev.decode(bound="geometric_sub", bias=np.zeros(wl.h_q))
 
 
 def test_pairblock_rescue():
@@ -179,3 +179,50 @@ def test_page_screen_after_subblock_decode(block):
     res = oracle_decode(wl, summaries=summ)
     check_sets_and_counts(wl, res, st)
     check_output(wl, res, o)
+
+
+def test_invalid_second_page_of_a_128_token_block_is_never_rescued():
+    """A 128-token block whose second page id is out of range is not a
+    complete block: the screen neither admits nor ranks it, so the top-1
+    rescue picks the best block among the valid ones, nothing reads the bad
+    page, and eta_stats reports ETA_ERR_DEVICE_DATA. Lengths are multiples of
+    128 and lwb = 0, so no block is forced, and every threshold lies above
+    every bound, so every head is rescued."""
+    block = 128
+    wl, summ = prepared("seq_32k", bound="geometric_sub", block=block, seq_lens=[64 * 16, 64 * 10], h_q=8, h_kv=2,
+                        d=128, paged=True)
+    wl.bias = np.full(wl.h_q, 1e3, dtype=np.float32)
+    res = oracle_decode(wl, summaries=summ, bound="geometric_sub", block=block)
+    assert res.rescued.all()
+    nb0 = int(wl.seq_lens[0]) // block
+    jb = int(np.argmax(res.ub[0, 0, :nb0]))  # the block head 0 of sequence 0 would get
+    dev = Dev(wl, sub_block=block)
+    dev.build()
+    bt_bad = dev.bt.clone()
+    bt_bad[0, 2 * jb + 1] = wl.num_pages + 100
+    dev.decode(bound="geometric_sub")
+    eta.decode(dev.cache, dev.seq_lens, bt_bad, dev.q, eta.ETA_TAU_LEARNED, torch.from_numpy(wl.bias).cuda(),
+               w=dev.w, out=dev.out, workspace=dev.ws, bound="geometric_sub")
+    torch.cuda.synchronize()
+    st = dev.stats(check=False)
+    assert st.status == eta.ETA_ERR_DEVICE_DATA
+    out = dev.out.cpu().numpy().astype(np.float64)
+    check_output(wl, res, out, heads=[(1, h) for h in range(wl.h_q)])
+    adm = st.admitted(res.admitted.shape[2])
+    qf = E.upcast(wl.q, wl.kv_dtype)
+    scale = 1.0 / np.sqrt(wl.d)
+    for h in range(wl.h_q):
+        ub = res.ub[0, h, :nb0].copy()
+        ub[jb] = -np.inf
+        best = int(np.argmax(ub))
+        gap = ub[best] - np.max(np.delete(ub, best))
+        assert gap > 1e-4, gap
+        want = np.zeros(adm.shape[2], dtype=bool)
+        want[best] = True
+        assert np.array_equal(adm[0, h], want), (h, np.flatnonzero(adm[0, h]), best)
+        g = h // wl.group
+        pages = [int(wl.block_table[0, 2 * best]), int(wl.block_table[0, 2 * best + 1])]
+        K = np.concatenate([E.upcast(wl.k_pages[p, g], wl.kv_dtype) for p in pages])
+        V = np.concatenate([E.upcast(wl.v_pages[p, g], wl.kv_dtype) for p in pages])
+        ref = E.filtered_attention(qf[0, h], K, V, res.tau[0, h], wl.beta, scale)
+        assert float(np.max(np.abs(out[0, h] - ref))) <= 2e-3

@@ -50,6 +50,7 @@ MUTANTS = {
                                    "hist += wt * np.bincount(bins[i, :t], minlength=num_bins)"),
     "calibration_search_strict": ("        if tail[mid] <= target:\n", "        if tail[mid] < target:\n"),
     "calibration_threshold_strict": ("np.count_nonzero(S[i, :t + 1] >= tau[i])", "np.count_nonzero(S[i, :t + 1] > tau[i])"),
+    "prefill_masked_value_enters": ("causal_weighted_sum(wts, V[:t1], causal) / wts.sum", "(wts @ V[:t1]) / wts.sum"),
     "prefill_excludes_diagonal": ("causal = np.arange(t1)[None, :] <= r[:, None]",
                                   "causal = np.arange(t1)[None, :] < r[:, None]"),
     "prefill_threshold_of_first_row": ("threshold(tau_mode, Q[t], None if w is None else w[h], b_or_c[h], a) for t in r",
