@@ -22,7 +22,8 @@
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless the comment says "host".
  *   - The caller owns all memory. The library allocates nothing and keeps no
- *     state between calls apart from a per-device launch-geometry cache.
+ *     state between calls apart from a per-device launch-geometry cache and
+ *     the per-device array that serves eta_decode_noalloc as its workspace.
  *     A decode workspace carries the previous call's per-die work weights
  *     and range timings to the next call on it; they steer only how the work
  *     is split, never what is computed.
@@ -205,6 +206,25 @@ eta_status eta_decode(const eta_cache* cache, const eta_seqs* seqs, const void* 
                       int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
                       float a, float beta, int lwb, int block_size, float* out,
                       void* workspace, size_t ws_bytes, eta_stream_t stream);
+
+/* Bytes of the device array that eta_decode_noalloc uses as its workspace. */
+#define ETA_NOALLOC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/* eta_decode for callers that cannot allocate device memory (code under stream
+ * capture, tight serving loops, hosts that forbid allocation): the same
+ * arguments without the workspace, which is instead a fixed array of
+ * ETA_NOALLOC_WORKSPACE_BYTES in the library's device memory. Each GPU holds its
+ * own copy from its first call until the process ends. The call allocates
+ * nothing. Sizes whose workspace (eta_decode_workspace_size) exceeds the array
+ * return ETA_ERR_WORKSPACE_TOO_SMALL before any launch; every other argument is
+ * checked as by eta_decode. All calls on one GPU share its array: calls that
+ * overlap in time on one GPU (on different streams, or from several threads
+ * without ordering) race and give wrong results. Counts of these calls are not
+ * available through eta_stats. */
+eta_status eta_decode_noalloc(const eta_cache* cache, const eta_seqs* seqs, const void* q,
+                              int num_q_heads, int tau_mode, const float* w, const float* b_or_c,
+                              float a, float beta, int lwb, int block_size, float* out,
+                              eta_stream_t stream);
 
 /* Block screen of a decode step (Sections 3.1 and F.1).
  *   ETA_BOUND_GEOMETRIC : score s (q . mu + ||q|| R), an upper bound on the

@@ -19,7 +19,7 @@ from ._lib import (  # noqa: F401
     ETA_BF16, ETA_BOUND_DUAL, ETA_BOUND_GEOMETRIC, ETA_BOUND_GEOMETRIC_FP8, ETA_BOUND_GEOMETRIC_SUB, ETA_BOUND_QUEST, ETA_ERR_DEVICE_DATA,
     ETA_FP8_E4M3, ETA_FP8_E5M2, ETA_ERR_HIP, ETA_ERR_INVALID_ARGUMENT, ETA_ERR_UNSUPPORTED,
     ETA_ERR_WORKSPACE_TOO_SMALL, ETA_F32, ETA_OK, ETA_PHASE_ALL, ETA_PHASE_ATTEND, ETA_PHASE_MERGE, ETA_PHASE_SCREEN,
-    ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
+    ETA_NOALLOC_WORKSPACE_BYTES, ETA_TAU_CALIBRATED, ETA_TAU_LEARNED, EtaError, status_string,
 )
 
 BLOCK = 64
@@ -261,6 +261,30 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
         _check(_lib.lib().eta_decode_ex(ph, ctypes.byref(opts), *args), "eta_decode_ex")
     else:
         raise ValueError(f"unknown bound {bound!r}")
+    return out
+
+
+def decode_noalloc(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None, a: float = 0.0,
+                   beta: float = 5.0, lwb: int = 0, out=None, stream=None) -> torch.Tensor:
+    """eta_decode_noalloc: one decode step (geometric screen) whose workspace
+    is the library's own fixed device array (ETA_NOALLOC_WORKSPACE_BYTES per
+    GPU), so the call allocates nothing; `out` [num_seqs][H_Q][d] float32 must
+    then be given. Calls that overlap in time on one GPU race."""
+    dev = cache.k_pages.device
+    _need(q, "q", cache.k_pages.dtype, dev)
+    _need(b_or_c, "b_or_c", torch.float32, dev)
+    if w is not None:
+        _need(w, "w", torch.float32, dev)
+    N, HQ, D = _decode_shapes(cache.head_dim, seq_lens, block_table, q, tau_mode, b_or_c, w)
+    if out is None:
+        raise ValueError("decode_noalloc needs a preallocated out tensor")
+    _need(out, "out", torch.float32, dev)
+    if tuple(out.shape) != (N, HQ, D):
+        raise ValueError(f"out must be [num_seqs][H_Q][d] = {(N, HQ, D)}, got {tuple(out.shape)}")
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    _check(_lib.lib().eta_decode_noalloc(ctypes.byref(c), ctypes.byref(s), _ptr(q), HQ, int(tau_mode), _ptr(w),
+                                         _ptr(b_or_c), float(a), float(beta), int(lwb), BLOCK, _ptr(out),
+                                         _stream(stream)), "eta_decode_noalloc")
     return out
 
 

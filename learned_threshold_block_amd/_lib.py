@@ -33,12 +33,14 @@ ETA_BOUND_GEOMETRIC_FP8 = 3
 ETA_BOUND_GEOMETRIC_SUB = 4
 ETA_FP8_E4M3 = 0
 ETA_FP8_E5M2 = 1
+ETA_NOALLOC_WORKSPACE_BYTES = 32 << 20
 
 EXPORTS = (
     "eta_build_block_summaries",
     "eta_append_kv",
     "eta_decode_workspace_size",
     "eta_decode",
+    "eta_decode_noalloc",
     "eta_decode_phase",
     "eta_decode_ex",
     "eta_calibrate",
@@ -123,6 +125,8 @@ def lib() -> ctypes.CDLL:
     dec = [cp, sp, P, I, I, P, P, F, F, I, I, P, P, S, P]
     L.eta_decode.argtypes = dec
     L.eta_decode.restype = I
+    L.eta_decode_noalloc.argtypes = dec[:12] + [P]
+    L.eta_decode_noalloc.restype = I
     L.eta_decode_phase.argtypes = [I] + dec
     L.eta_decode_phase.restype = I
     L.eta_decode_ex.argtypes = [I, ctypes.POINTER(EtaScreenOptsC)] + dec

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 LIB = os.path.join(HERE, "libeta.so")
-SOURCES = ["eta_summary.hip", "eta_screen.hip", "eta_attend.hip", "eta_calib.hip", "eta_prefill.hip", "eta_host.cpp"]
+SOURCES = ["eta_summary.hip", "eta_screen.hip", "eta_attend.hip", "eta_calib.hip", "eta_prefill.hip", "eta_noalloc.hip", "eta_host.cpp"]
 ARCH = os.environ.get("ETA_OFFLOAD_ARCH", "gfx950")
 
 HIP_FLAGS = [
