@@ -54,6 +54,9 @@ def parse():
                         "and carries no stored traffic)")
     p.add_argument("--no-dense", action="store_true", help="skip the dense comparator")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    p.add_argument("--no-others", action="store_true",
+                   help="time only the chosen workload (by default the 512K headline run also times "
+                        + ", ".join(OTHER_WORKLOADS) + ")")
     p.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work to time")
     p.add_argument("--sweep", action="store_true", help="also time batch_4x128k at 10/38/70/100%% density")
     p.add_argument("--bound", default="geometric",
@@ -642,6 +645,74 @@ def host_cpu_model():
     return "unknown"
 
 
+def describe(S, workload, seq_len, bound="geometric", z=2.0, sub_block=16):
+    """The workload's name for the JSON line: shapes, dtype, thresholds, screen."""
+    wl = S.wl
+    base = ({"seq_32k": "1 seq x 32768 ctx", "batch_4x128k": "4 seq x 131072 ctx",
+             "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[workload]
+            if seq_len is None else f"{wl.n_seqs} seq x {seq_len} ctx")
+    dens = "per-head density U[0.05, 0.90]" if workload == "ragged_16" else \
+        f"target per-head density {float(np.mean(wl.target_density)):.2f}"
+    return (base + f", GQA {wl.h_q}/{wl.h_kv}, d={wl.d}, {wl.kv_dtype} paged KV (64-token pages), "
+            + f"{wl.tau_mode} thresholds, {dens}, {len(wl.needles)} needle keys"
+            + {"geometric": "", "dual": f", dual screen z={z:g}", "quest": ", comparator box-bound screen",
+               "geometric_fp8": ", geometric screen over E4M3 records",
+               "geometric_sub": f", geometric screen on {sub_block}-token blocks"}[bound])
+
+
+def measure(S, workload, steps, warmup, bound="geometric", seq_len=None):
+    """Step time, densities, bandwidths, phase times and the attend kernel's
+    roofline of one calibrated workload."""
+    st, dens_head, dens_union = S.densities()
+    kv_bytes, all_bytes = S.step_bytes(st)
+    log(f"{workload}: density per-head {dens_head:.3f} union {dens_union:.3f}; union K/V {kv_bytes / 1e9:.3f} GB")
+    us = time_steps(S, steps, warmup)
+    ph = time_phases(S, steps)
+    log(f"{workload}: step {us:.1f} us; phases screen / attend+merge {ph[0]:.1f} / {ph[1]:.1f} us")
+    wl = S.wl
+    esz = 2 if wl.kv_dtype == "bf16" else 4
+    U = int(st.union_per_kv.sum())  # union blocks in the screen's block size
+    # K/V rows of the union's blocks (kv_bytes follows the screen's block size),
+    # one 8-byte entry per block, the queries
+    attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * wl.d * esz
+    attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
+    key = traffic_key(workload, float(np.mean(wl.target_density)), bound, seq_len)
+    return {
+        "us_per_step": round(us, 2),
+        "density_per_head": round(dens_head, 4),
+        "density_union": round(dens_union, 4),
+        "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
+        "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),
+        "phase_us": {"screen": round(float(ph[0]), 2), "attend_and_merge": round(float(ph[1]), 2)},
+        "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": stored_traffic(key),
+                     "kernel": "k_attend", "bytes_per_launch": attend_bytes},
+    }
+
+
+# The other configurations of the benchmark's workload set, timed after the
+# headline one in the default run: 4 x 128K (the metric's 128K context, config
+# with calibrated per-head constants at 38% per-head density), one 32K
+# sequence, and 16 ragged sequences on a paged cache in random page order.
+OTHER_WORKLOADS = ("batch_4x128k", "seq_32k", "ragged_16")
+
+
+def other_workloads(steps, warmup):
+    import torch
+
+    out = {}
+    for name in OTHER_WORKLOADS:
+        S = Setup(name)
+        S.calibrate()
+        m = measure(S, name, steps, warmup)
+        m["config"] = describe(S, name, None)
+        m["kv_copies_rotated"] = len(S.caches)
+        out[name] = m
+        del S
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -669,26 +740,12 @@ def main():
 
     S = Setup(args.workload, args.density, args.bound, args.z, args.sub_block, args.seq_len)
     S.calibrate()
-    st, dens_head, dens_union = S.densities()
-    kv_bytes, all_bytes = S.step_bytes(st)
-    log(f"density per-head {dens_head:.3f} union {dens_union:.3f}; union K/V {kv_bytes / 1e9:.3f} GB")
-
-    us = time_steps(S, args.steps, args.warmup)
-    ph = time_phases(S, args.steps)
-    log(f"step {us:.1f} us; phases screen / attend+merge {ph[0]:.1f} / {ph[1]:.1f} us")
+    m = measure(S, args.workload, args.steps, args.warmup, args.bound, args.seq_len)
+    us = m["us_per_step"]
     wl = S.wl
-    esz = 2 if wl.kv_dtype == "bf16" else 4
-    U = int(st.union_per_kv.sum())  # union blocks in the screen's block size
-    G, D = wl.group, wl.d
-    # K/V rows of the union's blocks (kv_bytes follows the screen's block size),
-    # one 8-byte entry per block, the queries
-    attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * D * esz
-    attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
-    workload_key = traffic_key(args.workload, float(np.mean(wl.target_density)), args.bound, args.seq_len)
-    traffic = stored_traffic(workload_key)
     result = {
         "metric": "ETA decode us/step + achieved HBM GB/s at 128K/512K ctx, ~38% block density",
-        "value": round(us, 2),
+        "value": us,
         "unit": "us/step",
         "n_gpus": 1,
         "steps": args.steps,
@@ -700,29 +757,18 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": ({"seq_32k": "1 seq x 32768 ctx", "batch_4x128k": "4 seq x 131072 ctx",
-                          "seq_512k": "1 seq x 524288 ctx", "ragged_16": "16 ragged seqs 4K-256K"}[args.workload]
-                         if args.seq_len is None else f"{wl.n_seqs} seq x {args.seq_len} ctx")
-                        + f", GQA {wl.h_q}/{wl.h_kv}, d={D}, {wl.kv_dtype} paged KV (64-token pages), "
-                        + f"{wl.tau_mode} thresholds, target per-head density "
-                        + f"{float(np.mean(wl.target_density)):.2f}, {len(wl.needles)} needle keys"
-                        + {"geometric": "", "dual": f", dual screen z={args.z:g}",
-                           "quest": ", comparator box-bound screen",
-                           "geometric_fp8": ", geometric screen over E4M3 records",
-                           "geometric_sub": f", geometric screen on {args.sub_block}-token blocks"}[args.bound],
+            "workload": describe(S, args.workload, args.seq_len, args.bound, args.z, args.sub_block),
             "kv_dtype": wl.kv_dtype,
             "screen": f"dual z={args.z:g}" if args.bound == "dual" else args.bound,
             "seq_lens_total": int(wl.seq_lens.sum()),
-            "density_per_head": round(dens_head, 4),
-            "density_union": round(dens_union, 4),
+            "density_per_head": m["density_per_head"],
+            "density_union": m["density_union"],
             "kv_copies_rotated": len(S.caches),
         },
-        "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
-        "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),
-        "phase_us": {"screen": round(float(ph[0]), 2), "attend_and_merge": round(float(ph[1]), 2)},
-        "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "k_attend", "bytes_per_launch": attend_bytes},
+        "achieved_gbs_union_kv": m["achieved_gbs_union_kv"],
+        "achieved_gbs_all_bytes": m["achieved_gbs_all_bytes"],
+        "phase_us": m["phase_us"],
+        "roofline": m["roofline"],
     }
     if not args.no_dense:
         dense_bias = torch.full((wl.h_q,), -math.inf, device="cuda")
@@ -745,6 +791,12 @@ def main():
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(S, args.cpu_budget)
         log(f"cpu baseline {result['cpu_baseline']['value'] / 1e3:.1f} ms/step")
+    if not args.no_others and args.workload == "seq_512k" and args.seq_len is None and args.bound == "geometric" \
+            and args.density is None:
+        del S
+        torch.cuda.empty_cache()
+        result["workloads"] = other_workloads(max(10, args.steps // 2), min(args.warmup, 5))
+        S = None
     if args.sweep:
         del S
         torch.cuda.empty_cache()

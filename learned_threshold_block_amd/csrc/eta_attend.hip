@@ -72,13 +72,17 @@ __device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2*
   return ev;
 }
 
-// Claim of kClaim consecutive entries of the workgroup's current part: through
-// an LDS counter (the fastest wavefronts take the most entries), or, with
-// `fixed`, the wavefront's static share (claims wave, wave + NW, ... counted
-// from e0), which makes the result independent of timing.
+// Claim of kClaim consecutive entries of the workgroup's current part. The
+// first claim of every wavefront is static (entries e0 + wave kClaim ..), so
+// no wavefront waits for the counter to be set up; later ones come from an
+// LDS counter that starts at e0 + nw kClaim (the fastest wavefronts take the
+// most entries), or, with `fixed`, follow the static pattern (claims wave,
+// wave + nw, ... counted from e0), which makes the result independent of
+// timing.
 __device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nclaim, int wave, int nw,
                                          int e0) {
-  if (fixed) return e0 + (nclaim++ * nw + wave) * kClaim;
+  const int c = nclaim++;
+  if (fixed || c == 0) return e0 + (c * nw + wave) * kClaim;
   int v = 0;
   if (lane == 0) v = atomicAdd(ctr, kClaim);
   return __builtin_amdgcn_readfirstlane(v);
@@ -87,90 +91,101 @@ __device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nc
 // Merge of one segment's partials into the output, by the workgroup that
 // completed the segment: for each of its G heads,
 // o = sum_p e^{m_p - M} acc_p / sum_p e^{m_p - M} l_p over the partial slots
-// p = kf + s .. kl + s. Thread (group pg, head h, float4 column group cg)
-// loads the partials pg, pg + PG, ... (kMergeBatch of them in flight) and
-// folds them with an online maximum; the PG groups are then combined in a
-// fixed order, so the result does not depend on timing. NaN when nothing was
-// accumulated.
-constexpr int kMergeBatch = 16;
+// p = kf + s .. kl + s. NG threads take one segment: thread (group pg, head
+// h, float4 column group cg) loads the partials pg, pg + PG, ...
+// (kMergeBatch of them in flight: 48 partials in one round at 256 threads and 128 outputs) and folds them with an online maximum;
+// the PG groups are then combined in a fixed order, so the result does not
+// depend on timing. NaN when nothing was accumulated. The partials are read
+// with device-coherent loads (they were written by workgroups on any die).
+constexpr int kMergeBatch = 24;
 
-template <int D, int G, int NTH>
-__device__ void merge_segment(const Ws& ws, float* out, int s, int n, int g, int HQ, int kf, int kl) {
-  constexpr int CG = D / 4;                       // float4 column groups
-  constexpr int OUTS = G * CG;                    // (head, column group) outputs
-  static_assert(OUTS <= NTH, "one thread per output at least");
-  constexpr int PG = NTH / OUTS;                  // thread groups splitting the partials
-  __shared__ float4 red_a[PG][OUTS];
-  __shared__ float2 red_ml[PG][OUTS];
-  const int tid = threadIdx.x;
-  const int o = tid % OUTS, pg = tid / OUTS;
-  const bool act = pg < PG;
-  const int h = o / CG, cg = o % CG;
+template <int D, int G, int NG>
+struct MergeLds {
+  static constexpr int CG = D / 4;         // float4 column groups
+  static constexpr int OUTS = G * CG;      // (head, column group) outputs
+  static_assert(OUTS <= NG, "one thread per output at least");
+  static constexpr int PG = NG / OUTS;     // thread groups splitting the partials
+  float4 a[PG][OUTS];
+  float2 ml[PG][OUTS];
+};
+
+// Part 1 (thread t < NG of the merge): fold this thread's share of the partials into M.a/M.ml.
+template <int D, int G, int NG>
+__device__ void merge_fold(const Ws& ws, MergeLds<D, G, NG>& M, int s, int kf, int kl, int t) {
+  using ML = MergeLds<D, G, NG>;
+  const int o = t % ML::OUTS, pg = t / ML::OUTS;
+  if (pg >= ML::PG) return;
+  const int h = o / ML::CG, cg = o % ML::CG;
   const int np = kl - kf + 1;
   const int64_t slot0 = (int64_t)kf + s;
-  float M = -__builtin_inff(), l = 0.f;
+  float Mx = -__builtin_inff(), l = 0.f;
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (act) {
-    for (int p0 = pg; p0 < np; p0 += kMergeBatch * PG) {
-      float4 v[kMergeBatch];
-      float2 ml[kMergeBatch];
+  for (int p0 = pg; p0 < np; p0 += kMergeBatch * ML::PG) {
+    float4 v[kMergeBatch];
+    float2 ml[kMergeBatch];
 #pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const int p = p0 + j * PG;
-        const int64_t sl = slot0 + (p < np ? p : 0);
-        v[j] = *(const float4*)&ws.part_acc[(sl * G + h) * D + 4 * cg];
-        ml[j] = *(const float2*)&ws.part_ml[(sl * G + h) * 2];
-        if (p >= np) ml[j].x = -__builtin_inff();
-      }
-      float Mb = M;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j].x);
-      if (Mb == -__builtin_inff()) continue;
-      const float sc = M == -__builtin_inff() ? 0.f : fast_exp(M - Mb);
-      l *= sc;
-      a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
-      M = Mb;
-#pragma unroll
-      for (int j = 0; j < kMergeBatch; ++j) {
-        const float wgt = ml[j].x == -__builtin_inff() ? 0.f : fast_exp(ml[j].x - M);
-        l = fmaf(wgt, ml[j].y, l);
-        a.x = fmaf(wgt, v[j].x, a.x);
-        a.y = fmaf(wgt, v[j].y, a.y);
-        a.z = fmaf(wgt, v[j].z, a.z);
-        a.w = fmaf(wgt, v[j].w, a.w);
-      }
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const int p = p0 + j * ML::PG;
+      const int64_t sl = slot0 + (p < np ? p : 0);
+      v[j] = load_agent4(&ws.part_acc[(sl * G + h) * D + 4 * cg]);
+      ml[j] = load_agent2(&ws.part_ml[(sl * G + h) * 2]);
+      if (p >= np) ml[j].x = -__builtin_inff();
     }
-    red_a[pg][o] = a;
-    red_ml[pg][o] = make_float2(M, l);
+    float Mb = Mx;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) Mb = fmaxf(Mb, ml[j].x);
+    if (Mb == -__builtin_inff()) continue;
+    const float sc = Mx == -__builtin_inff() ? 0.f : fast_exp(Mx - Mb);
+    l *= sc;
+    a.x *= sc; a.y *= sc; a.z *= sc; a.w *= sc;
+    Mx = Mb;
+#pragma unroll
+    for (int j = 0; j < kMergeBatch; ++j) {
+      const float wgt = ml[j].x == -__builtin_inff() ? 0.f : fast_exp(ml[j].x - Mx);
+      l = fmaf(wgt, ml[j].y, l);
+      a.x = fmaf(wgt, v[j].x, a.x);
+      a.y = fmaf(wgt, v[j].y, a.y);
+      a.z = fmaf(wgt, v[j].z, a.z);
+      a.w = fmaf(wgt, v[j].w, a.w);
+    }
   }
-  __syncthreads();
-  if (pg == 0) {
-    float Mt = -__builtin_inff();
+  M.a[pg][o] = a;
+  M.ml[pg][o] = make_float2(Mx, l);
+}
+
+// Part 2 (after a workgroup barrier): combine the groups and write the output.
+template <int D, int G, int NG>
+__device__ void merge_write(const Ws& ws, const MergeLds<D, G, NG>& M, float* out, int s, int n, int g, int HQ,
+                            int t) {
+  using ML = MergeLds<D, G, NG>;
+  const int o = t % ML::OUTS, pg = t / ML::OUTS;
+  if (pg != 0) return;
+  const int h = o / ML::CG, cg = o % ML::CG;
+  float Mt = -__builtin_inff();
 #pragma unroll
-    for (int q = 0; q < PG; ++q) Mt = fmaxf(Mt, red_ml[q][o].x);
-    float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-    float lt = 0.f;
+  for (int q = 0; q < ML::PG; ++q) Mt = fmaxf(Mt, M.ml[q][o].x);
+  float4 tt = make_float4(0.f, 0.f, 0.f, 0.f);
+  float lt = 0.f;
 #pragma unroll
-    for (int q = 0; q < PG; ++q) {
-      const float2 mq = red_ml[q][o];
-      const float wq = mq.x == -__builtin_inff() ? 0.f : fast_exp(mq.x - Mt);
-      const float4 u = red_a[q][o];
-      lt = fmaf(wq, mq.y, lt);
-      t.x = fmaf(wq, u.x, t.x);
-      t.y = fmaf(wq, u.y, t.y);
-      t.z = fmaf(wq, u.z, t.z);
-      t.w = fmaf(wq, u.w, t.w);
-    }
-    float4 r;
-    if (lt > 0.f) {
-      r = make_float4(t.x / lt, t.y / lt, t.z / lt, t.w / lt);
-    } else {
-      const float nan = __builtin_nanf("");
-      r = make_float4(nan, nan, nan, nan);
-    }
-    *(float4*)&out[((int64_t)n * HQ + g * G + h) * D + 4 * cg] = r;
+  for (int q = 0; q < ML::PG; ++q) {
+    const float2 mq = M.ml[q][o];
+    const float wq = mq.x == -__builtin_inff() ? 0.f : fast_exp(mq.x - Mt);
+    const float4 u = M.a[q][o];
+    lt = fmaf(wq, mq.y, lt);
+    tt.x = fmaf(wq, u.x, tt.x);
+    tt.y = fmaf(wq, u.y, tt.y);
+    tt.z = fmaf(wq, u.z, tt.z);
+    tt.w = fmaf(wq, u.w, tt.w);
   }
-  if (tid == 0) ws.seg_done[s] = 0;  // ready for the next decode
+  float4 r;
+  if (lt > 0.f) {
+    r = make_float4(tt.x / lt, tt.y / lt, tt.z / lt, tt.w / lt);
+  } else {
+    const float nan = __builtin_nanf("");
+    r = make_float4(nan, nan, nan, nan);
+  }
+  *(float4*)&out[((int64_t)n * HQ + g * G + h) * D + 4 * cg] = r;
+  if (t == 0) __hip_atomic_store(&ws.seg_done[s], (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Wavefronts per attend workgroup: eight (two per SIMD, one workgroup per CU)
@@ -196,7 +211,11 @@ __device__ __forceinline__ uint32_t block_union(uint32_t sw, int sb) {
 // entry carries a word of per-head block bits (bit q G + h); a head attends
 // only to the rows of its own blocks, and rows of blocks that no head of the
 // group admitted are not loaded.
-template <typename T, int D, int G, bool SUBB>
+// ALL: every segment's tile prefix, used-tile count and union count fit in
+// LDS (kSegLds ints); they are then read once in the first round.
+constexpr int kSegLds = 12288;
+
+template <typename T, int D, int G, bool SUBB, bool ALL>
 __global__ __launch_bounds__((64 * attend_waves<T, D, G>()))
 __attribute__((amdgpu_waves_per_eu((attend_waves<T, D, G>() / 4), (attend_waves<T, D, G>() / 4))))
 void k_attend(AttendArgs A) {
@@ -219,15 +238,36 @@ void k_attend(AttendArgs A) {
   __shared__ int ctr_lds;
   __shared__ int scan_lds[NW];
   __shared__ int pick_lds[3];
-  __shared__ int last_lds;
   const int NT = A.d.NT;
 
-  // ---- the work split, from the segments' union counts: Utot entries in
-  //      W' = min(grid, Utot) ranges weighted per die class; this workgroup
-  //      takes range k (one load round trip when there are at most NTH segments)
-  int wts[kXcdClasses];
-  load_weights(A.ws.xcd_w, A.p.deterministic, wts);
+  // ---- round 1: the segments' union counts (the work split needs them all)
+  //      and, when they fit in LDS, every segment's tile prefix, used-tile
+  //      count and union count, so that the first segment's entries can be
+  //      located without another round trip
+  __shared__ int seg_lds[ALL ? kSegLds : 1];
+  const int rowlen = NT + 2;
+  constexpr bool all_lds = ALL;  // the host checked S (NT + 4) <= kSegLds
+  // (lane x of wavefront 0 loads the weight of die class x: a lane-dependent
+  // load, which the compiler does not move to scalar registers at once, so
+  // nothing waits for it before the other loads are issued)
+  __shared__ int w_lds[kXcdClasses];
   const int v0 = (int)threadIdx.x < S ? A.ws.seg_U[threadIdx.x] : 0;
+  const int wv = (int)threadIdx.x < kXcdClasses ? A.ws.xcd_w[threadIdx.x] : 0;
+  if constexpr (ALL) {  // [S][NT + 2] tile prefixes, then [S] used tiles, then [S] union counts
+    // loaded straight into LDS (lane l of a wavefront's 64-element chunk
+    // writes element l): no registers, no wait until the scan's barrier, and
+    // a short loop instead of a long unrolled one
+    const int ntile = S * rowlen;
+    for (int c = wave * 64; c < ntile; c += NTH)
+      if (c + lane < ntile) __builtin_amdgcn_global_load_lds(A.ws.tile_off + c + lane, seg_lds + c, 4, 0, 0);
+    for (int c = wave * 64; c < S; c += NTH)
+      if (c + lane < S) {
+        __builtin_amdgcn_global_load_lds(A.ws.seg_ntn + c + lane, seg_lds + ntile + c, 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(A.ws.seg_U + c + lane, seg_lds + ntile + S + c, 4, 0, 0);
+      }
+  }
+  if ((int)threadIdx.x < kXcdClasses) w_lds[threadIdx.x] = clamp_weight(wv, A.p.deterministic);
+  wait_stores();  // the loads into LDS above have landed before the scan's first barrier
   int tot0;
   const int incl0 = block_incl_scan<NW>(v0, &tot0, scan_lds);
   int Utot = tot0;
@@ -246,17 +286,22 @@ void k_attend(AttendArgs A) {
   if (k >= Wp) return;
   int64_t lo, hi;
   {
+    int wts[kXcdClasses];
+#pragma unroll
+    for (int x = 0; x < kXcdClasses; ++x) wts[x] = w_lds[x];  // written before the scan's barriers
     RangeSplit sp;
     sp.init(Utot, Wp, wts);
     lo = sp.B(k);
     hi = sp.B(k + 1);
   }
   const int n_entries = (int)(hi - lo);
-  // the segment holding entry lo, its first entry and its count
+  // the segment holding entry lo, its first entry and its count; the thread
+  // that finds it also sets up the claim counter of that segment's part
   if (v0 > 0 && incl0 - v0 <= lo && lo < incl0) {
     pick_lds[0] = threadIdx.x;
     pick_lds[1] = incl0 - v0;
     pick_lds[2] = v0;
+    ctr_lds = (int)(lo - (incl0 - v0)) + NW * kClaim;
   }
   if (lo < hi && lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
     int carry = tot0;
@@ -269,6 +314,7 @@ void k_attend(AttendArgs A) {
         pick_lds[0] = i;
         pick_lds[1] = incl - v;
         pick_lds[2] = v;
+        ctr_lds = (int)(lo - (incl - v)) + NW * kClaim;
       }
       carry += tot;
     }
@@ -281,6 +327,7 @@ void k_attend(AttendArgs A) {
   int Us = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[2] : 0);
   const int s_first = s, P_first = P, U_first = Us;
   const int64_t lo_first = lo;
+  bool first_part = true;
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -295,7 +342,7 @@ void k_attend(AttendArgs A) {
     while (lo >= (int64_t)P + Us) {  // next segment with entries
       P += Us;
       ++s;
-      Us = A.ws.seg_U[s];
+      Us = all_lds ? seg_lds[S * rowlen + S + s] : A.ws.seg_U[s];
     }
     const int e0 = (int)(lo - P);
     const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
@@ -333,14 +380,24 @@ void k_attend(AttendArgs A) {
     }
 
     // the segment's tile prefix (to locate entries in the per-tile lists), and
-    // the part's claim counter
-    const int ntn = A.ws.seg_ntn[s];
-    {  // the whole row, so that the loads do not wait for ntn
-      const int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
-      for (int v = threadIdx.x; v < NT + 2; v += NTH) toff_lds[v] = toff[v];
+    // the part's claim counter (for the first part, set up with the pick)
+    const int* toffp = toff_lds;
+    int ntn;
+    if constexpr (ALL) {
+      toffp = seg_lds + s * rowlen;
+      ntn = seg_lds[S * rowlen + s];
+      if (!first_part) {
+        if (threadIdx.x == 0) ctr_lds = e0 + NW * kClaim;
+        __syncthreads();
+      }
+    } else {
+      ntn = A.ws.seg_ntn[s];
+      const int32_t* toff = A.ws.tile_off + (int64_t)s * rowlen;  // the whole row: the loads do not wait for ntn
+      for (int v = threadIdx.x; v < rowlen; v += NTH) toff_lds[v] = toff[v];
+      if (threadIdx.x == 0) ctr_lds = e0 + NW * kClaim;
+      __syncthreads();
     }
-    if (threadIdx.x == 0) ctr_lds = e0;
-    __syncthreads();
+    first_part = false;
     const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
     const uint32_t* tsubs = SUBB ? A.ws.tile_sub + (int64_t)s * (NT + 1) * kTile : nullptr;
 
@@ -352,10 +409,7 @@ void k_attend(AttendArgs A) {
     int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
     if (bc > 0) {
       uint32_t ews = 0, ewsn = 0;
-      int2 ev = resolve_entries(toff_lds, tents, ntn, NT, c0, bc, lane, tsubs, &ews);
-      const int c1 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
-      int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
-      int2 evn = resolve_entries(toff_lds, tents, ntn, NT, c1, bcn, lane, tsubs, &ewsn);
+      int2 ev = resolve_entries(toffp, tents, ntn, NT, c0, bc, lane, tsubs, &ews);
       int it = 0;
       int page_nx = __builtin_amdgcn_readlane(ev.x, 0);
       int jm_nx = __builtin_amdgcn_readlane(ev.y, 0);
@@ -372,6 +426,10 @@ void k_attend(AttendArgs A) {
             kr[i][c] = (!SUBB || ((ub >> ((RPI * i) >> lbs)) & 1u)) ? load_stream16(kt + loff[c] + i * RPI * D)
                                                                    : make_uint4(0, 0, 0, 0);
       }
+      // the next claim is resolved while the first tile's keys are in flight
+      const int c1 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
+      int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
+      int2 evn = resolve_entries(toffp, tents, ntn, NT, c1, bcn, lane, tsubs, &ewsn);
       for (;;) {
         const int cur_page = page_nx, cur_jm = jm_nx;
         const uint32_t cur_sw = sw_nx;
@@ -395,7 +453,7 @@ void k_attend(AttendArgs A) {
           if (bc > 0) {
             const int c2 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
             bcn = c2 < e1 ? min(kClaim, e1 - c2) : 0;
-            evn = resolve_entries(toff_lds, tents, ntn, NT, c2, bcn, lane, tsubs, &ewsn);
+            evn = resolve_entries(toffp, tents, ntn, NT, c2, bcn, lane, tsubs, &ewsn);
           } else {
             has_next = false;
           }
@@ -567,12 +625,9 @@ void k_attend(AttendArgs A) {
         float a = 0.f;
 #pragma unroll
         for (int w = 0; w < NW; ++w) a = fmaf(sc[w], acc_lds[w][h][dd], a);
-        pa[dd] = a;
+        store_agent(pa + dd, a);
       }
-      if (lane == 0) {
-        A.ws.part_ml[(piece * G + h) * 2] = M;
-        A.ws.part_ml[(piece * G + h) * 2 + 1] = Lsum;
-      }
+      if (lane == 0) store_agent2(A.ws.part_ml + (piece * G + h) * 2, M, Lsum);
     }
     __syncthreads();
     lo = (int64_t)P + e1;
@@ -581,41 +636,81 @@ void k_attend(AttendArgs A) {
   // ---- arrivals: for every segment the range touched, add its entries to the
   //      segment's count; the workgroup that completes a segment merges the
   //      segment's partials (slots kf + s .. kl + s) into the output. The
-  //      workgroup barrier orders every wavefront's partial stores before
-  //      thread 0's device-scope release and counts; a merging workgroup
-  //      acquires at device scope after its count.
+  //      partials were written with device-coherent stores; every wavefront
+  //      waits for its stores to complete and the workgroup barrier orders
+  //      that before thread 0's counts. A merging workgroup reads the
+  //      partials with device-coherent loads after its count returned. No
+  //      cache maintenance of the dies' L2s is needed.
+  wait_stores();
   __syncthreads();
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   {
+    // The segments this range touched, up to 64 at a time: wave 0's lane j
+    // adds the entry count of the j-th of them with one 64-bit add, which
+    // also carries, from the ranges holding the segment's first and last
+    // entries, their indices. Every count is added before any merge starts,
+    // so a merge here never delays another segment's completion; two
+    // completed segments are merged side by side when the workgroup has the
+    // threads for it.
+    constexpr int NG2 = 2 * (G * D / 4) <= NTH ? NTH / 2 : NTH;  // threads per merge (one per output at least)
+    constexpr int NPAR = NTH / NG2;                                               // merges side by side
+    __shared__ MergeLds<D, G, NG2> mg[NPAR];
+    __shared__ int done_s[64], done_kf[64], done_kl[64];
+    __shared__ int ndone_lds;
     int s2 = s_first, P2 = P_first, U2 = U_first;
     int64_t x = lo_first;
     while (x < hi) {
-      while (x >= (int64_t)P2 + U2) {
-        P2 += U2;
-        ++s2;
-        U2 = A.ws.seg_U[s2];
-      }
-      const int c0 = (int)(x - P2);
-      const int c1 = (int)((hi < (int64_t)P2 + U2 ? hi : (int64_t)P2 + U2) - P2);
-      if (threadIdx.x == 0) {
-        // one 64-bit add carries the entry count and, from the ranges that
-        // hold the segment's first and last entries, their indices
-        const uint64_t add = (uint64_t)(c1 - c0) + (c0 == 0 ? (uint64_t)k << 32 : 0ull) +
-                             (c1 == U2 ? (uint64_t)k << 48 : 0ull);
-        const uint64_t tot =
-            __hip_atomic_fetch_add(&A.ws.seg_done[s2], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
-        const bool last = (uint32_t)tot == (uint32_t)U2;
-        last_lds = last ? 1 : 0;
-        pick_lds[0] = (int)((tot >> 32) & 0xffffu);  // kf
-        pick_lds[1] = (int)(tot >> 48);              // kl
+      if (threadIdx.x == 0) ndone_lds = 0;
+      __syncthreads();
+      if (wave == 0) {
+        int my_s = -1, my_c0 = 0, my_c1 = 0, my_u = 0;
+        for (int j = 0; j < 64 && x < hi; ++j) {
+          while (x >= (int64_t)P2 + U2) {
+            P2 += U2;
+            ++s2;
+            U2 = all_lds ? seg_lds[S * rowlen + S + s2] : A.ws.seg_U[s2];
+          }
+          const int c0 = (int)(x - P2);
+          const int c1 = (int)((hi < (int64_t)P2 + U2 ? hi : (int64_t)P2 + U2) - P2);
+          if (lane == j) {
+            my_s = s2;
+            my_c0 = c0;
+            my_c1 = c1;
+            my_u = U2;
+          }
+          x = (int64_t)P2 + c1;
+        }
+        if (my_s >= 0) {
+          const uint64_t add = (uint64_t)(my_c1 - my_c0) + (my_c0 == 0 ? (uint64_t)k << 32 : 0ull) +
+                               (my_c1 == my_u ? (uint64_t)k << 48 : 0ull);
+          const uint64_t tot =
+              __hip_atomic_fetch_add(&A.ws.seg_done[my_s], add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+          if ((uint32_t)tot == (uint32_t)my_u) {
+            const int at = atomicAdd(&ndone_lds, 1);
+            done_s[at] = my_s;
+            done_kf[at] = (int)((tot >> 32) & 0xffffu);
+            done_kl[at] = (int)(tot >> 48);
+          }
+        }
+      } else {  // keep the other wavefronts' copy of the walk in step
+        for (int j = 0; j < 64 && x < hi; ++j) {
+          while (x >= (int64_t)P2 + U2) {
+            P2 += U2;
+            ++s2;
+            U2 = all_lds ? seg_lds[S * rowlen + S + s2] : A.ws.seg_U[s2];
+          }
+          x = (int64_t)P2 + (int)((hi < (int64_t)P2 + U2 ? hi : (int64_t)P2 + U2) - P2);
+        }
       }
       __syncthreads();
-      if (last_lds) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        merge_segment<D, G, NTH>(A.ws, A.p.out, s2, s2 / HKV, s2 % HKV, HQ, pick_lds[0], pick_lds[1]);
+      const int nd = ndone_lds;
+      for (int d0 = 0; d0 < nd; d0 += NPAR) {
+        const int part = (int)threadIdx.x / NG2, t = (int)threadIdx.x % NG2;
+        const int d = d0 + part;
+        if (d < nd) merge_fold<D, G, NG2>(A.ws, mg[part], done_s[d], done_kf[d], done_kl[d], t);
+        __syncthreads();
+        if (d < nd) merge_write<D, G, NG2>(A.ws, mg[part], A.p.out, done_s[d], done_s[d] / HKV, done_s[d] % HKV, HQ, t);
+        __syncthreads();
       }
-      __syncthreads();
-      x = (int64_t)P2 + c1;
     }
   }
   // entries and duration of this range, read by the next decode's weighting
@@ -634,8 +729,15 @@ template <typename T, int D, int G>
 hipError_t attend_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, int W, hipStream_t st) {
   AttendArgs a{c, s, p, d, ws};
-  if (d.SB > 1) hipLaunchKernelGGL((k_attend<T, D, G, true>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
-  else hipLaunchKernelGGL((k_attend<T, D, G, false>), dim3(W), dim3(64 * attend_waves<T, D, G>()), 0, st, a);
+  const dim3 grid(W), block(64 * attend_waves<T, D, G>());
+  const bool all = (int64_t)d.S * (d.NT + 4) <= kSegLds;
+  if (d.SB > 1) {
+    if (all) hipLaunchKernelGGL((k_attend<T, D, G, true, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attend<T, D, G, true, false>), grid, block, 0, st, a);
+  } else {
+    if (all) hipLaunchKernelGGL((k_attend<T, D, G, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_attend<T, D, G, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
@@ -654,7 +756,7 @@ hipError_t attend_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
 template <typename T, int D, int G>
 int occupancy_impl() {
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G, false>),
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, reinterpret_cast<const void*>(&k_attend<T, D, G, false, true>),
                                                    64 * attend_waves<T, D, G>(), 0) != hipSuccess)
     return 1;
   return nb > 0 ? nb : 1;

@@ -198,14 +198,10 @@ struct RangeSplit {
   __device__ int64_t B(int k) const { return utot * C(k) / cw; }
 };
 
-// Per-die weights as stored in the workspace, clamped to the range the
+// A per-die weight as stored in the workspace, clamped to the range the
 // weighting step writes (anything else reads as equal weights).
-__device__ __forceinline__ void load_weights(const int32_t* xcd_w, int deterministic, int* w) {
-#pragma unroll
-  for (int x = 0; x < kXcdClasses; ++x) {
-    const int v = deterministic ? kWeightOne : xcd_w[x];
-    w[x] = (v >= kWeightOne / 2 && v <= 2 * kWeightOne) ? v : kWeightOne;
-  }
+__device__ __forceinline__ int clamp_weight(int v, int deterministic) {
+  return (!deterministic && v >= kWeightOne / 2 && v <= 2 * kWeightOne) ? v : kWeightOne;
 }
 
 // Raw buffer resource over [base, base + bytes): loads at offsets past the end
@@ -214,6 +210,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Stores and loads coherent across the accelerator's dies (each die has its
+// own L2): relaxed atomics at device scope are written through to, and read
+// from, the device's coherence point, so data handed from one workgroup to
+// another needs no L2 write-back or invalidation (which device-scope
+// release and acquire fences perform on the whole L2 of a die). The writer
+// waits for its stores to complete (wait_stores) before it signals.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent2(float* p, float a, float b) {  // 8-byte aligned
+  const uint64_t u = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {  // 8-byte aligned
+  const uint64_t u = __hip_atomic_load((uint64_t*)const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float((uint32_t)u), __uint_as_float((uint32_t)(u >> 32)));
+}
+__device__ __forceinline__ float4 load_agent4(const float* p) {  // 16-byte aligned
+  const float2 a = load_agent2(p), b = load_agent2(p + 2);
+  return make_float4(a.x, a.y, b.x, b.y);
+}
+// Wait until every vector memory access of this wavefront has completed (on
+// gfx9 stores count in vmcnt too); the memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // exp(x) for the softmax weights: 2^(x log2 e) on the transcendental unit.
 __device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
