@@ -9,7 +9,9 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libeta.so")
+# ETA_LIBRARY names another build of the same library (the host-sanitizer
+# build of sanitized_build.py); by default the in-tree libeta.so
+LIB_PATH = os.environ.get("ETA_LIBRARY") or os.path.join(HERE, "libeta.so")
 
 ETA_OK = 0
 ETA_ERR_INVALID_ARGUMENT = -1

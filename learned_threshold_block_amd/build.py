@@ -29,6 +29,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+OBJ_DIR = os.path.join(HERE, "_build")  # objects of the last build (the sanitized build relinks them)
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every source and link libeta.so; always rebuilds."""
     cc = hipcc()
@@ -55,6 +58,9 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         if r.returncode:
             raise RuntimeError("link failed:\n" + r.stdout)
         os.replace(out_tmp, LIB)
+        os.makedirs(OBJ_DIR, exist_ok=True)
+        for o in objs:
+            shutil.copyfile(o, os.path.join(OBJ_DIR, os.path.basename(o)))
     return LIB
 
 

@@ -526,6 +526,28 @@ def pin_calibration_grid(E):
     assert res[0]["c"] == 4.0
 
 
+def pin_calibration_nonfinite_key(E):
+    """The grid trace with key 5 not finite (its first coordinate NaN): every
+    score against it (rows t >= 5) is NaN. By hand: those scores leave bin 5,
+    which held nothing else, and land in bin 0; the total weight is
+    unchanged; and a NaN score is never at or above a threshold."""
+    T = 8
+    wl, q = _grid_trace(E, T)
+    wl.k_pages[wl.block_table[0, 0], 0, 5, 0] = np.nan
+    hist, above, total = E.calibration_histogram(wl.k_pages, "f32", wl.block_table, wl.seq_lens, q, 0, 1,
+                                                 0.0, float(T), T, w_h=np.zeros(4), b_h=3.5)
+    W = [(1 << 31) // (t + 1) for t in range(T)]
+    clean = [sum(W[t] for t in range(b, T)) for b in range(T)]
+    moved = sum(W[t] for t in range(5, T))
+    want = list(clean)
+    want[5] -= moved
+    want[0] += moved
+    assert want[5] == 0
+    assert hist.tolist() == want
+    assert total == sum(W[t] * (t + 1) for t in range(T))
+    assert above == sum(W[t] * (max(0, t - 3) - (1 if t >= 5 else 0)) for t in range(T))
+
+
 def pin_calibration_row_weighting(E):
     """Every row weighs about 2^31 whatever its length: two sequences whose rows
     each have exactly half of their scores at or above 0 give a density of 1/2
@@ -898,6 +920,7 @@ ALL_PINS = [
     pin_tail_masking, pin_page_permutation, pin_nonfinite_keys, pin_threshold_tie_admitted,
     pin_sigma_rne, pin_dual_closed_form, pin_dual_within_geometric, pin_dual_bruteforce,
     pin_calibration_grid, pin_calibration_row_weighting, pin_calibration_target_property,
+    pin_calibration_nonfinite_key,
     pin_prefill_causal_sdpa, pin_prefill_prefix_means, pin_prefill_last_row_is_decode, pin_prefill_bruteforce,
     pin_prefill_future_value_excluded,
     pin_quest_directed_rounding, pin_quest_box_corners, pin_quest_bruteforce,

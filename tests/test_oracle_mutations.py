@@ -45,6 +45,7 @@ MUTANTS = {
     "dual_drops_z": ("prob = scale * (mu @ q + z * spread)", "prob = scale * (mu @ q + spread)"),
     "dual_spread_unsquared": ("spread = np.sqrt(((sigma * q[None, :]) ** 2).sum(axis=1))",
                               "spread = (sigma * np.abs(q[None, :])).sum(axis=1)"),
+    "calibration_nan_in_last_bin": ("x = np.where(np.isnan(x), 0.0, x)", "x = np.where(np.isnan(x), num_bins - 1.0, x)"),
     "calibration_unweighted_rows": ("    return CALIB_WEIGHT_ONE // (t + 1)\n", "    return CALIB_WEIGHT_ONE\n"),
     "calibration_drops_diagonal": ("hist += wt * np.bincount(bins[i, :t + 1], minlength=num_bins)",
                                    "hist += wt * np.bincount(bins[i, :t], minlength=num_bins)"),
