@@ -72,6 +72,9 @@ def parse():
                    help="geometric, dual, box-bound and FP8 screens at the same thresholds")
     p.add_argument("--prefill", action="store_true",
                    help="time the causal prompt pass over the seq_32k prompt instead of the decode step")
+    p.add_argument("--regime", type=int, default=0, metavar="BATCH",
+                   help="only run the block-size ablation at the pages' head shape (G = 8, d = 64, 512K tokens) "
+                        "with BATCH sequences and print its own JSON line")
     p.add_argument("--append", action="store_true",
                    help="only time eta_append_kv on the workload's last pages and print its own JSON line")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -214,6 +217,82 @@ def compare_screens(workload, density, steps, warmup, z):
                                f"{float(np.mean(wl.target_density)):.2f}; dual z={z:g}"},
         "screens": rows,
     }), flush=True)
+
+
+def regime_bench(batch, steps, warmup):
+    """The head shape of the pages' decode benchmark (Table 5 and Table 10 of
+    the ETA page): 32 query heads over 4 KV heads (G = 8), d = 64, 64-token
+    pages, `batch` sequences of 524,288 tokens (batch 64: a 32 GiB cache, the
+    size Table 10 names), frozen per-head constants (the calibrated mode),
+    queries correlated within each group. Two settings:
+    per-head density 0.38 with rho = 0.97 (about half the blocks in each
+    group's union) and per-head density 0.10 with rho = 0.98 (about a sixth).
+    For each: thresholds bisected for the per-head density on 64-token blocks;
+    then the geometric screen on 16-, 32-, 64- and 128-token blocks at those
+    thresholds (densities counted in each size's blocks), and the dense
+    comparator (every block, plain softmax) on the same cache."""
+    import torch
+
+    import workloads as W
+
+    S = Setup("table5_512k", 0.38, "geometric_sub", 2.0, 16, None, n_seqs=batch)
+    wl = S.wl
+    settings = {}
+    for dens, rho in ((0.38, 0.97), (0.10, 0.98)):
+        if rho != W.recipe("table5_512k")["rho"] or dens != 0.38:
+            # same keys and values; only the queries (a function of rho) and the targets change
+            wq = W.make_workload("table5_512k", n_seqs=batch, seq_len=64, rho=rho)
+            wl.q = wq.q
+            S.q.copy_(S.eta.upload(wq.q, wl.kv_dtype, "cuda"))
+        wl.target_density = np.full(wl.h_q, dens)
+        S.bound = "geometric"
+        S.calibrate()
+        rows = {}
+        dense_us = None
+        for b in (64, 16, 32, 128, "dense"):
+            if b == "dense":
+                saved, mode = S.bias.clone(), S.mode
+                S.bias.fill_(-math.inf)
+                S.mode = S.eta.ETA_TAU_CALIBRATED
+                S.bound = "geometric"
+            elif b == 64:
+                S.bound = "geometric"
+            else:
+                if S.sub_block != b:
+                    S.use_sub_block(b)
+                S.bound = "geometric_sub"
+            st, dh, du = S.densities()
+            kv, _ = S.step_bytes(st)
+            us = time_steps(S, steps, warmup)
+            ph = time_phases(S, steps)
+            row = {"density_per_head": round(dh, 4), "density_union": round(du, 4), "us_per_step": round(us, 2),
+                   "screen_us": round(float(ph[0]), 2), "attend_and_merge_us": round(float(ph[1]), 2),
+                   "attend_gbs_union_kv": round(kv / (ph[1] * 1e-6) / 1e9, 1),
+                   "attend_frac_of_peak": round(kv / (ph[1] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+            if b == "dense":
+                S.bias.copy_(saved)
+                S.mode = mode
+                dense_us = us
+            rows["dense" if b == "dense" else f"b{b}"] = row
+            log(f"regime per-head {dens} rho {rho}: {b}: per-head {dh:.3f} union {du:.3f} step {us:.1f} us "
+                f"attend {ph[1]:.1f} us")
+        for key, row in rows.items():
+            if key != "dense":
+                row["speedup_vs_dense"] = round(dense_us / row["us_per_step"], 3)
+        settings[f"per_head_{dens:.2f}_rho_{rho:.2f}"] = {"rho": rho, "target_density_per_head": dens,
+                                                          "screens": rows}
+    print(json.dumps({
+        "metric": "block-size ablation at the pages' decode head shape: step time, densities, attend bandwidth",
+        "unit": "us/step", "higher_is_better": False, "steps": steps, "warmup": warmup, "data": "synthetic",
+        "dtype": wl.kv_dtype, "n_gpus": 1,
+        "config": {"workload": f"table5_512k: {wl.n_seqs} x {int(wl.seq_lens.max())} tokens, GQA {wl.h_q}/{wl.h_kv} "
+                               f"(G = {wl.group}), d={wl.d}, {wl.kv_dtype} paged KV, {wl.kv_bytes() / 2**30:.1f} GiB; "
+                               "calibrated per-head constants bisected on 64-token blocks, the other block sizes at the same "
+                               "thresholds"},
+        "settings": settings,
+    }), flush=True)
+    del S
+    torch.cuda.empty_cache()
 
 
 def prefill_bench(steps, warmup, cpu_budget, no_cpu):
@@ -417,14 +496,14 @@ def copy_probe(mib, steps):
 class Setup:
     """One workload resident on the GPU."""
 
-    def __init__(self, name, density=None, bound="geometric", z=2.0, sub_block=16, seq_len=None):
+    def __init__(self, name, density=None, bound="geometric", z=2.0, sub_block=16, seq_len=None, **gen):
         import torch
 
         import learned_threshold_block_amd as eta
         import workloads as W
 
         t0 = time.time()
-        kw = {} if density is None else dict(density=density)
+        kw = dict(gen) if density is None else dict(gen, density=density)
         if seq_len is not None:
             kw["seq_len"] = seq_len
         self.wl = wl = W.make_workload(name, **kw)
@@ -730,6 +809,9 @@ def main():
         return
     if args.compare_screens:
         compare_screens(args.workload, args.density, max(5, min(args.steps, 50)), min(args.warmup, 5), args.z)
+        return
+    if args.regime:
+        regime_bench(args.regime, max(5, min(args.steps, 20)), min(args.warmup, 3))
         return
     if args.append:
         append_bench(args.workload, max(20, min(args.steps * 2, 100)), max(3, args.warmup))

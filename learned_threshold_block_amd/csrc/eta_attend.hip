@@ -192,7 +192,7 @@ __device__ void merge_write(const Ws& ws, const MergeLds<D, G, NG>& M, float* ou
 // when a wavefront fits in 256 VGPRs, else four with the full register file.
 template <typename T, int D, int G>
 constexpr int attend_waves() {
-  return ((T::kBytes == 2 || D == 64) && G <= 4) ? 8 : 4;
+  return (((T::kBytes == 2 || D == 64) && G <= 4) || (T::kBytes == 2 && D == 64)) ? 8 : 4;
 }
 
 // Bit q set when some head of the group admitted block q of the page (word

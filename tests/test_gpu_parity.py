@@ -271,6 +271,25 @@ def test_repeatable(monkeypatch):
     check_output(wl, res, d1)
 
 
+def test_many_segments_attend_without_lds_tables():
+    """400 (sequence, KV head) segments with a 2048-page block table: the
+    segments' tile prefixes (400 x 36 ints) do not fit the attend kernel's LDS
+    tables, so it locates each segment's entries with per-segment loads (its
+    other variant). One long sequence and 99 short ones, paged."""
+    lens = [64 * 2048 - 5] + [300 + 37 * i for i in range(99)]
+    wl, summ = prepared("seq_32k", seq_lens=lens, h_q=8, h_kv=4, d=64, needles=0, paged=True)
+    S = wl.n_seqs * wl.h_kv
+    NT = -(-wl.max_blocks // 64)
+    assert S * (NT + 4) > 12288
+    dev = Dev(wl)
+    dev.build()
+    o = dev.decode()
+    st = dev.stats()
+    res = oracle_decode(wl, summaries=summ)
+    check_sets_and_counts(wl, res, st)
+    check_output(wl, res, o)
+
+
 def test_junk_tail_rows_do_not_leak(monkeypatch):
     """Rows past the end hold NaN (the generator's fill); results stay finite and
     equal, bit for bit under the static work split, those with zeroed junk."""

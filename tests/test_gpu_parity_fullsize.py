@@ -106,3 +106,18 @@ def test_longest_supported_sequence():
     screen's 1,024 tiles, the attend kernel's full tile prefix in LDS. Sets and
     counts bit-exact for all heads, outputs on two of them."""
     _run_full("seq_32k", per_seq=2, seq_lens=[64 * 65536], h_q=4, h_kv=1, d=64, needles=0)
+
+
+@pytest.mark.timeout(600)
+def test_table5_shape_full():
+    """The head shape of the pages' decode benchmark (32 query heads over 4 KV
+    heads, G = 8, d = 64) at 524,288 tokens, two sequences, queries correlated
+    within each group (rho = 0.97): sets and counts bit-exact for all heads,
+    outputs on 6 heads per sequence."""
+    _run_full("table5_512k", per_seq=6, n_seqs=2)
+
+
+@pytest.mark.timeout(600)
+def test_table5_shape_subblock16_full():
+    """The same shape with 16-token screen blocks: 4 heads per sequence."""
+    _run_full("table5_512k", per_seq=4, n_seqs=2, bound="geometric_sub", block=16)

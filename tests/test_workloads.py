@@ -1,5 +1,6 @@
 """Generators and test-side threshold placement (CPU)."""
 import numpy as np
+import pytest
 import torch
 
 import oracle.eta_oracle as E
@@ -55,3 +56,31 @@ def test_placement_hits_density_with_margin():
     assert 0.6 < union.mean() < 1.0
     gap = np.abs(res.ub - res.tau[:, :, None])
     assert np.nanmin(gap) >= 1e-3
+
+
+def test_query_correlation_within_groups():
+    """rho = 0 draws the uncorrelated queries; rho = 1 makes a group's query
+    heads equal; in between, two heads of a group correlate by about rho^2 per
+    coordinate and heads of different groups not at all."""
+    base = W.make_workload("seq_32k", seq_len=640, h_q=8, h_kv=2, d=128)
+    zero = W.make_workload("seq_32k", seq_len=640, h_q=8, h_kv=2, d=128, rho=0.0)
+    assert np.array_equal(base.q, zero.q)
+    one = W.make_workload("seq_32k", seq_len=640, h_q=8, h_kv=2, d=128, rho=1.0)
+    for h in range(8):
+        assert np.array_equal(one.q[0, h], one.q[0, (h // 4) * 4])
+    assert not np.array_equal(one.q[0, 0], one.q[0, 4])
+    rho = 0.9
+    wl = W.make_workload("seq_32k", seq_len=64, n_seqs=64, h_q=16, h_kv=2, d=128, rho=rho, threads=1)
+    qf = W.storage_to_f32(wl.q, "bf16").astype(np.float64)
+    same = np.mean([np.corrcoef(qf[n, 0], qf[n, 1 + k])[0, 1] for n in range(64) for k in range(7)])
+    other = np.mean([np.corrcoef(qf[n, 0], qf[n, 8 + k])[0, 1] for n in range(64) for k in range(8)])
+    assert abs(same - rho * rho) < 0.03, same
+    assert abs(other) < 0.03, other
+    with pytest.raises(ValueError):
+        W.make_workload("seq_32k", seq_len=64, rho=1.5)
+
+
+def test_table5_recipe_shape():
+    wl = W.make_workload("table5_512k", n_seqs=1, seq_len=1000)
+    assert (wl.h_q, wl.h_kv, wl.d, wl.kv_dtype, wl.tau_mode) == (32, 4, 64, "bf16", "calibrated")
+    assert W.recipe("table5_512k")["n"] == 64 and W.recipe("table5_512k")["T"] == 524288

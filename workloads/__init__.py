@@ -122,6 +122,12 @@ _RECIPES = {
     # lengths log-uniform in [t_lo, t_hi], pages in a seeded random physical order, per-head density U[0.05, 0.90]
     "ragged_16": dict(seed=1004, n=16, h_q=32, h_kv=8, d=128, T=None, dtype="bf16", mode="learned",
                       density=None, needles=0, t_lo=4096, t_hi=262144, paged=True),
+    # the head shape of the pages' decode benchmark (32 query heads over 4 KV heads, G = 8, d = 64) at
+    # 512K tokens per sequence and a batch of 64 (a 32 GiB cache); frozen per-head constants (the
+    # calibrated mode) and queries correlated within a group (rho), so that the group's union of admitted
+    # blocks is about half the blocks at 38% per head
+    "table5_512k": dict(seed=1005, n=64, h_q=32, h_kv=4, d=64, T=524288, dtype="bf16", mode="calibrated",
+                        density=0.38, needles=0, rho=0.97),
 }
 
 WORKLOAD_NAMES = tuple(_RECIPES)
@@ -140,9 +146,15 @@ def make_workload(name: str, seed: Optional[int] = None, *, n_seqs: Optional[int
                   h_kv: Optional[int] = None, d: Optional[int] = None, kv_dtype: Optional[str] = None,
                   mode: Optional[str] = None, density=None, needles: Optional[int] = None,
                   paged: Optional[bool] = None, lwb: int = 0, a: float = 0.0, beta: float = 5.0,
-                  tail_fill: float = float("nan"), threads: int = 8) -> Workload:
+                  tail_fill: float = float("nan"), threads: int = 8, rho: Optional[float] = None) -> Workload:
     """Draw one seeded workload. `name` picks the base recipe (one of WORKLOAD_NAMES);
-    keyword overrides shrink or reshape it for parity-size cases."""
+    keyword overrides shrink or reshape it for parity-size cases.
+
+    rho: correlation of the queries within a KV head's group. Query head h of
+    group g is q_h = rho c_g + sqrt(1 - rho^2) e_h, with c_g and e_h independent
+    N(0, I_d) draws (e_h is the uncorrelated workloads' query), so every pair of
+    heads of a group has correlation rho^2 per coordinate. None (the default
+    of most recipes) or 0 gives independent queries."""
     spec = recipe(name)
     seed = spec["seed"] if seed is None else int(seed)
     N = spec["n"] if n_seqs is None else int(n_seqs)
@@ -156,7 +168,10 @@ def make_workload(name: str, seed: Optional[int] = None, *, n_seqs: Optional[int
     if HQ % HKV:
         raise ValueError("H_Q must be a multiple of H_KV")
 
-    (ss_len, ss_ctr, ss_noise, ss_v, ss_q, ss_w, ss_dens, ss_needle, ss_perm) = _streams(seed, 9)
+    (ss_len, ss_ctr, ss_noise, ss_v, ss_q, ss_w, ss_dens, ss_needle, ss_perm, ss_qgroup) = _streams(seed, 10)
+    rho = spec.get("rho") if rho is None else float(rho)
+    if rho is not None and not 0.0 <= rho <= 1.0:
+        raise ValueError("rho must lie in [0, 1]")
 
     # sequence lengths
     if seq_lens is not None:
@@ -233,6 +248,10 @@ def make_workload(name: str, seed: Optional[int] = None, *, n_seqs: Optional[int
             fill_segment(s)
 
     q32 = np.random.default_rng(ss_q).standard_normal((N, HQ, D), dtype=np.float32)
+    if rho:  # a component shared by the heads of each group
+        c = np.random.default_rng(ss_qgroup).standard_normal((N, HKV, D), dtype=np.float32)
+        q32 = (np.float32(rho) * np.repeat(c, HQ // HKV, axis=1)
+               + np.float32(math.sqrt(1.0 - rho * rho)) * q32).astype(np.float32)
     q = to_storage(q32, dt)
     w = (np.random.default_rng(ss_w).standard_normal((HQ, D), dtype=np.float32)
          / np.float32(math.sqrt(D))).astype(np.float32)
