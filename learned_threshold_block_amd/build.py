@@ -22,6 +22,12 @@ HIP_FLAGS = [
 ]
 
 
+# per-source flags: the calibration kernel's MFMA results go straight to
+# vector registers (its binning reads every element; accumulation registers
+# would need a copy of each first)
+SOURCE_FLAGS = {"eta_calib.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -41,7 +47,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = ["-x", "hip"] if src.endswith(".hip") else []
-            cmd = [cc, *HIP_FLAGS, "-I", INCLUDE, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [cc, *HIP_FLAGS, *SOURCE_FLAGS.get(src, []), "-I", INCLUDE, *lang, "-c", os.path.join(CSRC, src),
+                   "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))

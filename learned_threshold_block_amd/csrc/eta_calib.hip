@@ -116,6 +116,21 @@ __device__ __forceinline__ void row_totals(const CalibArgs& A, int g, int t0, in
   if (lane < G) atomicAdd(&A.total[g * G + lane], tw);
 }
 
+// Workgroup -> (sequence, KV head, query tile). Consecutive workgroups are
+// dispatched round-robin over the accelerator's eight dies, each with its own
+// L2; the remap gives every die a contiguous run of (pair, tile) indices, so
+// the tiles of one (sequence, KV head) pair, which all read the same key
+// tiles, run on one die. The first 8 floor(n / 8) workgroups are permuted
+// among themselves; the rest keep their index.
+__device__ __forceinline__ void calib_tile(int MB, int HKV, int& n, int& g, int& qt) {
+  const int total = gridDim.x, per = total / kXcdClasses, bid = blockIdx.x;
+  const int L = bid < kXcdClasses * per ? (bid % kXcdClasses) * per + bid / kXcdClasses : bid;
+  const int pair = L / MB;
+  qt = L % MB;
+  n = pair / HKV;
+  g = pair % HKV;
+}
+
 template <typename T, int D, int G>
 __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   using L = TileLayout<T::kBytes, D>;
@@ -126,8 +141,8 @@ __global__ __launch_bounds__(256) void k_calib_hist(CalibArgs A) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
   const int HKV = A.c.HKV, MB = A.s.MB, B = A.B;
-  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
-  const int qt = blockIdx.x;
+  int n, g, qt;
+  calib_tile(MB, HKV, n, g, qt);
   const int len = A.s.lens[n];
   if (len < 1 || len > kBlock * MB || qt * kBlock >= len) return;
   for (int i = threadIdx.x; i < G * B; i += 256) lhist[i] = 0ull;
@@ -231,77 +246,120 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 // bfloat16 caches: the same histogram with the scores of each 64-query x
 // 64-key tile pair on the matrix cores. Wavefront w takes the quadrant (query
 // half w >> 1, key half w & 1) for every head of the group: S^T = K Q^T on
-// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims, B = 32 queries x 16 dims,
-// both loaded straight from memory as 16-byte rows), so lane l holds query
-// l % 32 of its half and, in element 4 i + j, key 8 i + 4 (l / 32) + j of its
-// half. Rows past the sequence end and keys after the query are skipped.
+// v_mfma_f32_32x32x16_bf16 (A = 32 keys x 16 dims from an LDS key tile, B =
+// 32 queries x 16 dims held in registers), so lane l holds query l % 32 of its
+// half and, in element 4 i + j, key 8 i + 4 (l / 32) + j of its half. Rows
+// past the sequence end and keys after the query are skipped. The workgroup
+// order keeps the tiles of one (sequence, KV head) pair on one die.
 template <int D, int G>
 __global__ __launch_bounds__(256) void k_calib_mfma(CalibArgs A) {
   constexpr int KS = D / 16;  // 16-dim steps
   extern __shared__ unsigned long long lhist[];  // [G][B]
-  __shared__ float s_tau[kBlock][kMaxGroup];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int HKV = A.c.HKV, MB = A.s.MB, B = A.B;
-  const int n = blockIdx.y / HKV, g = blockIdx.y % HKV;
-  const int qt = blockIdx.x;
+  int n, g, qt;
+  calib_tile(MB, HKV, n, g, qt);
   const int len = A.s.lens[n];
   if (len < 1 || len > kBlock * MB || qt * kBlock >= len) return;
   for (int i = threadIdx.x; i < G * B; i += 256) lhist[i] = 0ull;
   const bool learned = A.w != nullptr;
-  if (learned) row_thresholds<Bf16, D, G>(A, n, g, qt * kBlock, len, wave, lane, s_tau);
   if (wave == 0) row_totals<G>(A, g, qt * kBlock, len, lane);
-  __syncthreads();
 
   const int qh = wave >> 1, kh = wave & 1, nq = lane & 31, hi = lane >> 5;
   const int t = qt * kBlock + 32 * qh + nq;  // this lane's query (below 64 MB = Lq)
   const bool t_ok = t < len;
   const unsigned long long wt = t_ok ? (unsigned long long)((1u << 31) / (unsigned)(t + 1)) : 0ull;
   const float scale = 1.0f / sqrtf((float)D);
-  float tau[G];
-  unsigned long long abv[G];
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    tau[h] = learned ? s_tau[32 * qh + nq][h] : 0.f;
-    abv[h] = 0ull;
-  }
+  // bin position of a product a (score a scale): (a scale - lo) B / (hi - lo)
+  // as one fma; the threshold test compares a with tau / scale
+  const float bmul = scale * A.bscale, badd = -A.lo * A.bscale, blast = (float)(B - 1);
   const uint16_t* qrow0 = (const uint16_t*)A.q + (((int64_t)n * A.Lq + t) * A.HQ + g * G) * D + 8 * hi;
-  // the B operands (this lane's query, 16-byte rows of 8 dims) of up to four
+  // The B operands (this lane's query, 16-byte rows of 8 dims) of up to four
   // heads stay in registers for a whole pass over the key tiles; eight heads
-  // take two passes. The key tiles go through a double-buffered LDS area
-  // (rows padded by 16 bytes): the workgroup loads tile j + 1 with 16-byte
-  // loads of whole rows while tile j is scored.
+  // take two passes. Key tiles go through a double-buffered LDS area. Chunk c
+  // (8 dims) of key row r sits at chunk c ^ swz(r) of its LDS row: a
+  // wavefront's operand reads (consecutive lanes on consecutive rows, one
+  // chunk) then spread over the banks.
   constexpr int HB = G < 4 ? G : 4;
-  constexpr int KSTR = D + 8;            // LDS row stride (elements)
-  constexpr int CPT = kBlock * D / 8 / 256;  // 16-byte chunks per thread per tile
-  __shared__ __attribute__((aligned(16))) uint16_t klds[2][kBlock * KSTR];
+  constexpr int CH = D / 8;              // 16-byte chunks per key row
+  constexpr int TCH = kBlock * CH;       // chunks per tile
+  static_assert(TCH % 256 == 0, "tile chunks");
+  __shared__ __attribute__((aligned(16))) uint4 klds[2][TCH];
+  const auto swz = [](int r) { return (r ^ (r / CH)) & (CH - 1); };
   const int tid = threadIdx.x;
-  const auto tile_ok = [&](int jj) {
-    const int page = A.s.bt[(int64_t)n * MB + jj];
-    return page >= 0 && page < A.c.num_pages ? page : -1;
-  };
-  const auto load_tile = [&](int page, uint4 (&rg)[CPT]) {
-    const uint16_t* kt = (const uint16_t*)A.c.k + ((int64_t)page * HKV + g) * (kBlock * D);
+  const auto valid_page = [&](int page) { return page >= 0 && page < A.c.num_pages ? page : -1; };
+  const int* const bt_row = A.s.bt + (int64_t)n * MB;
+  const int kr = 32 * kh + nq;  // this lane's key row of the A operand
+  const auto mfma_head = [&](const uint4 (&ka)[KS], const uint4 (&qh_)[KS]) {
+    f32x16_t acc = {};
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      rg[c] = page >= 0 ? *(const uint4*)(kt + row * D + col) : make_uint4(0, 0, 0, 0);
+    for (int ks = 0; ks < KS; ++ks)
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                    __builtin_bit_cast(bf16x8_t, qh_[ks]), acc, 0, 0, 0);
+    return acc;
+  };
+  // Tile j + 1 is loaded into registers while tile j is scored and stored to
+  // the other LDS buffer afterwards (loads straight into LDS would make every
+  // histogram atomic wait for them).
+  uint4* const kb = &klds[0][0];
+  constexpr int CPT = TCH / 256;  // 16-byte chunks per thread per tile
+  const auto load_tile = [&](int page, uint4 (&rg)[CPT]) {  // zeros for a missing page
+    const uint16_t* kt = (const uint16_t*)A.c.k + ((int64_t)(page >= 0 ? page : 0) * HKV + g) * (kBlock * D);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int p = tid + 256 * i, r = p / CH;
+      rg[i] = page >= 0 ? *(const uint4*)(kt + r * D + 8 * ((p % CH) ^ swz(r))) : make_uint4(0, 0, 0, 0);
     }
   };
   const auto store_tile = [&](const uint4 (&rg)[CPT], int buf) {
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) {
-      const int ch = tid + 256 * c, row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-      *(uint4*)(&klds[buf][row * KSTR + col]) = rg[c];
-    }
+    for (int i = 0; i < CPT; ++i) kb[buf * TCH + tid + 256 * i] = rg[i];
   };
-#pragma unroll
+  // one product: its bin (the position clamped to [0, B - 1] by a median,
+  // which is 0 for NaN; truncation is then the floor), the weighted count
+  // into the workgroup's histogram, the threshold test
+  const auto bin_score = [&](int h, float a, float taua, int& nabv) {
+    const int bin = (int)__builtin_amdgcn_fmed3f(fmaf(a, bmul, badd), 0.f, blast);
+    atomicAdd(&lhist[h * B + bin], wt);
+    nabv += a >= taua ? 1 : 0;
+  };
+#pragma unroll 1
   for (int hb = 0; hb < G; hb += HB) {
+    float taua[HB];
+    int nabv[HB];  // products at or above the threshold: every score of a lane has its row's weight
     uint4 qr[HB][KS];
 #pragma unroll
     for (int hh = 0; hh < HB; ++hh)
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) qr[hh][ks] = *(const uint4*)(qrow0 + (hb + hh) * D + 16 * ks);
-    int page = tile_ok(0);
+    // the learned threshold w_h . q_t + b_h of this lane's row from the B
+    // operands it holds (dims 16 ks + 8 hi .. + 7; the lane 32 apart holds the
+    // other half), compared in product units
+#pragma unroll
+    for (int hh = 0; hh < HB; ++hh) {
+      float tau = __builtin_inff();
+      if (learned) {
+        const float* wr = A.w + (int64_t)(g * G + hb + hh) * D + 8 * hi;
+        float pw = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const float4 w0 = *(const float4*)(wr + 16 * ks), w1 = *(const float4*)(wr + 16 * ks + 4);
+          const uint4 v = qr[hh][ks];
+          pw = fmaf(w0.x, bf16_lo(v.x), pw); pw = fmaf(w0.y, bf16_hi(v.x), pw);
+          pw = fmaf(w0.z, bf16_lo(v.y), pw); pw = fmaf(w0.w, bf16_hi(v.y), pw);
+          pw = fmaf(w1.x, bf16_lo(v.z), pw); pw = fmaf(w1.y, bf16_hi(v.z), pw);
+          pw = fmaf(w1.z, bf16_lo(v.w), pw); pw = fmaf(w1.w, bf16_hi(v.w), pw);
+        }
+        pw += __shfl_xor(pw, 32, 64);
+        tau = (pw + A.b[g * G + hb + hh]) / scale;
+      }
+      taua[hh] = tau;
+      nabv[hh] = 0;
+    }
+    // lane l holds the block-table entry of tile 64 c + l of the current
+    // chunk c of 64 tiles (a register read per tile, a load per chunk)
+    int ents = lane <= qt ? bt_row[lane] : -1;
+    int page = valid_page(__builtin_amdgcn_readlane(ents, 0));
     {
       uint4 rg[CPT];
       load_tile(page, rg);
@@ -311,49 +369,52 @@ __global__ __launch_bounds__(256) void k_calib_mfma(CalibArgs A) {
     for (int j = 0; j <= qt; ++j) {
       const bool cur_ok = page >= 0;
       if (!cur_ok && tid == 0) A.err[0] = 1;
+      // the operand reads and the MFMA stay uniform over the workgroup: a
+      // lane supplies a key row of the A operand for every lane's scores,
+      // so only the binning is skipped for queries past the sequence end
       uint4 rg[CPT];
       const bool has_next = j < qt;
+      int next_page = -1;
       if (has_next) {
-        page = tile_ok(j + 1);
-        load_tile(page, rg);
+        const int jn = j + 1;
+        if ((jn & 63) == 0) ents = jn + lane <= qt ? bt_row[jn + lane] : -1;
+        next_page = valid_page(__builtin_amdgcn_readlane(ents, jn & 63));
+        load_tile(next_page, rg);
       }
       if (cur_ok) {
-        const uint16_t* krow = &klds[j & 1][(32 * kh + nq) * KSTR + 8 * hi];
         uint4 ka[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) ka[ks] = *(const uint4*)(krow + 16 * ks);
+        for (int ks = 0; ks < KS; ++ks) ka[ks] = kb[(j & 1) * TCH + kr * CH + ((2 * ks + hi) ^ swz(kr))];
         const int s0 = j * kBlock + 32 * kh + 4 * hi;  // key of element 0
 #pragma unroll
         for (int hh = 0; hh < HB; ++hh) {
           const int h = hb + hh;
-          f32x16_t acc = {};
+          const f32x16_t acc = mfma_head(ka, qr[hh]);
+          if (t_ok) {
+            if (j < qt) {  // every key of the tile precedes every query of this one
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                          __builtin_bit_cast(bf16x8_t, qr[hh][ks]), acc, 0, 0, 0);
+              for (int e = 0; e < 16; ++e) bin_score(h, acc[e], taua[hh], nabv[hh]);
+            } else {  // the diagonal tile: keys after the query are skipped
 #pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            const int sk = s0 + 8 * (e >> 2) + (e & 3);
-            if (t_ok && sk <= t) {
-              const float S = acc[e] * scale;
-              const float x = floorf((S - A.lo) * A.bscale);
-              const int bin = !(x > 0.f) ? 0 : (x >= (float)(B - 1) ? B - 1 : (int)x);  // NaN: bin 0
-              atomicAdd(&lhist[h * B + bin], wt);
-              if (learned && S >= tau[h]) abv[h] += wt;
+              for (int e = 0; e < 16; ++e)
+                if (s0 + 8 * (e >> 2) + (e & 3) <= t) bin_score(h, acc[e], taua[hh], nabv[hh]);
             }
           }
         }
       }
       if (has_next) store_tile(rg, (j + 1) & 1);
       __syncthreads();
+      page = next_page;
     }
-  }
+    if (learned) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    unsigned long long a = abv[h];
+      for (int hh = 0; hh < HB; ++hh) {
+        unsigned long long a = (unsigned long long)nabv[hh] * wt;
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
-    if (lane == 0 && learned && a) atomicAdd(&A.above[g * G + h], a);
+        for (int m = 32; m >= 1; m >>= 1) a += __shfl_xor(a, m, 64);
+        if (lane == 0 && a) atomicAdd(&A.above[g * G + hb + hh], a);
+      }
+    }
   }
   __syncthreads();
   for (int i = threadIdx.x; i < G * B; i += 256) {
@@ -400,8 +461,8 @@ __global__ __launch_bounds__(64) void k_calib_search(CalibArgs A) {
 template <typename T, int D, int G>
 hipError_t calib_impl(const CalibArgs& a, int N, int MB, hipStream_t st) {
   const size_t lds = (size_t)G * a.B * sizeof(unsigned long long);
-  if constexpr (T::kBytes == 2) hipLaunchKernelGGL((k_calib_mfma<D, G>), dim3(MB, N * a.c.HKV), dim3(256), lds, st, a);
-  else hipLaunchKernelGGL((k_calib_hist<T, D, G>), dim3(MB, N * a.c.HKV), dim3(256), lds, st, a);
+  if constexpr (T::kBytes == 2) hipLaunchKernelGGL((k_calib_mfma<D, G>), dim3(MB * N * a.c.HKV), dim3(256), lds, st, a);
+  else hipLaunchKernelGGL((k_calib_hist<T, D, G>), dim3(MB * N * a.c.HKV), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 

@@ -150,3 +150,37 @@ def test_out_of_range_page_is_reported(kv_dtype):
     assert all(int(x) == want for x in cal.total.cpu().numpy())
     # the skipped tile's scores are missing from the histogram: less weight than the full triangle
     assert all(int(x) < want for x in cal.hist.cpu().numpy().sum(axis=1))
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "f32"])
+def test_nonfinite_keys_follow_the_oracle(kv_dtype):
+    """Keys holding NaN, +inf and -inf: a NaN score falls in bin 0 and is never
+    at or above the threshold; an infinite score falls in the end bin of its
+    sign and counts as above when positive. Histograms, above-counts and
+    constants match the oracle under the same allowance as finite scores."""
+    wl = W.make_workload("seq_32k", seq_lens=[64 * 7 + 21, 300], h_q=4, h_kv=2, d=128, needles=0,
+                         kv_dtype=kv_dtype)
+    q_all = W.trace_queries(wl, seed=12)
+    plant = [(0, 0, 70, 3, np.nan), (0, 1, 200, 5, np.inf), (0, 0, 411, 7, -np.inf), (1, 1, 299, 0, np.nan)]
+    for n, g, s, e, x in plant:
+        page = wl.block_table[n, s // 64]
+        wl.k_pages[page, g, s % 64, e] = W.to_storage(np.array([x], np.float32), kv_dtype)[0]
+    log(f"[calibration non-finite keys] {kv_dtype}: (seq, kv head, position, element, value) {plant}")
+    lo, hi, B = -8.0, 8.0, 512
+    dev = Dev(wl)
+    bias = np.linspace(0.5, 2.0, wl.h_q).astype(np.float32)
+    cal = eta.calibrate(dev.cache, dev.seq_lens, dev.bt, eta.upload(q_all, wl.kv_dtype, "cuda"), B, lo, hi,
+                        w=dev.w, b=torch.from_numpy(bias).cuda())
+    ref = E.calibrate(wl.k_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q_all, wl.h_kv, lo, hi, B,
+                      w=wl.w, b=bias)
+    torch.cuda.synchronize()
+    assert int(cal.err.item()) == 0
+    hist = cal.hist.cpu().numpy()
+    above = cal.above.cpu().numpy()
+    total = cal.total.cpu().numpy()
+    c = cal.c.cpu().numpy()
+    with np.errstate(invalid="ignore"):
+        for h in range(wl.h_q):
+            amb_bin, amb_tau = _ambiguity(wl, q_all, h, lo, hi, B, wl.w[h], bias[h])
+            _check_head(hist[h], int(above[h]), int(total[h]), float(c[h]), ref[h], amb_bin, amb_tau, lo, hi, B,
+                        True)
