@@ -282,8 +282,7 @@ eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
   hipError_t e = hipSuccess;
   switch (phase) {
     case ETA_PHASE_SCREEN:
-      e = launch_screen(P.c, P.s, P.p, P.d, P.ws, st);
-      if (e == hipSuccess) e = launch_finalize(P.c, P.s, P.p, P.d, P.ws, st);
+      e = launch_screen_phase(P.c, P.s, P.p, P.d, P.ws, st);
       break;
     case ETA_PHASE_ATTEND:
       e = launch_attend(P.c, P.s, P.p, P.d, P.ws, grid, st);

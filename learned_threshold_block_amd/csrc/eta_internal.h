@@ -147,10 +147,10 @@ struct PrefillParams {
 hipError_t launch_build_summaries(const CacheView& c, const SeqView& s, hipStream_t st);
 hipError_t launch_append(const CacheView& c, const SeqView& s, const void* k_new, const void* v_new,
                          hipStream_t st);
-hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                         const Ws& ws, hipStream_t st);
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                           const Ws& ws, hipStream_t st);  // also writes NaN rows for segments with no entries
+// screen and finalize (in one launch for short segments with the geometric
+// bound); also writes NaN rows for segments with no entries
+hipError_t launch_screen_phase(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                               const Ws& ws, hipStream_t st);
 hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                          const Ws& ws, int attend_wgs, hipStream_t st);
 hipError_t launch_calibrate(const CacheView& c, const SeqView& s, const CalibParams& p, hipStream_t st);

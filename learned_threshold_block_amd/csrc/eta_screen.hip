@@ -35,6 +35,10 @@
 //   The split of the total work over the attend grid needs only the union
 //   counts; each attend and merge workgroup derives it from them itself, so no
 //   workgroup has to wait for all the others here.
+// k_screen_fin: both in one launch when every segment has at most eight tiles
+//   (512 screen blocks) and the bound is the geometric one: one workgroup per
+//   segment screens its tiles and then finalizes it, which saves a launch and
+//   a dependent round at short lengths.
 #include <limits.h>
 
 #include "eta_device.h"
@@ -73,29 +77,29 @@ __device__ __forceinline__ void load8<F32>(const float* p, float (&out)[8]) {
 // MODE: 0 geometric bound, 1 dual score, 2 comparator box bound, 3 geometric
 // bound over the FP8 records, 4 geometric bound on smaller screen blocks
 // (SB = A.d.SB of them per page), 5 geometric bound on 128-token blocks.
-template <typename T, int D, int G, int MODE>
-__global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
+// The sizes this decode laid the workspace out for (the header).
+template <int D>
+__device__ __forceinline__ void write_glob(const ScreenArgs& A) {
+  A.ws.glob[kGlobN] = A.d.N;
+  A.ws.glob[kGlobMB] = A.d.MB;
+  A.ws.glob[kGlobHQ] = A.d.HQ;
+  A.ws.glob[kGlobHKV] = A.d.HKV;
+  A.ws.glob[kGlobD] = D;
+  A.ws.glob[kGlobSB] = A.d.SB;
+  A.ws.glob[kGlobPB] = A.d.PB;
+}
+
+// Tile t (64 consecutive screen blocks) of segment s (sequence, KV head),
+// screened by one wavefront.
+template <typename T, int D, int G, int MODE, int NW>
+__device__ __forceinline__ void screen_tile(const ScreenArgs& A, int s, int t, int wave, int lane) {
   constexpr bool DUAL = MODE == 1, BOX = MODE == 2, FP8 = MODE == 3, SUBB = MODE == 4, PAIR = MODE == 5;
   using L = TileLayout<2, D>;  // float16 centroid rows
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI;
   static_assert(L::CPL == 1 && L::EPC == 8, "centroid rows are one 8-half chunk per lane");
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int r = lane / LPR, cb = lane % LPR;
-  const int s = blockIdx.y;
   const int HKV = A.d.HKV, MB = A.d.MB, NT = A.d.NT, HQ = A.d.HQ;
   const int n = s / HKV, g = s % HKV;
-  const int t = blockIdx.x * 4 + wave;
-
-  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
-    A.ws.glob[kGlobN] = A.d.N;
-    A.ws.glob[kGlobMB] = MB;
-    A.ws.glob[kGlobHQ] = HQ;
-    A.ws.glob[kGlobHKV] = HKV;
-    A.ws.glob[kGlobD] = D;
-    A.ws.glob[kGlobSB] = A.d.SB;
-    A.ws.glob[kGlobPB] = A.d.PB;
-  }
-  if (t >= NT) return;
   const int64_t tix = (int64_t)s * NT + t;
   const int64_t tcx = (int64_t)s * (NT + 1) + t;  // index into tile_cnt / tile_ent
   const int j0 = t * kTile;
@@ -309,9 +313,9 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   // ---- back to block order (lane l then holds block j0 + l), the largest
   //      bound per head among complete blocks (lowest index on ties), and
   //      ballot compaction in ascending block order
-  __shared__ uint32_t smask[4][64];
-  __shared__ int spage[4][64];
-  __shared__ float sub[4][G][64];
+  __shared__ uint32_t smask[NW][64];
+  __shared__ int spage[NW][64];
+  __shared__ float sub[NW][G][64];
   smask[wave][jl - j0] = mask | (complete ? 0x10000u : 0u);
   spage[wave][jl - j0] = page_l;
 #pragma unroll
@@ -374,6 +378,16 @@ __global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
   }
 }
 
+// One wavefront per tile: grid ((NT + 3) / 4, S).
+template <typename T, int D, int G, int MODE>
+__global__ __launch_bounds__(256) void k_screen(ScreenArgs A) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) write_glob<D>(A);
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= A.d.NT) return;
+  screen_tile<T, D, G, MODE, 4>(A, blockIdx.y, t, wave, lane);
+}
+
 // ---------------------------------------------------------------- finalize
 struct FinArgs {
   CacheView c;
@@ -392,13 +406,14 @@ struct FinArgs {
 // with its previous weight, becomes its weight for this decode, clamped to
 // [1/2, 2]. Equal weights when there is no valid record or in the
 // deterministic mode. Runs as one extra workgroup of the finalize grid.
+template <int NW>
 __device__ void update_weights(const FinArgs& A) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (A.fixed_w[0] > 0 && !A.deterministic) {
     if (tid < kXcdClasses) A.ws.xcd_w[tid] = A.fixed_w[tid];
     return;
   }
-  __shared__ int s_acc[4][2 * kXcdClasses];
+  __shared__ int s_acc[NW][2 * kXcdClasses];
   const int magic = A.ws.glob[kGlobStatMagic];
   const int Wprev = A.ws.glob[kGlobStatW];
   const bool valid = !A.deterministic && magic == kStatMagic && Wprev >= 1 && Wprev <= kMaxAttendWgs;
@@ -406,7 +421,7 @@ __device__ void update_weights(const FinArgs& A) {
 #pragma unroll
   for (int x = 0; x < kXcdClasses; ++x) e[x] = t[x] = 0;
   if (valid) {
-    for (int k = tid; k < Wprev; k += 256) {
+    for (int k = tid; k < Wprev; k += 64 * NW) {
       const int ek = A.ws.rng_stat[2 * k], tk = min(A.ws.rng_stat[2 * k + 1], 1 << 22);
       if (ek > 0 && tk > 0) {
 #pragma unroll
@@ -432,9 +447,12 @@ __device__ void update_weights(const FinArgs& A) {
   int nr = 0;
 #pragma unroll
   for (int x = 0; x < kXcdClasses; ++x) {
-    const float es = (float)(s_acc[0][x] + s_acc[1][x] + s_acc[2][x] + s_acc[3][x]);
-    const float ts = (float)(s_acc[0][kXcdClasses + x] + s_acc[1][kXcdClasses + x] + s_acc[2][kXcdClasses + x] +
-                             s_acc[3][kXcdClasses + x]);
+    int ei = 0, ti = 0;
+    for (int w = 0; w < NW; ++w) {
+      ei += s_acc[w][x];
+      ti += s_acc[w][kXcdClasses + x];
+    }
+    const float es = (float)ei, ts = (float)ti;
     rate[x] = (es > 0.f && ts > 0.f) ? es / ts : 0.f;
     if (rate[x] > 0.f) {
       mean += rate[x];
@@ -456,14 +474,12 @@ __device__ void update_weights(const FinArgs& A) {
   }
 }
 
-// One workgroup per (sequence, KV head): totals, rescue, tile prefix, counts.
-template <int G>
-__global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
-  if ((int)blockIdx.x == A.d.S) {
-    update_weights(A);
-    return;
-  }
-  const int s = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+// Segment s (sequence, KV head), by a workgroup of 256 threads once every
+// tile of the segment is screened: totals, rescue, tile prefix, counts.
+template <int G, int NW>
+__device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
+  constexpr int NTH = 64 * NW;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int HKV = A.d.HKV, MB = A.d.MB, NT = A.d.NT, HQ = A.d.HQ;
   const int n = s / HKV, g = s % HKV;
@@ -483,15 +499,15 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   const int32_t* bt = A.s.bt + (int64_t)n * MB;
   int32_t* toff = A.ws.tile_off + (int64_t)s * (NT + 2);
 
-  __shared__ int s_scan[4];
-  __shared__ int s_hcnt[4][G];
-  __shared__ float s_umax[4][G];
-  __shared__ int s_uarg[4][G];
-  __shared__ int s_err[4];
+  __shared__ int s_scan[NW];
+  __shared__ int s_hcnt[NW][G];
+  __shared__ float s_umax[NW][G];
+  __shared__ int s_uarg[NW][G];
+  __shared__ int s_err[NW];
   __shared__ int s_nres;
   __shared__ int s_res_j[2 * G];
   __shared__ int s_resc[G];
-  __shared__ int s_ub[4];
+  __shared__ int s_ub[NW];
 
   // 1. per-head totals, largest bound, errors; exclusive prefix over tiles
   int hc[G];
@@ -507,7 +523,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   // row is read (the screen wrote all of them) and those past the sequence
   // are masked afterwards
   int err = 0, carry = 0, ublk = 0;
-  for (int t0 = 0; t0 < NT; t0 += 256) {
+  for (int t0 = 0; t0 < NT; t0 += NTH) {
     const int t = t0 + tid;
     int c = 0, e = 0, hcl[G], ual[G];
     uint64_t orb = 0;
@@ -545,7 +561,7 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
       c = 0;
     }
     int tot;
-    const int ex = block_incl_scan<4>(c, &tot, s_scan) - c;
+    const int ex = block_incl_scan<NW>(c, &tot, s_scan) - c;
     if (use) toff[t] = carry + ex;
     carry += tot;
   }
@@ -566,7 +582,12 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   // nothing (the same decision in every thread)
   bool need_rescue = false;
 #pragma unroll
-  for (int h = 0; h < G; ++h) need_rescue |= (s_hcnt[0][h] + s_hcnt[1][h] + s_hcnt[2][h] + s_hcnt[3][h]) == 0;
+  for (int h = 0; h < G; ++h) {
+    int tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += s_hcnt[w][h];
+    need_rescue |= tot == 0;
+  }
   if (need_rescue) {
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -594,14 +615,16 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
   //    128-token block (whose two pages both get the head's bit).
   if (tid == 0) {
     int nres = 0;
-    int ub = blk_bits ? s_ub[0] + s_ub[1] + s_ub[2] + s_ub[3] : 0;  // screen blocks admitted by any head
+    int ub = 0;  // screen blocks admitted by any head
+    if (blk_bits)
+      for (int w = 0; w < NW; ++w) ub += s_ub[w];
     for (int h = 0; h < G; ++h) {
       int tot = 0;
-      for (int w = 0; w < 4; ++w) tot += s_hcnt[w][h];
+      for (int w = 0; w < NW; ++w) tot += s_hcnt[w][h];
       float v = -__builtin_inff();
       int jb = INT_MAX;
       if (tot == 0) {  // the per-wave maxima exist only in this case
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
           if (s_umax[w][h] > v || (s_umax[w][h] == v && s_uarg[w][h] < jb)) {
             v = s_umax[w][h];
             jb = s_uarg[w][h];
@@ -674,22 +697,58 @@ __global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
     A.ws.seg_U[s] = U;
     A.ws.seg_ub[s] = blk_bits ? (badT ? 0 : s_ub[0]) : U;
     A.ws.seg_ntn[s] = ntn;
-    A.ws.seg_err[s] = (badT || s_err[0] || s_err[1] || s_err[2] || s_err[3]) ? 1 : 0;
+    int errs = 0;
+    for (int w = 0; w < NW; ++w) errs |= s_err[w];
+    A.ws.seg_err[s] = (badT || errs) ? 1 : 0;
     A.ws.seg_done[s] = 0;
   }
   // a segment without entries (invalid length) gets no attend work: its
   // heads' outputs are NaN, as for an empty softmax
   if (U == 0) {
     const int D = A.d.D;
-    for (int i = tid; i < G * D; i += 256)
+    for (int i = tid; i < G * D; i += NTH)
       A.out[((int64_t)n * HQ + g * G) * D + i] = __builtin_nanf("");
   }
+}
+
+// One workgroup per segment, and one more for the per-die weights.
+template <int G>
+__global__ __launch_bounds__(256) void k_finalize(FinArgs A) {
+  if ((int)blockIdx.x == A.d.S) {
+    update_weights<4>(A);
+    return;
+  }
+  finalize_segment<G, 4>(A, blockIdx.x);
+}
+
+// Short segments (at most kFusedTiles tiles) in one launch: a workgroup of
+// kFusedTiles wavefronts screens one tile per wavefront, then finalizes its
+// segment itself (the barrier publishes the tiles' results to the whole
+// workgroup); one more workgroup updates the per-die weights.
+constexpr int kFusedTiles = 8;
+template <typename T, int D, int G>
+__global__ __launch_bounds__(64 * kFusedTiles) void k_screen_fin(ScreenArgs A, FinArgs F) {
+  if ((int)blockIdx.x == A.d.S) {
+    update_weights<kFusedTiles>(F);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blockIdx.x == 0 && threadIdx.x == 0) write_glob<D>(A);
+  if (wave < A.d.NT) screen_tile<T, D, G, 0, kFusedTiles>(A, blockIdx.x, wave, wave, lane);
+  __syncthreads();
+  finalize_segment<G, kFusedTiles>(F, blockIdx.x);
 }
 
 template <typename T, int D, int G>
 hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
                        const Ws& ws, hipStream_t st) {
   ScreenArgs a{c, s, p, d, ws};
+  FinArgs f{c, s, d, ws, p.out, p.deterministic, {}};
+  for (int x = 0; x < kXcdClasses; ++x) f.fixed_w[x] = p.fixed_w[x];
+  if (p.bound == 0 && d.NT <= kFusedTiles) {
+    hipLaunchKernelGGL((k_screen_fin<T, D, G>), dim3(d.S + 1), dim3(64 * kFusedTiles), 0, st, a, f);
+    return hipGetLastError();
+  }
   dim3 grid((d.NT + 3) / 4, d.S);
   if (p.bound == 1) hipLaunchKernelGGL((k_screen<T, D, G, 1>), grid, dim3(256), 0, st, a);
   else if (p.bound == 2) hipLaunchKernelGGL((k_screen<T, D, G, 2>), grid, dim3(256), 0, st, a);
@@ -697,6 +756,9 @@ hipError_t screen_impl(const CacheView& c, const SeqView& s, const DecodeParams&
   else if (p.bound == 4) hipLaunchKernelGGL((k_screen<T, D, G, 4>), grid, dim3(256), 0, st, a);
   else if (p.bound == 5) hipLaunchKernelGGL((k_screen<T, D, G, 5>), grid, dim3(256), 0, st, a);
   else hipLaunchKernelGGL((k_screen<T, D, G, 0>), grid, dim3(256), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_finalize<G>), dim3(d.S + 1), dim3(256), 0, st, f);
   return hipGetLastError();
 }
 
@@ -712,32 +774,12 @@ hipError_t screen_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
   return hipErrorInvalidValue;
 }
 
-template <int G>
-hipError_t finalize_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                         const Ws& ws, hipStream_t st) {
-  FinArgs a{c, s, d, ws, p.out, p.deterministic, {}};
-  for (int x = 0; x < kXcdClasses; ++x) a.fixed_w[x] = p.fixed_w[x];
-  hipLaunchKernelGGL((k_finalize<G>), dim3(d.S + 1), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-
 }  // namespace
 
-hipError_t launch_screen(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                         const Ws& ws, hipStream_t st) {
+hipError_t launch_screen_phase(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                              const Ws& ws, hipStream_t st) {
   if (c.kv_dtype == 1) return d.D == 128 ? screen_g<Bf16, 128>(c, s, p, d, ws, st) : screen_g<Bf16, 64>(c, s, p, d, ws, st);
   return d.D == 128 ? screen_g<F32, 128>(c, s, p, d, ws, st) : screen_g<F32, 64>(c, s, p, d, ws, st);
-}
-
-hipError_t launch_finalize(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
-                           const Ws& ws, hipStream_t st) {
-  switch (d.G) {
-    case 1: return finalize_impl<1>(c, s, p, d, ws, st);
-    case 2: return finalize_impl<2>(c, s, p, d, ws, st);
-    case 4: return finalize_impl<4>(c, s, p, d, ws, st);
-    case 8: return finalize_impl<8>(c, s, p, d, ws, st);
-  }
-  return hipErrorInvalidValue;
 }
 
 }  // namespace eta
