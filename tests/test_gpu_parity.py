@@ -331,3 +331,25 @@ def test_invalid_device_data_is_reported():
     # a clean call afterwards reports OK again
     dev.decode()
     assert dev.stats().status == eta.ETA_OK
+
+
+@pytest.mark.parametrize("blocks", [512, 513])
+def test_screen_launch_forms_at_their_boundary(blocks):
+    """Up to 8 tiles (512 blocks) per sequence the screen and the finalize run
+    as one launch (one workgroup per segment); from 513 blocks on, as two. The
+    same sets, counts and outputs at the bar either way: a ragged partner
+    sequence, and KV head 0's group needing the rescue (its bias is so large
+    that nothing passes, and no block is forced: both lengths fill their last
+    page) next to a group that admits blocks at the placed thresholds."""
+    wl, summ = prepared("seq_32k", seq_lens=[64 * blocks, 64 * 3], h_q=8, h_kv=2, d=128, needles=0)
+    bias = np.array(wl.bias, dtype=np.float32).copy()
+    bias[:4] = 1e4
+    log(f"[screen launch form] {blocks} blocks")
+    dev = Dev(wl)
+    dev.build()
+    o = dev.decode(bias=bias)
+    st = dev.stats()
+    res = oracle_decode(wl, summaries=summ, bias=bias)
+    assert np.asarray(res.rescued)[:, :4].all()
+    check_sets_and_counts(wl, res, st)
+    check_output(wl, res, o)
