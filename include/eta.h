@@ -357,26 +357,31 @@ eta_status eta_calibrate(const eta_cache* cache, const eta_seqs* seqs, const voi
  * (centroid, radius, and the deviation if cache->sigma is set) of every
  * complete block (64 j + 64 <= seq_len) are written, bit-identical to
  * eta_build_block_summaries'; the cache must hold the prompt's keys and values.
- *   q        [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] bfloat16
- *            bits (device, 16-byte aligned); positions >= seq_len are not read.
+ *   q        [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] of
+ *            kv_dtype (device, 16-byte aligned); positions >= seq_len are not
+ *            read.
  *   w, b_or_c  as for eta_decode (device float32; w ignored when calibrated).
  *   out      [num_seqs][64*max_blocks_per_seq][num_q_heads][head_dim] float32
  *            (device, 16-byte aligned); rows at positions >= seq_len are NaN.
  *   err_flag [1] int32 device out: 1 if a length outside [0, 64*max_blocks]
  *            (that sequence's rows are then NaN) or an out-of-range page id
  *            (the block reads as zeros and its record is left alone) was met.
- * Products on the matrix cores: S with bfloat16 operands; the weights times V
- * in float16 (one term, V converted exactly) when every value of V in the
- * prompts lies within +-65280, else in two bfloat16 terms of each weight (a
- * range check over V picks the path for the whole call). A non-finite element
- * i of V at key s makes element i of the outputs of s's (sequence, KV head)
- * non-finite at every position of s's 64-token key block and later: from s on
- * as the exact rule gives, and at the block's positions before s as well,
- * where the exact rule does not use key s (the block's masked keys enter the
- * products with weight 0, and 0 times a non-finite value is NaN). Earlier
- * positions and the other elements are unaffected.
- * Requires a bfloat16 cache (ETA_ERR_UNSUPPORTED otherwise), beta > 0 finite,
- * a finite, and num_seqs * num_q_heads <= 65535. Asynchronous on `stream`. */
+ * bfloat16 caches: products on the matrix cores, S with bfloat16 operands;
+ * the weights times V in float16 (one term, V converted exactly) when every
+ * value of V in the prompts lies within +-65280, else in two bfloat16 terms of
+ * each weight (a range check over V picks the path for the whole call). A
+ * non-finite element i of V at key s makes element i of the outputs of s's
+ * (sequence, KV head) non-finite at every position of s's 64-token key block
+ * and later: from s on as the exact rule gives, and at the block's positions
+ * before s as well, where the exact rule does not use key s (the block's
+ * masked keys enter the products with weight 0, and 0 times a non-finite
+ * value is NaN). Earlier positions and the other elements are unaffected.
+ * float32 caches: float32 arithmetic on the vector units; keys after a
+ * position are skipped, so a non-finite element i of V at key s reaches
+ * element i of the outputs at positions s and later only, as the exact rule
+ * gives.
+ * Requires beta > 0 finite, a finite, and num_seqs * num_q_heads <= 65535
+ * (ETA_ERR_UNSUPPORTED otherwise). Asynchronous on `stream`. */
 eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void* q, int num_q_heads,
                        int tau_mode, const float* w, const float* b_or_c, float a, float beta, float* out,
                        int32_t* err_flag, eta_stream_t stream);

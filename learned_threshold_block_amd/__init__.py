@@ -333,7 +333,7 @@ def prefill(cache: Cache, seq_lens, block_table, q_all, tau_mode: int, b_or_c, w
             beta: float = 5.0, out=None, stream=None) -> Prefill:
     """Causal prompt pass (eta_prefill): gated attention at every position of
     every sequence over the keys up to it, and the records of every complete
-    block. q_all is [N][64*max_blocks][H_Q][d] bfloat16."""
+    block. q_all is [N][64*max_blocks][H_Q][d] of the cache's element type."""
     dev = cache.k_pages.device
     _need(q_all, "q_all", cache.k_pages.dtype, dev)
     N, L, HQ, D = q_all.shape

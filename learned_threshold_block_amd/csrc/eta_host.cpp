@@ -431,7 +431,6 @@ eta_status eta_prefill(const eta_cache* cache, const eta_seqs* seqs, const void*
   Dims d;
   st = dims_of(cache, seqs->num_seqs, seqs->max_blocks_per_seq, num_q_heads, &d);
   if (st != ETA_OK) return st;
-  if (cache->kv_dtype != ETA_BF16) return ETA_ERR_UNSUPPORTED;  // the matrix-core path is bfloat16
   if ((int64_t)seqs->num_seqs * num_q_heads > 65535) return ETA_ERR_UNSUPPORTED;  // grid rows
   PrefillParams p;
   p.q = q;

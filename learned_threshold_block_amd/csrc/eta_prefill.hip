@@ -469,6 +469,182 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// float32 caches: the same rule in float32 on the vector units. One
+// workgroup of 256 threads takes one (sequence, query head) and 64 positions
+// (one key block's worth, longest rows first); position P0 + i is handled by
+// the four lanes 4 i .. 4 i + 3, lane part c owning dims c D/4 .. + D/4 - 1 of
+// the query and of the output. Each key block of 64 tokens goes to LDS (K and
+// V, float32); a position scores the keys up to it (keys after it are skipped,
+// not weighted by 0, so a non-finite V reaches exactly the positions at or
+// after its key), then the block's weights against the running maximum and
+// the values. The workgroup of the group's first head that holds a complete
+// block builds its records (the bulk builder's device function).
+template <int D, int G>
+__global__ __launch_bounds__(256) void k_prefill_f32(PrefillArgs A) {
+  constexpr int DP = D / 4;  // dims per lane
+  __shared__ __attribute__((aligned(16))) float ks[kBlock][D];
+  __shared__ __attribute__((aligned(16))) float vs[kBlock][D];
+  const int tid = threadIdx.x, lane = tid & 63, part = tid & 3, row = tid >> 2;
+  const int HKV = A.c.HKV, MB = A.s.MB, HQ = A.HQ, Lq = A.Lq;
+  const int n = blockIdx.y / HQ, hq = blockIdx.y % HQ, g = hq / G;
+  const int P0 = ((int)gridDim.x - 1 - (int)blockIdx.x) * kBlock;
+  const int p = P0 + row;
+  int T = A.s.lens[n];
+  if (T < 0 || T > kBlock * MB) {  // invalid length: flagged, every row NaN
+    if (tid == 0) atomicOr(A.err, kErrData);
+    T = 0;
+  }
+  float* orow = A.out + (((int64_t)n * Lq + p) * HQ + hq) * D + part * DP;
+  if (P0 >= T) {
+#pragma unroll
+    for (int i = 0; i < DP; i += 4)
+      *(float4*)(orow + i) = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""));
+    return;
+  }
+  const bool pok = p < T;
+  const float* qrow = (const float*)A.q + (((int64_t)n * Lq + p) * HQ + hq) * D + part * DP;
+  float q[DP];
+#pragma unroll
+  for (int i = 0; i < DP; i += 4) {
+    const float4 v = pok ? *(const float4*)(qrow + i) : make_float4(0.f, 0.f, 0.f, 0.f);
+    q[i] = v.x; q[i + 1] = v.y; q[i + 2] = v.z; q[i + 3] = v.w;
+  }
+  float tau;
+  if (A.tau_mode == 0) {
+    const float* wr = A.w + (int64_t)hq * D + part * DP;
+    float dw = 0.f;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) dw = fmaf(wr[i], q[i], dw);
+    dw += __shfl_xor(dw, 1, 64);
+    dw += __shfl_xor(dw, 2, 64);
+    tau = (dw + A.b[hq]) - A.a;
+  } else {
+    tau = A.b[hq] - A.a;
+  }
+  const float scale = 1.0f / sqrtf((float)D);
+  float acc[DP];
+#pragma unroll
+  for (int i = 0; i < DP; ++i) acc[i] = 0.f;
+  float m = -__builtin_inff(), l = 0.f;
+  const int32_t* bt = A.s.bt + (int64_t)n * MB;
+  const int last = (min(P0 + kBlock, T) - 1) / kBlock;  // the tile's own block
+  for (int kt = 0; kt <= last; ++kt) {
+    const int page = bt[kt];
+    const bool valid = page >= 0 && page < A.c.num_pages;
+    if (!valid && tid == 0) atomicOr(A.err, kErrData);
+    const int rem = T - kt * kBlock;  // rows of the block inside the sequence
+    const float* kt_p = (const float*)A.c.k + ((int64_t)(valid ? page : 0) * HKV + g) * (kBlock * D);
+    const float* vt_p = (const float*)A.c.v + ((int64_t)(valid ? page : 0) * HKV + g) * (kBlock * D);
+    __syncthreads();  // the previous block's reads are done
+    for (int c = tid; c < kBlock * D / 4; c += 256) {
+      const int r = c / (D / 4);
+      const bool ok = valid && r < rem;
+      *(float4*)(&ks[0][0] + 4 * c) = ok ? *(const float4*)(kt_p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+      *(float4*)(&vs[0][0] + 4 * c) = ok ? *(const float4*)(vt_p + 4 * c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();
+    // keys kt 64 + s with s <= lim are at or before the position
+    const int lim = pok ? min(kBlock - 1, p - kt * kBlock) : -1;
+    float sc[kBlock];
+    float mb = -__builtin_inff();
+#pragma unroll
+    for (int s2 = 0; s2 < kBlock; ++s2) {
+      float d = 0.f;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) d = fmaf(q[i], ks[s2][part * DP + i], d);
+      d += __shfl_xor(d, 1, 64);
+      d += __shfl_xor(d, 2, 64);
+      const float S = d * scale;
+      const float sg = __builtin_amdgcn_rcpf(1.0f + fast_exp(-A.beta * (S - tau)));
+      const float y = S * sg;
+      sc[s2] = y;
+      if (s2 <= lim) mb = fmaxf(mb, y);
+    }
+    if (lim < 0) continue;
+    const float mnew = fmaxf(m, mb);
+    const float alpha = m == -__builtin_inff() ? 0.f : fast_exp(m - mnew);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) acc[i] *= alpha;
+    m = mnew;
+#pragma unroll
+    for (int s2 = 0; s2 < kBlock; ++s2) {
+      if (s2 > lim) continue;
+      const float w = fast_exp(sc[s2] - m);
+      l += w;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) acc[i] = fmaf(w, vs[s2][part * DP + i], acc[i]);
+    }
+  }
+  if (p < Lq) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int i = 0; i < DP; i += 4) {
+      float4 r4;
+      r4.x = pok ? acc[i] * inv : __builtin_nanf("");
+      r4.y = pok ? acc[i + 1] * inv : __builtin_nanf("");
+      r4.z = pok ? acc[i + 2] * inv : __builtin_nanf("");
+      r4.w = pok ? acc[i + 3] * inv : __builtin_nanf("");
+      *(float4*)(orow + i) = r4;
+    }
+  }
+  // ---- records of the tile's block (the group's first head only)
+  if (hq % G != 0) return;
+  const int wave = tid >> 6;
+  const int jb = P0 / kBlock;
+  if (wave == 0 && jb * kBlock + kBlock <= T) {
+    const int page = bt[jb];
+    if (page >= 0 && page < A.c.num_pages) {
+      const int64_t rec = (int64_t)page * HKV + g;
+      const float* tile = (const float*)A.c.k + rec * kBlock * D;
+      build_record<F32, D>(tile, nullptr, A.c.mu + rec * D, A.c.radius + rec,
+                           A.c.sigma ? A.c.sigma + rec * D : nullptr, A.c.kmin ? A.c.kmin + rec * D : nullptr,
+                           A.c.kmax ? A.c.kmax + rec * D : nullptr, A.c.mu8 ? A.c.mu8 + rec * D : nullptr,
+                           A.c.mu8 ? A.c.radius8 + rec : nullptr, A.c.mu8_fmt, lane);
+    }
+  }
+  // records of the other screen blocks (16, 32 or 128 tokens) that end in this
+  // tile, one wavefront each
+  if (A.c.sub_rows) {
+    const int rows = A.c.sub_rows, sb = sub_slots(rows);
+    const int js_end = (P0 + kBlock) / rows;  // one past the last block ending in the tile
+    for (int js = P0 / rows + wave; js < js_end; js += 4) {
+      if (js * rows + rows > T) break;
+      const int p0 = (int)((int64_t)js * rows / kBlock);  // table entry of the block's first page
+      const int page = bt[p0];
+      if (page < 0 || page >= A.c.num_pages) continue;
+      const int64_t srec = ((int64_t)page * HKV + g) * sb + js % sb;
+      const float* tile = (const float*)A.c.k + (((int64_t)page * HKV + g) * kBlock + (js % sb) * (kBlock / sb)) * D;
+      if (rows == 16) {
+        build_record<F32, D, 16>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, 0, lane);
+      } else if (rows == 32) {
+        build_record<F32, D, 32>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                 nullptr, nullptr, nullptr, 0, lane);
+      } else {
+        const int page1 = bt[p0 + 1];  // p0 + 1 < ceil(T / 64): the block is complete
+        if (page1 < 0 || page1 >= A.c.num_pages) continue;
+        build_record<F32, D, 128>(tile, nullptr, A.c.mu_sub + srec * D, A.c.radius_sub + srec, nullptr, nullptr,
+                                  nullptr, nullptr, nullptr, 0, lane,
+                                  (const float*)A.c.k + ((int64_t)page1 * HKV + g) * kBlock * D);
+      }
+    }
+  }
+}
+
+template <int D>
+hipError_t pf_f32_g(const PrefillArgs& a, int G, hipStream_t st) {
+  const dim3 grid((a.Lq + kBlock - 1) / kBlock, a.s.N * a.HQ);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((k_prefill_f32<D, 1>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_prefill_f32<D, 2>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((k_prefill_f32<D, 4>), grid, dim3(256), 0, st, a); break;
+    case 8: hipLaunchKernelGGL((k_prefill_f32<D, 8>), grid, dim3(256), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int D, int G>
 hipError_t pf_launch(const PrefillArgs& a, hipStream_t st) {
   constexpr int NW = kPfWaves;
@@ -509,6 +685,12 @@ hipError_t launch_prefill(const CacheView& c, const SeqView& s, const PrefillPar
   a.out = p.out;
   a.err = p.err;
   hipLaunchKernelGGL(k_prefill_zero, dim3(1), dim3(1), 0, st, p.err);
+  if (c.kv_dtype != 1) {  // float32 cache
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int G = p.HQ / c.HKV;
+    return c.D == 128 ? pf_f32_g<128>(a, G, st) : pf_f32_g<64>(a, G, st);
+  }
   const dim3 cgrid(s.MB, s.N * c.HKV);
   if (c.D == 128) hipLaunchKernelGGL((k_prefill_vcheck<128>), cgrid, dim3(256), 0, st, c, s, p.err);
   else hipLaunchKernelGGL((k_prefill_vcheck<64>), cgrid, dim3(256), 0, st, c, s, p.err);

@@ -258,7 +258,7 @@ def test_prefill_rejects():
     assert call(err=None) == bad
     assert call(hq=30) == bad
     assert call(ss=seqs(num_seqs=0)) == bad
-    assert call(c=cache(kv_dtype=_lib.ETA_F32)) == _lib.ETA_ERR_UNSUPPORTED    # bfloat16 matrix cores only
+    assert call(c=cache(kv_dtype=_lib.ETA_F32), w=None) == bad  # float32 caches take the same checks
     assert call(c=cache(head_dim=96)) == _lib.ETA_ERR_UNSUPPORTED
     assert call(hq=8 * 16) == _lib.ETA_ERR_UNSUPPORTED                         # G = 16
     assert call(ss=seqs(num_seqs=65536 // 32 + 1)) == _lib.ETA_ERR_UNSUPPORTED  # grid rows

@@ -196,3 +196,58 @@ def test_prefill_values_beyond_float16(wide):
         err = np.abs(g[fin] - r[fin]) / np.maximum(1.0, np.abs(r[fin]))
         assert float(err.max()) <= TOL["bf16"], float(err.max())
     assert np.all(np.isfinite(got[0, :int(wl.seq_lens[0])]))  # the other sequence is untouched
+
+
+F32_CASES = [
+    (dict(seq_lens=[700, 64 * 5], h_q=8, h_kv=2, d=128), "learned", np.linspace(-1.0, 2.5, 8), 5.0, 0.0),
+    (dict(seq_lens=[300, 65], h_q=2, h_kv=2, d=64), "calibrated", [0.5, 1.5], 2.0, 0.3),
+    (dict(seq_lens=[64 * 4 + 9, 129, 64], h_q=4, h_kv=2, d=128, paged=True), "calibrated",
+     [-np.inf, 1.0, np.inf, 0.0], 5.0, 0.0),
+    (dict(seq_lens=[1, 63, 200], h_q=8, h_kv=1, d=64), "learned", np.linspace(0.0, 1.0, 8), 1.0, -0.2),
+]
+
+
+@pytest.mark.parametrize("kw,mode,b,beta,a", F32_CASES)
+def test_prefill_parity_f32(kw, mode, b, beta, a):
+    """float32 caches: every row at the float32 bar, and the records equal to
+    the bulk builder's bit for bit (G = 4, 1, 2 and 8; both head dims)."""
+    log(f"[prefill f32] {mode} {kw} beta={beta} a={a}")
+    wl = W.make_workload("tiny_4k_f32", needles=0, **kw)
+    assert wl.kv_dtype == "f32"
+    q_all = W.trace_queries(wl, seed=21)
+    b = np.asarray(b, np.float32)
+    dev, got, _ = _run(wl, q_all, mode, b, beta, a)
+    ref = E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q_all, mode, wl.w, b, a, beta)
+    worst = 0.0
+    for n in range(wl.n_seqs):
+        T = int(wl.seq_lens[n])
+        assert np.all(np.isfinite(got[n, :T]))
+        worst = max(worst, float(np.max(np.abs(got[n, :T] - ref[n, :T]))))
+        assert np.all(np.isnan(got[n, T:]))
+    log(f"  max abs err {worst:.3g} (tolerance {TOL['f32']:g})")
+    assert worst <= TOL["f32"]
+    dev2 = Dev(wl)
+    dev2.build()
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.mu_bits(), dev2.mu_bits())
+    assert np.array_equal(dev.radius().view(np.uint32), dev2.radius().view(np.uint32))
+
+
+def test_prefill_f32_nonfinite_v_reaches_only_later_positions():
+    """float32 caches skip the keys after a position: an infinite element of V
+    at key s makes that element of the outputs non-finite at positions >= s
+    only, as in the oracle; the other elements stay at the bar."""
+    wl = W.make_workload("tiny_4k_f32", seq_lens=[64 * 3 + 20], h_q=4, h_kv=2, d=64, needles=0)
+    q_all = W.trace_queries(wl, seed=22)
+    s_key, elem = 64 + 37, 5
+    wl.v_pages[wl.block_table[0, s_key // 64], 1, s_key % 64, elem] = np.float32(np.inf)
+    b = np.full(4, 0.5, np.float32)
+    _, got, _ = _run(wl, q_all, "learned", b, 5.0)
+    ref = E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q_all, "learned", wl.w, b,
+                    0.0, 5.0)
+    T = int(wl.seq_lens[0])
+    g, r = got[0, :T], ref[0, :T]
+    assert np.array_equal(np.isfinite(g), np.isfinite(r))
+    assert not np.isfinite(g[s_key:, 2:4, elem]).any() and np.isfinite(g[:s_key, 2:4, elem]).all()
+    fin = np.isfinite(r)
+    assert float(np.max(np.abs(g[fin] - r[fin]))) <= TOL["f32"]
