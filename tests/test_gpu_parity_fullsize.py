@@ -121,3 +121,12 @@ def test_table5_shape_full():
 def test_table5_shape_subblock16_full():
     """The same shape with 16-token screen blocks: 4 heads per sequence."""
     _run_full("table5_512k", per_seq=4, n_seqs=2, bound="geometric_sub", block=16)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("density", [0.10, 0.70, 1.00])
+def test_batch_4x128k_densities_full(density):
+    """The 4 x 128K workload at the other points of the benchmark's density
+    sweep (10%, 70% and 100% per head): every set and count, 4 heads per
+    sequence for the outputs."""
+    _run_full("batch_4x128k", per_seq=4, seed=11, density=density)
