@@ -150,16 +150,18 @@ def test_prefill_empty_sequence():
 
 def test_prefill_seq32k_sampled():
     """The full 32768-token prompt (32 query heads over 8 KV heads, d = 128),
-    as the benchmark runs it: sampled rows of four heads against the oracle,
-    every row finite, and every record equal to the bulk builder's."""
+    as the benchmark runs it: 260 sampled rows (every workgroup tile's first
+    and last row among them at a stride of 16 tiles, plus random ones) of
+    eight heads, two per KV head, against the oracle; every row finite, and
+    every record equal to the bulk builder's."""
     wl = W.make_workload("seq_32k")
     q_all = W.trace_queries(wl, seed=21)
     b = np.linspace(-1.0, 2.5, wl.h_q).astype(np.float32)
     dev, got, _ = _run(wl, q_all, "learned", b, 5.0)
     rng = np.random.default_rng(5)
-    rows = sorted(set([0, 1, 31, 32, 63, 64, 4095, 4096, 16383, 32766, 32767] +
-                      rng.integers(0, 32768, 21).tolist()))
-    heads = [(0, 0), (0, 3), (0, 17), (0, 31)]
+    edges = [t for j in range(0, 512, 16) for t in (64 * j, 64 * j + 31, 64 * j + 32, 64 * j + 63)]
+    rows = sorted(set([0, 1, 4095, 4096, 16383, 32766, 32767] + edges + rng.integers(0, 32768, 128).tolist()))
+    heads = [(0, 0), (0, 3), (0, 5), (0, 10), (0, 17), (0, 22), (0, 28), (0, 31)]
     ref = E.prefill(wl.k_pages, wl.v_pages, wl.kv_dtype, wl.block_table, wl.seq_lens, q_all, "learned", wl.w, b,
                     0.0, 5.0, heads=heads, positions=rows)
     assert np.all(np.isfinite(got[0]))
