@@ -145,13 +145,20 @@ __device__ __forceinline__ void screen_tile(const ScreenArgs& A, int s, int t, i
     }
   }
 
-  // tiles past the sequence run through with every block invalid: no entries,
-  // zero bitmap words
   const bool badT = seq_len < 1 || seq_len > kBlock * MB;
   const int bsz = PAIR ? 2 * kBlock : kBlock >> lsb;  // tokens per screen block
   const int nfull = badT ? 0 : seq_len / bsz;
   const int nblk = badT ? 0 : (seq_len + bsz - 1) / bsz;
   const int nunit = PAIR ? (badT ? 0 : (seq_len + kBlock - 1) / kBlock) : nblk;  // lanes' units in the sequence
+  // A tile wholly past the sequence has nothing to screen, and the finalize
+  // uses only the tiles below ceil(nunit / 64): it stops here, writing only
+  // its zero head bitmaps (they are the per-head admitted sets the statistics
+  // copy out whole). Tile 0 always runs (it writes the thresholds; with a bad
+  // or zero length every block of it is invalid: no entries, zero bitmaps).
+  if (t > 0 && j0 >= nunit) {
+    if (lane < G) A.ws.tile_bits[((int64_t)s * G + lane) * NT + t] = 0;
+    return;
+  }
   const int jbl = PAIR ? jl >> 1 : jl;                                            // the lane's screen block
   const bool lvalid = jl < nunit && page_l >= 0 && page_l < A.c.num_pages;
   // a 128-token block is complete only when both of its pages are valid, so
@@ -520,8 +527,8 @@ __device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
     ua[h] = INT_MAX;
   }
   // the tile loads do not wait for the length: every tile of the segment's
-  // row is read (the screen wrote all of them) and those past the sequence
-  // are masked afterwards
+  // row is read, and those past the sequence (which the screen skips, so
+  // they hold an earlier decode's values) are masked afterwards
   int err = 0, carry = 0, ublk = 0;
   for (int t0 = 0; t0 < NT; t0 += NTH) {
     const int t = t0 + tid;
