@@ -35,7 +35,7 @@ PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PROFILES = os.path.join(ROOT, "profiles")
 # sources whose change invalidates a stored counter measurement of the attend kernel
 ATTEND_SOURCES = ("learned_threshold_block_amd/csrc/eta_attend.hip", "learned_threshold_block_amd/csrc/eta_device.h",
-                  "learned_threshold_block_amd/csrc/eta_internal.h")
+                  "learned_threshold_block_amd/csrc/eta_internal.h", "learned_threshold_block_amd/csrc/eta_screen_dev.h")
 
 
 def log(msg):
@@ -565,6 +565,11 @@ class Setup:
         wl = self.wl
         return self.eta.stats(self.ws, wl.n_seqs, wl.max_blocks, wl.h_q, wl.h_kv, bitmap=False)
 
+    def launches(self):
+        """1 when a step of this setup runs as one launch (short segments), 2
+        when it runs as the screen phase and the attend phase."""
+        return self.eta.decode_launches(self.cache, self.seq_lens, self.bt, self.wl.h_q, bound=self.bound)
+
     def calibrate(self, iters=40):
         """Bisect each head's bias/constant so that its admitted fraction of
         blocks (averaged over sequences) reaches the workload's target."""
@@ -677,6 +682,34 @@ def time_phases(S, steps):
     return np.array(out)
 
 
+def time_one_launch(S, steps):
+    """Average duration (us) of a step that runs as one launch: HIP events on
+    the launch stream around `steps` back-to-back eta_decode calls."""
+    torch = S.torch
+    S.run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        S.run()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps * 1e3
+
+
+def two_launch_step_us(S, steps, warmup):
+    """Step time of the same setup forced into its two launches (ETA_FUSED=0)."""
+    old = os.environ.get("ETA_FUSED")
+    os.environ["ETA_FUSED"] = "0"
+    try:
+        return time_steps(S, steps, warmup)
+    finally:
+        if old is None:
+            del os.environ["ETA_FUSED"]
+        else:
+            os.environ["ETA_FUSED"] = old
+
+
 def cpu_baseline(S, budget_s):
     """The fp64 oracle's decode step on one (sequence, KV head) segment at a
     time, single-threaded, for about `budget_s` seconds; scaled to a full step."""
@@ -756,16 +789,30 @@ def measure(S, workload, steps, warmup, bound="geometric", seq_len=None):
     attend_bytes = kv_bytes + U * 8 + wl.n_seqs * wl.h_q * wl.d * esz
     attend_gbs = attend_bytes / (ph[1] * 1e-6) / 1e9
     key = traffic_key(workload, float(np.mean(wl.target_density)), bound, seq_len)
+    kernel, kbytes, kus = "k_attend", attend_bytes, ph[1]
+    extra = {}
+    if S.launches() == 1:
+        # the whole step is one kernel: its algorithmic bytes are the step's
+        # (union K/V, every complete block's record read once, the block
+        # table, queries, predictor weights and the output)
+        kus = time_one_launch(S, steps)
+        kbytes = all_bytes
+        kernel = "k_attend (one launch: screen, attend, merge)"
+        two = two_launch_step_us(S, steps, warmup)
+        log(f"{workload}: one launch {kus:.1f} us (events); the same step as two launches {two:.1f} us")
+        extra = {"one_launch_us": round(kus, 2), "two_launch_us_per_step": round(two, 2)}
+    kgbs = kbytes / (kus * 1e-6) / 1e9
     return {
+        **extra,
         "us_per_step": round(us, 2),
         "density_per_head": round(dens_head, 4),
         "density_union": round(dens_union, 4),
         "achieved_gbs_union_kv": round(kv_bytes / (us * 1e-6) / 1e9, 1),
         "achieved_gbs_all_bytes": round(all_bytes / (us * 1e-6) / 1e9, 1),
         "phase_us": {"screen": round(float(ph[0]), 2), "attend_and_merge": round(float(ph[1]), 2)},
-        "roofline": {"bound": "hbm", "achieved": round(attend_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(attend_gbs / PEAK_HBM_GBS, 4), "traffic": stored_traffic(key),
-                     "kernel": "k_attend", "bytes_per_launch": attend_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(kgbs / PEAK_HBM_GBS, 4), "traffic": stored_traffic(key),
+                     "kernel": kernel, "bytes_per_launch": int(kbytes)},
     }
 
 

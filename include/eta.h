@@ -196,7 +196,8 @@ size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_b
  *   lwb        number of most recent complete blocks always admitted, >= 0.
  *   block_size must equal cache->block_size (64).
  * num_q_heads must be a multiple of num_kv_heads with G = num_q_heads /
- * num_kv_heads in {1, 2, 4, 8}. Equivalent to the three phases below in order.
+ * num_kv_heads in {1, 2, 4, 8}. Equivalent to the three phases below in order
+ * (short segments run them as one launch: see eta_decode_launches).
  * Values of V: those of a block a head did not admit never reach that head's
  * output (with ETA_BOUND_GEOMETRIC_SUB, per screen block, also between the
  * blocks of one page); a non-finite element i of V at a token a head attends
@@ -275,6 +276,20 @@ eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cac
                          const float* w, const float* b_or_c, float a, float beta, int lwb,
                          int block_size, float* out, void* workspace, size_t ws_bytes,
                          eta_stream_t stream);
+
+/* How eta_decode (eta_decode_ex with ETA_PHASE_ALL) runs a step of these
+ * sizes on the current device: 1 = as one launch, 2 = as the screen phase
+ * followed by the attend phase. Short segments (at most 512 screen blocks,
+ * i.e. 32,768 tokens, per sequence) with the geometric bound on page blocks
+ * run in one launch: each (sequence, KV head) gets several workgroups, each
+ * of which screens and finalizes the whole segment on its own (the records of
+ * such a segment are a few hundred KB) and attends to its share of the
+ * admitted blocks; the last of them merges. Results and statistics are those
+ * of the two phases up to float32 rounding. ETA_FUSED=0 in the environment
+ * keeps the two phases. A negative value is the eta_status of invalid sizes
+ * (checked as by eta_decode_ex). */
+int eta_decode_launches(const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs,
+                        int num_q_heads);
 
 /* One phase of eta_decode with the same arguments, for callers that overlap or
  * time the phases: ETA_PHASE_SCREEN (thresholds, bound screen, compaction of

@@ -264,6 +264,22 @@ def decode(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None
     return out
 
 
+def decode_launches(cache: Cache, seq_lens, block_table, num_q_heads: int, bound: str = "geometric",
+                    z: float = 2.0) -> int:
+    """eta_decode_launches: 1 when a decode step of these sizes runs as one
+    launch on the current device (short segments, geometric screen on page
+    blocks), 2 when it runs as the screen phase then the attend phase."""
+    dev = cache.k_pages.device
+    c, s = cache.c_struct(), _seqs(seq_lens, block_table, dev)
+    code = {"geometric": _lib.ETA_BOUND_GEOMETRIC, "dual": _lib.ETA_BOUND_DUAL, "quest": _lib.ETA_BOUND_QUEST,
+            "geometric_fp8": _lib.ETA_BOUND_GEOMETRIC_FP8, "geometric_sub": _lib.ETA_BOUND_GEOMETRIC_SUB}[bound]
+    opts = _lib.EtaScreenOptsC(code, float(z))
+    r = int(_lib.lib().eta_decode_launches(ctypes.byref(opts), ctypes.byref(c), ctypes.byref(s), int(num_q_heads)))
+    if r < 0:
+        _check(r, "eta_decode_launches")
+    return r
+
+
 def decode_noalloc(cache: Cache, seq_lens, block_table, q, tau_mode: int, b_or_c, w=None, a: float = 0.0,
                    beta: float = 5.0, lwb: int = 0, out=None, stream=None) -> torch.Tensor:
     """eta_decode_noalloc: one decode step (geometric screen) whose workspace

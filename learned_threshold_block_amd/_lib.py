@@ -45,6 +45,7 @@ EXPORTS = (
     "eta_decode_noalloc",
     "eta_decode_phase",
     "eta_decode_ex",
+    "eta_decode_launches",
     "eta_calibrate",
     "eta_prefill",
     "eta_stats",
@@ -133,6 +134,8 @@ def lib() -> ctypes.CDLL:
     L.eta_decode_phase.restype = I
     L.eta_decode_ex.argtypes = [I, ctypes.POINTER(EtaScreenOptsC)] + dec
     L.eta_decode_ex.restype = I
+    L.eta_decode_launches.argtypes = [ctypes.POINTER(EtaScreenOptsC), cp, sp, I]
+    L.eta_decode_launches.restype = I
     L.eta_calibrate.argtypes = [cp, sp, P, I, P, P, P, ctypes.POINTER(EtaCalibOptsC), P, P, P, P, P, P]
     L.eta_calibrate.restype = I
     L.eta_prefill.argtypes = [cp, sp, P, I, I, P, P, F, F, P, P, P]

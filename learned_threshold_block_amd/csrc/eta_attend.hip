@@ -34,7 +34,7 @@
 // matching value rows. V of tile i streams while the logits of tile i are
 // computed, K of tile i+1 while the values of tile i are accumulated. No float
 // atomics anywhere.
-#include "eta_device.h"
+#include "eta_screen_dev.h"
 
 namespace eta {
 namespace {
@@ -45,7 +45,34 @@ struct AttendArgs {
   DecodeParams p;
   Dims d;
   Ws ws;
+  int fz_P;         // one-launch decode: workgroups per segment
+  uint64_t fz_tag;  // one-launch decode: tag of this call in the arrival words (40 bits, not 0)
 };
+
+// Copy p of the screen's results (copy 0 is the one the statistics read).
+__device__ __forceinline__ Ws screen_copy(Ws w, int p) {
+  if (p == 0) return w;
+  const int64_t off = (int64_t)p * w.scr_stride;
+  auto sh = [off](auto* q) { return reinterpret_cast<decltype(q)>(reinterpret_cast<char*>(q) + off); };
+  w.tau = sh(w.tau);
+  w.tile_cnt = sh(w.tile_cnt);
+  w.tile_ent = sh(w.tile_ent);
+  w.tile_sub = sh(w.tile_sub);
+  w.tile_off = sh(w.tile_off);
+  w.tile_hcnt = sh(w.tile_hcnt);
+  w.tile_bits = sh(w.tile_bits);
+  w.tile_umax = sh(w.tile_umax);
+  w.tile_uarg = sh(w.tile_uarg);
+  w.tile_err = sh(w.tile_err);
+  w.seg_U = sh(w.seg_U);
+  w.seg_ub = sh(w.seg_ub);
+  w.seg_ntn = sh(w.seg_ntn);
+  w.seg_err = sh(w.seg_err);
+  w.st_head = sh(w.st_head);
+  w.st_tokens = sh(w.st_tokens);
+  w.st_rescued = sh(w.st_rescued);
+  return w;
+}
 
 // Entries [c, c + cnt) of the segment's compacted lists, one per lane
 // (lane < cnt): the tile whose prefix covers the index is found by binary
@@ -214,11 +241,24 @@ __device__ __forceinline__ uint32_t block_union(uint32_t sw, int sb) {
 // ALL: every segment's tile prefix, used-tile count and union count fit in
 // LDS (kSegLds ints); they are then read once in the first round.
 constexpr int kSegLds = 12288;
+// FUSED: the one-launch decode of short segments (at most kFusedTiles tiles of
+// 64 blocks each, the geometric bound on page blocks): workgroup k belongs to
+// segment k / fz_P as its member p = k % fz_P. It screens and finalizes the
+// whole segment itself (a wavefront per tile) into copy p of the screen's
+// results, so the segment's fz_P workgroups share nothing before their
+// partials; each then attends to its share [p U / fz_P, (p + 1) U / fz_P) of
+// the segment's U compacted entries. The screen's records of a segment are a
+// few hundred KB, read by all its workgroups mostly from the dies' L2.
+// Workgroup 0's copy is the one the statistics read. The last of a segment's
+// workgroups to write its partial merges them; arrivals are counted in a
+// word tagged with the call, so no earlier launch has to zero it.
 
-template <typename T, int D, int G, bool SUBB, bool ALL>
+template <typename T, int D, int G, bool SUBB, bool ALL, bool FUSED = false>
 __global__ __launch_bounds__((64 * attend_waves<T, D, G>()))
 __attribute__((amdgpu_waves_per_eu((attend_waves<T, D, G>() / 4), (attend_waves<T, D, G>() / 4))))
 void k_attend(AttendArgs A) {
+  static_assert(!FUSED || (!SUBB && !ALL && attend_waves<T, D, G>() == kFusedTiles),
+                "the one-launch decode screens a tile per wavefront on page blocks");
   using L = TileLayout<T::kBytes, D>;
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
   constexpr int NW = attend_waves<T, D, G>();  // wavefronts per workgroup
@@ -240,94 +280,120 @@ void k_attend(AttendArgs A) {
   __shared__ int pick_lds[3];
   const int NT = A.d.NT;
 
-  // ---- round 1: the segments' union counts (the work split needs them all)
-  //      and, when they fit in LDS, every segment's tile prefix, used-tile
-  //      count and union count, so that the first segment's entries can be
-  //      located without another round trip
+  // the screen's results this workgroup reads (its own copy in the one-launch decode)
+  Ws W = A.ws;
+  const int k = blockIdx.x;
+  int s = 0, P = 0, Us = 0, Wp = 0, n_entries = 0;
+  uint64_t arrival_seen = 0;  // one-launch decode, thread 0
+  int64_t lo = 0, hi = 0;
   __shared__ int seg_lds[ALL ? kSegLds : 1];
   const int rowlen = NT + 2;
   constexpr bool all_lds = ALL;  // the host checked S (NT + 4) <= kSegLds
-  // (lane x of wavefront 0 loads the weight of die class x: a lane-dependent
-  // load, which the compiler does not move to scalar registers at once, so
-  // nothing waits for it before the other loads are issued)
-  __shared__ int w_lds[kXcdClasses];
-  const int v0 = (int)threadIdx.x < S ? A.ws.seg_U[threadIdx.x] : 0;
-  const int wv = (int)threadIdx.x < kXcdClasses ? A.ws.xcd_w[threadIdx.x] : 0;
-  if constexpr (ALL) {  // [S][NT + 2] tile prefixes, then [S] used tiles, then [S] union counts
-    // loaded straight into LDS (lane l of a wavefront's 64-element chunk
-    // writes element l): no registers, no wait until the scan's barrier, and
-    // a short loop instead of a long unrolled one
-    const int ntile = S * rowlen;
-    for (int c = wave * 64; c < ntile; c += NTH)
-      if (c + lane < ntile) __builtin_amdgcn_global_load_lds(A.ws.tile_off + c + lane, seg_lds + c, 4, 0, 0);
-    for (int c = wave * 64; c < S; c += NTH)
-      if (c + lane < S) {
-        __builtin_amdgcn_global_load_lds(A.ws.seg_ntn + c + lane, seg_lds + ntile + c, 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(A.ws.seg_U + c + lane, seg_lds + ntile + S + c, 4, 0, 0);
-      }
-  }
-  if ((int)threadIdx.x < kXcdClasses) w_lds[threadIdx.x] = clamp_weight(wv, A.p.deterministic);
-  wait_stores();  // the loads into LDS above have landed before the scan's first barrier
-  int tot0;
-  const int incl0 = block_incl_scan<NW>(v0, &tot0, scan_lds);
-  int Utot = tot0;
-  if (S > NTH) {
-    int rest = 0;
-    for (int i = NTH + threadIdx.x; i < S; i += NTH) rest += A.ws.seg_U[i];
-    int totr;
-    block_incl_scan<NW>(rest, &totr, scan_lds);
-    Utot += totr;
-  }
-  Utot = __builtin_amdgcn_readfirstlane(Utot);
-  // at least 8 entries per range on average, so that no range is empty at any
-  // weights in [1/2, 2]
-  const int Wp = Utot < 8 * (int)gridDim.x ? (Utot + 7) / 8 : (int)gridDim.x;
-  const int k = blockIdx.x;
-  if (k >= Wp) return;
-  int64_t lo, hi;
-  {
-    int wts[kXcdClasses];
-#pragma unroll
-    for (int x = 0; x < kXcdClasses; ++x) wts[x] = w_lds[x];  // written before the scan's barriers
-    RangeSplit sp;
-    sp.init(Utot, Wp, wts);
-    lo = sp.B(k);
-    hi = sp.B(k + 1);
-  }
-  const int n_entries = (int)(hi - lo);
-  // the segment holding entry lo, its first entry and its count; the thread
-  // that finds it also sets up the claim counter of that segment's part
-  if (v0 > 0 && incl0 - v0 <= lo && lo < incl0) {
-    pick_lds[0] = threadIdx.x;
-    pick_lds[1] = incl0 - v0;
-    pick_lds[2] = v0;
-    ctr_lds = (int)(lo - (incl0 - v0)) + NW * kClaim;
-  }
-  if (lo < hi && lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
-    int carry = tot0;
-    for (int c0 = NTH; c0 < S && carry <= lo; c0 += NTH) {
-      const int i = c0 + threadIdx.x;
-      const int v = i < S ? A.ws.seg_U[i] : 0;
-      int tot;
-      const int incl = carry + block_incl_scan<NW>(v, &tot, scan_lds);
-      if (v > 0 && incl - v <= lo && lo < incl) {
-        pick_lds[0] = i;
-        pick_lds[1] = incl - v;
-        pick_lds[2] = v;
-        ctr_lds = (int)(lo - (incl - v)) + NW * kClaim;
-      }
-      carry += tot;
+  if constexpr (FUSED) {
+    const int fp = k % A.fz_P;
+    s = k / A.fz_P;
+    W = screen_copy(A.ws, fp);
+    // the segment's arrival word as it is now (read long before it is needed)
+    if (threadIdx.x == 0)
+      arrival_seen = __hip_atomic_load(&A.ws.fused_done[(int64_t)s * kArrivalStride], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+    ScreenArgs sa{A.c, A.s, A.p, A.d, W};
+    if (k == 0 && threadIdx.x == 0) write_glob<D>(sa);
+    if (wave < NT) screen_tile<T, D, G, 0, NW>(sa, s, wave, wave, lane);
+    __syncthreads();
+    FinArgs fa{A.c, A.s, A.d, W, A.p.out, A.p.deterministic, {}};
+    finalize_segment<G, NW>(fa, s);
+    __syncthreads();
+    Us = __builtin_amdgcn_readfirstlane(W.seg_U[s]);  // written by this workgroup before the barrier
+    lo = (int64_t)fp * Us / A.fz_P;
+    hi = (int64_t)(fp + 1) * Us / A.fz_P;
+    n_entries = (int)(hi - lo);
+  } else {
+    // ---- round 1: the segments' union counts (the work split needs them all)
+    //      and, when they fit in LDS, every segment's tile prefix, used-tile
+    //      count and union count, so that the first segment's entries can be
+    //      located without another round trip
+    // (lane x of wavefront 0 loads the weight of die class x: a lane-dependent
+    // load, which the compiler does not move to scalar registers at once, so
+    // nothing waits for it before the other loads are issued)
+    __shared__ int w_lds[kXcdClasses];
+    const int v0 = (int)threadIdx.x < S ? A.ws.seg_U[threadIdx.x] : 0;
+    const int wv = (int)threadIdx.x < kXcdClasses ? A.ws.xcd_w[threadIdx.x] : 0;
+    if constexpr (ALL) {  // [S][NT + 2] tile prefixes, then [S] used tiles, then [S] union counts
+      // loaded straight into LDS (lane l of a wavefront's 64-element chunk
+      // writes element l): no registers, no wait until the scan's barrier, and
+      // a short loop instead of a long unrolled one
+      const int ntile = S * rowlen;
+      for (int c = wave * 64; c < ntile; c += NTH)
+        if (c + lane < ntile) __builtin_amdgcn_global_load_lds(A.ws.tile_off + c + lane, seg_lds + c, 4, 0, 0);
+      for (int c = wave * 64; c < S; c += NTH)
+        if (c + lane < S) {
+          __builtin_amdgcn_global_load_lds(A.ws.seg_ntn + c + lane, seg_lds + ntile + c, 4, 0, 0);
+          __builtin_amdgcn_global_load_lds(A.ws.seg_U + c + lane, seg_lds + ntile + S + c, 4, 0, 0);
+        }
     }
+    if ((int)threadIdx.x < kXcdClasses) w_lds[threadIdx.x] = clamp_weight(wv, A.p.deterministic);
+    wait_stores();  // the loads into LDS above have landed before the scan's first barrier
+    int tot0;
+    const int incl0 = block_incl_scan<NW>(v0, &tot0, scan_lds);
+    int Utot = tot0;
+    if (S > NTH) {
+      int rest = 0;
+      for (int i = NTH + threadIdx.x; i < S; i += NTH) rest += A.ws.seg_U[i];
+      int totr;
+      block_incl_scan<NW>(rest, &totr, scan_lds);
+      Utot += totr;
+    }
+    Utot = __builtin_amdgcn_readfirstlane(Utot);
+    // at least 8 entries per range on average, so that no range is empty at any
+    // weights in [1/2, 2]
+    Wp = Utot < 8 * (int)gridDim.x ? (Utot + 7) / 8 : (int)gridDim.x;
+    if (k >= Wp) return;
+    {
+      int wts[kXcdClasses];
+#pragma unroll
+      for (int x = 0; x < kXcdClasses; ++x) wts[x] = w_lds[x];  // written before the scan's barriers
+      RangeSplit sp;
+      sp.init(Utot, Wp, wts);
+      lo = sp.B(k);
+      hi = sp.B(k + 1);
+    }
+    n_entries = (int)(hi - lo);
+    // the segment holding entry lo, its first entry and its count; the thread
+    // that finds it also sets up the claim counter of that segment's part
+    if (v0 > 0 && incl0 - v0 <= lo && lo < incl0) {
+      pick_lds[0] = threadIdx.x;
+      pick_lds[1] = incl0 - v0;
+      pick_lds[2] = v0;
+      ctr_lds = (int)(lo - (incl0 - v0)) + NW * kClaim;
+    }
+    if (lo < hi && lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
+      int carry = tot0;
+      for (int c0 = NTH; c0 < S && carry <= lo; c0 += NTH) {
+        const int i = c0 + threadIdx.x;
+        const int v = i < S ? A.ws.seg_U[i] : 0;
+        int tot;
+        const int incl = carry + block_incl_scan<NW>(v, &tot, scan_lds);
+        if (v > 0 && incl - v <= lo && lo < incl) {
+          pick_lds[0] = i;
+          pick_lds[1] = incl - v;
+          pick_lds[2] = v;
+          ctr_lds = (int)(lo - (incl - v)) + NW * kClaim;
+        }
+        carry += tot;
+      }
+    }
+    __syncthreads();
+    // (uniform values go through readfirstlane so that they live in scalar
+    // registers: the streaming loop needs every vector register)
+    s = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[0] : 0);
+    P = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[1] : 0);
+    Us = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[2] : 0);
   }
-  __syncthreads();
-  // (uniform values go through readfirstlane so that they live in scalar
-  // registers: the streaming loop needs every vector register)
-  int s = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[0] : 0);
-  int P = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[1] : 0);
-  int Us = __builtin_amdgcn_readfirstlane(lo < hi ? pick_lds[2] : 0);
   const int s_first = s, P_first = P, U_first = Us;
   const int64_t lo_first = lo;
   bool first_part = true;
+  bool part_due = FUSED;  // the one-launch decode writes a partial even for an empty share
 
   // lane offset (elements) of load (i=0, c) inside a tile
   int loff[CPL];
@@ -338,11 +404,14 @@ void k_attend(AttendArgs A) {
   // smaller screen blocks: log2 of their tokens, and the block of load i's rows
   const int lbs = SUBB ? (A.d.SB == 4 ? 4 : 5) : 6;
 
-  while (lo < hi) {
-    while (lo >= (int64_t)P + Us) {  // next segment with entries
-      P += Us;
-      ++s;
-      Us = all_lds ? seg_lds[S * rowlen + S + s] : A.ws.seg_U[s];
+  while (lo < hi || part_due) {
+    part_due = false;
+    if constexpr (!FUSED) {
+      while (lo >= (int64_t)P + Us) {  // next segment with entries
+        P += Us;
+        ++s;
+        Us = all_lds ? seg_lds[S * rowlen + S + s] : A.ws.seg_U[s];
+      }
     }
     const int e0 = (int)(lo - P);
     const int e1 = (int)((hi < (int64_t)P + Us ? hi : (int64_t)P + Us) - P);
@@ -368,7 +437,7 @@ void k_attend(AttendArgs A) {
           qf[h][c * 4 + 2] = __uint_as_float(v.z); qf[h][c * 4 + 3] = __uint_as_float(v.w);
         }
       }
-      tau[h] = A.ws.tau[(int64_t)n * HQ + g * G + h];
+      tau[h] = W.tau[(int64_t)n * HQ + g * G + h];
     }
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
@@ -391,15 +460,15 @@ void k_attend(AttendArgs A) {
         __syncthreads();
       }
     } else {
-      ntn = A.ws.seg_ntn[s];
-      const int32_t* toff = A.ws.tile_off + (int64_t)s * rowlen;  // the whole row: the loads do not wait for ntn
+      ntn = W.seg_ntn[s];
+      const int32_t* toff = W.tile_off + (int64_t)s * rowlen;  // the whole row: the loads do not wait for ntn
       for (int v = threadIdx.x; v < rowlen; v += NTH) toff_lds[v] = toff[v];
       if (threadIdx.x == 0) ctr_lds = e0 + NW * kClaim;
       __syncthreads();
     }
     first_part = false;
-    const int2* tents = A.ws.tile_ent + (int64_t)s * (NT + 1) * kTile;
-    const uint32_t* tsubs = SUBB ? A.ws.tile_sub + (int64_t)s * (NT + 1) * kTile : nullptr;
+    const int2* tents = W.tile_ent + (int64_t)s * (NT + 1) * kTile;
+    const uint32_t* tsubs = SUBB ? W.tile_sub + (int64_t)s * (NT + 1) * kTile : nullptr;
 
     // claims, two deep: the batch being streamed, the next one (resolved while
     // the current one streams) and the claim after it
@@ -606,7 +675,7 @@ void k_attend(AttendArgs A) {
       }
     }
     __syncthreads();
-    const int64_t piece = (int64_t)k + s;
+    const int64_t piece = FUSED ? (int64_t)k : (int64_t)k + s;
     for (int h = wave; h < G; h += NW) {
       float Mw[NW], M = -__builtin_inff();
 #pragma unroll
@@ -643,7 +712,36 @@ void k_attend(AttendArgs A) {
   //      cache maintenance of the dies' L2s is needed.
   wait_stores();
   __syncthreads();
-  {
+  if constexpr (FUSED) {
+    // one arrival per workgroup in the segment's word (bits 24-63 the call's
+    // tag, bits 0-23 the count). A word without this call's tag (another
+    // call's, or whatever the workspace held) counts as no arrival: it is
+    // replaced by (tag, 1) with one compare-and-swap against the value read
+    // at the start; once the word carries the tag, arrivals are additions.
+    __shared__ int last_lds;
+    __shared__ MergeLds<D, G, NTH> mgf;
+    if (threadIdx.x == 0) {
+      uint64_t* wp = &A.ws.fused_done[(int64_t)s * kArrivalStride];
+      const uint64_t tag = A.fz_tag;
+      uint64_t old = arrival_seen, nw = 0;
+      while ((old >> 24) != tag) {
+        if (__hip_atomic_compare_exchange_strong(wp, &old, (tag << 24) + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)) {
+          nw = (tag << 24) + 1;
+          break;
+        }
+      }
+      if (nw == 0) nw = __hip_atomic_fetch_add(wp, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+      last_lds = (int)(nw & 0xffffffu) == A.fz_P ? 1 : 0;
+    }
+    __syncthreads();
+    if (last_lds) {  // the segment's partials are slots s fz_P .. s fz_P + fz_P - 1
+      merge_fold<D, G, NTH>(A.ws, mgf, s * A.fz_P, 0, A.fz_P - 1, threadIdx.x);
+      __syncthreads();
+      merge_write<D, G, NTH>(A.ws, mgf, A.p.out, s, s / HKV, s % HKV, HQ, threadIdx.x);
+    }
+    return;
+  } else {
     // The segments this range touched, up to 64 at a time: wave 0's lane j
     // adds the entry count of the j-th of them with one 64-bit add, which
     // also carries, from the ranges holding the segment's first and last
@@ -753,6 +851,43 @@ hipError_t attend_g(const CacheView& c, const SeqView& s, const DecodeParams& p,
   return hipErrorInvalidValue;
 }
 
+// One-launch decode of short segments: fz_P workgroups per segment.
+template <typename T, int D, int G>
+hipError_t short_impl(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                      const Ws& ws, int fz_P, uint64_t tag, hipStream_t st) {
+  if constexpr (attend_waves<T, D, G>() != kFusedTiles) {
+    return hipErrorNotSupported;
+  } else {
+    AttendArgs a{c, s, p, d, ws, fz_P, tag};
+    hipLaunchKernelGGL((k_attend<T, D, G, false, false, true>), dim3(d.S * fz_P), dim3(64 * kFusedTiles), 0, st,
+                       a);
+    return hipGetLastError();
+  }
+}
+
+template <typename T, int D>
+hipError_t short_g(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d, const Ws& ws,
+                   int fz_P, uint64_t tag, hipStream_t st) {
+  switch (d.G) {
+    case 1: return short_impl<T, D, 1>(c, s, p, d, ws, fz_P, tag, st);
+    case 2: return short_impl<T, D, 2>(c, s, p, d, ws, fz_P, tag, st);
+    case 4: return short_impl<T, D, 4>(c, s, p, d, ws, fz_P, tag, st);
+    case 8: return short_impl<T, D, 8>(c, s, p, d, ws, fz_P, tag, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D>
+bool short_ok(int G) {
+  switch (G) {
+    case 1: return attend_waves<T, D, 1>() == kFusedTiles;
+    case 2: return attend_waves<T, D, 2>() == kFusedTiles;
+    case 4: return attend_waves<T, D, 4>() == kFusedTiles;
+    case 8: return attend_waves<T, D, 8>() == kFusedTiles;
+  }
+  return false;
+}
+
 template <typename T, int D, int G>
 int occupancy_impl() {
   int nb = 0;
@@ -779,6 +914,20 @@ hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParam
                          const Ws& ws, int W, hipStream_t st) {
   if (c.kv_dtype == 1) return d.D == 128 ? attend_g<Bf16, 128>(c, s, p, d, ws, W, st) : attend_g<Bf16, 64>(c, s, p, d, ws, W, st);
   return d.D == 128 ? attend_g<F32, 128>(c, s, p, d, ws, W, st) : attend_g<F32, 64>(c, s, p, d, ws, W, st);
+}
+
+hipError_t launch_decode_short(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                               const Ws& ws, int wgs_per_segment, uint64_t tag, hipStream_t st) {
+  if (c.kv_dtype == 1)
+    return d.D == 128 ? short_g<Bf16, 128>(c, s, p, d, ws, wgs_per_segment, tag, st)
+                      : short_g<Bf16, 64>(c, s, p, d, ws, wgs_per_segment, tag, st);
+  return d.D == 128 ? short_g<F32, 128>(c, s, p, d, ws, wgs_per_segment, tag, st)
+                    : short_g<F32, 64>(c, s, p, d, ws, wgs_per_segment, tag, st);
+}
+
+bool decode_short_supported(int kv_dtype, int D, int G) {
+  if (kv_dtype == 1) return D == 128 ? short_ok<Bf16, 128>(G) : short_ok<Bf16, 64>(G);
+  return D == 128 ? short_ok<F32, 128>(G) : short_ok<F32, 64>(G);
 }
 
 int attend_wgs_per_cu(int kv_dtype, int D, int G) {

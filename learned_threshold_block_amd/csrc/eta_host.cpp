@@ -6,6 +6,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -30,6 +31,10 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   const size_t pieces = (size_t)kMaxAttendWgs + S;
   Ws w;
   w.glob = (int32_t*)take(sizeof(int32_t) * kGlobCount);
+  // the screen's results, in one block that the one-launch decode of short
+  // segments repeats once per workgroup of a segment (private copies)
+  off = align_up(off, 256);
+  const size_t scr0 = off;
   w.tau = (float*)take(sizeof(float) * nq);
   w.tile_cnt = (int32_t*)take(sizeof(int32_t) * S * (NT + 1));
   w.tile_ent = (int2*)take(sizeof(int2) * S * (NT + 1) * kTile);
@@ -44,12 +49,17 @@ size_t workspace_layout(const Dims& d, void* base, Ws* ws) {
   w.seg_ub = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_ntn = (int32_t*)take(sizeof(int32_t) * S);
   w.seg_err = (int32_t*)take(sizeof(int32_t) * S);
-  w.seg_done = (uint64_t*)take(sizeof(uint64_t) * S);
-  w.rng_stat = (int32_t*)take(sizeof(int32_t) * 2 * kMaxAttendWgs);
-  w.xcd_w = (int32_t*)take(sizeof(int32_t) * kXcdClasses);
   w.st_head = (int32_t*)take(sizeof(int32_t) * nq);
   w.st_tokens = (int64_t*)take(sizeof(int64_t) * nq);
   w.st_rescued = (int32_t*)take(sizeof(int32_t) * nq);
+  off = align_up(off, 256);
+  w.scr_stride = (int64_t)(off - scr0);
+  w.scr_copies = (d.NT <= kFusedTiles && S < (size_t)kFusedMaxWgs) ? (int)(kFusedMaxWgs / S) - 1 : 0;
+  off += (size_t)w.scr_copies * (size_t)w.scr_stride;
+  w.seg_done = (uint64_t*)take(sizeof(uint64_t) * S);
+  w.fused_done = (uint64_t*)take(sizeof(uint64_t) * S * kArrivalStride);
+  w.rng_stat = (int32_t*)take(sizeof(int32_t) * 2 * kMaxAttendWgs);
+  w.xcd_w = (int32_t*)take(sizeof(int32_t) * kXcdClasses);
   w.part_ml = (float*)take(sizeof(float) * pieces * G * 2);
   w.part_acc = (float*)take(sizeof(float) * pieces * G * (size_t)d.D);
   if (ws) *ws = w;
@@ -277,6 +287,29 @@ eta_status prepare(const eta_screen_opts* screen, const eta_cache* cache, const 
   return ETA_OK;
 }
 
+// Workgroups per segment of the one-launch decode of short segments for these
+// sizes, or 0 when the step runs as the screen phase and the attend phase.
+// ETA_FUSED=0 in the environment keeps the two phases (for testing).
+int short_plan(const Prepared& P) {
+  if (P.p.bound != 0 || P.d.SB != 1 || P.d.PB != 1 || P.d.NT > kFusedTiles) return 0;
+  if (const char* env = getenv("ETA_FUSED"))
+    if (env[0] == '0') return 0;
+  if (!decode_short_supported(P.c.kv_dtype, P.d.D, P.d.G)) return 0;
+  int grid = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
+  if (grid > kFusedMaxWgs) grid = kFusedMaxWgs;
+  const int per = grid / P.d.S;
+  if (per < 2 || per - 1 > P.ws.scr_copies) return 0;
+  return per;
+}
+
+// Tags of the one-launch decode's arrival words: 40 bits, never 0, a new one
+// per call in this process.
+std::atomic<uint64_t> g_call_tag{0};
+uint64_t next_tag() {
+  const uint64_t t = (g_call_tag.fetch_add(1, std::memory_order_relaxed) + 1) & ((1ull << 40) - 1);
+  return t ? t : 1;
+}
+
 eta_status run_phase(int phase, const Prepared& P, hipStream_t st) {
   const int grid = attend_grid(P.c.kv_dtype, P.d.D, P.d.G);
   hipError_t e = hipSuccess;
@@ -337,9 +370,17 @@ size_t eta_decode_workspace_size(const eta_cache* cache, int num_seqs, int max_b
                                  int num_q_heads) {
   if (check_cache(cache) != ETA_OK) return 0;
   Dims d;
+  if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d) != ETA_OK) return 0;
+  size_t need = workspace_layout(d, nullptr, nullptr);
   // large enough for a decode on the cache's smallest screen blocks as well
-  if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d, sub_blocks(cache)) != ETA_OK) return 0;
-  return workspace_layout(d, nullptr, nullptr);
+  // (more tiles; the page-block layout may still be the larger one, since it
+  // carries the private copies of the one-launch decode when it has few tiles)
+  if (sub_blocks(cache) > 1) {
+    if (dims_of(cache, num_seqs, max_blocks_per_seq, num_q_heads, &d, sub_blocks(cache)) != ETA_OK) return 0;
+    const size_t sub = workspace_layout(d, nullptr, nullptr);
+    if (sub > need) need = sub;
+  }
+  return need;
 }
 
 eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs,
@@ -352,11 +393,26 @@ eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cac
                           out, workspace, ws_bytes, &P);
   if (st != ETA_OK) return st;
   if (phase != ETA_PHASE_ALL) return run_phase(phase, P, (hipStream_t)stream);
+  if (const int per = short_plan(P))
+    return hip_status(launch_decode_short(P.c, P.s, P.p, P.d, P.ws, per, next_tag(), (hipStream_t)stream));
   for (int ph = ETA_PHASE_SCREEN; ph <= ETA_PHASE_MERGE; ++ph) {
     st = run_phase(ph, P, (hipStream_t)stream);
     if (st != ETA_OK) return st;
   }
   return ETA_OK;
+}
+
+int eta_decode_launches(const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs,
+                        int num_q_heads) {
+  // the checks of prepare() that these arguments decide, on stand-in buffers
+  // (nothing is read through them)
+  alignas(256) static const char dummy[256] = {0};
+  const float one = 1.f;
+  Prepared P;
+  eta_status st = prepare(screen, cache, seqs, dummy, num_q_heads, ETA_TAU_CALIBRATED, nullptr, &one, 0.f, 1.f,
+                          0, cache ? cache->block_size : 0, (float*)dummy, (void*)dummy, (size_t)-1, &P);
+  if (st != ETA_OK) return (int)st;
+  return short_plan(P) ? 1 : 2;
 }
 
 eta_status eta_decode_phase(int phase, const eta_cache* cache, const eta_seqs* seqs, const void* q,

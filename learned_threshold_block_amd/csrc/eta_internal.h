@@ -17,6 +17,9 @@ constexpr int kMaxGroup = 8;
 constexpr int kXcdClasses = 8;       // attend workgroup k runs on accelerator complex die k % 8
 constexpr int kWeightOne = 1024;     // fixed-point unit of the per-die work weights
 constexpr int kStatMagic = 0x45544131;
+constexpr int kFusedTiles = 8;       // segments of at most this many tiles are screened in one workgroup
+constexpr int kFusedMaxWgs = 512;    // largest grid of the one-launch decode of short segments
+constexpr int kArrivalStride = 32;   // 64-bit words between two segments' arrival words (own 256-byte line)
 
 // header of the workspace: the sizes the last decode laid it out for, and
 // whether the attend timings of the last decode are present
@@ -67,6 +70,15 @@ struct Ws {
   int32_t* st_head;     // [N*HQ]       admitted blocks per head
   int64_t* st_tokens;   // [N*HQ]
   int32_t* st_rescued;  // [N*HQ]
+  // The arrays from tau to st_rescued lie in one block of scr_stride bytes,
+  // followed by scr_copies more blocks of the same layout: the private copies
+  // of the screen's results for the workgroups of the one-launch decode of
+  // short segments (copy p at byte offset p * scr_stride from the first).
+  int64_t scr_stride;
+  int scr_copies;
+  uint64_t* fused_done; // [S][kArrivalStride] arrivals of the one-launch decode (word 0 of each row):
+                        //              bits 24-63 the call's tag, bits 0-23 the workgroups of the
+                        //              segment whose partial is written
   float* part_ml;       // [(kMaxAttendWgs + S)][G][2]  split running max and sum
   float* part_acc;      // [(kMaxAttendWgs + S)][G][D]  split unnormalised outputs; the partial of
                         //              attend range k in segment s is slot k + s
@@ -156,5 +168,12 @@ hipError_t launch_attend(const CacheView& c, const SeqView& s, const DecodeParam
 hipError_t launch_calibrate(const CacheView& c, const SeqView& s, const CalibParams& p, hipStream_t st);
 hipError_t launch_prefill(const CacheView& c, const SeqView& s, const PrefillParams& p, hipStream_t st);
 int attend_wgs_per_cu(int kv_dtype, int D, int G);  // occupancy of the attend kernel
+// One launch for the whole decode step when every segment has at most
+// kFusedTiles tiles and the bound is the geometric one on page blocks:
+// wgs_per_segment workgroups per segment (at least 2, at most
+// ws.scr_copies + 1), tag identifies the call in the arrival words.
+hipError_t launch_decode_short(const CacheView& c, const SeqView& s, const DecodeParams& p, const Dims& d,
+                               const Ws& ws, int wgs_per_segment, uint64_t tag, hipStream_t st);
+bool decode_short_supported(int kv_dtype, int D, int G);
 
 }  // namespace eta

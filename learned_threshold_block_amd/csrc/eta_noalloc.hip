@@ -11,8 +11,9 @@
 // array's name, which in host code is only a stand-in.
 //
 // Contents carried from one call to the next are either rewritten by every
-// call before they are read (lists, counts, partials; the arrival words are
-// zeroed by the screen phase of each call) or validated when read (the
+// call before they are read (lists, counts, partials; the two-phase decode's
+// arrival words are zeroed by its screen phase, the one-launch decode's carry
+// the call's tag and count as empty otherwise) or validated when read (the
 // per-die weights and the previous call's range timings, which only steer
 // the split of the work), so no clearing is needed between calls.
 #include <hip/hip_runtime.h>
