@@ -294,9 +294,7 @@ void k_attend(AttendArgs A) {
     s = k / A.fz_P;
     W = screen_copy(A.ws, fp);
     // the segment's arrival word as it is now (read long before it is needed)
-    if (threadIdx.x == 0)
-      arrival_seen = __hip_atomic_load(&A.ws.fused_done[(int64_t)s * kArrivalStride], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) arrival_seen = arrival_word(&A.ws.fused_done[(int64_t)s * kArrivalStride]);
     ScreenArgs sa{A.c, A.s, A.p, A.d, W};
     if (k == 0 && threadIdx.x == 0) write_glob<D>(sa);
     if (wave < NT) screen_tile<T, D, G, 0, NW>(sa, s, wave, wave, lane);
@@ -713,27 +711,11 @@ void k_attend(AttendArgs A) {
   wait_stores();
   __syncthreads();
   if constexpr (FUSED) {
-    // one arrival per workgroup in the segment's word (bits 24-63 the call's
-    // tag, bits 0-23 the count). A word without this call's tag (another
-    // call's, or whatever the workspace held) counts as no arrival: it is
-    // replaced by (tag, 1) with one compare-and-swap against the value read
-    // at the start; once the word carries the tag, arrivals are additions.
+    // one arrival per workgroup in the segment's tagged arrival word
     __shared__ int last_lds;
     __shared__ MergeLds<D, G, NTH> mgf;
-    if (threadIdx.x == 0) {
-      uint64_t* wp = &A.ws.fused_done[(int64_t)s * kArrivalStride];
-      const uint64_t tag = A.fz_tag;
-      uint64_t old = arrival_seen, nw = 0;
-      while ((old >> 24) != tag) {
-        if (__hip_atomic_compare_exchange_strong(wp, &old, (tag << 24) + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)) {
-          nw = (tag << 24) + 1;
-          break;
-        }
-      }
-      if (nw == 0) nw = __hip_atomic_fetch_add(wp, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
-      last_lds = (int)(nw & 0xffffffu) == A.fz_P ? 1 : 0;
-    }
+    if (threadIdx.x == 0)
+      last_lds = arrive_tagged(&A.ws.fused_done[(int64_t)s * kArrivalStride], arrival_seen, A.fz_tag, A.fz_P) ? 1 : 0;
     __syncthreads();
     if (last_lds) {  // the segment's partials are slots s fz_P .. s fz_P + fz_P - 1
       merge_fold<D, G, NTH>(A.ws, mgf, s * A.fz_P, 0, A.fz_P - 1, threadIdx.x);

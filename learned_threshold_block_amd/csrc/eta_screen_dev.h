@@ -365,6 +365,30 @@ struct FinArgs {
   int fixed_w[kXcdClasses];
 };
 
+// Arrival of one of a segment's `parts` workgroups in the segment's arrival
+// word (bits 24-63 a call's tag, bits 0-23 the count), after everything the
+// workgroup wrote for the others is at the device's coherence point. A word
+// without this call's tag (another call's, or whatever the workspace held)
+// counts as no arrival: it is replaced by (tag, 1) with one compare-and-swap
+// against `seen`, the word as read when the workgroup started; once the word
+// carries the tag, arrivals are additions. Returns true for the last arrival
+// (thread 0 only).
+__device__ __forceinline__ bool arrive_tagged(uint64_t* wp, uint64_t seen, uint64_t tag, int parts) {
+  uint64_t old = seen, nw = 0;
+  while ((old >> 24) != tag) {
+    if (__hip_atomic_compare_exchange_strong(wp, &old, (tag << 24) + 1, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT)) {
+      nw = (tag << 24) + 1;
+      break;
+    }
+  }
+  if (nw == 0) nw = __hip_atomic_fetch_add(wp, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1;
+  return (int)(nw & 0xffffffu) == parts;
+}
+__device__ __forceinline__ uint64_t arrival_word(const uint64_t* wp) {
+  return __hip_atomic_load(const_cast<uint64_t*>(wp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Work weights of the attend ranges per die class (workgroup k of a launch runs
 // on die k % 8; dies differ in memory throughput by several percent). The
 // previous decode's attend kernel left entries and duration per range; a
