@@ -897,6 +897,7 @@ def main():
         "achieved_gbs_union_kv": m["achieved_gbs_union_kv"],
         "achieved_gbs_all_bytes": m["achieved_gbs_all_bytes"],
         "phase_us": m["phase_us"],
+        **{k: m[k] for k in ("one_launch_us", "two_launch_us_per_step") if k in m},
         "roofline": m["roofline"],
     }
     if not args.no_dense:
