@@ -712,20 +712,17 @@ def two_launch_step_us(S, steps, warmup):
 
 def cpu_baseline(S, budget_s):
     """The fp64 oracle's decode step on one (sequence, KV head) segment at a
-    time, its NumPy products on every BLAS thread the host gives the process,
-    for about `budget_s` seconds; scaled to a full step."""
-    from threadpoolctl import threadpool_info, threadpool_limits
+    time, single-threaded, for about `budget_s` seconds; scaled to a full step."""
+    from threadpoolctl import threadpool_limits
 
     import oracle.eta_oracle as E
-
-    threads = max([int(i["num_threads"]) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
 
     wl = S.wl
     G = wl.group
     bias = S.bias.cpu().numpy()
     segs = [(n, g) for n in range(wl.n_seqs) for g in range(wl.h_kv)]
     done, elapsed, blocks_done = 0, 0.0, 0
-    with threadpool_limits(limits=threads, user_api="blas"):
+    with threadpool_limits(limits=1):
         for (n, g) in segs:
             sub = dict(k_pages=wl.k_pages[:, g:g + 1], v_pages=wl.v_pages[:, g:g + 1])
             bt = wl.block_table[n:n + 1]
@@ -742,9 +739,9 @@ def cpu_baseline(S, budget_s):
                 break
     total_blocks = sum(wl.nblk(n) for (n, g) in segs)
     per_step_s = elapsed * total_blocks / blocks_done
-    return {"value": per_step_s * 1e6, "unit": "us/step", "cores": threads, "kind": "oracle",
+    return {"value": per_step_s * 1e6, "unit": "us/step", "cores": 1, "kind": "oracle",
             "sample": f"{done} of {len(segs)} (sequence, KV head) segments ({G} query heads each), "
-                      f"{elapsed:.1f}s of fp64 NumPy with {threads} BLAS threads, scaled by blocks to the full step",
+                      f"{elapsed:.1f}s of single-threaded fp64 NumPy, scaled by blocks to the full step",
             "cpu": host_cpu_model()}
 
 
