@@ -712,7 +712,9 @@ def two_launch_step_us(S, steps, warmup):
 
 def cpu_baseline(S, budget_s):
     """The fp64 oracle's decode step on one (sequence, KV head) segment at a
-    time, single-threaded, for about `budget_s` seconds; scaled to a full step."""
+    time, single-threaded, for about `budget_s` seconds; scaled to a full step.
+    (Its NumPy products on 16 BLAS threads made the 512K step slower, 3.32 s
+    against 1.94 s on one thread: the products per block are too small.)"""
     from threadpoolctl import threadpool_limits
 
     import oracle.eta_oracle as E
