@@ -51,6 +51,9 @@ CASES = [
     dict(seq_lens=[64 * 300], h_q=8, h_kv=2, d=128, mode="calibrated", density=0.1),   # sparse
     dict(n_seqs=5, h_q=8, h_kv=2, d=128, paged=True, density=[0.05, 0.3, 0.6, 0.9] * 2,
          seq_lens=[9000, 300, 64 * 12, 4097, 32768]),                                  # paged, spread, 512 blocks
+    dict(seq_lens=[4000, 64 * 90], h_q=4, h_kv=4, d=128),                               # G=1, d=128 bf16
+    dict(seq_lens=[64 * 200 + 1, 2500], h_q=8, h_kv=4, d=128, lwb=3),                   # G=2, d=128 bf16, lwb
+    dict(seq_lens=[3000, 64 * 45 + 9], h_q=16, h_kv=4, d=64, kv_dtype="f32"),          # f32 d=64 G=4
 ]
 
 
