@@ -20,7 +20,8 @@
 // the segment's partials into the output, so no separate merge launch waits
 // for the slowest workgroup of all.
 //
-// Inside a workgroup the wavefronts claim kClaim entries at a time from an LDS
+// Inside a workgroup the wavefronts claim kClaim entries at a time (one in the
+// one-launch decode of short segments) from an LDS
 // counter, so the wavefronts that run faster (older waves get issue priority on
 // a SIMD) take more tiles. With ETA_DETERMINISTIC=1 in the environment the
 // split uses equal weights and the claims are static (wavefront w takes claims
@@ -99,19 +100,19 @@ __device__ __forceinline__ int2 resolve_entries(const int* toff_lds, const int2*
   return ev;
 }
 
-// Claim of kClaim consecutive entries of the workgroup's current part. The
-// first claim of every wavefront is static (entries e0 + wave kClaim ..), so
-// no wavefront waits for the counter to be set up; later ones come from an
-// LDS counter that starts at e0 + nw kClaim (the fastest wavefronts take the
-// most entries), or, with `fixed`, follow the static pattern (claims wave,
+// Claim of CL consecutive entries of the workgroup's current part. The first
+// claim of every wavefront is static (entries e0 + wave CL ..), so no
+// wavefront waits for the counter to be set up; later ones come from an LDS
+// counter that starts at e0 + nw CL (the fastest wavefronts take the most
+// entries), or, with `fixed`, follow the static pattern (claims wave,
 // wave + nw, ... counted from e0), which makes the result independent of
 // timing.
-__device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nclaim, int wave, int nw,
-                                         int e0) {
+template <int CL>
+__device__ __forceinline__ int claim_lds(int* ctr, int lane, bool fixed, int& nclaim, int wave, int nw, int e0) {
   const int c = nclaim++;
-  if (fixed || c == 0) return e0 + (c * nw + wave) * kClaim;
+  if (fixed || c == 0) return e0 + (c * nw + wave) * CL;
   int v = 0;
-  if (lane == 0) v = atomicAdd(ctr, kClaim);
+  if (lane == 0) v = atomicAdd(ctr, CL);
   return __builtin_amdgcn_readfirstlane(v);
 }
 
@@ -263,6 +264,10 @@ void k_attend(AttendArgs A) {
   constexpr int LPR = L::LPR, RPI = L::RPI, NI = L::NI, CPL = L::CPL, EPL = L::EPL, EPC = L::EPC;
   constexpr int NW = attend_waves<T, D, G>();  // wavefronts per workgroup
   constexpr int NTH = 64 * NW;
+  // entries per claim: two on the long ranges of the two-launch path; one in
+  // the one-launch decode, whose workgroups hold a dozen entries or so, where
+  // the last claims' tail weighs more (both measured)
+  constexpr int CL = FUSED ? 1 : kClaim;
   constexpr bool kBf16 = T::kBytes == 2;
   using St = typename T::Stored;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -282,6 +287,28 @@ void k_attend(AttendArgs A) {
 
   // the screen's results this workgroup reads (its own copy in the one-launch decode)
   Ws W = A.ws;
+  // queries of a group at this lane's columns, and its thresholds
+  uint32_t qb[G][CPL * 4];  // packed bf16 pairs (bf16 path)
+  float qf[G][EPL];         // float32 path
+  float tau[G];
+  const auto load_q_tau = [&](int n, int g) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const St* qrow = (const St*)A.p.q + ((int64_t)n * HQ + g * G + h) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
+        if constexpr (kBf16) {
+          qb[h][c * 4 + 0] = v.x; qb[h][c * 4 + 1] = v.y; qb[h][c * 4 + 2] = v.z; qb[h][c * 4 + 3] = v.w;
+        } else {
+          qf[h][c * 4 + 0] = __uint_as_float(v.x); qf[h][c * 4 + 1] = __uint_as_float(v.y);
+          qf[h][c * 4 + 2] = __uint_as_float(v.z); qf[h][c * 4 + 3] = __uint_as_float(v.w);
+        }
+      }
+      tau[h] = W.tau[(int64_t)n * HQ + g * G + h];
+    }
+  };
+  __shared__ int fz_ntn;
   const int k = blockIdx.x;
   int s = 0, P = 0, Us = 0, Wp = 0, n_entries = 0;
   uint64_t arrival_seen = 0;  // one-launch decode, thread 0
@@ -299,13 +326,17 @@ void k_attend(AttendArgs A) {
     if (k == 0 && threadIdx.x == 0) write_glob<D>(sa);
     if (wave < NT) screen_tile<T, D, G, 0, NW>(sa, s, wave, wave, lane);
     __syncthreads();
+    // the segment's queries and thresholds (the screen has written them) load
+    // while the finalize runs; the finalize hands over the union count, the
+    // used tiles and the tile prefix (in toff_lds) without a memory round trip
+    load_q_tau(s / HKV, s % HKV);
     FinArgs fa{A.c, A.s, A.d, W, A.p.out, A.p.deterministic, {}};
-    finalize_segment<G, NW>(fa, s);
-    __syncthreads();
-    Us = __builtin_amdgcn_readfirstlane(W.seg_U[s]);  // written by this workgroup before the barrier
+    Us = __builtin_amdgcn_readfirstlane(finalize_segment<G, NW>(fa, s, toff_lds, &fz_ntn));
     lo = (int64_t)fp * Us / A.fz_P;
     hi = (int64_t)(fp + 1) * Us / A.fz_P;
     n_entries = (int)(hi - lo);
+    if (threadIdx.x == 0) ctr_lds = (int)lo + NW * CL;
+    __syncthreads();
   } else {
     // ---- round 1: the segments' union counts (the work split needs them all)
     //      and, when they fit in LDS, every segment's tile prefix, used-tile
@@ -363,7 +394,7 @@ void k_attend(AttendArgs A) {
       pick_lds[0] = threadIdx.x;
       pick_lds[1] = incl0 - v0;
       pick_lds[2] = v0;
-      ctr_lds = (int)(lo - (incl0 - v0)) + NW * kClaim;
+      ctr_lds = (int)(lo - (incl0 - v0)) + NW * CL;
     }
     if (lo < hi && lo >= tot0) {  // beyond the first NTH segments: scan the rest in chunks
       int carry = tot0;
@@ -376,7 +407,7 @@ void k_attend(AttendArgs A) {
           pick_lds[0] = i;
           pick_lds[1] = incl - v;
           pick_lds[2] = v;
-          ctr_lds = (int)(lo - (incl - v)) + NW * kClaim;
+          ctr_lds = (int)(lo - (incl - v)) + NW * CL;
         }
         carry += tot;
       }
@@ -418,25 +449,7 @@ void k_attend(AttendArgs A) {
     const int nfull = seq_len / kBlock;
     const int rem = seq_len - nfull * kBlock;
 
-    // queries of the group at this lane's columns, and thresholds
-    uint32_t qb[G][CPL * 4];  // packed bf16 pairs (bf16 path)
-    float qf[G][EPL];         // float32 path
-    float tau[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const St* qrow = (const St*)A.p.q + ((int64_t)n * HQ + g * G + h) * D;
-#pragma unroll
-      for (int c = 0; c < CPL; ++c) {
-        const uint4 v = *(const uint4*)(qrow + L::col(c, cb));
-        if constexpr (kBf16) {
-          qb[h][c * 4 + 0] = v.x; qb[h][c * 4 + 1] = v.y; qb[h][c * 4 + 2] = v.z; qb[h][c * 4 + 3] = v.w;
-        } else {
-          qf[h][c * 4 + 0] = __uint_as_float(v.x); qf[h][c * 4 + 1] = __uint_as_float(v.y);
-          qf[h][c * 4 + 2] = __uint_as_float(v.z); qf[h][c * 4 + 3] = __uint_as_float(v.w);
-        }
-      }
-      tau[h] = W.tau[(int64_t)n * HQ + g * G + h];
-    }
+    if constexpr (!FUSED) load_q_tau(n, g);  // (the one-launch decode loaded them in its prologue)
     float m[G], l[G], acc[G][EPL];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
@@ -454,14 +467,16 @@ void k_attend(AttendArgs A) {
       toffp = seg_lds + s * rowlen;
       ntn = seg_lds[S * rowlen + s];
       if (!first_part) {
-        if (threadIdx.x == 0) ctr_lds = e0 + NW * kClaim;
+        if (threadIdx.x == 0) ctr_lds = e0 + NW * CL;
         __syncthreads();
       }
+    } else if constexpr (FUSED) {
+      ntn = fz_ntn;  // toff_lds and the claim counter were set up in the prologue
     } else {
       ntn = W.seg_ntn[s];
       const int32_t* toff = W.tile_off + (int64_t)s * rowlen;  // the whole row: the loads do not wait for ntn
       for (int v = threadIdx.x; v < rowlen; v += NTH) toff_lds[v] = toff[v];
-      if (threadIdx.x == 0) ctr_lds = e0 + NW * kClaim;
+      if (threadIdx.x == 0) ctr_lds = e0 + NW * CL;
       __syncthreads();
     }
     first_part = false;
@@ -472,8 +487,8 @@ void k_attend(AttendArgs A) {
     // the current one streams) and the claim after it
     const bool fixed = A.p.deterministic != 0;
     int nclaim = 0;
-    const int c0 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
-    int bc = c0 < e1 ? min(kClaim, e1 - c0) : 0;
+    const int c0 = claim_lds<CL>(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
+    int bc = c0 < e1 ? min(CL, e1 - c0) : 0;
     if (bc > 0) {
       uint32_t ews = 0, ewsn = 0;
       int2 ev = resolve_entries(toffp, tents, ntn, NT, c0, bc, lane, tsubs, &ews);
@@ -494,8 +509,8 @@ void k_attend(AttendArgs A) {
                                                                    : make_uint4(0, 0, 0, 0);
       }
       // the next claim is resolved while the first tile's keys are in flight
-      const int c1 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
-      int bcn = c1 < e1 ? min(kClaim, e1 - c1) : 0;
+      const int c1 = claim_lds<CL>(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
+      int bcn = c1 < e1 ? min(CL, e1 - c1) : 0;
       int2 evn = resolve_entries(toffp, tents, ntn, NT, c1, bcn, lane, tsubs, &ewsn);
       for (;;) {
         const int cur_page = page_nx, cur_jm = jm_nx;
@@ -518,8 +533,8 @@ void k_attend(AttendArgs A) {
           bc = bcn;
           it = 0;
           if (bc > 0) {
-            const int c2 = claim_lds(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
-            bcn = c2 < e1 ? min(kClaim, e1 - c2) : 0;
+            const int c2 = claim_lds<CL>(&ctr_lds, lane, fixed, nclaim, wave, NW, e0);
+            bcn = c2 < e1 ? min(CL, e1 - c2) : 0;
             evn = resolve_entries(toffp, tents, ntn, NT, c2, bcn, lane, tsubs, &ewsn);
           } else {
             has_next = false;

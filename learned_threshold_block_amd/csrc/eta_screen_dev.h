@@ -466,8 +466,13 @@ __device__ void update_weights(const FinArgs& A) {
 
 // Segment s (sequence, KV head), by a workgroup of 256 threads once every
 // tile of the segment is screened: totals, rescue, tile prefix, counts.
+// Returns the segment's union entry count U (every thread). With `lds_toff`,
+// the tile prefix is also written there (entries 0 .. ntn + 1, as in
+// tile_off) and *lds_ntn receives the used-tile count, for a caller in the same
+// workgroup that attends to the segment right after.
 template <int G, int NW>
-__device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
+__device__ __forceinline__ int finalize_segment(const FinArgs& A, int s, int* lds_toff = nullptr,
+                                                int* lds_ntn = nullptr) {
   constexpr int NTH = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -552,7 +557,10 @@ __device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
     }
     int tot;
     const int ex = block_incl_scan<NW>(c, &tot, s_scan) - c;
-    if (use) toff[t] = carry + ex;
+    if (use) {
+      toff[t] = carry + ex;
+      if (lds_toff) lds_toff[t] = carry + ex;
+    }
     carry += tot;
   }
   const int ucnt = carry;
@@ -669,6 +677,11 @@ __device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
     A.ws.tile_cnt[tcx0 + NT] = nres;
     toff[ntn] = ucnt;
     toff[ntn + 1] = ucnt + nres;
+    if (lds_toff) {
+      lds_toff[ntn] = ucnt;
+      lds_toff[ntn + 1] = ucnt + nres;
+      *lds_ntn = ntn;
+    }
   }
   __syncthreads();
   const int U = badT ? 0 : ucnt + s_nres;
@@ -699,6 +712,7 @@ __device__ __forceinline__ void finalize_segment(const FinArgs& A, int s) {
     for (int i = tid; i < G * D; i += NTH)
       A.out[((int64_t)n * HQ + g * G) * D + i] = __builtin_nanf("");
   }
+  return U;
 }
 
 }  // namespace
