@@ -314,3 +314,30 @@ def test_binding_shape_checks():
         a.update(kw)
         with pytest.raises(ValueError):
             _decode_shapes(a["head_dim"], a["lens"], a["bt"], a["q"], learned, a["b"], a["w"])
+
+
+def launches(c=None, s=None, hq=32, bound=_lib.ETA_BOUND_GEOMETRIC):
+    c = c or cache()
+    s = s or seqs()
+    opts = _lib.EtaScreenOptsC(bound, 2.0)
+    return _lib.lib().eta_decode_launches(ctypes.byref(opts), ctypes.byref(c), ctypes.byref(s), hq)
+
+
+def test_launch_form_rule():
+    """One launch for sequences of at most 512 blocks with the geometric page
+    screen and a group size whose attend runs 8 wavefronts; two otherwise;
+    invalid sizes give the same status as eta_decode (host logic only: without
+    a device the attend grid defaults to 256 workgroups)."""
+    assert launches(s=seqs(max_blocks_per_seq=512)) == 1                       # 32K tokens, G = 4, bf16
+    assert launches(s=seqs(max_blocks_per_seq=513)) == 2                       # more than 8 tiles
+    assert launches(c=cache(kmin=FAKE * 12, kmax=FAKE * 13), bound=_lib.ETA_BOUND_QUEST) == 2
+    assert launches(hq=64) == 2                                                # G = 8 at d = 128: 4 wavefronts
+    assert launches(c=cache(head_dim=64), hq=64) == 1                          # G = 8 at d = 64: 8 wavefronts
+    assert launches(s=seqs(num_seqs=64)) == 2                                  # 512 segments: under two per segment
+    assert launches(hq=31) == _lib.ETA_ERR_INVALID_ARGUMENT
+    assert launches(c=cache(head_dim=96)) == _lib.ETA_ERR_UNSUPPORTED
+
+
+def test_launch_form_can_be_forced_to_two(monkeypatch):
+    monkeypatch.setenv("ETA_FUSED", "0")
+    assert launches(s=seqs(max_blocks_per_seq=512)) == 2
