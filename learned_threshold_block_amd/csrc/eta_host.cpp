@@ -404,13 +404,15 @@ eta_status eta_decode_ex(int phase, const eta_screen_opts* screen, const eta_cac
 
 int eta_decode_launches(const eta_screen_opts* screen, const eta_cache* cache, const eta_seqs* seqs,
                         int num_q_heads) {
-  // the checks of prepare() that these arguments decide, on stand-in buffers
-  // (nothing is read through them)
-  alignas(256) static const char dummy[256] = {0};
-  const float one = 1.f;
+  // the checks of prepare() that these arguments decide, with a host stand-in
+  // for the query, output and workspace pointers (prepare only checks their
+  // alignment and lays the workspace out; nothing is read or written there)
+  alignas(256) static char stand_in[256];
+  float one = 1.f;
   Prepared P;
-  eta_status st = prepare(screen, cache, seqs, dummy, num_q_heads, ETA_TAU_CALIBRATED, nullptr, &one, 0.f, 1.f,
-                          0, cache ? cache->block_size : 0, (float*)dummy, (void*)dummy, (size_t)-1, &P);
+  eta_status st = prepare(screen, cache, seqs, stand_in, num_q_heads, ETA_TAU_CALIBRATED, nullptr, &one, 0.f, 1.f,
+                          0, cache ? cache->block_size : 0, reinterpret_cast<float*>(stand_in), stand_in,
+                          (size_t)-1, &P);
   if (st != ETA_OK) return (int)st;
   return short_plan(P) ? 1 : 2;
 }
